@@ -1,0 +1,101 @@
+"""Exact rational arithmetic used to pin the oracle on tiny inputs.
+
+Independent of oracle/: every value is an exact Fraction and every fp32 rounding is done by
+comparing the exact value with its neighbouring fp32 numbers.
+"""
+from __future__ import annotations
+
+from decimal import Decimal, localcontext
+from fractions import Fraction
+
+import numpy as np
+
+
+def _f32_bits(x: np.float32) -> int:
+    return int(np.array(x, dtype=np.float32).view(np.uint32))
+
+
+def rn32(fr: Fraction) -> np.float32:
+    """Round an exact rational to the nearest fp32 value, ties to the even significand."""
+    if fr == 0:
+        return np.float32(0.0)
+    f = np.float32(float(fr))
+    cands = [f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf))]
+    best = None
+    for c in cands:
+        if not np.isfinite(c):
+            continue
+        key = (abs(Fraction(float(c)) - fr), _f32_bits(c) & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return np.float32(best[1])
+
+
+def round_half_even(fr: Fraction) -> int:
+    """Nearest integer to an exact rational, halves to the even integer."""
+    fl = fr.numerator // fr.denominator
+    rem = fr - fl
+    if rem > Fraction(1, 2):
+        return fl + 1
+    if rem < Fraction(1, 2):
+        return fl
+    return fl if fl % 2 == 0 else fl + 1
+
+
+def nearest_code(t: Fraction, qmin: int, qmax: int) -> int:
+    """Exhaustive search over every code c in [qmin, qmax] for the one nearest to t
+    (ties to the even code)."""
+    best = None
+    for c in range(qmin, qmax + 1):
+        key = (abs(t - c), c % 2)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def pow_rn32(x: float, a: float, digits: int = 45) -> np.float32:
+    """fp32 rounding of x**a computed as exp(a ln x) with `digits` decimal digits."""
+    if a == 0.0:
+        return np.float32(1.0)
+    with localcontext() as ctx:
+        ctx.prec = digits
+        v = (Decimal(a) * Decimal(x).ln()).exp()
+    return rn32(Fraction(v))
+
+
+def quantize_group_exact(w, s, qmin: int, qmax: int):
+    """One group: ws = rn32(w s); Delta = rn32(max|ws| / qmax); code = nearest code to
+    rn32(ws / Delta). Returns (codes, Delta) with Delta an fp32 value."""
+    ws = [rn32(Fraction(float(wi)) * Fraction(float(si))) for wi, si in zip(w, s)]
+    m = max(abs(Fraction(float(v))) for v in ws)
+    if m == 0:
+        return [0] * len(w), np.float32(0.0)
+    delta = rn32(m / qmax)
+    if delta == 0:
+        return [0] * len(w), np.float32(0.0)
+    codes = []
+    for v in ws:
+        t = rn32(Fraction(float(v)) / Fraction(float(delta)))
+        codes.append(nearest_code(Fraction(float(t)), qmin, qmax))
+    return codes, delta
+
+
+def loss_exact(X, W, codes, deltas, s, group: int) -> Fraction:
+    """|| X E^T ||_F^2 / (M N) with E = q Delta / s - W, all exact."""
+    M, K = X.shape
+    N = W.shape[0]
+    Xf = [[Fraction(float(X[m, k])) for k in range(K)] for m in range(M)]
+    sf = [Fraction(float(v)) for v in s]
+    E = []
+    for n in range(N):
+        row = []
+        for k in range(K):
+            d = Fraction(float(deltas[n][k // group]))
+            row.append(Fraction(int(codes[n][k])) * d / sf[k] - Fraction(float(W[n, k])))
+        E.append(row)
+    tot = Fraction(0)
+    for m in range(M):
+        for n in range(N):
+            y = sum(Xf[m][k] * E[n][k] for k in range(K))
+            tot += y * y
+    return tot / (M * N)

@@ -1,0 +1,320 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix (no GPU).
+
+Each test names the passage it follows. A plausible slip in the oracle -- a dropped term, a
+wrong sign or index, a transposed operand, a wrong rounding mode or step denominator -- fails
+at least one of them.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import exact_ref as ex
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+def _small_layer(seed, n, k, m, n_out=2, mult=8.0):
+    g = np.random.default_rng(seed)
+    W = (g.integers(-64, 65, size=(n, k)) / 256.0).astype(np.float16)
+    X = g.integers(-16, 17, size=(m, k)) / 8.0
+    X[:, g.choice(k, n_out, replace=False)] *= mult
+    return W, X.astype(np.float16)
+
+
+# --- P1: the equivalent transform ---------------------------------------------------------------
+def test_p1_equivalent_transform_loss_vanishes_without_quantization():
+    """"AWQ 量化方案..." section 二 (W X = (W/s)(X s)) and the AWQ notes' 方法 objective: with
+    Q the identity, Q(W s)(s^-1 X) - W X = 0 for any positive s."""
+    L = workloads.c1_layer()
+    g = np.random.default_rng(11)
+    s = np.exp(g.normal(0, 1.5, size=L.W.shape[1]))
+    ref = (L.X.astype(np.float64) @ L.W.astype(np.float64).T)
+    scale = float((ref * ref).mean())
+    loss = oracle.output_loss(L.X, L.W, s, L.W.astype(np.float64) * s[None, :])
+    assert loss / scale <= 1e-26
+    # the opposite direction is a real error: the test can tell the two apart
+    wrong = oracle.output_loss(L.X, L.W, s, L.W.astype(np.float64) / s[None, :])
+    assert wrong / scale > 1e-2
+
+
+# --- P2: alpha = 0 is plain round-to-nearest -----------------------------------------------------
+def test_p2_alpha_zero_is_plain_rtn():
+    """AWQ notes, 发现: RTN quantizes directly; at alpha = 0, s = s_X^0 = 1 exactly, so codes and
+    loss reduce to per-group RTN. Reference RTN = torch's fp32 division and torch.round."""
+    L = workloads.c1_layer()
+    sx = oracle.act_stats(L.X)
+    S = oracle.scale_table(sx, 20)
+    assert np.all(S[0] == np.float32(1.0))
+    q, delta = oracle.quantize(L.W, S[0], 4, 128)
+    Wt = torch.from_numpy(L.W.astype(np.float32)).reshape(512, 4, 128)
+    step = Wt.abs().amax(dim=2, keepdim=True) / 7.0
+    q_rtn = torch.round(Wt / step).clamp(-8, 7).reshape(512, 512).to(torch.int8).numpy()
+    assert np.array_equal(q, q_rtn)
+    assert np.array_equal(delta, step.squeeze(2).numpy())
+    Xd = torch.from_numpy(L.X.astype(np.float64))
+    Wd = torch.from_numpy(L.W.astype(np.float64))
+    Wq = torch.from_numpy(q_rtn.astype(np.float64)) * step.double().expand(-1, -1, 128).reshape(512, 512)
+    rtn_loss = float(((Xd @ Wq.T - Xd @ Wd.T) ** 2).mean())
+    res = oracle.search_layer(L.W, L.X, sx)
+    assert res["losses"][0] == pytest.approx(rtn_loss, rel=1e-12)
+
+
+# --- P3: the step formula ---------------------------------------------------------------------
+@pytest.mark.parametrize("bits", [4, 3])
+def test_p3_step_reaches_qmax_and_never_qmin(bits):
+    """Delta = max|ws| / (2^(b-1) - 1) ("AWQ 量化方案..." section 三, g_scale): the largest
+    magnitude of each group maps to exactly +-qmax, and -2^(b-1) is never produced.
+    (With the AWQ notes' 2^(b-1) denominator the maximum would map to 2^(b-1) and saturate.)"""
+    L = workloads.c1_layer()
+    S = oracle.scale_table(oracle.act_stats(L.X), 20)
+    qmin, qmax = oracle.code_range(bits)
+    for i in range(20):
+        q, delta = oracle.quantize(L.W, S[i], bits, 128)
+        ws = L.W.astype(np.float32) * S[i][None, :]
+        qg = q.reshape(512, 4, 128)
+        wsg = np.abs(ws.reshape(512, 4, 128))
+        assert np.all(np.abs(qg).max(axis=2) == qmax)
+        am = wsg.argmax(axis=2)
+        assert np.all(np.abs(np.take_along_axis(qg, am[:, :, None], 2)) == qmax)
+        assert not np.any(q == qmin)
+
+
+# --- P4: rounding mode ------------------------------------------------------------------------
+def test_p4_round_half_to_even_golden():
+    rows = _golden_rows("round_half_even.txt")
+    W = np.zeros((1, 128), dtype=np.float32)
+    for j, (v, _) in enumerate(rows):
+        W[0, j] = float(v)
+    q, delta = oracle.quantize(W, np.ones(128, np.float32), 4, 128)
+    assert delta[0, 0] == np.float32(1.0)
+    assert [int(c) for c in q[0, :len(rows)]] == [int(c) for _, c in rows]
+
+
+# --- P5: the pages' worked example -------------------------------------------------------------
+def test_p5_worked_example_quantization_schemes():
+    kv = dict(_golden_rows("worked_example_quant_schemes.txt"))
+    r, w, a = float(kv["range_max"]), float(kv["weight"]), float(kv["activation"])
+    W = np.zeros((1, 128), dtype=np.float32)
+    W[0, 0], W[0, 1], W[0, 2] = r, w, -r
+    s = np.ones(128, np.float32)
+    q, delta = oracle.quantize(W, s, 4, 128)
+    assert int(q[0, 1]) == int(kv["expected_code"])
+    E = oracle.error_matrix(W, q, delta, s, 128)
+    assert abs(E[0, 1]) == pytest.approx(float(kv["expected_weight_error"]), rel=1e-6)
+    X = np.zeros((1, 128))
+    X[0, 1] = a
+    loss = oracle.output_loss(X, W, s, oracle.dequant_scaled(q, delta, 128))
+    assert math.sqrt(loss) == pytest.approx(float(kv["expected_output_error"]), rel=1e-6)
+
+
+# --- P6: a power-of-two factor on s changes no code -------------------------------------------
+def test_p6_power_of_two_rescale_of_s_keeps_codes():
+    """Normalising s (÷mean in the FlashAttention+AWQ page's AWQQuantizer, ÷max in section 三 of
+    "AWQ 量化方案...") is a global factor; a power of two leaves every code bit-identical."""
+    L = workloads.c1_layer()
+    S = oracle.scale_table(oracle.act_stats(L.X), 20)
+    for i in (0, 5, 12, 19):
+        q1, d1 = oracle.quantize(L.W, S[i], 4, 128)
+        q2, d2 = oracle.quantize(L.W, S[i] * np.float32(4.0), 4, 128)
+        assert np.array_equal(q1, q2)
+        assert np.array_equal(d2, d1 * np.float32(4.0))
+
+
+# --- P7: the error-ratio argument --------------------------------------------------------------
+def test_p7_scaling_one_channel_by_two_halves_its_error():
+    """AWQ notes, 方法: rounding error is uniform on [0, 0.5] steps; scaling one weight by s > 1
+    barely moves the group maximum, so its error in original units shrinks by Delta'/Delta * 1/s.
+    With s = 2 on a non-maximal channel the step is unchanged and the mean error halves."""
+    g = np.random.default_rng(7)
+    G = 100_000
+    W = g.standard_normal((G, 128)).astype(np.float32)
+    m = np.abs(W).max(axis=1)
+    cand = np.abs(W) < (m[:, None] / 2)
+    k = np.argmax(np.where(cand, g.random((G, 128)), -1.0), axis=1)   # a random admissible channel
+    ones = np.ones(128, np.float32)
+    q1, d1 = oracle.quantize(W, ones, 4, 128)
+    err1 = np.abs(oracle.error_matrix(W, q1, d1, ones, 128)[np.arange(G), k])
+    err2 = np.empty(G)
+    d2 = np.empty(G, np.float32)
+    # one row at a time would be slow; group rows by their chosen channel
+    for kk in range(128):
+        rows = np.flatnonzero(k == kk)
+        if rows.size == 0:
+            continue
+        s = ones.copy()
+        s[kk] = 2.0
+        q, d = oracle.quantize(W[rows], s, 4, 128)
+        err2[rows] = np.abs(oracle.error_matrix(W[rows], q, d, s, 128)[:, kk])
+        d2[rows] = d[:, 0]
+    assert np.array_equal(d2, d1[:, 0])
+    ratio = err2.mean() / err1.mean()
+    assert abs(ratio - 0.5) < 0.01
+
+
+# --- P8: brute force on tiny layers ------------------------------------------------------------
+@pytest.mark.parametrize("seed,n,k,m,bits", [(1, 2, 128, 3, 4), (2, 3, 256, 5, 4),
+                                             (3, 2, 256, 4, 3)])
+def test_p8_brute_force_tiny_layer(seed, n, k, m, bits):
+    """Every code is the nearest of all 2^b codes to the fp32 quotient (ties to even), every loss
+    is the exact rational ||X E^T||^2/(MN), and alpha* is the exhaustive argmin."""
+    W, X = _small_layer(seed, n, k, m)
+    n_grid = 6
+    sx = oracle.act_stats(X)
+    for kk in range(k):
+        exact = Fraction(sum(abs(Fraction(float(v))) for v in X[:, kk])) / m
+        assert sx[kk] == ex.rn32(exact)
+    res = oracle.search_layer(W, X, sx, bits=bits, group=128, n_grid=n_grid)
+    qmin, qmax = oracle.code_range(bits)
+    exact_losses = []
+    for i in range(n_grid):
+        s = res["scales"][i]
+        q, delta = oracle.quantize(W, s, bits, 128)
+        codes, deltas = [], []
+        for r in range(n):
+            row_c, row_d = [], []
+            for g0 in range(0, k, 128):
+                c, d = ex.quantize_group_exact(W[r, g0:g0 + 128], s[g0:g0 + 128], qmin, qmax)
+                row_c += c
+                row_d.append(d)
+            codes.append(row_c)
+            deltas.append(row_d)
+        assert np.array_equal(q, np.array(codes, dtype=np.int8))
+        assert np.array_equal(delta, np.array(deltas, dtype=np.float32))
+        le = ex.loss_exact(X, W, codes, deltas, s, 128)
+        exact_losses.append(le)
+        assert res["losses"][i] == pytest.approx(float(le), rel=1e-12)
+    best = min(range(n_grid), key=lambda i: (exact_losses[i], i))
+    assert res["best"] == best
+
+
+# --- P9: direct and Gram forms -----------------------------------------------------------------
+def test_p9_direct_and_gram_forms_agree():
+    """The GPTQ section of "量化方案详解" writes the layer objective as (W - Wq)^T H (W - Wq)
+    with H = X^T X; the same identity gives ||X E^T||^2 = sum_n E_n H E_n^T."""
+    L = workloads.c1_layer()
+    sx = oracle.act_stats(L.X)
+    d = oracle.search_layer(L.W, L.X, sx, form="direct")
+    g = oracle.search_layer(L.W, L.X, sx, form="gram")
+    np.testing.assert_allclose(g["losses"], d["losses"], rtol=1e-12)
+    Ls = workloads.c2_like_layer(n=192, k=384, m=1500, config=2)
+    sx = oracle.act_stats(Ls.X)
+    d = oracle.search_layer(Ls.W, Ls.X, sx, form="direct")
+    g = oracle.search_layer(Ls.W, Ls.X, sx, form="gram")
+    np.testing.assert_allclose(g["losses"], d["losses"], rtol=1e-12)
+    assert d["best"] == g["best"]
+
+
+# --- P10: activation statistics -----------------------------------------------------------------
+def test_p10_stats_constant_column_and_order_independence():
+    g = np.random.default_rng(5)
+    X = (g.standard_normal((3000, 256)) * np.exp(g.normal(0, 2, 256))).astype(np.float16)
+    X[:, 7] = np.float16(-1.375)
+    X[:, 9] = np.float16(6.1e-5)           # fp16 subnormal magnitudes still sum exactly
+    sx = oracle.act_stats(X)
+    assert sx[7] == np.float32(1.375)
+    assert sx[9] == np.float32(float(np.float16(6.1e-5)))
+    perm = g.permutation(3000)
+    assert np.array_equal(oracle.act_stats(X[perm]), sx)
+    assert np.array_equal(oracle.act_stats(X, chunk_rows=7), sx)
+    for kk in (0, 100, 255):
+        exact = Fraction(math.fsum(abs(float(v)) for v in X[:, kk])) / 3000
+        assert sx[kk] == ex.rn32(exact)
+
+
+# --- P11: packing ------------------------------------------------------------------------------
+def test_p11_pack_golden_and_roundtrip():
+    rows = _golden_rows("pack_nibbles.txt")
+    q = np.array([[int(v) for v in r[:8]] for r in rows], dtype=np.int8)
+    words = oracle.pack_int4(q)
+    assert [int(w[0]) for w in words] == [int(r[8], 16) for r in rows]
+    g = np.random.default_rng(3)
+    q = g.integers(-8, 8, size=(37, 256), dtype=np.int8)
+    assert np.array_equal(oracle.unpack_int4(oracle.pack_int4(q)), q)
+
+
+# --- P12: W4A16 ---------------------------------------------------------------------------------
+def test_p12_w4a16_integer_case_and_exact_rationals():
+    """"AWQ 量化方案..." section 三, QuantLinear.forward: unit steps and s make the product an
+    integer matmul; general fp16 steps and s checked against exact rationals."""
+    g = np.random.default_rng(9)
+    q = g.integers(-8, 8, size=(24, 256), dtype=np.int8)
+    A = g.integers(-3, 4, size=(5, 256)).astype(np.float16)
+    qw = oracle.pack_int4(q)
+    y = oracle.w4a16(A, qw, np.ones((24, 2), np.float16), np.ones(256, np.float16), 128)
+    assert np.array_equal(y, (A.astype(np.int64) @ q.astype(np.int64).T).astype(np.float64))
+    sc = (0.01 * np.abs(g.standard_normal((24, 2))) + 1e-3).astype(np.float16)
+    s = (1 + np.abs(g.standard_normal(256))).astype(np.float16)
+    A = g.standard_normal((3, 256)).astype(np.float16)
+    y = oracle.w4a16(A, qw, sc, s, 128)
+    for mm in range(3):
+        for nn in (0, 5, 23):
+            e = sum(Fraction(float(A[mm, kk])) / Fraction(float(s[kk])) * int(q[nn, kk]) *
+                    Fraction(float(sc[nn, kk // 128])) for kk in range(256))
+            assert y[mm, nn] == pytest.approx(float(e), rel=1e-13, abs=1e-300)
+
+
+# --- grid and scale table ----------------------------------------------------------------------
+def test_scale_table_matches_high_precision_power():
+    """s_i = fp32(max(s_X, 1e-5)^alpha_i) (AWQ notes 方法: s = s_X^alpha, alpha in [0, 1]),
+    checked against a 45-digit exp(alpha ln x) correctly rounded to fp32; ends exact."""
+    L = workloads.c1_layer()
+    sx = oracle.act_stats(L.X)
+    S = oracle.scale_table(sx, 20)
+    base = np.maximum(sx, np.float32(1e-5))
+    assert np.array_equal(S[-1], base)
+    assert np.all(S[0] == 1.0)
+    alphas = oracle.alpha_grid(20)
+    assert alphas[0] == 0.0 and alphas[-1] == 1.0 and alphas[5] == 5 / 19
+    for i in range(1, 19):
+        for kk in range(0, 512, 7):
+            assert S[i, kk] == ex.pow_rn32(float(base[kk]), alphas[i]), (i, kk)
+
+
+def test_floor_applies_to_dead_channels():
+    sx = np.array([0.0, 1e-7, 2.0], np.float32)
+    S = oracle.scale_table(sx, 3)
+    f = np.float32(1e-5)
+    assert S[2, 0] == f and S[2, 1] == f and S[2, 2] == np.float32(2.0)
+    assert S[1, 0] == np.float32(math.sqrt(float(f)))
+
+
+def test_argmin_takes_lowest_index_on_ties():
+    assert oracle.argmin_lowest([3.0, 1.0, 1.0, 2.0]) == 1
+    assert oracle.argmin_lowest([1.0, 1.0]) == 0
+
+
+def test_all_zero_group_has_zero_step_and_codes():
+    W = np.zeros((2, 256), np.float32)
+    W[1, 200] = 0.5
+    q, d = oracle.quantize(W, np.ones(256, np.float32), 4, 128)
+    assert d[0, 0] == 0 and d[0, 1] == 0 and d[1, 0] == 0 and d[1, 1] == np.float32(0.5 / 7)
+    assert np.count_nonzero(q) == 1 and q[1, 200] == 7
+
+
+def test_search_improves_on_rtn_for_outlier_layer():
+    """AWQ notes, 方法: protecting the salient channels lowers the output error, so on a layer
+    with outlier activation channels some alpha > 0 beats alpha = 0 (RTN)."""
+    L = workloads.c1_layer()
+    res = oracle.search_layer(L.W, L.X, oracle.act_stats(L.X))
+    assert res["best"] > 0
+    assert res["losses"][res["best"]] < 0.6 * res["losses"][0]
+
+
+def test_nonfinite_inputs_are_rejected():
+    W = np.ones((1, 128), np.float32)
+    W[0, 3] = np.nan
+    with pytest.raises(ValueError):
+        oracle.quantize(W, np.ones(128, np.float32))
+    with pytest.raises(ValueError):
+        oracle.act_stats(np.array([[np.inf, 1.0]]))
