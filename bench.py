@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the AWQ hot path on one MI355X.
+
+One step = one pass of the whole path over the LLaMA-7B-shaped attention projection (W fp16
+4096x4096, 65536 calibration tokens = 128 samples x 512 tokens, INT4, group 128, 20 alpha points):
+    awq_act_stats -> awq_search_layer -> awq_pack_int4(s*) -> w4a16_gemm (decode, M = 1).
+Inputs are synthetic (seeded, see workloads/) and resident in HBM before the timed region.
+
+Prints ONE JSON line. `value` is milliseconds per layer (lower is better). Besides the contract
+fields it carries
+  roofline      the loss contraction (the dominant kernel) against the dense fp16 MFMA peak,
+                its duration measured with HIP events on the library's stream in every step;
+  stages_ms     mean duration of every kernel of the step;
+  w4a16         the W4A16 kernel at the batch sizes 1, 4, 16, 64, 512 for 4096x4096 and
+                11008x4096, over rotated weight copies (> 256 MB, so HBM and not the
+                Infinity Cache is measured): GB/s and fraction of 8 TB/s (TFLOP/s and MFMA
+                fraction at M = 512);
+  cpu_baseline  the CPU oracle on a bounded sample of the same layer, scaled to ms per layer.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
+N_, K_, M_ = 4096, 4096, 65536
+N_GRID = 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-w4a16-sweep", action="store_true")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------------------------
+def w4a16_sweep(awq, torch):
+    """Time W4A16 over rotated weight copies with HIP events on the current stream."""
+    import numpy as np
+    import workloads
+    out = []
+    for (n, k) in ((4096, 4096), (11008, 4096)):
+        qw, sc, s = workloads.w4a16_random_artifacts(n, k, config=4)
+        wbytes = qw.nbytes + sc.nbytes
+        copies = max(4, int(600e6 // wbytes) + 1)      # > 2 x the 256 MB Infinity Cache
+        qws = [torch.from_numpy(qw.view(np.int32)).cuda() for _ in range(copies)]
+        scs = [torch.from_numpy(sc).cuda() for _ in range(copies)]
+        s_d = torch.from_numpy(s).cuda()
+        for m in (1, 4, 16, 64, 512):
+            A = torch.from_numpy(workloads.w4a16_activations(m, k, config=4)).cuda()
+            Y = torch.empty((m, n), dtype=torch.float16, device="cuda")
+            for i in range(copies):                     # warm-up, one pass over every copy
+                awq.w4a16_gemm(A, qws[i], scs[i], s_d, out=Y)
+            reps = max(copies, 200)
+            st = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(st)
+            for r in range(reps):
+                i = r % copies
+                awq.w4a16_gemm(A, qws[i], scs[i], s_d, out=Y)
+            e1.record(st)
+            e1.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            nbytes = n * k // 2 + n * (k // 128) * 2 + k * 2 + m * k * 2 + m * n * 2
+            flops = 2.0 * m * n * k
+            rec = {"n": n, "k": k, "m": m, "us": round(us, 3), "bytes": nbytes,
+                   "gbs": round(nbytes / us / 1e3, 1),
+                   "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                   "tflops": round(flops / us / 1e6, 2)}
+            if m >= 512:
+                rec["mfma_frac"] = round(flops / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4)
+            out.append(rec)
+            log("w4a16", rec)
+        del qws, scs
+        torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+def cpu_baseline(L, n_grid):
+    """The oracle as it stands, on a bounded sample of the same layer, scaled to ms per layer.
+
+    Sample: the activation statistics and the Gram matrix H = X^T X over the first 4096 of the
+    65536 tokens (both scale linearly in the token count: x16), the quantization and the
+    Gram-form loss of 2 of the 20 grid points (x10), then the argmin, the packing and one
+    decode-sized W4A16 (x1)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    Ms = 4096
+    Xs = L.X[:Ms]
+    t = {}
+    t0 = time.perf_counter()
+    sx = oracle.act_stats(Xs)
+    t["stats"] = (time.perf_counter() - t0) * (L.X.shape[0] / Ms)
+    t0 = time.perf_counter()
+    H = oracle.gram(Xs)
+    t["gram"] = (time.perf_counter() - t0) * (L.X.shape[0] / Ms)
+    S = oracle.scale_table(sx, n_grid)
+    t0 = time.perf_counter()
+    losses = []
+    for i in (5, 6):
+        q, d = oracle.quantize(L.W, S[i])
+        losses.append(oracle.loss_gram(H, oracle.error_matrix(L.W, q, d, S[i]), Ms))
+    t["alpha_points"] = (time.perf_counter() - t0) * (n_grid / 2)
+    t0 = time.perf_counter()
+    best = oracle.argmin_lowest(losses)
+    p = oracle.pack_layer(L.W, S[5 + best])
+    A = np.ones((1, L.W.shape[1]), np.float16)
+    oracle.w4a16(A, p["qweight"], p["scales16"], p["s16"])
+    t["pack_w4a16"] = time.perf_counter() - t0
+    total_ms = 1e3 * sum(t.values())
+    return {"value": round(total_ms, 1), "unit": "ms/layer", "cores": int(cores),
+            "kind": "oracle",
+            "sample": "stats and H=X^T X over 4096 of 65536 tokens (x16), quantize+Gram loss "
+                      "for 2 of 20 alpha points (x10), argmin+pack+W4A16(M=1) once",
+            "parts_ms": {k: round(1e3 * v, 1) for k, v in t.items()}}
+
+
+# ---------------------------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
+              "(the search shards by layer or by output rows with one small exchange; see the "
+              "design notes)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import workloads
+    import post_weight_quantization_channel_amd as awq
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    log("generating the synthetic layer (W 4096x4096 fp16, X 65536x4096 fp16) ...")
+    L = workloads.c2_like_layer()
+    W = torch.from_numpy(L.W).to(dev)
+    X = torch.from_numpy(L.X).to(dev)
+    A1 = torch.from_numpy(workloads.w4a16_activations(1, K_, config=2)).to(dev)
+    cfg = awq.AwqConfig(bits=4, group=128, n_grid=N_GRID)
+    ws_stats = torch.empty(awq.act_stats_workspace_bytes(M_, K_), dtype=torch.uint8, device=dev)
+    ws_search = torch.empty(awq.search_workspace_bytes(M_, N_, K_, torch.float16, cfg),
+                            dtype=torch.uint8, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream()
+
+    def step(prof):
+        e0, e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+        e0.record(st)
+        sx, _ = awq.act_stats(X, flags=flags, workspace=ws_stats)
+        e1.record(st)
+        res = awq.search_layer(W, X, sx, cfg, flags=flags, workspace=ws_search, stage_ms=prof)
+        e2.record(st)
+        p = awq.pack_int4(W, res.s_best, cfg, flags=flags)
+        e3.record(st)
+        Y = awq.w4a16_gemm(A1, p.qweight, p.scales16, p.s16)
+        return res, (e0, e1, e2, e3), Y
+
+    log(f"warmup {args.warmup} step(s) ...")
+    for _ in range(args.warmup):
+        step({})
+    torch.cuda.synchronize()
+
+    stage_runs, ev_runs = [], []
+    log(f"timing {args.steps} step(s) ...")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(st)
+    for _ in range(args.steps):
+        prof = {}
+        res, evs, _ = step(prof)
+        stage_runs.append(prof)
+        ev_runs.append(evs)
+    t_end.record(st)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    stats_ms = statistics.mean(a.elapsed_time(b) for a, b, _, _ in ev_runs)
+    pack_ms = statistics.mean(c.elapsed_time(d) for _, _, c, d in ev_runs)
+    stages = {k: statistics.mean(r[k] for r in stage_runs) for k in stage_runs[0]}
+    flag_bits = int(flags.item())
+    losses = res.losses.cpu().numpy()
+    best = int(res.best.item())
+    ls = np.sort(losses)
+    log(f"ms/step {ms_per_step:.3f}; stages {stages}; stats {stats_ms:.4f} ms; pack "
+        f"{pack_ms:.4f} ms; alpha* {best}; flags {flag_bits}")
+
+    loss_ms = stages["lossgemm"]
+    flops = 2.0 * M_ * N_ * K_ * N_GRID
+    achieved = flops / (loss_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "lossgemm_kernel", "achieved": round(achieved, 1),
+                "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": flops, "launch_ms": round(loss_ms, 4)}
+
+    other = {
+        "act_stats": {"ms": round(stats_ms, 4), "bytes": M_ * K_ * 2},
+        "quantize_stack": {"ms": round(stages["quantize_stack"], 4),
+                           "bytes": N_ * K_ * 2 + N_GRID * N_ * K_ * 2},
+        "pack": {"ms": round(pack_ms, 4), "bytes": N_ * K_ * 2 + N_ * K_ // 2 + N_ * K_ // 64},
+    }
+    for v in other.values():
+        v["gbs"] = round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)
+        v["hbm_frac"] = round(v["gbs"] / HBM_PEAK_GBS, 4)
+
+    del ws_search, X
+    torch.cuda.empty_cache()
+    w4 = [] if args.no_w4a16_sweep else w4a16_sweep(awq, torch)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on a bounded sample) ...")
+        cpu = cpu_baseline(L, N_GRID)
+        log("cpu baseline", cpu)
+
+    line = {
+        "metric": "AWQ search ms per 4096x4096 layer + % MFMA peak; W4A16 GEMV HBM GB/s",
+        "value": round(ms_per_step, 3), "unit": "ms/layer", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "llama7b_attn_proj_4096x4096_tokens65536_int4_g128_grid20",
+                   "N": N_, "K": K_, "M": M_, "bits": 4, "group": 128, "n_grid": N_GRID,
+                   "w4a16_decode_m": 1},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "hbm_stages": other,
+        "w4a16": w4,
+        "alpha_star": best,
+        "loss_gap": float((ls[1] - ls[0]) / ls[0]),
+        "flags": flag_bits,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

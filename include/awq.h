@@ -1,0 +1,181 @@
+/*
+ * awq.h -- C ABI of the AWQ (activation-aware weight quantization) engine for AMD gfx950.
+ *
+ * The engine computes, for one linear layer y = W x with W [N, K] (rows = output channels,
+ * columns = input channels) and calibration activations X [M, K] (tokens x input channels):
+ *   1. awq_act_stats     s_X[k] = mean_m |X[m,k]|
+ *   2. awq_search_layer  for alpha_i = i/(n_grid-1): s_i = max(s_X, s_floor)^alpha_i,
+ *                        group-wise symmetric round-to-nearest quantization of W*s_i, and the
+ *                        output loss L_i = ||Q(W s_i)(s_i^-1 X) - W X||_F^2 / (M N);
+ *                        alpha* = argmin_i L_i (lowest index on ties), s* = s_{i*}
+ *   3. awq_pack_int4     codes of Q(W s*) packed 8 per uint32, fp16 group steps, fp16 s*
+ *   4. w4a16_gemm        Y = (A / s) (q * step)^T with fp16 A and Y
+ *
+ * Pages defining the operations (cited by title and section):
+ *   [notes]  bg51717.github.io/14592, notes on "AWQ: Activation-aware Weight Quantization for
+ *            LLM Compression and Acceleration", section 方法: Q(w) = Delta * Round(w / Delta),
+ *            the objective L(s) = ||Q(W s)(s^-1 X) - W X||, and s = s_X^alpha, alpha in [0,1].
+ *   [eng]    qwbw.cn/news/39982, "AWQ 量化方案：激活感知的权重量化与工程实现全解析", section 三:
+ *            awq_quantize (per-channel activation norm, group 128, step max/(2^(b-1)-1), round,
+ *            clamp to [-2^(b-1), 2^(b-1)-1]) and QuantLinear (packed codes, per-group fp16
+ *            steps, per-channel scale; forward = scale the input, dequantize, linear).
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library never allocates,
+ *     frees or synchronises; it launches kernels on `stream` and returns. Outputs are valid once
+ *     the stream has reached that point.
+ *   - Matrices are dense row-major. fp16/bf16 values are passed as their 16-bit patterns.
+ *   - Host-checkable problems return a non-zero awq_status BEFORE any HIP call; no output is
+ *     touched then. Problems only the device can see set bits (AWQ_FLAG_*) in the caller's
+ *     uint32 `flags` word with atomic OR; the library never clears it, so the caller zeroes it.
+ *   - Every device-side reduction has a fixed order: results are bitwise reproducible.
+ *   - No global state; calls are thread-safe. Calls that share a workspace must be ordered.
+ *   - The awq_cfg struct is read during the call only.
+ */
+#ifndef AWQ_H_
+#define AWQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AWQ_OK = 0,
+  AWQ_ERR_NULL = 1,       /* a required pointer is NULL                                   */
+  AWQ_ERR_SHAPE = 2,      /* M, N or K out of range, K % group != 0, ldx < K, misalignment */
+  AWQ_ERR_DTYPE = 3,      /* dtype not accepted by this call                               */
+  AWQ_ERR_CONFIG = 4,     /* bits not in {3,4}, group != 128, n_grid not in [2,64],        */
+                          /* s_floor not a positive finite number                          */
+  AWQ_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than the *_workspace_bytes query    */
+  AWQ_ERR_HIP = 6         /* a kernel launch reported an error                             */
+} awq_status;
+
+typedef enum { AWQ_F32 = 0, AWQ_F16 = 1, AWQ_BF16 = 2 } awq_dtype;
+
+/* Device-side conditions, OR-ed into *flags. */
+enum {
+  AWQ_FLAG_NONFINITE_X = 1u << 0,      /* X holds an Inf or NaN                                */
+  AWQ_FLAG_NONFINITE_W = 1u << 1,      /* W holds an Inf or NaN                                */
+  AWQ_FLAG_STATS_INEXACT = 1u << 2,    /* a column sum of |X| reached 2^29 (fp16/bf16 X): the   */
+                                       /* fp64 sum is no longer exact / order-free              */
+  AWQ_FLAG_X_F16_RANGE = 1u << 3,      /* fp32/bf16 X has a value beyond fp16 range; the loss   */
+                                       /* contraction runs on fp16 operands                     */
+  AWQ_FLAG_SCALE16_OVERFLOW = 1u << 4, /* a group step or s exceeds the fp16 range at packing   */
+  AWQ_FLAG_SCALE16_SUBNORMAL = 1u << 5,/* a non-zero group step or s is fp16-subnormal or 0     */
+  AWQ_FLAG_NONFINITE_LOSS = 1u << 6,   /* some L_i is not finite                                */
+  AWQ_FLAG_STEP_UNDERFLOW = 1u << 7    /* a group with max|w s| > 0 got step 0 (codes set to 0)*/
+};
+
+typedef struct {
+  int32_t bits;    /* 4 (codes [-8,7]) or 3 (codes [-4,3]); the step is max|w s|/(2^(bits-1)-1) */
+  int32_t group;   /* input channels per step; 128 is the only accepted value                  */
+  int32_t n_grid;  /* number of alpha points, alpha_i = i/(n_grid-1), 2 <= n_grid <= 64         */
+  float s_floor;   /* s = max(s_X, s_floor)^alpha, typically 1e-5f                              */
+} awq_cfg;
+
+/* Human-readable name of a status code (static storage). */
+const char* awq_status_string(awq_status status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t awq_version(void);
+
+/* ------------------------------------------------------------------------------------------
+ * awq_act_stats -- per-input-channel activation magnitude.
+ *   [notes] 方法 (s_X is computed from the layer input); [eng] 三 Step 1 (act_norm = mean|X|
+ *   over calibration samples).
+ * X      [M, K] with row stride ldx elements (ldx >= K, ldx % 8 == 0, K % 8 == 0), dtype xdt
+ *        (AWQ_F16, AWQ_BF16 or AWQ_F32); 16-byte aligned.
+ * sx     out, fp32 [K]: sx[k] = fp32( (sum_m |X[m,k]|) / M ), the sum accumulated in fp64
+ *        (exact for fp16/bf16 while below 2^29, see AWQ_FLAG_STATS_INEXACT) and the division
+ *        done in fp64 before the single rounding to fp32.
+ * flags  in/out, uint32 [1]: NONFINITE_X, STATS_INEXACT.
+ * ws     device workspace of at least awq_act_stats_workspace_bytes(M, K) bytes.
+ * Errors: NULL pointers -> AWQ_ERR_NULL; M < 1, K < 8, shape/stride rules -> AWQ_ERR_SHAPE;
+ *         unknown xdt -> AWQ_ERR_DTYPE; small workspace -> AWQ_ERR_WORKSPACE.
+ * ---------------------------------------------------------------------------------------- */
+size_t awq_act_stats_workspace_bytes(int64_t M, int64_t K);
+awq_status awq_act_stats(const void* X, awq_dtype xdt, int64_t M, int64_t K, int64_t ldx,
+                         float* sx, uint32_t* flags, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * awq_search_layer -- the alpha grid search of [notes] 方法.
+ * W      [N, K] row-major, dtype wdt (AWQ_F16 or AWQ_F32), 16-byte aligned; N >= 1.
+ * X      [M, K] row-major (row stride K), dtype xdt (AWQ_F16, AWQ_BF16 or AWQ_F32).
+ * sx     fp32 [K], typically the output of awq_act_stats on the same X.
+ * cfg    host pointer, see awq_cfg. K must be a multiple of cfg->group.
+ * For each i: s_i[k] = fp32(pow_f64(max(sx[k], s_floor), i/(n_grid-1))),
+ *   codes q = clamp(rint(fp32(fp32(w s_i) / Delta)), -2^(b-1), 2^(b-1)-1) with
+ *   Delta = fp32(max_group |fp32(w s_i)| / (2^(b-1)-1)) per (row, group of 128), all in IEEE
+ *   fp32 with round-to-nearest-even (bit-identical to the specification);
+ *   L_i = ||X E_i^T||_F^2 / (M N), E_i = q Delta / s_i - W, contracted on fp16 operands with
+ *   fp32 accumulation and fp64 reduction (relative error ~1e-5).
+ * losses out, fp64 [n_grid]; best out, int32 [1] = i*; s_best out, fp32 [K] = s_{i*}.
+ * flags  in/out: NONFINITE_W, X_F16_RANGE, NONFINITE_LOSS.
+ * ws     device workspace of at least awq_search_workspace_bytes(M, N, K, xdt, cfg) bytes
+ *        (dominated by the n_grid * N * K fp16 error stack).
+ * Errors: as for awq_act_stats, plus AWQ_ERR_CONFIG for an invalid cfg.
+ * ---------------------------------------------------------------------------------------- */
+size_t awq_search_workspace_bytes(int64_t M, int64_t N, int64_t K, awq_dtype xdt,
+                                  const awq_cfg* cfg);
+awq_status awq_search_layer(const void* W, awq_dtype wdt, int64_t N, int64_t K,
+                            const void* X, awq_dtype xdt, int64_t M, const float* sx,
+                            const awq_cfg* cfg, double* losses, int32_t* best, float* s_best,
+                            uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * awq_search_layer_profiled -- awq_search_layer plus the duration of each of its kernels,
+ * measured with HIP events recorded between the launches on `stream`. Unlike every other call
+ * it BLOCKS the host until the stream has finished the search (it reads the events back).
+ * stage_ms  host array of AWQ_SEARCH_STAGES floats (milliseconds), in the order
+ *           scale table, max|W|, X to fp16 (0 when X is fp16), quantize + error stack,
+ *           loss contraction, finalize.
+ * Errors: as awq_search_layer; AWQ_ERR_NULL when stage_ms is NULL; AWQ_ERR_HIP when an event
+ *         call fails.
+ * ---------------------------------------------------------------------------------------- */
+#define AWQ_SEARCH_STAGES 6
+awq_status awq_search_layer_profiled(const void* W, awq_dtype wdt, int64_t N, int64_t K,
+                                     const void* X, awq_dtype xdt, int64_t M, const float* sx,
+                                     const awq_cfg* cfg, double* losses, int32_t* best,
+                                     float* s_best, uint32_t* flags, void* ws, size_t ws_bytes,
+                                     hipStream_t stream, float* stage_ms);
+
+/* ------------------------------------------------------------------------------------------
+ * awq_pack_int4 -- the stored result of [eng] 三 (QuantLinear(q_weight, scales_per_group,
+ * awq_scale)).
+ * W        [N, K], dtype wdt (AWQ_F16 or AWQ_F32); s fp32 [K] (typically s_best).
+ * qweight  out, uint32 [N, K/8]: qweight[n,j] = sum_t (q[n,8j+t] & 0xF) << 4t, the codes of
+ *          the same quantization as awq_search_layer (bit-identical).
+ * scales16 out, fp16 bits [N, K/group]: fp16(Delta), round to nearest even.
+ * s16      out, fp16 bits [K]: fp16(s).
+ * codes    out, int8 [N, K] or NULL (not written).
+ * flags    in/out: NONFINITE_W, SCALE16_OVERFLOW, SCALE16_SUBNORMAL, STEP_UNDERFLOW.
+ * Errors: AWQ_ERR_NULL, AWQ_ERR_SHAPE, AWQ_ERR_DTYPE, AWQ_ERR_CONFIG.
+ * ---------------------------------------------------------------------------------------- */
+awq_status awq_pack_int4(const void* W, awq_dtype wdt, int64_t N, int64_t K, const float* s,
+                         const awq_cfg* cfg, uint32_t* qweight, uint16_t* scales16,
+                         uint16_t* s16, int8_t* codes, uint32_t* flags, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * w4a16_gemm -- QuantLinear.forward of [eng] 三 on the packed artefacts:
+ *   Y[m,n] = sum_k (A[m,k] / s16[k]) * sext4(q[n,k]) * scales16[n, k/group]
+ * A        fp16 bits [M, K]; qweight uint32 [N, K/8]; scales16 fp16 bits [N, K/group];
+ *          s16 fp16 bits [K]; Y out, fp16 bits [M, N]. group must be 128; K % 128 == 0.
+ * Products are formed on fp16 operands (activation / s and code * step each rounded once to
+ * fp16) with fp32 accumulation; Y is rounded once to fp16 (relative error ~1e-3 or better).
+ * Errors: AWQ_ERR_NULL, AWQ_ERR_SHAPE (M < 1, N < 1, K % 128), AWQ_ERR_CONFIG (group).
+ * ---------------------------------------------------------------------------------------- */
+awq_status w4a16_gemm(const uint16_t* A, int64_t M, int64_t N, int64_t K, int32_t group,
+                      const uint32_t* qweight, const uint16_t* scales16, const uint16_t* s16,
+                      uint16_t* Y, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_H_ */

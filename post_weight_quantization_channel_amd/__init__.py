@@ -1,0 +1,12 @@
+"""AWQ search, INT4 pack and W4A16 on AMD MI355X (gfx950).
+
+The engine is the HIP library libawq.so (C ABI in include/awq.h); this package holds its sources
+(csrc/), the in-tree build (build.py) and a thin torch binding (api.py) with the same call names.
+"""
+from .api import (AwqConfig, PackResult, SearchResult, act_stats, act_stats_workspace_bytes,
+                  pack_int4, search_layer, search_workspace_bytes, w4a16_gemm)
+from ._lib import AwqError
+
+__all__ = ["AwqConfig", "AwqError", "PackResult", "SearchResult", "act_stats",
+           "act_stats_workspace_bytes", "pack_int4", "search_layer", "search_workspace_bytes",
+           "w4a16_gemm"]

@@ -1,0 +1,86 @@
+"""ctypes loader of libawq.so and the C declarations of include/awq.h.
+
+The library is built in-tree by post_weight_quantization_channel_amd.build. There is no fallback
+path: if the library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libawq.so")
+
+AWQ_OK, AWQ_ERR_NULL, AWQ_ERR_SHAPE, AWQ_ERR_DTYPE, AWQ_ERR_CONFIG, AWQ_ERR_WORKSPACE, \
+    AWQ_ERR_HIP = range(7)
+AWQ_F32, AWQ_F16, AWQ_BF16 = 0, 1, 2
+
+SEARCH_STAGES = ("scale_table", "absmax_w", "x_to_f16", "quantize_stack", "lossgemm",
+                 "finalize")
+
+FLAG_NONFINITE_X = 1 << 0
+FLAG_NONFINITE_W = 1 << 1
+FLAG_STATS_INEXACT = 1 << 2
+FLAG_X_F16_RANGE = 1 << 3
+FLAG_SCALE16_OVERFLOW = 1 << 4
+FLAG_SCALE16_SUBNORMAL = 1 << 5
+FLAG_NONFINITE_LOSS = 1 << 6
+FLAG_STEP_UNDERFLOW = 1 << 7
+
+
+class AwqCfg(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("n_grid", ctypes.c_int32), ("s_floor", ctypes.c_float)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_E = ctypes.c_int
+
+SIGNATURES = {
+    "awq_status_string": (ctypes.c_char_p, [_E]),
+    "awq_version": (_I32, []),
+    "awq_act_stats_workspace_bytes": (_SZ, [_I64, _I64]),
+    "awq_act_stats": (_E, [_P, _E, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "awq_search_workspace_bytes": (_SZ, [_I64, _I64, _I64, _E, ctypes.POINTER(AwqCfg)]),
+    "awq_search_layer": (_E, [_P, _E, _I64, _I64, _P, _E, _I64, _P, ctypes.POINTER(AwqCfg),
+                              _P, _P, _P, _P, _P, _SZ, _P]),
+    "awq_search_layer_profiled": (_E, [_P, _E, _I64, _I64, _P, _E, _I64, _P,
+                                       ctypes.POINTER(AwqCfg), _P, _P, _P, _P, _P, _SZ, _P,
+                                       ctypes.POINTER(ctypes.c_float)]),
+    "awq_pack_int4": (_E, [_P, _E, _I64, _I64, _P, ctypes.POINTER(AwqCfg), _P, _P, _P, _P, _P,
+                           _P]),
+    "w4a16_gemm": (_E, [_P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P]),
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libawq.so once and attach the C signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m post_weight_quantization_channel_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+class AwqError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        msg = load().awq_status_string(status).decode()
+        super().__init__(f"{call}: {msg}")
+        self.status = status
+
+
+def check(call: str, status: int) -> None:
+    if status != AWQ_OK:
+        raise AwqError(call, status)

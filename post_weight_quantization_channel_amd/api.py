@@ -1,0 +1,174 @@
+"""Python face of libawq: the four C-ABI calls on torch tensors.
+
+Argument marshalling only -- torch supplies device memory and the current HIP stream; every step
+of the computation runs in the library's HIP kernels. Names follow the C ABI (include/awq.h).
+Nothing here synchronises: results are ready when the current stream reaches them.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+
+import torch
+
+from . import _lib
+from ._lib import AwqCfg, check
+
+_DT = {torch.float32: _lib.AWQ_F32, torch.float16: _lib.AWQ_F16, torch.bfloat16: _lib.AWQ_BF16}
+
+
+@dataclasses.dataclass(frozen=True)
+class AwqConfig:
+    """bits in {3, 4}; group = 128 input channels per step; n_grid alpha points i/(n_grid-1);
+    s = max(s_X, s_floor)^alpha."""
+    bits: int = 4
+    group: int = 128
+    n_grid: int = 20
+    s_floor: float = 1e-5
+
+    def c(self) -> AwqCfg:
+        return AwqCfg(self.bits, self.group, self.n_grid, self.s_floor)
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _flags(device, flags):
+    if flags is None:
+        return torch.zeros(1, dtype=torch.int32, device=device)
+    return flags
+
+
+@dataclasses.dataclass
+class SearchResult:
+    losses: torch.Tensor   # fp64 [n_grid]
+    best: torch.Tensor     # int32 [1]
+    s_best: torch.Tensor   # fp32 [K]
+    flags: torch.Tensor    # int32 [1] holding the uint32 flag bits
+
+
+@dataclasses.dataclass
+class PackResult:
+    qweight: torch.Tensor   # int32 [N, K/8] holding the uint32 words
+    scales16: torch.Tensor  # fp16 [N, K/group]
+    s16: torch.Tensor       # fp16 [K]
+    codes: torch.Tensor | None
+    flags: torch.Tensor
+
+
+def act_stats_workspace_bytes(M: int, K: int) -> int:
+    return int(_lib.load().awq_act_stats_workspace_bytes(M, K))
+
+
+def search_workspace_bytes(M: int, N: int, K: int, x_dtype: torch.dtype, cfg: AwqConfig) -> int:
+    c = cfg.c()
+    return int(_lib.load().awq_search_workspace_bytes(M, N, K, _DT[x_dtype], c))
+
+
+def act_stats(X: torch.Tensor, flags: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """s_X = mean over tokens of |X| per input channel (fp32 [K]). X may be a row-strided view
+    (unit column stride, row stride a multiple of 8 elements)."""
+    lib = _lib.load()
+    if not X.is_cuda or X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be a 2-D device tensor with unit column stride")
+    M, K = X.shape
+    ldx = X.stride(0) if M > 1 else K
+    flags = _flags(X.device, flags)
+    nbytes = lib.awq_act_stats_workspace_bytes(M, K)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=X.device)
+    sx = torch.empty(K, dtype=torch.float32, device=X.device)
+    check("awq_act_stats", lib.awq_act_stats(X.data_ptr(), _DT[X.dtype], M, K, ldx, sx.data_ptr(),
+                                             flags.data_ptr(), workspace.data_ptr(),
+                                             workspace.numel(), _stream(X)))
+    return sx, flags
+
+
+def search_layer(W: torch.Tensor, X: torch.Tensor, sx: torch.Tensor,
+                 cfg: AwqConfig = AwqConfig(), flags: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None,
+                 stage_ms: dict | None = None) -> SearchResult:
+    """Grid search over alpha: losses L_i, best index, s_best = s_{i*}.
+
+    With a dict as `stage_ms` the profiled C call is used: it fills the dict with the duration
+    of each kernel of the search (HIP events on the current stream) and blocks until done."""
+    lib = _lib.load()
+    for t, nm in ((W, "W"), (X, "X"), (sx, "sx")):
+        _dev(t, nm)
+    N, K = W.shape
+    M = X.shape[0]
+    if X.shape[1] != K or sx.shape != (K,) or sx.dtype != torch.float32:
+        raise ValueError("shape mismatch: W [N,K], X [M,K], sx fp32 [K]")
+    c = cfg.c()
+    flags = _flags(W.device, flags)
+    nbytes = lib.awq_search_workspace_bytes(M, N, K, _DT[X.dtype], c)
+    if nbytes == 0:
+        raise ValueError("invalid shape or config for the search")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    losses = torch.empty(cfg.n_grid, dtype=torch.float64, device=W.device)
+    best = torch.empty(1, dtype=torch.int32, device=W.device)
+    s_best = torch.empty(K, dtype=torch.float32, device=W.device)
+    args = (W.data_ptr(), _DT[W.dtype], N, K, X.data_ptr(), _DT[X.dtype], M, sx.data_ptr(), c,
+            losses.data_ptr(), best.data_ptr(), s_best.data_ptr(), flags.data_ptr(),
+            workspace.data_ptr(), workspace.numel(), _stream(W))
+    if stage_ms is None:
+        check("awq_search_layer", lib.awq_search_layer(*args))
+    else:
+        ms = (ctypes.c_float * len(_lib.SEARCH_STAGES))()
+        check("awq_search_layer_profiled", lib.awq_search_layer_profiled(*args, ms))
+        stage_ms.update({k: float(v) for k, v in zip(_lib.SEARCH_STAGES, ms)})
+    return SearchResult(losses, best, s_best, flags)
+
+
+def pack_int4(W: torch.Tensor, s: torch.Tensor, cfg: AwqConfig = AwqConfig(),
+              with_codes: bool = False, flags: torch.Tensor | None = None) -> PackResult:
+    """Packed codes of Q(W s), fp16 group steps and fp16 s."""
+    lib = _lib.load()
+    _dev(W, "W")
+    _dev(s, "s")
+    N, K = W.shape
+    if s.shape != (K,) or s.dtype != torch.float32:
+        raise ValueError("s must be fp32 [K]")
+    c = cfg.c()
+    flags = _flags(W.device, flags)
+    qweight = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
+    scales16 = torch.empty((N, K // cfg.group), dtype=torch.float16, device=W.device)
+    s16 = torch.empty(K, dtype=torch.float16, device=W.device)
+    codes = torch.empty((N, K), dtype=torch.int8, device=W.device) if with_codes else None
+    check("awq_pack_int4", lib.awq_pack_int4(
+        W.data_ptr(), _DT[W.dtype], N, K, s.data_ptr(), c, qweight.data_ptr(),
+        scales16.data_ptr(), s16.data_ptr(), codes.data_ptr() if codes is not None else None,
+        flags.data_ptr(), _stream(W)))
+    return PackResult(qweight, scales16, s16, codes, flags)
+
+
+def w4a16_gemm(A: torch.Tensor, qweight: torch.Tensor, scales16: torch.Tensor,
+               s16: torch.Tensor, group: int = 128, out: torch.Tensor | None = None
+               ) -> torch.Tensor:
+    """Y = (A / s) (q * step)^T, fp16 [M, N]."""
+    lib = _lib.load()
+    for t, nm in ((A, "A"), (qweight, "qweight"), (scales16, "scales16"), (s16, "s16")):
+        _dev(t, nm)
+    M, K = A.shape
+    N = qweight.shape[0]
+    if A.dtype != torch.float16 or scales16.dtype != torch.float16 or s16.dtype != torch.float16:
+        raise ValueError("A, scales16 and s16 must be fp16")
+    if qweight.shape != (N, K // 8) or scales16.shape != (N, K // group) or s16.shape != (K,):
+        raise ValueError("packed artefact shapes do not match A")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    check("w4a16_gemm", lib.w4a16_gemm(A.data_ptr(), M, N, K, group, qweight.data_ptr(),
+                                       scales16.data_ptr(), s16.data_ptr(), out.data_ptr(),
+                                       _stream(A)))
+    return out

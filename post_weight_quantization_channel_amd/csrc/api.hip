@@ -1,0 +1,215 @@
+// extern "C" entry points of libawq (declared in include/awq.h): argument validation, workspace
+// layout and the launch sequence of each call. Nothing here allocates, frees or synchronises;
+// every host-checkable error returns before the first HIP call.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/awq.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(awq_dtype d) { return d == AWQ_F32 || d == AWQ_F16 || d == AWQ_BF16; }
+
+awq_status check_cfg(const awq_cfg* cfg) {
+  if (!cfg) return AWQ_ERR_NULL;
+  if (cfg->bits != 3 && cfg->bits != 4) return AWQ_ERR_CONFIG;
+  if (cfg->group != 128) return AWQ_ERR_CONFIG;
+  if (cfg->n_grid < 2 || cfg->n_grid > 64) return AWQ_ERR_CONFIG;
+  if (!(cfg->s_floor > 0.0f) || !isfinite(cfg->s_floor)) return AWQ_ERR_CONFIG;
+  return AWQ_OK;
+}
+
+// Largest accepted extent of one dimension; keeps every element index and tile index in range.
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+
+struct SearchLayout {
+  size_t ctrl, S, X16, E, partials, total;
+  int64_t tiles_per_alpha;
+};
+
+SearchLayout search_layout(int64_t M, int64_t N, int64_t K, awq_dtype xdt, int n_grid) {
+  SearchLayout L{};
+  const int64_t tilesM = (M + awq::kLossBM - 1) / awq::kLossBM;
+  const int64_t tilesN = (N + awq::kLossBN - 1) / awq::kLossBN;
+  L.tiles_per_alpha = tilesM * tilesN;
+  size_t off = 0;
+  L.ctrl = off;
+  off += align_up(sizeof(awq::SearchCtrl));
+  L.S = off;
+  off += align_up((size_t)n_grid * (size_t)K * sizeof(float));
+  L.X16 = off;
+  if (xdt != AWQ_F16) off += align_up((size_t)M * (size_t)K * 2);
+  L.E = off;
+  off += align_up((size_t)n_grid * (size_t)N * (size_t)K * 2);
+  L.partials = off;
+  off += align_up((size_t)n_grid * (size_t)L.tiles_per_alpha * sizeof(double));
+  L.total = off;
+  return L;
+}
+
+awq_status hip_status(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* awq_status_string(awq_status status) {
+  switch (status) {
+    case AWQ_OK: return "AWQ_OK";
+    case AWQ_ERR_NULL: return "AWQ_ERR_NULL: a required pointer is NULL";
+    case AWQ_ERR_SHAPE: return "AWQ_ERR_SHAPE: shape, stride or alignment not accepted";
+    case AWQ_ERR_DTYPE: return "AWQ_ERR_DTYPE: dtype not accepted by this call";
+    case AWQ_ERR_CONFIG: return "AWQ_ERR_CONFIG: invalid awq_cfg or group";
+    case AWQ_ERR_WORKSPACE: return "AWQ_ERR_WORKSPACE: workspace missing or too small";
+    case AWQ_ERR_HIP: return "AWQ_ERR_HIP: kernel launch failed";
+  }
+  return "unknown awq_status";
+}
+
+int32_t awq_version(void) { return 10000; }
+
+size_t awq_act_stats_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 1 || K < 1 || M > kMaxDim || K > kMaxDim) return 0;
+  return align_up((size_t)awq::stats_chunks(M) * (size_t)K * sizeof(double));
+}
+
+awq_status awq_act_stats(const void* X, awq_dtype xdt, int64_t M, int64_t K, int64_t ldx,
+                         float* sx, uint32_t* flags, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  if (!X || !sx || !flags) return AWQ_ERR_NULL;
+  if (!valid_dtype(xdt)) return AWQ_ERR_DTYPE;
+  if (M < 1 || K < 8 || K % 8 || ldx < K || ldx % 8 || M > kMaxDim || K > kMaxDim ||
+      ldx > kMaxDim || !aligned16(X) || awq::stats_chunks(M) > 65535)
+    return AWQ_ERR_SHAPE;
+  if (!ws || ws_bytes < awq_act_stats_workspace_bytes(M, K)) return AWQ_ERR_WORKSPACE;
+  return hip_status(awq::launch_stats(X, (int)xdt, M, K, ldx, sx, flags,
+                                      static_cast<double*>(ws), stream));
+}
+
+size_t awq_search_workspace_bytes(int64_t M, int64_t N, int64_t K, awq_dtype xdt,
+                                  const awq_cfg* cfg) {
+  if (check_cfg(cfg) != AWQ_OK || !valid_dtype(xdt)) return 0;
+  if (M < 1 || N < 1 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+  return search_layout(M, N, K, xdt, cfg->n_grid).total;
+}
+
+namespace {
+
+// Shared body of awq_search_layer and awq_search_layer_profiled. With `ev` non-null, event
+// ev[j] is recorded before stage j and ev[AWQ_SEARCH_STAGES] after the last stage.
+awq_status search_impl(const void* W, awq_dtype wdt, int64_t N, int64_t K, const void* X,
+                       awq_dtype xdt, int64_t M, const float* sx, const awq_cfg* cfg,
+                       double* losses, int32_t* best, float* s_best, uint32_t* flags, void* ws,
+                       size_t ws_bytes, hipStream_t stream, hipEvent_t* ev) {
+  if (!W || !X || !sx || !cfg || !losses || !best || !s_best || !flags) return AWQ_ERR_NULL;
+  const awq_status cs = check_cfg(cfg);
+  if (cs != AWQ_OK) return cs;
+  if (wdt != AWQ_F16 && wdt != AWQ_F32) return AWQ_ERR_DTYPE;
+  if (!valid_dtype(xdt)) return AWQ_ERR_DTYPE;
+  if (M < 1 || N < 1 || K < cfg->group || K % cfg->group || M > kMaxDim || N > kMaxDim ||
+      K > kMaxDim || !aligned16(W) || !aligned16(X))
+    return AWQ_ERR_SHAPE;
+  const SearchLayout L = search_layout(M, N, K, xdt, cfg->n_grid);
+  if ((int64_t)L.tiles_per_alpha * cfg->n_grid > (int64_t(1) << 31) - 1) return AWQ_ERR_SHAPE;
+  if (!ws || ws_bytes < L.total || !aligned16(ws)) return AWQ_ERR_WORKSPACE;
+
+  char* base = static_cast<char*>(ws);
+  auto* ctrl = reinterpret_cast<awq::SearchCtrl*>(base + L.ctrl);
+  auto* S = reinterpret_cast<float*>(base + L.S);
+  auto* E = reinterpret_cast<uint16_t*>(base + L.E);
+  auto* partials = reinterpret_cast<double*>(base + L.partials);
+  const uint16_t* X16 = static_cast<const uint16_t*>(X);
+
+  hipError_t e = hipSuccess;
+  auto mark = [&](int j) {
+    if (ev && e == hipSuccess) e = hipEventRecord(ev[j], stream);
+  };
+  mark(0);
+  if (e == hipSuccess)
+    e = awq::launch_search_prep(sx, (int)K, cfg->n_grid, cfg->s_floor, S, ctrl, stream);
+  mark(1);
+  if (e == hipSuccess) e = awq::launch_absmax(W, (int)wdt, N * K, ctrl, flags, stream);
+  mark(2);
+  if (e == hipSuccess && xdt != AWQ_F16) {
+    auto* x16 = reinterpret_cast<uint16_t*>(base + L.X16);
+    e = awq::launch_x_to_f16(X, (int)xdt, M * K, x16, flags, stream);
+    X16 = x16;
+  }
+  mark(3);
+  if (e == hipSuccess)
+    e = awq::launch_quantize_stack(W, (int)wdt, N, K, S, cfg->n_grid, cfg->bits, ctrl, E, flags,
+                                   stream);
+  mark(4);
+  if (e == hipSuccess) e = awq::launch_lossgemm(X16, M, K, E, N, cfg->n_grid, partials, stream);
+  mark(5);
+  if (e == hipSuccess)
+    e = awq::launch_finalize(partials, L.tiles_per_alpha, cfg->n_grid, M, N, K, S, ctrl, losses,
+                             best, s_best, flags, stream);
+  mark(6);
+  return hip_status(e);
+}
+
+}  // namespace
+
+awq_status awq_search_layer(const void* W, awq_dtype wdt, int64_t N, int64_t K,
+                            const void* X, awq_dtype xdt, int64_t M, const float* sx,
+                            const awq_cfg* cfg, double* losses, int32_t* best, float* s_best,
+                            uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return search_impl(W, wdt, N, K, X, xdt, M, sx, cfg, losses, best, s_best, flags, ws, ws_bytes,
+                     stream, nullptr);
+}
+
+awq_status awq_search_layer_profiled(const void* W, awq_dtype wdt, int64_t N, int64_t K,
+                                     const void* X, awq_dtype xdt, int64_t M, const float* sx,
+                                     const awq_cfg* cfg, double* losses, int32_t* best,
+                                     float* s_best, uint32_t* flags, void* ws, size_t ws_bytes,
+                                     hipStream_t stream, float* stage_ms) {
+  if (!stage_ms) return AWQ_ERR_NULL;
+  hipEvent_t ev[AWQ_SEARCH_STAGES + 1] = {};
+  int made = 0;
+  for (; made <= AWQ_SEARCH_STAGES; ++made)
+    if (hipEventCreate(&ev[made]) != hipSuccess) break;
+  awq_status st = AWQ_ERR_HIP;
+  if (made == AWQ_SEARCH_STAGES + 1) {
+    st = search_impl(W, wdt, N, K, X, xdt, M, sx, cfg, losses, best, s_best, flags, ws,
+                     ws_bytes, stream, ev);
+    if (st == AWQ_OK && hipEventSynchronize(ev[AWQ_SEARCH_STAGES]) != hipSuccess) st = AWQ_ERR_HIP;
+    for (int j = 0; st == AWQ_OK && j < AWQ_SEARCH_STAGES; ++j)
+      if (hipEventElapsedTime(&stage_ms[j], ev[j], ev[j + 1]) != hipSuccess) st = AWQ_ERR_HIP;
+  }
+  for (int j = 0; j < made; ++j) (void)hipEventDestroy(ev[j]);
+  return st;
+}
+
+awq_status awq_pack_int4(const void* W, awq_dtype wdt, int64_t N, int64_t K, const float* s,
+                         const awq_cfg* cfg, uint32_t* qweight, uint16_t* scales16,
+                         uint16_t* s16, int8_t* codes, uint32_t* flags, hipStream_t stream) {
+  if (!W || !s || !cfg || !qweight || !scales16 || !s16 || !flags) return AWQ_ERR_NULL;
+  const awq_status cs = check_cfg(cfg);
+  if (cs != AWQ_OK) return cs;
+  if (wdt != AWQ_F16 && wdt != AWQ_F32) return AWQ_ERR_DTYPE;
+  if (N < 1 || K < cfg->group || K % cfg->group || N > kMaxDim || K > kMaxDim ||
+      !aligned16(W) || !aligned16(s) || !aligned16(s16) ||
+      (codes && (reinterpret_cast<uintptr_t>(codes) & 7u)))
+    return AWQ_ERR_SHAPE;
+  return hip_status(awq::launch_pack(W, (int)wdt, N, K, s, cfg->bits, qweight, scales16, s16,
+                                     codes, flags, stream));
+}
+
+awq_status w4a16_gemm(const uint16_t* A, int64_t M, int64_t N, int64_t K, int32_t group,
+                      const uint32_t* qweight, const uint16_t* scales16, const uint16_t* s16,
+                      uint16_t* Y, hipStream_t stream) {
+  if (!A || !qweight || !scales16 || !s16 || !Y) return AWQ_ERR_NULL;
+  if (group != 128) return AWQ_ERR_CONFIG;
+  if (M < 1 || N < 1 || K < 128 || K % 128 || M > kMaxDim || N > kMaxDim || K > kMaxDim ||
+      !aligned16(A) || !aligned16(qweight) || !aligned16(s16))
+    return AWQ_ERR_SHAPE;
+  return hip_status(awq::launch_w4a16(A, M, N, K, qweight, scales16, s16, Y, stream));
+}
+
+}  // extern "C"

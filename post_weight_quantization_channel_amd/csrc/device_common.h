@@ -1,0 +1,139 @@
+// Device helpers shared by the AWQ kernels (gfx950, wave64).
+//
+// The integer-deciding arithmetic (scaled weight, group step, rounded quotient) follows the
+// quantizer of the AWQ notes (bg51717.github.io/14592, section 方法: Q(w) = Delta*Round(w/Delta))
+// with the step denominator and clamp of "AWQ 量化方案：激活感知的权重量化与工程实现全解析"
+// (qwbw.cn/news/39982, section 三, awq_quantize): Delta = max|w s| / (2^(b-1)-1), codes clamped to
+// [-2^(b-1), 2^(b-1)-1], torch.round semantics (half to even). Every step is one IEEE fp32
+// operation with round-to-nearest-even; the library is built with -ffp-contract=off so no step is
+// fused, and fp32 division is the correctly rounded sequence.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace awq {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+enum : uint32_t {
+  kFlagNonfiniteX = 1u << 0,
+  kFlagNonfiniteW = 1u << 1,
+  kFlagStatsInexact = 1u << 2,
+  kFlagXF16Range = 1u << 3,
+  kFlagScale16Overflow = 1u << 4,
+  kFlagScale16Subnormal = 1u << 5,
+  kFlagNonfiniteLoss = 1u << 6,
+  kFlagStepUnderflow = 1u << 7,
+};
+
+__device__ __forceinline__ float h2f(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+__device__ __forceinline__ uint16_t f2h(float f) {  // round to nearest even
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ float bf2f(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Load 8 consecutive elements starting at p (16-byte aligned for 16-bit types, 32-byte for f32)
+// and widen them to fp32 (exact for every input type).
+template <int DT>
+__device__ __forceinline__ void load8_f32(const void* p, float (&v)[8]) {
+  if constexpr (DT == kF32) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+    float4 a = q[0], b = q[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint16_t lo = (uint16_t)(w[t] & 0xFFFFu), hi = (uint16_t)(w[t] >> 16);
+      if constexpr (DT == kF16) {
+        v[2 * t] = h2f(lo);
+        v[2 * t + 1] = h2f(hi);
+      } else {
+        v[2 * t] = bf2f(lo);
+        v[2 * t + 1] = bf2f(hi);
+      }
+    }
+  }
+}
+
+// DPP row (16-lane) permutations.
+#define AWQ_DPP_QUAD_1032 0xB1   // quad_perm [1,0,3,2]
+#define AWQ_DPP_QUAD_2301 0x4E   // quad_perm [2,3,0,1]
+#define AWQ_DPP_ROW_MIRROR 0x140
+#define AWQ_DPP_ROW_HALF_MIRROR 0x141
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane gets the result.
+// Used for the per-group maximum: one group of 128 input channels = 16 lanes x 8 elements.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<AWQ_DPP_QUAD_1032>(v));
+  v = fmaxf(v, dpp_f32<AWQ_DPP_QUAD_2301>(v));
+  v = fmaxf(v, dpp_f32<AWQ_DPP_ROW_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f32<AWQ_DPP_ROW_MIRROR>(v));
+  return v;
+}
+
+// Quantize 8 scaled weights ws[] held by this lane; the 16 lanes of the lane's DPP row hold the
+// rest of the 128-channel group. On return q[] holds the codes (as exact small floats) and the
+// group step Delta is returned (0 for an all-zero group, or when max/qmax underflows to 0, in
+// which case *underflow is set when the group was not all zero).
+//
+//   Delta = fp32(m / qmax),  q = clamp(rint(fp32(ws / Delta)), qmin, qmax)
+//
+// The quotient is formed as t' = fp32(ws * fp32(1/Delta)) first. For |ws| <= m, |t'| <= ~7 and
+// |t' - fp32(ws/Delta)| <= 1.2e-6, so rint(t') equals the specified rint(fp32(ws/Delta)) unless t'
+// lies within that distance of a half-integer; in that case (probability ~1.5e-5 per element) and
+// whenever Delta is not a normal number, the exact quotient is computed by IEEE division.
+__device__ __forceinline__ float quant8(const float (&ws)[8], float qmin, float qmax,
+                                        float (&q)[8], bool& underflow) {
+  float m = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(ws[t]));
+  m = row16_max(m);
+  const float delta = m / qmax;
+  underflow = (m > 0.0f) && !(delta > 0.0f);
+  if (!(delta > 0.0f)) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) q[t] = 0.0f;
+    return 0.0f;
+  }
+  const float r = 1.0f / delta;
+  const bool exact_only = !(delta >= 0x1p-126f) || !(r < 0x1p+127f);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const float tq = ws[t] * r;
+    float qq = rintf(tq);
+    if (exact_only || fabsf(tq - qq) > 0.5f - 0x1p-17f) qq = rintf(ws[t] / delta);
+    q[t] = fminf(fmaxf(qq, qmin), qmax);
+  }
+  return delta;
+}
+
+__device__ __forceinline__ void flag_or(uint32_t* flags, uint32_t bits) {
+  if (bits) atomicOr(flags, bits);
+}
+
+// OR `bits` into *flags once per wave for the lanes where `cond` holds.
+__device__ __forceinline__ void wave_flag(uint32_t* flags, bool cond, uint32_t bits) {
+  const unsigned long long b = __ballot(cond);
+  if (b != 0ull && __lane_id() == (unsigned)(__ffsll((long long)b) - 1)) atomicOr(flags, bits);
+}
+
+}  // namespace awq

@@ -1,0 +1,261 @@
+// The alpha grid search of the AWQ notes (bg51717.github.io/14592, section 方法):
+//   s = s_X^alpha, alpha in [0, 1];  alpha* = argmin_alpha L(s_X^alpha),
+//   L(s) = || Q(W s)(s^-1 X) - W X ||.
+// This file holds every stage except the loss contraction (lossgemm.hip):
+//   search_prep      s_i[k] = fp32(pow(max(s_X[k], s_floor), i/(n-1))) in fp64, and the reset
+//                    of the control block;
+//   absmax           max |W| (integer atomicMax on the fp32 bit patterns: order-free);
+//   x_to_f16         fp16 copy of an fp32/bf16 X for the fp16 contraction;
+//   quantize_stack   for all alpha at once: Q(W s_i) group-wise (the fp32 specification of
+//                    device_common.h) and the error E_i = Q(W s_i)/s_i - W, stored in fp16 as
+//                    E_i * 2^escale. By linearity X E_i^T = Q(W s_i)(s_i^-1 X) - W X.
+//   finalize         fixed-order fp64 sum of the per-tile partial losses, L_i / (M N),
+//                    argmin with the lowest index on ties, s_best = s_{i*}.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace awq {
+
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void search_prep_kernel(const float* __restrict__ sx, int K,
+                                                          int n_grid, float s_floor,
+                                                          float* __restrict__ S,
+                                                          SearchCtrl* __restrict__ ctrl) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx == 0) {
+    ctrl->absmax_bits = 0u;
+    ctrl->escale = 0;
+  }
+  if (idx >= (int64_t)n_grid * K) return;
+  const int i = (int)(idx / K);
+  const int k = (int)(idx % K);
+  const float b = fmaxf(sx[k], s_floor);          // floor compared in fp32
+  const double alpha = (double)i / (double)(n_grid - 1);
+  S[idx] = (float)pow((double)b, alpha);          // fp64 power, one rounding to fp32
+}
+
+hipError_t launch_search_prep(const float* sx, int K, int n_grid, float s_floor, float* S,
+                              SearchCtrl* ctrl, hipStream_t stream) {
+  const int64_t total = (int64_t)n_grid * K;
+  search_prep_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(sx, K, n_grid, s_floor,
+                                                                           S, ctrl);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(256) void absmax_kernel(const void* __restrict__ W, int64_t count8,
+                                                     SearchCtrl* __restrict__ ctrl,
+                                                     uint32_t* __restrict__ flags) {
+  constexpr int ES = (DT == kF32) ? 4 : 2;
+  float m = 0.0f;
+  bool bad = false;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < count8;
+       c += (int64_t)gridDim.x * 256) {
+    float v[8];
+    load8_f32<DT>(reinterpret_cast<const char*>(W) + c * 8 * ES, v);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      bad |= !isfinite(v[t]);
+      m = fmaxf(m, fabsf(v[t]));
+    }
+  }
+  // wave maximum, then one atomic per wave
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (__lane_id() == 0) atomicMax(&ctrl->absmax_bits, __float_as_uint(m));
+  wave_flag(flags, bad, kFlagNonfiniteW);
+}
+
+hipError_t launch_absmax(const void* W, int dtype, int64_t count, SearchCtrl* ctrl,
+                         uint32_t* flags, hipStream_t stream) {
+  const int64_t count8 = count / 8;
+  int64_t blocks = (count8 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  if (dtype == kF32)
+    absmax_kernel<kF32><<<(unsigned)blocks, 256, 0, stream>>>(W, count8, ctrl, flags);
+  else
+    absmax_kernel<kF16><<<(unsigned)blocks, 256, 0, stream>>>(W, count8, ctrl, flags);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(256) void x_to_f16_kernel(const void* __restrict__ X, int64_t count8,
+                                                       uint16_t* __restrict__ X16,
+                                                       uint32_t* __restrict__ flags) {
+  constexpr int ES = (DT == kF32) ? 4 : 2;
+  bool over = false;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < count8;
+       c += (int64_t)gridDim.x * 256) {
+    float v[8];
+    load8_f32<DT>(reinterpret_cast<const char*>(X) + c * 8 * ES, v);
+    uint32_t w[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint16_t lo = f2h(v[2 * t]), hi = f2h(v[2 * t + 1]);
+      over |= ((lo & 0x7C00u) == 0x7C00u) || ((hi & 0x7C00u) == 0x7C00u);
+      w[t] = (uint32_t)lo | ((uint32_t)hi << 16);
+    }
+    *reinterpret_cast<uint4*>(X16 + c * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  wave_flag(flags, over, kFlagXF16Range);
+}
+
+hipError_t launch_x_to_f16(const void* X, int dtype, int64_t count, uint16_t* X16,
+                           uint32_t* flags, hipStream_t stream) {
+  const int64_t count8 = count / 8;
+  int64_t blocks = (count8 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  if (dtype == kBF16)
+    x_to_f16_kernel<kBF16><<<(unsigned)blocks, 256, 0, stream>>>(X, count8, X16, flags);
+  else
+    x_to_f16_kernel<kF32><<<(unsigned)blocks, 256, 0, stream>>>(X, count8, X16, flags);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// The error stack is stored as E * 2^escale with 2^escale * max|W| in [2^14, 2^15): every |E|
+// is at most ~|w| (a code of 0 gives E = -w; a non-zero code means |w s| >= Delta/2 and the
+// rounding error is at most Delta/2), so the fp16 values stay finite, and small errors keep
+// fp16 normal precision instead of falling into the fp16 subnormal range.
+__device__ __forceinline__ int escale_from_absmax(uint32_t bits) {
+  const float m = __uint_as_float(bits);
+  if (!(m > 0.0f) || !isfinite(m)) return 0;
+  const int e2 = (int)((bits >> 23) & 0xFFu);  // biased exponent; 0 for subnormal
+  const int fl = (e2 == 0) ? -127 : e2 - 127;  // floor(log2 m) (subnormals clamped)
+  int e = 14 - fl;
+  if (e > 100) e = 100;
+  if (e < -100) e = -100;
+  return e;
+}
+
+constexpr int kQuantRows = 4;  // rows per thread in quantize_stack
+
+// Thread layout: one thread owns 8 consecutive input channels (one 16-byte fp16 load) of
+// kQuantRows rows; 16 consecutive lanes cover one 128-channel group (a DPP row), so the group
+// maximum is four DPP steps. The scale row s_i for the thread's 8 channels is loaded once per
+// alpha and reused for all its rows. Stores: 16 bytes per lane, 1 KiB per wave, contiguous.
+template <int DT>
+__global__ __launch_bounds__(256) void quantize_stack_kernel(
+    const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ S, int n_grid,
+    float qmin, float qmax, const SearchCtrl* __restrict__ ctrl, uint16_t* __restrict__ Estack,
+    uint32_t* __restrict__ flags) {
+  constexpr int ES = (DT == kF32) ? 4 : 2;
+  const int64_t chunks = K / 8;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rb = id / chunks;
+  const int64_t c8 = id % chunks;
+  const int64_t row0 = rb * kQuantRows;
+  if (row0 >= N) return;  // whole 16-lane groups share rb: no partial group exits here
+  const int e = escale_from_absmax(ctrl->absmax_bits);
+  const float esc = ldexpf(1.0f, e);
+
+  float w[kQuantRows][8];
+  bool live[kQuantRows];
+#pragma unroll
+  for (int r = 0; r < kQuantRows; ++r) {
+    live[r] = (row0 + r) < N;
+    if (live[r]) {
+      load8_f32<DT>(reinterpret_cast<const char*>(W) + ((row0 + r) * K + c8 * 8) * ES, w[r]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) w[r][t] = 0.0f;
+    }
+  }
+  const size_t stride_alpha = (size_t)N * (size_t)K;
+  for (int i = 0; i < n_grid; ++i) {
+    float s[8], inv[8];
+    load8_f32<kF32>(S + (size_t)i * K + c8 * 8, s);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) inv[t] = __builtin_amdgcn_rcpf(s[t]);
+#pragma unroll
+    for (int r = 0; r < kQuantRows; ++r) {
+      if (!live[r]) continue;  // uniform over the 16-lane group
+      float ws[8], q[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) ws[t] = w[r][t] * s[t];
+      bool uf;
+      const float delta = quant8(ws, qmin, qmax, q, uf);
+      uint32_t packed[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        // E = (q Delta)/s - w, then scaled by the exact power of two and rounded once to fp16
+        const float e0 = (__builtin_fmaf(q[2 * t] * delta, inv[2 * t], -w[r][2 * t])) * esc;
+        const float e1 = (__builtin_fmaf(q[2 * t + 1] * delta, inv[2 * t + 1], -w[r][2 * t + 1])) * esc;
+        packed[t] = (uint32_t)f2h(e0) | ((uint32_t)f2h(e1) << 16);
+      }
+      *reinterpret_cast<uint4*>(Estack + i * stride_alpha + (row0 + r) * K + c8 * 8) =
+          make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    }
+  }
+}
+
+hipError_t launch_quantize_stack(const void* W, int dtype, int64_t N, int64_t K, const float* S,
+                                 int n_grid, int bits, const SearchCtrl* ctrl, uint16_t* Estack,
+                                 uint32_t* flags, hipStream_t stream) {
+  const float qmax = (float)((1 << (bits - 1)) - 1);
+  const float qmin = -(float)(1 << (bits - 1));
+  const int64_t threads = ((N + kQuantRows - 1) / kQuantRows) * (K / 8);
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  if (dtype == kF32)
+    quantize_stack_kernel<kF32><<<blocks, 256, 0, stream>>>(W, N, K, S, n_grid, qmin, qmax, ctrl,
+                                                            Estack, flags);
+  else
+    quantize_stack_kernel<kF16><<<blocks, 256, 0, stream>>>(W, N, K, S, n_grid, qmin, qmax, ctrl,
+                                                            Estack, flags);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void finalize_kernel(
+    const double* __restrict__ partials, int64_t tiles, int n_grid, int64_t M, int64_t N,
+    int64_t K, const float* __restrict__ S, const SearchCtrl* __restrict__ ctrl,
+    double* __restrict__ losses, int32_t* __restrict__ best, float* __restrict__ s_best,
+    uint32_t* __restrict__ flags) {
+  __shared__ double red[256];
+  __shared__ double L[64];
+  __shared__ int sbest;
+  const int tid = threadIdx.x;
+  const int e = escale_from_absmax(ctrl->absmax_bits);
+  const double denom = (double)M * (double)N;
+  for (int i = 0; i < n_grid; ++i) {
+    double acc = 0.0;
+    for (int64_t t = tid; t < tiles; t += 256) acc += partials[(int64_t)i * tiles + t];
+    red[tid] = acc;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+      if (tid < w) red[tid] += red[tid + w];
+      __syncthreads();
+    }
+    if (tid == 0) L[i] = ldexp(red[0], -2 * e) / denom;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    int b = 0;
+    bool bad = false;
+    for (int i = 0; i < n_grid; ++i) {
+      losses[i] = L[i];
+      bad |= !isfinite(L[i]);
+      if (L[i] < L[b]) b = i;
+    }
+    *best = b;
+    sbest = b;
+    if (bad) atomicOr(flags, kFlagNonfiniteLoss);
+  }
+  __syncthreads();
+  const float* src = S + (int64_t)sbest * K;
+  for (int64_t k = tid; k < K; k += 256) s_best[k] = src[k];
+}
+
+hipError_t launch_finalize(const double* partials, int64_t tiles_per_alpha, int n_grid,
+                           int64_t M, int64_t N, int64_t K, const float* S,
+                           const SearchCtrl* ctrl, double* losses, int32_t* best,
+                           float* s_best, uint32_t* flags, hipStream_t stream) {
+  finalize_kernel<<<1, 256, 0, stream>>>(partials, tiles_per_alpha, n_grid, M, N, K, S, ctrl,
+                                         losses, best, s_best, flags);
+  return hipGetLastError();
+}
+
+}  // namespace awq

@@ -1,0 +1,94 @@
+// Activation statistics: s_X[k] = mean_m |X[m,k]|.
+//
+// AWQ notes (bg51717.github.io/14592), section 方法: the scale is a power of s_X, a statistic of
+// the layer input; "AWQ 量化方案..." (qwbw.cn/news/39982), section 三 Step 1: act_norm =
+// calib_data.abs().mean(dim=0).
+//
+// HBM-bound column reduction. Pass 1: each thread owns 8 consecutive columns (one 16-byte load
+// per row for 16-bit inputs) and sums |x| over a chunk of 256 rows in fp64; a 64-lane wave reads
+// 1 KiB of a row contiguously. Pass 2 adds the chunk partials of each column in ascending chunk
+// order and divides by M in fp64 before the single rounding to fp32. For fp16 inputs every
+// partial sum is exact (all |x| are multiples of 2^-24 and the sums stay below 2^29, which is
+// checked), so the result does not depend on the reduction order at all.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace awq {
+
+template <int DT>
+__global__ __launch_bounds__(256) void stats_partial_kernel(const void* __restrict__ X, int64_t M,
+                                                            int64_t K, int64_t ldx,
+                                                            double* __restrict__ partials) {
+  const int64_t c8 = (int64_t)blockIdx.x * 256 + threadIdx.x;  // column chunk of 8
+  if (c8 * 8 >= K) return;
+  const int64_t chunk = blockIdx.y;
+  const int64_t r0 = chunk * kStatsRowsPerChunk;
+  const int64_t r1 = (r0 + kStatsRowsPerChunk < M) ? r0 + kStatsRowsPerChunk : M;
+  constexpr int ES = (DT == kF32) ? 4 : 2;
+  const char* base = reinterpret_cast<const char*>(X) + (c8 * 8) * ES;
+  double acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = 0.0;
+  int64_t r = r0;
+  for (; r + 4 <= r1; r += 4) {
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8_f32<DT>(base + (r + u) * ldx * ES, v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] += (double)fabsf(v[u][t]);
+  }
+  for (; r < r1; ++r) {
+    float v[8];
+    load8_f32<DT>(base + r * ldx * ES, v);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] += (double)fabsf(v[t]);
+  }
+  double* out = partials + chunk * K + c8 * 8;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) out[t] = acc[t];
+}
+
+__global__ __launch_bounds__(256) void stats_final_kernel(const double* __restrict__ partials,
+                                                          int64_t chunks, int64_t M, int64_t K,
+                                                          int dtype, float* __restrict__ sx,
+                                                          uint32_t* __restrict__ flags) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  bool bad = false, inexact = false;
+  if (k < K) {
+    double S = 0.0;
+    for (int64_t c = 0; c < chunks; ++c) S += partials[c * K + k];
+    bad = !isfinite(S);
+    inexact = (dtype == kF16) && (S >= 0x1p29);
+    sx[k] = (float)(S / (double)M);
+  }
+  wave_flag(flags, bad, kFlagNonfiniteX);
+  wave_flag(flags, inexact, kFlagStatsInexact);
+}
+
+int64_t stats_chunks(int64_t M) { return (M + kStatsRowsPerChunk - 1) / kStatsRowsPerChunk; }
+
+hipError_t launch_stats(const void* X, int dtype, int64_t M, int64_t K, int64_t ldx, float* sx,
+                        uint32_t* flags, double* partials, hipStream_t stream) {
+  const int64_t chunks = stats_chunks(M);
+  dim3 grid((unsigned)((K / 8 + 255) / 256), (unsigned)chunks);
+  switch (dtype) {
+    case kF16:
+      stats_partial_kernel<kF16><<<grid, 256, 0, stream>>>(X, M, K, ldx, partials);
+      break;
+    case kBF16:
+      stats_partial_kernel<kBF16><<<grid, 256, 0, stream>>>(X, M, K, ldx, partials);
+      break;
+    default:
+      stats_partial_kernel<kF32><<<grid, 256, 0, stream>>>(X, M, K, ldx, partials);
+      break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  stats_final_kernel<<<(unsigned)((K + 255) / 256), 256, 0, stream>>>(partials, chunks, M, K,
+                                                                       dtype, sx, flags);
+  return hipGetLastError();
+}
+
+}  // namespace awq

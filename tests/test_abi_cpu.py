@@ -1,0 +1,145 @@
+"""The C-ABI library loads, exports every call include/awq.h declares, and rejects bad arguments
+with the documented status before any HIP call (these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq.h")
+
+from post_weight_quantization_channel_amd import _lib  # noqa: E402
+from post_weight_quantization_channel_amd._lib import AwqCfg  # noqa: E402
+
+FAKE = 0x10000        # aligned, never dereferenced: every call below fails validation first
+FAKE2 = 0x20000
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    names = re.findall(r"^[A-Za-z_][\w \t\*]*?\b([A-Za-z_]\w*)\s*\([^;{]*\)\s*;", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for n in ("awq_act_stats", "awq_search_layer", "awq_pack_int4", "w4a16_gemm",
+              "awq_search_workspace_bytes", "awq_act_stats_workspace_bytes",
+              "awq_status_string", "awq_version"):
+        assert n in names
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = lib.awq_status_string(code).decode()
+        assert s.startswith("AWQ_")
+    assert lib.awq_version() == 10000
+
+
+def cfg(bits=4, group=128, n_grid=20, s_floor=1e-5):
+    return AwqCfg(bits, group, n_grid, s_floor)
+
+
+def test_workspace_queries(lib):
+    # stats: one fp64 partial per (256-row chunk, column)
+    assert lib.awq_act_stats_workspace_bytes(65536, 4096) == 256 * 4096 * 8
+    assert lib.awq_act_stats_workspace_bytes(0, 4096) == 0
+    ws = lib.awq_search_workspace_bytes(65536, 4096, 4096, _lib.AWQ_F16, cfg())
+    estack = 20 * 4096 * 4096 * 2
+    assert estack < ws < estack + 4 * 2**20
+    ws32 = lib.awq_search_workspace_bytes(256, 512, 512, _lib.AWQ_F32, cfg())
+    assert ws32 >= 256 * 512 * 2 + 20 * 512 * 512 * 2
+    assert lib.awq_search_workspace_bytes(256, 512, 512, _lib.AWQ_F16, cfg(bits=5)) == 0
+    assert lib.awq_search_workspace_bytes(256, 512, 512, _lib.AWQ_F16, cfg(n_grid=1)) == 0
+
+
+def test_act_stats_rejects(lib):
+    f = lib.awq_act_stats
+    assert f(None, 1, 4, 8, 8, FAKE, FAKE, FAKE, 1 << 20, None) == _lib.AWQ_ERR_NULL
+    assert f(FAKE, 7, 4, 8, 8, FAKE, FAKE, FAKE, 1 << 20, None) == _lib.AWQ_ERR_DTYPE
+    assert f(FAKE, 1, 0, 8, 8, FAKE, FAKE, FAKE, 1 << 20, None) == _lib.AWQ_ERR_SHAPE
+    assert f(FAKE, 1, 4, 12, 12, FAKE, FAKE, FAKE, 1 << 20, None) == _lib.AWQ_ERR_SHAPE
+    assert f(FAKE, 1, 4, 8, 4, FAKE, FAKE, FAKE, 1 << 20, None) == _lib.AWQ_ERR_SHAPE
+    assert f(FAKE + 2, 1, 4, 8, 8, FAKE, FAKE, FAKE, 1 << 20, None) == _lib.AWQ_ERR_SHAPE
+    assert f(FAKE, 1, 4, 8, 8, FAKE, FAKE, FAKE, 8, None) == _lib.AWQ_ERR_WORKSPACE
+    assert f(FAKE, 1, 4, 8, 8, FAKE, FAKE, None, 1 << 20, None) == _lib.AWQ_ERR_WORKSPACE
+
+
+def _search(lib, **kw):
+    a = dict(W=FAKE, wdt=1, N=256, K=512, X=FAKE2, xdt=1, M=300, sx=FAKE, cfg=cfg(),
+             losses=FAKE, best=FAKE, s_best=FAKE, flags=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    c = a["cfg"]
+    return lib.awq_search_layer(a["W"], a["wdt"], a["N"], a["K"], a["X"], a["xdt"], a["M"],
+                                a["sx"], ctypes.byref(c) if c is not None else None,
+                                a["losses"], a["best"], a["s_best"], a["flags"], a["ws"],
+                                a["ws_bytes"], None)
+
+
+def test_search_rejects(lib):
+    E = _lib
+    for k in ("W", "X", "sx", "losses", "best", "s_best", "flags"):
+        assert _search(lib, **{k: None}) == E.AWQ_ERR_NULL, k
+    assert _search(lib, cfg=None) == E.AWQ_ERR_NULL
+    assert _search(lib, cfg=cfg(bits=2)) == E.AWQ_ERR_CONFIG
+    assert _search(lib, cfg=cfg(group=64)) == E.AWQ_ERR_CONFIG
+    assert _search(lib, cfg=cfg(n_grid=1)) == E.AWQ_ERR_CONFIG
+    assert _search(lib, cfg=cfg(n_grid=65)) == E.AWQ_ERR_CONFIG
+    assert _search(lib, cfg=cfg(s_floor=0.0)) == E.AWQ_ERR_CONFIG
+    assert _search(lib, cfg=cfg(s_floor=float("nan"))) == E.AWQ_ERR_CONFIG
+    assert _search(lib, wdt=2) == E.AWQ_ERR_DTYPE      # bf16 W is not accepted
+    assert _search(lib, xdt=9) == E.AWQ_ERR_DTYPE
+    assert _search(lib, K=500) == E.AWQ_ERR_SHAPE
+    assert _search(lib, K=64) == E.AWQ_ERR_SHAPE
+    assert _search(lib, M=0) == E.AWQ_ERR_SHAPE
+    assert _search(lib, N=0) == E.AWQ_ERR_SHAPE
+    assert _search(lib, W=FAKE + 4) == E.AWQ_ERR_SHAPE
+    assert _search(lib, ws=None) == E.AWQ_ERR_WORKSPACE
+    need = lib.awq_search_workspace_bytes(300, 256, 512, 1, cfg())
+    assert _search(lib, ws_bytes=need - 1) == E.AWQ_ERR_WORKSPACE
+
+
+def test_pack_rejects(lib):
+    E = _lib
+    c = cfg()
+    f = lib.awq_pack_int4
+    assert f(None, 1, 4, 128, FAKE, c, FAKE, FAKE, FAKE, None, FAKE, None) == E.AWQ_ERR_NULL
+    assert f(FAKE, 1, 4, 128, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, None) == E.AWQ_ERR_NULL
+    assert f(FAKE, 1, 4, 128, FAKE, cfg(bits=8), FAKE, FAKE, FAKE, None, FAKE, None) == \
+        E.AWQ_ERR_CONFIG
+    assert f(FAKE, 2, 4, 128, FAKE, c, FAKE, FAKE, FAKE, None, FAKE, None) == E.AWQ_ERR_DTYPE
+    assert f(FAKE, 1, 4, 130, FAKE, c, FAKE, FAKE, FAKE, None, FAKE, None) == E.AWQ_ERR_SHAPE
+    assert f(FAKE, 1, 0, 128, FAKE, c, FAKE, FAKE, FAKE, None, FAKE, None) == E.AWQ_ERR_SHAPE
+    assert f(FAKE, 1, 4, 128, FAKE, c, FAKE, FAKE, FAKE, FAKE + 3, FAKE, None) == E.AWQ_ERR_SHAPE
+
+
+def test_w4a16_rejects(lib):
+    E = _lib
+    f = lib.w4a16_gemm
+    assert f(None, 1, 16, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == E.AWQ_ERR_NULL
+    assert f(FAKE, 1, 16, 128, 64, FAKE, FAKE, FAKE, FAKE, None) == E.AWQ_ERR_CONFIG
+    assert f(FAKE, 0, 16, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == E.AWQ_ERR_SHAPE
+    assert f(FAKE, 1, 16, 200, 128, FAKE, FAKE, FAKE, FAKE, None) == E.AWQ_ERR_SHAPE
+    assert f(FAKE, 1, 0, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == E.AWQ_ERR_SHAPE
+    assert f(FAKE + 8, 1, 16, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == E.AWQ_ERR_SHAPE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load()

@@ -1,0 +1,384 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded inputs.
+
+Bars (the design doc lists their derivation):
+  * s_X, the scale table, codes, packed words, fp16 steps and fp16 s: bit-exact;
+  * each per-alpha loss: |L_gpu - L_oracle| <= 1e-4 L_oracle;
+  * alpha*: equal whenever the oracle's best-vs-runner-up relative gap exceeds 2e-4, otherwise
+    inside the oracle's tolerance band;
+  * W4A16: ||Y_gpu - Y||_F / ||Y||_F <= 2e-3 (fp64 reference), bit-exact on exact cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+LOSS_RTOL = 1e-4
+W4A16_RTOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def awq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU in this process")
+    import post_weight_quantization_channel_amd as m   # fails loudly if libawq.so is missing
+    from post_weight_quantization_channel_amd import _lib
+    _lib.load()
+    return m
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def say(*a):
+    print("  ", *a, flush=True)
+
+
+# The contraction runs on fp16 error matrices: each E entry carries a relative rounding error of
+# at most 2^-12, so one output's squared error is off by up to ~2 * 2^-12 ~ 5e-4 relative when a
+# few input channels dominate it. Over many weight rows these errors are independent and the
+# loss error shrinks like 1/sqrt(rows) (3-5e-5 at 384 rows, below 1e-4 for every benchmarked
+# layer). Layers with only a handful of rows get the single-output bound instead.
+TINY_ROWS_RTOL = 2e-3
+
+
+def check_alpha(losses_gpu, losses_orc, best_gpu, best_orc, tol=LOSS_RTOL):
+    rel = np.abs(losses_gpu - losses_orc) / losses_orc
+    assert rel.max() <= tol, f"loss rel err {rel.max():.3e} at alpha {rel.argmax()}"
+    gap = oracle.relative_gap(losses_orc)
+    band = 2 * tol
+    if gap > band:
+        assert best_gpu == best_orc, (best_gpu, best_orc, gap)
+    else:
+        lmin = losses_orc.min()
+        assert losses_orc[best_gpu] <= lmin * (1 + band), "alpha* outside the near-tie band"
+    return float(rel.max()), gap
+
+
+# ------------------------------------------------------------------------------------------------
+def _lognormal_layer(seed, n, k, m, xdt=np.float16, wdt=np.float16):
+    L = workloads.c2_like_layer(n=n, k=k, m=m, config=seed)
+    return L.W.astype(wdt), L.X.astype(xdt)
+
+
+STATS_CASES = [
+    ("f16_700x384", lambda: _lognormal_layer(21, 8, 384, 700)[1], torch.float16),
+    ("f16_1x256", lambda: _lognormal_layer(22, 8, 256, 1)[1], torch.float16),
+    ("f16_257x4096", lambda: _lognormal_layer(23, 8, 4096, 257)[1], torch.float16),
+    ("f32_c1", lambda: workloads.c1_layer().X, torch.float32),
+    ("bf16_513x2048", lambda: _lognormal_layer(24, 8, 2048, 513, np.float32)[1], torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("name,make,tdt", STATS_CASES, ids=[c[0] for c in STATS_CASES])
+def test_act_stats_bit_exact(awq, name, make, tdt):
+    X = make()
+    say("act_stats", name, X.shape, tdt)
+    Xt = torch.from_numpy(np.ascontiguousarray(X)).to(tdt).cuda()
+    Xref = Xt.float().cpu().numpy() if tdt == torch.bfloat16 else X
+    sx, flags = awq.act_stats(Xt)
+    assert np.array_equal(host(sx), oracle.act_stats(Xref))
+    assert int(host(flags)[0]) == 0
+
+
+def test_act_stats_row_strided_view(awq):
+    X = _lognormal_layer(25, 8, 512, 300)[1]
+    say("act_stats strided view of", X.shape)
+    Xt = dev(X)[:, :384]
+    sx, _ = awq.act_stats(Xt)
+    assert np.array_equal(host(sx), oracle.act_stats(X[:, :384]))
+
+
+# ------------------------------------------------------------------------------------------------
+SEARCH_CASES = [
+    # name, builder, bits, n_grid
+    ("c1_512x512_m256_f32", lambda: (workloads.c1_layer().W, workloads.c1_layer().X), 4, 20),
+    ("ragged_384x512_m700", lambda: _lognormal_layer(31, 384, 512, 700), 4, 20),
+    ("int3_384x512_m700", lambda: _lognormal_layer(31, 384, 512, 700), 3, 20),
+    ("grid7_320x256_m513_bf16x", lambda: _lognormal_layer(32, 320, 256, 513, np.float32), 4, 7),
+    ("one_row_1x128_m33", lambda: _lognormal_layer(33, 1, 128, 33), 4, 20),
+    ("wide_k_96x1152_m300", lambda: _lognormal_layer(34, 96, 1152, 300), 4, 20),
+]
+
+
+@pytest.mark.parametrize("name,make,bits,n_grid", SEARCH_CASES, ids=[c[0] for c in SEARCH_CASES])
+def test_search_parity(awq, name, make, bits, n_grid):
+    W, X = make()
+    tdt = torch.bfloat16 if "bf16x" in name else None
+    say("search", name, "W", W.shape, W.dtype, "X", X.shape, X.dtype, "bits", bits, "grid", n_grid)
+    Wt = dev(W)
+    Xt = dev(X) if tdt is None else dev(X).to(tdt)
+    Xref = Xt.float().cpu().numpy() if tdt is not None else X
+    cfg = awq.AwqConfig(bits=bits, n_grid=n_grid)
+    sx, flags = awq.act_stats(Xt)
+    res = awq.search_layer(Wt, Xt, sx, cfg, flags=flags)
+    sx_o = oracle.act_stats(Xref)
+    assert np.array_equal(host(sx), sx_o)
+    orc = oracle.search_layer(W, Xref, sx_o, bits=bits, n_grid=n_grid)
+    lg = host(res.losses)
+    bg = int(host(res.best)[0])
+    tol = LOSS_RTOL if W.shape[0] >= 64 else TINY_ROWS_RTOL
+    err, gap = check_alpha(lg, orc["losses"], bg, orc["best"], tol)
+    say(f"max loss rel err {err:.2e}, oracle gap {gap:.2e}, alpha* {bg} / {orc['best']}")
+    assert np.array_equal(host(res.s_best), orc["scales"][bg])
+    assert int(host(res.flags)[0]) == 0
+
+
+def test_search_is_deterministic(awq):
+    W, X = _lognormal_layer(35, 384, 512, 700)
+    say("determinism", W.shape, X.shape)
+    Wt, Xt = dev(W), dev(X)
+    sx, _ = awq.act_stats(Xt)
+    r1 = awq.search_layer(Wt, Xt, sx)
+    r2 = awq.search_layer(Wt, Xt, sx)
+    assert np.array_equal(host(r1.losses).view(np.uint64), host(r2.losses).view(np.uint64))
+    assert np.array_equal(host(r1.s_best), host(r2.s_best))
+
+
+def test_search_zero_rows_and_dead_channels(awq):
+    """All-zero rows (step 0, codes 0, E = 0) and all-zero activation channels (s_floor path)."""
+    W, X = _lognormal_layer(36, 300, 384, 400)
+    W[5] = 0
+    W[17, 128:256] = 0
+    X[:, 3] = 0
+    X[:, 200:210] = 0
+    say("zero rows / dead channels", W.shape, X.shape)
+    Wt, Xt = dev(W), dev(X)
+    sx, _ = awq.act_stats(Xt)
+    res = awq.search_layer(Wt, Xt, sx)
+    orc = oracle.search_layer(W, X, oracle.act_stats(X))
+    check_alpha(host(res.losses), orc["losses"], int(host(res.best)[0]), orc["best"])
+
+
+# ------------------------------------------------------------------------------------------------
+PACK_CASES = [
+    ("c1_f32", lambda: workloads.c1_layer().W, lambda: workloads.c1_layer().X, 4),
+    ("ragged_f16", lambda: _lognormal_layer(41, 300, 640, 600)[0],
+     lambda: _lognormal_layer(41, 300, 640, 600)[1], 4),
+    ("int3_f16", lambda: _lognormal_layer(42, 260, 384, 500)[0],
+     lambda: _lognormal_layer(42, 260, 384, 500)[1], 3),
+]
+
+
+@pytest.mark.parametrize("name,mw,mx,bits", PACK_CASES, ids=[c[0] for c in PACK_CASES])
+def test_pack_bit_exact_every_alpha(awq, name, mw, mx, bits):
+    """Codes of the same quantization at every grid point (the oracle's scale table fed in),
+    packed words, fp16 steps and fp16 s: all bit-exact."""
+    W, X = mw(), mx()
+    say("pack", name, W.shape, W.dtype, "bits", bits)
+    S = oracle.scale_table(oracle.act_stats(X), 20)
+    Wt = dev(W)
+    cfg = awq.AwqConfig(bits=bits)
+    for i in range(20):
+        p = awq.pack_int4(Wt, dev(S[i]), cfg, with_codes=True)
+        o = oracle.pack_layer(W, S[i], bits=bits)
+        assert np.array_equal(host(p.codes), o["codes"]), i
+        assert np.array_equal(host(p.qweight).view(np.uint32), o["qweight"]), i
+        assert np.array_equal(host(p.scales16).view(np.uint16), o["scales16"].view(np.uint16)), i
+        assert np.array_equal(host(p.s16).view(np.uint16), o["s16"].view(np.uint16)), i
+        assert int(host(p.flags)[0]) == 0
+
+
+def test_pack_matches_on_extreme_scales(awq):
+    """Scales spanning 2^-20 .. 2^20 exercise steps near the fp32 extremes and the exact-division
+    fallback of the quotient."""
+    g = np.random.default_rng(43)
+    W = (0.02 * g.standard_normal((200, 512))).astype(np.float32)
+    s = np.exp2(g.uniform(-20, 20, 512)).astype(np.float32)
+    say("pack extreme scales", W.shape)
+    p = awq.pack_int4(dev(W), dev(s), awq.AwqConfig(), with_codes=True)
+    o = oracle.pack_layer(W, s)
+    assert np.array_equal(host(p.codes), o["codes"])
+    assert np.array_equal(host(p.qweight).view(np.uint32), o["qweight"])
+
+
+def test_pack_half_integer_quotients(awq):
+    """Groups whose scaled values sit exactly on k + 1/2 steps: round half to even decides."""
+    W = np.zeros((4, 128), np.float32)
+    vals = [7.0, 0.5, 1.5, 2.5, 3.5, -2.5, 6.5, -0.5, -1.5, -3.5, 4.5, 5.5, -4.5, -5.5, -6.5]
+    for r in range(4):
+        W[r, :len(vals)] = np.array(vals, np.float32) * (r + 1) / 8
+    s = np.ones(128, np.float32)
+    say("pack half-integer quotients")
+    p = awq.pack_int4(dev(W), dev(s), awq.AwqConfig(), with_codes=True)
+    o = oracle.pack_layer(W, s)
+    assert np.array_equal(host(p.codes), o["codes"])
+
+
+# ------------------------------------------------------------------------------------------------
+def _w4a16_case(n, k, m, seed):
+    qw, sc, s = workloads.w4a16_random_artifacts(n, k, config=4, j=seed)
+    A = workloads.w4a16_activations(m, k, config=4, j=seed)
+    return A, qw, sc, s
+
+
+W4A16_CASES = [(384, 512, m) for m in (1, 3, 16, 17, 64, 100)] + \
+              [(4096, 4096, m) for m in (1, 4, 16, 64, 512)] + \
+              [(11008, 4096, m) for m in (1, 64)] + [(4096, 11008, 16)]
+
+
+@pytest.mark.parametrize("n,k,m", W4A16_CASES)
+def test_w4a16_parity(awq, n, k, m):
+    A, qw, sc, s = _w4a16_case(n, k, m, seed=n + m)
+    say("w4a16", (m, k), "x", (n, k))
+    Y = awq.w4a16_gemm(dev(A), dev(qw.view(np.int32)), dev(sc), dev(s))
+    ref = oracle.w4a16(A, qw, sc, s)
+    rep = oracle.accuracy_report(host(Y).astype(np.float64), ref)
+    say(rep)
+    assert rep["rel_fro"] <= W4A16_RTOL
+
+
+def test_w4a16_exact_integer_case(awq):
+    """Unit steps and s, small integer activations: the fp16 output is exact."""
+    g = np.random.default_rng(44)
+    q = g.integers(-8, 8, size=(272, 384), dtype=np.int8)
+    qw = oracle.pack_int4(q)
+    A = g.integers(-3, 4, size=(37, 384)).astype(np.float16)
+    sc = np.ones((272, 3), np.float16)
+    s = np.ones(384, np.float16)
+    say("w4a16 exact integers")
+    Y = awq.w4a16_gemm(dev(A), dev(qw.view(np.int32)), dev(sc), dev(s))
+    ref = oracle.w4a16(A, qw, sc, s)
+    assert np.array_equal(host(Y).astype(np.float64), ref)
+
+
+# ------------------------------------------------------------------------------------------------
+def test_end_to_end_c1(awq):
+    """The four calls chained on the 512x512 fp32 layer: stats -> search -> pack(s*) -> W4A16."""
+    L = workloads.c1_layer()
+    say("end-to-end c1")
+    Wt, Xt = dev(L.W), dev(L.X)
+    sx, flags = awq.act_stats(Xt)
+    res = awq.search_layer(Wt, Xt, sx, flags=flags)
+    p = awq.pack_int4(Wt, res.s_best, flags=flags, with_codes=True)
+    A = workloads.w4a16_activations(16, 512, config=1)
+    Y = awq.w4a16_gemm(dev(A), p.qweight, p.scales16, p.s16)
+    orc = oracle.search_layer(L.W, L.X, oracle.act_stats(L.X))
+    bg = int(host(res.best)[0])
+    check_alpha(host(res.losses), orc["losses"], bg, orc["best"])
+    o = oracle.pack_layer(L.W, orc["scales"][bg])
+    assert np.array_equal(host(p.qweight).view(np.uint32), o["qweight"])
+    assert np.array_equal(host(p.scales16).view(np.uint16), o["scales16"].view(np.uint16))
+    ref = oracle.w4a16(A, o["qweight"], o["scales16"], o["s16"])
+    assert oracle.accuracy_report(host(Y), ref)["rel_fro"] <= W4A16_RTOL
+    assert int(host(flags)[0]) == 0
+
+
+# ------------------------------------------------------------------------------------------------
+def test_flags_are_raised(awq):
+    from post_weight_quantization_channel_amd import _lib as L
+    say("flags")
+    W = (0.02 * np.random.default_rng(45).standard_normal((64, 256))).astype(np.float16)
+    X = np.random.default_rng(46).standard_normal((100, 256)).astype(np.float16)
+    Wn = W.copy()
+    Wn[3, 7] = np.nan
+    sx, _ = awq.act_stats(dev(X))
+    r = awq.search_layer(dev(Wn), dev(X), sx)
+    assert int(host(r.flags)[0]) & L.FLAG_NONFINITE_W
+    Xf = X.astype(np.float32)
+    Xf[5, 9] = 1e6
+    r = awq.search_layer(dev(W), dev(Xf), sx)
+    assert int(host(r.flags)[0]) & L.FLAG_X_F16_RANGE
+    Xb = np.full((9000, 8), 60000.0, np.float16)
+    _, f = awq.act_stats(dev(Xb))
+    assert int(host(f)[0]) & L.FLAG_STATS_INEXACT
+    Xi = X.copy()
+    Xi[0, 0] = np.inf
+    _, f = awq.act_stats(dev(Xi))
+    assert int(host(f)[0]) & L.FLAG_NONFINITE_X
+    p = awq.pack_int4(dev(np.ones((2, 128), np.float32)), dev(np.full(128, 1e6, np.float32)))
+    assert int(host(p.flags)[0]) & L.FLAG_SCALE16_OVERFLOW
+
+
+# ------------------------------------------------------------------------------------------------
+REDUCED_SHAPE_CASES = [
+    # LLaMA-7B MLP and 70B-class shapes at a reduced token count (the oracle's fp64 contraction
+    # at 65536 tokens would take minutes per grid point); K and N as in the full layers.
+    ("c3_gate_11008x4096", lambda: (workloads.weight(3, 11008, 4096), None), 4096, 512, 4),
+    ("c3_down_4096x11008", lambda: (workloads.weight(3, 4096, 11008, j=2), "abs"), 11008, 512, 4),
+    ("c5_kv_1024x8192_int4", lambda: (workloads.c5_weight(1024, j=1), "c5"), 8192, 1024, 4),
+    ("c5_kv_1024x8192_int3", lambda: (workloads.c5_weight(1024, j=2), "c5"), 8192, 1024, 3),
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,make,k,m,bits", REDUCED_SHAPE_CASES,
+                         ids=[c[0] for c in REDUCED_SHAPE_CASES])
+def test_search_parity_layer_shapes(awq, name, make, k, m, bits):
+    W, kind = make()
+    if kind == "abs":
+        X = workloads.activations(3, m, workloads.channel_gains_choice(3, k, 110, 30.0, j=2),
+                                  np.float16, j=2, absolute=True)
+    elif kind == "c5":
+        X = workloads.c5_x(m=m, k=k)
+    else:
+        X = workloads.activations(3, m, workloads.channel_gains_lognormal(3, k, 0.01, 50.0))
+    say("search", name, W.shape, X.shape, "bits", bits)
+    Wt, Xt = dev(W), dev(X)
+    sx, flags = awq.act_stats(Xt)
+    res = awq.search_layer(Wt, Xt, sx, awq.AwqConfig(bits=bits), flags=flags)
+    sx_o = oracle.act_stats(X)
+    assert np.array_equal(host(sx), sx_o)
+    form = "gram" if 2 * m > k else "direct"
+    orc = oracle.search_layer(W, X, sx_o, bits=bits, form=form)
+    bg = int(host(res.best)[0])
+    err, gap = check_alpha(host(res.losses), orc["losses"], bg, orc["best"])
+    say(f"max loss rel err {err:.2e}, oracle gap {gap:.2e}, alpha* {bg} / {orc['best']}")
+    rows = np.arange(0, W.shape[0], 97)
+    p = awq.pack_int4(Wt, res.s_best, awq.AwqConfig(bits=bits), with_codes=True)
+    o = oracle.pack_layer(W[rows], orc["scales"][bg], bits=bits)
+    assert np.array_equal(host(p.codes)[rows], o["codes"])
+    assert int(host(flags)[0]) == 0
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(1200)
+def test_full_c2_layer(awq):
+    """The benchmarked workload at full size: 4096x4096 fp16 weight, 65536 calibration tokens.
+    Every s_X, every per-alpha loss (oracle in the Gram form), alpha*, and sampled rows of the
+    packed result; then W4A16 on the packed artefacts."""
+    L = workloads.c2_like_layer()
+    say("full c2", L.W.shape, L.X.shape)
+    Wt, Xt = dev(L.W), dev(L.X)
+    sx, flags = awq.act_stats(Xt)
+    res = awq.search_layer(Wt, Xt, sx, flags=flags)
+    p = awq.pack_int4(Wt, res.s_best, flags=flags, with_codes=True)
+    A = workloads.w4a16_activations(16, 4096, config=2)
+    Y = awq.w4a16_gemm(dev(A), p.qweight, p.scales16, p.s16)
+    sx_g, losses, bg = host(sx), host(res.losses), int(host(res.best)[0])
+    codes_g, qw_g, sc_g, s16_g, Y_g = (host(p.codes), host(p.qweight).view(np.uint32),
+                                       host(p.scales16), host(p.s16), host(Y))
+    assert int(host(flags)[0]) == 0
+    del Xt
+    sx_o = oracle.act_stats(L.X)
+    assert np.array_equal(sx_g, sx_o)
+    # the oracle's Gram-form search, step by step so that progress is visible
+    say("oracle: H = X^T X in fp64 ...")
+    H = oracle.gram(L.X)
+    S = oracle.scale_table(sx_o, 20)
+    lo = np.empty(20)
+    for i in range(20):
+        q, d = oracle.quantize(L.W, S[i])
+        lo[i] = oracle.loss_gram(H, oracle.error_matrix(L.W, q, d, S[i]), L.X.shape[0])
+        say(f"oracle alpha {i}: L = {lo[i]:.9e}  gpu {losses[i]:.9e}")
+    best_o = oracle.argmin_lowest(lo)
+    err, gap = check_alpha(losses, lo, bg, best_o)
+    say(f"max loss rel err {err:.2e}, oracle gap {gap:.2e}, alpha* {bg} / {best_o}")
+    orc = {"scales": S}
+    rows = np.arange(0, 4096, 61)
+    o = oracle.pack_layer(L.W[rows], orc["scales"][bg])
+    assert np.array_equal(codes_g[rows], o["codes"])
+    assert np.array_equal(qw_g[rows], o["qweight"])
+    assert np.array_equal(sc_g[rows].view(np.uint16), o["scales16"].view(np.uint16))
+    full = oracle.pack_layer(L.W, orc["scales"][bg])
+    ref = oracle.w4a16(A, full["qweight"], full["scales16"], full["s16"])
+    assert oracle.accuracy_report(Y_g, ref)["rel_fro"] <= W4A16_RTOL
