@@ -108,7 +108,7 @@ awq_status awq_act_stats(const void* X, awq_dtype xdt, int64_t M, int64_t K, int
  * W      [N, K] row-major, dtype wdt (AWQ_F16 or AWQ_F32), 16-byte aligned; N >= 1.
  * X      [M, K] row-major (row stride K), dtype xdt (AWQ_F16, AWQ_BF16 or AWQ_F32).
  * sx     fp32 [K], typically the output of awq_act_stats on the same X.
- * cfg    host pointer, see awq_cfg. K must be a multiple of cfg->group.
+ * cfg    host pointer, see awq_cfg. K must be a multiple of cfg->group and at most 2^22.
  * For each i: s_i[k] = fp32(pow_f64(max(sx[k], s_floor), i/(n_grid-1))),
  *   codes q = clamp(rint(fp32(fp32(w s_i) / Delta)), -2^(b-1), 2^(b-1)-1) with
  *   Delta = fp32(max_group |fp32(w s_i)| / (2^(b-1)-1)) per (row, group of 128), all in IEEE

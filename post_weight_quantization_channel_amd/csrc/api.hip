@@ -26,6 +26,7 @@ awq_status check_cfg(const awq_cfg* cfg) {
 
 // Largest accepted extent of one dimension; keeps every element index and tile index in range.
 constexpr int64_t kMaxDim = int64_t(1) << 24;
+constexpr int64_t kMaxSearchK = int64_t(1) << 22;
 
 struct SearchLayout {
   size_t ctrl, S, X16, E, partials, total;
@@ -111,8 +112,9 @@ awq_status search_impl(const void* W, awq_dtype wdt, int64_t N, int64_t K, const
   if (cs != AWQ_OK) return cs;
   if (wdt != AWQ_F16 && wdt != AWQ_F32) return AWQ_ERR_DTYPE;
   if (!valid_dtype(xdt)) return AWQ_ERR_DTYPE;
+  // K <= 2^22 keeps the loss kernel's 32-bit buffer offsets (256 rows x 2K bytes) in range
   if (M < 1 || N < 1 || K < cfg->group || K % cfg->group || M > kMaxDim || N > kMaxDim ||
-      K > kMaxDim || !aligned16(W) || !aligned16(X))
+      K > kMaxSearchK || !aligned16(W) || !aligned16(X))
     return AWQ_ERR_SHAPE;
   const SearchLayout L = search_layout(M, N, K, xdt, cfg->n_grid);
   if ((int64_t)L.tiles_per_alpha * cfg->n_grid > (int64_t(1) << 31) - 1) return AWQ_ERR_SHAPE;

@@ -126,6 +126,50 @@ __device__ __forceinline__ float quant8(const float (&ws)[8], float qmin, float 
   return delta;
 }
 
+// Buffer resource over [base, base + num_bytes): loads at offsets >= num_bytes return zero,
+// which handles ragged tiles without branches. Word 1 holds the top 16 address bits with
+// stride 0 (raw buffer); word 3 = 0x00020000 is the raw 32-bit data format used for untyped
+// buffer access on gfx9-family (CDNA) parts. The descriptor must be wave-uniform (SGPRs).
+typedef int rsrc_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  rsrc_t r;
+  r[0] = (int)(uint32_t)b;
+  r[1] = (int)((uint32_t)(b >> 32) & 0xFFFFu);
+  r[2] = (int)num_bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// LDS byte address of a __shared__ object (for M0 below).
+typedef __attribute__((address_space(3))) char lds_char_t;
+__device__ __forceinline__ uint32_t lds_addr(const void* shared_obj) {
+  return (uint32_t)(uintptr_t)(const lds_char_t*)shared_obj;
+}
+
+// 16 bytes per lane from global memory (buffer offset `voff`) straight into LDS: lane l writes
+// bytes [16 l, 16 l + 16) of the 1 KiB block at LDS address `lds` (wave-uniform).
+//
+// Written as inline asm on purpose: the compiler cannot tell which LDS bytes such a load writes,
+// so with the builtin it would wait for every load in flight before each LDS read of the K loop,
+// which serialises the multi-stage pipeline. The asm block has no register outputs (the data goes
+// to LDS); it keeps the one wait state the hardware needs between writing M0 and the load that
+// reads it, restores M0 before it ends, and the callers order LDS accesses against these loads
+// with explicit vmcnt waits and barriers.
+__device__ __forceinline__ void buffer_load16_lds(rsrc_t r, uint32_t lds, uint32_t voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"                      // one wait state between an M0 write and its LDS-DMA use
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(voff), "s"(r)
+      : "memory");
+}
+
 __device__ __forceinline__ void flag_or(uint32_t* flags, uint32_t bits) {
   if (bits) atomicOr(flags, bits);
 }

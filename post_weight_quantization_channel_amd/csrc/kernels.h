@@ -17,11 +17,11 @@ hipError_t launch_stats(const void* X, int dtype, int64_t M, int64_t K, int64_t 
 // ---- search ----
 constexpr int kLossBM = 256;
 constexpr int kLossBN = 256;
-constexpr int kLossBK = 64;
+constexpr int kLossBK = 32;
 
 struct SearchCtrl {        // lives at the start of the search workspace
   uint32_t absmax_bits;    // max |W| as fp32 bits (atomicMax on non-negative floats)
-  int32_t escale;          // error stack stored as E * 2^escale
+  uint32_t done;           // grid points whose loss is final (finalize's completion count)
 };
 
 hipError_t launch_search_prep(const float* sx, int K, int n_grid, float s_floor, float* S,
@@ -37,7 +37,7 @@ hipError_t launch_lossgemm(const uint16_t* X16, int64_t M, int64_t K, const uint
                            int64_t N, int n_grid, double* partials, hipStream_t stream);
 hipError_t launch_finalize(const double* partials, int64_t tiles_per_alpha, int n_grid,
                            int64_t M, int64_t N, int64_t K, const float* S,
-                           const SearchCtrl* ctrl, double* losses, int32_t* best,
+                           SearchCtrl* ctrl, double* losses, int32_t* best,
                            float* s_best, uint32_t* flags, hipStream_t stream);
 
 // ---- pack ----

@@ -6,13 +6,20 @@
 // the objective of the AWQ notes (bg51717.github.io/14592, section 方法).
 //
 // gfx950 design:
-//   * 256 threads = 4 waves (2 x 2), workgroup tile 256 x 256, wave tile 128 x 128, BK = 64;
+//   * 256 threads = 4 waves (2 x 2), workgroup tile 256 x 256, wave tile 128 x 128, BK = 32;
 //   * v_mfma_f32_32x32x16_f16: 4 x 4 MFMA blocks per wave, 256 fp32 accumulators per lane
 //     (held in AGPRs; one wave per SIMD);
-//   * both operands are K-contiguous rows; global -> register -> LDS staging, double-buffered
-//     (2 x 64 KiB), one barrier per K step; the 16-byte chunks of each 128-byte LDS row are
-//     XOR-swizzled by (row & 7) so the 128-bit fragment reads of 8 consecutive rows hit
-//     distinct banks;
+//   * operands go from HBM straight into LDS (buffer_load_dwordx4 ... lds): no staging
+//     registers and no ds_write; each wave instruction fills 1 KiB = 16 rows x 64 bytes. The
+//     buffer range of each operand panel ends at its last valid row, so rows of a ragged tile
+//     read as zeros without branches;
+//   * four LDS stages of 32 KiB: the loads of steps k+1..k+4 are in flight while step k
+//     computes (one stage ahead left the waves waiting ~40% of the time on loads whose lines
+//     missed L2; LDS bank conflicts: none). Fragment reads of the next step overlap the second
+//     half of the current step's MFMAs;
+//   * LDS layout: row r holds its 4 chunks of 16 bytes at positions c ^ f(r),
+//     f(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1), so the 128-bit fragment reads of 8 (and of 16)
+//     consecutive rows at one chunk touch distinct banks whether the LDS has 32 or 64 banks;
 //   * tile order: blocks are dealt round-robin to the 8 XCDs, so block b is remapped to give
 //     each XCD a contiguous range of tiles, and tiles are walked in groups of 8 M-tiles so the
 //     32 workgroups resident on one XCD share X and E panels in that XCD's L2;
@@ -28,20 +35,103 @@ namespace {
 constexpr int BM = kLossBM, BN = kLossBN, BK = kLossBK;
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
-constexpr int kRowsPerPass = kThreads / (BK / 8);           // 32 rows per load pass
-constexpr int kLoadsPerOp = BM / kRowsPerPass;              // 8 x 16-byte loads per operand
-constexpr int kStageHalves = (BM + BN) * BK;                // halves per LDS stage
+constexpr int kStages = 4;
+constexpr int kRowBytes = BK * 2;                           // 64 bytes of a row per K step
+constexpr int kStageBytes = (BM + BN) * kRowBytes;          // 32 KiB per stage
+constexpr int kRowsPerWave = BM / 4;                        // rows each wave loads per operand
+constexpr int kRowsPerInst = 1024 / kRowBytes;              // 16 rows per 1 KiB wave load
+constexpr int kInstPerOp = kRowsPerWave / kRowsPerInst;     // 4 loads per operand per step
 
-__device__ __forceinline__ int swz(int row, int chunk) {   // half offset inside a stage operand
-  return row * BK + ((chunk ^ (row & 7)) << 3);
-}
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+
+// s_waitcnt immediate that waits until at most n vector-memory loads are outstanding (gfx9
+// encoding: vmcnt in bits [3:0] and [15:14]; expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 
 }  // namespace
+
+// The K loop over four LDS stages (addresses base + j * kStageBytes).
+//
+// Per step kt (stage kt % 4): read the second half (k 16..31) of the stage's fragments, issue the
+// 16 MFMAs of the first half, wait until step kt+1 has landed (steps kt+2, kt+3 may still be in
+// flight) and until this wave's LDS reads are done, barrier, refill stage kt with step kt+4,
+// read the first half of step kt+1's fragments, issue the 16 MFMAs of the second half of step kt.
+struct LossTile {
+  rsrc_t ra, rb;        // operand panels
+  uint32_t voff;        // this lane's byte offset for load j = 0, step 0
+  uint32_t row_stride;  // bytes between rows (K * 2)
+  int wave, wm, wn, frow, fhalf;
+};
+
+__device__ __forceinline__ void loss_kloop(const char* smem, const LossTile& T, int nk,
+                                           floatx16 (&acc)[4][4]) {
+  const uint32_t lds0 = lds_addr(smem);
+  auto issue = [&](int stage, int kt) {
+    const uint32_t la = lds0 + (uint32_t)(stage * kStageBytes);
+    const uint32_t lb = la + (uint32_t)(BM * kRowBytes);
+    const uint32_t kofs = (uint32_t)kt * (uint32_t)kRowBytes;
+#pragma unroll
+    for (int j = 0; j < kInstPerOp; ++j) {
+      const uint32_t o = T.voff + (uint32_t)(kRowsPerInst * j) * T.row_stride + kofs;
+      const uint32_t row_ofs = (uint32_t)((T.wave * kRowsPerWave + kRowsPerInst * j) * kRowBytes);
+      buffer_load16_lds(T.ra, la + row_ofs, o);
+      buffer_load16_lds(T.rb, lb + row_ofs, o);
+    }
+  };
+  auto read_frags = [&](int stage, int kk, half8_t (&af)[4], half8_t (&bf)[4]) {
+    const char* sa = smem + stage * kStageBytes;
+    const char* sb = sa + BM * kRowBytes;
+    const int chunk = kk * 2 + T.fhalf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = T.wm * 128 + i * 32 + T.frow;
+      af[i] = *reinterpret_cast<const half8_t*>(sa + r * kRowBytes + ((chunk ^ swz(r)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = T.wn * 128 + j * 32 + T.frow;
+      bf[j] = *reinterpret_cast<const half8_t*>(sb + r * kRowBytes + ((chunk ^ swz(r)) << 4));
+    }
+  };
+  auto mfma16 = [&](const half8_t (&af)[4], const half8_t (&bf)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  };
+
+  half8_t a0[4], b0[4], a1[4], b1[4];
+  auto step = [&](int stage, int kt) {
+    read_frags(stage, 1, a1, b1);
+    mfma16(a0, b0);
+    // wait: step kt+1 landed (this wave's loads) and this wave's LDS reads returned
+    if (kt + 3 < nk) __builtin_amdgcn_s_waitcnt(vmcnt(16) & ~0x0F00);
+    else if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(vmcnt(8) & ~0x0F00);
+    else __builtin_amdgcn_s_waitcnt(vmcnt(0) & ~0x0F00);
+    __syncthreads();
+    if (kt + 4 < nk) issue(stage, kt + 4);
+    if (kt + 1 < nk) read_frags((stage + 1) & 3, 0, a0, b0);
+    mfma16(a1, b1);
+  };
+
+#pragma unroll
+  for (int p = 0; p < kStages; ++p) issue(p, p);   // nk >= 4 (K is a multiple of 128)
+  __builtin_amdgcn_s_waitcnt(vmcnt(24));           // step 0 has landed
+  __syncthreads();
+  read_frags(0, 0, a0, b0);
+  for (int q = 0; q < nk; q += 4) {
+    step(0, q);
+    step(1, q + 1);
+    step(2, q + 2);
+    step(3, q + 3);
+  }
+}
 
 __global__ __launch_bounds__(kThreads, 1) void lossgemm_kernel(
     const uint16_t* __restrict__ X, int64_t M, int64_t K, const uint16_t* __restrict__ Est,
     int64_t N, int tilesM, int tilesN, int n_grid, double* __restrict__ partials) {
-  __shared__ __attribute__((aligned(16))) _Float16 smem[2 * kStageHalves];
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
 
   // ---- tile assignment -------------------------------------------------------------------
   const int G = gridDim.x;
@@ -61,44 +151,24 @@ __global__ __launch_bounds__(kThreads, 1) void lossgemm_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- global load mapping: row = tid/8 + 32*j, 16-byte chunk = tid%8 ---------------------
-  const int lchunk = tid & 7;
-  const int lrow = tid >> 3;
-  // row j of this thread's load set is lrow + 32 j; one base pointer per operand plus the
-  // uniform stride 32 K keeps the addresses in a few registers.
-  const int64_t arow0 = (int64_t)mt * BM + lrow;
-  const int64_t brow0 = (int64_t)nt * BN + lrow;
-  const int64_t a_left = M - arow0;   // rows of this thread's set that exist: 32 j < a_left
-  const int64_t b_left = N - brow0;
-  const uint16_t* abase = X + arow0 * K + lchunk * 8;
-  const uint16_t* bbase = Est + ((int64_t)alpha * N + brow0) * K + lchunk * 8;
-  const int64_t jstride = (int64_t)kRowsPerPass * K;
-
-  uint4 ra[kLoadsPerOp], rb[kLoadsPerOp];
-  auto gload = [&](int64_t k0) {
-#pragma unroll
-    for (int j = 0; j < kLoadsPerOp; ++j) {
-      ra[j] = (kRowsPerPass * j < a_left)
-                  ? *reinterpret_cast<const uint4*>(abase + j * jstride + k0)
-                  : make_uint4(0, 0, 0, 0);
-      rb[j] = (kRowsPerPass * j < b_left)
-                  ? *reinterpret_cast<const uint4*>(bbase + j * jstride + k0)
-                  : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto lstore = [&](int stage) {
-    _Float16* sa = smem + stage * kStageHalves;
-    _Float16* sb = sa + BM * BK;
-#pragma unroll
-    for (int j = 0; j < kLoadsPerOp; ++j) {
-      const int r = lrow + kRowsPerPass * j;
-      *reinterpret_cast<uint4*>(sa + swz(r, lchunk)) = ra[j];
-      *reinterpret_cast<uint4*>(sb + swz(r, lchunk)) = rb[j];
-    }
-  };
+  // ---- operand panels as buffer ranges ---------------------------------------------------
+  const int64_t a_rows = (M - (int64_t)mt * BM < BM) ? M - (int64_t)mt * BM : BM;
+  const int64_t b_rows = (N - (int64_t)nt * BN < BN) ? N - (int64_t)nt * BN : BN;
+  LossTile T;
+  T.ra = make_rsrc(X + (int64_t)mt * BM * K, (uint32_t)(a_rows * K * 2));
+  T.rb = make_rsrc(Est + ((int64_t)alpha * N + (int64_t)nt * BN) * K, (uint32_t)(b_rows * K * 2));
+  T.wave = tid >> 6;
+  T.wm = T.wave >> 1;
+  T.wn = T.wave & 1;
+  T.frow = lane & 31;   // fragment row within a 32-row block
+  T.fhalf = lane >> 5;  // which 8-element half of a 16-wide k slice
+  // lane l of load instruction j fills LDS row wave*64 + 16j + l/4, physical chunk l%4, i.e.
+  // the logical chunk (l%4) ^ swz(row); swz depends on row % 16 = l/4 only.
+  const int lrow = lane >> 2;
+  T.row_stride = (uint32_t)(K * 2);
+  T.voff = (uint32_t)(T.wave * kRowsPerWave + lrow) * T.row_stride +
+           (uint32_t)(((lane & 3) ^ swz(lrow)) * 16);
 
   floatx16 acc[4][4];
 #pragma unroll
@@ -108,42 +178,7 @@ __global__ __launch_bounds__(kThreads, 1) void lossgemm_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int frow = lane & 31;   // fragment row within a 32-row block
-  const int fhalf = lane >> 5;  // which 8-element half of the 16-wide k slice
-  const int nk = (int)(K / BK);
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < nk) gload((int64_t)(kt + 1) * BK);
-    const _Float16* sa = smem + stage * kStageHalves;
-    const _Float16* sb = sa + BM * BK;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int chunk = kk * 2 + fhalf;
-      half8_t af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 128 + i * 32 + frow;
-        af[i] = *reinterpret_cast<const half8_t*>(sa + swz(r, chunk));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wn * 128 + j * 32 + frow;
-        bf[j] = *reinterpret_cast<const half8_t*>(sb + swz(r, chunk));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) lstore(stage ^ 1);
-    __syncthreads();
-  }
+  loss_kloop(smem, T, (int)(K / BK), acc);
 
   // ---- epilogue: sum of squares, fixed order ---------------------------------------------
   double tot = 0.0;
@@ -158,7 +193,7 @@ __global__ __launch_bounds__(kThreads, 1) void lossgemm_kernel(
     }
   for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
   __shared__ double wsum[4];
-  if (lane == 0) wsum[wave] = tot;
+  if (lane == 0) wsum[T.wave] = tot;
   __syncthreads();
   if (tid == 0) {
     const double t = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];

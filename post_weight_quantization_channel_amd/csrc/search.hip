@@ -24,7 +24,7 @@ __global__ __launch_bounds__(256) void search_prep_kernel(const float* __restric
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx == 0) {
     ctrl->absmax_bits = 0u;
-    ctrl->escale = 0;
+    ctrl->done = 0u;
   }
   if (idx >= (int64_t)n_grid * K) return;
   const int i = (int)(idx / K);
@@ -50,8 +50,22 @@ __global__ __launch_bounds__(256) void absmax_kernel(const void* __restrict__ W,
   constexpr int ES = (DT == kF32) ? 4 : 2;
   float m = 0.0f;
   bool bad = false;
-  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < count8;
-       c += (int64_t)gridDim.x * 256) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; c + 3 * stride < count8; c += 4 * stride) {     // four loads in flight per thread
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      load8_f32<DT>(reinterpret_cast<const char*>(W) + (c + u * stride) * 8 * ES, v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        bad |= !isfinite(v[u][t]);
+        m = fmaxf(m, fabsf(v[u][t]));
+      }
+  }
+  for (; c < count8; c += stride) {
     float v[8];
     load8_f32<DT>(reinterpret_cast<const char*>(W) + c * 8 * ES, v);
 #pragma unroll
@@ -60,17 +74,23 @@ __global__ __launch_bounds__(256) void absmax_kernel(const void* __restrict__ W,
       m = fmaxf(m, fabsf(v[t]));
     }
   }
-  // wave maximum, then one atomic per wave
+  // wave maximum, then workgroup maximum, then one atomic per workgroup (max is order-free)
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if (__lane_id() == 0) atomicMax(&ctrl->absmax_bits, __float_as_uint(m));
+  __shared__ float wmax[4];
+  if (__lane_id() == 0) wmax[threadIdx.x >> 6] = m;
   wave_flag(flags, bad, kFlagNonfiniteW);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float bm = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    atomicMax(&ctrl->absmax_bits, __float_as_uint(bm));
+  }
 }
 
 hipError_t launch_absmax(const void* W, int dtype, int64_t count, SearchCtrl* ctrl,
                          uint32_t* flags, hipStream_t stream) {
   const int64_t count8 = count / 8;
-  int64_t blocks = (count8 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
+  int64_t blocks = (count8 + 1023) / 1024;
+  if (blocks > 1024) blocks = 1024;
   if (blocks < 1) blocks = 1;
   if (dtype == kF32)
     absmax_kernel<kF32><<<(unsigned)blocks, 256, 0, stream>>>(W, count8, ctrl, flags);
@@ -209,36 +229,52 @@ hipError_t launch_quantize_stack(const void* W, int dtype, int64_t N, int64_t K,
 }
 
 // ------------------------------------------------------------------------------------------
+// One workgroup per grid point sums that point's tile partials (thread t takes tiles t, t+256,
+// ... into four independent accumulators, combined and tree-reduced in a fixed order). The last
+// workgroup to finish -- found with an atomic counter -- picks the argmin and copies s_best.
 __global__ __launch_bounds__(256) void finalize_kernel(
     const double* __restrict__ partials, int64_t tiles, int n_grid, int64_t M, int64_t N,
-    int64_t K, const float* __restrict__ S, const SearchCtrl* __restrict__ ctrl,
+    int64_t K, const float* __restrict__ S, SearchCtrl* __restrict__ ctrl,
     double* __restrict__ losses, int32_t* __restrict__ best, float* __restrict__ s_best,
     uint32_t* __restrict__ flags) {
   __shared__ double red[256];
-  __shared__ double L[64];
+  __shared__ int is_last;
   __shared__ int sbest;
   const int tid = threadIdx.x;
-  const int e = escale_from_absmax(ctrl->absmax_bits);
-  const double denom = (double)M * (double)N;
-  for (int i = 0; i < n_grid; ++i) {
-    double acc = 0.0;
-    for (int64_t t = tid; t < tiles; t += 256) acc += partials[(int64_t)i * tiles + t];
-    red[tid] = acc;
-    __syncthreads();
-    for (int w = 128; w >= 1; w >>= 1) {
-      if (tid < w) red[tid] += red[tid + w];
-      __syncthreads();
-    }
-    if (tid == 0) L[i] = ldexp(red[0], -2 * e) / denom;
+  const int i = blockIdx.x;
+  const double* p = partials + (int64_t)i * tiles;
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  int64_t t = tid;
+  for (; t + 768 < tiles; t += 1024) {
+    a0 += p[t];
+    a1 += p[t + 256];
+    a2 += p[t + 512];
+    a3 += p[t + 768];
+  }
+  for (; t < tiles; t += 256) a0 += p[t];
+  red[tid] = (a0 + a1) + (a2 + a3);
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
     __syncthreads();
   }
   if (tid == 0) {
+    const int e = escale_from_absmax(ctrl->absmax_bits);
+    losses[i] = ldexp(red[0], -2 * e) / ((double)M * (double)N);
+    __threadfence();
+    is_last = (atomicAdd(&ctrl->done, 1u) == (unsigned)(n_grid - 1));
+  }
+  __syncthreads();
+  if (!is_last) return;
+  if (tid == 0) {
+    __threadfence();
+    volatile double* L = losses;
     int b = 0;
     bool bad = false;
-    for (int i = 0; i < n_grid; ++i) {
-      losses[i] = L[i];
-      bad |= !isfinite(L[i]);
-      if (L[i] < L[b]) b = i;
+    for (int j = 0; j < n_grid; ++j) {
+      const double v = L[j];
+      bad |= !isfinite(v);
+      if (v < L[b]) b = j;
     }
     *best = b;
     sbest = b;
@@ -251,10 +287,10 @@ __global__ __launch_bounds__(256) void finalize_kernel(
 
 hipError_t launch_finalize(const double* partials, int64_t tiles_per_alpha, int n_grid,
                            int64_t M, int64_t N, int64_t K, const float* S,
-                           const SearchCtrl* ctrl, double* losses, int32_t* best,
+                           SearchCtrl* ctrl, double* losses, int32_t* best,
                            float* s_best, uint32_t* flags, hipStream_t stream) {
-  finalize_kernel<<<1, 256, 0, stream>>>(partials, tiles_per_alpha, n_grid, M, N, K, S, ctrl,
-                                         losses, best, s_best, flags);
+  finalize_kernel<<<n_grid, 256, 0, stream>>>(partials, tiles_per_alpha, n_grid, M, N, K, S, ctrl,
+                                              losses, best, s_best, flags);
   return hipGetLastError();
 }
 

@@ -105,6 +105,7 @@ def test_search_rejects(lib):
     assert _search(lib, xdt=9) == E.AWQ_ERR_DTYPE
     assert _search(lib, K=500) == E.AWQ_ERR_SHAPE
     assert _search(lib, K=64) == E.AWQ_ERR_SHAPE
+    assert _search(lib, K=(1 << 22) + 128) == E.AWQ_ERR_SHAPE
     assert _search(lib, M=0) == E.AWQ_ERR_SHAPE
     assert _search(lib, N=0) == E.AWQ_ERR_SHAPE
     assert _search(lib, W=FAKE + 4) == E.AWQ_ERR_SHAPE
