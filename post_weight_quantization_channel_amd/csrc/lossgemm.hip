@@ -50,82 +50,89 @@ constexpr int vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 
 }  // namespace
 
-// The K loop over four LDS stages (addresses base + j * kStageBytes).
+// The K loop over four LDS stages (LDS addresses base + stage * kStageBytes, stage = kt % 4).
 //
-// Per step kt (stage kt % 4): read the second half (k 16..31) of the stage's fragments, issue the
-// 16 MFMAs of the first half, wait until step kt+1 has landed (steps kt+2, kt+3 may still be in
-// flight) and until this wave's LDS reads are done, barrier, refill stage kt with step kt+4,
-// read the first half of step kt+1's fragments, issue the 16 MFMAs of the second half of step kt.
+// Per step kt: the 16 MFMAs of the first half (k 0..15) with the reads of the second-half
+// fragments in between; wait until step kt+1 has landed (steps kt+2, kt+3 may still be in
+// flight) and this wave's LDS reads are done; barrier; the 16 MFMAs of the second half with the
+// refill of stage kt (step kt+4) and the reads of step kt+1's first-half fragments in between.
+// The instruction stream is laid out by hand (sched_barrier stops the scheduler from regrouping
+// it): each MFMA keeps the matrix core busy for 32 cycles while the following load or LDS read
+// issues.
 struct LossTile {
   rsrc_t ra, rb;        // operand panels
-  uint32_t voff;        // this lane's byte offset for load j = 0, step 0
+  uint32_t voff;        // this lane's byte offset for load slice 0, step 0
   uint32_t row_stride;  // bytes between rows (K * 2)
-  int wave, wm, wn, frow, fhalf;
+  uint32_t lds0;        // LDS address of stage 0
+  uint32_t rd[2][2];    // this lane's fragment read offsets in a stage: [operand][k half]
+  int wave;
 };
+
+struct LossFrags {
+  half8_t a[2][4], b[2][4];   // [k half][row block]
+};
+
+// Fragment i (i < 4: A row block i, else B row block i - 4) of k half h from stage `st`.
+__device__ __forceinline__ void loss_read(const char* smem, const LossTile& T, int st, int h,
+                                          int i, LossFrags& F) {
+  const char* base = smem + st * kStageBytes;
+  if (i < 4)
+    F.a[h][i] = *reinterpret_cast<const half8_t*>(base + T.rd[0][h] + i * 32 * kRowBytes);
+  else
+    F.b[h][i - 4] = *reinterpret_cast<const half8_t*>(base + T.rd[1][h] + (i - 4) * 32 * kRowBytes);
+}
+
+// Load slice idx in [0, 8) of step kt into stage `st` (even idx: A, odd: B; rows 16 (idx/2) ..
+// of this wave's 64 rows).
+__device__ __forceinline__ void loss_issue(const LossTile& T, int st, int kt, int idx) {
+  const int j = idx >> 1;
+  const uint32_t lds = T.lds0 + (uint32_t)(st * kStageBytes) + ((idx & 1) ? BM * kRowBytes : 0) +
+                       (uint32_t)((T.wave * kRowsPerWave + kRowsPerInst * j) * kRowBytes);
+  const uint32_t o = T.voff + (uint32_t)(kRowsPerInst * j) * T.row_stride +
+                     (uint32_t)kt * (uint32_t)kRowBytes;
+  buffer_load16_lds((idx & 1) ? T.rb : T.ra, lds, o);
+}
+
+template <bool REFILL, bool MORE, int VM>
+__device__ __forceinline__ void loss_step(const char* smem, const LossTile& T, int kt,
+                                          LossFrags& F, floatx16 (&acc)[4][4]) {
+  const int st = kt & 3;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[0][m >> 2], F.b[0][m & 3],
+                                                                acc[m >> 2][m & 3], 0, 0, 0);
+    if ((m & 1) == 0) loss_read(smem, T, st, 1, m >> 1, F);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt(VM) & ~0x0F00);   // + lgkmcnt(0)
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[1][m >> 2], F.b[1][m & 3],
+                                                                acc[m >> 2][m & 3], 0, 0, 0);
+    if (REFILL && (m & 1) == 0) loss_issue(T, st, kt + 4, m >> 1);
+    if (MORE && (m & 1)) loss_read(smem, T, (st + 1) & 3, 0, m >> 1, F);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
 
 __device__ __forceinline__ void loss_kloop(const char* smem, const LossTile& T, int nk,
                                            floatx16 (&acc)[4][4]) {
-  const uint32_t lds0 = lds_addr(smem);
-  auto issue = [&](int stage, int kt) {
-    const uint32_t la = lds0 + (uint32_t)(stage * kStageBytes);
-    const uint32_t lb = la + (uint32_t)(BM * kRowBytes);
-    const uint32_t kofs = (uint32_t)kt * (uint32_t)kRowBytes;
+  LossFrags F;
 #pragma unroll
-    for (int j = 0; j < kInstPerOp; ++j) {
-      const uint32_t o = T.voff + (uint32_t)(kRowsPerInst * j) * T.row_stride + kofs;
-      const uint32_t row_ofs = (uint32_t)((T.wave * kRowsPerWave + kRowsPerInst * j) * kRowBytes);
-      buffer_load16_lds(T.ra, la + row_ofs, o);
-      buffer_load16_lds(T.rb, lb + row_ofs, o);
-    }
-  };
-  auto read_frags = [&](int stage, int kk, half8_t (&af)[4], half8_t (&bf)[4]) {
-    const char* sa = smem + stage * kStageBytes;
-    const char* sb = sa + BM * kRowBytes;
-    const int chunk = kk * 2 + T.fhalf;
+  for (int p = 0; p < kStages; ++p)                 // nk >= 4 (K is a multiple of 128)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = T.wm * 128 + i * 32 + T.frow;
-      af[i] = *reinterpret_cast<const half8_t*>(sa + r * kRowBytes + ((chunk ^ swz(r)) << 4));
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = T.wn * 128 + j * 32 + T.frow;
-      bf[j] = *reinterpret_cast<const half8_t*>(sb + r * kRowBytes + ((chunk ^ swz(r)) << 4));
-    }
-  };
-  auto mfma16 = [&](const half8_t (&af)[4], const half8_t (&bf)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-  };
-
-  half8_t a0[4], b0[4], a1[4], b1[4];
-  auto step = [&](int stage, int kt) {
-    read_frags(stage, 1, a1, b1);
-    mfma16(a0, b0);
-    // wait: step kt+1 landed (this wave's loads) and this wave's LDS reads returned
-    if (kt + 3 < nk) __builtin_amdgcn_s_waitcnt(vmcnt(16) & ~0x0F00);
-    else if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(vmcnt(8) & ~0x0F00);
-    else __builtin_amdgcn_s_waitcnt(vmcnt(0) & ~0x0F00);
-    __syncthreads();
-    if (kt + 4 < nk) issue(stage, kt + 4);
-    if (kt + 1 < nk) read_frags((stage + 1) & 3, 0, a0, b0);
-    mfma16(a1, b1);
-  };
-
-#pragma unroll
-  for (int p = 0; p < kStages; ++p) issue(p, p);   // nk >= 4 (K is a multiple of 128)
+    for (int idx = 0; idx < 2 * kInstPerOp; ++idx) loss_issue(T, p, p, idx);
   __builtin_amdgcn_s_waitcnt(vmcnt(24));           // step 0 has landed
   __syncthreads();
-  read_frags(0, 0, a0, b0);
-  for (int q = 0; q < nk; q += 4) {
-    step(0, q);
-    step(1, q + 1);
-    step(2, q + 2);
-    step(3, q + 3);
-  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) loss_read(smem, T, 0, 0, i, F);
+  // steps whose successors kt+1..kt+4 all exist, then the last four with constant flags
+  for (int kt = 0; kt < nk - 4; ++kt) loss_step<true, true, 16>(smem, T, kt, F, acc);
+  loss_step<false, true, 16>(smem, T, nk - 4, F, acc);
+  loss_step<false, true, 8>(smem, T, nk - 3, F, acc);
+  loss_step<false, true, 0>(smem, T, nk - 2, F, acc);
+  loss_step<false, false, 0>(smem, T, nk - 1, F, acc);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void lossgemm_kernel(
@@ -159,16 +166,24 @@ __global__ __launch_bounds__(kThreads, 1) void lossgemm_kernel(
   T.ra = make_rsrc(X + (int64_t)mt * BM * K, (uint32_t)(a_rows * K * 2));
   T.rb = make_rsrc(Est + ((int64_t)alpha * N + (int64_t)nt * BN) * K, (uint32_t)(b_rows * K * 2));
   T.wave = tid >> 6;
-  T.wm = T.wave >> 1;
-  T.wn = T.wave & 1;
-  T.frow = lane & 31;   // fragment row within a 32-row block
-  T.fhalf = lane >> 5;  // which 8-element half of a 16-wide k slice
-  // lane l of load instruction j fills LDS row wave*64 + 16j + l/4, physical chunk l%4, i.e.
-  // the logical chunk (l%4) ^ swz(row); swz depends on row % 16 = l/4 only.
+  T.lds0 = lds_addr(smem);
+  // lane l of load slice j fills LDS row wave*64 + 16j + l/4, physical chunk l%4, i.e. the
+  // logical chunk (l%4) ^ swz(row); swz depends on row % 16 = l/4 only.
   const int lrow = lane >> 2;
   T.row_stride = (uint32_t)(K * 2);
   T.voff = (uint32_t)(T.wave * kRowsPerWave + lrow) * T.row_stride +
            (uint32_t)(((lane & 3) ^ swz(lrow)) * 16);
+  // fragment reads: lane l reads row (wave block) + 32 i + l%32 at chunk 2h + l/32; the
+  // swizzle of a row does not change with the +32 i block offset, so one offset per (operand,
+  // k half) serves all four row blocks.
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const int wm = T.wave >> 1, wn = T.wave & 1;
+  const int ra0 = wm * 128 + frow, rb0 = wn * 128 + frow;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    T.rd[0][h] = (uint32_t)(ra0 * kRowBytes + (((2 * h + fhalf) ^ swz(ra0)) << 4));
+    T.rd[1][h] = (uint32_t)(BM * kRowBytes + rb0 * kRowBytes + (((2 * h + fhalf) ^ swz(rb0)) << 4));
+  }
 
   floatx16 acc[4][4];
 #pragma unroll
