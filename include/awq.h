@@ -165,10 +165,12 @@ awq_status awq_pack_int4(const void* W, awq_dtype wdt, int64_t N, int64_t K, con
  * w4a16_gemm -- QuantLinear.forward of [eng] 三 on the packed artefacts:
  *   Y[m,n] = sum_k (A[m,k] / s16[k]) * sext4(q[n,k]) * scales16[n, k/group]
  * A        fp16 bits [M, K]; qweight uint32 [N, K/8]; scales16 fp16 bits [N, K/group];
- *          s16 fp16 bits [K]; Y out, fp16 bits [M, N]. group must be 128; K % 128 == 0.
- * Products are formed on fp16 operands (activation / s and code * step each rounded once to
- * fp16) with fp32 accumulation; Y is rounded once to fp16 (relative error ~1e-3 or better).
- * Errors: AWQ_ERR_NULL, AWQ_ERR_SHAPE (M < 1, N < 1, K % 128), AWQ_ERR_CONFIG (group).
+ *          s16 fp16 bits [K]; Y out, fp16 bits [M, N]. group must be 128; K % 128 == 0,
+ *          K <= 12288.
+ * Products are formed on fp16 operands (fp16(1/s) and fp16(code * fp16(1/s)), each rounded
+ * once) with fp32 accumulation; the per-group step multiplies the fp32 partial of each group;
+ * Y is rounded once to fp16 (relative Frobenius error ~5e-4).
+ * Errors: AWQ_ERR_NULL, AWQ_ERR_SHAPE (M < 1, N < 1, K % 128, K > 12288), AWQ_ERR_CONFIG.
  * ---------------------------------------------------------------------------------------- */
 awq_status w4a16_gemm(const uint16_t* A, int64_t M, int64_t N, int64_t K, int32_t group,
                       const uint32_t* qweight, const uint16_t* scales16, const uint16_t* s16,

@@ -27,6 +27,7 @@ awq_status check_cfg(const awq_cfg* cfg) {
 // Largest accepted extent of one dimension; keeps every element index and tile index in range.
 constexpr int64_t kMaxDim = int64_t(1) << 24;
 constexpr int64_t kMaxSearchK = int64_t(1) << 22;
+constexpr int64_t kMaxW4A16K = 12288;   // the W4A16 kernel keeps per-channel tables in LDS
 
 struct SearchLayout {
   size_t ctrl, S, X16, E, partials, total;
@@ -208,7 +209,7 @@ awq_status w4a16_gemm(const uint16_t* A, int64_t M, int64_t N, int64_t K, int32_
                       uint16_t* Y, hipStream_t stream) {
   if (!A || !qweight || !scales16 || !s16 || !Y) return AWQ_ERR_NULL;
   if (group != 128) return AWQ_ERR_CONFIG;
-  if (M < 1 || N < 1 || K < 128 || K % 128 || M > kMaxDim || N > kMaxDim || K > kMaxDim ||
+  if (M < 1 || N < 1 || K < 128 || K % 128 || M > kMaxDim || N > kMaxDim || K > kMaxW4A16K ||
       !aligned16(A) || !aligned16(qweight) || !aligned16(s16))
     return AWQ_ERR_SHAPE;
   return hip_status(awq::launch_w4a16(A, M, N, K, qweight, scales16, s16, Y, stream));

@@ -5,14 +5,25 @@
 // The activation is divided by s because the weight was multiplied by s (AWQ notes,
 // bg51717.github.io/14592, section 方法: Q(w s) x / s).
 //
-// gfx950 design: v_mfma_f32_16x16x32_f16 with the weights as the 16-row A operand (rows n) and
-// the activations as the B operand (columns m). A workgroup owns 16 weight rows and all of K;
-// its 4 waves take the 128-channel groups round-robin (split K), so each lane issues one
-// 16-byte load per group (4 words = 32 codes of one row; 16 lanes x 4 cover 16 rows), the
-// nibbles are unpacked in registers (never materialised in memory), and the four waves' partial
-// outputs are added in a fixed order through LDS. Per group and row the step is one fp16
-// value; code * step and activation / s are each rounded once to fp16 for the MFMA; the
-// accumulation is fp32 and Y is rounded once to fp16.
+// gfx950 design (batch M <= 64 per pass; the bytes of the packed weight dominate, so the kernel
+// is built to stream them at HBM speed):
+//   * v_mfma_f32_16x16x32_f16 with the weights as the 16-row A operand (rows n) and the
+//     activations as the B operand (columns m, zero beyond M);
+//   * a workgroup owns 16 weight rows and all of K; its 8 waves take the 128-channel groups
+//     round-robin, and every lane issues the 16-byte loads of its groups (up to 4 at a time,
+//     double-buffered) before unpacking any of them;
+//   * unpacking: one 32-bit word holds the codes of 8 consecutive channels. x = w ^ 0x88888888
+//     turns each two's-complement nibble into q + 8; (x >> 4j) & 0x000F000F | 0x64006400 is the
+//     fp16 pair (1024 + q_j + 8, 1024 + q_{j+4} + 8) and one packed subtract of 1032 gives
+//     (q_j, q_{j+4}) exactly. The MFMA k slots therefore hold channels in the order
+//     0,4,1,5,2,6,3,7 of each 8; the activations are permuted the same way, which leaves the
+//     dot products unchanged;
+//   * 1/s is folded into the weight pairs (one packed multiply per pair) from a table of
+//     fp16(1/s) that each workgroup builds in LDS, stored in the same permuted order; the
+//     per-group step multiplies the fp32 partial of each group's 4 MFMAs;
+//   * the eight waves' partial outputs are added in a fixed order through LDS.
+// Rounding: 1/s and q/s are each rounded once to fp16, the accumulation is fp32 and Y is rounded
+// once to fp16.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -20,98 +31,224 @@ namespace awq {
 
 namespace {
 constexpr int kRows = 16;       // weight rows per workgroup
-constexpr int kMB = 4;          // 16-column activation blocks per pass (M <= 64 per pass)
+constexpr int kWaves = 8;       // waves per workgroup; wave w takes groups w, w + 8, ...
+constexpr int kThreads = 64 * kWaves;
+constexpr int kChunk = 4;       // groups whose weight words a lane keeps in flight at once
+constexpr int kTableIters = 4;  // table chunks per thread: 4 * 512 * 16 B = 32 KiB
+constexpr int kMaxK = 12288;    // LDS tables + reduction buffer stay below 64 KiB
+constexpr size_t kActLdsBytes = 32768;   // largest M * K * 2 staged as fp16(A / s) in LDS
 }  // namespace
 
-__global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__ A, int64_t M,
-                                                    int64_t N, int64_t K,
-                                                    const uint32_t* __restrict__ qweight,
-                                                    const uint16_t* __restrict__ scales16,
-                                                    const uint16_t* __restrict__ s16,
-                                                    uint16_t* __restrict__ Y, int64_t m0) {
-  __shared__ floatx4 red[4][kMB][64];
+// permuted position of channel t (0..7) inside its block of 8: order 0,4,1,5,2,6,3,7
+__device__ __forceinline__ int perm8(int t) { return ((t & 3) << 1) | (t >> 2); }
+
+// ACT_LDS (small batches, M * K * 2 bytes <= kActLdsBytes): the workgroup first writes
+// fp16(A / s) for all M rows into LDS in the permuted order, and the weights are used as exact
+// integers. Otherwise 1/s is folded into the weight pairs and the activations are read from
+// global memory.
+//
+// Latency structure: a workgroup's critical path is table loads -> table -> weight loads ->
+// unpack/MFMA -> cross-wave sum. The table loads (at most 2 per thread, into registers) are
+// issued first and the weight loads right after them, so both are in flight together (loads
+// complete in order: consuming the table waits only for the table loads); 8 waves split the
+// groups so each unpacks only K/1024 of them.
+template <int MB, bool ACT_LDS>
+__global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restrict__ A, int64_t M,
+                                                         int64_t N, int64_t K,
+                                                         const uint32_t* __restrict__ qweight,
+                                                         const uint16_t* __restrict__ scales16,
+                                                         const uint16_t* __restrict__ s16,
+                                                         uint16_t* __restrict__ Y, int64_t m0) {
+  extern __shared__ __attribute__((aligned(16))) char dyn[];
+  // LDS: [K] fp16 1/s (permuted) or [mrows][K] fp16 A / s (permuted; ACT_LDS), then the 16
+  // rows' fp32 group steps [groups][16], then the cross-wave reduction buffer.
+  const int64_t mrows = ACT_LDS ? (M - m0 < 16 ? M - m0 : 16) : 0;
+  const int64_t table_bytes = ACT_LDS ? mrows * K * 2 : K * 2;
+  uint16_t* table = reinterpret_cast<uint16_t*>(dyn);
+  float* step_lds = reinterpret_cast<float*>(dyn + table_bytes);
+  floatx4* red = reinterpret_cast<floatx4*>(dyn + table_bytes + (K / 128) * kRows * 4);
+  uint4* trash = reinterpret_cast<uint4*>(red + kWaves * MB * 64);   // 16 bytes
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int li = lane & 15;   // weight row within the 16 (A operand) / activation column (B)
-  const int lg = lane >> 4;   // which 32-channel quarter of the 128-channel group
-  const int64_t n = (int64_t)blockIdx.x * kRows + li;
-  const bool nok = n < N;
+  const int li = lane & 15;   // weight row of the A operand / activation column of the B operand
+  const int lg = lane >> 4;   // which 32-channel quarter of a 128-channel group
+  const int64_t n0 = (int64_t)blockIdx.x * kRows;
   const int64_t groups = K / 128;
   const int64_t words_per_row = K / 8;
 
-  floatx4 acc[kMB];
+  // All prologue loads are unconditional (out-of-range indices are clamped and their values
+  // discarded): a load inside a divergent branch makes the compiler wait for it -- and, as loads
+  // complete in order, for every earlier load -- at the branch's join.
+  const int kc = (int)(K / 8);                                  // 16-byte chunks per row
+  const int gr = (int)groups;
+  // ---- 1. table loads into registers (at most kTableIters per thread) ------------------------
+  const int tchunks = ACT_LDS ? (int)mrows * kc : kc;           // 16-byte chunks of the table
+  uint4 ta[kTableIters], ts[kTableIters];
 #pragma unroll
-  for (int b = 0; b < kMB; ++b) acc[b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < kTableIters; ++it) {
+    const int e = tid + it * kThreads;
+    const int ec = e < tchunks ? e : 0;
+    const int k8 = ACT_LDS ? ec % kc : ec;
+    ts[it] = *reinterpret_cast<const uint4*>(s16 + (int64_t)k8 * 8);
+    if (ACT_LDS) ta[it] = *reinterpret_cast<const uint4*>(A + (m0 + ec / kc) * K + (int64_t)k8 * 8);
+  }
+  uint16_t sraw[kTableIters];
+#pragma unroll
+  for (int it = 0; it < kTableIters; ++it) {
+    const int e = tid + it * kThreads;
+    const int ec = e < gr * kRows ? e : 0;
+    const int64_t row = (n0 + (ec & (kRows - 1)) < N) ? n0 + (ec & (kRows - 1)) : N - 1;
+    sraw[it] = scales16[row * groups + (ec >> 4)];
+  }
 
-  for (int64_t g = wave; g < groups; g += 4) {
-    // weights: 4 words = codes of k = 128 g + 32 lg + [0, 32)
-    uint4 wq = make_uint4(0, 0, 0, 0);
-    float sc = 0.0f;
-    if (nok) {
-      wq = *reinterpret_cast<const uint4*>(qweight + n * words_per_row + g * 16 + lg * 4);
-      sc = h2f(scales16[n * groups + g]);
+  __builtin_amdgcn_sched_barrier(0);   // keep the issue order: tables, steps, then weights
+  // ---- 2. this wave's weight words (first chunk) --------------------------------------------
+  const int64_t n = n0 + li;
+  const bool nok = n < N;
+  const uint4* wrow = reinterpret_cast<const uint4*>(qweight + (nok ? n : N - 1) * words_per_row) + lg;
+  const int my_groups = (gr - wave + kWaves - 1) / kWaves;     // g = wave + kWaves i
+  uint4 wbuf[2][kChunk];
+  auto load_chunk = [&](int c, uint4 (&dst)[kChunk]) {
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int i = c * kChunk + u;
+      const int gi = (i < my_groups) ? wave + kWaves * i : wave;
+      dst[u] = wrow[(int64_t)gi * 4];      // rows >= N: a valid row whose results are dropped
     }
-    const uint32_t words[4] = {wq.x, wq.y, wq.z, wq.w};
-    half8_t wf[4];
+  };
+  load_chunk(0, wbuf[0]);
+  // an empty asm that may read or write the weight rows: no weight load above may be moved
+  // below it (sinking them to their first use, after the barrier, would serialise them behind
+  // the table). It names only the row pointer, not the loaded values, so it adds no wait.
+  asm volatile("" : : "v"(wrow) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 3. tables into LDS (straight-line: out-of-range entries go to a trash slot, so no
+  // load above is sunk into a conditional block and waited for there) ------------------------
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+  for (int it = 0; it < kTableIters; ++it) {
+    const int e = tid + it * kThreads;
+    const uint32_t sw[4] = {ts[it].x, ts[it].y, ts[it].z, ts[it].w};
+    uint32_t aw[4] = {0u, 0u, 0u, 0u};
+    if (ACT_LDS) { aw[0] = ta[it].x; aw[1] = ta[it].y; aw[2] = ta[it].z; aw[3] = ta[it].w; }
+    uint16_t h[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int code = ((int)(words[u] << (28 - 4 * t))) >> 28;
-        wf[u][t] = (_Float16)((float)code * sc);
-      }
-    // 1/s for k = 128 g + 32 lg + 8u + t
-    float inv[4][8];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float sv[8];
-      load8_f32<kF16>(s16 + g * 128 + lg * 32 + u * 8, sv);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) inv[u][t] = __builtin_amdgcn_rcpf(sv[t]);
+    for (int t = 0; t < 8; ++t) {
+      const float sv = h2f((uint16_t)(sw[t >> 1] >> (16 * (t & 1))));
+      const float num = ACT_LDS ? h2f((uint16_t)(aw[t >> 1] >> (16 * (t & 1)))) : 1.0f;
+      h[perm8(t)] = f2h(num / sv);
     }
+    uint32_t w[4];
 #pragma unroll
-    for (int b = 0; b < kMB; ++b) {
-      const int64_t m = m0 + b * 16 + li;
-      if (m0 + b * 16 >= M) break;   // uniform: whole block beyond M
-      const bool mok = m < M;
+    for (int p = 0; p < 4; ++p) w[p] = (uint32_t)h[2 * p] | ((uint32_t)h[2 * p + 1] << 16);
+    uint4* dst = (e < tchunks) ? reinterpret_cast<uint4*>(table + e * 8) : trash;
+    *dst = make_uint4(w[0], w[1], w[2], w[3]);
+    const float stv = (n0 + (e & (kRows - 1)) < N) ? h2f(sraw[it]) : 0.0f;
+    float* sdst = (e < gr * kRows) ? step_lds + e : reinterpret_cast<float*>(trash);
+    *sdst = stv;
+  }
+  __syncthreads();
+
+  floatx4 acc[MB];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        half8_t af;
-        if (mok) {
-          float av[8];
-          load8_f32<kF16>(A + m * K + g * 128 + lg * 32 + u * 8, av);
+  for (int b = 0; b < MB; ++b) acc[b] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto process = [&](const uint4 (&cur)[kChunk], int c) {
 #pragma unroll
-          for (int t = 0; t < 8; ++t) af[t] = (_Float16)(av[t] * inv[u][t]);
-        } else {
+    for (int u = 0; u < kChunk; ++u) {
+      const int i = c * kChunk + u;
+      if (i >= my_groups) break;                            // uniform over the wave
+      const int64_t g = wave + kWaves * i;
+      const int64_t kbase = g * 128 + lg * 32;              // this lane's 32 channels
+      const uint32_t words[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
+      half8_t wf[4];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) af[t] = (_Float16)0.0f;
+      for (int v = 0; v < 4; ++v) {                          // word v: channels kbase + 8v ..
+        const uint32_t x = words[v] ^ 0x88888888u;
+        uint32_t invw[4] = {0u, 0u, 0u, 0u};
+        if (!ACT_LDS) {
+          const uint4 inv = *reinterpret_cast<const uint4*>(table + kbase + 8 * v);
+          invw[0] = inv.x; invw[1] = inv.y; invw[2] = inv.z; invw[3] = inv.w;
         }
-        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[u], af, acc[b], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t bits = ((x >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+          half2_t q = __builtin_bit_cast(half2_t, bits) - half2_t{(_Float16)1032.0f, (_Float16)1032.0f};
+          if (!ACT_LDS) q = q * __builtin_bit_cast(half2_t, invw[j]);
+          wf[v][2 * j] = q[0];
+          wf[v][2 * j + 1] = q[1];
+        }
       }
+      // per-group fp32 steps of this lane's 4 output rows (rows 4 lg + r)
+      const floatx4 st = *reinterpret_cast<const floatx4*>(step_lds + g * kRows + 4 * lg);
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        const int64_t m = m0 + b * 16 + li;
+        floatx4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          half8_t af;
+          if (ACT_LDS) {
+            af = (m < M) ? *reinterpret_cast<const half8_t*>(table + (m - m0) * K + kbase + 8 * v)
+                         : half8_t{};
+          } else if (m < M) {
+            const uint4 a = *reinterpret_cast<const uint4*>(A + m * K + kbase + 8 * v);
+            // permute channels 0..7 to the order 0,4,1,5,2,6,3,7 of the weight operand
+            const uint32_t p0 = __builtin_amdgcn_perm(a.z, a.x, 0x05040100u);  // (a0, a4)
+            const uint32_t p1 = __builtin_amdgcn_perm(a.z, a.x, 0x07060302u);  // (a1, a5)
+            const uint32_t p2 = __builtin_amdgcn_perm(a.w, a.y, 0x05040100u);  // (a2, a6)
+            const uint32_t p3 = __builtin_amdgcn_perm(a.w, a.y, 0x07060302u);  // (a3, a7)
+            af = __builtin_bit_cast(half8_t, make_uint4(p0, p1, p2, p3));
+          } else {
+            af = half8_t{};
+          }
+          part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[v], af, part, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[b][r] = __builtin_fmaf(part[r], st[r], acc[b][r]);
+      }
+    }
+  };
+
+  // chunks alternate between the two register buffers (static indices: no scratch)
+  const int nchunks = (my_groups + kChunk - 1) / kChunk;
+  for (int c = 0; c < nchunks; c += 2) {
+    if (c + 1 < nchunks) load_chunk(c + 1, wbuf[1]);
+    process(wbuf[0], c);
+    if (c + 1 < nchunks) {
+      if (c + 2 < nchunks) load_chunk(c + 2, wbuf[0]);
+      process(wbuf[1], c + 1);
     }
   }
+
 #pragma unroll
-  for (int b = 0; b < kMB; ++b) red[wave][b][lane] = acc[b];
+  for (int b = 0; b < MB; ++b) red[(wave * MB + b) * 64 + lane] = acc[b];
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
-    for (int b = 0; b < kMB; ++b) {
-      if (m0 + b * 16 >= M) break;
-      floatx4 t = red[0][b][lane];
+    for (int b = 0; b < MB; ++b) {
+      floatx4 t = red[b * 64 + lane];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) {
-        const floatx4 o = red[w][b][lane];
+      for (int w = 1; w < kWaves; ++w) {
+        const floatx4 o = red[(w * MB + b) * 64 + lane];
         t[0] += o[0]; t[1] += o[1]; t[2] += o[2]; t[3] += o[3];
       }
       // D layout of the 16x16 MFMA: lane holds D[4*(lane/16) + r][lane % 16], r = 0..3,
       // i.e. weight rows 4*lg + r and activation column li.
       const int64_t m = m0 + b * 16 + li;
-      const int64_t nb = (int64_t)blockIdx.x * kRows + 4 * lg;
+      const int64_t nb = n0 + 4 * lg;
       if (m < M) {
+        if (nb + 3 < N && ((N & 3) == 0)) {
+          const uint32_t lo = (uint32_t)f2h(t[0]) | ((uint32_t)f2h(t[1]) << 16);
+          const uint32_t hi = (uint32_t)f2h(t[2]) | ((uint32_t)f2h(t[3]) << 16);
+          *reinterpret_cast<uint2*>(Y + m * N + nb) = make_uint2(lo, hi);
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (nb + r < N) Y[m * N + nb + r] = f2h(t[r]);
+          for (int r = 0; r < 4; ++r)
+            if (nb + r < N) Y[m * N + nb + r] = f2h(t[r]);
+        }
       }
     }
   }
@@ -120,13 +257,30 @@ __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__
 hipError_t launch_w4a16(const uint16_t* A, int64_t M, int64_t N, int64_t K,
                         const uint32_t* qweight, const uint16_t* scales16, const uint16_t* s16,
                         uint16_t* Y, hipStream_t stream) {
+  if (K > kMaxK) return hipErrorInvalidValue;
   const unsigned blocks = (unsigned)((N + kRows - 1) / kRows);
-  for (int64_t m0 = 0; m0 < M; m0 += 16 * kMB) {
-    w4a16_kernel<<<blocks, 256, 0, stream>>>(A, M, N, K, qweight, scales16, s16, Y, m0);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  const size_t steps_bytes = (size_t)(K / 128) * kRows * 4;
+  hipError_t e = hipSuccess;
+  for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += 64) {
+    const int64_t rest = M - m0;
+    if (rest <= 16 && (size_t)rest * K * 2 <= kActLdsBytes) {
+      const size_t lds = (size_t)rest * K * 2 + steps_bytes + kWaves * 1 * 64 * 16 + 16;
+      w4a16_kernel<1, true><<<blocks, kThreads, lds, stream>>>(A, M, N, K, qweight, scales16, s16, Y, m0);
+    } else {
+      const size_t base = (size_t)K * 2 + steps_bytes;
+      if (rest <= 16)
+        w4a16_kernel<1, false><<<blocks, kThreads, base + kWaves * 1 * 64 * 16 + 16, stream>>>(
+            A, M, N, K, qweight, scales16, s16, Y, m0);
+      else if (rest <= 32)
+        w4a16_kernel<2, false><<<blocks, kThreads, base + kWaves * 2 * 64 * 16 + 16, stream>>>(
+            A, M, N, K, qweight, scales16, s16, Y, m0);
+      else
+        w4a16_kernel<4, false><<<blocks, kThreads, base + kWaves * 4 * 64 * 16 + 16, stream>>>(
+            A, M, N, K, qweight, scales16, s16, Y, m0);
+    }
+    e = hipGetLastError();
   }
-  return hipSuccess;
+  return e;
 }
 
 }  // namespace awq
