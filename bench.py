@@ -42,7 +42,60 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-w4a16-sweep", action="store_true")
+    ap.add_argument("--mode", choices=("bench", "traffic"), default="bench",
+                    help="traffic: one 1 GiB device copy (counter calibration) and one pass of "
+                         "the path, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
     return ap.parse_args()
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "lossgemm_c2_traffic.json")
+LOSS_SRC = os.path.join(ROOT, "post_weight_quantization_channel_amd", "csrc", "lossgemm.hip")
+
+
+def source_digest(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per loss-kernel launch from the committed counter record, or None when the
+    kernel source has changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("lossgemm_src_sha256_16") != source_digest(LOSS_SRC):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def traffic_pass():
+    """Counter workload: a plain device copy of known size, then one pass of the path on a
+    layer of the benchmarked shape (values drawn on the device; traffic does not depend on
+    them)."""
+    import torch
+    import post_weight_quantization_channel_amd as awq
+    dev = torch.device("cuda:0")
+    src = torch.ones(1 << 29, dtype=torch.float16, device=dev)      # 1 GiB
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy of", src.numel() * 2, "bytes done")
+    del src, dst
+    g = torch.Generator(device=dev).manual_seed(0)
+    W = (0.02 * torch.randn(N_, K_, device=dev, generator=g)).half()
+    X = (torch.randn(M_, K_, device=dev, generator=g) *
+         torch.exp(torch.randn(K_, device=dev, generator=g))).half()
+    cfg = awq.AwqConfig(n_grid=N_GRID)
+    sx, flags = awq.act_stats(X)
+    res = awq.search_layer(W, X, sx, cfg, flags=flags)
+    p = awq.pack_int4(W, res.s_best, cfg, flags=flags)
+    awq.w4a16_gemm(torch.ones(1, K_, dtype=torch.float16, device=dev), p.qweight, p.scales16,
+                   p.s16)
+    torch.cuda.synchronize()
+    log("path pass done; alpha*", int(res.best.item()))
 
 
 def log(*a):
@@ -141,6 +194,9 @@ def cpu_baseline(L, n_grid):
 # ---------------------------------------------------------------------------------------------
 def main():
     args = parse()
+    if args.mode == "traffic":
+        traffic_pass()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
               "(the search shards by layer or by output rows with one small exchange; see the "
@@ -215,7 +271,7 @@ def main():
     achieved = flops / (loss_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": "lossgemm_kernel", "achieved": round(achieved, 1),
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
                 "flops_per_launch": flops, "launch_ms": round(loss_ms, 4)}
 
     other = {
