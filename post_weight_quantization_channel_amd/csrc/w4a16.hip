@@ -254,12 +254,195 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restr
   }
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// Larger batches (M > 64): a tiled MFMA GEMM. Workgroup tile 128 (batch rows m) x 64 (weight
+// rows n), BK = 128 = one quantization group per K step, 4 waves of 64 x 32 (2 x 2), each a
+// 4 x 2 grid of v_mfma_f32_16x16x32_f16 blocks (weights as the A operand, activations as B).
+// The workgroup first builds a table of fp16(1/s) for all K in LDS. Per K step every thread
+// loads 128 bytes of the activation tile, one 16-byte word group of the packed weight tile and
+// its row's step into registers (the next step is prefetched while the current one computes),
+// unpacks its 32 codes into fp16 q * (fp16(step) * fp16(1/s)) in natural channel order (two
+// packed multiplies per channel pair) and writes both tiles to LDS (double-buffered). The weight
+// tile is unpacked once per 128-row batch tile, not once per batch row. LDS rows are 256 bytes; 16-byte chunks are XOR-swizzled by (row & 15) so the
+// fragment reads of 16 consecutive rows touch distinct banks.
+namespace {
+constexpr int TBM = 128, TBN = 64, TBK = 128;
+constexpr int kTileStage = (TBM + TBN) * TBK * 2;   // 48 KiB
+__device__ __forceinline__ int tswz(int row, int chunk) {   // byte offset inside a 256-byte row
+  return row * (TBK * 2) + ((chunk ^ (row & 15)) << 4);
+}
+}  // namespace
+
+__global__ __launch_bounds__(256) void w4a16_tiled_kernel(const uint16_t* __restrict__ A,
+                                                          int64_t M, int64_t N, int64_t K,
+                                                          const uint32_t* __restrict__ qweight,
+                                                          const uint16_t* __restrict__ scales16,
+                                                          const uint16_t* __restrict__ s16,
+                                                          uint16_t* __restrict__ Y) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kTileStage];
+  __shared__ __attribute__((aligned(16))) uint16_t inv_s[kMaxK];   // fp16(1/s), natural order
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;     // wave tile: batch rows 64 wm.., weight rows 32 wn..
+  const int64_t tilesN = (N + TBN - 1) / TBN;
+  const int64_t m0 = (int64_t)(blockIdx.x / tilesN) * TBM;
+  const int64_t n0 = (int64_t)(blockIdx.x % tilesN) * TBN;
+  const int64_t groups = K / 128;
+
+  // activation tile: thread t loads rows (t / 16) + 16 j (j = 0..7), 16-byte chunk t % 16
+  const int arow = tid >> 4, achunk = tid & 15;
+  // weight tile: thread t loads row t / 4, words 4 (t % 4) .. 4 (t % 4) + 3 of the group
+  const int wrow_l = tid >> 2, wq = tid & 3;
+  const int64_t wn_row = n0 + wrow_l;
+  const bool wok = wn_row < N;
+  const uint4* wsrc = reinterpret_cast<const uint4*>(qweight + (wok ? wn_row : 0) * (K / 8)) + wq;
+
+  constexpr int kARows = TBM / 16;   // activation rows per thread per step
+  for (int64_t k8 = tid; k8 < K / 8; k8 += 256) {
+    float sv[8];
+    load8_f32<kF16>(s16 + k8 * 8, sv);
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      w[p] = (uint32_t)f2h(1.0f / sv[2 * p]) | ((uint32_t)f2h(1.0f / sv[2 * p + 1]) << 16);
+    *reinterpret_cast<uint4*>(inv_s + k8 * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  __syncthreads();
+
+  struct Regs {
+    uint4 a[kARows];
+    uint4 w;
+    uint16_t step;
+  };
+  auto gload = [&](int64_t g, Regs& R) {
+#pragma unroll
+    for (int j = 0; j < kARows; ++j) {
+      const int64_t m = m0 + arow + 16 * j;
+      R.a[j] = (m < M) ? *reinterpret_cast<const uint4*>(A + m * K + g * 128 + achunk * 8)
+                       : make_uint4(0, 0, 0, 0);
+    }
+    R.w = wok ? wsrc[g * 4] : make_uint4(0, 0, 0, 0);
+    R.step = wok ? scales16[wn_row * groups + g] : (uint16_t)0;
+  };
+  auto lstore = [&](int stage, int64_t g, const Regs& R) {
+    char* sa = smem + stage * kTileStage;
+    char* sw = sa + TBM * TBK * 2;
+#pragma unroll
+    for (int j = 0; j < kARows; ++j)
+      *reinterpret_cast<uint4*>(sa + tswz(arow + 16 * j, achunk)) = R.a[j];
+    // unpack 4 words = 32 channels k = 128 g + 32 wq + 8 v + t into q * (step * 1/s) in fp16
+    const _Float16 sth = __builtin_bit_cast(_Float16, R.step);
+    const half2_t st2 = half2_t{sth, sth};
+    const uint32_t words[4] = {R.w.x, R.w.y, R.w.z, R.w.w};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint4 iv = *reinterpret_cast<const uint4*>(inv_s + g * 128 + wq * 32 + v * 8);
+      // (1/s) pairs (j, j + 4) to match the unpack order
+      const uint32_t i04 = __builtin_amdgcn_perm(iv.z, iv.x, 0x05040100u);
+      const uint32_t i15 = __builtin_amdgcn_perm(iv.z, iv.x, 0x07060302u);
+      const uint32_t i26 = __builtin_amdgcn_perm(iv.w, iv.y, 0x05040100u);
+      const uint32_t i37 = __builtin_amdgcn_perm(iv.w, iv.y, 0x07060302u);
+      const uint32_t invp[4] = {i04, i15, i26, i37};
+      const uint32_t x = words[v] ^ 0x88888888u;
+      uint32_t pr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t bits = ((x >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+        const half2_t q = __builtin_bit_cast(half2_t, bits) -
+                          half2_t{(_Float16)1032.0f, (_Float16)1032.0f};
+        const half2_t c = st2 * __builtin_bit_cast(half2_t, invp[j]);
+        pr[j] = __builtin_bit_cast(uint32_t, q * c);              // channels (j, j + 4)
+      }
+      // back to natural order: (0,1) (2,3) (4,5) (6,7)
+      const uint32_t n01 = __builtin_amdgcn_perm(pr[1], pr[0], 0x05040100u);
+      const uint32_t n23 = __builtin_amdgcn_perm(pr[3], pr[2], 0x05040100u);
+      const uint32_t n45 = __builtin_amdgcn_perm(pr[1], pr[0], 0x07060302u);
+      const uint32_t n67 = __builtin_amdgcn_perm(pr[3], pr[2], 0x07060302u);
+      *reinterpret_cast<uint4*>(sw + tswz(wrow_l, wq * 4 + v)) = make_uint4(n01, n23, n45, n67);
+    }
+  };
+
+  floatx4 acc[2][4];   // [weight block i][batch block j]
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int li = lane & 15, lg = lane >> 4;
+  auto compute = [&](int stage) {
+    const char* sa = smem + stage * kTileStage;
+    const char* sw = sa + TBM * TBK * 2;
+#pragma unroll
+    for (int kk = 0; kk < TBK / 32; ++kk) {
+      const int chunk = kk * 4 + lg;         // this lane's 8 channels of the 32-wide slice
+      half8_t wf[2], af[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        wf[i] = *reinterpret_cast<const half8_t*>(sw + tswz(wn * 32 + i * 16 + li, chunk));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        af[j] = *reinterpret_cast<const half8_t*>(sa + tswz(wm * 64 + j * 16 + li, chunk));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[i], af[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Two register sets: the loads of step g + 2 are issued while step g computes, so each load
+  // has two steps of MFMA work to land before its tile is written to LDS.
+  Regs R0, R1;
+  gload(0, R0);
+  if (groups > 1) gload(1, R1);
+  lstore(0, 0, R0);
+  __syncthreads();
+  for (int64_t g = 0; g < groups; g += 2) {
+    if (g + 2 < groups) gload(g + 2, R0);
+    compute(0);
+    if (g + 1 < groups) lstore(1, g + 1, R1);
+    __syncthreads();
+    if (g + 1 >= groups) break;
+    if (g + 3 < groups) gload(g + 3, R1);
+    compute(1);
+    if (g + 2 < groups) lstore(0, g + 2, R0);
+    __syncthreads();
+  }
+  // D layout of the 16x16 MFMA: lane holds D[4 (lane / 16) + r][lane % 16] -> weight rows
+  // 4 lg + r of block i, batch row li of block j.
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t m = m0 + wm * 64 + j * 16 + li;
+      const int64_t nb = n0 + wn * 32 + i * 16 + 4 * lg;
+      if (m < M) {
+        if (nb + 3 < N && ((N & 3) == 0)) {
+          const uint32_t lo = (uint32_t)f2h(acc[i][j][0]) | ((uint32_t)f2h(acc[i][j][1]) << 16);
+          const uint32_t hi = (uint32_t)f2h(acc[i][j][2]) | ((uint32_t)f2h(acc[i][j][3]) << 16);
+          *reinterpret_cast<uint2*>(Y + m * N + nb) = make_uint2(lo, hi);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (nb + r < N) Y[m * N + nb + r] = f2h(acc[i][j][r]);
+        }
+      }
+    }
+}
+
 hipError_t launch_w4a16(const uint16_t* A, int64_t M, int64_t N, int64_t K,
                         const uint32_t* qweight, const uint16_t* scales16, const uint16_t* s16,
                         uint16_t* Y, hipStream_t stream) {
   if (K > kMaxK) return hipErrorInvalidValue;
   const unsigned blocks = (unsigned)((N + kRows - 1) / kRows);
   const size_t steps_bytes = (size_t)(K / 128) * kRows * 4;
+  if (M > 64) {
+    const int64_t tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
+    w4a16_tiled_kernel<<<(unsigned)tiles, 256, 0, stream>>>(A, M, N, K, qweight, scales16, s16, Y);
+    return hipGetLastError();
+  }
   hipError_t e = hipSuccess;
   for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += 64) {
     const int64_t rest = M - m0;
