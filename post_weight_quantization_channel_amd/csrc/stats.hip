@@ -6,8 +6,9 @@
 //
 // HBM-bound column reduction. Pass 1: each thread owns 8 consecutive columns (one 16-byte load
 // per row for 16-bit inputs) and sums |x| over a chunk of 256 rows in fp64; a 64-lane wave reads
-// 1 KiB of a row contiguously. Pass 2 adds the chunk partials of each column in ascending chunk
-// order and divides by M in fp64 before the single rounding to fp32. For fp16 inputs every
+// 1 KiB of a row contiguously. Pass 2 adds the chunk partials of each column in a fixed order
+// (eight interleaved slices per column, combined in slice order) and divides by M in fp64 before
+// the single rounding to fp32, so a run is reproducible bit for bit. For fp16 inputs every
 // partial sum is exact (all |x| are multiples of 2^-24 and the sums stay below 2^29, which is
 // checked), so the result does not depend on the reduction order at all.
 #include "device_common.h"
@@ -50,15 +51,34 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(const void* __restri
   for (int t = 0; t < 8; ++t) out[t] = acc[t];
 }
 
+// Pass 2: a workgroup owns 32 columns; its 256 threads are (column c = t % 32, slice
+// j = t / 32): slice j adds the chunks j, j + 8, j + 16, ... of its column with four independent
+// accumulators (fixed assignment), then the 8 slices are added in slice order through LDS.
 __global__ __launch_bounds__(256) void stats_final_kernel(const double* __restrict__ partials,
                                                           int64_t chunks, int64_t M, int64_t K,
                                                           int dtype, float* __restrict__ sx,
                                                           uint32_t* __restrict__ flags) {
-  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  bool bad = false, inexact = false;
+  __shared__ double part[8][32];
+  const int c = threadIdx.x & 31, j = threadIdx.x >> 5;
+  const int64_t k = (int64_t)blockIdx.x * 32 + c;
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
   if (k < K) {
-    double S = 0.0;
-    for (int64_t c = 0; c < chunks; ++c) S += partials[c * K + k];
+    int64_t ch = j;
+    for (; ch + 24 < chunks; ch += 32) {
+      a0 += partials[ch * K + k];
+      a1 += partials[(ch + 8) * K + k];
+      a2 += partials[(ch + 16) * K + k];
+      a3 += partials[(ch + 24) * K + k];
+    }
+    for (; ch < chunks; ch += 8) a0 += partials[ch * K + k];
+  }
+  part[j][c] = (a0 + a1) + (a2 + a3);
+  __syncthreads();
+  bool bad = false, inexact = false;
+  if (j == 0 && k < K) {
+    double S = part[0][c];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) S += part[q][c];
     bad = !isfinite(S);
     inexact = (dtype == kF16) && (S >= 0x1p29);
     sx[k] = (float)(S / (double)M);
@@ -86,8 +106,8 @@ hipError_t launch_stats(const void* X, int dtype, int64_t M, int64_t K, int64_t 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  stats_final_kernel<<<(unsigned)((K + 255) / 256), 256, 0, stream>>>(partials, chunks, M, K,
-                                                                       dtype, sx, flags);
+  stats_final_kernel<<<(unsigned)((K + 31) / 32), 256, 0, stream>>>(partials, chunks, M, K,
+                                                                     dtype, sx, flags);
   return hipGetLastError();
 }
 
