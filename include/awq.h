@@ -50,7 +50,7 @@ typedef enum {
   AWQ_ERR_SHAPE = 2,      /* M, N or K out of range, K % group != 0, ldx < K, misalignment */
   AWQ_ERR_DTYPE = 3,      /* dtype not accepted by this call                               */
   AWQ_ERR_CONFIG = 4,     /* bits not in {3,4}, group != 128, n_grid not in [2,64],        */
-                          /* s_floor not a positive finite number                          */
+                          /* s_floor not a positive finite number, unknown form            */
   AWQ_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than the *_workspace_bytes query    */
   AWQ_ERR_HIP = 6         /* a kernel launch reported an error                             */
 } awq_status;
@@ -71,11 +71,21 @@ enum {
   AWQ_FLAG_STEP_UNDERFLOW = 1u << 7    /* a group with max|w s| > 0 got step 0 (codes set to 0)*/
 };
 
+/* How awq_search_layer evaluates the loss (same value, different contraction):
+ *   AWQ_FORM_DIRECT  ||X E_i^T||_F^2 as one fp16 GEMM of X [M,K] with the n_grid error matrices
+ *                    (2 M N K n_grid flops);
+ *   AWQ_FORM_GRAM    H = X^T X once (about M K^2 flops), then sum_n E_i,n H E_i,n^T for each
+ *                    grid point (about N K^2 flops each): the quadratic form the GPTQ section of
+ *                    "一文搞懂大模型量化技术：GGUF、GPTQ、AWQ" builds on. Needs K <= 32768 and
+ *                    M <= 2^23 - 128. */
+enum { AWQ_FORM_DIRECT = 0, AWQ_FORM_GRAM = 1 };
+
 typedef struct {
   int32_t bits;    /* 4 (codes [-8,7]) or 3 (codes [-4,3]); the step is max|w s|/(2^(bits-1)-1) */
   int32_t group;   /* input channels per step; 128 is the only accepted value                  */
   int32_t n_grid;  /* number of alpha points, alpha_i = i/(n_grid-1), 2 <= n_grid <= 64         */
   float s_floor;   /* s = max(s_X, s_floor)^alpha, typically 1e-5f                              */
+  int32_t form;    /* AWQ_FORM_DIRECT or AWQ_FORM_GRAM                                          */
 } awq_cfg;
 
 /* Human-readable name of a status code (static storage). */
@@ -114,12 +124,16 @@ awq_status awq_act_stats(const void* X, awq_dtype xdt, int64_t M, int64_t K, int
  *   Delta = fp32(max_group |fp32(w s_i)| / (2^(b-1)-1)) per (row, group of 128), all in IEEE
  *   fp32 with round-to-nearest-even (bit-identical to the specification);
  *   L_i = ||X E_i^T||_F^2 / (M N), E_i = q Delta / s_i - W, contracted on fp16 operands with
- *   fp32 accumulation and fp64 reduction (relative error ~1e-5).
+ *   fp32 accumulation and fp64 reduction (relative error ~1e-5). In the Gram form the fp16
+ *   operands are the correlation matrix D^-1 H D^-1 (D = diag(sqrt(H_kk))) and E_i D; H itself
+ *   is accumulated in fp32 over token chunks and summed in fp64.
  * losses out, fp64 [n_grid]; best out, int32 [1] = i*; s_best out, fp32 [K] = s_{i*}.
  * flags  in/out: NONFINITE_W, X_F16_RANGE, NONFINITE_LOSS.
  * ws     device workspace of at least awq_search_workspace_bytes(M, N, K, xdt, cfg) bytes
- *        (dominated by the n_grid * N * K fp16 error stack).
- * Errors: as for awq_act_stats, plus AWQ_ERR_CONFIG for an invalid cfg.
+ *        (dominated by the n_grid * N * K fp16 error stack; the Gram form adds K * K fp16 and
+ *        shares the stack's memory with the transposed X and the partial sums of H).
+ * Errors: as for awq_act_stats, plus AWQ_ERR_CONFIG for an invalid cfg (bits, group, n_grid,
+ *         s_floor or form) and AWQ_ERR_SHAPE for the Gram form's K and M limits.
  * ---------------------------------------------------------------------------------------- */
 size_t awq_search_workspace_bytes(int64_t M, int64_t N, int64_t K, awq_dtype xdt,
                                   const awq_cfg* cfg);
@@ -133,12 +147,14 @@ awq_status awq_search_layer(const void* W, awq_dtype wdt, int64_t N, int64_t K,
  * measured with HIP events recorded between the launches on `stream`. Unlike every other call
  * it BLOCKS the host until the stream has finished the search (it reads the events back).
  * stage_ms  host array of AWQ_SEARCH_STAGES floats (milliseconds), in the order
- *           scale table, max|W|, X to fp16 (0 when X is fp16), quantize + error stack,
- *           loss contraction, finalize.
+ *           scale table; X preparation (direct: X to fp16, 0 when X is fp16; Gram: transpose
+ *           to fp16 X^T); X^T X (0 in the direct form); d and the correlation operand (0 in
+ *           the direct form); max|W| (Gram: max|W d|); quantize + error stack; loss
+ *           contraction; finalize.
  * Errors: as awq_search_layer; AWQ_ERR_NULL when stage_ms is NULL; AWQ_ERR_HIP when an event
  *         call fails.
  * ---------------------------------------------------------------------------------------- */
-#define AWQ_SEARCH_STAGES 6
+#define AWQ_SEARCH_STAGES 8
 awq_status awq_search_layer_profiled(const void* W, awq_dtype wdt, int64_t N, int64_t K,
                                      const void* X, awq_dtype xdt, int64_t M, const float* sx,
                                      const awq_cfg* cfg, double* losses, int32_t* best,

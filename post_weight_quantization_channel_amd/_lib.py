@@ -14,8 +14,11 @@ AWQ_OK, AWQ_ERR_NULL, AWQ_ERR_SHAPE, AWQ_ERR_DTYPE, AWQ_ERR_CONFIG, AWQ_ERR_WORK
     AWQ_ERR_HIP = range(7)
 AWQ_F32, AWQ_F16, AWQ_BF16 = 0, 1, 2
 
-SEARCH_STAGES = ("scale_table", "absmax_w", "x_to_f16", "quantize_stack", "lossgemm",
-                 "finalize")
+AWQ_FORM_DIRECT, AWQ_FORM_GRAM = 0, 1
+
+# stage order of awq_search_layer_profiled (the Gram-only stages read 0 in the direct form)
+SEARCH_STAGES = ("scale_table", "x_prep", "gram_gemm", "gram_finish", "absmax_w",
+                 "quantize_stack", "loss", "finalize")
 
 FLAG_NONFINITE_X = 1 << 0
 FLAG_NONFINITE_W = 1 << 1
@@ -29,7 +32,7 @@ FLAG_STEP_UNDERFLOW = 1 << 7
 
 class AwqCfg(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32),
-                ("n_grid", ctypes.c_int32), ("s_floor", ctypes.c_float)]
+                ("n_grid", ctypes.c_int32), ("s_floor", ctypes.c_float), ("form", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p

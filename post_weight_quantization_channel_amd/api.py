@@ -20,14 +20,19 @@ _DT = {torch.float32: _lib.AWQ_F32, torch.float16: _lib.AWQ_F16, torch.bfloat16:
 @dataclasses.dataclass(frozen=True)
 class AwqConfig:
     """bits in {3, 4}; group = 128 input channels per step; n_grid alpha points i/(n_grid-1);
-    s = max(s_X, s_floor)^alpha."""
+    s = max(s_X, s_floor)^alpha; form "direct" (contract X with every error matrix) or "gram"
+    (form H = X^T X once, then contract each error matrix with H)."""
     bits: int = 4
     group: int = 128
     n_grid: int = 20
     s_floor: float = 1e-5
+    form: str = "direct"
 
     def c(self) -> AwqCfg:
-        return AwqCfg(self.bits, self.group, self.n_grid, self.s_floor)
+        forms = {"direct": _lib.AWQ_FORM_DIRECT, "gram": _lib.AWQ_FORM_GRAM}
+        if self.form not in forms:
+            raise ValueError(f"form must be one of {sorted(forms)}, got {self.form!r}")
+        return AwqCfg(self.bits, self.group, self.n_grid, self.s_floor, forms[self.form])
 
 
 def _dev(t: torch.Tensor, name: str) -> torch.Tensor:

@@ -21,6 +21,7 @@ awq_status check_cfg(const awq_cfg* cfg) {
   if (cfg->group != 128) return AWQ_ERR_CONFIG;
   if (cfg->n_grid < 2 || cfg->n_grid > 64) return AWQ_ERR_CONFIG;
   if (!(cfg->s_floor > 0.0f) || !isfinite(cfg->s_floor)) return AWQ_ERR_CONFIG;
+  if (cfg->form != AWQ_FORM_DIRECT && cfg->form != AWQ_FORM_GRAM) return AWQ_ERR_CONFIG;
   return AWQ_OK;
 }
 
@@ -28,28 +29,59 @@ awq_status check_cfg(const awq_cfg* cfg) {
 constexpr int64_t kMaxDim = int64_t(1) << 24;
 constexpr int64_t kMaxSearchK = int64_t(1) << 22;
 constexpr int64_t kMaxW4A16K = 12288;   // the W4A16 kernel keeps per-channel tables in LDS
+// Gram form: the K x K operand is stored (2 GiB at K = 32768); 256 rows of the transposed X
+// must fit a 32-bit buffer range.
+constexpr int64_t kMaxGramK = 32768;
+constexpr int64_t kMaxGramMp = (int64_t(1) << 23) - awq::kGramMAlign;
 
 struct SearchLayout {
   size_t ctrl, S, X16, E, partials, total;
+  size_t d64, d32, B, Xt, Hpart;   // Gram form only (Xt and Hpart share memory with E)
   int64_t tiles_per_alpha;
+  awq::GramPlan plan;
 };
 
-SearchLayout search_layout(int64_t M, int64_t N, int64_t K, awq_dtype xdt, int n_grid) {
+// Direct form: ctrl | S | X16 (non-fp16 X) | E stack | partials.
+// Gram form:   ctrl | S | d64 | d32 | B | partials | union(Xt + Hpart, E stack); Xt and the H
+//              partials are dead before the error stack is written.
+SearchLayout search_layout(int64_t M, int64_t N, int64_t K, awq_dtype xdt, int n_grid,
+                           int form) {
   SearchLayout L{};
-  const int64_t tilesM = (M + awq::kLossBM - 1) / awq::kLossBM;
   const int64_t tilesN = (N + awq::kLossBN - 1) / awq::kLossBN;
-  L.tiles_per_alpha = tilesM * tilesN;
   size_t off = 0;
   L.ctrl = off;
   off += align_up(sizeof(awq::SearchCtrl));
   L.S = off;
   off += align_up((size_t)n_grid * (size_t)K * sizeof(float));
-  L.X16 = off;
-  if (xdt != AWQ_F16) off += align_up((size_t)M * (size_t)K * 2);
-  L.E = off;
-  off += align_up((size_t)n_grid * (size_t)N * (size_t)K * 2);
-  L.partials = off;
-  off += align_up((size_t)n_grid * (size_t)L.tiles_per_alpha * sizeof(double));
+  const size_t e_bytes = align_up((size_t)n_grid * (size_t)N * (size_t)K * 2);
+  if (form == AWQ_FORM_GRAM) {
+    L.plan = awq::gram_plan(M, K);
+    L.tiles_per_alpha = tilesN * L.plan.t;
+    L.d64 = off;
+    off += align_up((size_t)K * sizeof(double));
+    L.d32 = off;
+    off += align_up((size_t)K * sizeof(float));
+    L.B = off;
+    off += align_up((size_t)K * (size_t)K * 2);
+    L.partials = off;
+    off += align_up((size_t)n_grid * (size_t)L.tiles_per_alpha * sizeof(double));
+    const size_t xt_bytes = align_up((size_t)K * (size_t)L.plan.Mp * 2);
+    const size_t h_bytes = align_up((size_t)L.plan.S * (size_t)L.plan.T *
+                                    (size_t)(awq::kLossBM * awq::kLossBN) * sizeof(float));
+    L.Xt = off;
+    L.Hpart = off + xt_bytes;
+    L.E = off;
+    off += (xt_bytes + h_bytes > e_bytes) ? xt_bytes + h_bytes : e_bytes;
+  } else {
+    const int64_t tilesM = (M + awq::kLossBM - 1) / awq::kLossBM;
+    L.tiles_per_alpha = tilesM * tilesN;
+    L.X16 = off;
+    if (xdt != AWQ_F16) off += align_up((size_t)M * (size_t)K * 2);
+    L.E = off;
+    off += e_bytes;
+    L.partials = off;
+    off += align_up((size_t)n_grid * (size_t)L.tiles_per_alpha * sizeof(double));
+  }
   L.total = off;
   return L;
 }
@@ -73,7 +105,7 @@ const char* awq_status_string(awq_status status) {
   return "unknown awq_status";
 }
 
-int32_t awq_version(void) { return 10000; }
+int32_t awq_version(void) { return 10100; }
 
 size_t awq_act_stats_workspace_bytes(int64_t M, int64_t K) {
   if (M < 1 || K < 1 || M > kMaxDim || K > kMaxDim) return 0;
@@ -93,11 +125,27 @@ awq_status awq_act_stats(const void* X, awq_dtype xdt, int64_t M, int64_t K, int
                                       static_cast<double*>(ws), stream));
 }
 
+namespace {
+
+// Shape rules of awq_search_layer beyond the per-dimension limits.
+bool search_shape_ok(int64_t M, int64_t N, int64_t K, const awq_cfg* cfg) {
+  if (M < 1 || N < 1 || K < cfg->group || K % cfg->group || M > kMaxDim || N > kMaxDim ||
+      K > kMaxSearchK)
+    return false;
+  if (cfg->form == AWQ_FORM_GRAM) {
+    const int64_t Mp = (M + awq::kGramMAlign - 1) / awq::kGramMAlign * awq::kGramMAlign;
+    if (K > kMaxGramK || Mp > kMaxGramMp) return false;
+  }
+  return true;
+}
+
+}  // namespace
+
 size_t awq_search_workspace_bytes(int64_t M, int64_t N, int64_t K, awq_dtype xdt,
                                   const awq_cfg* cfg) {
   if (check_cfg(cfg) != AWQ_OK || !valid_dtype(xdt)) return 0;
-  if (M < 1 || N < 1 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
-  return search_layout(M, N, K, xdt, cfg->n_grid).total;
+  if (!search_shape_ok(M, N, K, cfg)) return 0;
+  return search_layout(M, N, K, xdt, cfg->n_grid, cfg->form).total;
 }
 
 namespace {
@@ -114,10 +162,8 @@ awq_status search_impl(const void* W, awq_dtype wdt, int64_t N, int64_t K, const
   if (wdt != AWQ_F16 && wdt != AWQ_F32) return AWQ_ERR_DTYPE;
   if (!valid_dtype(xdt)) return AWQ_ERR_DTYPE;
   // K <= 2^22 keeps the loss kernel's 32-bit buffer offsets (256 rows x 2K bytes) in range
-  if (M < 1 || N < 1 || K < cfg->group || K % cfg->group || M > kMaxDim || N > kMaxDim ||
-      K > kMaxSearchK || !aligned16(W) || !aligned16(X))
-    return AWQ_ERR_SHAPE;
-  const SearchLayout L = search_layout(M, N, K, xdt, cfg->n_grid);
+  if (!search_shape_ok(M, N, K, cfg) || !aligned16(W) || !aligned16(X)) return AWQ_ERR_SHAPE;
+  const SearchLayout L = search_layout(M, N, K, xdt, cfg->n_grid, cfg->form);
   if ((int64_t)L.tiles_per_alpha * cfg->n_grid > (int64_t(1) << 31) - 1) return AWQ_ERR_SHAPE;
   if (!ws || ws_bytes < L.total || !aligned16(ws)) return AWQ_ERR_WORKSPACE;
 
@@ -126,6 +172,9 @@ awq_status search_impl(const void* W, awq_dtype wdt, int64_t N, int64_t K, const
   auto* S = reinterpret_cast<float*>(base + L.S);
   auto* E = reinterpret_cast<uint16_t*>(base + L.E);
   auto* partials = reinterpret_cast<double*>(base + L.partials);
+  const bool gram = cfg->form == AWQ_FORM_GRAM;
+  const float* dcol = gram ? reinterpret_cast<const float*>(base + L.d32) : nullptr;
+  const uint16_t* B = reinterpret_cast<const uint16_t*>(base + L.B);
   const uint16_t* X16 = static_cast<const uint16_t*>(X);
 
   hipError_t e = hipSuccess;
@@ -136,24 +185,43 @@ awq_status search_impl(const void* W, awq_dtype wdt, int64_t N, int64_t K, const
   if (e == hipSuccess)
     e = awq::launch_search_prep(sx, (int)K, cfg->n_grid, cfg->s_floor, S, ctrl, stream);
   mark(1);
-  if (e == hipSuccess) e = awq::launch_absmax(W, (int)wdt, N * K, ctrl, flags, stream);
-  mark(2);
-  if (e == hipSuccess && xdt != AWQ_F16) {
-    auto* x16 = reinterpret_cast<uint16_t*>(base + L.X16);
-    e = awq::launch_x_to_f16(X, (int)xdt, M * K, x16, flags, stream);
-    X16 = x16;
+  if (gram) {
+    // records ev[2] after the transpose and ev[3] after the X^T X partials
+    if (e == hipSuccess)
+      e = awq::launch_gram_prepare(X, (int)xdt, M, K, L.plan,
+                                   reinterpret_cast<uint16_t*>(base + L.Xt),
+                                   reinterpret_cast<float*>(base + L.Hpart),
+                                   reinterpret_cast<double*>(base + L.d64),
+                                   reinterpret_cast<float*>(base + L.d32),
+                                   reinterpret_cast<uint16_t*>(base + L.B), flags, stream,
+                                   ev ? ev + 2 : nullptr);
+  } else {
+    if (e == hipSuccess && xdt != AWQ_F16) {
+      auto* x16 = reinterpret_cast<uint16_t*>(base + L.X16);
+      e = awq::launch_x_to_f16(X, (int)xdt, M * K, x16, flags, stream);
+      X16 = x16;
+    }
+    mark(2);
+    mark(3);
   }
-  mark(3);
-  if (e == hipSuccess)
-    e = awq::launch_quantize_stack(W, (int)wdt, N, K, S, cfg->n_grid, cfg->bits, ctrl, E, flags,
-                                   stream);
   mark(4);
-  if (e == hipSuccess) e = awq::launch_lossgemm(X16, M, K, E, N, cfg->n_grid, partials, stream);
+  if (e == hipSuccess) e = awq::launch_absmax(W, (int)wdt, N, K, dcol, ctrl, flags, stream);
   mark(5);
+  if (e == hipSuccess)
+    e = awq::launch_quantize_stack(W, (int)wdt, N, K, S, cfg->n_grid, cfg->bits, dcol, ctrl, E,
+                                   flags, stream);
+  mark(6);
+  if (e == hipSuccess) {
+    if (gram)
+      e = awq::launch_gram_loss(E, N, K, B, cfg->n_grid, partials, stream);
+    else
+      e = awq::launch_lossgemm(X16, M, K, E, N, cfg->n_grid, partials, stream);
+  }
+  mark(7);
   if (e == hipSuccess)
     e = awq::launch_finalize(partials, L.tiles_per_alpha, cfg->n_grid, M, N, K, S, ctrl, losses,
                              best, s_best, flags, stream);
-  mark(6);
+  mark(8);
   return hip_status(e);
 }
 

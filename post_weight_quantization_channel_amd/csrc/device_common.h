@@ -170,6 +170,24 @@ __device__ __forceinline__ void buffer_load16_lds(rsrc_t r, uint32_t lds, uint32
       : "memory");
 }
 
+// The same load with a wave-uniform byte offset `soff` added in the scalar offset field, so a
+// run of loads can share one per-lane offset register.
+__device__ __forceinline__ void buffer_load16_lds_so(rsrc_t r, uint32_t lds, uint32_t voff,
+                                                     uint32_t soff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(voff), "s"(r), "s"(so)
+      : "memory");
+}
+
 __device__ __forceinline__ void flag_or(uint32_t* flags, uint32_t bits) {
   if (bits) atomicOr(flags, bits);
 }

@@ -1,0 +1,359 @@
+// Gram form of the AWQ loss: the objective of the AWQ notes (bg51717.github.io/14592, section
+// 方法), L(s) = ||Q(W s)(s^-1 X) - W X||_F^2 / (M N), written with E = Q(W s)/s - W as
+//   L = sum_n E_n H E_n^T / (M N),   H = X^T X,
+// the quadratic form that GPTQ ("一文搞懂大模型量化技术：GGUF、GPTQ、AWQ", section on GPTQ) builds
+// its layer objective on. H is computed once per layer; each grid point then costs a K x K
+// contraction instead of an M x K one.
+//
+// Conditioning for fp16 operands. With d_k = sqrt(H_kk) (d_k = 0 for a channel that is zero in
+// every token) the correlation matrix C = D^-1 H D^-1 has a unit diagonal and entries in
+// [-1, 1], and E' = 2^e E D carries the loss: E_n H E_n^T = 2^-2e E'_n C E'_n^T. By symmetry,
+//   E'_n C E'_n^T = 2 sum_l E'_nl P_nl,   P_nl = sum_{k<l} E'_nk C_kl + E'_nl / 2,
+// so the contraction only needs B[l][k] = C_kl for k < l, 1/2 for k = l and 0 for k > l: a
+// lower-triangular operand that halves the work and keeps the dominant diagonal exact.
+//
+// Kernels, in launch order:
+//   gram_transpose   X [M, K] (fp16/bf16/fp32) -> Xt [K, Mp] fp16, zero for m >= M, so that
+//                    the token index is the contiguous reduction index of X^T X;
+//   gram_gemm        partials of H over chunks of tokens, upper-triangle 256 x 256 tiles only
+//                    (the K loop of mfma_kloop.h), fp32 accumulation, stored in fragment order;
+//   gram_diag        d_k = sqrt(sum over chunks of the H_kk partials) in fp64;
+//   gram_finish      B from the fp64 sums of the partials (fixed chunk order);
+//   gram_loss        per (grid point, row tile, pair of column tiles): P on the MFMA K loop,
+//                    epilogue 2 sum E'_nl P_nl against E' read back from the error stack.
+#include "mfma_kloop.h"
+
+namespace awq {
+
+// ------------------------------------------------------------------------------------------
+// Work split of X^T X over token chunks: every (tile, chunk) is one workgroup; the chunk count
+// is picked so that the workgroups fill whole waves of the 256 compute units.
+GramPlan gram_plan(int64_t M, int64_t K) {
+  GramPlan p{};
+  p.t = (int)((K + kLossBN - 1) / kLossBN);
+  p.T = (int64_t)p.t * (p.t + 1) / 2;
+  p.Mp = (M + kGramMAlign - 1) / kGramMAlign * kGramMAlign;
+  // at most kGramMaxChunks chunks, at least kGramMAlign tokens each, and no more than
+  // kGramMaxBlocks workgroups once one chunk per tile is there (bounds the partials' memory)
+  int64_t max_s = p.Mp / kGramMAlign < kGramMaxChunks ? p.Mp / kGramMAlign : kGramMaxChunks;
+  if (max_s > kGramMaxBlocks / p.T) max_s = kGramMaxBlocks / p.T;
+  if (max_s < 1) max_s = 1;
+  int64_t best_cost = -1;
+  for (int64_t s = 1; s <= max_s; ++s) {
+    const int64_t per = (p.Mp + s - 1) / s;
+    const int64_t chunk = (per + kGramMAlign - 1) / kGramMAlign * kGramMAlign;
+    const int64_t se = (p.Mp + chunk - 1) / chunk;
+    const int64_t waves = (p.T * se + 255) / 256;
+    const int64_t cost = waves * chunk;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      p.chunk = chunk;
+      p.S = (int)se;
+    }
+  }
+  return p;
+}
+
+// ------------------------------------------------------------------------------------------
+// One lane moves an 8 x 8 block: 8 rows of 16 bytes in, transposed in registers with byte
+// permutes, 8 rows of 16 bytes out. Lane l of a wave takes channel block l % 8 and token block
+// l / 8, so a load instruction reads 8 runs of 128 contiguous bytes (one per token row) and a
+// store instruction writes 8 runs of 128 contiguous bytes (one per channel row of Xt).
+template <int DT>
+__global__ __launch_bounds__(256) void gram_transpose_kernel(const void* __restrict__ X,
+                                                             int64_t M, int64_t K, int64_t Mp,
+                                                             uint16_t* __restrict__ Xt,
+                                                             uint32_t* __restrict__ flags) {
+  constexpr int ES = (DT == kF32) ? 4 : 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t k0 = (int64_t)blockIdx.x * 64 + (lane & 7) * 8;
+  const int64_t m0 = (int64_t)blockIdx.y * 256 + wave * 64 + (lane >> 3) * 8;
+  if (m0 >= Mp) return;   // Mp is a multiple of 64: whole waves leave together
+  bool over = false;
+  uint32_t v[8][4];       // v[r][w]: channels 2w, 2w+1 of token row m0 + r
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int64_t m = m0 + r;
+    if (m < M) {
+      if (DT == kF16) {
+        const uint4 u = *reinterpret_cast<const uint4*>(
+            reinterpret_cast<const char*>(X) + (m * K + k0) * ES);
+        v[r][0] = u.x; v[r][1] = u.y; v[r][2] = u.z; v[r][3] = u.w;
+      } else {
+        float f[8];
+        load8_f32<DT>(reinterpret_cast<const char*>(X) + (m * K + k0) * ES, f);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint16_t lo = f2h(f[2 * w]), hi = f2h(f[2 * w + 1]);
+          over |= ((lo & 0x7C00u) == 0x7C00u) || ((hi & 0x7C00u) == 0x7C00u);
+          v[r][w] = (uint32_t)lo | ((uint32_t)hi << 16);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v[r][w] = 0u;
+    }
+  }
+  // output row c (channel k0 + c) holds tokens m0..m0+7: word w = (token 2w, token 2w+1)
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t o[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(v[2 * w + 1][c >> 1], v[2 * w][c >> 1], sel);
+    *reinterpret_cast<uint4*>(Xt + (k0 + c) * Mp + m0) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (DT != kF16) wave_flag(flags, over, kFlagXF16Range);
+}
+
+// ------------------------------------------------------------------------------------------
+// Upper-triangle tile index -> (a, b), a <= b, row-major over a.
+__device__ __forceinline__ void tri_tile(int64_t idx, int t, int& a, int& b) {
+  int aa = 0;
+  while (idx >= t - aa) {
+    idx -= t - aa;
+    ++aa;
+  }
+  a = aa;
+  b = aa + (int)idx;
+}
+
+// Offset (in floats) of acc[i][j][e] of `lane` in `wave` inside a tile stored in fragment order:
+// [wave][i][j][e / 4][lane][e % 4] -- each float4 store of a wave writes 1 KiB contiguously.
+__device__ __forceinline__ int64_t frag_off(int wave, int i, int j, int e, int lane) {
+  return ((((int64_t)(wave * 4 + i) * 4 + j) * 4 + (e >> 2)) * 64 + lane) * 4 + (e & 3);
+}
+
+__global__ __launch_bounds__(kloop::kThreads, 1) void gram_gemm_kernel(
+    const uint16_t* __restrict__ Xt, int64_t K, int64_t Mp, int t, int64_t T, int64_t chunk,
+    float* __restrict__ Hpart) {
+  using namespace kloop;
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  const int64_t logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int64_t c = logical / T, tile = logical % T;    // chunk-major: neighbours share tokens
+  int a, b;
+  tri_tile(tile, t, a, b);
+  const int64_t m0 = c * chunk;
+  const int64_t clen = (Mp - m0 < chunk) ? Mp - m0 : chunk;   // multiple of 128
+  const int64_t rows_a = (K - (int64_t)a * BM < BM) ? K - (int64_t)a * BM : BM;
+  const int64_t rows_b = (K - (int64_t)b * BN < BN) ? K - (int64_t)b * BN : BN;
+  Tile T_;
+  T_.ra = make_rsrc(Xt + (int64_t)a * BM * Mp + m0, (uint32_t)(((rows_a - 1) * Mp + clen) * 2));
+  T_.rb = make_rsrc(Xt + (int64_t)b * BN * Mp + m0, (uint32_t)(((rows_b - 1) * Mp + clen) * 2));
+  tile_setup(T_, smem, (uint32_t)(Mp * 2));
+  floatx16 acc[4][4];
+  acc_zero(acc);
+  kl_run(smem, T_, (int)(clen / BK), acc);
+
+  const int lane = threadIdx.x & 63;
+  float* out = Hpart + (c * T + tile) * (int64_t)(BM * BN);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        *reinterpret_cast<float4*>(out + frag_off(T_.wave, i, j, 4 * e4, lane)) =
+            make_float4(acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2],
+                        acc[i][j][4 * e4 + 3]);
+}
+
+// ------------------------------------------------------------------------------------------
+// d_k = sqrt(H_kk): H_kk is element (k', k') of diagonal tile (a, a), k = 256 a + k'. In the
+// fragment order that element sits in wave 3 (k' / 128), block (i, i) with i = (k' % 128) / 32,
+// lane r + 32 ((r / 4) % 2) and register 4 (r / 8) + r % 4, r = k' % 32.
+__global__ __launch_bounds__(256) void gram_diag_kernel(const float* __restrict__ Hpart,
+                                                        int64_t K, int t, int64_t T, int S,
+                                                        double* __restrict__ d64,
+                                                        float* __restrict__ d32) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k >= K) return;
+  const int a = (int)(k / kLossBN), kp = (int)(k % kLossBN);
+  const int64_t tile = (int64_t)a * t - (int64_t)a * (a - 1) / 2;
+  const int wm = kp >> 7, i = (kp & 127) >> 5, r = kp & 31;
+  const int lane = r + 32 * ((r >> 2) & 1);
+  const int e = 4 * (r >> 3) + (r & 3);
+  const int64_t off = frag_off(3 * wm, i, i, e, lane);
+  double h = 0.0;
+  for (int c = 0; c < S; ++c) h += (double)Hpart[((int64_t)c * T + tile) * (kLossBM * kLossBN) + off];
+  const double d = sqrt(h);
+  d64[k] = d;
+  d32[k] = (float)d;
+}
+
+// One thread per float4 of the fragment order: tokens-chunk sums in fp64 (chunk order fixed),
+// then B[l][k..k+3] for the four channels k..k+3 (consecutive A rows) of output row l.
+__global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restrict__ Hpart,
+                                                          int64_t K, int t, int64_t T, int S,
+                                                          const double* __restrict__ d64,
+                                                          uint16_t* __restrict__ B) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;   // float4 index
+  constexpr int64_t kPerTile = kLossBM * kLossBN / 4;
+  if (g >= T * kPerTile) return;
+  const int64_t tile = g / kPerTile;
+  const int rem = (int)(g % kPerTile);
+  const int lane = rem & 63, e4 = (rem >> 6) & 3, j = (rem >> 8) & 3, i = (rem >> 10) & 3,
+            wave = rem >> 12;
+  int a, b;
+  tri_tile(tile, t, a, b);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t l = (int64_t)b * kLossBN + wn * 128 + 32 * j + (lane & 31);
+  const int64_t k = (int64_t)a * kLossBM + wm * 128 + 32 * i + 8 * e4 + 4 * (lane >> 5);
+  if (l >= K || k >= K) return;   // k is a multiple of 4 and K of 128: k..k+3 all valid
+  double h[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int c = 0; c < S; ++c) {
+    const float4 p = *reinterpret_cast<const float4*>(Hpart + ((int64_t)c * T + tile) * (4 * kPerTile) +
+                                                      (int64_t)rem * 4);
+    h[0] += (double)p.x;
+    h[1] += (double)p.y;
+    h[2] += (double)p.z;
+    h[3] += (double)p.w;
+  }
+  const double dl = d64[l];
+  uint16_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t kq = k + q;
+    float v = 0.0f;
+    if (kq == l) {
+      v = 0.5f;
+    } else if (kq < l) {
+      const double dk = d64[kq];
+      v = (dk > 0.0 && dl > 0.0) ? (float)(h[q] / (dk * dl)) : 0.0f;
+    }
+    o[q] = f2h(v);
+  }
+  *reinterpret_cast<uint2*>(B + l * K + k) =
+      make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+}
+
+// ------------------------------------------------------------------------------------------
+// Workgroup (grid point, row tile nt, pair q) computes the column tiles t-1-q and q (one if they
+// coincide): lt needs the K steps of channels below 256 (lt + 1) only, so every pair costs the
+// same 8 (t + 1) steps and the grid has no long tail.
+__global__ __launch_bounds__(kloop::kThreads, 1) void gram_loss_kernel(
+    const uint16_t* __restrict__ Est, int64_t N, int64_t K, const uint16_t* __restrict__ B,
+    int tilesN, int t, int pairs, double* __restrict__ partials) {
+  using namespace kloop;
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  __shared__ double wsum[4];
+  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int panel = logical / pairs, q = logical % pairs;
+  const int alpha = panel / tilesN, nt = panel % tilesN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t rows = (N - (int64_t)nt * BM < BM) ? N - (int64_t)nt * BM : BM;
+  const uint16_t* Ep = Est + ((int64_t)alpha * N + (int64_t)nt * BM) * K;
+  const int nk_all = (int)(K / BK);
+
+  Tile T_;
+  T_.ra = make_rsrc(Ep, (uint32_t)(rows * K * 2));
+  tile_setup(T_, smem, (uint32_t)(K * 2));
+  const int wm = T_.wave >> 1, wn = T_.wave & 1;
+
+#pragma nounroll
+  for (int u = 0; u < 2; ++u) {
+    const int lt = (u == 0) ? t - 1 - q : q;
+    if (u == 1 && lt == t - 1 - q) break;
+    const int64_t brows = (K - (int64_t)lt * BN < BN) ? K - (int64_t)lt * BN : BN;
+    T_.rb = make_rsrc(B + (int64_t)lt * BN * K, (uint32_t)(brows * K * 2));
+    const int nk = (8 * (lt + 1) < nk_all) ? 8 * (lt + 1) : nk_all;
+    floatx16 acc[4][4];
+    acc_zero(acc);
+    kl_run(smem, T_, nk, acc);
+
+    // E' tile [256 n][256 l] (128 KiB) into the LDS stages, which no wave reads any more: row n
+    // at byte 512 n. Rows past the panel read as zeros; columns past K (ragged last tile) pick
+    // up neighbouring values, which meet P = 0 there and are masked below anyway.
+    // wave w, load p: LDS bytes (32 w + p) KiB .. +1 KiB = tile rows 64 w + 2 p + lane / 32
+    {
+      const uint32_t rowb = (uint32_t)(K * 2);
+      const uint32_t voff = (uint32_t)(T_.wave * 64 + (lane >> 5)) * rowb + (uint32_t)(lane & 31) * 16u;
+#pragma unroll
+      for (int p = 0; p < 32; ++p)
+        buffer_load16_lds_so(T_.ra, T_.lds0 + (uint32_t)((T_.wave * 32 + p) * 1024), voff,
+                             (uint32_t)(2 * p) * rowb + (uint32_t)lt * 512u);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt(0));
+    __syncthreads();
+
+    // epilogue: sum over the tile of E'_nl P_nl (P = acc)
+    double tot = 0.0;
+    const uint16_t* et = reinterpret_cast<const uint16_t*>(smem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int lcol = wn * 128 + 32 * j + (lane & 31);
+        const bool lok = (int64_t)lt * BN + lcol < K;
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {   // the LDS tile is read in full: no branches here
+          const int n = wm * 128 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          s = __builtin_fmaf(h2f(et[n * 256 + lcol]), acc[i][j][e], s);
+        }
+        tot += lok ? (double)s : 0.0;
+      }
+    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
+    if (lane == 0) wsum[T_.wave] = tot;
+    __syncthreads();   // also: no wave reads the LDS tile any more
+    if (tid == 0) {
+      const double v = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+      partials[(int64_t)alpha * ((int64_t)tilesN * t) + (int64_t)nt * t + lt] = 2.0 * v;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+hipError_t launch_gram_prepare(const void* X, int xdt, int64_t M, int64_t K, const GramPlan& p,
+                               uint16_t* Xt, float* Hpart, double* d64, float* d32, uint16_t* B,
+                               uint32_t* flags, hipStream_t stream, hipEvent_t* ev) {
+  hipError_t e = hipSuccess;
+  {
+    dim3 grid((unsigned)(K / 64), (unsigned)((p.Mp + 255) / 256));
+    switch (xdt) {
+      case kF16:
+        gram_transpose_kernel<kF16><<<grid, 256, 0, stream>>>(X, M, K, p.Mp, Xt, flags);
+        break;
+      case kBF16:
+        gram_transpose_kernel<kBF16><<<grid, 256, 0, stream>>>(X, M, K, p.Mp, Xt, flags);
+        break;
+      default:
+        gram_transpose_kernel<kF32><<<grid, 256, 0, stream>>>(X, M, K, p.Mp, Xt, flags);
+        break;
+    }
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[0], stream);
+  if (e == hipSuccess) {
+    gram_gemm_kernel<<<(unsigned)(p.T * p.S), kloop::kThreads, 0, stream>>>(Xt, K, p.Mp, p.t, p.T,
+                                                                            p.chunk, Hpart);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[1], stream);
+  if (e == hipSuccess) {
+    gram_diag_kernel<<<(unsigned)((K + 255) / 256), 256, 0, stream>>>(Hpart, K, p.t, p.T, p.S,
+                                                                      d64, d32);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) {
+    const int64_t threads = p.T * (kLossBM * kLossBN / 4);
+    gram_finish_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(Hpart, K, p.t, p.T,
+                                                                              p.S, d64, B);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_gram_loss(const uint16_t* Estack, int64_t N, int64_t K, const uint16_t* B,
+                            int n_grid, double* partials, hipStream_t stream) {
+  const int tilesN = (int)((N + kLossBM - 1) / kLossBM);
+  const int t = (int)((K + kLossBN - 1) / kLossBN);
+  const int pairs = (t + 1) / 2;
+  const int64_t blocks = (int64_t)n_grid * tilesN * pairs;
+  gram_loss_kernel<<<(unsigned)blocks, kloop::kThreads, 0, stream>>>(Estack, N, K, B, tilesN, t,
+                                                                     pairs, partials);
+  return hipGetLastError();
+}
+
+}  // namespace awq

@@ -24,15 +24,36 @@ struct SearchCtrl {        // lives at the start of the search workspace
   uint32_t done;           // grid points whose loss is final (finalize's completion count)
 };
 
+// Gram form (gram.hip): H = X^T X over token chunks, then the lower-triangular operand B.
+constexpr int64_t kGramMAlign = 128;     // tokens are padded to this multiple (>= 4 K steps)
+constexpr int64_t kGramMaxChunks = 32;
+constexpr int64_t kGramMaxBlocks = 4096;
+struct GramPlan {
+  int t;          // 256-channel blocks, ceil(K / 256)
+  int S;          // token chunks
+  int64_t T;      // upper-triangle tiles, t (t + 1) / 2
+  int64_t Mp;     // padded token count
+  int64_t chunk;  // tokens per chunk (multiple of kGramMAlign; the last chunk may be shorter)
+};
+GramPlan gram_plan(int64_t M, int64_t K);
+// transpose -> ev[0] -> X^T X partials -> ev[1] -> d and B
+hipError_t launch_gram_prepare(const void* X, int xdt, int64_t M, int64_t K, const GramPlan& p,
+                               uint16_t* Xt, float* Hpart, double* d64, float* d32, uint16_t* B,
+                               uint32_t* flags, hipStream_t stream, hipEvent_t* ev);
+hipError_t launch_gram_loss(const uint16_t* Estack, int64_t N, int64_t K, const uint16_t* B,
+                            int n_grid, double* partials, hipStream_t stream);
+
 hipError_t launch_search_prep(const float* sx, int K, int n_grid, float s_floor, float* S,
                               SearchCtrl* ctrl, hipStream_t stream);
-hipError_t launch_absmax(const void* W, int dtype, int64_t count, SearchCtrl* ctrl,
-                         uint32_t* flags, hipStream_t stream);
+// max |W| (dcol == nullptr) or max |W[n,k]| * dcol[k] over W [N, K]
+hipError_t launch_absmax(const void* W, int dtype, int64_t N, int64_t K, const float* dcol,
+                         SearchCtrl* ctrl, uint32_t* flags, hipStream_t stream);
 hipError_t launch_x_to_f16(const void* X, int dtype, int64_t count, uint16_t* X16,
                            uint32_t* flags, hipStream_t stream);
+// E_i * 2^escale (dcol == nullptr) or E_i[n,k] * dcol[k] * 2^escale
 hipError_t launch_quantize_stack(const void* W, int dtype, int64_t N, int64_t K, const float* S,
-                                 int n_grid, int bits, const SearchCtrl* ctrl, uint16_t* Estack,
-                                 uint32_t* flags, hipStream_t stream);
+                                 int n_grid, int bits, const float* dcol, const SearchCtrl* ctrl,
+                                 uint16_t* Estack, uint32_t* flags, hipStream_t stream);
 hipError_t launch_lossgemm(const uint16_t* X16, int64_t M, int64_t K, const uint16_t* Estack,
                            int64_t N, int n_grid, double* partials, hipStream_t stream);
 hipError_t launch_finalize(const double* partials, int64_t tiles_per_alpha, int n_grid,

@@ -1,0 +1,180 @@
+// The MFMA K loop shared by the three contractions of the search (direct loss, X^T X, and the
+// Gram-form loss): a 256 x 256 fp32 tile of A B^T accumulated over K, where A and B are two
+// row-major fp16 panels of 256 rows whose reduction index runs along the row.
+//
+// gfx950 design:
+//   * 256 threads = 4 waves (2 x 2), workgroup tile 256 x 256, wave tile 128 x 128, BK = 32;
+//   * v_mfma_f32_32x32x16_f16: 4 x 4 MFMA blocks per wave, 256 fp32 accumulators per lane
+//     (held in AGPRs; one wave per SIMD);
+//   * operands go from HBM straight into LDS (buffer_load_dwordx4 ... lds): no staging
+//     registers and no ds_write; each wave instruction fills 1 KiB = 16 rows x 64 bytes. The
+//     buffer range of each operand panel ends at its last valid row, so rows of a ragged tile
+//     read as zeros without branches;
+//   * four LDS stages of 32 KiB: the loads of steps k+1..k+4 are in flight while step k
+//     computes (one stage ahead left the waves waiting ~40% of the time on loads whose lines
+//     missed L2; LDS bank conflicts: none). Fragment reads of the next step overlap the second
+//     half of the current step's MFMAs;
+//   * LDS layout: row r holds its 4 chunks of 16 bytes at positions c ^ f(r),
+//     f(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1), so the 128-bit fragment reads of 8 (and of 16)
+//     consecutive rows at one chunk touch distinct banks whether the LDS has 32 or 64 banks.
+//
+// Accumulator layout (v_mfma_f32_32x32x16_f16): acc[i][j][e] of lane l holds the tile element
+//   A row  wm * 128 + 32 i + 8 (e / 4) + 4 (l / 32) + e % 4,
+//   B row  wn * 128 + 32 j + l % 32,
+// with wave w = 2 wm + wn.
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace awq {
+namespace kloop {
+
+constexpr int BM = kLossBM, BN = kLossBN, BK = kLossBK;
+constexpr int kThreads = 256;
+constexpr int kStages = 4;
+constexpr int kRowBytes = BK * 2;                           // 64 bytes of a row per K step
+constexpr int kStageBytes = (BM + BN) * kRowBytes;          // 32 KiB per stage
+constexpr int kSmemBytes = kStages * kStageBytes;           // 128 KiB
+constexpr int kRowsPerWave = BM / 4;                        // rows each wave loads per operand
+constexpr int kRowsPerInst = 1024 / kRowBytes;              // 16 rows per 1 KiB wave load
+constexpr int kInstPerOp = kRowsPerWave / kRowsPerInst;     // 4 loads per operand per step
+
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+
+// s_waitcnt immediate that waits until at most n vector-memory loads are outstanding (gfx9
+// encoding: vmcnt in bits [3:0] and [15:14]; expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
+
+// The K loop over four LDS stages (LDS addresses base + stage * kStageBytes, stage = kt % 4).
+//
+// Per step kt: the 16 MFMAs of the first half (k 0..15) with the reads of the second-half
+// fragments in between; wait until step kt+1 has landed (steps kt+2, kt+3 may still be in
+// flight) and this wave's LDS reads are done; barrier; the 16 MFMAs of the second half with the
+// refill of stage kt (step kt+4) and the reads of step kt+1's first-half fragments in between.
+// The instruction stream is laid out by hand (sched_barrier stops the scheduler from regrouping
+// it): each MFMA keeps the matrix core busy for 32 cycles while the following load or LDS read
+// issues.
+struct Tile {
+  rsrc_t ra, rb;        // operand panels
+  uint32_t voff;        // this lane's byte offset for load slice 0, step 0
+  uint32_t row_stride;  // bytes between rows
+  uint32_t lds0;        // LDS address of stage 0
+  uint32_t rd[2][2];    // this lane's fragment read offsets in a stage: [operand][k half]
+  int wave;
+};
+
+struct Frags {
+  half8_t a[2][4], b[2][4];   // [k half][row block]
+};
+
+// Lane-dependent parts of a tile: load offsets and fragment read offsets. `row_stride` is the
+// byte distance between consecutive rows of both panels.
+__device__ __forceinline__ void tile_setup(Tile& T, const char* smem, uint32_t row_stride) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  T.wave = tid >> 6;
+  T.lds0 = lds_addr(smem);
+  // lane l of load slice j fills LDS row wave*64 + 16j + l/4, physical chunk l%4, i.e. the
+  // logical chunk (l%4) ^ swz(row); swz depends on row % 16 = l/4 only.
+  const int lrow = lane >> 2;
+  T.row_stride = row_stride;
+  T.voff = (uint32_t)(T.wave * kRowsPerWave + lrow) * T.row_stride +
+           (uint32_t)(((lane & 3) ^ swz(lrow)) * 16);
+  // fragment reads: lane l reads row (wave block) + 32 i + l%32 at chunk 2h + l/32; the
+  // swizzle of a row does not change with the +32 i block offset, so one offset per (operand,
+  // k half) serves all four row blocks.
+  const int frow = lane & 31, fhalf = lane >> 5;
+  const int wm = T.wave >> 1, wn = T.wave & 1;
+  const int ra0 = wm * 128 + frow, rb0 = wn * 128 + frow;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    T.rd[0][h] = (uint32_t)(ra0 * kRowBytes + (((2 * h + fhalf) ^ swz(ra0)) << 4));
+    T.rd[1][h] = (uint32_t)(BM * kRowBytes + rb0 * kRowBytes + (((2 * h + fhalf) ^ swz(rb0)) << 4));
+  }
+}
+
+// Fragment i (i < 4: A row block i, else B row block i - 4) of k half h from stage `st`.
+__device__ __forceinline__ void kl_read(const char* smem, const Tile& T, int st, int h, int i,
+                                        Frags& F) {
+  const char* base = smem + st * kStageBytes;
+  if (i < 4)
+    F.a[h][i] = *reinterpret_cast<const half8_t*>(base + T.rd[0][h] + i * 32 * kRowBytes);
+  else
+    F.b[h][i - 4] = *reinterpret_cast<const half8_t*>(base + T.rd[1][h] + (i - 4) * 32 * kRowBytes);
+}
+
+// Load slice idx in [0, 8) of step kt into stage `st` (even idx: A, odd: B; rows 16 (idx/2) ..
+// of this wave's 64 rows).
+__device__ __forceinline__ void kl_issue(const Tile& T, int st, int kt, int idx) {
+  const int j = idx >> 1;
+  const uint32_t lds = T.lds0 + (uint32_t)(st * kStageBytes) + ((idx & 1) ? BM * kRowBytes : 0) +
+                       (uint32_t)((T.wave * kRowsPerWave + kRowsPerInst * j) * kRowBytes);
+  const uint32_t o = T.voff + (uint32_t)(kRowsPerInst * j) * T.row_stride +
+                     (uint32_t)kt * (uint32_t)kRowBytes;
+  buffer_load16_lds((idx & 1) ? T.rb : T.ra, lds, o);
+}
+
+template <bool REFILL, bool MORE, int VM>
+__device__ __forceinline__ void kl_step(const char* smem, const Tile& T, int kt, Frags& F,
+                                        floatx16 (&acc)[4][4]) {
+  const int st = kt & 3;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[0][m >> 2], F.b[0][m & 3],
+                                                                acc[m >> 2][m & 3], 0, 0, 0);
+    if ((m & 1) == 0) kl_read(smem, T, st, 1, m >> 1, F);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt(VM) & ~0x0F00);   // + lgkmcnt(0)
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[1][m >> 2], F.b[1][m & 3],
+                                                                acc[m >> 2][m & 3], 0, 0, 0);
+    if (REFILL && (m & 1) == 0) kl_issue(T, st, kt + 4, m >> 1);
+    if (MORE && (m & 1)) kl_read(smem, T, (st + 1) & 3, 0, m >> 1, F);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// acc += A B^T over nk steps of BK (nk >= 4). The LDS stages must be free on entry (a barrier
+// after any previous use); on return every wave has passed the last step's barrier and the
+// stages are no longer read.
+__device__ __forceinline__ void kl_run(const char* smem, const Tile& T, int nk,
+                                       floatx16 (&acc)[4][4]) {
+  Frags F;
+#pragma unroll
+  for (int p = 0; p < kStages; ++p)
+#pragma unroll
+    for (int idx = 0; idx < 2 * kInstPerOp; ++idx) kl_issue(T, p, p, idx);
+  __builtin_amdgcn_s_waitcnt(vmcnt(24));           // step 0 has landed
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kl_read(smem, T, 0, 0, i, F);
+  // steps whose successors kt+1..kt+4 all exist, then the last four with constant flags
+  for (int kt = 0; kt < nk - 4; ++kt) kl_step<true, true, 16>(smem, T, kt, F, acc);
+  kl_step<false, true, 16>(smem, T, nk - 4, F, acc);
+  kl_step<false, true, 8>(smem, T, nk - 3, F, acc);
+  kl_step<false, true, 0>(smem, T, nk - 2, F, acc);
+  kl_step<false, false, 0>(smem, T, nk - 1, F, acc);
+}
+
+__device__ __forceinline__ void acc_zero(floatx16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+}
+
+// Block b of a grid of G is dealt to XCD b % 8; returns the logical index that gives each XCD a
+// contiguous range of the logical order.
+__device__ __forceinline__ int xcd_logical(int b, int G) {
+  const int per = G / 8, rem = G % 8, xcd = b % 8, loc = b / 8;
+  return (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+}
+
+}  // namespace kloop
+}  // namespace awq

@@ -1,14 +1,16 @@
 // The alpha grid search of the AWQ notes (bg51717.github.io/14592, section 方法):
 //   s = s_X^alpha, alpha in [0, 1];  alpha* = argmin_alpha L(s_X^alpha),
 //   L(s) = || Q(W s)(s^-1 X) - W X ||.
-// This file holds every stage except the loss contraction (lossgemm.hip):
+// This file holds every stage except the contractions (lossgemm.hip, gram.hip):
 //   search_prep      s_i[k] = fp32(pow(max(s_X[k], s_floor), i/(n-1))) in fp64, and the reset
 //                    of the control block;
-//   absmax           max |W| (integer atomicMax on the fp32 bit patterns: order-free);
+//   absmax           max |W|, or max |W[n,k]| d_k in the Gram form (integer atomicMax on the
+//                    fp32 bit patterns: order-free);
 //   x_to_f16         fp16 copy of an fp32/bf16 X for the fp16 contraction;
 //   quantize_stack   for all alpha at once: Q(W s_i) group-wise (the fp32 specification of
 //                    device_common.h) and the error E_i = Q(W s_i)/s_i - W, stored in fp16 as
-//                    E_i * 2^escale. By linearity X E_i^T = Q(W s_i)(s_i^-1 X) - W X.
+//                    E_i * 2^escale (Gram form: E_i[n,k] d_k 2^escale). By linearity
+//                    X E_i^T = Q(W s_i)(s_i^-1 X) - W X.
 //   finalize         fixed-order fp64 sum of the per-tile partial losses, L_i / (M N),
 //                    argmin with the lowest index on ties, s_best = s_{i*}.
 #include "device_common.h"
@@ -43,8 +45,11 @@ hipError_t launch_search_prep(const float* sx, int K, int n_grid, float s_floor,
 }
 
 // ------------------------------------------------------------------------------------------
-template <int DT>
+// With COL, every |W[n,k]| is weighted by dcol[k] (the Gram form's column scaling). K is a
+// multiple of 8, so the 8 elements of a chunk share one row and consecutive columns.
+template <int DT, bool COL>
 __global__ __launch_bounds__(256) void absmax_kernel(const void* __restrict__ W, int64_t count8,
+                                                     int64_t K, const float* __restrict__ dcol,
                                                      SearchCtrl* __restrict__ ctrl,
                                                      uint32_t* __restrict__ flags) {
   constexpr int ES = (DT == kF32) ? 4 : 2;
@@ -52,27 +57,29 @@ __global__ __launch_bounds__(256) void absmax_kernel(const void* __restrict__ W,
   bool bad = false;
   const int64_t stride = (int64_t)gridDim.x * 256;
   int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  auto fold = [&](int64_t cc, const float (&v)[8]) {
+    float d[8];
+    if (COL) {
+      load8_f32<kF32>(dcol + (cc * 8) % K, d);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      bad |= !isfinite(v[t]);
+      m = fmaxf(m, COL ? fabsf(v[t]) * d[t] : fabsf(v[t]));
+    }
+  };
   for (; c + 3 * stride < count8; c += 4 * stride) {     // four loads in flight per thread
     float v[4][8];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       load8_f32<DT>(reinterpret_cast<const char*>(W) + (c + u * stride) * 8 * ES, v[u]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        bad |= !isfinite(v[u][t]);
-        m = fmaxf(m, fabsf(v[u][t]));
-      }
+    for (int u = 0; u < 4; ++u) fold(c + u * stride, v[u]);
   }
   for (; c < count8; c += stride) {
     float v[8];
     load8_f32<DT>(reinterpret_cast<const char*>(W) + c * 8 * ES, v);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      bad |= !isfinite(v[t]);
-      m = fmaxf(m, fabsf(v[t]));
-    }
+    fold(c, v);
   }
   // wave maximum, then workgroup maximum, then one atomic per workgroup (max is order-free)
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -86,16 +93,24 @@ __global__ __launch_bounds__(256) void absmax_kernel(const void* __restrict__ W,
   }
 }
 
-hipError_t launch_absmax(const void* W, int dtype, int64_t count, SearchCtrl* ctrl,
-                         uint32_t* flags, hipStream_t stream) {
-  const int64_t count8 = count / 8;
+hipError_t launch_absmax(const void* W, int dtype, int64_t N, int64_t K, const float* dcol,
+                         SearchCtrl* ctrl, uint32_t* flags, hipStream_t stream) {
+  const int64_t count8 = N * K / 8;
   int64_t blocks = (count8 + 1023) / 1024;
   if (blocks > 1024) blocks = 1024;
   if (blocks < 1) blocks = 1;
-  if (dtype == kF32)
-    absmax_kernel<kF32><<<(unsigned)blocks, 256, 0, stream>>>(W, count8, ctrl, flags);
-  else
-    absmax_kernel<kF16><<<(unsigned)blocks, 256, 0, stream>>>(W, count8, ctrl, flags);
+  const unsigned g = (unsigned)blocks;
+  if (dtype == kF32) {
+    if (dcol)
+      absmax_kernel<kF32, true><<<g, 256, 0, stream>>>(W, count8, K, dcol, ctrl, flags);
+    else
+      absmax_kernel<kF32, false><<<g, 256, 0, stream>>>(W, count8, K, dcol, ctrl, flags);
+  } else {
+    if (dcol)
+      absmax_kernel<kF16, true><<<g, 256, 0, stream>>>(W, count8, K, dcol, ctrl, flags);
+    else
+      absmax_kernel<kF16, false><<<g, 256, 0, stream>>>(W, count8, K, dcol, ctrl, flags);
+  }
   return hipGetLastError();
 }
 
@@ -139,7 +154,8 @@ hipError_t launch_x_to_f16(const void* X, int dtype, int64_t count, uint16_t* X1
 // The error stack is stored as E * 2^escale with 2^escale * max|W| in [2^14, 2^15): every |E|
 // is at most ~|w| (a code of 0 gives E = -w; a non-zero code means |w s| >= Delta/2 and the
 // rounding error is at most Delta/2), so the fp16 values stay finite, and small errors keep
-// fp16 normal precision instead of falling into the fp16 subnormal range.
+// fp16 normal precision instead of falling into the fp16 subnormal range. In the Gram form the
+// same bound holds for E d_k against max |W d| (d_k >= 0).
 __device__ __forceinline__ int escale_from_absmax(uint32_t bits) {
   const float m = __uint_as_float(bits);
   if (!(m > 0.0f) || !isfinite(m)) return 0;
@@ -157,11 +173,11 @@ constexpr int kQuantRows = 4;  // rows per thread in quantize_stack
 // kQuantRows rows; 16 consecutive lanes cover one 128-channel group (a DPP row), so the group
 // maximum is four DPP steps. The scale row s_i for the thread's 8 channels is loaded once per
 // alpha and reused for all its rows. Stores: 16 bytes per lane, 1 KiB per wave, contiguous.
-template <int DT>
+template <int DT, bool COL>
 __global__ __launch_bounds__(256) void quantize_stack_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ S, int n_grid,
-    float qmin, float qmax, const SearchCtrl* __restrict__ ctrl, uint16_t* __restrict__ Estack,
-    uint32_t* __restrict__ flags) {
+    float qmin, float qmax, const float* __restrict__ dcol, const SearchCtrl* __restrict__ ctrl,
+    uint16_t* __restrict__ Estack, uint32_t* __restrict__ flags) {
   constexpr int ES = (DT == kF32) ? 4 : 2;
   const int64_t chunks = K / 8;
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -171,6 +187,15 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
   if (row0 >= N) return;  // whole 16-lane groups share rb: no partial group exits here
   const int e = escale_from_absmax(ctrl->absmax_bits);
   const float esc = ldexpf(1.0f, e);
+  float cs[8];   // per-column factor: 2^escale, times dcol[k] in the Gram form
+  if (COL) {
+    load8_f32<kF32>(dcol + c8 * 8, cs);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) cs[t] *= esc;
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) cs[t] = esc;
+  }
 
   float w[kQuantRows][8];
   bool live[kQuantRows];
@@ -201,9 +226,11 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
       uint32_t packed[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        // E = (q Delta)/s - w, then scaled by the exact power of two and rounded once to fp16
-        const float e0 = (__builtin_fmaf(q[2 * t] * delta, inv[2 * t], -w[r][2 * t])) * esc;
-        const float e1 = (__builtin_fmaf(q[2 * t + 1] * delta, inv[2 * t + 1], -w[r][2 * t + 1])) * esc;
+        // E = (q Delta)/s - w, then scaled (by the exact power of two, or by d_k 2^escale) and
+        // rounded once to fp16
+        const float e0 = (__builtin_fmaf(q[2 * t] * delta, inv[2 * t], -w[r][2 * t])) * cs[2 * t];
+        const float e1 =
+            (__builtin_fmaf(q[2 * t + 1] * delta, inv[2 * t + 1], -w[r][2 * t + 1])) * cs[2 * t + 1];
         packed[t] = (uint32_t)f2h(e0) | ((uint32_t)f2h(e1) << 16);
       }
       *reinterpret_cast<uint4*>(Estack + i * stride_alpha + (row0 + r) * K + c8 * 8) =
@@ -213,18 +240,21 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
 }
 
 hipError_t launch_quantize_stack(const void* W, int dtype, int64_t N, int64_t K, const float* S,
-                                 int n_grid, int bits, const SearchCtrl* ctrl, uint16_t* Estack,
-                                 uint32_t* flags, hipStream_t stream) {
+                                 int n_grid, int bits, const float* dcol, const SearchCtrl* ctrl,
+                                 uint16_t* Estack, uint32_t* flags, hipStream_t stream) {
   const float qmax = (float)((1 << (bits - 1)) - 1);
   const float qmin = -(float)(1 << (bits - 1));
   const int64_t threads = ((N + kQuantRows - 1) / kQuantRows) * (K / 8);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
-  if (dtype == kF32)
-    quantize_stack_kernel<kF32><<<blocks, 256, 0, stream>>>(W, N, K, S, n_grid, qmin, qmax, ctrl,
-                                                            Estack, flags);
-  else
-    quantize_stack_kernel<kF16><<<blocks, 256, 0, stream>>>(W, N, K, S, n_grid, qmin, qmax, ctrl,
-                                                            Estack, flags);
+#define AWQ_QS(DT_, COL_)                                                                       \
+  quantize_stack_kernel<DT_, COL_><<<blocks, 256, 0, stream>>>(W, N, K, S, n_grid, qmin, qmax,   \
+                                                               dcol, ctrl, Estack, flags)
+  if (dtype == kF32) {
+    if (dcol) AWQ_QS(kF32, true); else AWQ_QS(kF32, false);
+  } else {
+    if (dcol) AWQ_QS(kF16, true); else AWQ_QS(kF16, false);
+  }
+#undef AWQ_QS
   return hipGetLastError();
 }
 

@@ -47,11 +47,11 @@ def test_status_strings(lib):
     for code in range(7):
         s = lib.awq_status_string(code).decode()
         assert s.startswith("AWQ_")
-    assert lib.awq_version() == 10000
+    assert lib.awq_version() == 10100
 
 
-def cfg(bits=4, group=128, n_grid=20, s_floor=1e-5):
-    return AwqCfg(bits, group, n_grid, s_floor)
+def cfg(bits=4, group=128, n_grid=20, s_floor=1e-5, form=0):
+    return AwqCfg(bits, group, n_grid, s_floor, form)
 
 
 def test_workspace_queries(lib):
@@ -65,6 +65,46 @@ def test_workspace_queries(lib):
     assert ws32 >= 256 * 512 * 2 + 20 * 512 * 512 * 2
     assert lib.awq_search_workspace_bytes(256, 512, 512, _lib.AWQ_F16, cfg(bits=5)) == 0
     assert lib.awq_search_workspace_bytes(256, 512, 512, _lib.AWQ_F16, cfg(n_grid=1)) == 0
+    assert lib.awq_search_workspace_bytes(256, 512, 512, _lib.AWQ_F16, cfg(form=2)) == 0
+
+
+def _gram_chunks(M, K):
+    """Token chunks of X^T X: (tile, chunk) workgroups should fill whole waves of 256 CUs, so
+    the count minimises ceil(tiles * chunks / 256) * chunk_length (chunks of a multiple of 128
+    tokens, at most 32 chunks and 4096 workgroups; ties go to fewer chunks)."""
+    t = -(-K // 256)
+    T = t * (t + 1) // 2
+    Mp = -(-M // 128) * 128
+    best = None
+    for s in range(1, max(1, min(Mp // 128, 32, 4096 // T)) + 1):
+        chunk = -(-(-(-Mp // s)) // 128) * 128
+        se = -(-Mp // chunk)
+        cost = -(-T * se // 256) * chunk
+        if best is None or cost < best[0]:
+            best = (cost, se)
+    return T, best[1]
+
+
+def test_gram_workspace(lib):
+    """Gram form: K x K fp16 operand + d, and one region shared by the error stack and by the
+    transposed X plus the fp32 partials of X^T X (one 256 KiB tile per (tile, chunk))."""
+    g = cfg(form=_lib.AWQ_FORM_GRAM)
+    ws = lib.awq_search_workspace_bytes(65536, 4096, 4096, _lib.AWQ_F16, g)
+    T, S = _gram_chunks(65536, 4096)
+    assert T == 136 and S == 13       # 13 chunks of 5120 tokens: 1768 workgroups, 7 waves
+    xt = 4096 * 65536 * 2
+    hpart = S * T * 256 * 256 * 4
+    estack = 20 * 4096 * 4096 * 2
+    fixed = 4096 * 4096 * 2
+    assert fixed + max(xt + hpart, estack) < ws < fixed + max(xt + hpart, estack) + 4 * 2**20
+    # a small layer: the error stack dominates the shared region
+    ws_small = lib.awq_search_workspace_bytes(256, 512, 512, _lib.AWQ_F16, g)
+    assert 512 * 512 * 2 + 20 * 512 * 512 * 2 < ws_small < 512 * 512 * 2 + 20 * 512 * 512 * 2 + 2**20
+    # limits of the Gram form: K <= 32768, padded M < 2^23
+    assert lib.awq_search_workspace_bytes(256, 64, 32768 + 128, _lib.AWQ_F16, g) == 0
+    assert lib.awq_search_workspace_bytes(256, 64, 32768, _lib.AWQ_F16, g) > 0
+    assert lib.awq_search_workspace_bytes((1 << 23) - 128, 64, 256, _lib.AWQ_F16, g) > 0
+    assert lib.awq_search_workspace_bytes((1 << 23) - 127, 64, 256, _lib.AWQ_F16, g) == 0
 
 
 def test_act_stats_rejects(lib):
@@ -101,6 +141,13 @@ def test_search_rejects(lib):
     assert _search(lib, cfg=cfg(n_grid=65)) == E.AWQ_ERR_CONFIG
     assert _search(lib, cfg=cfg(s_floor=0.0)) == E.AWQ_ERR_CONFIG
     assert _search(lib, cfg=cfg(s_floor=float("nan"))) == E.AWQ_ERR_CONFIG
+    assert _search(lib, cfg=cfg(form=2)) == E.AWQ_ERR_CONFIG
+    assert _search(lib, cfg=cfg(form=-1)) == E.AWQ_ERR_CONFIG
+    gram = cfg(form=E.AWQ_FORM_GRAM)
+    assert _search(lib, cfg=gram, K=32768 + 128) == E.AWQ_ERR_SHAPE
+    assert _search(lib, cfg=gram, M=(1 << 23) - 127) == E.AWQ_ERR_SHAPE
+    need_g = lib.awq_search_workspace_bytes(300, 256, 512, 1, gram)
+    assert _search(lib, cfg=gram, ws_bytes=need_g - 1) == E.AWQ_ERR_WORKSPACE
     assert _search(lib, wdt=2) == E.AWQ_ERR_DTYPE      # bf16 W is not accepted
     assert _search(lib, xdt=9) == E.AWQ_ERR_DTYPE
     assert _search(lib, K=500) == E.AWQ_ERR_SHAPE

@@ -110,15 +110,20 @@ SEARCH_CASES = [
 ]
 
 
+FORMS = ("direct", "gram")
+
+
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("name,make,bits,n_grid", SEARCH_CASES, ids=[c[0] for c in SEARCH_CASES])
-def test_search_parity(awq, name, make, bits, n_grid):
+def test_search_parity(awq, name, make, bits, n_grid, form):
     W, X = make()
     tdt = torch.bfloat16 if "bf16x" in name else None
-    say("search", name, "W", W.shape, W.dtype, "X", X.shape, X.dtype, "bits", bits, "grid", n_grid)
+    say("search", form, name, "W", W.shape, W.dtype, "X", X.shape, X.dtype, "bits", bits,
+        "grid", n_grid)
     Wt = dev(W)
     Xt = dev(X) if tdt is None else dev(X).to(tdt)
     Xref = Xt.float().cpu().numpy() if tdt is not None else X
-    cfg = awq.AwqConfig(bits=bits, n_grid=n_grid)
+    cfg = awq.AwqConfig(bits=bits, n_grid=n_grid, form=form)
     sx, flags = awq.act_stats(Xt)
     res = awq.search_layer(Wt, Xt, sx, cfg, flags=flags)
     sx_o = oracle.act_stats(Xref)
@@ -133,30 +138,76 @@ def test_search_parity(awq, name, make, bits, n_grid):
     assert int(host(res.flags)[0]) == 0
 
 
-def test_search_is_deterministic(awq):
+@pytest.mark.parametrize("form", FORMS)
+def test_search_is_deterministic(awq, form):
     W, X = _lognormal_layer(35, 384, 512, 700)
-    say("determinism", W.shape, X.shape)
+    say("determinism", form, W.shape, X.shape)
     Wt, Xt = dev(W), dev(X)
     sx, _ = awq.act_stats(Xt)
-    r1 = awq.search_layer(Wt, Xt, sx)
-    r2 = awq.search_layer(Wt, Xt, sx)
+    cfg = awq.AwqConfig(form=form)
+    r1 = awq.search_layer(Wt, Xt, sx, cfg)
+    r2 = awq.search_layer(Wt, Xt, sx, cfg)
     assert np.array_equal(host(r1.losses).view(np.uint64), host(r2.losses).view(np.uint64))
     assert np.array_equal(host(r1.s_best), host(r2.s_best))
 
 
-def test_search_zero_rows_and_dead_channels(awq):
-    """All-zero rows (step 0, codes 0, E = 0) and all-zero activation channels (s_floor path)."""
+@pytest.mark.parametrize("form", FORMS)
+def test_search_zero_rows_and_dead_channels(awq, form):
+    """All-zero rows (step 0, codes 0, E = 0) and all-zero activation channels (s_floor path;
+    in the Gram form d_k = 0 for them)."""
     W, X = _lognormal_layer(36, 300, 384, 400)
     W[5] = 0
     W[17, 128:256] = 0
     X[:, 3] = 0
     X[:, 200:210] = 0
-    say("zero rows / dead channels", W.shape, X.shape)
+    say("zero rows / dead channels", form, W.shape, X.shape)
     Wt, Xt = dev(W), dev(X)
     sx, _ = awq.act_stats(Xt)
-    res = awq.search_layer(Wt, Xt, sx)
+    res = awq.search_layer(Wt, Xt, sx, awq.AwqConfig(form=form))
     orc = oracle.search_layer(W, X, oracle.act_stats(X))
     check_alpha(host(res.losses), orc["losses"], int(host(res.best)[0]), orc["best"])
+    assert int(host(res.flags)[0]) == 0
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_search_all_zero_activations(awq, form):
+    """X = 0: every loss is exactly 0 and the lowest index wins."""
+    W, X = _lognormal_layer(37, 256, 256, 130)
+    X[:] = 0
+    say("all-zero X", form)
+    Wt, Xt = dev(W), dev(X)
+    sx, _ = awq.act_stats(Xt)
+    res = awq.search_layer(Wt, Xt, sx, awq.AwqConfig(form=form))
+    assert np.array_equal(host(res.losses), np.zeros(20))
+    assert int(host(res.best)[0]) == 0
+
+
+GRAM_CASES = [
+    # tokens spread over many X^T X chunks (4096 tokens, 3 upper-triangle tiles -> 32 chunks)
+    ("many_chunks_256x512_m4096", lambda: _lognormal_layer(38, 256, 512, 4096)),
+    # strongly correlated channels: correlations up to 0.98, cond(X^T X) ~ 4e7
+    ("correlated_320x768_m1500", lambda: (
+        workloads.weight(39, 320, 768),
+        workloads.correlated_activations(1500, 768, rank=8, config=39))),
+    # a single 128-channel group: one ragged 256-wide tile, K steps clamped to K/32
+    ("k128_200x128_m640", lambda: _lognormal_layer(40, 200, 128, 640)),
+]
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("name,make", GRAM_CASES, ids=[c[0] for c in GRAM_CASES])
+def test_search_parity_gram_stress(awq, name, make, form):
+    W, X = make()
+    say("search", form, name, W.shape, X.shape)
+    Wt, Xt = dev(W), dev(X)
+    sx, flags = awq.act_stats(Xt)
+    res = awq.search_layer(Wt, Xt, sx, awq.AwqConfig(form=form), flags=flags)
+    orc = oracle.search_layer(W, X, oracle.act_stats(X))
+    bg = int(host(res.best)[0])
+    err, gap = check_alpha(host(res.losses), orc["losses"], bg, orc["best"])
+    say(f"max loss rel err {err:.2e}, oracle gap {gap:.2e}, alpha* {bg} / {orc['best']}")
+    assert np.array_equal(host(res.s_best), orc["scales"][bg])
+    assert int(host(flags)[0]) == 0
 
 
 # ------------------------------------------------------------------------------------------------
@@ -286,8 +337,9 @@ def test_flags_are_raised(awq):
     assert int(host(r.flags)[0]) & L.FLAG_NONFINITE_W
     Xf = X.astype(np.float32)
     Xf[5, 9] = 1e6
-    r = awq.search_layer(dev(W), dev(Xf), sx)
-    assert int(host(r.flags)[0]) & L.FLAG_X_F16_RANGE
+    for form in FORMS:
+        r = awq.search_layer(dev(W), dev(Xf), sx, awq.AwqConfig(form=form))
+        assert int(host(r.flags)[0]) & L.FLAG_X_F16_RANGE, form
     Xb = np.full((9000, 8), 60000.0, np.float16)
     _, f = awq.act_stats(dev(Xb))
     assert int(host(f)[0]) & L.FLAG_STATS_INEXACT
@@ -326,13 +378,17 @@ def test_search_parity_layer_shapes(awq, name, make, k, m, bits):
     Wt, Xt = dev(W), dev(X)
     sx, flags = awq.act_stats(Xt)
     res = awq.search_layer(Wt, Xt, sx, awq.AwqConfig(bits=bits), flags=flags)
+    res_g = awq.search_layer(Wt, Xt, sx, awq.AwqConfig(bits=bits, form="gram"), flags=flags)
     sx_o = oracle.act_stats(X)
     assert np.array_equal(host(sx), sx_o)
-    form = "gram" if 2 * m > k else "direct"
-    orc = oracle.search_layer(W, X, sx_o, bits=bits, form=form)
+    oform = "gram" if 2 * m > k else "direct"
+    orc = oracle.search_layer(W, X, sx_o, bits=bits, form=oform)
     bg = int(host(res.best)[0])
     err, gap = check_alpha(host(res.losses), orc["losses"], bg, orc["best"])
-    say(f"max loss rel err {err:.2e}, oracle gap {gap:.2e}, alpha* {bg} / {orc['best']}")
+    say(f"direct: max loss rel err {err:.2e}, oracle gap {gap:.2e}, alpha* {bg} / {orc['best']}")
+    bgg = int(host(res_g.best)[0])
+    err, gap = check_alpha(host(res_g.losses), orc["losses"], bgg, orc["best"])
+    say(f"gram:   max loss rel err {err:.2e}, alpha* {bgg}")
     rows = np.arange(0, W.shape[0], 97)
     p = awq.pack_int4(Wt, res.s_best, awq.AwqConfig(bits=bits), with_codes=True)
     o = oracle.pack_layer(W[rows], orc["scales"][bg], bits=bits)
@@ -351,10 +407,12 @@ def test_full_c2_layer(awq):
     Wt, Xt = dev(L.W), dev(L.X)
     sx, flags = awq.act_stats(Xt)
     res = awq.search_layer(Wt, Xt, sx, flags=flags)
+    res_g = awq.search_layer(Wt, Xt, sx, awq.AwqConfig(form="gram"), flags=flags)
     p = awq.pack_int4(Wt, res.s_best, flags=flags, with_codes=True)
     A = workloads.w4a16_activations(16, 4096, config=2)
     Y = awq.w4a16_gemm(dev(A), p.qweight, p.scales16, p.s16)
     sx_g, losses, bg = host(sx), host(res.losses), int(host(res.best)[0])
+    losses_g, bgg = host(res_g.losses), int(host(res_g.best)[0])
     codes_g, qw_g, sc_g, s16_g, Y_g = (host(p.codes), host(p.qweight).view(np.uint32),
                                        host(p.scales16), host(p.s16), host(Y))
     assert int(host(flags)[0]) == 0
@@ -369,10 +427,13 @@ def test_full_c2_layer(awq):
     for i in range(20):
         q, d = oracle.quantize(L.W, S[i])
         lo[i] = oracle.loss_gram(H, oracle.error_matrix(L.W, q, d, S[i]), L.X.shape[0])
-        say(f"oracle alpha {i}: L = {lo[i]:.9e}  gpu {losses[i]:.9e}")
+        say(f"oracle alpha {i}: L = {lo[i]:.9e}  gpu direct {losses[i]:.9e}  "
+            f"gram {losses_g[i]:.9e}")
     best_o = oracle.argmin_lowest(lo)
     err, gap = check_alpha(losses, lo, bg, best_o)
-    say(f"max loss rel err {err:.2e}, oracle gap {gap:.2e}, alpha* {bg} / {best_o}")
+    say(f"direct: max loss rel err {err:.2e}, oracle gap {gap:.2e}, alpha* {bg} / {best_o}")
+    err, gap = check_alpha(losses_g, lo, bgg, best_o)
+    say(f"gram:   max loss rel err {err:.2e}, alpha* {bgg}")
     orc = {"scales": S}
     rows = np.arange(0, 4096, 61)
     o = oracle.pack_layer(L.W[rows], orc["scales"][bg])

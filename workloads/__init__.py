@@ -72,6 +72,20 @@ def activations(config: int, m: int, gains: np.ndarray, dtype=np.float16, j: int
     return out
 
 
+def correlated_activations(m: int, k: int, rank: int, config: int, dtype=np.float16,
+                           noise: float = 0.1) -> np.ndarray:
+    """Channels that move together: X = (Z F + noise * N) * gains with Z [m, rank] and
+    F [rank, k] standard normal (t = 1 for Z and N, t = 2 for F and the gains), so many channel
+    pairs have correlations near +-1. Stands in for the correlated hidden states of a real
+    model; the main workloads keep independent channels."""
+    g = rng(config, 1)
+    gf = rng(config, 2)
+    F = gf.standard_normal((rank, k)) / np.sqrt(rank)
+    gains = np.exp(gf.standard_normal(k))
+    z = g.standard_normal((m, rank)) @ F + noise * g.standard_normal((m, k))
+    return (z * gains[None, :]).astype(dtype)
+
+
 @dataclasses.dataclass
 class Layer:
     name: str
