@@ -4,13 +4,18 @@
 One step = one pass of the whole path over the LLaMA-7B-shaped attention projection (W fp16
 4096x4096, 65536 calibration tokens = 128 samples x 512 tokens, INT4, group 128, 20 alpha points):
     awq_act_stats -> awq_search_layer -> awq_pack_int4(s*) -> w4a16_gemm (decode, M = 1).
-Inputs are synthetic (seeded, see workloads/) and resident in HBM before the timed region.
+The search runs in the Gram form (H = X^T X once, then one K x K contraction per grid point);
+--form direct times the direct form (X contracted with every error matrix) instead. Inputs are
+synthetic (seeded, see workloads/) and resident in HBM before the timed region.
 
 Prints ONE JSON line. `value` is milliseconds per layer (lower is better). Besides the contract
 fields it carries
-  roofline      the loss contraction (the dominant kernel) against the dense fp16 MFMA peak,
-                its duration measured with HIP events on the library's stream in every step;
-  stages_ms     mean duration of every kernel of the step;
+  roofline      the step's longest kernel against the dense fp16 MFMA peak, its duration
+                measured with HIP events on the library's stream in every step; `mfma` lists
+                every MFMA kernel of the step the same way;
+  stages_ms     mean duration of every kernel of the search;
+  other_form    the search in the other form (a few repetitions): ms and its loss kernel;
+  hbm_stages    the bandwidth-bound kernels: algorithmic bytes, GB/s, fraction of 8 TB/s;
   w4a16         the W4A16 kernel at the batch sizes 1, 4, 16, 64, 512 for 4096x4096 and
                 11008x4096, over rotated weight copies (> 256 MB, so HBM and not the
                 Infinity Cache is measured): GB/s and fraction of 8 TB/s (TFLOP/s and MFMA
@@ -42,33 +47,64 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-w4a16-sweep", action="store_true")
+    ap.add_argument("--form", choices=("gram", "direct"), default="gram",
+                    help="loss form of the timed search (the other form is reported as context)")
+    ap.add_argument("--other-form-reps", type=int, default=3,
+                    help="repetitions of the search in the other form (0: skip)")
     ap.add_argument("--mode", choices=("bench", "traffic"), default="bench",
                     help="traffic: one 1 GiB device copy (counter calibration) and one pass of "
-                         "the path, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
+                         "the path in each form, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
     return ap.parse_args()
 
 
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "lossgemm_c2_traffic.json")
-LOSS_SRC = os.path.join(ROOT, "post_weight_quantization_channel_amd", "csrc", "lossgemm.hip")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "search_c2_traffic.json")
+CSRC = os.path.join(ROOT, "post_weight_quantization_channel_amd", "csrc")
+# the sources each MFMA kernel is compiled from (a counter record is valid only for these bytes)
+KERNEL_SOURCES = {
+    "lossgemm_kernel": ("lossgemm.hip", "mfma_kloop.h", "device_common.h"),
+    "gram_loss_kernel": ("gram.hip", "mfma_kloop.h", "device_common.h"),
+    "gram_gemm_kernel": ("gram.hip", "mfma_kloop.h", "device_common.h"),
+}
 
 
-def source_digest(path):
+def source_digest(kernel):
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per loss-kernel launch from the committed counter record, or None when the
-    kernel source has changed since the counters were taken."""
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter record, or None when the
+    kernel's sources have changed since the counters were taken."""
     try:
         with open(TRAFFIC_RECORD) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            rec = json.load(f)["kernels"][kernel]
+    except (OSError, ValueError, KeyError):
         return None
-    if rec.get("lossgemm_src_sha256_16") != source_digest(LOSS_SRC):
+    if rec.get("src_sha256_16") != source_digest(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def gram_loss_flops(N, K, n_grid):
+    """MFMA flops of one Gram-form loss launch: per grid point and 256-row tile of E, column
+    tile lt runs min(8 (lt + 1), K / 32) K steps of a 256 x 256 x 32 product (the lower
+    triangle plus the diagonal blocks in full): ~ n_grid N K (K + 256)."""
+    t = -(-K // 256)
+    tiles_n = -(-N // 256)
+    steps = sum(min(8 * (lt + 1), K // 32) for lt in range(t))
+    return 2.0 * 256 * 256 * 32 * steps * tiles_n * n_grid
+
+
+def gram_gemm_flops(M, K):
+    """MFMA flops of X^T X: the t (t + 1) / 2 upper-triangle 256 x 256 tiles over the padded
+    token count: ~ M K (K + 256)."""
+    t = -(-K // 256)
+    Mp = -(-M // 128) * 128
+    return 2.0 * 256 * 256 * Mp * (t * (t + 1) // 2)
 
 
 def traffic_pass():
@@ -88,14 +124,17 @@ def traffic_pass():
     W = (0.02 * torch.randn(N_, K_, device=dev, generator=g)).half()
     X = (torch.randn(M_, K_, device=dev, generator=g) *
          torch.exp(torch.randn(K_, device=dev, generator=g))).half()
-    cfg = awq.AwqConfig(n_grid=N_GRID)
     sx, flags = awq.act_stats(X)
-    res = awq.search_layer(W, X, sx, cfg, flags=flags)
+    for form in ("direct", "gram"):
+        cfg = awq.AwqConfig(n_grid=N_GRID, form=form)
+        res = awq.search_layer(W, X, sx, cfg, flags=flags)
+        torch.cuda.synchronize()
+        log(form, "search done; alpha*", int(res.best.item()))
     p = awq.pack_int4(W, res.s_best, cfg, flags=flags)
     awq.w4a16_gemm(torch.ones(1, K_, dtype=torch.float16, device=dev), p.qweight, p.scales16,
                    p.s16)
     torch.cuda.synchronize()
-    log("path pass done; alpha*", int(res.best.item()))
+    log("path pass done")
 
 
 def log(*a):
@@ -216,7 +255,7 @@ def main():
     W = torch.from_numpy(L.W).to(dev)
     X = torch.from_numpy(L.X).to(dev)
     A1 = torch.from_numpy(workloads.w4a16_activations(1, K_, config=2)).to(dev)
-    cfg = awq.AwqConfig(bits=4, group=128, n_grid=N_GRID)
+    cfg = awq.AwqConfig(bits=4, group=128, n_grid=N_GRID, form=args.form)
     ws_stats = torch.empty(awq.act_stats_workspace_bytes(M_, K_), dtype=torch.uint8, device=dev)
     ws_search = torch.empty(awq.search_workspace_bytes(M_, N_, K_, torch.float16, cfg),
                             dtype=torch.uint8, device=dev)
@@ -266,25 +305,65 @@ def main():
     log(f"ms/step {ms_per_step:.3f}; stages {stages}; stats {stats_ms:.4f} ms; pack "
         f"{pack_ms:.4f} ms; alpha* {best}; flags {flag_bits}")
 
-    loss_ms = stages["lossgemm"]
-    flops = 2.0 * M_ * N_ * K_ * N_GRID
-    achieved = flops / (loss_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "lossgemm_kernel", "achieved": round(achieved, 1),
+    def mfma_rec(kernel, ms, flops):
+        achieved = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 1),
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
-                "flops_per_launch": flops, "launch_ms": round(loss_ms, 4)}
+                "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(kernel), "flops_per_launch": flops,
+                "launch_ms": round(ms, 4)}
 
+    if args.form == "gram":
+        mfma = [mfma_rec("gram_loss_kernel", stages["loss"], gram_loss_flops(N_, K_, N_GRID)),
+                mfma_rec("gram_gemm_kernel", stages["gram_gemm"], gram_gemm_flops(M_, K_))]
+    else:
+        mfma = [mfma_rec("lossgemm_kernel", stages["loss"], 2.0 * M_ * N_ * K_ * N_GRID)]
+    roofline = max(mfma, key=lambda r: r["launch_ms"])
+
+    t_ = -(-K_ // 256)
     other = {
         "act_stats": {"ms": round(stats_ms, 4), "bytes": M_ * K_ * 2},
         "quantize_stack": {"ms": round(stages["quantize_stack"], 4),
                            "bytes": N_ * K_ * 2 + N_GRID * N_ * K_ * 2},
         "pack": {"ms": round(pack_ms, 4), "bytes": N_ * K_ * 2 + N_ * K_ // 2 + N_ * K_ // 64},
     }
+    if args.form == "gram":
+        other["x_transpose"] = {"ms": round(stages["x_prep"], 4), "bytes": 2 * M_ * K_ * 2}
     for v in other.values():
         v["gbs"] = round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)
         v["hbm_frac"] = round(v["gbs"] / HBM_PEAK_GBS, 4)
 
-    del ws_search, X
+    other_form = None
+    if args.other_form_reps > 0:
+        oform = "direct" if args.form == "gram" else "gram"
+        ocfg = awq.AwqConfig(bits=4, group=128, n_grid=N_GRID, form=oform)
+        del ws_search
+        torch.cuda.empty_cache()
+        ws_o = torch.empty(awq.search_workspace_bytes(M_, N_, K_, torch.float16, ocfg),
+                           dtype=torch.uint8, device=dev)
+        sx_o, _ = awq.act_stats(X, workspace=ws_stats)
+        runs = []
+        for r in range(args.other_form_reps + 1):       # the first run is a warm-up
+            prof = {}
+            ro = awq.search_layer(W, X, sx_o, ocfg, workspace=ws_o, stage_ms=prof)
+            if r:
+                runs.append(prof)
+        ost = {k: statistics.mean(p[k] for p in runs) for k in runs[0]}
+        lo = ro.losses.cpu().numpy()
+        if oform == "direct":
+            orec = mfma_rec("lossgemm_kernel", ost["loss"], 2.0 * M_ * N_ * K_ * N_GRID)
+        else:
+            orec = mfma_rec("gram_loss_kernel", ost["loss"], gram_loss_flops(N_, K_, N_GRID))
+        other_form = {"form": oform, "search_ms": round(sum(ost.values()), 3),
+                      "alpha_star": int(ro.best.item()),
+                      "max_loss_rel_diff": float(np.max(np.abs(lo - losses) / losses)),
+                      "loss_kernel": orec, "stages_ms": {k: round(v, 4) for k, v in ost.items()}}
+        log("other form", other_form)
+        del ws_o
+    else:
+        del ws_search
+
+    del X
     torch.cuda.empty_cache()
     w4 = [] if args.no_w4a16_sweep else w4a16_sweep(awq, torch)
 
@@ -301,10 +380,13 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": "llama7b_attn_proj_4096x4096_tokens65536_int4_g128_grid20",
                    "N": N_, "K": K_, "M": M_, "bits": 4, "group": 128, "n_grid": N_GRID,
-                   "w4a16_decode_m": 1},
+                   "w4a16_decode_m": 1, "search_form": args.form},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "search_form": args.form,
+        "mfma": mfma,
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "other_form": other_form,
         "hbm_stages": other,
         "w4a16": w4,
         "alpha_star": best,

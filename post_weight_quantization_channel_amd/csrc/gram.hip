@@ -19,8 +19,8 @@
 //                    (the K loop of mfma_kloop.h), fp32 accumulation, stored in fragment order;
 //   gram_diag        d_k = sqrt(sum over chunks of the H_kk partials) in fp64;
 //   gram_finish      B from the fp64 sums of the partials (fixed chunk order);
-//   gram_loss        per (grid point, row tile, pair of column tiles): P on the MFMA K loop,
-//                    epilogue 2 sum E'_nl P_nl against E' read back from the error stack.
+//   gram_loss        per (grid point, row tile, column tile): P on the MFMA K loop, epilogue
+//                    2 sum E'_nl P_nl against E' read back from the error stack.
 #include "mfma_kloop.h"
 
 namespace awq {
@@ -228,17 +228,21 @@ __global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restric
 }
 
 // ------------------------------------------------------------------------------------------
-// Workgroup (grid point, row tile nt, pair q) computes the column tiles t-1-q and q (one if they
-// coincide): lt needs the K steps of channels below 256 (lt + 1) only, so every pair costs the
-// same 8 (t + 1) steps and the grid has no long tail.
+// Workgroup (grid point, row tile nt, column tile lt): column tile lt needs the K steps of
+// channels below 256 (lt + 1) only. The tiles of one row panel are consecutive in the logical
+// order, longest first, so the workgroups resident on an XCD share E' panels in its L2 and the
+// short tiles fill in behind the long ones. (Pairing tiles lt and t-1-lt in one workgroup
+// balances the work exactly but was slower: the second tile of a pair runs out of phase with
+// its neighbours and loses the L2 sharing.)
 __global__ __launch_bounds__(kloop::kThreads, 1) void gram_loss_kernel(
     const uint16_t* __restrict__ Est, int64_t N, int64_t K, const uint16_t* __restrict__ B,
-    int tilesN, int t, int pairs, double* __restrict__ partials) {
+    int tilesN, int t, double* __restrict__ partials) {
   using namespace kloop;
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   __shared__ double wsum[4];
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
-  const int panel = logical / pairs, q = logical % pairs;
+  const int panel = logical / t;
+  const int lt = t - 1 - logical % t;
   const int alpha = panel / tilesN, nt = panel % tilesN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t rows = (N - (int64_t)nt * BM < BM) ? N - (int64_t)nt * BM : BM;
@@ -247,15 +251,11 @@ __global__ __launch_bounds__(kloop::kThreads, 1) void gram_loss_kernel(
 
   Tile T_;
   T_.ra = make_rsrc(Ep, (uint32_t)(rows * K * 2));
+  const int64_t brows = (K - (int64_t)lt * BN < BN) ? K - (int64_t)lt * BN : BN;
+  T_.rb = make_rsrc(B + (int64_t)lt * BN * K, (uint32_t)(brows * K * 2));
   tile_setup(T_, smem, (uint32_t)(K * 2));
   const int wm = T_.wave >> 1, wn = T_.wave & 1;
-
-#pragma nounroll
-  for (int u = 0; u < 2; ++u) {
-    const int lt = (u == 0) ? t - 1 - q : q;
-    if (u == 1 && lt == t - 1 - q) break;
-    const int64_t brows = (K - (int64_t)lt * BN < BN) ? K - (int64_t)lt * BN : BN;
-    T_.rb = make_rsrc(B + (int64_t)lt * BN * K, (uint32_t)(brows * K * 2));
+  {
     const int nk = (8 * (lt + 1) < nk_all) ? 8 * (lt + 1) : nk_all;
     floatx16 acc[4][4];
     acc_zero(acc);
@@ -295,12 +295,11 @@ __global__ __launch_bounds__(kloop::kThreads, 1) void gram_loss_kernel(
       }
     for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
     if (lane == 0) wsum[T_.wave] = tot;
-    __syncthreads();   // also: no wave reads the LDS tile any more
+    __syncthreads();
     if (tid == 0) {
       const double v = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
       partials[(int64_t)alpha * ((int64_t)tilesN * t) + (int64_t)nt * t + lt] = 2.0 * v;
     }
-    __syncthreads();
   }
 }
 
@@ -349,10 +348,9 @@ hipError_t launch_gram_loss(const uint16_t* Estack, int64_t N, int64_t K, const 
                             int n_grid, double* partials, hipStream_t stream) {
   const int tilesN = (int)((N + kLossBM - 1) / kLossBM);
   const int t = (int)((K + kLossBN - 1) / kLossBN);
-  const int pairs = (t + 1) / 2;
-  const int64_t blocks = (int64_t)n_grid * tilesN * pairs;
+  const int64_t blocks = (int64_t)n_grid * tilesN * t;
   gram_loss_kernel<<<(unsigned)blocks, kloop::kThreads, 0, stream>>>(Estack, N, K, B, tilesN, t,
-                                                                     pairs, partials);
+                                                                     partials);
   return hipGetLastError();
 }
 
