@@ -35,6 +35,11 @@ Readings taken where the pages are silent, ambiguous or disagree (each is also u
   R11 packing: 8 two's-complement nibbles per uint32, element 8j+t at bits 4t ([eng] 三 says
       "INT4 packed" only); steps and s stored as fp16 (round to nearest even).
   R12 W4A16 divides the activation by s: y = sum_k (A[m,k]/s[k]) q[n,k] step[n,k/G].
+  R17 clipping ([notes] 方法 lists "clip the scaled-up weights" among further optimisations and
+      says nothing more): per (row, group), W*s is clipped to [-r max|W*s|, r max|W*s|] before
+      it is quantized; r is chosen on the grid 1 .. clip_min at the fixed s*, by the part of the
+      output error that the group causes on its own (the [notes] objective restricted to the
+      group's channels, so that the choices are separable), lowest index on ties.
 """
 from __future__ import annotations
 
@@ -97,7 +102,7 @@ def code_range(bits: int) -> tuple[int, int]:
     return -(2 ** (bits - 1)), 2 ** (bits - 1) - 1
 
 
-def quantize(W: np.ndarray, s: np.ndarray, bits: int = 4, group: int = 128):
+def quantize(W: np.ndarray, s: np.ndarray, bits: int = 4, group: int = 128, clip=None):
     """Codes and steps of Q(W*s), one step per (row, group of `group` input channels).
 
     Steps in the order of [notes] 方法 (Q(w) = Delta * Round(w / Delta)) and [eng] 三 Step 4:
@@ -105,6 +110,9 @@ def quantize(W: np.ndarray, s: np.ndarray, bits: int = 4, group: int = 128):
       m     = max |ws| over the group               (R4)
       Delta = fp32(m / qmax)                        IEEE division (R1)
       q     = clamp(rint(fp32(ws / Delta)))         round half to even (R7), clamp (R2)
+    With `clip` (fp32 ratios r in (0, 1], one per (row, group)), the scaled weights are first
+    clipped to [-c, c], c = fp32(r * m) ([notes] 方法, further optimisations: clip the scaled-up
+    weights; R17), and the steps above run on the clipped values (so m becomes c).
     Returns (q int8 [N, K], Delta fp32 [N, K/group]).
     """
     W = np.asarray(W)
@@ -117,6 +125,12 @@ def quantize(W: np.ndarray, s: np.ndarray, bits: int = 4, group: int = 128):
     w = W.astype(F32)                                  # exact for fp16 / fp32 inputs
     ws = w * np.asarray(s, dtype=F32)[None, :]         # fp32 * fp32 -> fp32, round to nearest
     wsg = ws.reshape(N, K // group, group)
+    if clip is not None:
+        r = np.asarray(clip, dtype=F32).reshape(N, K // group)
+        if not np.all((r > 0) & (r <= 1)):
+            raise ValueError("clip ratios must lie in (0, 1]")
+        c = (r * np.abs(wsg).max(axis=2)).astype(F32)  # fp32 * fp32 -> fp32
+        wsg = np.clip(wsg, -c[:, :, None], c[:, :, None])
     m = np.abs(wsg).max(axis=2)
     delta = (m / F32(qmax)).astype(F32)                # fp32 / fp32 -> fp32
     live = delta > 0                                   # R8
@@ -168,6 +182,55 @@ def loss_gram(H: np.ndarray, E: np.ndarray, M: int) -> float:
     """L = sum_n E_n H E_n^T / (M N): the same value as output_loss, since
     ||X E^T||_F^2 = trace(E X^T X E^T)."""
     return float(((E @ H) * E).sum() / (M * E.shape[0]))
+
+
+def clip_grid(n_clip: int = 11, clip_min: float = 0.5) -> np.ndarray:
+    """Clip ratios r_j = fp32(1 - (1 - clip_min) j / (n_clip - 1)), j = 0 .. n_clip-1: from no
+    clipping (r = 1) down to clip_min, evenly in fp64, each rounded once to fp32 (R17)."""
+    if n_clip < 2 or not (0.0 < clip_min < 1.0):
+        raise ValueError("n_clip >= 2 and 0 < clip_min < 1 required")
+    return np.array([1.0 - (1.0 - clip_min) * j / (n_clip - 1) for j in range(n_clip)],
+                    dtype=F64).astype(F32)
+
+
+def group_errors(E: np.ndarray, group: int = 128, X=None, H=None) -> np.ndarray:
+    """err[n, g] = sum_m ( sum_{k in g} X[m, k] E[n, k] )^2: the part of the output error of row
+    n that the channels of group g cause on their own, in fp64. With H = X^T X it is the same
+    value as E_g H_gg E_g^T (the diagonal block of H)."""
+    E = np.asarray(E, dtype=F64)
+    N, K = E.shape
+    out = np.empty((N, K // group), dtype=F64)
+    for g in range(K // group):
+        sl = slice(g * group, (g + 1) * group)
+        if H is not None:
+            Eg = E[:, sl]
+            out[:, g] = np.einsum("nk,kl,nl->n", Eg, np.asarray(H, dtype=F64)[sl, sl], Eg)
+        else:
+            P = np.asarray(X).astype(F64)[:, sl] @ E[:, sl].T          # [M, N]
+            out[:, g] = (P * P).sum(axis=0)
+    return out
+
+
+def clip_search(W, X, s, bits: int = 4, group: int = 128, n_clip: int = 11,
+                clip_min: float = 0.5, H=None):
+    """Per (row, group), the clip ratio of `clip_grid` whose quantization of W*s gives the
+    smallest group error (`group_errors`), the lowest index on ties (R17, R10). The search runs
+    at a fixed s (typically s*). Returns {"ratio": fp32 [N, K/group], "best": int [N, K/group],
+    "err": fp64 [n_clip, N, K/group]}."""
+    r = clip_grid(n_clip, clip_min)
+    W = np.asarray(W)
+    N, K = W.shape
+    s = np.asarray(s, dtype=F32)
+    err = np.empty((n_clip, N, K // group), dtype=F64)
+    for j in range(n_clip):
+        q, d = quantize(W, s, bits, group, clip=np.full((N, K // group), r[j], dtype=F32))
+        E = error_matrix(W, q, d, s, group)
+        err[j] = group_errors(E, group, X=None if H is not None else X, H=H)
+    best = np.zeros((N, K // group), dtype=np.int64)
+    for j in range(1, n_clip):                      # strict < keeps the lowest index on ties
+        better = err[j] < err[best, np.arange(N)[:, None], np.arange(K // group)[None, :]]
+        best = np.where(better, j, best)
+    return {"ratio": r[best], "best": best, "err": err}
 
 
 def argmin_lowest(losses) -> int:
@@ -235,11 +298,12 @@ def unpack_int4(qweight: np.ndarray) -> np.ndarray:
     return out
 
 
-def pack_layer(W, s, bits: int = 4, group: int = 128):
+def pack_layer(W, s, bits: int = 4, group: int = 128, clip=None):
     """The stored result of [eng] 三 (QuantLinear(q_weight, scales_per_group, awq_scale)):
     packed codes of Q(W*s), per-group fp16 steps and the per-channel s in fp16 (R11).
-    The codes are those of `quantize`, not re-derived from the fp16 step."""
-    q, delta = quantize(W, s, bits, group)
+    The codes are those of `quantize` (with the clip ratios, if given), not re-derived from the
+    fp16 step."""
+    q, delta = quantize(W, s, bits, group, clip=clip)
     return {"qweight": pack_int4(q), "scales16": delta.astype(np.float16),
             "s16": np.asarray(s, dtype=F32).astype(np.float16), "codes": q, "delta": delta}
 

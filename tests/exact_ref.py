@@ -63,11 +63,17 @@ def pow_rn32(x: float, a: float, digits: int = 45) -> np.float32:
     return rn32(Fraction(v))
 
 
-def quantize_group_exact(w, s, qmin: int, qmax: int):
-    """One group: ws = rn32(w s); Delta = rn32(max|ws| / qmax); code = nearest code to
-    rn32(ws / Delta). Returns (codes, Delta) with Delta an fp32 value."""
-    ws = [rn32(Fraction(float(wi)) * Fraction(float(si))) for wi, si in zip(w, s)]
-    m = max(abs(Fraction(float(v))) for v in ws)
+def quantize_group_exact(w, s, qmin: int, qmax: int, ratio=None):
+    """One group: ws = rn32(w s); with a clip ratio r, every ws is first moved into [-c, c],
+    c = rn32(r max|ws|); Delta = rn32(max|ws| / qmax) of the (clipped) values; code = nearest
+    code to rn32(ws / Delta). Returns (codes, Delta) with Delta an fp32 value."""
+    ws = [Fraction(float(rn32(Fraction(float(wi)) * Fraction(float(si)))))
+          for wi, si in zip(w, s)]
+    m = max(abs(v) for v in ws)
+    if ratio is not None:
+        c = Fraction(float(rn32(Fraction(float(ratio)) * m)))
+        ws = [min(max(v, -c), c) for v in ws]
+        m = max(abs(v) for v in ws)
     if m == 0:
         return [0] * len(w), np.float32(0.0)
     delta = rn32(m / qmax)
@@ -75,9 +81,20 @@ def quantize_group_exact(w, s, qmin: int, qmax: int):
         return [0] * len(w), np.float32(0.0)
     codes = []
     for v in ws:
-        t = rn32(Fraction(float(v)) / Fraction(float(delta)))
+        t = rn32(v / Fraction(float(delta)))
         codes.append(nearest_code(Fraction(float(t)), qmin, qmax))
     return codes, delta
+
+
+def group_error_exact(X, w, s, codes, delta):
+    """sum_m ( sum_k X[m,k] (code_k Delta / s_k - w_k) )^2 over one group, exactly."""
+    e = [Fraction(c) * Fraction(float(delta)) / Fraction(float(sk)) - Fraction(float(wk))
+         for c, sk, wk in zip(codes, s, w)]
+    tot = Fraction(0)
+    for row in X:
+        acc = sum(Fraction(float(x)) * ek for x, ek in zip(row, e))
+        tot += acc * acc
+    return tot
 
 
 def loss_exact(X, W, codes, deltas, s, group: int) -> Fraction:

@@ -318,3 +318,93 @@ def test_nonfinite_inputs_are_rejected():
         oracle.quantize(W, np.ones(128, np.float32))
     with pytest.raises(ValueError):
         oracle.act_stats(np.array([[np.inf, 1.0]]))
+
+
+# --- P13: clipping (R17) ---------------------------------------------------------------------
+def _outlier_layer(seed, n, k, m):
+    """Groups with a few large weights of either sign among small ones, so that clipping
+    changes codes in both directions."""
+    g = np.random.default_rng(seed)
+    W = (0.02 * g.standard_normal((n, k))).astype(np.float32)
+    for r in range(n):
+        for g0 in range(0, k, 128):
+            idx = g.choice(128, 2, replace=False) + g0
+            W[r, idx] = np.float32(0.3) * np.sign(g.standard_normal(2)).astype(np.float32)
+    X = g.standard_normal((m, k)).astype(np.float32)
+    s = np.exp(0.3 * g.standard_normal(k)).astype(np.float32)
+    return W, X, s
+
+
+def test_p13_ratio_one_is_the_unclipped_quantizer():
+    W, X, s = _outlier_layer(60, 7, 384, 5)
+    q0, d0 = oracle.quantize(W, s, 4, 128)
+    q1, d1 = oracle.quantize(W, s, 4, 128, clip=np.ones((7, 3), np.float32))
+    assert np.array_equal(q0, q1) and np.array_equal(d0, d1)
+
+
+def test_p13_group_errors_add_up_to_the_output_loss():
+    """For a single-group layer the group errors of all rows add up to M N L of the literal
+    objective (output_loss); for several groups the direct and Gram evaluations agree."""
+    W, X, s = _outlier_layer(61, 9, 128, 40)
+    q, d = oracle.quantize(W, s, 4, 128)
+    err = oracle.group_errors(oracle.error_matrix(W, q, d, s), 128, X=X)
+    L = oracle.output_loss(X, W, s, oracle.dequant_scaled(q, d))
+    assert err.sum() == pytest.approx(L * X.shape[0] * W.shape[0], rel=1e-12)
+    W2, X2, s2 = _outlier_layer(62, 5, 512, 30)
+    q2, d2 = oracle.quantize(W2, s2, 4, 128)
+    E2 = oracle.error_matrix(W2, q2, d2, s2)
+    np.testing.assert_allclose(oracle.group_errors(E2, 128, X=X2),
+                               oracle.group_errors(E2, 128, H=oracle.gram(X2)), rtol=1e-11)
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_p13_clip_search_brute_force_exact(bits):
+    """Every clipped code is the nearest code to the fp32 quotient of the clipped value, every
+    group error equals the exact rational, and each (row, group) gets the exhaustive argmin."""
+    W, X, s = _outlier_layer(63 + bits, 3, 256, 6)
+    n_clip, clip_min = 6, 0.4
+    res = oracle.clip_search(W, X, s, bits=bits, n_clip=n_clip, clip_min=clip_min)
+    ratios = oracle.clip_grid(n_clip, clip_min)
+    qmin, qmax = oracle.code_range(bits)
+    for n in range(3):
+        for g in range(2):
+            sl = slice(128 * g, 128 * (g + 1))
+            errs = []
+            for j, r in enumerate(ratios):
+                codes, delta = ex.quantize_group_exact(W[n, sl], s[sl], qmin, qmax, ratio=r)
+                q, d = oracle.quantize(W, s, bits, 128, clip=np.full((3, 2), r, np.float32))
+                assert list(q[n, sl]) == codes and d[n, g] == delta, (n, g, j)
+                e = ex.group_error_exact(X[:, sl], W[n, sl], s[sl], codes, delta)
+                errs.append(e)
+                assert res["err"][j, n, g] == pytest.approx(float(e), rel=1e-12)
+            best = min(range(n_clip), key=lambda j: (errs[j], j))
+            assert res["best"][n, g] == best
+            assert res["ratio"][n, g] == ratios[best]
+
+
+def test_p13_clipping_helps_an_outlier_group():
+    """One weight of 1 among 127 weights of 0.06, unit activations on every channel (X = I):
+    unclipped, the step is 1/7 and every small weight rounds to 0 (error 127 * 0.06^2); half-way
+    clipping (r = 0.5) costs 0.5^2 on the outlier but represents the small weights (code 1,
+    step 1/14), so the search must leave r = 1."""
+    W = np.full((1, 128), 0.06, np.float32)
+    W[0, 0] = 1.0
+    X = np.eye(128, dtype=np.float32)
+    s = np.ones(128, np.float32)
+    res = oracle.clip_search(W, X, s, n_clip=11, clip_min=0.5)
+    w_small = float(np.float32(0.06))
+    assert res["err"][0, 0, 0] == pytest.approx(127 * w_small ** 2, rel=1e-6)
+    r05 = 0.25 + 127 * (w_small - 1 / 14) ** 2
+    assert res["err"][10, 0, 0] == pytest.approx(r05, rel=1e-5)
+    assert res["best"][0, 0] > 0 and res["err"][res["best"][0, 0], 0, 0] <= r05
+
+
+def test_p13_ties_keep_the_lowest_ratio_index():
+    """A zero weight group, or a group whose channels never activate, has error 0 at every
+    ratio: the first grid point (r = 1, no clipping) is kept (R10)."""
+    W, X, s = _outlier_layer(67, 4, 256, 8)
+    W[1, :128] = 0
+    X[:, 128:] = 0
+    res = oracle.clip_search(W, X, s, n_clip=5, clip_min=0.5)
+    assert res["best"][1, 0] == 0 and res["ratio"][1, 0] == np.float32(1.0)
+    assert (res["best"][:, 1] == 0).all() and (res["err"][:, :, 1] == 0).all()
