@@ -186,10 +186,12 @@ def loss_gram(H: np.ndarray, E: np.ndarray, M: int) -> float:
 
 def clip_grid(n_clip: int = 11, clip_min: float = 0.5) -> np.ndarray:
     """Clip ratios r_j = fp32(1 - (1 - clip_min) j / (n_clip - 1)), j = 0 .. n_clip-1: from no
-    clipping (r = 1) down to clip_min, evenly in fp64, each rounded once to fp32 (R17)."""
-    if n_clip < 2 or not (0.0 < clip_min < 1.0):
+    clipping (r = 1) down to clip_min, evenly in fp64 (clip_min taken as an fp32 value, the
+    precision of the configuration), each rounded once to fp32 (R17)."""
+    cm = float(F32(clip_min))
+    if n_clip < 2 or not (0.0 < cm < 1.0):
         raise ValueError("n_clip >= 2 and 0 < clip_min < 1 required")
-    return np.array([1.0 - (1.0 - clip_min) * j / (n_clip - 1) for j in range(n_clip)],
+    return np.array([1.0 - (1.0 - cm) * j / (n_clip - 1) for j in range(n_clip)],
                     dtype=F64).astype(F32)
 
 
