@@ -8,8 +8,11 @@
  *                        group-wise symmetric round-to-nearest quantization of W*s_i, and the
  *                        output loss L_i = ||Q(W s_i)(s_i^-1 X) - W X||_F^2 / (M N);
  *                        alpha* = argmin_i L_i (lowest index on ties), s* = s_{i*}
- *   3. awq_pack_int4     codes of Q(W s*) packed 8 per uint32, fp16 group steps, fp16 s*
- *   4. w4a16_gemm        Y = (A / s) (q * step)^T with fp16 A and Y
+ *   3. awq_clip_search   (optional) per row and group, the clip ratio r of W s* that minimises
+ *                        the group's own output error
+ *   4. awq_pack_int4     codes of Q(W s*) (clipped by r if given) packed 8 per uint32, fp16
+ *                        group steps, fp16 s*
+ *   5. w4a16_gemm        Y = (A / s) (q * step)^T with fp16 A and Y
  *
  * Pages defining the operations (cited by title and section):
  *   [notes]  bg51717.github.io/14592, notes on "AWQ: Activation-aware Weight Quantization for
@@ -68,7 +71,9 @@ enum {
   AWQ_FLAG_SCALE16_OVERFLOW = 1u << 4, /* a group step or s exceeds the fp16 range at packing   */
   AWQ_FLAG_SCALE16_SUBNORMAL = 1u << 5,/* a non-zero group step or s is fp16-subnormal or 0     */
   AWQ_FLAG_NONFINITE_LOSS = 1u << 6,   /* some L_i is not finite                                */
-  AWQ_FLAG_STEP_UNDERFLOW = 1u << 7    /* a group with max|w s| > 0 got step 0 (codes set to 0)*/
+  AWQ_FLAG_STEP_UNDERFLOW = 1u << 7,   /* a group with max|w s| > 0 got step 0 (codes set to 0)*/
+  AWQ_FLAG_CLIP_RANGE = 1u << 8        /* a clip ratio given to awq_pack_int4 is outside (0, 1]; */
+                                       /* that group was packed unclipped                       */
 };
 
 /* How awq_search_layer evaluates the loss (same value, different contraction):
@@ -86,6 +91,9 @@ typedef struct {
   int32_t n_grid;  /* number of alpha points, alpha_i = i/(n_grid-1), 2 <= n_grid <= 64         */
   float s_floor;   /* s = max(s_X, s_floor)^alpha, typically 1e-5f                              */
   int32_t form;    /* AWQ_FORM_DIRECT or AWQ_FORM_GRAM                                          */
+  int32_t n_clip;  /* clipping search: ratios r_j = fp32(1 - (1 - clip_min) j / (n_clip - 1)),   */
+  float clip_min;  /* j = 0 .. n_clip-1 in fp64; 2 <= n_clip <= 64, 0 < clip_min < 1 (read by    */
+                   /* awq_clip_search only; typically 11 and 0.5)                                 */
 } awq_cfg;
 
 /* Human-readable name of a status code (static storage). */
@@ -162,20 +170,54 @@ awq_status awq_search_layer_profiled(const void* W, awq_dtype wdt, int64_t N, in
                                      hipStream_t stream, float* stage_ms);
 
 /* ------------------------------------------------------------------------------------------
+ * awq_clip_search -- clipping of the scaled-up weights, one of the further optimisations listed
+ * in [notes] 方法 (the page gives no details; the reading below is this library's).
+ * For every output row n and group g of 128 input channels, each ratio r_j of the grid in
+ * awq_cfg is tried: the group of W s is clipped to [-c, c], c = fp32(r_j max|w s|), quantized
+ * exactly as in awq_search_layer (so that Delta = c / (2^(b-1)-1)), and scored by the output
+ * error the group causes on its own,
+ *   err_j[n, g] = sum_m ( sum_{k in g} X[m,k] E[n,k] )^2,  E = Q(W s)/s - W,
+ * evaluated as E_g H_gg E_g^T with the 128 x 128 diagonal blocks of H = X^T X (fp16 correlation
+ * operand and error rows, fp32 accumulation, as in the Gram form of awq_search_layer).
+ * clip[n, g] = r of the smallest error (the lowest j on ties).
+ * W        [N, K], dtype wdt (AWQ_F16 or AWQ_F32); X [M, K] (row stride K), dtype xdt;
+ * s        fp32 [K], the scale to clip at (typically s_best of awq_search_layer).
+ * cfg      bits, group (128), n_clip, clip_min (the other fields are not read).
+ * clip     out, fp32 [N, K/128]: the chosen ratios (pass them to awq_pack_int4).
+ * clip_err out, fp32 [n_clip, N, K/128] or NULL: err_j[n, g] for every ratio.
+ * flags    in/out: NONFINITE_W, X_F16_RANGE, STEP_UNDERFLOW.
+ * ws       device workspace of at least awq_clip_workspace_bytes(M, N, K, xdt, cfg) bytes
+ *          (the transposed fp16 X dominates: K * M * 2 bytes).
+ * Limits: K a multiple of 128 and at most 2^22, M <= 2^23 - 128.
+ * Errors: AWQ_ERR_NULL, AWQ_ERR_SHAPE, AWQ_ERR_DTYPE, AWQ_ERR_CONFIG (also n_clip, clip_min),
+ *         AWQ_ERR_WORKSPACE.
+ * ---------------------------------------------------------------------------------------- */
+size_t awq_clip_workspace_bytes(int64_t M, int64_t N, int64_t K, awq_dtype xdt,
+                                const awq_cfg* cfg);
+awq_status awq_clip_search(const void* W, awq_dtype wdt, int64_t N, int64_t K, const void* X,
+                           awq_dtype xdt, int64_t M, const float* s, const awq_cfg* cfg,
+                           float* clip, float* clip_err, uint32_t* flags, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * awq_pack_int4 -- the stored result of [eng] 三 (QuantLinear(q_weight, scales_per_group,
  * awq_scale)).
  * W        [N, K], dtype wdt (AWQ_F16 or AWQ_F32); s fp32 [K] (typically s_best).
+ * clip     fp32 [N, K/group] clip ratios in (0, 1] (typically from awq_clip_search), or NULL
+ *          for none: the group of W s is clipped to +-fp32(r max|w s|) before quantization.
+ *          A ratio outside (0, 1] sets AWQ_FLAG_CLIP_RANGE and that group is packed unclipped.
  * qweight  out, uint32 [N, K/8]: qweight[n,j] = sum_t (q[n,8j+t] & 0xF) << 4t, the codes of
- *          the same quantization as awq_search_layer (bit-identical).
+ *          the same quantization as awq_search_layer / awq_clip_search (bit-identical).
  * scales16 out, fp16 bits [N, K/group]: fp16(Delta), round to nearest even.
  * s16      out, fp16 bits [K]: fp16(s).
  * codes    out, int8 [N, K] or NULL (not written).
- * flags    in/out: NONFINITE_W, SCALE16_OVERFLOW, SCALE16_SUBNORMAL, STEP_UNDERFLOW.
+ * flags    in/out: NONFINITE_W, SCALE16_OVERFLOW, SCALE16_SUBNORMAL, STEP_UNDERFLOW, CLIP_RANGE.
  * Errors: AWQ_ERR_NULL, AWQ_ERR_SHAPE, AWQ_ERR_DTYPE, AWQ_ERR_CONFIG.
  * ---------------------------------------------------------------------------------------- */
 awq_status awq_pack_int4(const void* W, awq_dtype wdt, int64_t N, int64_t K, const float* s,
-                         const awq_cfg* cfg, uint32_t* qweight, uint16_t* scales16,
-                         uint16_t* s16, int8_t* codes, uint32_t* flags, hipStream_t stream);
+                         const float* clip, const awq_cfg* cfg, uint32_t* qweight,
+                         uint16_t* scales16, uint16_t* s16, int8_t* codes, uint32_t* flags,
+                         hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * w4a16_gemm -- QuantLinear.forward of [eng] 三 on the packed artefacts:

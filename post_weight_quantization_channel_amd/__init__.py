@@ -3,10 +3,11 @@
 The engine is the HIP library libawq.so (C ABI in include/awq.h); this package holds its sources
 (csrc/), the in-tree build (build.py) and a thin torch binding (api.py) with the same call names.
 """
-from .api import (AwqConfig, PackResult, SearchResult, act_stats, act_stats_workspace_bytes,
-                  pack_int4, search_layer, search_workspace_bytes, w4a16_gemm)
+from .api import (AwqConfig, ClipResult, PackResult, SearchResult, act_stats,
+                  act_stats_workspace_bytes, clip_search, clip_workspace_bytes, pack_int4,
+                  search_layer, search_workspace_bytes, w4a16_gemm)
 from ._lib import AwqError
 
-__all__ = ["AwqConfig", "AwqError", "PackResult", "SearchResult", "act_stats",
-           "act_stats_workspace_bytes", "pack_int4", "search_layer", "search_workspace_bytes",
-           "w4a16_gemm"]
+__all__ = ["AwqConfig", "AwqError", "ClipResult", "PackResult", "SearchResult", "act_stats",
+           "act_stats_workspace_bytes", "clip_search", "clip_workspace_bytes", "pack_int4",
+           "search_layer", "search_workspace_bytes", "w4a16_gemm"]

@@ -28,11 +28,13 @@ FLAG_SCALE16_OVERFLOW = 1 << 4
 FLAG_SCALE16_SUBNORMAL = 1 << 5
 FLAG_NONFINITE_LOSS = 1 << 6
 FLAG_STEP_UNDERFLOW = 1 << 7
+FLAG_CLIP_RANGE = 1 << 8
 
 
 class AwqCfg(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32),
-                ("n_grid", ctypes.c_int32), ("s_floor", ctypes.c_float), ("form", ctypes.c_int32)]
+                ("n_grid", ctypes.c_int32), ("s_floor", ctypes.c_float), ("form", ctypes.c_int32),
+                ("n_clip", ctypes.c_int32), ("clip_min", ctypes.c_float)]
 
 
 _P = ctypes.c_void_p
@@ -52,8 +54,11 @@ SIGNATURES = {
     "awq_search_layer_profiled": (_E, [_P, _E, _I64, _I64, _P, _E, _I64, _P,
                                        ctypes.POINTER(AwqCfg), _P, _P, _P, _P, _P, _SZ, _P,
                                        ctypes.POINTER(ctypes.c_float)]),
-    "awq_pack_int4": (_E, [_P, _E, _I64, _I64, _P, ctypes.POINTER(AwqCfg), _P, _P, _P, _P, _P,
-                           _P]),
+    "awq_clip_workspace_bytes": (_SZ, [_I64, _I64, _I64, _E, ctypes.POINTER(AwqCfg)]),
+    "awq_clip_search": (_E, [_P, _E, _I64, _I64, _P, _E, _I64, _P, ctypes.POINTER(AwqCfg), _P,
+                             _P, _P, _P, _SZ, _P]),
+    "awq_pack_int4": (_E, [_P, _E, _I64, _I64, _P, _P, ctypes.POINTER(AwqCfg), _P, _P, _P, _P,
+                           _P, _P]),
     "w4a16_gemm": (_E, [_P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P]),
 }
 

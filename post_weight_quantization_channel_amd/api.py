@@ -21,18 +21,22 @@ _DT = {torch.float32: _lib.AWQ_F32, torch.float16: _lib.AWQ_F16, torch.bfloat16:
 class AwqConfig:
     """bits in {3, 4}; group = 128 input channels per step; n_grid alpha points i/(n_grid-1);
     s = max(s_X, s_floor)^alpha; form "direct" (contract X with every error matrix) or "gram"
-    (form H = X^T X once, then contract each error matrix with H)."""
+    (form H = X^T X once, then contract each error matrix with H); the clipping search tries
+    n_clip ratios from 1 down to clip_min."""
     bits: int = 4
     group: int = 128
     n_grid: int = 20
     s_floor: float = 1e-5
     form: str = "direct"
+    n_clip: int = 11
+    clip_min: float = 0.5
 
     def c(self) -> AwqCfg:
         forms = {"direct": _lib.AWQ_FORM_DIRECT, "gram": _lib.AWQ_FORM_GRAM}
         if self.form not in forms:
             raise ValueError(f"form must be one of {sorted(forms)}, got {self.form!r}")
-        return AwqCfg(self.bits, self.group, self.n_grid, self.s_floor, forms[self.form])
+        return AwqCfg(self.bits, self.group, self.n_grid, self.s_floor, forms[self.form],
+                      self.n_clip, self.clip_min)
 
 
 def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
@@ -136,15 +140,62 @@ def search_layer(W: torch.Tensor, X: torch.Tensor, sx: torch.Tensor,
     return SearchResult(losses, best, s_best, flags)
 
 
+@dataclasses.dataclass
+class ClipResult:
+    clip: torch.Tensor               # fp32 [N, K/group]: the chosen ratios
+    err: torch.Tensor | None         # fp32 [n_clip, N, K/group]: group error of every ratio
+    flags: torch.Tensor
+
+
+def clip_workspace_bytes(M: int, N: int, K: int, x_dtype: torch.dtype, cfg: AwqConfig) -> int:
+    return int(_lib.load().awq_clip_workspace_bytes(M, N, K, _DT[x_dtype], cfg.c()))
+
+
+def clip_search(W: torch.Tensor, X: torch.Tensor, s: torch.Tensor, cfg: AwqConfig = AwqConfig(),
+                with_err: bool = False, flags: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> ClipResult:
+    """Per (row, group), the clip ratio of the grid whose clipped quantization of W s gives the
+    smallest group output error."""
+    lib = _lib.load()
+    for t, nm in ((W, "W"), (X, "X"), (s, "s")):
+        _dev(t, nm)
+    N, K = W.shape
+    M = X.shape[0]
+    if X.shape[1] != K or s.shape != (K,) or s.dtype != torch.float32:
+        raise ValueError("shape mismatch: W [N,K], X [M,K], s fp32 [K]")
+    c = cfg.c()
+    flags = _flags(W.device, flags)
+    nbytes = lib.awq_clip_workspace_bytes(M, N, K, _DT[X.dtype], c)
+    if nbytes == 0:
+        raise ValueError("invalid shape or config for the clipping search")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    G = K // cfg.group
+    clip = torch.empty((N, G), dtype=torch.float32, device=W.device)
+    err = torch.empty((cfg.n_clip, N, G), dtype=torch.float32, device=W.device) \
+        if with_err else None
+    check("awq_clip_search", lib.awq_clip_search(
+        W.data_ptr(), _DT[W.dtype], N, K, X.data_ptr(), _DT[X.dtype], M, s.data_ptr(), c,
+        clip.data_ptr(), err.data_ptr() if err is not None else None, flags.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), _stream(W)))
+    return ClipResult(clip, err, flags)
+
+
 def pack_int4(W: torch.Tensor, s: torch.Tensor, cfg: AwqConfig = AwqConfig(),
-              with_codes: bool = False, flags: torch.Tensor | None = None) -> PackResult:
-    """Packed codes of Q(W s), fp16 group steps and fp16 s."""
+              with_codes: bool = False, flags: torch.Tensor | None = None,
+              clip: torch.Tensor | None = None) -> PackResult:
+    """Packed codes of Q(W s) (clipped by the per-group ratios `clip`, if given), fp16 group
+    steps and fp16 s."""
     lib = _lib.load()
     _dev(W, "W")
     _dev(s, "s")
     N, K = W.shape
     if s.shape != (K,) or s.dtype != torch.float32:
         raise ValueError("s must be fp32 [K]")
+    if clip is not None:
+        _dev(clip, "clip")
+        if clip.shape != (N, K // cfg.group) or clip.dtype != torch.float32:
+            raise ValueError("clip must be fp32 [N, K/group]")
     c = cfg.c()
     flags = _flags(W.device, flags)
     qweight = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
@@ -152,7 +203,8 @@ def pack_int4(W: torch.Tensor, s: torch.Tensor, cfg: AwqConfig = AwqConfig(),
     s16 = torch.empty(K, dtype=torch.float16, device=W.device)
     codes = torch.empty((N, K), dtype=torch.int8, device=W.device) if with_codes else None
     check("awq_pack_int4", lib.awq_pack_int4(
-        W.data_ptr(), _DT[W.dtype], N, K, s.data_ptr(), c, qweight.data_ptr(),
+        W.data_ptr(), _DT[W.dtype], N, K, s.data_ptr(),
+        clip.data_ptr() if clip is not None else None, c, qweight.data_ptr(),
         scales16.data_ptr(), s16.data_ptr(), codes.data_ptr() if codes is not None else None,
         flags.data_ptr(), _stream(W)))
     return PackResult(qweight, scales16, s16, codes, flags)

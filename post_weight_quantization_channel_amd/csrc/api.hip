@@ -105,7 +105,7 @@ const char* awq_status_string(awq_status status) {
   return "unknown awq_status";
 }
 
-int32_t awq_version(void) { return 10100; }
+int32_t awq_version(void) { return 10200; }
 
 size_t awq_act_stats_workspace_bytes(int64_t M, int64_t K) {
   if (M < 1 || K < 1 || M > kMaxDim || K > kMaxDim) return 0;
@@ -258,8 +258,9 @@ awq_status awq_search_layer_profiled(const void* W, awq_dtype wdt, int64_t N, in
 }
 
 awq_status awq_pack_int4(const void* W, awq_dtype wdt, int64_t N, int64_t K, const float* s,
-                         const awq_cfg* cfg, uint32_t* qweight, uint16_t* scales16,
-                         uint16_t* s16, int8_t* codes, uint32_t* flags, hipStream_t stream) {
+                         const float* clip, const awq_cfg* cfg, uint32_t* qweight,
+                         uint16_t* scales16, uint16_t* s16, int8_t* codes, uint32_t* flags,
+                         hipStream_t stream) {
   if (!W || !s || !cfg || !qweight || !scales16 || !s16 || !flags) return AWQ_ERR_NULL;
   const awq_status cs = check_cfg(cfg);
   if (cs != AWQ_OK) return cs;
@@ -268,8 +269,87 @@ awq_status awq_pack_int4(const void* W, awq_dtype wdt, int64_t N, int64_t K, con
       !aligned16(W) || !aligned16(s) || !aligned16(s16) ||
       (codes && (reinterpret_cast<uintptr_t>(codes) & 7u)))
     return AWQ_ERR_SHAPE;
-  return hip_status(awq::launch_pack(W, (int)wdt, N, K, s, cfg->bits, qweight, scales16, s16,
-                                     codes, flags, stream));
+  if (clip && (reinterpret_cast<uintptr_t>(clip) & 3u)) return AWQ_ERR_SHAPE;
+  return hip_status(awq::launch_pack(W, (int)wdt, N, K, s, clip, cfg->bits, qweight, scales16,
+                                     s16, codes, flags, stream));
+}
+
+namespace {
+
+struct ClipLayout {
+  size_t d64, d32, Bd, Xt, Hpart, total;
+  awq::GramPlan plan;
+};
+
+ClipLayout clip_layout(int64_t M, int64_t K) {
+  ClipLayout L{};
+  L.plan = awq::gram_plan(M, K, /*diag=*/true);
+  size_t off = 0;
+  L.d64 = off;
+  off += align_up((size_t)K * sizeof(double));
+  L.d32 = off;
+  off += align_up((size_t)K * sizeof(float));
+  L.Bd = off;
+  off += align_up((size_t)L.plan.t * (size_t)(awq::kLossBM * awq::kLossBN) * 2);
+  L.Xt = off;
+  off += align_up((size_t)K * (size_t)L.plan.Mp * 2);
+  L.Hpart = off;
+  off += align_up((size_t)L.plan.S * (size_t)L.plan.T *
+                  (size_t)(awq::kLossBM * awq::kLossBN) * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+awq_status check_clip_cfg(const awq_cfg* cfg) {
+  const awq_status cs = check_cfg(cfg);
+  if (cs != AWQ_OK) return cs;
+  if (cfg->n_clip < 2 || cfg->n_clip > 64) return AWQ_ERR_CONFIG;
+  if (!(cfg->clip_min > 0.0f && cfg->clip_min < 1.0f)) return AWQ_ERR_CONFIG;
+  return AWQ_OK;
+}
+
+bool clip_shape_ok(int64_t M, int64_t N, int64_t K, const awq_cfg* cfg) {
+  if (M < 1 || N < 1 || K < cfg->group || K % cfg->group || M > kMaxDim || N > kMaxDim ||
+      K > kMaxSearchK)
+    return false;
+  const int64_t Mp = (M + awq::kGramMAlign - 1) / awq::kGramMAlign * awq::kGramMAlign;
+  return Mp <= kMaxGramMp;
+}
+
+}  // namespace
+
+size_t awq_clip_workspace_bytes(int64_t M, int64_t N, int64_t K, awq_dtype xdt,
+                                const awq_cfg* cfg) {
+  if (check_clip_cfg(cfg) != AWQ_OK || !valid_dtype(xdt)) return 0;
+  if (!clip_shape_ok(M, N, K, cfg)) return 0;
+  return clip_layout(M, K).total;
+}
+
+awq_status awq_clip_search(const void* W, awq_dtype wdt, int64_t N, int64_t K, const void* X,
+                           awq_dtype xdt, int64_t M, const float* s, const awq_cfg* cfg,
+                           float* clip, float* clip_err, uint32_t* flags, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  if (!W || !X || !s || !cfg || !clip || !flags) return AWQ_ERR_NULL;
+  const awq_status cs = check_clip_cfg(cfg);
+  if (cs != AWQ_OK) return cs;
+  if (wdt != AWQ_F16 && wdt != AWQ_F32) return AWQ_ERR_DTYPE;
+  if (!valid_dtype(xdt)) return AWQ_ERR_DTYPE;
+  if (!clip_shape_ok(M, N, K, cfg) || !aligned16(W) || !aligned16(X) || !aligned16(s))
+    return AWQ_ERR_SHAPE;
+  const ClipLayout L = clip_layout(M, K);
+  if (!ws || ws_bytes < L.total || !aligned16(ws)) return AWQ_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  auto* d32 = reinterpret_cast<float*>(base + L.d32);
+  auto* Bd = reinterpret_cast<uint16_t*>(base + L.Bd);
+  hipError_t e = awq::launch_gram_prepare(X, (int)xdt, M, K, L.plan,
+                                          reinterpret_cast<uint16_t*>(base + L.Xt),
+                                          reinterpret_cast<float*>(base + L.Hpart),
+                                          reinterpret_cast<double*>(base + L.d64), d32, Bd, flags,
+                                          stream, nullptr);
+  if (e == hipSuccess)
+    e = awq::launch_clip_search(W, (int)wdt, N, K, s, d32, Bd, cfg->n_clip, cfg->clip_min,
+                                cfg->bits, clip, clip_err, flags, stream);
+  return hip_status(e);
 }
 
 awq_status w4a16_gemm(const uint16_t* A, int64_t M, int64_t N, int64_t K, int32_t group,

@@ -1,0 +1,215 @@
+// Clipping search: the AWQ notes (bg51717.github.io/14592, section 方法) list clipping the
+// scaled-up weights among the method's further optimisations. Per (output row n, group g of 128
+// input channels), every ratio r_j of the grid 1 .. clip_min is tried on W s: the scaled weights
+// are clipped to [-c, c], c = fp32(r_j max|w s|), quantized as in the search (quant_step /
+// quant_code), and scored by the output error the group causes on its own,
+//   err_j[n, g] = sum_m ( sum_{k in g} X[m,k] E[n,k] )^2 = E_g H_gg E_g^T,  E = Q(W s)/s - W;
+// the smallest wins, the lowest index on ties.
+//
+// The quadratic form uses the Gram form's conditioning (gram.hip): with E' = 2^e E d (d_k =
+// sqrt(H_kk), e a power of two per row and group so that |E'| < 2^15) and C the correlation
+// block, E_g H_gg E_g^T = 2^(1-2e) sum_l E'_l P_l, P_l = sum_{k<l} E'_k C_kl + E'_l / 2, where the
+// operand B_gg (strict lower correlations, 1/2 diagonal) is the diagonal block of the
+// block-diagonal correlation operand.
+//
+// gfx950 layout: a workgroup of 4 waves takes 64 rows of one group. Lane (i = lane % 16,
+// q = lane / 16) of a wave owns row 16 w + i and the channels 32 kb + 8 q + t (kb, t < 4, 8) of
+// the group: exactly the A operand of v_mfma_f32_16x16x32_f16 for the four 32-channel K blocks,
+// so the quantized E' goes from registers straight into the MFMA. B_gg sits in LDS and its 20
+// lower-triangular 32 x 16 fragments in registers; P for 16 rows costs 20 MFMAs. The epilogue
+// needs E' in the accumulator layout (lane holds rows 4 q .. 4 q + 3 of column 16 cb + i), which
+// it reads back from a per-wave LDS tile.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace awq {
+
+namespace {
+constexpr int kClipWaves = 4;
+constexpr int kClipRows = 16 * kClipWaves;   // rows per workgroup
+constexpr int kPitch = 136;                  // LDS row pitch in halves (272 bytes: no conflicts)
+
+// Offset of the fragments of column block cb in the register array: blocks kb <= cb / 2.
+__device__ __forceinline__ constexpr int frag_base(int cb) {
+  return (cb == 0) ? 0 : (cb == 1) ? 1 : (cb == 2) ? 2 : (cb == 3) ? 4 : (cb == 4) ? 6
+       : (cb == 5) ? 9 : (cb == 6) ? 12 : 16;
+}
+
+__device__ __forceinline__ float clip_ratio(int j, int n_clip, float clip_min) {
+  return (float)(1.0 - (1.0 - (double)clip_min) * j / (n_clip - 1));
+}
+}  // namespace
+
+template <int DT>
+__global__ __launch_bounds__(256) void clip_search_kernel(
+    const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s,
+    const float* __restrict__ d32, const uint16_t* __restrict__ Bd, int n_clip, float clip_min,
+    float qmin, float qmax, float* __restrict__ clip, float* __restrict__ clip_err,
+    uint32_t* __restrict__ flags) {
+  constexpr int ES = (DT == kF32) ? 4 : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t Bg[128 * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Et[kClipWaves][16 * kPitch];
+  const int64_t G = K / 128;
+  const int g = blockIdx.y;
+  const int64_t n0 = (int64_t)blockIdx.x * kClipRows;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i = lane & 15, q = lane >> 4;
+
+  // B_gg: rows l, columns k of the group, from diagonal block a = g / 2 at offset 128 (g % 2)
+  {
+    const int o = (g & 1) * 128;
+    const uint16_t* src = Bd + (int64_t)(g >> 1) * (256 * 256) + (int64_t)o * 256 + o;
+    for (int idx = tid; idx < 128 * 16; idx += 256) {
+      const int l = idx >> 4, ch = idx & 15;
+      *reinterpret_cast<uint4*>(&Bg[l * kPitch + ch * 8]) =
+          *reinterpret_cast<const uint4*>(src + l * 256 + ch * 8);
+    }
+  }
+
+  // this lane's row and channels
+  const int64_t n = n0 + wave * 16 + i;
+  const bool live = n < N;
+  const int64_t kb0 = (int64_t)g * 128 + 8 * q;
+  float ws[4][8], ca[4][8], cb_[4][8];   // w s;  E' = fma(q Delta, ca, -cb_)
+  float m = 0.0f, md = 0.0f;
+  bool bad = false;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    float w[8], sv[8], dv[8];
+    if (live) {
+      load8_f32<DT>(reinterpret_cast<const char*>(W) + (n * K + kb0 + 32 * kb) * ES, w);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) w[t] = 0.0f;
+    }
+    load8_f32<kF32>(s + kb0 + 32 * kb, sv);
+    load8_f32<kF32>(d32 + kb0 + 32 * kb, dv);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      bad |= !isfinite(w[t]);
+      ws[kb][t] = w[t] * sv[t];
+      m = fmaxf(m, fabsf(ws[kb][t]));
+      md = fmaxf(md, fabsf(w[t]) * dv[t]);
+      ca[kb][t] = dv[t] * __builtin_amdgcn_rcpf(sv[t]);
+      cb_[kb][t] = w[t] * dv[t];
+    }
+  }
+  // the four lanes q = 0..3 of row i hold its 128 channels
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  md = fmaxf(md, __shfl_xor(md, 16));
+  md = fmaxf(md, __shfl_xor(md, 32));
+  const int e = escale_for_max(md);   // |E| <= |w|, so |E'| < 2^15
+  const float esc = ldexpf(1.0f, e);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      ca[kb][t] *= esc;
+      cb_[kb][t] *= esc;
+    }
+  __syncthreads();
+
+  half8_t bf[20];
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+    for (int kb = 0; kb <= cb / 2; ++kb)
+      bf[frag_base(cb) + kb] =
+          *reinterpret_cast<const half8_t*>(&Bg[(16 * cb + i) * kPitch + 32 * kb + 8 * q]);
+
+  // lanes i < 4 of each 16-lane quarter track row R = 4 q + i of the accumulator layout
+  const int R = 4 * q + (i & 3);
+  const int eR = __shfl(e, R);           // lane R (< 16) owns row R
+  const int64_t nR = n0 + wave * 16 + R;
+  float best = 0.0f;
+  int best_j = 0;
+  bool uf_any = false;
+  uint16_t* et = Et[wave];
+
+  for (int j = 0; j < n_clip; ++j) {
+    const float c = clip_ratio(j, n_clip, clip_min) * m;
+    const QuantStep st = quant_step(c, qmax);
+    const bool zero = !(st.delta > 0.0f);
+    uf_any |= (c > 0.0f) && zero;
+    half8_t af[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      uint32_t wd[4];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float v = fminf(fmaxf(ws[kb][t], -c), c);
+        const float qv = zero ? 0.0f : quant_code(v, st, qmin, qmax);
+        const float ev = __builtin_fmaf(qv * st.delta, ca[kb][t], -cb_[kb][t]);
+        const uint16_t h = f2h(ev);
+        af[kb][t] = __builtin_bit_cast(_Float16, h);
+        if (t & 1)
+          wd[t >> 1] |= (uint32_t)h << 16;
+        else
+          wd[t >> 1] = h;
+      }
+      *reinterpret_cast<uint4*>(&et[i * kPitch + 32 * kb + 8 * q]) =
+          make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
+    floatx4 acc[8];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      acc[cb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb <= cb / 2; ++kb)
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[kb], bf[frag_base(cb) + kb], acc[cb],
+                                                        0, 0, 0);
+    }
+    // the tile written above is read back by other lanes of this wave: LDS accesses of one
+    // wave complete in order; keep the compiler from moving the reads above the writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float part[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      part[rr] = 0.0f;
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb)
+        part[rr] = __builtin_fmaf(h2f(et[(4 * q + rr) * kPitch + 16 * cb + i]), acc[cb][rr],
+                                  part[rr]);
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) part[rr] += __shfl_xor(part[rr], off);
+    const int sel = i & 3;
+    const float val = (sel == 0) ? part[0] : (sel == 1) ? part[1] : (sel == 2) ? part[2] : part[3];
+    if (j == 0 || val < best) {          // strict: the lowest index wins ties
+      best = val;
+      best_j = j;
+    }
+    if (clip_err && i < 4 && nR < N)
+      clip_err[((int64_t)j * N + nR) * G + g] = ldexpf(2.0f * val, -2 * eR);
+    // all reads of the tile are done before the next ratio overwrites it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  if (i < 4 && nR < N) clip[nR * G + g] = clip_ratio(best_j, n_clip, clip_min);
+  wave_flag(flags, bad, kFlagNonfiniteW);
+  wave_flag(flags, uf_any, kFlagStepUnderflow);
+}
+
+hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, const float* s,
+                              const float* d32, const uint16_t* Bd, int n_clip, float clip_min,
+                              int bits, float* clip, float* clip_err, uint32_t* flags,
+                              hipStream_t stream) {
+  const float qmax = (float)((1 << (bits - 1)) - 1);
+  const float qmin = -(float)(1 << (bits - 1));
+  dim3 grid((unsigned)((N + kClipRows - 1) / kClipRows), (unsigned)(K / 128));
+  if (dtype == kF32)
+    clip_search_kernel<kF32><<<grid, 256, 0, stream>>>(W, N, K, s, d32, Bd, n_clip, clip_min,
+                                                        qmin, qmax, clip, clip_err, flags);
+  else
+    clip_search_kernel<kF16><<<grid, 256, 0, stream>>>(W, N, K, s, d32, Bd, n_clip, clip_min,
+                                                        qmin, qmax, clip, clip_err, flags);
+  return hipGetLastError();
+}
+
+}  // namespace awq

@@ -31,6 +31,7 @@ enum : uint32_t {
   kFlagScale16Subnormal = 1u << 5,
   kFlagNonfiniteLoss = 1u << 6,
   kFlagStepUnderflow = 1u << 7,
+  kFlagClipRange = 1u << 8,
 };
 
 __device__ __forceinline__ float h2f(uint16_t b) {
@@ -101,29 +102,79 @@ __device__ __forceinline__ float row16_max(float v) {
 // |t' - fp32(ws/Delta)| <= 1.2e-6, so rint(t') equals the specified rint(fp32(ws/Delta)) unless t'
 // lies within that distance of a half-integer; in that case (probability ~1.5e-5 per element) and
 // whenever Delta is not a normal number, the exact quotient is computed by IEEE division.
+// Power-of-two exponent e for storing values bounded by m in fp16 as v * 2^e: 2^e m lies in
+// [2^14, 2^15), so the values stay finite and keep normal fp16 precision (e = 0 for m = 0 or a
+// non-finite m; e clamped to [-100, 100]).
+__device__ __forceinline__ int escale_for_max(float m) {
+  if (!(m > 0.0f) || !isfinite(m)) return 0;
+  const uint32_t bits = __float_as_uint(m);
+  const int e2 = (int)((bits >> 23) & 0xFFu);  // biased exponent; 0 for subnormal
+  const int fl = (e2 == 0) ? -127 : e2 - 127;  // floor(log2 m) (subnormals clamped)
+  int e = 14 - fl;
+  if (e > 100) e = 100;
+  if (e < -100) e = -100;
+  return e;
+}
+
+struct QuantStep {
+  float delta;      // Delta = fp32(m / qmax); 0 for m = 0 or when the quotient underflows
+  float rcp;        // fp32(1 / Delta)
+  bool exact_only;  // Delta or 1/Delta is not a normal number: always divide
+};
+
+__device__ __forceinline__ QuantStep quant_step(float m, float qmax) {
+  QuantStep st;
+  st.delta = m / qmax;
+  st.rcp = 1.0f / st.delta;
+  st.exact_only = !(st.delta >= 0x1p-126f) || !(st.rcp < 0x1p+127f);
+  return st;
+}
+
+// Code of one value v with |v| <= m for the step of quant_step(m, qmax) (st.delta > 0).
+__device__ __forceinline__ float quant_code(float v, const QuantStep& st, float qmin, float qmax) {
+  const float tq = v * st.rcp;
+  float qq = rintf(tq);
+  if (st.exact_only || fabsf(tq - qq) > 0.5f - 0x1p-17f) qq = rintf(v / st.delta);
+  return fminf(fmaxf(qq, qmin), qmax);
+}
+
+// Codes of ws[] for the group maximum m (every |ws| <= m); returns Delta.
+__device__ __forceinline__ float quant8_core(const float (&ws)[8], float m, float qmin,
+                                             float qmax, float (&q)[8], bool& underflow) {
+  const QuantStep st = quant_step(m, qmax);
+  underflow = (m > 0.0f) && !(st.delta > 0.0f);
+  if (!(st.delta > 0.0f)) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) q[t] = 0.0f;
+    return 0.0f;
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) q[t] = quant_code(ws[t], st, qmin, qmax);
+  return st.delta;
+}
+
 __device__ __forceinline__ float quant8(const float (&ws)[8], float qmin, float qmax,
                                         float (&q)[8], bool& underflow) {
   float m = 0.0f;
 #pragma unroll
   for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(ws[t]));
   m = row16_max(m);
-  const float delta = m / qmax;
-  underflow = (m > 0.0f) && !(delta > 0.0f);
-  if (!(delta > 0.0f)) {
+  return quant8_core(ws, m, qmin, qmax, q, underflow);
+}
+
+// Clipped quantization (the clipping search's ratio r in (0, 1]): ws[] is first moved into
+// [-c, c], c = fp32(r * m) with m the group maximum; since c <= m, the clipped group's maximum
+// is c, and the codes follow as in quant8.
+__device__ __forceinline__ float quant8_clip(float (&ws)[8], float ratio, float qmin, float qmax,
+                                             float (&q)[8], bool& underflow) {
+  float m = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) q[t] = 0.0f;
-    return 0.0f;
-  }
-  const float r = 1.0f / delta;
-  const bool exact_only = !(delta >= 0x1p-126f) || !(r < 0x1p+127f);
+  for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(ws[t]));
+  m = row16_max(m);
+  const float c = ratio * m;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const float tq = ws[t] * r;
-    float qq = rintf(tq);
-    if (exact_only || fabsf(tq - qq) > 0.5f - 0x1p-17f) qq = rintf(ws[t] / delta);
-    q[t] = fminf(fmaxf(qq, qmin), qmax);
-  }
-  return delta;
+  for (int t = 0; t < 8; ++t) ws[t] = fminf(fmaxf(ws[t], -c), c);
+  return quant8_core(ws, c, qmin, qmax, q, underflow);
 }
 
 // Buffer resource over [base, base + num_bytes): loads at offsets >= num_bytes return zero,

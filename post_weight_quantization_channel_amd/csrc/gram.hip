@@ -28,10 +28,11 @@ namespace awq {
 // ------------------------------------------------------------------------------------------
 // Work split of X^T X over token chunks: every (tile, chunk) is one workgroup; the chunk count
 // is picked so that the workgroups fill whole waves of the 256 compute units.
-GramPlan gram_plan(int64_t M, int64_t K) {
+GramPlan gram_plan(int64_t M, int64_t K, bool diag) {
   GramPlan p{};
   p.t = (int)((K + kLossBN - 1) / kLossBN);
-  p.T = (int64_t)p.t * (p.t + 1) / 2;
+  p.diag = diag;
+  p.T = diag ? (int64_t)p.t : (int64_t)p.t * (p.t + 1) / 2;
   p.Mp = (M + kGramMAlign - 1) / kGramMAlign * kGramMAlign;
   // at most kGramMaxChunks chunks, at least kGramMAlign tokens each, and no more than
   // kGramMaxBlocks workgroups once one chunk per tile is there (bounds the partials' memory)
@@ -126,13 +127,17 @@ __device__ __forceinline__ int64_t frag_off(int wave, int i, int j, int e, int l
 
 __global__ __launch_bounds__(kloop::kThreads, 1) void gram_gemm_kernel(
     const uint16_t* __restrict__ Xt, int64_t K, int64_t Mp, int t, int64_t T, int64_t chunk,
-    float* __restrict__ Hpart) {
+    int diag, float* __restrict__ Hpart) {
   using namespace kloop;
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   const int64_t logical = xcd_logical(blockIdx.x, gridDim.x);
   const int64_t c = logical / T, tile = logical % T;    // chunk-major: neighbours share tokens
   int a, b;
-  tri_tile(tile, t, a, b);
+  if (diag) {
+    a = b = (int)tile;
+  } else {
+    tri_tile(tile, t, a, b);
+  }
   const int64_t m0 = c * chunk;
   const int64_t clen = (Mp - m0 < chunk) ? Mp - m0 : chunk;   // multiple of 128
   const int64_t rows_a = (K - (int64_t)a * BM < BM) ? K - (int64_t)a * BM : BM;
@@ -164,12 +169,12 @@ __global__ __launch_bounds__(kloop::kThreads, 1) void gram_gemm_kernel(
 // lane r + 32 ((r / 4) % 2) and register 4 (r / 8) + r % 4, r = k' % 32.
 __global__ __launch_bounds__(256) void gram_diag_kernel(const float* __restrict__ Hpart,
                                                         int64_t K, int t, int64_t T, int S,
-                                                        double* __restrict__ d64,
+                                                        int diag, double* __restrict__ d64,
                                                         float* __restrict__ d32) {
   const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (k >= K) return;
   const int a = (int)(k / kLossBN), kp = (int)(k % kLossBN);
-  const int64_t tile = (int64_t)a * t - (int64_t)a * (a - 1) / 2;
+  const int64_t tile = diag ? (int64_t)a : (int64_t)a * t - (int64_t)a * (a - 1) / 2;
   const int wm = kp >> 7, i = (kp & 127) >> 5, r = kp & 31;
   const int lane = r + 32 * ((r >> 2) & 1);
   const int e = 4 * (r >> 3) + (r & 3);
@@ -182,9 +187,11 @@ __global__ __launch_bounds__(256) void gram_diag_kernel(const float* __restrict_
 }
 
 // One thread per float4 of the fragment order: tokens-chunk sums in fp64 (chunk order fixed),
-// then B[l][k..k+3] for the four channels k..k+3 (consecutive A rows) of output row l.
+// then B[l][k..k+3] for the four channels k..k+3 (consecutive A rows) of output row l. With
+// `diag`, B is stored as the diagonal blocks only: block a at B + 65536 a, row l - 256 a.
 __global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restrict__ Hpart,
                                                           int64_t K, int t, int64_t T, int S,
+                                                          int diag,
                                                           const double* __restrict__ d64,
                                                           uint16_t* __restrict__ B) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;   // float4 index
@@ -195,7 +202,11 @@ __global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restric
   const int lane = rem & 63, e4 = (rem >> 6) & 3, j = (rem >> 8) & 3, i = (rem >> 10) & 3,
             wave = rem >> 12;
   int a, b;
-  tri_tile(tile, t, a, b);
+  if (diag) {
+    a = b = (int)tile;
+  } else {
+    tri_tile(tile, t, a, b);
+  }
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t l = (int64_t)b * kLossBN + wn * 128 + 32 * j + (lane & 31);
   const int64_t k = (int64_t)a * kLossBM + wm * 128 + 32 * i + 8 * e4 + 4 * (lane >> 5);
@@ -223,7 +234,10 @@ __global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restric
     }
     o[q] = f2h(v);
   }
-  *reinterpret_cast<uint2*>(B + l * K + k) =
+  const int64_t off = diag ? (int64_t)a * (kLossBM * kLossBN) + (l - (int64_t)a * kLossBN) * kLossBN +
+                                (k - (int64_t)a * kLossBM)
+                          : l * K + k;
+  *reinterpret_cast<uint2*>(B + off) =
       make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
 }
 
@@ -326,19 +340,21 @@ hipError_t launch_gram_prepare(const void* X, int xdt, int64_t M, int64_t K, con
   if (e == hipSuccess && ev) e = hipEventRecord(ev[0], stream);
   if (e == hipSuccess) {
     gram_gemm_kernel<<<(unsigned)(p.T * p.S), kloop::kThreads, 0, stream>>>(Xt, K, p.Mp, p.t, p.T,
-                                                                            p.chunk, Hpart);
+                                                                            p.chunk, (int)p.diag,
+                                                                            Hpart);
     e = hipGetLastError();
   }
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], stream);
   if (e == hipSuccess) {
     gram_diag_kernel<<<(unsigned)((K + 255) / 256), 256, 0, stream>>>(Hpart, K, p.t, p.T, p.S,
-                                                                      d64, d32);
+                                                                      (int)p.diag, d64, d32);
     e = hipGetLastError();
   }
   if (e == hipSuccess) {
     const int64_t threads = p.T * (kLossBM * kLossBN / 4);
     gram_finish_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(Hpart, K, p.t, p.T,
-                                                                              p.S, d64, B);
+                                                                              p.S, (int)p.diag,
+                                                                              d64, B);
     e = hipGetLastError();
   }
   return e;

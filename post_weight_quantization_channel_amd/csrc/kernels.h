@@ -31,12 +31,14 @@ constexpr int64_t kGramMaxBlocks = 4096;
 struct GramPlan {
   int t;          // 256-channel blocks, ceil(K / 256)
   int S;          // token chunks
-  int64_t T;      // upper-triangle tiles, t (t + 1) / 2
+  bool diag;      // only the t diagonal 256 x 256 blocks of X^T X (the clipping search)
+  int64_t T;      // tiles: t (t + 1) / 2 upper-triangle tiles, or t diagonal ones
   int64_t Mp;     // padded token count
   int64_t chunk;  // tokens per chunk (multiple of kGramMAlign; the last chunk may be shorter)
 };
-GramPlan gram_plan(int64_t M, int64_t K);
-// transpose -> ev[0] -> X^T X partials -> ev[1] -> d and B
+GramPlan gram_plan(int64_t M, int64_t K, bool diag = false);
+// transpose -> ev[0] -> X^T X partials -> ev[1] -> d and B. B is [K, K] (row l, column k), or
+// with plan.diag the t diagonal blocks [t][256][256] (block a: rows and columns 256 a ..).
 hipError_t launch_gram_prepare(const void* X, int xdt, int64_t M, int64_t K, const GramPlan& p,
                                uint16_t* Xt, float* Hpart, double* d64, float* d32, uint16_t* B,
                                uint32_t* flags, hipStream_t stream, hipEvent_t* ev);
@@ -62,9 +64,19 @@ hipError_t launch_finalize(const double* partials, int64_t tiles_per_alpha, int 
                            float* s_best, uint32_t* flags, hipStream_t stream);
 
 // ---- pack ----
-hipError_t launch_pack(const void* W, int dtype, int64_t N, int64_t K, const float* s, int bits,
-                       uint32_t* qweight, uint16_t* scales16, uint16_t* s16, int8_t* codes,
-                       uint32_t* flags, hipStream_t stream);
+// clip: ratios [N, K/128] in (0, 1] or nullptr
+hipError_t launch_pack(const void* W, int dtype, int64_t N, int64_t K, const float* s,
+                       const float* clip, int bits, uint32_t* qweight, uint16_t* scales16,
+                       uint16_t* s16, int8_t* codes, uint32_t* flags, hipStream_t stream);
+
+// ---- clipping search (clip.hip) ----
+// Per (row, group of 128): the ratio of the grid 1 .. clip_min whose clipped quantization of
+// W * s gives the smallest group error E_g H_gg E_g^T, with H_gg taken from the diagonal blocks
+// of the correlation operand (Bd) and d = sqrt(diag H).
+hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, const float* s,
+                              const float* d32, const uint16_t* Bd, int n_clip, float clip_min,
+                              int bits, float* clip, float* clip_err, uint32_t* flags,
+                              hipStream_t stream);
 
 // ---- W4A16 ----
 hipError_t launch_w4a16(const uint16_t* A, int64_t M, int64_t N, int64_t K,

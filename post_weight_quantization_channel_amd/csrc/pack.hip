@@ -4,15 +4,17 @@
 //   qweight[n, j] = sum_t (q[n, 8j+t] & 0xF) << 4t      (element 8j+t in bits 4t..4t+3)
 //   scales16[n, g] = fp16(Delta[n, g]),  s16[k] = fp16(s[k])   (round to nearest even)
 // The codes come from quant8(), the same device function as the search, so they are
-// bit-identical to the codes the search scored.
+// bit-identical to the codes the search scored. With clip ratios (one per row and group, from
+// the clipping search) the codes come from quant8_clip(), as in that search.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace awq {
 
-template <int DT>
+template <int DT, bool CLIP>
 __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ W, int64_t N, int64_t K,
-                                                   const float* __restrict__ s, float qmin,
+                                                   const float* __restrict__ s,
+                                                   const float* __restrict__ clip, float qmin,
                                                    float qmax, uint32_t* __restrict__ qweight,
                                                    uint16_t* __restrict__ scales16,
                                                    uint16_t* __restrict__ s16,
@@ -23,7 +25,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ W, i
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t n = id / chunks;
   const int64_t c8 = id % chunks;
-  bool of = false, sub = false, uf_any = false;
+  bool of = false, sub = false, uf_any = false, bad_clip = false;
   if (n < N) {  // uniform over each 16-lane group (chunks % 16 == 0)
     float w[8], sv[8], ws[8], q[8];
     load8_f32<DT>(reinterpret_cast<const char*>(W) + (n * K + c8 * 8) * ES, w);
@@ -31,7 +33,17 @@ __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ W, i
 #pragma unroll
     for (int t = 0; t < 8; ++t) ws[t] = w[t] * sv[t];
     bool uf;
-    const float delta = quant8(ws, qmin, qmax, q, uf);
+    float delta;
+    if (CLIP) {
+      float r = clip[n * (K / 128) + c8 / 16];
+      if (!(r > 0.0f && r <= 1.0f)) {   // outside (0, 1]: flagged, packed unclipped
+        bad_clip = true;
+        r = 1.0f;
+      }
+      delta = quant8_clip(ws, r, qmin, qmax, q, uf);
+    } else {
+      delta = quant8(ws, qmin, qmax, q, uf);
+    }
     uint32_t word = 0;
 #pragma unroll
     for (int t = 0; t < 8; ++t) word |= ((uint32_t)((int)q[t]) & 0xFu) << (4 * t);
@@ -68,21 +80,25 @@ __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ W, i
   wave_flag(flags, of, kFlagScale16Overflow);
   wave_flag(flags, sub, kFlagScale16Subnormal);
   wave_flag(flags, uf_any, kFlagStepUnderflow);
+  if (CLIP) wave_flag(flags, bad_clip, kFlagClipRange);
 }
 
-hipError_t launch_pack(const void* W, int dtype, int64_t N, int64_t K, const float* s, int bits,
-                       uint32_t* qweight, uint16_t* scales16, uint16_t* s16, int8_t* codes,
-                       uint32_t* flags, hipStream_t stream) {
+hipError_t launch_pack(const void* W, int dtype, int64_t N, int64_t K, const float* s,
+                       const float* clip, int bits, uint32_t* qweight, uint16_t* scales16,
+                       uint16_t* s16, int8_t* codes, uint32_t* flags, hipStream_t stream) {
   const float qmax = (float)((1 << (bits - 1)) - 1);
   const float qmin = -(float)(1 << (bits - 1));
   const int64_t threads = N * (K / 8);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
-  if (dtype == kF32)
-    pack_kernel<kF32><<<blocks, 256, 0, stream>>>(W, N, K, s, qmin, qmax, qweight, scales16, s16,
-                                                  codes, flags);
-  else
-    pack_kernel<kF16><<<blocks, 256, 0, stream>>>(W, N, K, s, qmin, qmax, qweight, scales16, s16,
-                                                  codes, flags);
+#define AWQ_PACK(DT_, CLIP_)                                                                  \
+  pack_kernel<DT_, CLIP_><<<blocks, 256, 0, stream>>>(W, N, K, s, clip, qmin, qmax, qweight,   \
+                                                      scales16, s16, codes, flags)
+  if (dtype == kF32) {
+    if (clip) AWQ_PACK(kF32, true); else AWQ_PACK(kF32, false);
+  } else {
+    if (clip) AWQ_PACK(kF16, true); else AWQ_PACK(kF16, false);
+  }
+#undef AWQ_PACK
   return hipGetLastError();
 }
 

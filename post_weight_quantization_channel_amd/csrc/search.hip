@@ -157,14 +157,7 @@ hipError_t launch_x_to_f16(const void* X, int dtype, int64_t count, uint16_t* X1
 // fp16 normal precision instead of falling into the fp16 subnormal range. In the Gram form the
 // same bound holds for E d_k against max |W d| (d_k >= 0).
 __device__ __forceinline__ int escale_from_absmax(uint32_t bits) {
-  const float m = __uint_as_float(bits);
-  if (!(m > 0.0f) || !isfinite(m)) return 0;
-  const int e2 = (int)((bits >> 23) & 0xFFu);  // biased exponent; 0 for subnormal
-  const int fl = (e2 == 0) ? -127 : e2 - 127;  // floor(log2 m) (subnormals clamped)
-  int e = 14 - fl;
-  if (e > 100) e = 100;
-  if (e < -100) e = -100;
-  return e;
+  return escale_for_max(__uint_as_float(bits));
 }
 
 constexpr int kQuantRows = 4;  // rows per thread in quantize_stack

@@ -33,6 +33,7 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("awq_act_stats", "awq_search_layer", "awq_pack_int4", "w4a16_gemm",
               "awq_search_workspace_bytes", "awq_act_stats_workspace_bytes",
+              "awq_clip_search", "awq_clip_workspace_bytes",
               "awq_status_string", "awq_version"):
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
@@ -47,11 +48,11 @@ def test_status_strings(lib):
     for code in range(7):
         s = lib.awq_status_string(code).decode()
         assert s.startswith("AWQ_")
-    assert lib.awq_version() == 10100
+    assert lib.awq_version() == 10200
 
 
-def cfg(bits=4, group=128, n_grid=20, s_floor=1e-5, form=0):
-    return AwqCfg(bits, group, n_grid, s_floor, form)
+def cfg(bits=4, group=128, n_grid=20, s_floor=1e-5, form=0, n_clip=11, clip_min=0.5):
+    return AwqCfg(bits, group, n_grid, s_floor, form, n_clip, clip_min)
 
 
 def test_workspace_queries(lib):
@@ -165,14 +166,50 @@ def test_pack_rejects(lib):
     E = _lib
     c = cfg()
     f = lib.awq_pack_int4
-    assert f(None, 1, 4, 128, FAKE, c, FAKE, FAKE, FAKE, None, FAKE, None) == E.AWQ_ERR_NULL
-    assert f(FAKE, 1, 4, 128, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, None) == E.AWQ_ERR_NULL
-    assert f(FAKE, 1, 4, 128, FAKE, cfg(bits=8), FAKE, FAKE, FAKE, None, FAKE, None) == \
-        E.AWQ_ERR_CONFIG
-    assert f(FAKE, 2, 4, 128, FAKE, c, FAKE, FAKE, FAKE, None, FAKE, None) == E.AWQ_ERR_DTYPE
-    assert f(FAKE, 1, 4, 130, FAKE, c, FAKE, FAKE, FAKE, None, FAKE, None) == E.AWQ_ERR_SHAPE
-    assert f(FAKE, 1, 0, 128, FAKE, c, FAKE, FAKE, FAKE, None, FAKE, None) == E.AWQ_ERR_SHAPE
-    assert f(FAKE, 1, 4, 128, FAKE, c, FAKE, FAKE, FAKE, FAKE + 3, FAKE, None) == E.AWQ_ERR_SHAPE
+
+    def call(W=FAKE, wdt=1, N=4, K=128, s=FAKE, clip=None, cfg_=c, codes=None):
+        return f(W, wdt, N, K, s, clip, cfg_, FAKE, FAKE, FAKE, codes, FAKE, None)
+    assert call(W=None) == E.AWQ_ERR_NULL
+    assert call(cfg_=None) == E.AWQ_ERR_NULL
+    assert call(cfg_=cfg(bits=8)) == E.AWQ_ERR_CONFIG
+    assert call(wdt=2) == E.AWQ_ERR_DTYPE
+    assert call(K=130) == E.AWQ_ERR_SHAPE
+    assert call(N=0) == E.AWQ_ERR_SHAPE
+    assert call(codes=FAKE + 3) == E.AWQ_ERR_SHAPE
+    assert call(clip=FAKE + 2) == E.AWQ_ERR_SHAPE
+
+
+def _clip(lib, **kw):
+    a = dict(W=FAKE, wdt=1, N=256, K=512, X=FAKE2, xdt=1, M=300, s=FAKE, cfg=cfg(), clip=FAKE,
+             err=None, flags=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    c = a["cfg"]
+    return lib.awq_clip_search(a["W"], a["wdt"], a["N"], a["K"], a["X"], a["xdt"], a["M"],
+                               a["s"], ctypes.byref(c) if c is not None else None, a["clip"],
+                               a["err"], a["flags"], a["ws"], a["ws_bytes"], None)
+
+
+def test_clip_search_rejects(lib):
+    E = _lib
+    for k in ("W", "X", "s", "clip", "flags"):
+        assert _clip(lib, **{k: None}) == E.AWQ_ERR_NULL, k
+    assert _clip(lib, cfg=None) == E.AWQ_ERR_NULL
+    assert _clip(lib, cfg=cfg(n_clip=1)) == E.AWQ_ERR_CONFIG
+    assert _clip(lib, cfg=cfg(n_clip=65)) == E.AWQ_ERR_CONFIG
+    assert _clip(lib, cfg=cfg(clip_min=0.0)) == E.AWQ_ERR_CONFIG
+    assert _clip(lib, cfg=cfg(clip_min=1.0)) == E.AWQ_ERR_CONFIG
+    assert _clip(lib, cfg=cfg(bits=5)) == E.AWQ_ERR_CONFIG
+    assert _clip(lib, wdt=2) == E.AWQ_ERR_DTYPE
+    assert _clip(lib, xdt=7) == E.AWQ_ERR_DTYPE
+    assert _clip(lib, K=500) == E.AWQ_ERR_SHAPE
+    assert _clip(lib, M=(1 << 23) - 127) == E.AWQ_ERR_SHAPE
+    assert _clip(lib, s=FAKE + 4) == E.AWQ_ERR_SHAPE
+    assert _clip(lib, ws=None) == E.AWQ_ERR_WORKSPACE
+    need = lib.awq_clip_workspace_bytes(300, 256, 512, 1, cfg())
+    # d (fp64 + fp32), two diagonal 256x256 fp16 blocks, X^T fp16 [512, 384] and the partials
+    assert need >= 512 * 12 + 2 * 65536 * 2 + 512 * 384 * 2 + 2 * 65536 * 4
+    assert _clip(lib, ws_bytes=need - 1) == E.AWQ_ERR_WORKSPACE
+    assert lib.awq_clip_workspace_bytes(300, 256, 512, 1, cfg(clip_min=2.0)) == 0
 
 
 def test_w4a16_rejects(lib):

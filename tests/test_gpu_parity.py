@@ -443,3 +443,120 @@ def test_full_c2_layer(awq):
     full = oracle.pack_layer(L.W, orc["scales"][bg])
     ref = oracle.w4a16(A, full["qweight"], full["scales16"], full["s16"])
     assert oracle.accuracy_report(Y_g, ref)["rel_fro"] <= W4A16_RTOL
+
+
+# ------------------------------------------------------------------------------------------------
+# Clipping search and clipped packing
+CLIP_ERR_RTOL = 5e-3     # per (ratio, row, group) error: fp16 E' and correlation operand
+CLIP_BAND = 1e-2         # a chosen ratio may differ from the oracle's only inside this band
+
+
+def _oracle_s_best(W, X, bits=4):
+    sx = oracle.act_stats(X)
+    return oracle.search_layer(W, X, sx, bits=bits)["s_best"]
+
+
+CLIP_CASES = [
+    # name, builder, bits, n_clip, clip_min
+    ("c1_512x512_m256_f32", lambda: (workloads.c1_layer().W, workloads.c1_layer().X), 4, 11, 0.5),
+    ("ragged_300x384_m700", lambda: _lognormal_layer(51, 300, 384, 700), 4, 11, 0.5),
+    ("int3_200x256_m500", lambda: _lognormal_layer(52, 200, 256, 500), 3, 8, 0.4),
+    ("correlated_130x384_m900", lambda: (workloads.weight(53, 130, 384),
+                                         workloads.correlated_activations(900, 384, rank=8,
+                                                                          config=53)), 4, 11, 0.5),
+    ("k128_70x128_m256", lambda: _lognormal_layer(54, 70, 128, 256), 4, 5, 0.6),
+]
+
+
+@pytest.mark.parametrize("name,make,bits,n_clip,clip_min", CLIP_CASES,
+                         ids=[c[0] for c in CLIP_CASES])
+def test_clip_search_parity(awq, name, make, bits, n_clip, clip_min):
+    W, X = make()
+    say("clip search", name, W.shape, X.shape, "bits", bits, "grid", n_clip, clip_min)
+    s = _oracle_s_best(W, X, bits)
+    cfg = awq.AwqConfig(bits=bits, n_clip=n_clip, clip_min=clip_min)
+    r = awq.clip_search(dev(W), dev(X), dev(s), cfg, with_err=True)
+    orc = oracle.clip_search(W, X, s, bits=bits, n_clip=n_clip, clip_min=clip_min)
+    err_g = host(r.err).astype(np.float64)
+    err_o = orc["err"]
+    scale = err_o.max(axis=0, keepdims=True)          # per (row, group): the largest ratio error
+    rel = np.abs(err_g - err_o) / np.maximum(scale, 1e-300)
+    say(f"max err rel {rel.max():.2e} (relative to each group's largest error)")
+    assert rel.max() <= CLIP_ERR_RTOL
+    ratio_g = host(r.clip)
+    grid = oracle.clip_grid(n_clip, clip_min)
+    assert np.isin(ratio_g, grid).all()
+    j_g = np.searchsorted(-grid, -ratio_g)            # grid is decreasing
+    rows, groups = np.indices(ratio_g.shape)
+    chosen = err_o[j_g, rows, groups]
+    best = err_o.min(axis=0)
+    assert (chosen <= best * (1 + CLIP_BAND) + 1e-12 * scale[0]).all()
+    same = (j_g == orc["best"]).mean()
+    say(f"same ratio as the oracle in {100 * same:.2f}% of (row, group)")
+    assert int(host(r.flags)[0]) == 0
+
+
+def test_pack_with_clip_bit_exact(awq):
+    """The oracle's clip ratios (and random ratios in (0, 1]) fed to both packers: codes, packed
+    words and fp16 steps bit-identical."""
+    W, X = _lognormal_layer(55, 260, 512, 600)
+    s = _oracle_s_best(W, X)
+    orc = oracle.clip_search(W, X, s)
+    g = np.random.default_rng(56)
+    rnd = g.uniform(0.3, 1.0, size=(260, 4)).astype(np.float32)
+    rnd[::7] = np.float32(1.0)
+    for bits in (4, 3):
+        for name, ratios in (("oracle ratios", orc["ratio"]), ("random ratios", rnd)):
+            say("pack with clip", bits, name)
+            cfg = awq.AwqConfig(bits=bits)
+            p = awq.pack_int4(dev(W), dev(s), cfg, with_codes=True, clip=dev(ratios))
+            o = oracle.pack_layer(W, s, bits=bits, clip=ratios)
+            assert np.array_equal(host(p.codes), o["codes"])
+            assert np.array_equal(host(p.qweight).view(np.uint32), o["qweight"])
+            assert np.array_equal(host(p.scales16).view(np.uint16), o["scales16"].view(np.uint16))
+            assert int(host(p.flags)[0]) == 0
+
+
+def test_pack_clip_ratio_out_of_range_is_flagged(awq):
+    from post_weight_quantization_channel_amd import _lib as L
+    W, X = _lognormal_layer(57, 64, 256, 100)
+    s = np.ones(256, np.float32)
+    ratios = np.full((64, 2), 0.8, np.float32)
+    ratios[3, 1] = 1.5
+    say("clip ratio out of range")
+    p = awq.pack_int4(dev(W), dev(s), awq.AwqConfig(), with_codes=True, clip=dev(ratios))
+    assert int(host(p.flags)[0]) & L.FLAG_CLIP_RANGE
+    fixed = ratios.copy()
+    fixed[3, 1] = 1.0
+    o = oracle.pack_layer(W, s, clip=fixed)
+    assert np.array_equal(host(p.codes), o["codes"])
+
+
+def test_end_to_end_with_clipping(awq):
+    """search -> clip search -> clipped pack -> W4A16 on the GPU against the same chain in the
+    oracle: where the chosen ratios agree, the packed words are identical; the W4A16 output of
+    the GPU chain is within the W4A16 bar of the oracle chain's."""
+    W, X = _lognormal_layer(58, 384, 512, 800)
+    say("end-to-end with clipping", W.shape, X.shape)
+    Wt, Xt = dev(W), dev(X)
+    sx, flags = awq.act_stats(Xt)
+    res = awq.search_layer(Wt, Xt, sx, awq.AwqConfig(form="gram"), flags=flags)
+    cr = awq.clip_search(Wt, Xt, res.s_best, awq.AwqConfig(), flags=flags)
+    p = awq.pack_int4(Wt, res.s_best, awq.AwqConfig(), flags=flags, clip=cr.clip)
+    A = workloads.w4a16_activations(8, 512, config=5)
+    Y = awq.w4a16_gemm(dev(A), p.qweight, p.scales16, p.s16)
+    orc = oracle.search_layer(W, X, oracle.act_stats(X))
+    bg = int(host(res.best)[0])
+    check_alpha(host(res.losses), orc["losses"], bg, orc["best"])
+    s = orc["scales"][bg]
+    assert np.array_equal(host(res.s_best), s)
+    oc = oracle.clip_search(W, X, s)
+    o = oracle.pack_layer(W, s, clip=oc["ratio"])
+    agree = host(cr.clip) == oc["ratio"]
+    say(f"ratios agree in {100 * agree.mean():.2f}% of (row, group)")
+    assert agree.mean() >= 0.95
+    qw = host(p.qweight).view(np.uint32).reshape(384, 4, 16)
+    assert np.array_equal(qw[agree], o["qweight"].reshape(384, 4, 16)[agree])
+    ref = oracle.w4a16(A, o["qweight"], o["scales16"], o["s16"])
+    assert oracle.accuracy_report(host(Y), ref)["rel_fro"] <= W4A16_RTOL
+    assert int(host(flags)[0]) == 0
