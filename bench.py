@@ -15,6 +15,7 @@ fields it carries
                 every MFMA kernel of the step the same way;
   stages_ms     mean duration of every kernel of the search;
   other_form    the search in the other form (a few repetitions): ms and its loss kernel;
+  clip_search   the clipping search at s* (11 ratios 1 .. 0.5) and the clipped pack: ms;
   hbm_stages    the bandwidth-bound kernels: algorithmic bytes, GB/s, fraction of 8 TB/s;
   w4a16         the W4A16 kernel at the batch sizes 1, 4, 16, 64, 512 for 4096x4096 and
                 11008x4096, over rotated weight copies (> 256 MB, so HBM and not the
@@ -51,6 +52,8 @@ def parse():
                     help="loss form of the timed search (the other form is reported as context)")
     ap.add_argument("--other-form-reps", type=int, default=3,
                     help="repetitions of the search in the other form (0: skip)")
+    ap.add_argument("--clip-reps", type=int, default=5,
+                    help="repetitions of the clipping search at s* (0: skip)")
     ap.add_argument("--mode", choices=("bench", "traffic"), default="bench",
                     help="traffic: one 1 GiB device copy (counter calibration) and one pass of "
                          "the path in each form, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
@@ -130,7 +133,8 @@ def traffic_pass():
         res = awq.search_layer(W, X, sx, cfg, flags=flags)
         torch.cuda.synchronize()
         log(form, "search done; alpha*", int(res.best.item()))
-    p = awq.pack_int4(W, res.s_best, cfg, flags=flags)
+    cr = awq.clip_search(W, X, res.s_best, cfg, flags=flags)
+    p = awq.pack_int4(W, res.s_best, cfg, flags=flags, clip=cr.clip)
     awq.w4a16_gemm(torch.ones(1, K_, dtype=torch.float16, device=dev), p.qweight, p.scales16,
                    p.s16)
     torch.cuda.synchronize()
@@ -333,6 +337,33 @@ def main():
         v["gbs"] = round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)
         v["hbm_frac"] = round(v["gbs"] / HBM_PEAK_GBS, 4)
 
+    # clipping search at s* (a further optimisation of the method, reported beside the step)
+    clip_rec = None
+    if args.clip_reps > 0:
+        ccfg = awq.AwqConfig(bits=4, group=128, n_clip=11, clip_min=0.5)
+        ws_c = torch.empty(awq.clip_workspace_bytes(M_, N_, K_, torch.float16, ccfg),
+                           dtype=torch.uint8, device=dev)
+        s_star = res.s_best.clone()
+        times, ptimes = [], []
+        for r in range(args.clip_reps + 1):            # the first run is a warm-up
+            c0, c1, c2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            c0.record(st)
+            cr = awq.clip_search(W, X, s_star, ccfg, workspace=ws_c)
+            c1.record(st)
+            awq.pack_int4(W, s_star, ccfg, clip=cr.clip)
+            c2.record(st)
+            c2.synchronize()
+            if r:
+                times.append(c0.elapsed_time(c1))
+                ptimes.append(c1.elapsed_time(c2))
+        ratios = cr.clip.cpu().numpy()
+        clip_rec = {"n_clip": 11, "clip_min": 0.5, "ms": round(statistics.mean(times), 4),
+                    "pack_clipped_ms": round(statistics.mean(ptimes), 4),
+                    "groups_clipped_frac": round(float((ratios < 1.0).mean()), 4),
+                    "mean_ratio": round(float(ratios.mean()), 4)}
+        log("clip search", clip_rec)
+        del ws_c
+
     other_form = None
     if args.other_form_reps > 0:
         oform = "direct" if args.form == "gram" else "gram"
@@ -387,6 +418,7 @@ def main():
         "mfma": mfma,
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "other_form": other_form,
+        "clip_search": clip_rec,
         "hbm_stages": other,
         "w4a16": w4,
         "alpha_star": best,

@@ -2,7 +2,7 @@
 // scaled-up weights among the method's further optimisations. Per (output row n, group g of 128
 // input channels), every ratio r_j of the grid 1 .. clip_min is tried on W s: the scaled weights
 // are clipped to [-c, c], c = fp32(r_j max|w s|), quantized as in the search (quant_step /
-// quant_code), and scored by the output error the group causes on its own,
+// quant_codes), and scored by the output error the group causes on its own,
 //   err_j[n, g] = sum_m ( sum_{k in g} X[m,k] E[n,k] )^2 = E_g H_gg E_g^T,  E = Q(W s)/s - W;
 // the smallest wins, the lowest index on ties.
 //
@@ -130,17 +130,20 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
   for (int j = 0; j < n_clip; ++j) {
     const float c = clip_ratio(j, n_clip, clip_min) * m;
     const QuantStep st = quant_step(c, qmax);
-    const bool zero = !(st.delta > 0.0f);
-    uf_any |= (c > 0.0f) && zero;
+    uf_any |= (c > 0.0f) && !(st.delta > 0.0f);
+    float v[32], qv[32];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[8 * kb + t] = fminf(fmaxf(ws[kb][t], -c), c);
+    quant_codes(v, st, qmin, qmax, qv);
     half8_t af[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       uint32_t wd[4];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const float v = fminf(fmaxf(ws[kb][t], -c), c);
-        const float qv = zero ? 0.0f : quant_code(v, st, qmin, qmax);
-        const float ev = __builtin_fmaf(qv * st.delta, ca[kb][t], -cb_[kb][t]);
+        const float ev = __builtin_fmaf(qv[8 * kb + t] * st.delta, ca[kb][t], -cb_[kb][t]);
         const uint16_t h = f2h(ev);
         af[kb][t] = __builtin_bit_cast(_Float16, h);
         if (t & 1)
@@ -175,9 +178,7 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
                                   part[rr]);
     }
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) part[rr] += __shfl_xor(part[rr], off);
+    for (int rr = 0; rr < 4; ++rr) part[rr] = row16_sum(part[rr]);   // the 16 columns i
     const int sel = i & 3;
     const float val = (sel == 0) ? part[0] : (sel == 1) ? part[1] : (sel == 2) ? part[2] : part[3];
     if (j == 0 || val < best) {          // strict: the lowest index wins ties

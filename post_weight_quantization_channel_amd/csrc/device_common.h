@@ -91,6 +91,17 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
+// Sum over the 16 lanes of a DPP row, as a butterfly (adjacent pairs, pairs of pairs, the two
+// quads of each half, the two halves): addition is commutative, so every lane of the row ends
+// with the bit-identical sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v = v + dpp_f32<AWQ_DPP_QUAD_1032>(v);
+  v = v + dpp_f32<AWQ_DPP_QUAD_2301>(v);
+  v = v + dpp_f32<AWQ_DPP_ROW_HALF_MIRROR>(v);
+  v = v + dpp_f32<AWQ_DPP_ROW_MIRROR>(v);
+  return v;
+}
+
 // Quantize 8 scaled weights ws[] held by this lane; the 16 lanes of the lane's DPP row hold the
 // rest of the 128-channel group. On return q[] holds the codes (as exact small floats) and the
 // group step Delta is returned (0 for an all-zero group, or when max/qmax underflows to 0, in
@@ -118,27 +129,52 @@ __device__ __forceinline__ int escale_for_max(float m) {
 
 struct QuantStep {
   float delta;      // Delta = fp32(m / qmax); 0 for m = 0 or when the quotient underflows
-  float rcp;        // fp32(1 / Delta)
+  float rcp;        // fp32(1 / Delta); 0 when Delta is 0 (every code is then 0)
   bool exact_only;  // Delta or 1/Delta is not a normal number: always divide
 };
 
 __device__ __forceinline__ QuantStep quant_step(float m, float qmax) {
   QuantStep st;
   st.delta = m / qmax;
-  st.rcp = 1.0f / st.delta;
-  st.exact_only = !(st.delta >= 0x1p-126f) || !(st.rcp < 0x1p+127f);
+  if (st.delta > 0.0f) {
+    st.rcp = 1.0f / st.delta;
+    st.exact_only = !(st.delta >= 0x1p-126f) || !(st.rcp < 0x1p+127f);
+  } else {
+    st.delta = 0.0f;
+    st.rcp = 0.0f;
+    st.exact_only = false;
+  }
   return st;
 }
 
-// Code of one value v with |v| <= m for the step of quant_step(m, qmax) (st.delta > 0).
-__device__ __forceinline__ float quant_code(float v, const QuantStep& st, float qmin, float qmax) {
-  const float tq = v * st.rcp;
-  float qq = rintf(tq);
-  if (st.exact_only || fabsf(tq - qq) > 0.5f - 0x1p-17f) qq = rintf(v / st.delta);
-  return fminf(fmaxf(qq, qmin), qmax);
+// Codes of v[] (every |v| <= m) for the step of quant_step(m, qmax). The fast quotient is formed
+// for every element; a lane that holds a quotient near a half-integer (or has exact_only set)
+// redoes just those by IEEE division in one block that is rarely entered, so the common path has
+// no branches.
+template <int NV>
+__device__ __forceinline__ void quant_codes(const float (&v)[NV], const QuantStep& st, float qmin,
+                                            float qmax, float (&q)[NV]) {
+  bool slow = st.exact_only;
+#pragma unroll
+  for (int t = 0; t < NV; ++t) {
+    const float tq = v[t] * st.rcp;
+    q[t] = rintf(tq);
+    slow |= fabsf(tq - q[t]) > 0.5f - 0x1p-17f;
+  }
+  if (slow) {
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
+      const float tq = v[t] * st.rcp;
+      if (st.exact_only || fabsf(tq - rintf(tq)) > 0.5f - 0x1p-17f) q[t] = rintf(v[t] / st.delta);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NV; ++t) q[t] = fminf(fmaxf(q[t], qmin), qmax);
 }
 
-// Codes of ws[] for the group maximum m (every |ws| <= m); returns Delta.
+// Codes of ws[] for the group maximum m (every |ws| <= m); returns Delta. Here each element
+// takes its own (rarely used) division branch: for 8 elements per lane that measured faster
+// than quant_codes' single block.
 __device__ __forceinline__ float quant8_core(const float (&ws)[8], float m, float qmin,
                                              float qmax, float (&q)[8], bool& underflow) {
   const QuantStep st = quant_step(m, qmax);
@@ -149,7 +185,12 @@ __device__ __forceinline__ float quant8_core(const float (&ws)[8], float m, floa
     return 0.0f;
   }
 #pragma unroll
-  for (int t = 0; t < 8; ++t) q[t] = quant_code(ws[t], st, qmin, qmax);
+  for (int t = 0; t < 8; ++t) {
+    const float tq = ws[t] * st.rcp;
+    float qq = rintf(tq);
+    if (st.exact_only || fabsf(tq - qq) > 0.5f - 0x1p-17f) qq = rintf(ws[t] / st.delta);
+    q[t] = fminf(fmaxf(qq, qmin), qmax);
+  }
   return st.delta;
 }
 
