@@ -40,6 +40,11 @@ Readings taken where the pages are silent, ambiguous or disagree (each is also u
       it is quantized; r is chosen on the grid 1 .. clip_min at the fixed s*, by the part of the
       output error that the group causes on its own (the [notes] objective restricted to the
       group's channels, so that the choices are separable), lowest index on ties.
+  R18 folding ([notes] 方法, further optimisations: fuse the input's down-scaling into the
+      previous operator): every weight that reads the same X shares one s, searched on the
+      row-concatenated weights; s^-1 is folded into the previous operator's parameters along
+      its output channels (fp32 division, one rounding to their dtype), after which the
+      quantized layer takes its input unscaled (W4A16 without the division by s).
 """
 from __future__ import annotations
 
@@ -267,6 +272,29 @@ def search_layer(W, X, sx, bits: int = 4, group: int = 128, n_grid: int = 20,
             "s_best": S[best].copy(), "scales": S}
 
 
+def search_shared(Ws, X, sx, bits: int = 4, group: int = 128, n_grid: int = 20,
+                  s_floor: float = 1e-5, form: str = "direct", H=None):
+    """One alpha for several weights that read the same input X (q/k/v, gate/up): the search of
+    `search_layer` on the row-concatenated weights [W_0; W_1; ...] ([notes] 方法: the scale
+    multiplies input channels and its inverse is folded into the previous operator, so every
+    consumer of that operator's output must use the same s; R18). The loss is the mean of
+    squares over all N_0 + N_1 + ... outputs."""
+    Wc = np.concatenate([np.asarray(W) for W in Ws], axis=0)
+    return search_layer(Wc, X, sx, bits, group, n_grid, s_floor, form, H)
+
+
+def fold_scale(prev: np.ndarray, s: np.ndarray, axis: int) -> np.ndarray:
+    """The previous operator's parameters with s^-1 folded in ([notes] 方法, further
+    optimisations: fuse the input's down-scaling into the previous operator; R18): along `axis`
+    (1: columns, e.g. a norm weight [1, K]; 0: rows, e.g. the output channels of a previous
+    linear layer [K, ...]) every entry is divided by s of its channel, fp32(fp32(p) / s), then
+    rounded once to prev's dtype."""
+    p = np.asarray(prev)
+    s = np.asarray(s, dtype=F32)
+    s_b = s[None, :] if axis == 1 else s[:, None]
+    return (p.astype(F32) / s_b).astype(F32).astype(p.dtype)
+
+
 def relative_gap(losses) -> float:
     """(runner-up - best) / best: how clearly the grid point is the minimum."""
     ls = np.sort(np.asarray(losses, dtype=F64))
@@ -313,14 +341,17 @@ def pack_layer(W, s, bits: int = 4, group: int = 128, clip=None):
 # ---------------------------------------------------------------------------------------------
 # W4A16
 # ---------------------------------------------------------------------------------------------
-def w4a16(A: np.ndarray, qweight: np.ndarray, scales16: np.ndarray, s16: np.ndarray,
+def w4a16(A: np.ndarray, qweight: np.ndarray, scales16: np.ndarray, s16,
           group: int = 128) -> np.ndarray:
     """Y = (A / s) @ (q * step)^T in fp64 from the packed artefacts ([eng] 三 QuantLinear.forward:
     scale the input per channel, dequantize qweight * scales repeated over each group, then a
-    linear layer; R12: the activation is divided by s because W was multiplied by s)."""
+    linear layer; R12: the activation is divided by s because W was multiplied by s). With
+    s16 = None the division has been folded into the producer of A (R18): Y = A @ (q step)^T."""
     q = unpack_int4(qweight).astype(F64)
     Wd = q * np.repeat(np.asarray(scales16).astype(F64), group, axis=1)
-    Ap = np.asarray(A).astype(F64) / np.asarray(s16).astype(F64)[None, :]
+    Ap = np.asarray(A).astype(F64)
+    if s16 is not None:
+        Ap = Ap / np.asarray(s16).astype(F64)[None, :]
     return Ap @ Wd.T
 
 

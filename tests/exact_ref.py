@@ -116,3 +116,20 @@ def loss_exact(X, W, codes, deltas, s, group: int) -> Fraction:
             y = sum(Xf[m][k] * E[n][k] for k in range(K))
             tot += y * y
     return tot / (M * N)
+
+
+def rn16(fr: Fraction) -> np.float16:
+    """Round an exact rational to the nearest fp16 value, ties to the even significand."""
+    if fr == 0:
+        return np.float16(0.0)
+    f = np.float16(float(fr))
+    cands = [f, np.nextafter(f, np.float16(np.inf)), np.nextafter(f, np.float16(-np.inf))]
+    best = None
+    for c in cands:
+        if not np.isfinite(c):
+            continue
+        bits = int(np.array(c, dtype=np.float16).view(np.uint16))
+        key = (abs(Fraction(float(c)) - fr), bits & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return np.float16(best[1])

@@ -408,3 +408,72 @@ def test_p13_ties_keep_the_lowest_ratio_index():
     res = oracle.clip_search(W, X, s, n_clip=5, clip_min=0.5)
     assert res["best"][1, 0] == 0 and res["ratio"][1, 0] == np.float32(1.0)
     assert (res["best"][:, 1] == 0).all() and (res["err"][:, :, 1] == 0).all()
+
+
+
+# --- P14: shared scale and folding (R18) -----------------------------------------------------
+def test_p14_shared_loss_is_the_row_weighted_mean_of_the_layer_losses():
+    """One s for several weights: at every grid point the loss over the concatenated rows is the
+    row-count-weighted mean of each weight's own loss (search_layer) at that s."""
+    g = np.random.default_rng(70)
+    X = (g.standard_normal((120, 256)) * np.exp(g.standard_normal(256))).astype(np.float32)
+    Ws = [(0.02 * g.standard_normal((n, 256))).astype(np.float32) for n in (40, 16, 72)]
+    sx = oracle.act_stats(X)
+    sh = oracle.search_shared(Ws, X, sx, n_grid=7)
+    per = [oracle.search_layer(W, X, sx, n_grid=7)["losses"] for W in Ws]
+    want = sum(n * L for n, L in zip((40, 16, 72), per)) / 128
+    np.testing.assert_allclose(sh["losses"], want, rtol=1e-12)
+    assert sh["best"] == int(np.argmin(want))
+
+
+def test_p14_fold_is_the_correctly_rounded_quotient():
+    """fp16 and fp32 parameters: each folded value is the fp16 (fp32) value nearest to the fp32
+    quotient, both axes."""
+    g = np.random.default_rng(71)
+    s = np.exp(g.standard_normal(24)).astype(np.float32)
+    for dt, rn in ((np.float16, ex.rn16), (np.float32, lambda fr: np.float32(ex.rn32(fr)))):
+        gamma = (1 + 0.1 * g.standard_normal((1, 24))).astype(dt)
+        f1 = oracle.fold_scale(gamma, s, axis=1)
+        Wp = (0.05 * g.standard_normal((24, 5))).astype(dt)
+        f0 = oracle.fold_scale(Wp, s, axis=0)
+        for k in range(24):
+            q = ex.rn32(Fraction(float(gamma[0, k])) / Fraction(float(s[k])))
+            assert f1[0, k] == rn(Fraction(float(q)))
+            for c in range(5):
+                q = ex.rn32(Fraction(float(Wp[k, c])) / Fraction(float(s[k])))
+                assert f0[k, c] == rn(Fraction(float(q)))
+
+
+def test_p14_folding_then_the_scaled_layer_reproduces_the_layer():
+    """With s a power of two per channel, folding s^-1 into a norm weight and multiplying the
+    layer's weight by s changes nothing at all: (x gamma / s) (W s)^T == (x gamma) W^T exactly;
+    and W4A16 on the folded input without the division equals W4A16 with it."""
+    g = np.random.default_rng(72)
+    K = 256
+    s = np.exp2(g.integers(-3, 4, K)).astype(np.float32)
+    gamma = (1 + 0.1 * g.standard_normal((1, K))).astype(np.float32)
+    x = g.standard_normal((6, K)).astype(np.float32)
+    W = (0.02 * g.standard_normal((10, K))).astype(np.float32)
+    gf = oracle.fold_scale(gamma, s, axis=1)
+    lhs = (x.astype(np.float64) * gf.astype(np.float64)) @ (W.astype(np.float64) * s).T
+    rhs = (x.astype(np.float64) * gamma.astype(np.float64)) @ W.astype(np.float64).T
+    assert np.array_equal(lhs, rhs)
+    p = oracle.pack_layer(W, s)
+    A = (x * gamma).astype(np.float16)
+    Af = (A.astype(np.float32) / s[None, :]).astype(np.float16)   # exact: s is 2^k
+    np.testing.assert_array_equal(oracle.w4a16(Af, p["qweight"], p["scales16"], None),
+                                  oracle.w4a16(A, p["qweight"], p["scales16"], p["s16"]))
+
+
+def test_p14_w4a16_without_s_exact_on_a_tiny_case():
+    """W4A16 with the division folded away: Y = A (q step)^T, checked with exact rationals."""
+    g = np.random.default_rng(73)
+    q = g.integers(-8, 8, size=(3, 128)).astype(np.int8)
+    step = (0.01 * (1 + g.random((3, 1)))).astype(np.float16)
+    A = g.standard_normal((2, 128)).astype(np.float16)
+    Y = oracle.w4a16(A, oracle.pack_int4(q), step, None)
+    for m in range(2):
+        for n in range(3):
+            want = sum(Fraction(float(A[m, k])) * int(q[n, k]) * Fraction(float(step[n, 0]))
+                       for k in range(128))
+            assert Y[m, n] == pytest.approx(float(want), rel=1e-13, abs=1e-15)
