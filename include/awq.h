@@ -13,6 +13,9 @@
  *   4. awq_pack_int4     codes of Q(W s*) (clipped by r if given) packed 8 per uint32, fp16
  *                        group steps, fp16 s*
  *   5. w4a16_gemm        Y = (A / s) (q * step)^T with fp16 A and Y
+ * and, for weights that read the same input (q/k/v, gate/up), awq_search_layers (one s for all
+ * of them) with awq_fold_scale (s^-1 folded into the operator that produces the input, after
+ * which w4a16_gemm runs without s).
  *
  * Pages defining the operations (cited by title and section):
  *   [notes]  bg51717.github.io/14592, notes on "AWQ: Activation-aware Weight Quantization for
@@ -72,8 +75,9 @@ enum {
   AWQ_FLAG_SCALE16_SUBNORMAL = 1u << 5,/* a non-zero group step or s is fp16-subnormal or 0     */
   AWQ_FLAG_NONFINITE_LOSS = 1u << 6,   /* some L_i is not finite                                */
   AWQ_FLAG_STEP_UNDERFLOW = 1u << 7,   /* a group with max|w s| > 0 got step 0 (codes set to 0)*/
-  AWQ_FLAG_CLIP_RANGE = 1u << 8        /* a clip ratio given to awq_pack_int4 is outside (0, 1]; */
+  AWQ_FLAG_CLIP_RANGE = 1u << 8,       /* a clip ratio given to awq_pack_int4 is outside (0, 1]; */
                                        /* that group was packed unclipped                       */
+  AWQ_FLAG_FOLD_RANGE = 1u << 9        /* awq_fold_scale turned a finite parameter into Inf      */
 };
 
 /* How awq_search_layer evaluates the loss (same value, different contraction):
@@ -151,6 +155,37 @@ awq_status awq_search_layer(const void* W, awq_dtype wdt, int64_t N, int64_t K,
                             uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * awq_search_layers -- one alpha for several weights that read the same input X (the q, k and v
+ * projections after one norm, or gate and up): [notes] 方法 folds s^-1 into the operator that
+ * produces X (see awq_fold_scale), so all of X's consumers must share s. The search above runs
+ * on the rows of W[0], W[1], ... stacked (no copy is made): L_i is the mean of squares over all
+ * sum_l N[l] outputs.
+ * W      host array of n_w device pointers, each [N[l], K] row-major, dtype wdt, 16-byte
+ *        aligned; N host array of n_w row counts; 1 <= n_w <= 64.
+ * The workspace is awq_search_workspace_bytes(M, sum_l N[l], K, xdt, cfg). Everything else as
+ * awq_search_layer.
+ * ---------------------------------------------------------------------------------------- */
+awq_status awq_search_layers(const void* const* W, const int64_t* N, int32_t n_w,
+                             awq_dtype wdt, int64_t K, const void* X, awq_dtype xdt, int64_t M,
+                             const float* sx, const awq_cfg* cfg, double* losses,
+                             int32_t* best, float* s_best, uint32_t* flags, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * awq_fold_scale -- fold s^-1 into the previous operator's parameters, in place ([notes] 方法,
+ * further optimisations: fuse the input's down-scaling into the previous operator).
+ * prev   device [rows, cols] with row stride ld elements, dtype AWQ_F16, AWQ_BF16 or AWQ_F32.
+ * s      device fp32: [cols] for axis 1 (a norm weight or bias as rows = 1, cols = K), [rows]
+ *        for axis 0 (a previous linear layer's output channels, prev = its weight [K, *]).
+ * Each element becomes fp32(fp32(p) / s[channel]), rounded once to prev's dtype (nearest even).
+ * After folding, pass s16 = NULL to w4a16_gemm.
+ * flags  in/out: FOLD_RANGE.
+ * Errors: AWQ_ERR_NULL, AWQ_ERR_DTYPE, AWQ_ERR_SHAPE (sizes, ld < cols, axis, misalignment).
+ * ---------------------------------------------------------------------------------------- */
+awq_status awq_fold_scale(void* prev, awq_dtype dtype, int64_t rows, int64_t cols, int64_t ld,
+                          const float* s, int32_t axis, uint32_t* flags, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * awq_search_layer_profiled -- awq_search_layer plus the duration of each of its kernels,
  * measured with HIP events recorded between the launches on `stream`. Unlike every other call
  * it BLOCKS the host until the stream has finished the search (it reads the events back).
@@ -223,7 +258,8 @@ awq_status awq_pack_int4(const void* W, awq_dtype wdt, int64_t N, int64_t K, con
  * w4a16_gemm -- QuantLinear.forward of [eng] 三 on the packed artefacts:
  *   Y[m,n] = sum_k (A[m,k] / s16[k]) * sext4(q[n,k]) * scales16[n, k/group]
  * A        fp16 bits [M, K]; qweight uint32 [N, K/8]; scales16 fp16 bits [N, K/group];
- *          s16 fp16 bits [K]; Y out, fp16 bits [M, N]. group must be 128; K % 128 == 0,
+ *          s16 fp16 bits [K], or NULL when s^-1 has been folded into the producer of A (then
+ *          Y = A (q * step)^T); Y out, fp16 bits [M, N]. group must be 128; K % 128 == 0,
  *          K <= 12288.
  * Products are formed on fp16 operands (fp16(1/s) and fp16(code * fp16(1/s)), each rounded
  * once) with fp32 accumulation; the per-group step multiplies the fp32 partial of each group;

@@ -29,6 +29,7 @@ FLAG_SCALE16_SUBNORMAL = 1 << 5
 FLAG_NONFINITE_LOSS = 1 << 6
 FLAG_STEP_UNDERFLOW = 1 << 7
 FLAG_CLIP_RANGE = 1 << 8
+FLAG_FOLD_RANGE = 1 << 9
 
 
 class AwqCfg(ctypes.Structure):
@@ -54,6 +55,9 @@ SIGNATURES = {
     "awq_search_layer_profiled": (_E, [_P, _E, _I64, _I64, _P, _E, _I64, _P,
                                        ctypes.POINTER(AwqCfg), _P, _P, _P, _P, _P, _SZ, _P,
                                        ctypes.POINTER(ctypes.c_float)]),
+    "awq_search_layers": (_E, [ctypes.POINTER(_P), ctypes.POINTER(_I64), _I32, _E, _I64, _P, _E,
+                               _I64, _P, ctypes.POINTER(AwqCfg), _P, _P, _P, _P, _P, _SZ, _P]),
+    "awq_fold_scale": (_E, [_P, _E, _I64, _I64, _I64, _P, _I32, _P, _P]),
     "awq_clip_workspace_bytes": (_SZ, [_I64, _I64, _I64, _E, ctypes.POINTER(AwqCfg)]),
     "awq_clip_search": (_E, [_P, _E, _I64, _I64, _P, _E, _I64, _P, ctypes.POINTER(AwqCfg), _P,
                              _P, _P, _P, _SZ, _P]),

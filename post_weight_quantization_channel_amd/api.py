@@ -181,6 +181,58 @@ def clip_search(W: torch.Tensor, X: torch.Tensor, s: torch.Tensor, cfg: AwqConfi
     return ClipResult(clip, err, flags)
 
 
+def search_layers(Ws: list, X: torch.Tensor, sx: torch.Tensor, cfg: AwqConfig = AwqConfig(),
+                  flags: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> SearchResult:
+    """One alpha for several weights that read the same X (rows stacked, no copy)."""
+    lib = _lib.load()
+    for i, W in enumerate(Ws):
+        _dev(W, f"W[{i}]")
+    _dev(X, "X")
+    _dev(sx, "sx")
+    K = X.shape[1]
+    if any(W.shape[1] != K or W.dtype != Ws[0].dtype for W in Ws):
+        raise ValueError("every W must be [N_l, K] with the dtype of W[0]")
+    Ns = [int(W.shape[0]) for W in Ws]
+    M, N = X.shape[0], sum(Ns)
+    c = cfg.c()
+    flags = _flags(X.device, flags)
+    nbytes = lib.awq_search_workspace_bytes(M, N, K, _DT[X.dtype], c)
+    if nbytes == 0:
+        raise ValueError("invalid shape or config for the search")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=X.device)
+    losses = torch.empty(cfg.n_grid, dtype=torch.float64, device=X.device)
+    best = torch.empty(1, dtype=torch.int32, device=X.device)
+    s_best = torch.empty(K, dtype=torch.float32, device=X.device)
+    ptrs = (ctypes.c_void_p * len(Ws))(*[W.data_ptr() for W in Ws])
+    rows = (ctypes.c_int64 * len(Ws))(*Ns)
+    check("awq_search_layers", lib.awq_search_layers(
+        ptrs, rows, len(Ws), _DT[Ws[0].dtype], K, X.data_ptr(), _DT[X.dtype], M, sx.data_ptr(),
+        c, losses.data_ptr(), best.data_ptr(), s_best.data_ptr(), flags.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), _stream(X)))
+    return SearchResult(losses, best, s_best, flags)
+
+
+def fold_scale(prev: torch.Tensor, s: torch.Tensor, axis: int,
+               flags: torch.Tensor | None = None) -> torch.Tensor:
+    """In place: prev /= s along `axis` (1: columns of a [rows, K] parameter such as a norm
+    weight [1, K]; 0: rows, e.g. a previous linear layer's output channels). Returns flags."""
+    lib = _lib.load()
+    _dev(s, "s")
+    if not prev.is_cuda or prev.dim() != 2 or prev.stride(1) != 1:
+        raise ValueError("prev must be a 2-D device tensor with unit column stride")
+    rows, cols = prev.shape
+    if s.dtype != torch.float32 or s.shape != ((cols,) if axis == 1 else (rows,)):
+        raise ValueError("s must be fp32 with one entry per folded channel")
+    flags = _flags(prev.device, flags)
+    check("awq_fold_scale", lib.awq_fold_scale(prev.data_ptr(), _DT[prev.dtype], rows, cols,
+                                               prev.stride(0) if rows > 1 else cols,
+                                               s.data_ptr(), axis, flags.data_ptr(),
+                                               _stream(prev)))
+    return flags
+
+
 def pack_int4(W: torch.Tensor, s: torch.Tensor, cfg: AwqConfig = AwqConfig(),
               with_codes: bool = False, flags: torch.Tensor | None = None,
               clip: torch.Tensor | None = None) -> PackResult:
@@ -211,21 +263,26 @@ def pack_int4(W: torch.Tensor, s: torch.Tensor, cfg: AwqConfig = AwqConfig(),
 
 
 def w4a16_gemm(A: torch.Tensor, qweight: torch.Tensor, scales16: torch.Tensor,
-               s16: torch.Tensor, group: int = 128, out: torch.Tensor | None = None
+               s16: torch.Tensor | None, group: int = 128, out: torch.Tensor | None = None
                ) -> torch.Tensor:
-    """Y = (A / s) (q * step)^T, fp16 [M, N]."""
+    """Y = (A / s) (q * step)^T, fp16 [M, N]; s16 = None when s^-1 is folded into A's producer."""
     lib = _lib.load()
-    for t, nm in ((A, "A"), (qweight, "qweight"), (scales16, "scales16"), (s16, "s16")):
+    for t, nm in ((A, "A"), (qweight, "qweight"), (scales16, "scales16")):
         _dev(t, nm)
+    if s16 is not None:
+        _dev(s16, "s16")
     M, K = A.shape
     N = qweight.shape[0]
-    if A.dtype != torch.float16 or scales16.dtype != torch.float16 or s16.dtype != torch.float16:
+    if A.dtype != torch.float16 or scales16.dtype != torch.float16 or \
+            (s16 is not None and s16.dtype != torch.float16):
         raise ValueError("A, scales16 and s16 must be fp16")
-    if qweight.shape != (N, K // 8) or scales16.shape != (N, K // group) or s16.shape != (K,):
+    if qweight.shape != (N, K // 8) or scales16.shape != (N, K // group) or \
+            (s16 is not None and s16.shape != (K,)):
         raise ValueError("packed artefact shapes do not match A")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=A.device)
     check("w4a16_gemm", lib.w4a16_gemm(A.data_ptr(), M, N, K, group, qweight.data_ptr(),
-                                       scales16.data_ptr(), s16.data_ptr(), out.data_ptr(),
+                                       scales16.data_ptr(),
+                                       s16.data_ptr() if s16 is not None else None, out.data_ptr(),
                                        _stream(A)))
     return out

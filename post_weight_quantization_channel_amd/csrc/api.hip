@@ -105,7 +105,7 @@ const char* awq_status_string(awq_status status) {
   return "unknown awq_status";
 }
 
-int32_t awq_version(void) { return 10200; }
+int32_t awq_version(void) { return 10300; }
 
 size_t awq_act_stats_workspace_bytes(int64_t M, int64_t K) {
   if (M < 1 || K < 1 || M > kMaxDim || K > kMaxDim) return 0;
@@ -150,19 +150,31 @@ size_t awq_search_workspace_bytes(int64_t M, int64_t N, int64_t K, awq_dtype xdt
 
 namespace {
 
-// Shared body of awq_search_layer and awq_search_layer_profiled. With `ev` non-null, event
+// Shared body of the search calls: the weights Ws[0..n_w) (N_l rows each, all reading the same
+// X) are searched together, their rows stacked in one error stack. With `ev` non-null, event
 // ev[j] is recorded before stage j and ev[AWQ_SEARCH_STAGES] after the last stage.
-awq_status search_impl(const void* W, awq_dtype wdt, int64_t N, int64_t K, const void* X,
-                       awq_dtype xdt, int64_t M, const float* sx, const awq_cfg* cfg,
-                       double* losses, int32_t* best, float* s_best, uint32_t* flags, void* ws,
-                       size_t ws_bytes, hipStream_t stream, hipEvent_t* ev) {
-  if (!W || !X || !sx || !cfg || !losses || !best || !s_best || !flags) return AWQ_ERR_NULL;
+constexpr int kMaxSharedWeights = 64;
+
+awq_status search_impl(const void* const* Ws, const int64_t* Ns, int n_w, awq_dtype wdt,
+                       int64_t K, const void* X, awq_dtype xdt, int64_t M, const float* sx,
+                       const awq_cfg* cfg, double* losses, int32_t* best, float* s_best,
+                       uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream,
+                       hipEvent_t* ev) {
+  if (!Ws || !Ns || !X || !sx || !cfg || !losses || !best || !s_best || !flags)
+    return AWQ_ERR_NULL;
+  if (n_w < 1 || n_w > kMaxSharedWeights) return AWQ_ERR_SHAPE;
+  int64_t N = 0;
+  for (int l = 0; l < n_w; ++l) {
+    if (!Ws[l]) return AWQ_ERR_NULL;
+    if (Ns[l] < 1 || Ns[l] > kMaxDim || !aligned16(Ws[l])) return AWQ_ERR_SHAPE;
+    N += Ns[l];
+  }
   const awq_status cs = check_cfg(cfg);
   if (cs != AWQ_OK) return cs;
   if (wdt != AWQ_F16 && wdt != AWQ_F32) return AWQ_ERR_DTYPE;
   if (!valid_dtype(xdt)) return AWQ_ERR_DTYPE;
   // K <= 2^22 keeps the loss kernel's 32-bit buffer offsets (256 rows x 2K bytes) in range
-  if (!search_shape_ok(M, N, K, cfg) || !aligned16(W) || !aligned16(X)) return AWQ_ERR_SHAPE;
+  if (!search_shape_ok(M, N, K, cfg) || !aligned16(X)) return AWQ_ERR_SHAPE;
   const SearchLayout L = search_layout(M, N, K, xdt, cfg->n_grid, cfg->form);
   if ((int64_t)L.tiles_per_alpha * cfg->n_grid > (int64_t(1) << 31) - 1) return AWQ_ERR_SHAPE;
   if (!ws || ws_bytes < L.total || !aligned16(ws)) return AWQ_ERR_WORKSPACE;
@@ -205,11 +217,15 @@ awq_status search_impl(const void* W, awq_dtype wdt, int64_t N, int64_t K, const
     mark(3);
   }
   mark(4);
-  if (e == hipSuccess) e = awq::launch_absmax(W, (int)wdt, N, K, dcol, ctrl, flags, stream);
+  for (int l = 0; l < n_w && e == hipSuccess; ++l)
+    e = awq::launch_absmax(Ws[l], (int)wdt, Ns[l], K, dcol, ctrl, flags, stream);
   mark(5);
-  if (e == hipSuccess)
-    e = awq::launch_quantize_stack(W, (int)wdt, N, K, S, cfg->n_grid, cfg->bits, dcol, ctrl, E,
-                                   flags, stream);
+  int64_t row = 0;
+  for (int l = 0; l < n_w && e == hipSuccess; ++l) {
+    e = awq::launch_quantize_stack(Ws[l], (int)wdt, Ns[l], K, S, cfg->n_grid, cfg->bits, dcol,
+                                   ctrl, E + row * K, N, flags, stream);
+    row += Ns[l];
+  }
   mark(6);
   if (e == hipSuccess) {
     if (gram)
@@ -231,8 +247,18 @@ awq_status awq_search_layer(const void* W, awq_dtype wdt, int64_t N, int64_t K,
                             const void* X, awq_dtype xdt, int64_t M, const float* sx,
                             const awq_cfg* cfg, double* losses, int32_t* best, float* s_best,
                             uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return search_impl(W, wdt, N, K, X, xdt, M, sx, cfg, losses, best, s_best, flags, ws, ws_bytes,
-                     stream, nullptr);
+  if (!W) return AWQ_ERR_NULL;
+  return search_impl(&W, &N, 1, wdt, K, X, xdt, M, sx, cfg, losses, best, s_best, flags, ws,
+                     ws_bytes, stream, nullptr);
+}
+
+awq_status awq_search_layers(const void* const* W, const int64_t* N, int32_t n_w,
+                             awq_dtype wdt, int64_t K, const void* X, awq_dtype xdt, int64_t M,
+                             const float* sx, const awq_cfg* cfg, double* losses,
+                             int32_t* best, float* s_best, uint32_t* flags, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  return search_impl(W, N, n_w, wdt, K, X, xdt, M, sx, cfg, losses, best, s_best, flags, ws,
+                     ws_bytes, stream, nullptr);
 }
 
 awq_status awq_search_layer_profiled(const void* W, awq_dtype wdt, int64_t N, int64_t K,
@@ -247,8 +273,9 @@ awq_status awq_search_layer_profiled(const void* W, awq_dtype wdt, int64_t N, in
     if (hipEventCreate(&ev[made]) != hipSuccess) break;
   awq_status st = AWQ_ERR_HIP;
   if (made == AWQ_SEARCH_STAGES + 1) {
-    st = search_impl(W, wdt, N, K, X, xdt, M, sx, cfg, losses, best, s_best, flags, ws,
-                     ws_bytes, stream, ev);
+    st = W ? search_impl(&W, &N, 1, wdt, K, X, xdt, M, sx, cfg, losses, best, s_best, flags,
+                         ws, ws_bytes, stream, ev)
+           : AWQ_ERR_NULL;
     if (st == AWQ_OK && hipEventSynchronize(ev[AWQ_SEARCH_STAGES]) != hipSuccess) st = AWQ_ERR_HIP;
     for (int j = 0; st == AWQ_OK && j < AWQ_SEARCH_STAGES; ++j)
       if (hipEventElapsedTime(&stage_ms[j], ev[j], ev[j + 1]) != hipSuccess) st = AWQ_ERR_HIP;
@@ -352,13 +379,25 @@ awq_status awq_clip_search(const void* W, awq_dtype wdt, int64_t N, int64_t K, c
   return hip_status(e);
 }
 
+awq_status awq_fold_scale(void* prev, awq_dtype dtype, int64_t rows, int64_t cols, int64_t ld,
+                          const float* s, int32_t axis, uint32_t* flags, hipStream_t stream) {
+  if (!prev || !s || !flags) return AWQ_ERR_NULL;
+  if (!valid_dtype(dtype)) return AWQ_ERR_DTYPE;
+  const size_t es = dtype == AWQ_F32 ? 4 : 2;
+  if (rows < 1 || cols < 1 || ld < cols || rows > kMaxDim || cols > kMaxDim || ld > kMaxDim ||
+      (axis != 0 && axis != 1) || (reinterpret_cast<uintptr_t>(prev) % es) ||
+      (reinterpret_cast<uintptr_t>(s) & 3u))
+    return AWQ_ERR_SHAPE;
+  return hip_status(awq::launch_fold(prev, (int)dtype, rows, cols, ld, s, axis, flags, stream));
+}
+
 awq_status w4a16_gemm(const uint16_t* A, int64_t M, int64_t N, int64_t K, int32_t group,
                       const uint32_t* qweight, const uint16_t* scales16, const uint16_t* s16,
                       uint16_t* Y, hipStream_t stream) {
-  if (!A || !qweight || !scales16 || !s16 || !Y) return AWQ_ERR_NULL;
+  if (!A || !qweight || !scales16 || !Y) return AWQ_ERR_NULL;   // s16 NULL: s folded away
   if (group != 128) return AWQ_ERR_CONFIG;
   if (M < 1 || N < 1 || K < 128 || K % 128 || M > kMaxDim || N > kMaxDim || K > kMaxW4A16K ||
-      !aligned16(A) || !aligned16(qweight) || !aligned16(s16))
+      !aligned16(A) || !aligned16(qweight) || (s16 && !aligned16(s16)))
     return AWQ_ERR_SHAPE;
   return hip_status(awq::launch_w4a16(A, M, N, K, qweight, scales16, s16, Y, stream));
 }

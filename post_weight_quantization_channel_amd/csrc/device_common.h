@@ -32,6 +32,7 @@ enum : uint32_t {
   kFlagNonfiniteLoss = 1u << 6,
   kFlagStepUnderflow = 1u << 7,
   kFlagClipRange = 1u << 8,
+  kFlagFoldRange = 1u << 9,
 };
 
 __device__ __forceinline__ float h2f(uint16_t b) {
@@ -42,6 +43,12 @@ __device__ __forceinline__ uint16_t f2h(float f) {  // round to nearest even
 }
 __device__ __forceinline__ float bf2f(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even; NaN stays NaN
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
 }
 
 // Load 8 consecutive elements starting at p (16-byte aligned for 16-bit types, 32-byte for f32)

@@ -52,10 +52,13 @@ hipError_t launch_absmax(const void* W, int dtype, int64_t N, int64_t K, const f
                          SearchCtrl* ctrl, uint32_t* flags, hipStream_t stream);
 hipError_t launch_x_to_f16(const void* X, int dtype, int64_t count, uint16_t* X16,
                            uint32_t* flags, hipStream_t stream);
-// E_i * 2^escale (dcol == nullptr) or E_i[n,k] * dcol[k] * 2^escale
+// E_i * 2^escale (dcol == nullptr) or E_i[n,k] * dcol[k] * 2^escale, for the N rows of W, written
+// to rows 0..N-1 of Estack whose grid-point slices are ld_rows rows apart (ld_rows >= N: several
+// weights fill one stack)
 hipError_t launch_quantize_stack(const void* W, int dtype, int64_t N, int64_t K, const float* S,
                                  int n_grid, int bits, const float* dcol, const SearchCtrl* ctrl,
-                                 uint16_t* Estack, uint32_t* flags, hipStream_t stream);
+                                 uint16_t* Estack, int64_t ld_rows, uint32_t* flags,
+                                 hipStream_t stream);
 hipError_t launch_lossgemm(const uint16_t* X16, int64_t M, int64_t K, const uint16_t* Estack,
                            int64_t N, int n_grid, double* partials, hipStream_t stream);
 hipError_t launch_finalize(const double* partials, int64_t tiles_per_alpha, int n_grid,
@@ -68,6 +71,10 @@ hipError_t launch_finalize(const double* partials, int64_t tiles_per_alpha, int 
 hipError_t launch_pack(const void* W, int dtype, int64_t N, int64_t K, const float* s,
                        const float* clip, int bits, uint32_t* qweight, uint16_t* scales16,
                        uint16_t* s16, int8_t* codes, uint32_t* flags, hipStream_t stream);
+
+// ---- folding s^-1 into the previous operator (fold.hip) ----
+hipError_t launch_fold(void* prev, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                       const float* s, int axis, uint32_t* flags, hipStream_t stream);
 
 // ---- clipping search (clip.hip) ----
 // Per (row, group of 128): the ratio of the grid 1 .. clip_min whose clipped quantization of

@@ -170,7 +170,7 @@ template <int DT, bool COL>
 __global__ __launch_bounds__(256) void quantize_stack_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ S, int n_grid,
     float qmin, float qmax, const float* __restrict__ dcol, const SearchCtrl* __restrict__ ctrl,
-    uint16_t* __restrict__ Estack, uint32_t* __restrict__ flags) {
+    uint16_t* __restrict__ Estack, int64_t ld_rows, uint32_t* __restrict__ flags) {
   constexpr int ES = (DT == kF32) ? 4 : 2;
   const int64_t chunks = K / 8;
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
       for (int t = 0; t < 8; ++t) w[r][t] = 0.0f;
     }
   }
-  const size_t stride_alpha = (size_t)N * (size_t)K;
+  const size_t stride_alpha = (size_t)ld_rows * (size_t)K;
   for (int i = 0; i < n_grid; ++i) {
     float s[8], inv[8];
     load8_f32<kF32>(S + (size_t)i * K + c8 * 8, s);
@@ -234,14 +234,16 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
 
 hipError_t launch_quantize_stack(const void* W, int dtype, int64_t N, int64_t K, const float* S,
                                  int n_grid, int bits, const float* dcol, const SearchCtrl* ctrl,
-                                 uint16_t* Estack, uint32_t* flags, hipStream_t stream) {
+                                 uint16_t* Estack, int64_t ld_rows, uint32_t* flags,
+                                 hipStream_t stream) {
   const float qmax = (float)((1 << (bits - 1)) - 1);
   const float qmin = -(float)(1 << (bits - 1));
   const int64_t threads = ((N + kQuantRows - 1) / kQuantRows) * (K / 8);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
 #define AWQ_QS(DT_, COL_)                                                                       \
   quantize_stack_kernel<DT_, COL_><<<blocks, 256, 0, stream>>>(W, N, K, S, n_grid, qmin, qmax,   \
-                                                               dcol, ctrl, Estack, flags)
+                                                               dcol, ctrl, Estack, ld_rows,   \
+                                                               flags)
   if (dtype == kF32) {
     if (dcol) AWQ_QS(kF32, true); else AWQ_QS(kF32, false);
   } else {

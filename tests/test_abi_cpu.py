@@ -33,7 +33,8 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("awq_act_stats", "awq_search_layer", "awq_pack_int4", "w4a16_gemm",
               "awq_search_workspace_bytes", "awq_act_stats_workspace_bytes",
-              "awq_clip_search", "awq_clip_workspace_bytes",
+              "awq_clip_search", "awq_clip_workspace_bytes", "awq_search_layers",
+              "awq_fold_scale",
               "awq_status_string", "awq_version"):
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
@@ -48,7 +49,7 @@ def test_status_strings(lib):
     for code in range(7):
         s = lib.awq_status_string(code).decode()
         assert s.startswith("AWQ_")
-    assert lib.awq_version() == 10200
+    assert lib.awq_version() == 10300
 
 
 def cfg(bits=4, group=128, n_grid=20, s_floor=1e-5, form=0, n_clip=11, clip_min=0.5):
@@ -210,6 +211,51 @@ def test_clip_search_rejects(lib):
     assert need >= 512 * 12 + 2 * 65536 * 2 + 512 * 384 * 2 + 2 * 65536 * 4
     assert _clip(lib, ws_bytes=need - 1) == E.AWQ_ERR_WORKSPACE
     assert lib.awq_clip_workspace_bytes(300, 256, 512, 1, cfg(clip_min=2.0)) == 0
+
+
+def test_search_layers_rejects(lib):
+    E = _lib
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+
+    def call(ptrs=(FAKE, FAKE + 4096), rows=(100, 60), n_w=None, **kw):
+        a = dict(wdt=1, K=512, X=FAKE2, xdt=1, M=300, sx=FAKE, cfg=cfg(), losses=FAKE,
+                 best=FAKE, s_best=FAKE, flags=FAKE, ws=FAKE, ws_bytes=1 << 40)
+        a.update(kw)
+        n = len(ptrs) if n_w is None else n_w
+        pa = (P * max(1, len(ptrs)))(*ptrs)
+        ra = (I64 * max(1, len(rows)))(*rows)
+        c = a["cfg"]
+        return lib.awq_search_layers(pa, ra, n, a["wdt"], a["K"], a["X"], a["xdt"], a["M"],
+                                     a["sx"], ctypes.byref(c) if c is not None else None,
+                                     a["losses"], a["best"], a["s_best"], a["flags"], a["ws"],
+                                     a["ws_bytes"], None)
+    assert call(ptrs=(FAKE, None)) == E.AWQ_ERR_NULL
+    assert call(n_w=0) == E.AWQ_ERR_SHAPE
+    assert call(ptrs=(FAKE,) * 65, rows=(10,) * 65) == E.AWQ_ERR_SHAPE
+    assert call(rows=(100, 0)) == E.AWQ_ERR_SHAPE
+    assert call(ptrs=(FAKE, FAKE + 8)) == E.AWQ_ERR_SHAPE       # misaligned second weight
+    assert call(cfg=cfg(bits=2)) == E.AWQ_ERR_CONFIG
+    need = lib.awq_search_workspace_bytes(300, 160, 512, 1, cfg())
+    assert call(ws_bytes=need - 1) == E.AWQ_ERR_WORKSPACE
+    assert lib.awq_search_layers(None, None, 1, 1, 512, FAKE2, 1, 300, FAKE,
+                                 ctypes.byref(cfg()), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                 None) == E.AWQ_ERR_NULL
+
+
+def test_fold_scale_rejects(lib):
+    E = _lib
+    f = lib.awq_fold_scale
+    assert f(None, 1, 1, 64, 64, FAKE, 1, FAKE, None) == E.AWQ_ERR_NULL
+    assert f(FAKE, 1, 1, 64, 64, None, 1, FAKE, None) == E.AWQ_ERR_NULL
+    assert f(FAKE, 1, 1, 64, 64, FAKE, 1, None, None) == E.AWQ_ERR_NULL
+    assert f(FAKE, 5, 1, 64, 64, FAKE, 1, FAKE, None) == E.AWQ_ERR_DTYPE
+    assert f(FAKE, 1, 0, 64, 64, FAKE, 1, FAKE, None) == E.AWQ_ERR_SHAPE
+    assert f(FAKE, 1, 2, 64, 32, FAKE, 1, FAKE, None) == E.AWQ_ERR_SHAPE     # ld < cols
+    assert f(FAKE, 1, 2, 64, 64, FAKE, 2, FAKE, None) == E.AWQ_ERR_SHAPE     # axis
+    assert f(FAKE + 1, 1, 2, 64, 64, FAKE, 1, FAKE, None) == E.AWQ_ERR_SHAPE  # fp16 misaligned
+    assert f(FAKE + 2, 0, 2, 64, 64, FAKE, 1, FAKE, None) == E.AWQ_ERR_SHAPE  # fp32 misaligned
+    assert f(FAKE, 1, 2, 64, 64, FAKE + 2, 1, FAKE, None) == E.AWQ_ERR_SHAPE  # s misaligned
 
 
 def test_w4a16_rejects(lib):

@@ -560,3 +560,109 @@ def test_end_to_end_with_clipping(awq):
     ref = oracle.w4a16(A, o["qweight"], o["scales16"], o["s16"])
     assert oracle.accuracy_report(host(Y), ref)["rel_fro"] <= W4A16_RTOL
     assert int(host(flags)[0]) == 0
+
+
+# ------------------------------------------------------------------------------------------------
+# Shared scale for weights that read one input, and folding s^-1 into the previous operator
+@pytest.mark.parametrize("form", FORMS)
+def test_search_layers_shared_parity(awq, form):
+    """q/k/v-like weights of different heights searched together (rows stacked, no copy)."""
+    g = np.random.default_rng(80)
+    X = workloads.c2_like_layer(n=8, k=384, m=700, config=81).X
+    Ws = [(0.02 * g.standard_normal((n, 384))).astype(np.float16) for n in (200, 64, 136)]
+    say("shared search", form, [W.shape for W in Ws], X.shape)
+    Xt = dev(X)
+    sx, flags = awq.act_stats(Xt)
+    res = awq.search_layers([dev(W) for W in Ws], Xt, sx, awq.AwqConfig(form=form), flags=flags)
+    orc = oracle.search_shared(Ws, X, oracle.act_stats(X))
+    bg = int(host(res.best)[0])
+    err, gap = check_alpha(host(res.losses), orc["losses"], bg, orc["best"])
+    say(f"max loss rel err {err:.2e}, oracle gap {gap:.2e}, alpha* {bg} / {orc['best']}")
+    assert np.array_equal(host(res.s_best), orc["scales"][bg])
+    assert int(host(flags)[0]) == 0
+
+
+def test_fold_scale_bit_exact(awq):
+    """fp16 norm weight (axis 1), fp32 previous-linear weight (axis 0), bf16 rows read through a
+    row-strided view (ld > cols)."""
+    g = np.random.default_rng(82)
+    K = 384
+    s = np.exp(0.7 * g.standard_normal(K)).astype(np.float32)
+    sd = dev(s)
+    gamma = (1 + 0.2 * g.standard_normal((1, K))).astype(np.float16)
+    t = dev(gamma)
+    awq.fold_scale(t, sd, axis=1)
+    assert np.array_equal(host(t).view(np.uint16), oracle.fold_scale(gamma, s, 1).view(np.uint16))
+    Wp = (0.05 * g.standard_normal((K, 200))).astype(np.float32)
+    t = dev(Wp)
+    awq.fold_scale(t, sd, axis=0)
+    assert np.array_equal(host(t).view(np.uint32), oracle.fold_scale(Wp, s, 0).view(np.uint32))
+    wide = (1 + 0.2 * g.standard_normal((3, K + 64))).astype(np.float32)
+    tb = dev(wide).to(torch.bfloat16)
+    view = tb[:, :K]
+    base = view.float().cpu().numpy()
+    flags = awq.fold_scale(view, sd, axis=1)
+    want = torch.from_numpy(oracle.fold_scale(base, s, 1)).to(torch.bfloat16)   # RN to bf16
+    got = tb.cpu()
+    assert torch.equal(got[:, :K].view(torch.int16), want.view(torch.int16))
+    assert torch.equal(got[:, K:].view(torch.int16),
+                       dev(wide).to(torch.bfloat16).cpu()[:, K:].view(torch.int16))
+    assert int(host(flags)[0]) == 0
+    say("fold: fp16 axis 1, fp32 axis 0, bf16 strided axis 1 bit-exact")
+
+
+def test_fold_overflow_is_flagged(awq):
+    from post_weight_quantization_channel_amd import _lib as L
+    gamma = np.full((1, 128), 30000.0, np.float16)
+    s = np.full(128, 0.25, np.float32)
+    flags = awq.fold_scale(dev(gamma), dev(s), axis=1)
+    assert int(host(flags)[0]) & L.FLAG_FOLD_RANGE
+
+
+@pytest.mark.parametrize("n,k,m", [(384, 512, 1), (384, 512, 16), (256, 4096, 3),
+                                   (4096, 4096, 1), (320, 512, 100)])
+def test_w4a16_without_s(awq, n, k, m):
+    A, qw, sc, _ = _w4a16_case(n, k, m, seed=n + m + 7)
+    say("w4a16 without s", (m, k), "x", (n, k))
+    Y = awq.w4a16_gemm(dev(A), dev(qw.view(np.int32)), dev(sc), None)
+    ref = oracle.w4a16(A, qw, sc, None)
+    rep = oracle.accuracy_report(host(Y).astype(np.float64), ref)
+    say(rep)
+    assert rep["rel_fro"] <= W4A16_RTOL
+
+
+def test_end_to_end_shared_scale_and_fold(awq):
+    """x -> norm weight gamma -> X = x gamma feeds three weights. One s for all three (shared
+    search), s^-1 folded into gamma, W4A16 on the folded activations without s: the outputs match
+    W4A16 with s on the unfolded X, and the oracle chain."""
+    g = np.random.default_rng(83)
+    K, M = 512, 600
+    x = workloads.c2_like_layer(n=8, k=K, m=M, config=84).X.astype(np.float32)
+    gamma = (1 + 0.2 * g.standard_normal((1, K))).astype(np.float16)
+    X = (x * gamma.astype(np.float32)).astype(np.float16)
+    Ws = [(0.02 * g.standard_normal((n, K))).astype(np.float16) for n in (256, 128, 128)]
+    say("end-to-end shared scale + fold", [W.shape for W in Ws], X.shape)
+    Xt = dev(X)
+    sx, flags = awq.act_stats(Xt)
+    res = awq.search_layers([dev(W) for W in Ws], Xt, sx, awq.AwqConfig(form="gram"),
+                            flags=flags)
+    orc = oracle.search_shared(Ws, X, oracle.act_stats(X))
+    bg = int(host(res.best)[0])
+    check_alpha(host(res.losses), orc["losses"], bg, orc["best"])
+    s = orc["scales"][bg]
+    gt = dev(gamma)
+    awq.fold_scale(gt, res.s_best, axis=1, flags=flags)
+    gf = oracle.fold_scale(gamma, s, 1)
+    assert np.array_equal(host(gt).view(np.uint16), gf.view(np.uint16))
+    Af = (x[:16] * gf.astype(np.float32)).astype(np.float16)     # the folded norm's output
+    for W in Ws:
+        p = awq.pack_int4(dev(W), res.s_best, flags=flags)
+        Y_fold = host(awq.w4a16_gemm(dev(Af), p.qweight, p.scales16, None))
+        Y_s = host(awq.w4a16_gemm(dev(X[:16]), p.qweight, p.scales16, p.s16))
+        o = oracle.pack_layer(W, s)
+        ref = oracle.w4a16(X[:16], o["qweight"], o["scales16"], o["s16"])
+        r1 = oracle.accuracy_report(Y_fold.astype(np.float64), ref)["rel_fro"]
+        r2 = oracle.accuracy_report(Y_s.astype(np.float64), ref)["rel_fro"]
+        say(f"W {W.shape}: folded {r1:.2e}, with s {r2:.2e}")
+        assert r1 <= W4A16_RTOL and r2 <= W4A16_RTOL
+    assert int(host(flags)[0]) == 0
