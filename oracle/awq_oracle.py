@@ -40,6 +40,10 @@ Readings taken where the pages are silent, ambiguous or disagree (each is also u
       it is quantized; r is chosen on the grid 1 .. clip_min at the fixed s*, by the part of the
       output error that the group causes on its own (the [notes] objective restricted to the
       group's channels, so that the choices are separable), lowest index on ties.
+  R19 zero point ("AWQ 量化方案..." 三 Step 4 names a scale and a zero point per group; the
+      worked example of "量化方案详解", section AWQ, spreads 2^4 levels over a group's range
+      [min, max]): Delta = (max - min) / (2^b - 1), z = rint(-min / Delta), unsigned codes
+      clamp(rint(w s / Delta) + z, 0, 2^b - 1), each step in IEEE fp32, one rounding per step.
   R18 folding ([notes] 方法, further optimisations: fuse the input's down-scaling into the
       previous operator): every weight that reads the same X shares one s, searched on the
       row-concatenated weights; s^-1 is folded into the previous operator's parameters along
@@ -107,6 +111,43 @@ def code_range(bits: int) -> tuple[int, int]:
     return -(2 ** (bits - 1)), 2 ** (bits - 1) - 1
 
 
+def quantize_zp(W: np.ndarray, s: np.ndarray, bits: int = 4, group: int = 128, clip=None):
+    """Zero-point (asymmetric) codes of Q(W*s), one step and one zero point per (row, group)
+    (R19; "量化方案详解", section AWQ, worked example: a range [-3.2, 3.2] on 2^4 levels has the step
+    6.4 / 15 = 0.427; "AWQ 量化方案..." 三 Step 4 names a scale and a zero point per group):
+      ws    = fp32(w * s[k])                            (clipped first, as in `quantize`)
+      Delta = fp32( fp32(max ws - min ws) / (2^b - 1) )  over the group
+      z     = clamp(rint(fp32(-min ws / Delta)), 0, 2^b - 1)
+      q     = clamp(rint(fp32(ws / Delta)) + z, 0, 2^b - 1)
+    and Q(w*s) = (q - z) * Delta. A group with Delta = 0 gets q = z = 0 (R8).
+    Returns (q uint8 [N, K], Delta fp32 [N, K/group], z uint8 [N, K/group])."""
+    W = np.asarray(W)
+    if not np.all(np.isfinite(W)):
+        raise ValueError("non-finite weight")
+    N, K = W.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    qmax_u = 2 ** bits - 1
+    ws = W.astype(F32) * np.asarray(s, dtype=F32)[None, :]
+    wsg = ws.reshape(N, K // group, group)
+    if clip is not None:
+        r = np.asarray(clip, dtype=F32).reshape(N, K // group)
+        if not np.all((r > 0) & (r <= 1)):
+            raise ValueError("clip ratios must lie in (0, 1]")
+        c = (r * np.abs(wsg).max(axis=2)).astype(F32)
+        wsg = np.clip(wsg, -c[:, :, None], c[:, :, None])
+    mx = wsg.max(axis=2)
+    mn = wsg.min(axis=2)
+    rng_ = (mx - mn).astype(F32)                               # fp32 - fp32 -> fp32
+    delta = (rng_ / F32(qmax_u)).astype(F32)
+    live = delta > 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        z = np.where(live, np.clip(np.rint((-mn / delta).astype(F32)), 0, qmax_u), F32(0))
+        t = (wsg / delta[:, :, None]).astype(F32)
+    q = np.where(live[:, :, None], np.clip(np.rint(t) + z[:, :, None], 0, qmax_u), F32(0))
+    return q.reshape(N, K).astype(np.uint8), delta, z.astype(np.uint8)
+
+
 def quantize(W: np.ndarray, s: np.ndarray, bits: int = 4, group: int = 128, clip=None):
     """Codes and steps of Q(W*s), one step per (row, group of `group` input channels).
 
@@ -145,16 +186,19 @@ def quantize(W: np.ndarray, s: np.ndarray, bits: int = 4, group: int = 128, clip
     return q.reshape(N, K).astype(np.int8), delta
 
 
-def dequant_scaled(q: np.ndarray, delta: np.ndarray, group: int = 128) -> np.ndarray:
-    """Q(W*s) = q * Delta, in fp64, shape [N, K]."""
-    return q.astype(F64) * np.repeat(delta.astype(F64), group, axis=1)
+def dequant_scaled(q: np.ndarray, delta: np.ndarray, group: int = 128, z=None) -> np.ndarray:
+    """Q(W*s) = q * Delta (or (q - z) * Delta with zero points), in fp64, shape [N, K]."""
+    qq = q.astype(F64)
+    if z is not None:
+        qq = qq - np.repeat(np.asarray(z).astype(F64), group, axis=1)
+    return qq * np.repeat(delta.astype(F64), group, axis=1)
 
 
 def error_matrix(W: np.ndarray, q: np.ndarray, delta: np.ndarray, s: np.ndarray,
-                 group: int = 128) -> np.ndarray:
+                 group: int = 128, z=None) -> np.ndarray:
     """E = Q(W*s) / s - W in fp64. X @ E^T is Q(W*s)(s^-1 X) - W X in the tokens-by-rows
     layout, by linearity ([notes] 方法 objective; [eng] 二 equivalent transform)."""
-    return dequant_scaled(q, delta, group) / np.asarray(s, dtype=F64)[None, :] - \
+    return dequant_scaled(q, delta, group, z) / np.asarray(s, dtype=F64)[None, :] - \
         np.asarray(W).astype(F64)
 
 
@@ -219,7 +263,7 @@ def group_errors(E: np.ndarray, group: int = 128, X=None, H=None) -> np.ndarray:
 
 
 def clip_search(W, X, s, bits: int = 4, group: int = 128, n_clip: int = 11,
-                clip_min: float = 0.5, H=None):
+                clip_min: float = 0.5, H=None, zero_point: bool = False):
     """Per (row, group), the clip ratio of `clip_grid` whose quantization of W*s gives the
     smallest group error (`group_errors`), the lowest index on ties (R17, R10). The search runs
     at a fixed s (typically s*). Returns {"ratio": fp32 [N, K/group], "best": int [N, K/group],
@@ -230,8 +274,12 @@ def clip_search(W, X, s, bits: int = 4, group: int = 128, n_clip: int = 11,
     s = np.asarray(s, dtype=F32)
     err = np.empty((n_clip, N, K // group), dtype=F64)
     for j in range(n_clip):
-        q, d = quantize(W, s, bits, group, clip=np.full((N, K // group), r[j], dtype=F32))
-        E = error_matrix(W, q, d, s, group)
+        full = np.full((N, K // group), r[j], dtype=F32)
+        if zero_point:
+            q, d, z = quantize_zp(W, s, bits, group, clip=full)
+        else:
+            (q, d), z = quantize(W, s, bits, group, clip=full), None
+        E = error_matrix(W, q, d, s, group, z)
         err[j] = group_errors(E, group, X=None if H is not None else X, H=H)
     best = np.zeros((N, K // group), dtype=np.int64)
     for j in range(1, n_clip):                      # strict < keeps the lowest index on ties
@@ -250,7 +298,7 @@ def argmin_lowest(losses) -> int:
 
 
 def search_layer(W, X, sx, bits: int = 4, group: int = 128, n_grid: int = 20,
-                 s_floor: float = 1e-5, form: str = "direct", H=None):
+                 s_floor: float = 1e-5, form: str = "direct", H=None, zero_point: bool = False):
     """Grid search of [notes] 方法: for each alpha_i, s_i = s_X^alpha_i, quantize W*s_i, score
     L(s_i); alpha* = argmin. form='direct' evaluates the literal objective, form='gram' the
     identical quadratic form with H = X^T X (computed here unless given)."""
@@ -260,11 +308,14 @@ def search_layer(W, X, sx, bits: int = 4, group: int = 128, n_grid: int = 20,
         H = gram(X)
     losses = np.empty(n_grid, dtype=F64)
     for i in range(n_grid):
-        q, delta = quantize(W, S[i], bits, group)
+        if zero_point:
+            q, delta, z = quantize_zp(W, S[i], bits, group)
+        else:
+            (q, delta), z = quantize(W, S[i], bits, group), None
         if form == "direct":
-            losses[i] = output_loss(X, W, S[i], dequant_scaled(q, delta, group))
+            losses[i] = output_loss(X, W, S[i], dequant_scaled(q, delta, group, z))
         elif form == "gram":
-            losses[i] = loss_gram(H, error_matrix(W, q, delta, S[i], group), M)
+            losses[i] = loss_gram(H, error_matrix(W, q, delta, S[i], group, z), M)
         else:
             raise ValueError(form)
     best = argmin_lowest(losses)
@@ -273,14 +324,14 @@ def search_layer(W, X, sx, bits: int = 4, group: int = 128, n_grid: int = 20,
 
 
 def search_shared(Ws, X, sx, bits: int = 4, group: int = 128, n_grid: int = 20,
-                  s_floor: float = 1e-5, form: str = "direct", H=None):
+                  s_floor: float = 1e-5, form: str = "direct", H=None, zero_point: bool = False):
     """One alpha for several weights that read the same input X (q/k/v, gate/up): the search of
     `search_layer` on the row-concatenated weights [W_0; W_1; ...] ([notes] 方法: the scale
     multiplies input channels and its inverse is folded into the previous operator, so every
     consumer of that operator's output must use the same s; R18). The loss is the mean of
     squares over all N_0 + N_1 + ... outputs."""
     Wc = np.concatenate([np.asarray(W) for W in Ws], axis=0)
-    return search_layer(Wc, X, sx, bits, group, n_grid, s_floor, form, H)
+    return search_layer(Wc, X, sx, bits, group, n_grid, s_floor, form, H, zero_point)
 
 
 def fold_scale(prev: np.ndarray, s: np.ndarray, axis: int) -> np.ndarray:
@@ -317,6 +368,16 @@ def pack_int4(q: np.ndarray) -> np.ndarray:
     return out.astype(np.uint32)
 
 
+def unpack_uint4(qweight: np.ndarray) -> np.ndarray:
+    """Inverse of pack_int4 for zero-point codes: unsigned nibbles 0..15, uint8 [N, 8 * cols]."""
+    qw = np.asarray(qweight).astype(np.uint64)
+    N, C = qw.shape
+    out = np.empty((N, 8 * C), dtype=np.uint8)
+    for t in range(8):
+        out[:, t::8] = ((qw >> np.uint64(4 * t)) & np.uint64(0xF)).astype(np.uint8)
+    return out
+
+
 def unpack_int4(qweight: np.ndarray) -> np.ndarray:
     """Inverse of pack_int4: sign-extended nibbles, int8 [N, 8 * cols]."""
     qw = np.asarray(qweight).astype(np.uint64)
@@ -328,26 +389,36 @@ def unpack_int4(qweight: np.ndarray) -> np.ndarray:
     return out
 
 
-def pack_layer(W, s, bits: int = 4, group: int = 128, clip=None):
+def pack_layer(W, s, bits: int = 4, group: int = 128, clip=None, zero_point: bool = False):
     """The stored result of [eng] 三 (QuantLinear(q_weight, scales_per_group, awq_scale)):
-    packed codes of Q(W*s), per-group fp16 steps and the per-channel s in fp16 (R11).
-    The codes are those of `quantize` (with the clip ratios, if given), not re-derived from the
-    fp16 step."""
-    q, delta = quantize(W, s, bits, group, clip=clip)
+    packed codes of Q(W*s), per-group fp16 steps and the per-channel s in fp16 (R11); with zero
+    points (R19) the codes are the unsigned 0 .. 2^b-1 of `quantize_zp` in the same nibble
+    layout and "zeros" holds z per (row, group) as uint8. The codes are those of the quantizer
+    (with the clip ratios, if given), not re-derived from the fp16 step."""
+    if zero_point:
+        q, delta, z = quantize_zp(W, s, bits, group, clip=clip)
+    else:
+        (q, delta), z = quantize(W, s, bits, group, clip=clip), None
     return {"qweight": pack_int4(q), "scales16": delta.astype(np.float16),
-            "s16": np.asarray(s, dtype=F32).astype(np.float16), "codes": q, "delta": delta}
+            "s16": np.asarray(s, dtype=F32).astype(np.float16), "codes": q, "delta": delta,
+            "zeros": z}
 
 
 # ---------------------------------------------------------------------------------------------
 # W4A16
 # ---------------------------------------------------------------------------------------------
 def w4a16(A: np.ndarray, qweight: np.ndarray, scales16: np.ndarray, s16,
-          group: int = 128) -> np.ndarray:
+          group: int = 128, zeros=None) -> np.ndarray:
     """Y = (A / s) @ (q * step)^T in fp64 from the packed artefacts ([eng] 三 QuantLinear.forward:
     scale the input per channel, dequantize qweight * scales repeated over each group, then a
     linear layer; R12: the activation is divided by s because W was multiplied by s). With
-    s16 = None the division has been folded into the producer of A (R18): Y = A @ (q step)^T."""
-    q = unpack_int4(qweight).astype(F64)
+    s16 = None the division has been folded into the producer of A (R18): Y = A @ (q step)^T.
+    With zero points (R19) the codes are unsigned and the weight is (q - z) * step."""
+    if zeros is None:
+        q = unpack_int4(qweight).astype(F64)
+    else:
+        q = unpack_uint4(qweight).astype(F64) - np.repeat(np.asarray(zeros).astype(F64), group,
+                                                          axis=1)
     Wd = q * np.repeat(np.asarray(scales16).astype(F64), group, axis=1)
     Ap = np.asarray(A).astype(F64)
     if s16 is not None:

@@ -133,3 +133,24 @@ def rn16(fr: Fraction) -> np.float16:
         if best is None or key < best[0]:
             best = (key, c)
     return np.float16(best[1])
+
+
+def quantize_group_exact_zp(w, s, bits: int, ratio=None):
+    """Zero-point quantization of one group: ws = rn32(w s) (clipped to +-rn32(r max|ws|) with a
+    ratio); Delta = rn32(rn32(max - min) / (2^b - 1)); z = clamp(nearest integer to
+    rn32(-min / Delta), 0, 2^b - 1); code = clamp(nearest integer to rn32(ws / Delta) + z, 0,
+    2^b - 1). Returns (codes, Delta, z)."""
+    qmax_u = 2 ** bits - 1
+    ws = [Fraction(float(rn32(Fraction(float(wi)) * Fraction(float(si)))))
+          for wi, si in zip(w, s)]
+    if ratio is not None:
+        c = Fraction(float(rn32(Fraction(float(ratio)) * max(abs(v) for v in ws))))
+        ws = [min(max(v, -c), c) for v in ws]
+    mx, mn = max(ws), min(ws)
+    delta = rn32(Fraction(float(rn32(mx - mn))) / qmax_u)
+    if delta == 0:
+        return [0] * len(w), np.float32(0.0), 0
+    d = Fraction(float(delta))
+    z = min(max(round_half_even(Fraction(float(rn32(-mn / d)))), 0), qmax_u)
+    codes = [min(max(round_half_even(Fraction(float(rn32(v / d)))) + z, 0), qmax_u) for v in ws]
+    return codes, delta, z

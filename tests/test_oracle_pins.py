@@ -477,3 +477,92 @@ def test_p14_w4a16_without_s_exact_on_a_tiny_case():
             want = sum(Fraction(float(A[m, k])) * int(q[n, k]) * Fraction(float(step[n, 0]))
                        for k in range(128))
             assert Y[m, n] == pytest.approx(float(want), rel=1e-13, abs=1e-15)
+
+
+
+# --- P15: zero-point quantization (R19) --------------------------------------------------------
+def test_p15_worked_example_of_the_quantization_schemes_page():
+    """"量化方案详解", section AWQ: weights spanning [-3.2, 3.2] on 16 levels have the step
+    0.427; w = 0.21 is quantized to 0 (error 0.21), an output error of 21 at activation 100."""
+    W = np.zeros((1, 128), np.float32)
+    W[0, :3] = [-3.2, 3.2, 0.21]
+    q, d, z = oracle.quantize_zp(W, np.ones(128, np.float32), bits=4)
+    assert round(float(d[0, 0]), 3) == 0.427
+    level = (int(q[0, 2]) - int(z[0, 0])) * float(d[0, 0])
+    assert level == 0.0
+    assert abs(float(np.float32(0.21)) - level) == pytest.approx(0.21, abs=1e-7)
+    assert 100 * abs(float(np.float32(0.21)) - level) == pytest.approx(21, abs=1e-5)
+
+
+@pytest.mark.parametrize("bits,group", [(4, 128), (3, 64), (4, 64)])
+def test_p15_zero_point_brute_force_exact(bits, group):
+    """Codes, steps and zero points against exact rationals (with and without clipping), and
+    the search's losses against the exact rational objective with (q - z) Delta."""
+    W, X = _small_layer(90 + bits + group, 3, 256, 5)
+    W[1, :group] = np.abs(W[1, :group])          # a group with min >= 0: z clamps to 0
+    s = np.exp(0.3 * np.random.default_rng(91).standard_normal(256)).astype(np.float32)
+    for ratio in (None, np.float32(0.7)):
+        clip = None if ratio is None else np.full((3, 256 // group), ratio, np.float32)
+        q, d, z = oracle.quantize_zp(W, s, bits, group, clip=clip)
+        for n in range(3):
+            for g in range(256 // group):
+                sl = slice(g * group, (g + 1) * group)
+                c, dd, zz = ex.quantize_group_exact_zp(W[n, sl], s[sl], bits, ratio=ratio)
+                assert list(q[n, sl]) == c and d[n, g] == dd and z[n, g] == zz, (n, g, ratio)
+    assert z[1, 0] == 0
+    sx = oracle.act_stats(X)
+    res = oracle.search_layer(W, X, sx, bits=bits, group=group, n_grid=4, zero_point=True)
+    for i in range(4):
+        q, d, z = oracle.quantize_zp(W, res["scales"][i], bits, group)
+        centred = q.astype(np.int64) - np.repeat(z.astype(np.int64), group, axis=1)
+        le = ex.loss_exact(X, W, centred, d, res["scales"][i], group)
+        assert res["losses"][i] == pytest.approx(float(le), rel=1e-12)
+
+
+def test_p15_zero_point_pack_and_w4a16():
+    """Unsigned nibbles round-trip; W4A16 with zero points against exact rationals."""
+    g = np.random.default_rng(92)
+    q = g.integers(0, 16, size=(3, 256)).astype(np.uint8)
+    assert np.array_equal(oracle.unpack_uint4(oracle.pack_int4(q)), q)
+    z = g.integers(0, 16, size=(3, 2)).astype(np.uint8)
+    step = (0.01 * (1 + g.random((3, 2)))).astype(np.float16)
+    s16 = (1 + g.random(256)).astype(np.float16)
+    A = g.standard_normal((2, 256)).astype(np.float16)
+    Y = oracle.w4a16(A, oracle.pack_int4(q), step, s16, zeros=z)
+    for m in range(2):
+        for n in range(3):
+            want = sum(Fraction(float(A[m, k])) / Fraction(float(s16[k])) *
+                       (int(q[n, k]) - int(z[n, k // 128])) * Fraction(float(step[n, k // 128]))
+                       for k in range(256))
+            assert Y[m, n] == pytest.approx(float(want), rel=1e-12, abs=1e-14)
+
+
+# --- P16: group 64 -----------------------------------------------------------------------------
+@pytest.mark.parametrize("bits", [4, 3])
+def test_p16_group64_brute_force_exact(bits):
+    W, X = _small_layer(95 + bits, 3, 256, 4)
+    s = np.exp(0.3 * np.random.default_rng(96).standard_normal(256)).astype(np.float32)
+    qmin, qmax = oracle.code_range(bits)
+    q, d = oracle.quantize(W, s, bits, 64)
+    for n in range(3):
+        for g in range(4):
+            sl = slice(64 * g, 64 * (g + 1))
+            c, dd = ex.quantize_group_exact(W[n, sl], s[sl], qmin, qmax)
+            assert list(q[n, sl]) == c and d[n, g] == dd
+
+
+def test_p16_group64_equals_group128_when_both_halves_hold_the_maximum():
+    """If both 64-channel halves of every 128-channel group reach the group's max |w s|, the
+    steps coincide and group 64 gives the codes of group 128."""
+    g = np.random.default_rng(97)
+    W = (0.02 * g.standard_normal((5, 512))).astype(np.float32)
+    s = np.ones(512, np.float32)
+    for r in range(5):
+        for g0 in range(0, 512, 128):
+            m = np.abs(W[r, g0:g0 + 128]).max()
+            W[r, g0] = m
+            W[r, g0 + 64] = -m
+    q64, d64 = oracle.quantize(W, s, 4, 64)
+    q128, d128 = oracle.quantize(W, s, 4, 128)
+    assert np.array_equal(q64, q128)
+    assert np.array_equal(d64, np.repeat(d128, 2, axis=1))
