@@ -55,8 +55,9 @@ typedef enum {
   AWQ_ERR_NULL = 1,       /* a required pointer is NULL                                   */
   AWQ_ERR_SHAPE = 2,      /* M, N or K out of range, K % group != 0, ldx < K, misalignment */
   AWQ_ERR_DTYPE = 3,      /* dtype not accepted by this call                               */
-  AWQ_ERR_CONFIG = 4,     /* bits not in {3,4}, group != 128, n_grid not in [2,64],        */
-                          /* s_floor not a positive finite number, unknown form            */
+  AWQ_ERR_CONFIG = 4,     /* bits not in {3,4}, group not 64 or 128, n_grid not in [2,64], */
+                          /* s_floor not a positive finite number, unknown form,           */
+                          /* zero_point not 0 or 1                                         */
   AWQ_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than the *_workspace_bytes query    */
   AWQ_ERR_HIP = 6         /* a kernel launch reported an error                             */
 } awq_status;
@@ -91,13 +92,19 @@ enum { AWQ_FORM_DIRECT = 0, AWQ_FORM_GRAM = 1 };
 
 typedef struct {
   int32_t bits;    /* 4 (codes [-8,7]) or 3 (codes [-4,3]); the step is max|w s|/(2^(bits-1)-1) */
-  int32_t group;   /* input channels per step; 128 is the only accepted value                  */
+  int32_t group;   /* input channels per step: 128 or 64 (K a multiple of it and at least 128)  */
   int32_t n_grid;  /* number of alpha points, alpha_i = i/(n_grid-1), 2 <= n_grid <= 64         */
   float s_floor;   /* s = max(s_X, s_floor)^alpha, typically 1e-5f                              */
   int32_t form;    /* AWQ_FORM_DIRECT or AWQ_FORM_GRAM                                          */
   int32_t n_clip;  /* clipping search: ratios r_j = fp32(1 - (1 - clip_min) j / (n_clip - 1)),   */
   float clip_min;  /* j = 0 .. n_clip-1 in fp64; 2 <= n_clip <= 64, 0 < clip_min < 1 (read by    */
                    /* awq_clip_search only; typically 11 and 0.5)                                 */
+  int32_t zero_point; /* 0: symmetric codes as above. 1: zero-point (asymmetric) codes: per     */
+                   /* (row, group) Delta = fp32(fp32(max - min) / (2^bits - 1)), z =            */
+                   /* clamp(rint(fp32(-min / Delta)), 0, 2^bits - 1), unsigned codes             */
+                   /* clamp(rint(fp32(w s / Delta)) + z, 0, 2^bits - 1), Q(w s) = (q - z) Delta  */
+                   /* ("AWQ 量化方案..." 三 Step 4 names a scale and a zero point per group; the   */
+                   /* worked example of "量化方案详解", section AWQ, uses this 16-level range)     */
 } awq_cfg;
 
 /* Human-readable name of a status code (static storage). */
@@ -130,7 +137,8 @@ awq_status awq_act_stats(const void* X, awq_dtype xdt, int64_t M, int64_t K, int
  * W      [N, K] row-major, dtype wdt (AWQ_F16 or AWQ_F32), 16-byte aligned; N >= 1.
  * X      [M, K] row-major (row stride K), dtype xdt (AWQ_F16, AWQ_BF16 or AWQ_F32).
  * sx     fp32 [K], typically the output of awq_act_stats on the same X.
- * cfg    host pointer, see awq_cfg. K must be a multiple of cfg->group and at most 2^22.
+ * cfg    host pointer, see awq_cfg. K must be a multiple of cfg->group, at least 128 and at
+ *        most 2^22. With cfg->zero_point the codes below are the zero-point codes of awq_cfg.
  * For each i: s_i[k] = fp32(pow_f64(max(sx[k], s_floor), i/(n_grid-1))),
  *   codes q = clamp(rint(fp32(fp32(w s_i) / Delta)), -2^(b-1), 2^(b-1)-1) with
  *   Delta = fp32(max_group |fp32(w s_i)| / (2^(b-1)-1)) per (row, group of 128), all in IEEE
@@ -207,23 +215,24 @@ awq_status awq_search_layer_profiled(const void* W, awq_dtype wdt, int64_t N, in
 /* ------------------------------------------------------------------------------------------
  * awq_clip_search -- clipping of the scaled-up weights, one of the further optimisations listed
  * in [notes] 方法 (the page gives no details; the reading below is this library's).
- * For every output row n and group g of 128 input channels, each ratio r_j of the grid in
+ * For every output row n and group g of input channels, each ratio r_j of the grid in
  * awq_cfg is tried: the group of W s is clipped to [-c, c], c = fp32(r_j max|w s|), quantized
  * exactly as in awq_search_layer (so that Delta = c / (2^(b-1)-1)), and scored by the output
  * error the group causes on its own,
  *   err_j[n, g] = sum_m ( sum_{k in g} X[m,k] E[n,k] )^2,  E = Q(W s)/s - W,
- * evaluated as E_g H_gg E_g^T with the 128 x 128 diagonal blocks of H = X^T X (fp16 correlation
+ * evaluated as E_g H_gg E_g^T with the group's diagonal block of H = X^T X (fp16 correlation
  * operand and error rows, fp32 accumulation, as in the Gram form of awq_search_layer).
  * clip[n, g] = r of the smallest error (the lowest j on ties).
  * W        [N, K], dtype wdt (AWQ_F16 or AWQ_F32); X [M, K] (row stride K), dtype xdt;
  * s        fp32 [K], the scale to clip at (typically s_best of awq_search_layer).
- * cfg      bits, group (128), n_clip, clip_min (the other fields are not read).
- * clip     out, fp32 [N, K/128]: the chosen ratios (pass them to awq_pack_int4).
- * clip_err out, fp32 [n_clip, N, K/128] or NULL: err_j[n, g] for every ratio.
+ * cfg      bits, group, zero_point, n_clip, clip_min (the other fields are not read).
+ * clip     out, fp32 [N, K/group]: the chosen ratios (pass them to awq_pack_int4).
+ * clip_err out, fp32 [n_clip, N, K/group] or NULL: err_j[n, g] for every ratio.
  * flags    in/out: NONFINITE_W, X_F16_RANGE, STEP_UNDERFLOW.
  * ws       device workspace of at least awq_clip_workspace_bytes(M, N, K, xdt, cfg) bytes
  *          (the transposed fp16 X dominates: K * M * 2 bytes).
- * Limits: K a multiple of 128 and at most 2^22, M <= 2^23 - 128.
+ * Limits: K a multiple of cfg->group, at least 128 and at most 2^22, M <= 2^23 - 128. Groups of
+ *         128 or 64 channels, symmetric or zero-point codes (cfg->zero_point).
  * Errors: AWQ_ERR_NULL, AWQ_ERR_SHAPE, AWQ_ERR_DTYPE, AWQ_ERR_CONFIG (also n_clip, clip_min),
  *         AWQ_ERR_WORKSPACE.
  * ---------------------------------------------------------------------------------------- */
@@ -242,33 +251,38 @@ awq_status awq_clip_search(const void* W, awq_dtype wdt, int64_t N, int64_t K, c
  *          for none: the group of W s is clipped to +-fp32(r max|w s|) before quantization.
  *          A ratio outside (0, 1] sets AWQ_FLAG_CLIP_RANGE and that group is packed unclipped.
  * qweight  out, uint32 [N, K/8]: qweight[n,j] = sum_t (q[n,8j+t] & 0xF) << 4t, the codes of
- *          the same quantization as awq_search_layer / awq_clip_search (bit-identical).
+ *          the same quantization as awq_search_layer / awq_clip_search (bit-identical);
+ *          unsigned 0 .. 2^bits-1 with cfg->zero_point.
  * scales16 out, fp16 bits [N, K/group]: fp16(Delta), round to nearest even.
+ * zeros    out, uint8 [N, K/group]: z, required with cfg->zero_point and NULL without.
  * s16      out, fp16 bits [K]: fp16(s).
  * codes    out, int8 [N, K] or NULL (not written).
  * flags    in/out: NONFINITE_W, SCALE16_OVERFLOW, SCALE16_SUBNORMAL, STEP_UNDERFLOW, CLIP_RANGE.
- * Errors: AWQ_ERR_NULL, AWQ_ERR_SHAPE, AWQ_ERR_DTYPE, AWQ_ERR_CONFIG.
+ * Errors: AWQ_ERR_NULL (also zeros missing with cfg->zero_point), AWQ_ERR_SHAPE, AWQ_ERR_DTYPE,
+ *         AWQ_ERR_CONFIG (also zeros given without cfg->zero_point).
  * ---------------------------------------------------------------------------------------- */
 awq_status awq_pack_int4(const void* W, awq_dtype wdt, int64_t N, int64_t K, const float* s,
                          const float* clip, const awq_cfg* cfg, uint32_t* qweight,
-                         uint16_t* scales16, uint16_t* s16, int8_t* codes, uint32_t* flags,
-                         hipStream_t stream);
+                         uint16_t* scales16, uint8_t* zeros, uint16_t* s16, int8_t* codes,
+                         uint32_t* flags, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * w4a16_gemm -- QuantLinear.forward of [eng] 三 on the packed artefacts:
- *   Y[m,n] = sum_k (A[m,k] / s16[k]) * sext4(q[n,k]) * scales16[n, k/group]
+ *   Y[m,n] = sum_k (A[m,k] / s16[k]) * c(q[n,k]) * scales16[n, k/group]
+ * with c(q) = sext4(q) for symmetric codes, or q - zeros[n, k/group] for zero-point codes.
  * A        fp16 bits [M, K]; qweight uint32 [N, K/8]; scales16 fp16 bits [N, K/group];
+ *          zeros uint8 [N, K/group] for zero-point codes, or NULL for symmetric ones;
  *          s16 fp16 bits [K], or NULL when s^-1 has been folded into the producer of A (then
- *          Y = A (q * step)^T); Y out, fp16 bits [M, N]. group must be 128; K % 128 == 0,
+ *          Y = A (c(q) * step)^T); Y out, fp16 bits [M, N]. group 128 or 64; K % 128 == 0,
  *          K <= 12288.
- * Products are formed on fp16 operands (fp16(1/s) and fp16(code * fp16(1/s)), each rounded
+ * Products are formed on fp16 operands (fp16(1/s) and fp16(c(q) * fp16(1/s)), each rounded
  * once) with fp32 accumulation; the per-group step multiplies the fp32 partial of each group;
  * Y is rounded once to fp16 (relative Frobenius error ~5e-4).
  * Errors: AWQ_ERR_NULL, AWQ_ERR_SHAPE (M < 1, N < 1, K % 128, K > 12288), AWQ_ERR_CONFIG.
  * ---------------------------------------------------------------------------------------- */
 awq_status w4a16_gemm(const uint16_t* A, int64_t M, int64_t N, int64_t K, int32_t group,
-                      const uint32_t* qweight, const uint16_t* scales16, const uint16_t* s16,
-                      uint16_t* Y, hipStream_t stream);
+                      const uint32_t* qweight, const uint16_t* scales16, const uint8_t* zeros,
+                      const uint16_t* s16, uint16_t* Y, hipStream_t stream);
 
 #ifdef __cplusplus
 }

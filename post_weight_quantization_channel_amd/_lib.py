@@ -35,7 +35,8 @@ FLAG_FOLD_RANGE = 1 << 9
 class AwqCfg(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("n_grid", ctypes.c_int32), ("s_floor", ctypes.c_float), ("form", ctypes.c_int32),
-                ("n_clip", ctypes.c_int32), ("clip_min", ctypes.c_float)]
+                ("n_clip", ctypes.c_int32), ("clip_min", ctypes.c_float),
+                ("zero_point", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -62,8 +63,8 @@ SIGNATURES = {
     "awq_clip_search": (_E, [_P, _E, _I64, _I64, _P, _E, _I64, _P, ctypes.POINTER(AwqCfg), _P,
                              _P, _P, _P, _SZ, _P]),
     "awq_pack_int4": (_E, [_P, _E, _I64, _I64, _P, _P, ctypes.POINTER(AwqCfg), _P, _P, _P, _P,
-                           _P, _P]),
-    "w4a16_gemm": (_E, [_P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P]),
+                           _P, _P, _P]),
+    "w4a16_gemm": (_E, [_P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P]),
 }
 
 _lib = None

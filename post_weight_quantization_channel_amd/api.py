@@ -22,7 +22,8 @@ class AwqConfig:
     """bits in {3, 4}; group = 128 input channels per step; n_grid alpha points i/(n_grid-1);
     s = max(s_X, s_floor)^alpha; form "direct" (contract X with every error matrix) or "gram"
     (form H = X^T X once, then contract each error matrix with H); the clipping search tries
-    n_clip ratios from 1 down to clip_min."""
+    n_clip ratios from 1 down to clip_min; zero_point selects unsigned codes with a zero point
+    per (row, group) instead of symmetric ones; group 128 or 64."""
     bits: int = 4
     group: int = 128
     n_grid: int = 20
@@ -30,13 +31,14 @@ class AwqConfig:
     form: str = "direct"
     n_clip: int = 11
     clip_min: float = 0.5
+    zero_point: bool = False
 
     def c(self) -> AwqCfg:
         forms = {"direct": _lib.AWQ_FORM_DIRECT, "gram": _lib.AWQ_FORM_GRAM}
         if self.form not in forms:
             raise ValueError(f"form must be one of {sorted(forms)}, got {self.form!r}")
         return AwqCfg(self.bits, self.group, self.n_grid, self.s_floor, forms[self.form],
-                      self.n_clip, self.clip_min)
+                      self.n_clip, self.clip_min, int(bool(self.zero_point)))
 
 
 def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
@@ -72,6 +74,7 @@ class PackResult:
     s16: torch.Tensor       # fp16 [K]
     codes: torch.Tensor | None
     flags: torch.Tensor
+    zeros: torch.Tensor | None = None   # uint8 [N, K/group] for zero-point codes
 
 
 def act_stats_workspace_bytes(M: int, K: int) -> int:
@@ -254,18 +257,21 @@ def pack_int4(W: torch.Tensor, s: torch.Tensor, cfg: AwqConfig = AwqConfig(),
     scales16 = torch.empty((N, K // cfg.group), dtype=torch.float16, device=W.device)
     s16 = torch.empty(K, dtype=torch.float16, device=W.device)
     codes = torch.empty((N, K), dtype=torch.int8, device=W.device) if with_codes else None
+    zeros = torch.empty((N, K // cfg.group), dtype=torch.uint8, device=W.device) \
+        if cfg.zero_point else None
     check("awq_pack_int4", lib.awq_pack_int4(
         W.data_ptr(), _DT[W.dtype], N, K, s.data_ptr(),
         clip.data_ptr() if clip is not None else None, c, qweight.data_ptr(),
-        scales16.data_ptr(), s16.data_ptr(), codes.data_ptr() if codes is not None else None,
-        flags.data_ptr(), _stream(W)))
-    return PackResult(qweight, scales16, s16, codes, flags)
+        scales16.data_ptr(), zeros.data_ptr() if zeros is not None else None, s16.data_ptr(),
+        codes.data_ptr() if codes is not None else None, flags.data_ptr(), _stream(W)))
+    return PackResult(qweight, scales16, s16, codes, flags, zeros)
 
 
 def w4a16_gemm(A: torch.Tensor, qweight: torch.Tensor, scales16: torch.Tensor,
-               s16: torch.Tensor | None, group: int = 128, out: torch.Tensor | None = None
-               ) -> torch.Tensor:
-    """Y = (A / s) (q * step)^T, fp16 [M, N]; s16 = None when s^-1 is folded into A's producer."""
+               s16: torch.Tensor | None, group: int = 128, out: torch.Tensor | None = None,
+               zeros: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = (A / s) (c(q) * step)^T, fp16 [M, N], c(q) = q (symmetric) or q - z (zeros given);
+    s16 = None when s^-1 is folded into A's producer."""
     lib = _lib.load()
     for t, nm in ((A, "A"), (qweight, "qweight"), (scales16, "scales16")):
         _dev(t, nm)
@@ -279,10 +285,15 @@ def w4a16_gemm(A: torch.Tensor, qweight: torch.Tensor, scales16: torch.Tensor,
     if qweight.shape != (N, K // 8) or scales16.shape != (N, K // group) or \
             (s16 is not None and s16.shape != (K,)):
         raise ValueError("packed artefact shapes do not match A")
+    if zeros is not None:
+        _dev(zeros, "zeros")
+        if zeros.shape != (N, K // group) or zeros.dtype != torch.uint8:
+            raise ValueError("zeros must be uint8 [N, K/group]")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=A.device)
     check("w4a16_gemm", lib.w4a16_gemm(A.data_ptr(), M, N, K, group, qweight.data_ptr(),
                                        scales16.data_ptr(),
+                                       zeros.data_ptr() if zeros is not None else None,
                                        s16.data_ptr() if s16 is not None else None, out.data_ptr(),
                                        _stream(A)))
     return out

@@ -18,7 +18,8 @@ bool valid_dtype(awq_dtype d) { return d == AWQ_F32 || d == AWQ_F16 || d == AWQ_
 awq_status check_cfg(const awq_cfg* cfg) {
   if (!cfg) return AWQ_ERR_NULL;
   if (cfg->bits != 3 && cfg->bits != 4) return AWQ_ERR_CONFIG;
-  if (cfg->group != 128) return AWQ_ERR_CONFIG;
+  if (cfg->group != 128 && cfg->group != 64) return AWQ_ERR_CONFIG;
+  if (cfg->zero_point != 0 && cfg->zero_point != 1) return AWQ_ERR_CONFIG;
   if (cfg->n_grid < 2 || cfg->n_grid > 64) return AWQ_ERR_CONFIG;
   if (!(cfg->s_floor > 0.0f) || !isfinite(cfg->s_floor)) return AWQ_ERR_CONFIG;
   if (cfg->form != AWQ_FORM_DIRECT && cfg->form != AWQ_FORM_GRAM) return AWQ_ERR_CONFIG;
@@ -105,7 +106,7 @@ const char* awq_status_string(awq_status status) {
   return "unknown awq_status";
 }
 
-int32_t awq_version(void) { return 10300; }
+int32_t awq_version(void) { return 10400; }
 
 size_t awq_act_stats_workspace_bytes(int64_t M, int64_t K) {
   if (M < 1 || K < 1 || M > kMaxDim || K > kMaxDim) return 0;
@@ -128,8 +129,9 @@ awq_status awq_act_stats(const void* X, awq_dtype xdt, int64_t M, int64_t K, int
 namespace {
 
 // Shape rules of awq_search_layer beyond the per-dimension limits.
+// K >= 128 for every group size: the contractions take at least four 32-channel K steps.
 bool search_shape_ok(int64_t M, int64_t N, int64_t K, const awq_cfg* cfg) {
-  if (M < 1 || N < 1 || K < cfg->group || K % cfg->group || M > kMaxDim || N > kMaxDim ||
+  if (M < 1 || N < 1 || K < 128 || K % cfg->group || M > kMaxDim || N > kMaxDim ||
       K > kMaxSearchK)
     return false;
   if (cfg->form == AWQ_FORM_GRAM) {
@@ -222,8 +224,9 @@ awq_status search_impl(const void* const* Ws, const int64_t* Ns, int n_w, awq_dt
   mark(5);
   int64_t row = 0;
   for (int l = 0; l < n_w && e == hipSuccess; ++l) {
-    e = awq::launch_quantize_stack(Ws[l], (int)wdt, Ns[l], K, S, cfg->n_grid, cfg->bits, dcol,
-                                   ctrl, E + row * K, N, flags, stream);
+    e = awq::launch_quantize_stack(Ws[l], (int)wdt, Ns[l], K, S, cfg->n_grid, cfg->bits,
+                                   cfg->group, cfg->zero_point != 0, dcol, ctrl, E + row * K, N,
+                                   flags, stream);
     row += Ns[l];
   }
   mark(6);
@@ -286,19 +289,21 @@ awq_status awq_search_layer_profiled(const void* W, awq_dtype wdt, int64_t N, in
 
 awq_status awq_pack_int4(const void* W, awq_dtype wdt, int64_t N, int64_t K, const float* s,
                          const float* clip, const awq_cfg* cfg, uint32_t* qweight,
-                         uint16_t* scales16, uint16_t* s16, int8_t* codes, uint32_t* flags,
-                         hipStream_t stream) {
+                         uint16_t* scales16, uint8_t* zeros, uint16_t* s16, int8_t* codes,
+                         uint32_t* flags, hipStream_t stream) {
   if (!W || !s || !cfg || !qweight || !scales16 || !s16 || !flags) return AWQ_ERR_NULL;
   const awq_status cs = check_cfg(cfg);
   if (cs != AWQ_OK) return cs;
+  if (cfg->zero_point && !zeros) return AWQ_ERR_NULL;
+  if (!cfg->zero_point && zeros) return AWQ_ERR_CONFIG;
   if (wdt != AWQ_F16 && wdt != AWQ_F32) return AWQ_ERR_DTYPE;
-  if (N < 1 || K < cfg->group || K % cfg->group || N > kMaxDim || K > kMaxDim ||
-      !aligned16(W) || !aligned16(s) || !aligned16(s16) ||
+  if (N < 1 || K < 128 || K % cfg->group || N > kMaxDim ||
+      K > kMaxDim || !aligned16(W) || !aligned16(s) || !aligned16(s16) ||
       (codes && (reinterpret_cast<uintptr_t>(codes) & 7u)))
     return AWQ_ERR_SHAPE;
   if (clip && (reinterpret_cast<uintptr_t>(clip) & 3u)) return AWQ_ERR_SHAPE;
-  return hip_status(awq::launch_pack(W, (int)wdt, N, K, s, clip, cfg->bits, qweight, scales16,
-                                     s16, codes, flags, stream));
+  return hip_status(awq::launch_pack(W, (int)wdt, N, K, s, clip, cfg->bits, cfg->group, qweight,
+                                     scales16, zeros, s16, codes, flags, stream));
 }
 
 namespace {
@@ -336,7 +341,7 @@ awq_status check_clip_cfg(const awq_cfg* cfg) {
 }
 
 bool clip_shape_ok(int64_t M, int64_t N, int64_t K, const awq_cfg* cfg) {
-  if (M < 1 || N < 1 || K < cfg->group || K % cfg->group || M > kMaxDim || N > kMaxDim ||
+  if (M < 1 || N < 1 || K < 128 || K % cfg->group || M > kMaxDim || N > kMaxDim ||
       K > kMaxSearchK)
     return false;
   const int64_t Mp = (M + awq::kGramMAlign - 1) / awq::kGramMAlign * awq::kGramMAlign;
@@ -375,7 +380,8 @@ awq_status awq_clip_search(const void* W, awq_dtype wdt, int64_t N, int64_t K, c
                                           stream, nullptr);
   if (e == hipSuccess)
     e = awq::launch_clip_search(W, (int)wdt, N, K, s, d32, Bd, cfg->n_clip, cfg->clip_min,
-                                cfg->bits, clip, clip_err, flags, stream);
+                                cfg->bits, cfg->group, cfg->zero_point != 0, clip, clip_err,
+                                flags, stream);
   return hip_status(e);
 }
 
@@ -392,14 +398,15 @@ awq_status awq_fold_scale(void* prev, awq_dtype dtype, int64_t rows, int64_t col
 }
 
 awq_status w4a16_gemm(const uint16_t* A, int64_t M, int64_t N, int64_t K, int32_t group,
-                      const uint32_t* qweight, const uint16_t* scales16, const uint16_t* s16,
-                      uint16_t* Y, hipStream_t stream) {
+                      const uint32_t* qweight, const uint16_t* scales16, const uint8_t* zeros,
+                      const uint16_t* s16, uint16_t* Y, hipStream_t stream) {
   if (!A || !qweight || !scales16 || !Y) return AWQ_ERR_NULL;   // s16 NULL: s folded away
-  if (group != 128) return AWQ_ERR_CONFIG;
+  if (group != 128 && group != 64) return AWQ_ERR_CONFIG;
   if (M < 1 || N < 1 || K < 128 || K % 128 || M > kMaxDim || N > kMaxDim || K > kMaxW4A16K ||
       !aligned16(A) || !aligned16(qweight) || (s16 && !aligned16(s16)))
     return AWQ_ERR_SHAPE;
-  return hip_status(awq::launch_w4a16(A, M, N, K, qweight, scales16, s16, Y, stream));
+  return hip_status(awq::launch_w4a16(A, M, N, K, group, qweight, scales16, zeros, s16, Y,
+                                      stream));
 }
 
 }  // extern "C"

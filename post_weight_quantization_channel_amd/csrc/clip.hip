@@ -12,13 +12,15 @@
 // operand B_gg (strict lower correlations, 1/2 diagonal) is the diagonal block of the
 // block-diagonal correlation operand.
 //
-// gfx950 layout: a workgroup of 4 waves takes 64 rows of one group. Lane (i = lane % 16,
-// q = lane / 16) of a wave owns row 16 w + i and the channels 32 kb + 8 q + t (kb, t < 4, 8) of
-// the group: exactly the A operand of v_mfma_f32_16x16x32_f16 for the four 32-channel K blocks,
-// so the quantized E' goes from registers straight into the MFMA. B_gg sits in LDS and its 20
-// lower-triangular 32 x 16 fragments in registers; P for 16 rows costs 20 MFMAs. The epilogue
-// needs E' in the accumulator layout (lane holds rows 4 q .. 4 q + 3 of column 16 cb + i), which
-// it reads back from a per-wave LDS tile.
+// gfx950 layout: a workgroup of 4 waves takes 64 rows of one group of GS channels (128 or 64).
+// Lane (i = lane % 16, q = lane / 16) of a wave owns row 16 w + i and the channels 32 kb + 8 q + t
+// (kb < GS / 32, t < 8) of the group: exactly the A operand of v_mfma_f32_16x16x32_f16 for the
+// group's 32-channel K blocks, so the quantized E' goes from registers straight into the MFMA.
+// B_gg sits in LDS and its lower-triangular 32 x 16 fragments in registers (20 for 128 channels,
+// 6 for 64); P for 16 rows costs that many MFMAs. The epilogue needs E' in the accumulator layout
+// (lane holds rows 4 q .. 4 q + 3 of column 16 cb + i), which it reads back from a per-wave LDS
+// tile. With zero points (ZP) the clipped range is [max(min, -c), min(max, c)] of the unclipped
+// group extremes, so the ratios need no further cross-lane reductions.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -27,40 +29,46 @@ namespace awq {
 namespace {
 constexpr int kClipWaves = 4;
 constexpr int kClipRows = 16 * kClipWaves;   // rows per workgroup
-constexpr int kPitch = 136;                  // LDS row pitch in halves (272 bytes: no conflicts)
 
-// Offset of the fragments of column block cb in the register array: blocks kb <= cb / 2.
-__device__ __forceinline__ constexpr int frag_base(int cb) {
-  return (cb == 0) ? 0 : (cb == 1) ? 1 : (cb == 2) ? 2 : (cb == 3) ? 4 : (cb == 4) ? 6
-       : (cb == 5) ? 9 : (cb == 6) ? 12 : 16;
+// Offset of the fragments of column block cb in the register array: column block c holds the
+// K blocks kb <= c / 2, so the offset is sum_{c < cb} (c / 2 + 1) (and frag_base(CB) the count).
+__host__ __device__ constexpr int frag_base(int cb) {
+  return (cb % 2 == 0) ? (cb / 2) * (cb / 2 + 1) : (cb / 2 + 1) * (cb / 2 + 1);
 }
+static_assert(frag_base(8) == 20 && frag_base(4) == 6 && frag_base(7) == 16, "fragment count");
 
 __device__ __forceinline__ float clip_ratio(int j, int n_clip, float clip_min) {
   return (float)(1.0 - (1.0 - (double)clip_min) * j / (n_clip - 1));
 }
 }  // namespace
 
-template <int DT>
+template <int DT, int GS, bool ZP>
 __global__ __launch_bounds__(256) void clip_search_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s,
     const float* __restrict__ d32, const uint16_t* __restrict__ Bd, int n_clip, float clip_min,
     float qmin, float qmax, float* __restrict__ clip, float* __restrict__ clip_err,
     uint32_t* __restrict__ flags) {
   constexpr int ES = (DT == kF32) ? 4 : 2;
-  __shared__ __attribute__((aligned(16))) uint16_t Bg[128 * kPitch];
+  constexpr int KB = GS / 32;               // 32-channel K blocks per group
+  constexpr int CB = GS / 16;               // 16-channel column blocks per group
+  constexpr int NF = frag_base(CB);         // lower-triangular B fragments
+  constexpr int kPitch = GS + 8;            // LDS row pitch in halves (no bank conflicts)
+  constexpr int NV = 8 * KB;                // channels per lane
+  __shared__ __attribute__((aligned(16))) uint16_t Bg[GS * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t Et[kClipWaves][16 * kPitch];
-  const int64_t G = K / 128;
+  const int64_t G = K / GS;
   const int g = blockIdx.y;
   const int64_t n0 = (int64_t)blockIdx.x * kClipRows;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i = lane & 15, q = lane >> 4;
 
-  // B_gg: rows l, columns k of the group, from diagonal block a = g / 2 at offset 128 (g % 2)
+  // B_gg: rows l, columns k of the group, from the diagonal 256 x 256 block holding it
   {
-    const int o = (g & 1) * 128;
-    const uint16_t* src = Bd + (int64_t)(g >> 1) * (256 * 256) + (int64_t)o * 256 + o;
-    for (int idx = tid; idx < 128 * 16; idx += 256) {
-      const int l = idx >> 4, ch = idx & 15;
+    const int64_t c0 = (int64_t)g * GS;
+    const int o = (int)(c0 % 256);
+    const uint16_t* src = Bd + (c0 / 256) * (256 * 256) + (int64_t)o * 256 + o;
+    for (int idx = tid; idx < GS * (GS / 8); idx += 256) {
+      const int l = idx / (GS / 8), ch = idx % (GS / 8);
       *reinterpret_cast<uint4*>(&Bg[l * kPitch + ch * 8]) =
           *reinterpret_cast<const uint4*>(src + l * 256 + ch * 8);
     }
@@ -69,12 +77,12 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
   // this lane's row and channels
   const int64_t n = n0 + wave * 16 + i;
   const bool live = n < N;
-  const int64_t kb0 = (int64_t)g * 128 + 8 * q;
-  float ws[4][8], ca[4][8], cb_[4][8];   // w s;  E' = fma(q Delta, ca, -cb_)
-  float m = 0.0f, md = 0.0f;
+  const int64_t kb0 = (int64_t)g * GS + 8 * q;
+  float ws[KB][8], ca[KB][8], cb_[KB][8];   // w s;  E' = fma((q - z) Delta, ca, -cb_)
+  float m = 0.0f, md = 0.0f, mx = -INFINITY, nmn = -INFINITY;
   bool bad = false;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
+  for (int kb = 0; kb < KB; ++kb) {
     float w[8], sv[8], dv[8];
     if (live) {
       load8_f32<DT>(reinterpret_cast<const char*>(W) + (n * K + kb0 + 32 * kb) * ES, w);
@@ -89,20 +97,29 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
       bad |= !isfinite(w[t]);
       ws[kb][t] = w[t] * sv[t];
       m = fmaxf(m, fabsf(ws[kb][t]));
+      mx = fmaxf(mx, ws[kb][t]);
+      nmn = fmaxf(nmn, -ws[kb][t]);
       md = fmaxf(md, fabsf(w[t]) * dv[t]);
       ca[kb][t] = dv[t] * __builtin_amdgcn_rcpf(sv[t]);
       cb_[kb][t] = w[t] * dv[t];
     }
   }
-  // the four lanes q = 0..3 of row i hold its 128 channels
+  // the four lanes q = 0..3 of row i hold its channels
   m = fmaxf(m, __shfl_xor(m, 16));
   m = fmaxf(m, __shfl_xor(m, 32));
   md = fmaxf(md, __shfl_xor(md, 16));
   md = fmaxf(md, __shfl_xor(md, 32));
+  if (ZP) {
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    nmn = fmaxf(nmn, __shfl_xor(nmn, 16));
+    nmn = fmaxf(nmn, __shfl_xor(nmn, 32));
+  }
+  const float mn = -nmn;
   const int e = escale_for_max(md);   // |E| <= |w|, so |E'| < 2^15
   const float esc = ldexpf(1.0f, e);
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       ca[kb][t] *= esc;
@@ -110,9 +127,9 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
     }
   __syncthreads();
 
-  half8_t bf[20];
+  half8_t bf[NF];
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb)
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int kb = 0; kb <= cb / 2; ++kb)
       bf[frag_base(cb) + kb] =
@@ -129,17 +146,29 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
 
   for (int j = 0; j < n_clip; ++j) {
     const float c = clip_ratio(j, n_clip, clip_min) * m;
-    const QuantStep st = quant_step(c, qmax);
-    uf_any |= (c > 0.0f) && !(st.delta > 0.0f);
-    float v[32], qv[32];
+    float v[NV], qv[NV];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int t = 0; t < 8; ++t) v[8 * kb + t] = fminf(fmaxf(ws[kb][t], -c), c);
-    quant_codes(v, st, qmin, qmax, qv);
-    half8_t af[4];
+    QuantStep st;
+    float z = 0.0f;
+    if (ZP) {
+      const float range = fminf(mx, c) - fmaxf(mn, -c);
+      st = quant_step(range, qmax);
+      uf_any |= (range > 0.0f) && !(st.delta > 0.0f);
+      if (st.delta > 0.0f) z = fminf(fmaxf(rintf(-fmaxf(mn, -c) / st.delta), 0.0f), qmax);
+      quant_codes(v, st, -INFINITY, INFINITY, qv);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+      for (int t = 0; t < NV; ++t) qv[t] = fminf(fmaxf(qv[t] + z, 0.0f), qmax) - z;
+    } else {
+      st = quant_step(c, qmax);
+      uf_any |= (c > 0.0f) && !(st.delta > 0.0f);
+      quant_codes(v, st, qmin, qmax, qv);
+    }
+    half8_t af[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
       uint32_t wd[4];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -154,9 +183,9 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
       *reinterpret_cast<uint4*>(&et[i * kPitch + 32 * kb + 8 * q]) =
           make_uint4(wd[0], wd[1], wd[2], wd[3]);
     }
-    floatx4 acc[8];
+    floatx4 acc[CB];
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
       acc[cb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb <= cb / 2; ++kb)
@@ -173,7 +202,7 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
     for (int rr = 0; rr < 4; ++rr) {
       part[rr] = 0.0f;
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb)
+      for (int cb = 0; cb < CB; ++cb)
         part[rr] = __builtin_fmaf(h2f(et[(4 * q + rr) * kPitch + 16 * cb + i]), acc[cb][rr],
                                   part[rr]);
     }
@@ -199,17 +228,29 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
 
 hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, const float* s,
                               const float* d32, const uint16_t* Bd, int n_clip, float clip_min,
-                              int bits, float* clip, float* clip_err, uint32_t* flags,
-                              hipStream_t stream) {
-  const float qmax = (float)((1 << (bits - 1)) - 1);
-  const float qmin = -(float)(1 << (bits - 1));
-  dim3 grid((unsigned)((N + kClipRows - 1) / kClipRows), (unsigned)(K / 128));
-  if (dtype == kF32)
-    clip_search_kernel<kF32><<<grid, 256, 0, stream>>>(W, N, K, s, d32, Bd, n_clip, clip_min,
-                                                        qmin, qmax, clip, clip_err, flags);
-  else
-    clip_search_kernel<kF16><<<grid, 256, 0, stream>>>(W, N, K, s, d32, Bd, n_clip, clip_min,
-                                                        qmin, qmax, clip, clip_err, flags);
+                              int bits, int group, bool zero_point, float* clip, float* clip_err,
+                              uint32_t* flags, hipStream_t stream) {
+  const float qmax = zero_point ? (float)((1 << bits) - 1) : (float)((1 << (bits - 1)) - 1);
+  const float qmin = zero_point ? 0.0f : -(float)(1 << (bits - 1));
+  dim3 grid((unsigned)((N + kClipRows - 1) / kClipRows), (unsigned)(K / group));
+#define AWQ_CLIP(DT_, GS_, ZP_)                                                                  \
+  clip_search_kernel<DT_, GS_, ZP_><<<grid, 256, 0, stream>>>(W, N, K, s, d32, Bd, n_clip,        \
+                                                              clip_min, qmin, qmax, clip,        \
+                                                              clip_err, flags)
+  if (dtype == kF32) {
+    if (group == 64) {
+      if (zero_point) AWQ_CLIP(kF32, 64, true); else AWQ_CLIP(kF32, 64, false);
+    } else {
+      if (zero_point) AWQ_CLIP(kF32, 128, true); else AWQ_CLIP(kF32, 128, false);
+    }
+  } else {
+    if (group == 64) {
+      if (zero_point) AWQ_CLIP(kF16, 64, true); else AWQ_CLIP(kF16, 64, false);
+    } else {
+      if (zero_point) AWQ_CLIP(kF16, 128, true); else AWQ_CLIP(kF16, 128, false);
+    }
+  }
+#undef AWQ_CLIP
   return hipGetLastError();
 }
 

@@ -98,6 +98,17 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
+// Maximum over the GL lanes (16: a DPP row; 8: half a row) that hold one quantization group of
+// 8 GL channels; every lane of the group gets the result.
+template <int GL>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp_f32<AWQ_DPP_QUAD_1032>(v));
+  v = fmaxf(v, dpp_f32<AWQ_DPP_QUAD_2301>(v));
+  v = fmaxf(v, dpp_f32<AWQ_DPP_ROW_HALF_MIRROR>(v));
+  if (GL == 16) v = fmaxf(v, dpp_f32<AWQ_DPP_ROW_MIRROR>(v));
+  return v;
+}
+
 // Sum over the 16 lanes of a DPP row, as a butterfly (adjacent pairs, pairs of pairs, the two
 // quads of each half, the two halves): addition is commutative, so every lane of the row ends
 // with the bit-identical sum.
@@ -208,6 +219,64 @@ __device__ __forceinline__ float quant8(const float (&ws)[8], float qmin, float 
   for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(ws[t]));
   m = row16_max(m);
   return quant8_core(ws, m, qmin, qmax, q, underflow);
+}
+
+// The quantizer of the search and of the packing, for a group of 8 GL channels held as 8
+// values by each of GL consecutive lanes, optionally clipped (ratio r in (0, 1]: ws[] first moved
+// into [-c, c], c = fp32(r m), m the group's max |ws|) and optionally with a zero point:
+//   symmetric:  Delta = fp32(m' / qmax), q = clamp(rint(fp32(ws / Delta)), qmin, qmax)
+//   zero point: Delta = fp32(fp32(max - min) / qmax_u), z = clamp(rint(fp32(-min / Delta)), 0,
+//               qmax_u), q = clamp(rint(fp32(ws / Delta)) + z, 0, qmax_u)
+// (qmax_u = 2^b - 1 is passed as qmax and 0 as qmin for the zero-point form). Returns Delta and
+// sets z (0 for the symmetric form). Quotients as in quant8_core: |ws / Delta| <= 2^b - 1, so the
+// fast product quotient is within 3e-6 of the specified one and the near-half-integer test
+// decides when to divide exactly.
+template <int GL, bool ZP, bool CLIP>
+__device__ __forceinline__ float quant8_g(float (&ws)[8], float ratio, float qmin, float qmax,
+                                          float (&q)[8], float& z, bool& underflow) {
+  if (CLIP) {
+    float m = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(ws[t]));
+    m = group_max<GL>(m);
+    const float c = ratio * m;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ws[t] = fminf(fmaxf(ws[t], -c), c);
+  }
+  if (!ZP) {
+    float m = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(ws[t]));
+    m = group_max<GL>(m);
+    z = 0.0f;
+    return quant8_core(ws, m, qmin, qmax, q, underflow);
+  }
+  float mx = ws[0], nmn = -ws[0];
+#pragma unroll
+  for (int t = 1; t < 8; ++t) {
+    mx = fmaxf(mx, ws[t]);
+    nmn = fmaxf(nmn, -ws[t]);
+  }
+  mx = group_max<GL>(mx);
+  const float mn = -group_max<GL>(nmn);
+  const float range = mx - mn;
+  const QuantStep st = quant_step(range, qmax);
+  underflow = (range > 0.0f) && !(st.delta > 0.0f);
+  if (!(st.delta > 0.0f)) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) q[t] = 0.0f;
+    z = 0.0f;
+    return 0.0f;
+  }
+  z = fminf(fmaxf(rintf(-mn / st.delta), 0.0f), qmax);   // once per group: IEEE division
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const float tq = ws[t] * st.rcp;
+    float qq = rintf(tq);
+    if (st.exact_only || fabsf(tq - qq) > 0.5f - 0x1p-17f) qq = rintf(ws[t] / st.delta);
+    q[t] = fminf(fmaxf(qq + z, 0.0f), qmax);
+  }
+  return st.delta;
 }
 
 // Clipped quantization (the clipping search's ratio r in (0, 1]): ws[] is first moved into

@@ -56,9 +56,9 @@ hipError_t launch_x_to_f16(const void* X, int dtype, int64_t count, uint16_t* X1
 // to rows 0..N-1 of Estack whose grid-point slices are ld_rows rows apart (ld_rows >= N: several
 // weights fill one stack)
 hipError_t launch_quantize_stack(const void* W, int dtype, int64_t N, int64_t K, const float* S,
-                                 int n_grid, int bits, const float* dcol, const SearchCtrl* ctrl,
-                                 uint16_t* Estack, int64_t ld_rows, uint32_t* flags,
-                                 hipStream_t stream);
+                                 int n_grid, int bits, int group, bool zero_point,
+                                 const float* dcol, const SearchCtrl* ctrl, uint16_t* Estack,
+                                 int64_t ld_rows, uint32_t* flags, hipStream_t stream);
 hipError_t launch_lossgemm(const uint16_t* X16, int64_t M, int64_t K, const uint16_t* Estack,
                            int64_t N, int n_grid, double* partials, hipStream_t stream);
 hipError_t launch_finalize(const double* partials, int64_t tiles_per_alpha, int n_grid,
@@ -67,10 +67,12 @@ hipError_t launch_finalize(const double* partials, int64_t tiles_per_alpha, int 
                            float* s_best, uint32_t* flags, hipStream_t stream);
 
 // ---- pack ----
-// clip: ratios [N, K/128] in (0, 1] or nullptr
+// clip: ratios [N, K/group] in (0, 1] or nullptr; zeros: [N, K/group] (zero-point form) or
+// nullptr (symmetric)
 hipError_t launch_pack(const void* W, int dtype, int64_t N, int64_t K, const float* s,
-                       const float* clip, int bits, uint32_t* qweight, uint16_t* scales16,
-                       uint16_t* s16, int8_t* codes, uint32_t* flags, hipStream_t stream);
+                       const float* clip, int bits, int group, uint32_t* qweight,
+                       uint16_t* scales16, uint8_t* zeros, uint16_t* s16, int8_t* codes,
+                       uint32_t* flags, hipStream_t stream);
 
 // ---- folding s^-1 into the previous operator (fold.hip) ----
 hipError_t launch_fold(void* prev, int dtype, int64_t rows, int64_t cols, int64_t ld,
@@ -82,12 +84,13 @@ hipError_t launch_fold(void* prev, int dtype, int64_t rows, int64_t cols, int64_
 // of the correlation operand (Bd) and d = sqrt(diag H).
 hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, const float* s,
                               const float* d32, const uint16_t* Bd, int n_clip, float clip_min,
-                              int bits, float* clip, float* clip_err, uint32_t* flags,
-                              hipStream_t stream);
+                              int bits, int group, bool zero_point, float* clip, float* clip_err,
+                              uint32_t* flags, hipStream_t stream);
 
 // ---- W4A16 ----
-hipError_t launch_w4a16(const uint16_t* A, int64_t M, int64_t N, int64_t K,
-                        const uint32_t* qweight, const uint16_t* scales16, const uint16_t* s16,
-                        uint16_t* Y, hipStream_t stream);
+// group 128 or 64; zeros [N, K/group] (zero-point codes) or nullptr; s16 nullptr: s folded
+hipError_t launch_w4a16(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
+                        const uint32_t* qweight, const uint16_t* scales16, const uint8_t* zeros,
+                        const uint16_t* s16, uint16_t* Y, hipStream_t stream);
 
 }  // namespace awq

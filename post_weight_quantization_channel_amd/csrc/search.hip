@@ -8,7 +8,8 @@
 //                    fp32 bit patterns: order-free);
 //   x_to_f16         fp16 copy of an fp32/bf16 X for the fp16 contraction;
 //   quantize_stack   for all alpha at once: Q(W s_i) group-wise (the fp32 specification of
-//                    device_common.h) and the error E_i = Q(W s_i)/s_i - W, stored in fp16 as
+//                    device_common.h; symmetric or zero-point, groups of 128 or 64) and the error
+//                    E_i = Q(W s_i)/s_i - W, stored in fp16 as
 //                    E_i * 2^escale (Gram form: E_i[n,k] d_k 2^escale). By linearity
 //                    X E_i^T = Q(W s_i)(s_i^-1 X) - W X.
 //   finalize         fixed-order fp64 sum of the per-tile partial losses, L_i / (M N),
@@ -163,10 +164,12 @@ __device__ __forceinline__ int escale_from_absmax(uint32_t bits) {
 constexpr int kQuantRows = 4;  // rows per thread in quantize_stack
 
 // Thread layout: one thread owns 8 consecutive input channels (one 16-byte fp16 load) of
-// kQuantRows rows; 16 consecutive lanes cover one 128-channel group (a DPP row), so the group
-// maximum is four DPP steps. The scale row s_i for the thread's 8 channels is loaded once per
-// alpha and reused for all its rows. Stores: 16 bytes per lane, 1 KiB per wave, contiguous.
-template <int DT, bool COL>
+// kQuantRows rows; GL = group / 8 consecutive lanes cover one group (16 lanes, a DPP row, for
+// 128 channels; 8 for 64), so the group maximum (and minimum) is four (three) DPP steps. The
+// scale row s_i for the thread's 8 channels is loaded once per alpha and reused for all its rows.
+// Stores: 16 bytes per lane, 1 KiB per wave, contiguous. ZP: zero-point codes, E = (q - z) Delta
+// / s - w.
+template <int DT, bool COL, int GL, bool ZP>
 __global__ __launch_bounds__(256) void quantize_stack_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ S, int n_grid,
     float qmin, float qmax, const float* __restrict__ dcol, const SearchCtrl* __restrict__ ctrl,
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
   const int64_t rb = id / chunks;
   const int64_t c8 = id % chunks;
   const int64_t row0 = rb * kQuantRows;
-  if (row0 >= N) return;  // whole 16-lane groups share rb: no partial group exits here
+  if (row0 >= N) return;  // whole GL-lane groups share rb: no partial group exits here
   const int e = escale_from_absmax(ctrl->absmax_bits);
   const float esc = ldexpf(1.0f, e);
   float cs[8];   // per-column factor: 2^escale, times dcol[k] in the Gram form
@@ -210,17 +213,21 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
     for (int t = 0; t < 8; ++t) inv[t] = __builtin_amdgcn_rcpf(s[t]);
 #pragma unroll
     for (int r = 0; r < kQuantRows; ++r) {
-      if (!live[r]) continue;  // uniform over the 16-lane group
-      float ws[8], q[8];
+      if (!live[r]) continue;  // uniform over the GL-lane group
+      float ws[8], q[8], z;
 #pragma unroll
       for (int t = 0; t < 8; ++t) ws[t] = w[r][t] * s[t];
       bool uf;
-      const float delta = quant8(ws, qmin, qmax, q, uf);
+      const float delta = quant8_g<GL, ZP, false>(ws, 1.0f, qmin, qmax, q, z, uf);
+      if (ZP) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) q[t] -= z;   // exact: small integers
+      }
       uint32_t packed[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        // E = (q Delta)/s - w, then scaled (by the exact power of two, or by d_k 2^escale) and
-        // rounded once to fp16
+        // E = (q Delta)/s - w (q already centred by z), then scaled (by the exact power of two,
+        // or by d_k 2^escale) and rounded once to fp16
         const float e0 = (__builtin_fmaf(q[2 * t] * delta, inv[2 * t], -w[r][2 * t])) * cs[2 * t];
         const float e1 =
             (__builtin_fmaf(q[2 * t + 1] * delta, inv[2 * t + 1], -w[r][2 * t + 1])) * cs[2 * t + 1];
@@ -232,24 +239,45 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
   }
 }
 
-hipError_t launch_quantize_stack(const void* W, int dtype, int64_t N, int64_t K, const float* S,
-                                 int n_grid, int bits, const float* dcol, const SearchCtrl* ctrl,
-                                 uint16_t* Estack, int64_t ld_rows, uint32_t* flags,
-                                 hipStream_t stream) {
-  const float qmax = (float)((1 << (bits - 1)) - 1);
-  const float qmin = -(float)(1 << (bits - 1));
-  const int64_t threads = ((N + kQuantRows - 1) / kQuantRows) * (K / 8);
-  const unsigned blocks = (unsigned)((threads + 255) / 256);
-#define AWQ_QS(DT_, COL_)                                                                       \
-  quantize_stack_kernel<DT_, COL_><<<blocks, 256, 0, stream>>>(W, N, K, S, n_grid, qmin, qmax,   \
-                                                               dcol, ctrl, Estack, ld_rows,   \
-                                                               flags)
-  if (dtype == kF32) {
-    if (dcol) AWQ_QS(kF32, true); else AWQ_QS(kF32, false);
+template <int DT, bool COL>
+static void qs_dispatch(int group, bool zp, unsigned blocks, hipStream_t stream, const void* W,
+                        int64_t N, int64_t K, const float* S, int n_grid, float qmin, float qmax,
+                        const float* dcol, const SearchCtrl* ctrl, uint16_t* Estack,
+                        int64_t ld_rows, uint32_t* flags) {
+#define AWQ_QS(GL_, ZP_)                                                                         \
+  quantize_stack_kernel<DT, COL, GL_, ZP_><<<blocks, 256, 0, stream>>>(                          \
+      W, N, K, S, n_grid, qmin, qmax, dcol, ctrl, Estack, ld_rows, flags)
+  if (group == 64) {
+    if (zp) AWQ_QS(8, true); else AWQ_QS(8, false);
   } else {
-    if (dcol) AWQ_QS(kF16, true); else AWQ_QS(kF16, false);
+    if (zp) AWQ_QS(16, true); else AWQ_QS(16, false);
   }
 #undef AWQ_QS
+}
+
+hipError_t launch_quantize_stack(const void* W, int dtype, int64_t N, int64_t K, const float* S,
+                                 int n_grid, int bits, int group, bool zero_point,
+                                 const float* dcol, const SearchCtrl* ctrl, uint16_t* Estack,
+                                 int64_t ld_rows, uint32_t* flags, hipStream_t stream) {
+  const float qmax = zero_point ? (float)((1 << bits) - 1) : (float)((1 << (bits - 1)) - 1);
+  const float qmin = zero_point ? 0.0f : -(float)(1 << (bits - 1));
+  const int64_t threads = ((N + kQuantRows - 1) / kQuantRows) * (K / 8);
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  if (dtype == kF32) {
+    if (dcol)
+      qs_dispatch<kF32, true>(group, zero_point, blocks, stream, W, N, K, S, n_grid, qmin, qmax,
+                              dcol, ctrl, Estack, ld_rows, flags);
+    else
+      qs_dispatch<kF32, false>(group, zero_point, blocks, stream, W, N, K, S, n_grid, qmin, qmax,
+                               dcol, ctrl, Estack, ld_rows, flags);
+  } else {
+    if (dcol)
+      qs_dispatch<kF16, true>(group, zero_point, blocks, stream, W, N, K, S, n_grid, qmin, qmax,
+                              dcol, ctrl, Estack, ld_rows, flags);
+    else
+      qs_dispatch<kF16, false>(group, zero_point, blocks, stream, W, N, K, S, n_grid, qmin, qmax,
+                               dcol, ctrl, Estack, ld_rows, flags);
+  }
   return hipGetLastError();
 }
 

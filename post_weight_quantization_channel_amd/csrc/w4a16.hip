@@ -62,23 +62,31 @@ __device__ __forceinline__ int perm8(int t) { return ((t & 3) << 1) | (t >> 2); 
 // issued first and the weight loads right after them, so both are in flight together (loads
 // complete in order: consuming the table waits only for the table loads); 8 waves split the
 // groups so each unpacks only K/1024 of them.
-template <int MB, bool ACT_LDS>
+// Bytes of the skinny kernel's LDS regions (the launcher sizes the dynamic LDS with the same).
+__host__ __device__ constexpr int64_t w4a16_red_bytes(int MB) { return (int64_t)kWaves * MB * 64 * 16; }
+
+template <int MB, bool ACT_LDS, int GS, bool ZP>
 __global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restrict__ A, int64_t M,
                                                          int64_t N, int64_t K,
                                                          const uint32_t* __restrict__ qweight,
                                                          const uint16_t* __restrict__ scales16,
+                                                         const uint8_t* __restrict__ zeros,
                                                          const uint16_t* __restrict__ s16_in,
                                                          uint16_t* __restrict__ Y, int64_t m0) {
   extern __shared__ __attribute__((aligned(16))) char dyn[];
   const uint16_t* __restrict__ s16 = s16_in ? s16_in : kOnes16.v;
-  // LDS: [K] fp16 1/s (permuted) or [mrows][K] fp16 A / s (permuted; ACT_LDS), then the 16
-  // rows' fp32 group steps [groups][16], then the cross-wave reduction buffer.
+  // LDS: [K] fp16 1/s (permuted) or [mrows][K] fp16 A / s (permuted; ACT_LDS) -- the same
+  // region holds the cross-wave reduction buffer after the main loop -- then the 16 rows' fp32
+  // steps [K / GS][16], then (ZP) their zero points as fp16 (1024 + z) [K / GS][16].
   const int64_t mrows = ACT_LDS ? (M - m0 < 16 ? M - m0 : 16) : 0;
   const int64_t table_bytes = ACT_LDS ? mrows * K * 2 : K * 2;
+  const int64_t region0 = table_bytes > w4a16_red_bytes(MB) ? table_bytes : w4a16_red_bytes(MB);
+  const int64_t ngr = K / GS;                                   // quantization groups
   uint16_t* table = reinterpret_cast<uint16_t*>(dyn);
-  float* step_lds = reinterpret_cast<float*>(dyn + table_bytes);
-  floatx4* red = reinterpret_cast<floatx4*>(dyn + table_bytes + (K / 128) * kRows * 4);
-  uint4* trash = reinterpret_cast<uint4*>(red + kWaves * MB * 64);   // 16 bytes
+  floatx4* red = reinterpret_cast<floatx4*>(dyn);
+  float* step_lds = reinterpret_cast<float*>(dyn + region0);
+  uint16_t* zero_lds = reinterpret_cast<uint16_t*>(dyn + region0 + ngr * kRows * 4);
+  uint4* trash = reinterpret_cast<uint4*>(dyn + region0 + ngr * kRows * (ZP ? 6 : 4));  // 16 B
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -86,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restr
   const int li = lane & 15;   // weight row of the A operand / activation column of the B operand
   const int lg = lane >> 4;   // which 32-channel quarter of a 128-channel group
   const int64_t n0 = (int64_t)blockIdx.x * kRows;
-  const int64_t groups = K / 128;
+  const int64_t groups = K / 128;                               // 128-channel blocks
   const int64_t words_per_row = K / 8;
 
   // All prologue loads are unconditional (out-of-range indices are clamped and their values
@@ -105,13 +113,17 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restr
     ts[it] = *reinterpret_cast<const uint4*>(s16 + (int64_t)k8 * 8);
     if (ACT_LDS) ta[it] = *reinterpret_cast<const uint4*>(A + (m0 + ec / kc) * K + (int64_t)k8 * 8);
   }
-  uint16_t sraw[kTableIters];
+  constexpr int kStepIters = (kMaxK / GS * kRows + kThreads - 1) / kThreads;
+  const int ng = (int)ngr;
+  uint16_t sraw[kStepIters];
+  uint8_t zraw[kStepIters];
 #pragma unroll
-  for (int it = 0; it < kTableIters; ++it) {
+  for (int it = 0; it < kStepIters; ++it) {
     const int e = tid + it * kThreads;
-    const int ec = e < gr * kRows ? e : 0;
+    const int ec = e < ng * kRows ? e : 0;
     const int64_t row = (n0 + (ec & (kRows - 1)) < N) ? n0 + (ec & (kRows - 1)) : N - 1;
-    sraw[it] = scales16[row * groups + (ec >> 4)];
+    sraw[it] = scales16[row * ngr + (ec >> 4)];
+    if (ZP) zraw[it] = zeros[row * ngr + (ec >> 4)];
   }
 
   __builtin_amdgcn_sched_barrier(0);   // keep the issue order: tables, steps, then weights
@@ -156,9 +168,17 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restr
     for (int p = 0; p < 4; ++p) w[p] = (uint32_t)h[2 * p] | ((uint32_t)h[2 * p + 1] << 16);
     uint4* dst = (e < tchunks) ? reinterpret_cast<uint4*>(table + e * 8) : trash;
     *dst = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+#pragma unroll
+  for (int it = 0; it < kStepIters; ++it) {
+    const int e = tid + it * kThreads;
     const float stv = (n0 + (e & (kRows - 1)) < N) ? h2f(sraw[it]) : 0.0f;
-    float* sdst = (e < gr * kRows) ? step_lds + e : reinterpret_cast<float*>(trash);
+    float* sdst = (e < ng * kRows) ? step_lds + e : reinterpret_cast<float*>(trash);
     *sdst = stv;
+    if (ZP) {
+      uint16_t* zdst = (e < ng * kRows) ? zero_lds + e : reinterpret_cast<uint16_t*>(trash);
+      *zdst = f2h(1024.0f + (float)zraw[it]);   // exact: the subtrahend of the unpack
+    }
   }
   __syncthreads();
 
@@ -171,13 +191,21 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restr
     for (int u = 0; u < kChunk; ++u) {
       const int i = c * kChunk + u;
       if (i >= my_groups) break;                            // uniform over the wave
-      const int64_t g = wave + kWaves * i;
+      const int64_t g = wave + kWaves * i;                  // 128-channel block
       const int64_t kbase = g * 128 + lg * 32;              // this lane's 32 channels
       const uint32_t words[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
+      // fp16 subtrahend of the unpack: 1032 (signed codes, biased by the xor) or 1024 + z of
+      // this lane's row and group (the lane's 32 channels lie in one group for GS = 64 too)
+      half2_t sub2 = half2_t{(_Float16)1032.0f, (_Float16)1032.0f};
+      if (ZP) {
+        const int64_t gz = (GS == 64) ? 2 * g + (lg >> 1) : g;
+        const _Float16 zh = __builtin_bit_cast(_Float16, zero_lds[gz * kRows + li]);
+        sub2 = half2_t{zh, zh};
+      }
       half8_t wf[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {                          // word v: channels kbase + 8v ..
-        const uint32_t x = words[v] ^ 0x88888888u;
+        const uint32_t x = ZP ? words[v] : (words[v] ^ 0x88888888u);
         uint32_t invw[4] = {0u, 0u, 0u, 0u};
         if (!ACT_LDS) {
           const uint4 inv = *reinterpret_cast<const uint4*>(table + kbase + 8 * v);
@@ -186,18 +214,23 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restr
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t bits = ((x >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-          half2_t q = __builtin_bit_cast(half2_t, bits) - half2_t{(_Float16)1032.0f, (_Float16)1032.0f};
+          half2_t q = __builtin_bit_cast(half2_t, bits) - sub2;
           if (!ACT_LDS) q = q * __builtin_bit_cast(half2_t, invw[j]);
           wf[v][2 * j] = q[0];
           wf[v][2 * j + 1] = q[1];
         }
       }
-      // per-group fp32 steps of this lane's 4 output rows (rows 4 lg + r)
-      const floatx4 st = *reinterpret_cast<const floatx4*>(step_lds + g * kRows + 4 * lg);
+      // per-group fp32 steps of this lane's 4 output rows (rows 4 lg + r); with GS = 64 the two
+      // halves of the block have their own steps, so each MFMA is done twice with the A operand
+      // of the other half's lanes (lg < 2 hold channels 0..63, lg >= 2 channels 64..127) zeroed
+      const int64_t gs0 = (GS == 64) ? 2 * g : g;
+      const floatx4 st0 = *reinterpret_cast<const floatx4*>(step_lds + gs0 * kRows + 4 * lg);
+      floatx4 st1 = st0;
+      if (GS == 64) st1 = *reinterpret_cast<const floatx4*>(step_lds + (gs0 + 1) * kRows + 4 * lg);
 #pragma unroll
       for (int b = 0; b < MB; ++b) {
         const int64_t m = m0 + b * 16 + li;
-        floatx4 part = {0.f, 0.f, 0.f, 0.f};
+        floatx4 part = {0.f, 0.f, 0.f, 0.f}, part1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           half8_t af;
@@ -215,10 +248,20 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restr
           } else {
             af = half8_t{};
           }
-          part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[v], af, part, 0, 0, 0);
+          if (GS == 64) {
+            const half8_t w0 = (lg < 2) ? wf[v] : half8_t{};
+            const half8_t w1 = (lg < 2) ? half8_t{} : wf[v];
+            part = __builtin_amdgcn_mfma_f32_16x16x32_f16(w0, af, part, 0, 0, 0);
+            part1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(w1, af, part1, 0, 0, 0);
+          } else {
+            part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[v], af, part, 0, 0, 0);
+          }
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[b][r] = __builtin_fmaf(part[r], st[r], acc[b][r]);
+        for (int r = 0; r < 4; ++r) {
+          acc[b][r] = __builtin_fmaf(part[r], st0[r], acc[b][r]);
+          if (GS == 64) acc[b][r] = __builtin_fmaf(part1[r], st1[r], acc[b][r]);
+        }
       }
     }
   };
@@ -234,6 +277,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restr
     }
   }
 
+  __syncthreads();   // the reduction buffer reuses the table's LDS: every wave is done with it
 #pragma unroll
   for (int b = 0; b < MB; ++b) red[(wave * MB + b) * 64 + lane] = acc[b];
   __syncthreads();
@@ -285,10 +329,12 @@ __device__ __forceinline__ int tswz(int row, int chunk) {   // byte offset insid
 }
 }  // namespace
 
+template <int GS, bool ZP>
 __global__ __launch_bounds__(256) void w4a16_tiled_kernel(const uint16_t* __restrict__ A,
                                                           int64_t M, int64_t N, int64_t K,
                                                           const uint32_t* __restrict__ qweight,
                                                           const uint16_t* __restrict__ scales16,
+                                                          const uint8_t* __restrict__ zeros,
                                                           const uint16_t* __restrict__ s16_in,
                                                           uint16_t* __restrict__ Y) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kTileStage];
@@ -301,7 +347,8 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(const uint16_t* __rest
   const int64_t tilesN = (N + TBN - 1) / TBN;
   const int64_t m0 = (int64_t)(blockIdx.x / tilesN) * TBM;
   const int64_t n0 = (int64_t)(blockIdx.x % tilesN) * TBN;
-  const int64_t groups = K / 128;
+  const int64_t groups = K / 128;      // 128-channel K steps
+  const int64_t ngr = K / GS;          // quantization groups
 
   // activation tile: thread t loads rows (t / 16) + 16 j (j = 0..7), 16-byte chunk t % 16
   const int arow = tid >> 4, achunk = tid & 15;
@@ -327,6 +374,7 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(const uint16_t* __rest
     uint4 a[kARows];
     uint4 w;
     uint16_t step;
+    uint16_t zero;   // ZP: z of the thread's row and group
   };
   auto gload = [&](int64_t g, Regs& R) {
 #pragma unroll
@@ -336,7 +384,10 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(const uint16_t* __rest
                        : make_uint4(0, 0, 0, 0);
     }
     R.w = wok ? wsrc[g * 4] : make_uint4(0, 0, 0, 0);
-    R.step = wok ? scales16[wn_row * groups + g] : (uint16_t)0;
+    // the thread's 32 channels 128 g + 32 wq .. lie in one group for GS = 64 too
+    const int64_t gq = (GS == 64) ? 2 * g + (wq >> 1) : g;
+    R.step = wok ? scales16[wn_row * ngr + gq] : (uint16_t)0;
+    R.zero = (ZP && wok) ? (uint16_t)zeros[wn_row * ngr + gq] : (uint16_t)0;
   };
   auto lstore = [&](int stage, int64_t g, const Regs& R) {
     char* sa = smem + stage * kTileStage;
@@ -347,6 +398,8 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(const uint16_t* __rest
     // unpack 4 words = 32 channels k = 128 g + 32 wq + 8 v + t into q * (step * 1/s) in fp16
     const _Float16 sth = __builtin_bit_cast(_Float16, R.step);
     const half2_t st2 = half2_t{sth, sth};
+    const _Float16 subh = ZP ? (_Float16)(1024.0f + (float)R.zero) : (_Float16)1032.0f;
+    const half2_t sub2 = half2_t{subh, subh};
     const uint32_t words[4] = {R.w.x, R.w.y, R.w.z, R.w.w};
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -357,13 +410,12 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(const uint16_t* __rest
       const uint32_t i26 = __builtin_amdgcn_perm(iv.w, iv.y, 0x05040100u);
       const uint32_t i37 = __builtin_amdgcn_perm(iv.w, iv.y, 0x07060302u);
       const uint32_t invp[4] = {i04, i15, i26, i37};
-      const uint32_t x = words[v] ^ 0x88888888u;
+      const uint32_t x = ZP ? words[v] : (words[v] ^ 0x88888888u);
       uint32_t pr[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t bits = ((x >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-        const half2_t q = __builtin_bit_cast(half2_t, bits) -
-                          half2_t{(_Float16)1032.0f, (_Float16)1032.0f};
+        const half2_t q = __builtin_bit_cast(half2_t, bits) - sub2;
         const half2_t c = st2 * __builtin_bit_cast(half2_t, invp[j]);
         pr[j] = __builtin_bit_cast(uint32_t, q * c);              // channels (j, j + 4)
       }
@@ -444,38 +496,54 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(const uint16_t* __rest
     }
 }
 
-hipError_t launch_w4a16(const uint16_t* A, int64_t M, int64_t N, int64_t K,
-                        const uint32_t* qweight, const uint16_t* scales16, const uint16_t* s16,
-                        uint16_t* Y, hipStream_t stream) {
-  if (K > kMaxK) return hipErrorInvalidValue;
+template <int GS, bool ZP>
+static hipError_t w4a16_dispatch(const uint16_t* A, int64_t M, int64_t N, int64_t K,
+                                 const uint32_t* qweight, const uint16_t* scales16,
+                                 const uint8_t* zeros, const uint16_t* s16, uint16_t* Y,
+                                 hipStream_t stream) {
   const unsigned blocks = (unsigned)((N + kRows - 1) / kRows);
-  const size_t steps_bytes = (size_t)(K / 128) * kRows * 4;
+  const size_t tables = (size_t)(K / GS) * kRows * (ZP ? 6 : 4) + 16;   // steps, zeros, trash
   if (M > 64) {
     const int64_t tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
-    w4a16_tiled_kernel<<<(unsigned)tiles, 256, 0, stream>>>(A, M, N, K, qweight, scales16, s16, Y);
+    w4a16_tiled_kernel<GS, ZP><<<(unsigned)tiles, 256, 0, stream>>>(A, M, N, K, qweight, scales16,
+                                                                    zeros, s16, Y);
     return hipGetLastError();
   }
+  auto region0 = [&](size_t table, int MB) {
+    const size_t red = (size_t)w4a16_red_bytes(MB);
+    return table > red ? table : red;
+  };
   hipError_t e = hipSuccess;
   for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += 64) {
     const int64_t rest = M - m0;
     if (rest <= 16 && (size_t)rest * K * 2 <= kActLdsBytes) {
-      const size_t lds = (size_t)rest * K * 2 + steps_bytes + kWaves * 1 * 64 * 16 + 16;
-      w4a16_kernel<1, true><<<blocks, kThreads, lds, stream>>>(A, M, N, K, qweight, scales16, s16, Y, m0);
+      const size_t lds = region0((size_t)rest * K * 2, 1) + tables;
+      w4a16_kernel<1, true, GS, ZP><<<blocks, kThreads, lds, stream>>>(A, M, N, K, qweight,
+                                                                       scales16, zeros, s16, Y, m0);
+    } else if (rest <= 16) {
+      w4a16_kernel<1, false, GS, ZP><<<blocks, kThreads, region0((size_t)K * 2, 1) + tables,
+                                       stream>>>(A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
+    } else if (rest <= 32) {
+      w4a16_kernel<2, false, GS, ZP><<<blocks, kThreads, region0((size_t)K * 2, 2) + tables,
+                                       stream>>>(A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
     } else {
-      const size_t base = (size_t)K * 2 + steps_bytes;
-      if (rest <= 16)
-        w4a16_kernel<1, false><<<blocks, kThreads, base + kWaves * 1 * 64 * 16 + 16, stream>>>(
-            A, M, N, K, qweight, scales16, s16, Y, m0);
-      else if (rest <= 32)
-        w4a16_kernel<2, false><<<blocks, kThreads, base + kWaves * 2 * 64 * 16 + 16, stream>>>(
-            A, M, N, K, qweight, scales16, s16, Y, m0);
-      else
-        w4a16_kernel<4, false><<<blocks, kThreads, base + kWaves * 4 * 64 * 16 + 16, stream>>>(
-            A, M, N, K, qweight, scales16, s16, Y, m0);
+      w4a16_kernel<4, false, GS, ZP><<<blocks, kThreads, region0((size_t)K * 2, 4) + tables,
+                                       stream>>>(A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
     }
     e = hipGetLastError();
   }
   return e;
+}
+
+hipError_t launch_w4a16(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
+                        const uint32_t* qweight, const uint16_t* scales16, const uint8_t* zeros,
+                        const uint16_t* s16, uint16_t* Y, hipStream_t stream) {
+  if (K > kMaxK) return hipErrorInvalidValue;
+  if (group == 64)
+    return zeros ? w4a16_dispatch<64, true>(A, M, N, K, qweight, scales16, zeros, s16, Y, stream)
+                 : w4a16_dispatch<64, false>(A, M, N, K, qweight, scales16, zeros, s16, Y, stream);
+  return zeros ? w4a16_dispatch<128, true>(A, M, N, K, qweight, scales16, zeros, s16, Y, stream)
+               : w4a16_dispatch<128, false>(A, M, N, K, qweight, scales16, zeros, s16, Y, stream);
 }
 
 }  // namespace awq

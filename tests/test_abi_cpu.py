@@ -49,11 +49,12 @@ def test_status_strings(lib):
     for code in range(7):
         s = lib.awq_status_string(code).decode()
         assert s.startswith("AWQ_")
-    assert lib.awq_version() == 10300
+    assert lib.awq_version() == 10400
 
 
-def cfg(bits=4, group=128, n_grid=20, s_floor=1e-5, form=0, n_clip=11, clip_min=0.5):
-    return AwqCfg(bits, group, n_grid, s_floor, form, n_clip, clip_min)
+def cfg(bits=4, group=128, n_grid=20, s_floor=1e-5, form=0, n_clip=11, clip_min=0.5,
+        zero_point=0):
+    return AwqCfg(bits, group, n_grid, s_floor, form, n_clip, clip_min, zero_point)
 
 
 def test_workspace_queries(lib):
@@ -138,7 +139,8 @@ def test_search_rejects(lib):
         assert _search(lib, **{k: None}) == E.AWQ_ERR_NULL, k
     assert _search(lib, cfg=None) == E.AWQ_ERR_NULL
     assert _search(lib, cfg=cfg(bits=2)) == E.AWQ_ERR_CONFIG
-    assert _search(lib, cfg=cfg(group=64)) == E.AWQ_ERR_CONFIG
+    assert _search(lib, cfg=cfg(group=32)) == E.AWQ_ERR_CONFIG
+    assert _search(lib, cfg=cfg(zero_point=3)) == E.AWQ_ERR_CONFIG
     assert _search(lib, cfg=cfg(n_grid=1)) == E.AWQ_ERR_CONFIG
     assert _search(lib, cfg=cfg(n_grid=65)) == E.AWQ_ERR_CONFIG
     assert _search(lib, cfg=cfg(s_floor=0.0)) == E.AWQ_ERR_CONFIG
@@ -168,16 +170,34 @@ def test_pack_rejects(lib):
     c = cfg()
     f = lib.awq_pack_int4
 
-    def call(W=FAKE, wdt=1, N=4, K=128, s=FAKE, clip=None, cfg_=c, codes=None):
-        return f(W, wdt, N, K, s, clip, cfg_, FAKE, FAKE, FAKE, codes, FAKE, None)
+    def call(W=FAKE, wdt=1, N=4, K=128, s=FAKE, clip=None, cfg_=c, zeros=None, codes=None):
+        return f(W, wdt, N, K, s, clip, cfg_, FAKE, FAKE, zeros, FAKE, codes, FAKE, None)
     assert call(W=None) == E.AWQ_ERR_NULL
     assert call(cfg_=None) == E.AWQ_ERR_NULL
     assert call(cfg_=cfg(bits=8)) == E.AWQ_ERR_CONFIG
+    assert call(cfg_=cfg(group=32)) == E.AWQ_ERR_CONFIG
+    assert call(cfg_=cfg(zero_point=2)) == E.AWQ_ERR_CONFIG
+    assert call(cfg_=cfg(zero_point=1)) == E.AWQ_ERR_NULL       # zeros required
+    assert call(zeros=FAKE) == E.AWQ_ERR_CONFIG                 # zeros without zero points
     assert call(wdt=2) == E.AWQ_ERR_DTYPE
     assert call(K=130) == E.AWQ_ERR_SHAPE
+    assert call(K=192) == E.AWQ_ERR_SHAPE                        # not a multiple of 128
+    assert call(K=64, cfg_=cfg(group=64)) == E.AWQ_ERR_SHAPE     # K below 128
+    assert call(K=160, cfg_=cfg(group=64)) == E.AWQ_ERR_SHAPE
     assert call(N=0) == E.AWQ_ERR_SHAPE
     assert call(codes=FAKE + 3) == E.AWQ_ERR_SHAPE
     assert call(clip=FAKE + 2) == E.AWQ_ERR_SHAPE
+
+
+def test_group64_and_zero_point_configs_are_accepted(lib):
+    """Workspace queries accept group 64 (K a multiple of 64, at least 128) and zero points."""
+    for g, zp in ((64, 0), (64, 1), (128, 1)):
+        assert lib.awq_search_workspace_bytes(300, 256, 192 if g == 64 else 256, 1,
+                                              cfg(group=g, zero_point=zp)) > 0
+        assert lib.awq_clip_workspace_bytes(300, 256, 320 if g == 64 else 384, 1,
+                                            cfg(group=g, zero_point=zp)) > 0
+    assert lib.awq_search_workspace_bytes(300, 256, 64, 1, cfg(group=64)) == 0
+    assert lib.awq_search_workspace_bytes(300, 256, 192, 1, cfg(group=128)) == 0
 
 
 def _clip(lib, **kw):
@@ -261,12 +281,19 @@ def test_fold_scale_rejects(lib):
 def test_w4a16_rejects(lib):
     E = _lib
     f = lib.w4a16_gemm
-    assert f(None, 1, 16, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == E.AWQ_ERR_NULL
-    assert f(FAKE, 1, 16, 128, 64, FAKE, FAKE, FAKE, FAKE, None) == E.AWQ_ERR_CONFIG
-    assert f(FAKE, 0, 16, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == E.AWQ_ERR_SHAPE
-    assert f(FAKE, 1, 16, 200, 128, FAKE, FAKE, FAKE, FAKE, None) == E.AWQ_ERR_SHAPE
-    assert f(FAKE, 1, 0, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == E.AWQ_ERR_SHAPE
-    assert f(FAKE + 8, 1, 16, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == E.AWQ_ERR_SHAPE
+
+    def call(A=FAKE, M=1, N=16, K=128, group=128, qw=FAKE, sc=FAKE, zeros=None, s16=FAKE):
+        return f(A, M, N, K, group, qw, sc, zeros, s16, FAKE, None)
+    assert call(A=None) == E.AWQ_ERR_NULL
+    assert call(qw=None) == E.AWQ_ERR_NULL
+    assert call(group=32) == E.AWQ_ERR_CONFIG
+    assert call(M=0) == E.AWQ_ERR_SHAPE
+    assert call(K=200) == E.AWQ_ERR_SHAPE
+    assert call(K=192, group=64) == E.AWQ_ERR_SHAPE              # the kernels step 128 channels
+    assert call(K=12288 + 128) == E.AWQ_ERR_SHAPE
+    assert call(N=0) == E.AWQ_ERR_SHAPE
+    assert call(A=FAKE + 8) == E.AWQ_ERR_SHAPE
+    assert call(s16=FAKE + 8) == E.AWQ_ERR_SHAPE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

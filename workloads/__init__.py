@@ -147,6 +147,11 @@ def w4a16_random_artifacts(n: int, k: int, group: int = 128, config: int = 4, j:
     return qweight, steps, s
 
 
+def w4a16_random_zeros(n: int, k: int, group: int = 128, config: int = 4, j: int = 0):
+    """Zero points for zero-point artefacts: uint8 [n, k/group] uniform in 0..15 (t = 2)."""
+    return rng(config, 2, j).integers(0, 16, size=(n, k // group)).astype(np.uint8)
+
+
 def w4a16_activations(m: int, k: int, config: int = 4, j: int = 0) -> np.ndarray:
     """A = N(0,1) fp16 [m, k]."""
     return rng(config, 3, j).standard_normal((m, k)).astype(np.float16)
