@@ -16,6 +16,8 @@ fields it carries
   stages_ms     mean duration of every kernel of the search;
   other_form    the search in the other form (a few repetitions): ms and its loss kernel;
   clip_search   the clipping search at s* (11 ratios 1 .. 0.5) and the clipped pack: ms;
+  shared_qkv    one alpha for three 4096x4096 weights reading the same X, and the fold of s^-1
+                into the producing norm weight: ms;
   hbm_stages    the bandwidth-bound kernels: algorithmic bytes, GB/s, fraction of 8 TB/s;
   w4a16         the W4A16 kernel at the batch sizes 1, 4, 16, 64, 512 for 4096x4096 and
                 11008x4096, over rotated weight copies (> 256 MB, so HBM and not the
@@ -54,6 +56,8 @@ def parse():
                     help="repetitions of the search in the other form (0: skip)")
     ap.add_argument("--clip-reps", type=int, default=5,
                     help="repetitions of the clipping search at s* (0: skip)")
+    ap.add_argument("--shared-reps", type=int, default=3,
+                    help="repetitions of the shared q/k/v search and the fold (0: skip)")
     ap.add_argument("--mode", choices=("bench", "traffic"), default="bench",
                     help="traffic: one 1 GiB device copy (counter calibration) and one pass of "
                          "the path in each form, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
@@ -364,6 +368,39 @@ def main():
         log("clip search", clip_rec)
         del ws_c
 
+    # one s for three weights that read the same X (q/k/v of the attention block), and the fold
+    # of s^-1 into the norm weight that produces X
+    shared_rec = None
+    if args.shared_reps > 0:
+        del ws_search
+        torch.cuda.empty_cache()
+        Wk = torch.from_numpy(workloads.weight(2, N_, K_, j=1)).to(dev)
+        Wv = torch.from_numpy(workloads.weight(2, N_, K_, j=2)).to(dev)
+        scfg = awq.AwqConfig(bits=4, group=128, n_grid=N_GRID, form=args.form)
+        ws_search = torch.empty(awq.search_workspace_bytes(M_, 3 * N_, K_, torch.float16, scfg),
+                                dtype=torch.uint8, device=dev)
+        sx_s, _ = awq.act_stats(X, workspace=ws_stats)
+        gamma = torch.ones((1, K_), dtype=torch.float16, device=dev)
+        t_sh, t_fold = [], []
+        for r in range(args.shared_reps + 1):          # the first run is a warm-up
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record(st)
+            rs = awq.search_layers([W, Wk, Wv], X, sx_s, scfg, workspace=ws_search)
+            e1.record(st)
+            awq.fold_scale(gamma, rs.s_best, axis=1)
+            e2.record(st)
+            e2.synchronize()
+            if r:
+                t_sh.append(e0.elapsed_time(e1))
+                t_fold.append(e1.elapsed_time(e2))
+        shared_rec = {"weights": "q, k, v: 3 x 4096x4096 fp16 sharing X", "form": args.form,
+                      "search_ms": round(statistics.mean(t_sh), 3),
+                      "fold_ms": round(statistics.mean(t_fold), 4),
+                      "three_separate_searches_ms": round(3 * sum(stages.values()), 3),
+                      "alpha_star": int(rs.best.item())}
+        log("shared q/k/v search", shared_rec)
+        del Wk, Wv, rs
+
     other_form = None
     if args.other_form_reps > 0:
         oform = "direct" if args.form == "gram" else "gram"
@@ -419,6 +456,7 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "other_form": other_form,
         "clip_search": clip_rec,
+        "shared_qkv": shared_rec,
         "hbm_stages": other,
         "w4a16": w4,
         "alpha_star": best,

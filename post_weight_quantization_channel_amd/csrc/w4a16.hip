@@ -39,8 +39,11 @@ constexpr int kMaxK = 12288;    // LDS tables + reduction buffer stay below 64 K
 constexpr size_t kActLdsBytes = 32768;   // largest M * K * 2 staged as fp16(A / s) in LDS
 }  // namespace
 
-// s = 1 for every channel (fp16 1.0): used when s16 is NULL, i.e. when s^-1 has been folded
-// into the producer of A. A constant table, so the kernels' load code stays the same.
+// s = 1 for every channel (fp16 1.0): read instead of s16 when s^-1 has been folded into the
+// producer of A (the kernels' HAS_S = false instances). Selecting the pointer at compile time
+// keeps the HAS_S = true code unchanged: a run-time select measured ~10% slower on the
+// latency-bound decode path. (The table is only referenced from device code: as a namespace-scope
+// const object it has internal linkage, so the runtime cannot look up its address by name.)
 struct OnesTable {
   uint16_t v[kMaxK];
   constexpr OnesTable() : v() {
@@ -65,7 +68,7 @@ __device__ __forceinline__ int perm8(int t) { return ((t & 3) << 1) | (t >> 2); 
 // Bytes of the skinny kernel's LDS regions (the launcher sizes the dynamic LDS with the same).
 __host__ __device__ constexpr int64_t w4a16_red_bytes(int MB) { return (int64_t)kWaves * MB * 64 * 16; }
 
-template <int MB, bool ACT_LDS, int GS, bool ZP>
+template <int MB, bool ACT_LDS, int GS, bool ZP, bool HAS_S>
 __global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restrict__ A, int64_t M,
                                                          int64_t N, int64_t K,
                                                          const uint32_t* __restrict__ qweight,
@@ -74,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restr
                                                          const uint16_t* __restrict__ s16_in,
                                                          uint16_t* __restrict__ Y, int64_t m0) {
   extern __shared__ __attribute__((aligned(16))) char dyn[];
-  const uint16_t* __restrict__ s16 = s16_in ? s16_in : kOnes16.v;
+  const uint16_t* __restrict__ s16 = HAS_S ? s16_in : kOnes16.v;
   // LDS: [K] fp16 1/s (permuted) or [mrows][K] fp16 A / s (permuted; ACT_LDS) -- the same
   // region holds the cross-wave reduction buffer after the main loop -- then the 16 rows' fp32
   // steps [K / GS][16], then (ZP) their zero points as fp16 (1024 + z) [K / GS][16].
@@ -329,7 +332,7 @@ __device__ __forceinline__ int tswz(int row, int chunk) {   // byte offset insid
 }
 }  // namespace
 
-template <int GS, bool ZP>
+template <int GS, bool ZP, bool HAS_S>
 __global__ __launch_bounds__(256) void w4a16_tiled_kernel(const uint16_t* __restrict__ A,
                                                           int64_t M, int64_t N, int64_t K,
                                                           const uint32_t* __restrict__ qweight,
@@ -338,7 +341,7 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(const uint16_t* __rest
                                                           const uint16_t* __restrict__ s16_in,
                                                           uint16_t* __restrict__ Y) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kTileStage];
-  const uint16_t* __restrict__ s16 = s16_in ? s16_in : kOnes16.v;
+  const uint16_t* __restrict__ s16 = HAS_S ? s16_in : kOnes16.v;
   __shared__ __attribute__((aligned(16))) uint16_t inv_s[kMaxK];   // fp16(1/s), natural order
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -370,11 +373,13 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(const uint16_t* __rest
   }
   __syncthreads();
 
+  // step and zero are 32 bits wide: two 16-bit fields would share a register, and merging a
+  // load into half of it waits for the load at once, which undoes the two-step prefetch
   struct Regs {
     uint4 a[kARows];
     uint4 w;
-    uint16_t step;
-    uint16_t zero;   // ZP: z of the thread's row and group
+    uint32_t step;   // fp16 bits
+    uint32_t zero;   // ZP: z of the thread's row and group
   };
   auto gload = [&](int64_t g, Regs& R) {
 #pragma unroll
@@ -386,8 +391,8 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(const uint16_t* __rest
     R.w = wok ? wsrc[g * 4] : make_uint4(0, 0, 0, 0);
     // the thread's 32 channels 128 g + 32 wq .. lie in one group for GS = 64 too
     const int64_t gq = (GS == 64) ? 2 * g + (wq >> 1) : g;
-    R.step = wok ? scales16[wn_row * ngr + gq] : (uint16_t)0;
-    R.zero = (ZP && wok) ? (uint16_t)zeros[wn_row * ngr + gq] : (uint16_t)0;
+    R.step = wok ? (uint32_t)scales16[wn_row * ngr + gq] : 0u;
+    R.zero = (ZP && wok) ? (uint32_t)zeros[wn_row * ngr + gq] : 0u;
   };
   auto lstore = [&](int stage, int64_t g, const Regs& R) {
     char* sa = smem + stage * kTileStage;
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(const uint16_t* __rest
     for (int j = 0; j < kARows; ++j)
       *reinterpret_cast<uint4*>(sa + tswz(arow + 16 * j, achunk)) = R.a[j];
     // unpack 4 words = 32 channels k = 128 g + 32 wq + 8 v + t into q * (step * 1/s) in fp16
-    const _Float16 sth = __builtin_bit_cast(_Float16, R.step);
+    const _Float16 sth = __builtin_bit_cast(_Float16, (uint16_t)R.step);
     const half2_t st2 = half2_t{sth, sth};
     const _Float16 subh = ZP ? (_Float16)(1024.0f + (float)R.zero) : (_Float16)1032.0f;
     const half2_t sub2 = half2_t{subh, subh};
@@ -496,7 +501,7 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(const uint16_t* __rest
     }
 }
 
-template <int GS, bool ZP>
+template <int GS, bool ZP, bool HAS_S>
 static hipError_t w4a16_dispatch(const uint16_t* A, int64_t M, int64_t N, int64_t K,
                                  const uint32_t* qweight, const uint16_t* scales16,
                                  const uint8_t* zeros, const uint16_t* s16, uint16_t* Y,
@@ -505,7 +510,7 @@ static hipError_t w4a16_dispatch(const uint16_t* A, int64_t M, int64_t N, int64_
   const size_t tables = (size_t)(K / GS) * kRows * (ZP ? 6 : 4) + 16;   // steps, zeros, trash
   if (M > 64) {
     const int64_t tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
-    w4a16_tiled_kernel<GS, ZP><<<(unsigned)tiles, 256, 0, stream>>>(A, M, N, K, qweight, scales16,
+    w4a16_tiled_kernel<GS, ZP, HAS_S><<<(unsigned)tiles, 256, 0, stream>>>(A, M, N, K, qweight, scales16,
                                                                     zeros, s16, Y);
     return hipGetLastError();
   }
@@ -518,16 +523,16 @@ static hipError_t w4a16_dispatch(const uint16_t* A, int64_t M, int64_t N, int64_
     const int64_t rest = M - m0;
     if (rest <= 16 && (size_t)rest * K * 2 <= kActLdsBytes) {
       const size_t lds = region0((size_t)rest * K * 2, 1) + tables;
-      w4a16_kernel<1, true, GS, ZP><<<blocks, kThreads, lds, stream>>>(A, M, N, K, qweight,
+      w4a16_kernel<1, true, GS, ZP, HAS_S><<<blocks, kThreads, lds, stream>>>(A, M, N, K, qweight,
                                                                        scales16, zeros, s16, Y, m0);
     } else if (rest <= 16) {
-      w4a16_kernel<1, false, GS, ZP><<<blocks, kThreads, region0((size_t)K * 2, 1) + tables,
+      w4a16_kernel<1, false, GS, ZP, HAS_S><<<blocks, kThreads, region0((size_t)K * 2, 1) + tables,
                                        stream>>>(A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
     } else if (rest <= 32) {
-      w4a16_kernel<2, false, GS, ZP><<<blocks, kThreads, region0((size_t)K * 2, 2) + tables,
+      w4a16_kernel<2, false, GS, ZP, HAS_S><<<blocks, kThreads, region0((size_t)K * 2, 2) + tables,
                                        stream>>>(A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
     } else {
-      w4a16_kernel<4, false, GS, ZP><<<blocks, kThreads, region0((size_t)K * 2, 4) + tables,
+      w4a16_kernel<4, false, GS, ZP, HAS_S><<<blocks, kThreads, region0((size_t)K * 2, 4) + tables,
                                        stream>>>(A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
     }
     e = hipGetLastError();
@@ -535,15 +540,27 @@ static hipError_t w4a16_dispatch(const uint16_t* A, int64_t M, int64_t N, int64_
   return e;
 }
 
+template <int GS, bool ZP>
+static hipError_t w4a16_dispatch_s(const uint16_t* A, int64_t M, int64_t N, int64_t K,
+                                   const uint32_t* qweight, const uint16_t* scales16,
+                                   const uint8_t* zeros, const uint16_t* s16, uint16_t* Y,
+                                   hipStream_t stream) {
+  return s16 ? w4a16_dispatch<GS, ZP, true>(A, M, N, K, qweight, scales16, zeros, s16, Y, stream)
+             : w4a16_dispatch<GS, ZP, false>(A, M, N, K, qweight, scales16, zeros, s16, Y,
+                                             stream);
+}
+
 hipError_t launch_w4a16(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
                         const uint32_t* qweight, const uint16_t* scales16, const uint8_t* zeros,
                         const uint16_t* s16, uint16_t* Y, hipStream_t stream) {
   if (K > kMaxK) return hipErrorInvalidValue;
   if (group == 64)
-    return zeros ? w4a16_dispatch<64, true>(A, M, N, K, qweight, scales16, zeros, s16, Y, stream)
-                 : w4a16_dispatch<64, false>(A, M, N, K, qweight, scales16, zeros, s16, Y, stream);
-  return zeros ? w4a16_dispatch<128, true>(A, M, N, K, qweight, scales16, zeros, s16, Y, stream)
-               : w4a16_dispatch<128, false>(A, M, N, K, qweight, scales16, zeros, s16, Y, stream);
+    return zeros ? w4a16_dispatch_s<64, true>(A, M, N, K, qweight, scales16, zeros, s16, Y, stream)
+                 : w4a16_dispatch_s<64, false>(A, M, N, K, qweight, scales16, zeros, s16, Y,
+                                               stream);
+  return zeros ? w4a16_dispatch_s<128, true>(A, M, N, K, qweight, scales16, zeros, s16, Y, stream)
+               : w4a16_dispatch_s<128, false>(A, M, N, K, qweight, scales16, zeros, s16, Y,
+                                              stream);
 }
 
 }  // namespace awq
