@@ -339,7 +339,9 @@ __device__ __forceinline__ void buffer_load16_lds(rsrc_t r, uint32_t lds, uint32
 }
 
 // The same load with a wave-uniform byte offset `soff` added in the scalar offset field, so a
-// run of loads can share one per-lane offset register.
+// run of loads can share one per-lane offset register. The range check covers the whole offset
+// (voff + soff; measured on gfx950: bytes at or past the buffer's size read as zeros whether the
+// excess is in voff or in soff).
 __device__ __forceinline__ void buffer_load16_lds_so(rsrc_t r, uint32_t lds, uint32_t voff,
                                                      uint32_t soff) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);

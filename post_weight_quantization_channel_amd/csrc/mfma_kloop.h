@@ -49,19 +49,22 @@ constexpr int vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 // The K loop over four LDS stages (LDS addresses base + stage * kStageBytes, stage = kt % 4).
 //
 // Per step kt: the 16 MFMAs of the first half (k 0..15) with the reads of the second-half
-// fragments in between; wait until step kt+1 has landed (steps kt+2, kt+3 may still be in
-// flight) and this wave's LDS reads are done; barrier; the 16 MFMAs of the second half with the
-// refill of stage kt (step kt+4) and the reads of step kt+1's first-half fragments in between.
-// The instruction stream is laid out by hand (sched_barrier stops the scheduler from regrouping
-// it): each MFMA keeps the matrix core busy for 32 cycles while the following load or LDS read
-// issues.
+// fragments and the second half of the refill of stage kt-1 (step kt+3) in between; wait until
+// step kt+1 has landed (steps kt+2, kt+3 may still be in flight) and this wave's LDS reads are
+// done; barrier; the 16 MFMAs of the second half with the first half of the refill of stage kt
+// (step kt+4) and the reads of step kt+1's first-half fragments in between. The refill of a
+// stage is split over two half steps so that both halves issue twelve memory instructions, one
+// after each MFMA but every fourth. The instruction stream is laid out by hand (sched_barrier
+// stops the scheduler from regrouping it): each MFMA keeps the matrix core busy for 32 cycles
+// while the following load or LDS read issues.
 struct Tile {
   rsrc_t ra, rb;        // operand panels
-  uint32_t voff;        // this lane's byte offset for load slice 0, step 0
+  uint32_t voff;        // this lane's byte offset inside a 16-row load slice (per lane)
+  uint32_t soff;        // byte offset of this wave's first row (wave-uniform)
   uint32_t row_stride;  // bytes between rows
-  uint32_t lds0;        // LDS address of stage 0
+  uint32_t lds0;        // LDS address of stage 0 (wave-uniform)
   uint32_t rd[2][2];    // this lane's fragment read offsets in a stage: [operand][k half]
-  int wave;
+  int wave;             // wave-uniform
 };
 
 struct Frags {
@@ -73,14 +76,16 @@ struct Frags {
 __device__ __forceinline__ void tile_setup(Tile& T, const char* smem, uint32_t row_stride) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  T.wave = tid >> 6;
-  T.lds0 = lds_addr(smem);
+  // the wave index and the LDS base are uniform: in scalar registers, every load address of
+  // the loop below is scalar arithmetic plus the one per-lane offset
+  T.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  T.lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   // lane l of load slice j fills LDS row wave*64 + 16j + l/4, physical chunk l%4, i.e. the
   // logical chunk (l%4) ^ swz(row); swz depends on row % 16 = l/4 only.
   const int lrow = lane >> 2;
   T.row_stride = row_stride;
-  T.voff = (uint32_t)(T.wave * kRowsPerWave + lrow) * T.row_stride +
-           (uint32_t)(((lane & 3) ^ swz(lrow)) * 16);
+  T.voff = (uint32_t)lrow * row_stride + (uint32_t)(((lane & 3) ^ swz(lrow)) * 16);
+  T.soff = (uint32_t)(T.wave * kRowsPerWave) * row_stride;
   // fragment reads: lane l reads row (wave block) + 32 i + l%32 at chunk 2h + l/32; the
   // swizzle of a row does not change with the +32 i block offset, so one offset per (operand,
   // k half) serves all four row blocks.
@@ -110,12 +115,15 @@ __device__ __forceinline__ void kl_issue(const Tile& T, int st, int kt, int idx)
   const int j = idx >> 1;
   const uint32_t lds = T.lds0 + (uint32_t)(st * kStageBytes) + ((idx & 1) ? BM * kRowBytes : 0) +
                        (uint32_t)((T.wave * kRowsPerWave + kRowsPerInst * j) * kRowBytes);
-  const uint32_t o = T.voff + (uint32_t)(kRowsPerInst * j) * T.row_stride +
-                     (uint32_t)kt * (uint32_t)kRowBytes;
-  buffer_load16_lds((idx & 1) ? T.rb : T.ra, lds, o);
+  const uint32_t so = T.soff + (uint32_t)(kRowsPerInst * j) * T.row_stride +
+                      (uint32_t)kt * (uint32_t)kRowBytes;
+  buffer_load16_lds_so((idx & 1) ? T.rb : T.ra, lds, T.voff, so);
 }
 
-template <bool REFILL, bool MORE, int VM>
+// LO: issue loads 0..3 of step kt+4 (into stage kt); HI: issue loads 4..7 of step kt+3 (into
+// stage kt-1, free since the barrier of step kt-1); MORE: read step kt+1's first-half fragments;
+// VM: loads allowed in flight at the wait (those issued after the last load of step kt+1).
+template <bool LO, bool HI, bool MORE, int VM>
 __device__ __forceinline__ void kl_step(const char* smem, const Tile& T, int kt, Frags& F,
                                         floatx16 (&acc)[4][4]) {
   const int st = kt & 3;
@@ -124,6 +132,7 @@ __device__ __forceinline__ void kl_step(const char* smem, const Tile& T, int kt,
     acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[0][m >> 2], F.b[0][m & 3],
                                                                 acc[m >> 2][m & 3], 0, 0, 0);
     if ((m & 1) == 0) kl_read(smem, T, st, 1, m >> 1, F);
+    if (HI && (m & 3) == 1) kl_issue(T, (st + 3) & 3, kt + 3, 4 + (m >> 2));
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt(VM) & ~0x0F00);   // + lgkmcnt(0)
@@ -132,7 +141,7 @@ __device__ __forceinline__ void kl_step(const char* smem, const Tile& T, int kt,
   for (int m = 0; m < 16; ++m) {
     acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[1][m >> 2], F.b[1][m & 3],
                                                                 acc[m >> 2][m & 3], 0, 0, 0);
-    if (REFILL && (m & 1) == 0) kl_issue(T, st, kt + 4, m >> 1);
+    if (LO && (m & 3) == 0) kl_issue(T, st, kt + 4, m >> 2);
     if (MORE && (m & 1)) kl_read(smem, T, (st + 1) & 3, 0, m >> 1, F);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -144,20 +153,22 @@ __device__ __forceinline__ void kl_step(const char* smem, const Tile& T, int kt,
 __device__ __forceinline__ void kl_run(const char* smem, const Tile& T, int nk,
                                        floatx16 (&acc)[4][4]) {
   Frags F;
+  // steps 0..2 in full, loads 0..3 of step 3 (its loads 4..7 follow in step 0)
 #pragma unroll
   for (int p = 0; p < kStages; ++p)
 #pragma unroll
-    for (int idx = 0; idx < 2 * kInstPerOp; ++idx) kl_issue(T, p, p, idx);
-  __builtin_amdgcn_s_waitcnt(vmcnt(24));           // step 0 has landed
+    for (int idx = 0; idx < ((p < kStages - 1) ? 2 * kInstPerOp : kInstPerOp); ++idx)
+      kl_issue(T, p, p, idx);
+  __builtin_amdgcn_s_waitcnt(vmcnt(20));           // step 0 has landed
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 8; ++i) kl_read(smem, T, 0, 0, i, F);
-  // steps whose successors kt+1..kt+4 all exist, then the last four with constant flags
-  for (int kt = 0; kt < nk - 4; ++kt) kl_step<true, true, 16>(smem, T, kt, F, acc);
-  kl_step<false, true, 16>(smem, T, nk - 4, F, acc);
-  kl_step<false, true, 8>(smem, T, nk - 3, F, acc);
-  kl_step<false, true, 0>(smem, T, nk - 2, F, acc);
-  kl_step<false, false, 0>(smem, T, nk - 1, F, acc);
+  // at the wait of step kt, the loads of steps kt+2 and kt+3 (16) may be in flight
+  for (int kt = 0; kt < nk - 4; ++kt) kl_step<true, true, true, 16>(smem, T, kt, F, acc);
+  kl_step<false, true, true, 16>(smem, T, nk - 4, F, acc);
+  kl_step<false, false, true, 8>(smem, T, nk - 3, F, acc);
+  kl_step<false, false, true, 0>(smem, T, nk - 2, F, acc);
+  kl_step<false, false, false, 0>(smem, T, nk - 1, F, acc);
 }
 
 __device__ __forceinline__ void acc_zero(floatx16 (&acc)[4][4]) {
