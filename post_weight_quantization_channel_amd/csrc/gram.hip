@@ -150,6 +150,8 @@ __global__ __launch_bounds__(kloop::kThreads, 1) void gram_gemm_kernel(
   acc_zero(acc);
   kl_run(smem, T_, (int)(clen / BK), acc);
 
+  // the partials are read once, by the finish pass: non-temporal stores keep these 256 KiB per
+  // tile from displacing the X^T operand lines that the other workgroups are reading (-2%)
   const int lane = threadIdx.x & 63;
   float* out = Hpart + (c * T + tile) * (int64_t)(BM * BN);
 #pragma unroll
@@ -158,9 +160,10 @@ __global__ __launch_bounds__(kloop::kThreads, 1) void gram_gemm_kernel(
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4)
-        *reinterpret_cast<float4*>(out + frag_off(T_.wave, i, j, 4 * e4, lane)) =
-            make_float4(acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2],
-                        acc[i][j][4 * e4 + 3]);
+        __builtin_nontemporal_store(
+            floatx4{acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2],
+                    acc[i][j][4 * e4 + 3]},
+            reinterpret_cast<floatx4*>(out + frag_off(T_.wave, i, j, 4 * e4, lane)));
 }
 
 // ------------------------------------------------------------------------------------------
@@ -278,45 +281,62 @@ __global__ __launch_bounds__(kloop::kThreads, 1) void gram_loss_kernel(
   const int64_t brows = (K - (int64_t)lt * BN < BN) ? K - (int64_t)lt * BN : BN;
   T_.rb = make_rsrc(B + (int64_t)lt * BN * K, (uint32_t)(brows * K * 2));
   tile_setup(T_, smem, (uint32_t)(K * 2));
-  const int wm = T_.wave >> 1, wn = T_.wave & 1;
+  const int wn = T_.wave & 1;   // the wave's column half of the tile
   {
     const int nk = (8 * (lt + 1) < nk_all) ? 8 * (lt + 1) : nk_all;
     floatx16 acc[4][4];
     acc_zero(acc);
-    kl_run(smem, T_, nk, acc);
-
-    // E' tile [256 n][256 l] (128 KiB) into the LDS stages, which no wave reads any more: row n
-    // at byte 512 n. Rows past the panel read as zeros; columns past K (ragged last tile) pick
-    // up neighbouring values, which meet P = 0 there and are masked below anyway.
-    // wave w, load p: LDS bytes (32 w + p) KiB .. +1 KiB = tile rows 64 w + 2 p + lane / 32
-    {
-      const uint32_t rowb = (uint32_t)(K * 2);
-      const uint32_t voff = (uint32_t)(T_.wave * 64 + (lane >> 5)) * rowb + (uint32_t)(lane & 31) * 16u;
+    // The epilogue needs the E' tile [256 n][256 l]: operand A of steps 8 lt .. 8 lt + 7. A full
+    // tile (the last eight steps are exactly these) keeps them in LDS: steps 8 lt + 4 + s stay in
+    // the A half of stage s, and steps 8 lt + s are loaded again into the free B half of stage s
+    // during the last four steps. The ragged last tile (K % 256 != 0) loads all eight after the
+    // loop; its columns past K pick up neighbouring finite values (or zeros past the panel),
+    // which meet P = 0 there and are masked below anyway.
+    if (nk == 8 * (lt + 1)) {
+      kl_run_t<true>(smem, T_, nk, acc);
+    } else {
+      kl_run(smem, T_, nk, acc);
 #pragma unroll
-      for (int p = 0; p < 32; ++p)
-        buffer_load16_lds_so(T_.ra, T_.lds0 + (uint32_t)((T_.wave * 32 + p) * 1024), voff,
-                             (uint32_t)(2 * p) * rowb + (uint32_t)lt * 512u);
+      for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kl_issue_a_to_b(T_, s4, 8 * lt + s4, j);
+          kl_issue(T_, s4, 8 * lt + 4 + s4, 2 * j);
+        }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt(0));
     __syncthreads();
 
-    // epilogue: sum over the tile of E'_nl P_nl (P = acc)
-    double tot = 0.0;
-    const uint16_t* et = reinterpret_cast<const uint16_t*>(smem);
+    // epilogue: sum over the tile of E'_nl P_nl (P = acc). Columns l of block (wn, j) are those
+    // of step 8 lt + 4 wn + j. Two MFMAs against the identity put the E' block into the layout
+    // of the accumulators exactly (one product by 1 per element, fp16 -> fp32 is exact):
+    // D = A_0 I_0 + A_1 I_1 with I_h[k][c] = (c == 16 h + k) over the block's 32 columns.
+    const int l32 = lane & 31, lh = lane >> 5;
+    half8_t id0, id1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < 8; ++q) {
+      id0[q] = (_Float16)((l32 == 8 * lh + q) ? 1.0f : 0.0f);
+      id1[q] = (_Float16)((l32 == 16 + 8 * lh + q) ? 1.0f : 0.0f);
+    }
+    double tot = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int lcol = wn * 128 + 32 * j + (lane & 31);
+        const char* src = smem + j * kStageBytes + (wn ? 0 : BM * kRowBytes);
+        const half8_t f0 = *reinterpret_cast<const half8_t*>(src + T_.rd[0][0] + i * 32 * kRowBytes);
+        const half8_t f1 = *reinterpret_cast<const half8_t*>(src + T_.rd[0][1] + i * 32 * kRowBytes);
+        floatx16 ev = {};
+        ev = __builtin_amdgcn_mfma_f32_32x32x16_f16(f0, id0, ev, 0, 0, 0);
+        ev = __builtin_amdgcn_mfma_f32_32x32x16_f16(f1, id1, ev, 0, 0, 0);
+        const int lcol = wn * 128 + 32 * j + l32;
         const bool lok = (int64_t)lt * BN + lcol < K;
         float s = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {   // the LDS tile is read in full: no branches here
-          const int n = wm * 128 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          s = __builtin_fmaf(h2f(et[n * 256 + lcol]), acc[i][j][e], s);
-        }
+        for (int e = 0; e < 16; ++e) s = __builtin_fmaf(ev[e], acc[i][j][e], s);
         tot += lok ? (double)s : 0.0;
       }
+    }
     for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
     if (lane == 0) wsum[T_.wave] = tot;
     __syncthreads();

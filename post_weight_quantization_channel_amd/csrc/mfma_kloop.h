@@ -120,10 +120,22 @@ __device__ __forceinline__ void kl_issue(const Tile& T, int st, int kt, int idx)
   buffer_load16_lds_so((idx & 1) ? T.rb : T.ra, lds, T.voff, so);
 }
 
+// Load slice j in [0, 4) of operand A's rows of step `ksrc` into the B half of stage `st`, at
+// the rows and chunk positions the A half uses (so the A fragment offsets read it back).
+__device__ __forceinline__ void kl_issue_a_to_b(const Tile& T, int st, int ksrc, int j) {
+  const uint32_t lds = T.lds0 + (uint32_t)(st * kStageBytes) + BM * kRowBytes +
+                       (uint32_t)((T.wave * kRowsPerWave + kRowsPerInst * j) * kRowBytes);
+  const uint32_t so = T.soff + (uint32_t)(kRowsPerInst * j) * T.row_stride +
+                      (uint32_t)ksrc * (uint32_t)kRowBytes;
+  buffer_load16_lds_so(T.ra, lds, T.voff, so);
+}
+
 // LO: issue loads 0..3 of step kt+4 (into stage kt); HI: issue loads 4..7 of step kt+3 (into
 // stage kt-1, free since the barrier of step kt-1); MORE: read step kt+1's first-half fragments;
-// VM: loads allowed in flight at the wait (those issued after the last load of step kt+1).
-template <bool LO, bool HI, bool MORE, int VM>
+// VM: loads allowed in flight at the wait (those issued after the last load of step kt+1);
+// COPY: in the slots of LO, load operand A of step kt-4 into the B half of stage kt (free after
+// this step's barrier), for an epilogue that reads A of the last eight steps.
+template <bool LO, bool HI, bool MORE, int VM, bool COPY = false>
 __device__ __forceinline__ void kl_step(const char* smem, const Tile& T, int kt, Frags& F,
                                         floatx16 (&acc)[4][4]) {
   const int st = kt & 3;
@@ -142,16 +154,20 @@ __device__ __forceinline__ void kl_step(const char* smem, const Tile& T, int kt,
     acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[1][m >> 2], F.b[1][m & 3],
                                                                 acc[m >> 2][m & 3], 0, 0, 0);
     if (LO && (m & 3) == 0) kl_issue(T, st, kt + 4, m >> 2);
+    if (COPY && (m & 3) == 0) kl_issue_a_to_b(T, st, kt - 4, m >> 2);
     if (MORE && (m & 1)) kl_read(smem, T, (st + 1) & 3, 0, m >> 1, F);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// acc += A B^T over nk steps of BK (nk >= 4). The LDS stages must be free on entry (a barrier
-// after any previous use); on return every wave has passed the last step's barrier and the
-// stages are no longer read.
-__device__ __forceinline__ void kl_run(const char* smem, const Tile& T, int nk,
-                                       floatx16 (&acc)[4][4]) {
+// acc += A B^T over nk steps of BK (nk >= 4; nk >= 8 with COPY). The LDS stages must be free on
+// entry (a barrier after any previous use); on return every wave has passed the last step's
+// barrier and the stages are no longer read. With COPY, on return (once vmcnt(0) and a barrier
+// have followed) stage s holds operand A of step nk-8+s in its B half and of step nk-4+s in its
+// A half, s = 0..3 -- when nk is a multiple of 4 -- i.e. A of the last eight steps.
+template <bool COPY>
+__device__ __forceinline__ void kl_run_t(const char* smem, const Tile& T, int nk,
+                                         floatx16 (&acc)[4][4]) {
   Frags F;
   // steps 0..2 in full, loads 0..3 of step 3 (its loads 4..7 follow in step 0)
 #pragma unroll
@@ -165,10 +181,16 @@ __device__ __forceinline__ void kl_run(const char* smem, const Tile& T, int nk,
   for (int i = 0; i < 8; ++i) kl_read(smem, T, 0, 0, i, F);
   // at the wait of step kt, the loads of steps kt+2 and kt+3 (16) may be in flight
   for (int kt = 0; kt < nk - 4; ++kt) kl_step<true, true, true, 16>(smem, T, kt, F, acc);
-  kl_step<false, true, true, 16>(smem, T, nk - 4, F, acc);
-  kl_step<false, false, true, 8>(smem, T, nk - 3, F, acc);
-  kl_step<false, false, true, 0>(smem, T, nk - 2, F, acc);
-  kl_step<false, false, false, 0>(smem, T, nk - 1, F, acc);
+  // the copies (4 per step, from step nk-4 on) come after the last loads of steps nk-1
+  kl_step<false, true, true, 16, COPY>(smem, T, nk - 4, F, acc);
+  kl_step<false, false, true, COPY ? 12 : 8, COPY>(smem, T, nk - 3, F, acc);
+  kl_step<false, false, true, COPY ? 8 : 0, COPY>(smem, T, nk - 2, F, acc);
+  kl_step<false, false, false, COPY ? 12 : 0, COPY>(smem, T, nk - 1, F, acc);
+}
+
+__device__ __forceinline__ void kl_run(const char* smem, const Tile& T, int nk,
+                                       floatx16 (&acc)[4][4]) {
+  kl_run_t<false>(smem, T, nk, acc);
 }
 
 __device__ __forceinline__ void acc_zero(floatx16 (&acc)[4][4]) {
