@@ -236,20 +236,21 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restr
         floatx4 part = {0.f, 0.f, 0.f, 0.f}, part1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
+          // Batch rows past M read row M - 1 (a valid row): column m of the MFMA result depends
+          // on activation row m only, and columns m >= M are never stored. Zeroing instead
+          // would put each load under a divergent branch that waits for it at once.
+          const int64_t mc = (m < M) ? m : M - 1;
           half8_t af;
           if (ACT_LDS) {
-            af = (m < M) ? *reinterpret_cast<const half8_t*>(table + (m - m0) * K + kbase + 8 * v)
-                         : half8_t{};
-          } else if (m < M) {
-            const uint4 a = *reinterpret_cast<const uint4*>(A + m * K + kbase + 8 * v);
+            af = *reinterpret_cast<const half8_t*>(table + (mc - m0) * K + kbase + 8 * v);
+          } else {
+            const uint4 a = *reinterpret_cast<const uint4*>(A + mc * K + kbase + 8 * v);
             // permute channels 0..7 to the order 0,4,1,5,2,6,3,7 of the weight operand
             const uint32_t p0 = __builtin_amdgcn_perm(a.z, a.x, 0x05040100u);  // (a0, a4)
             const uint32_t p1 = __builtin_amdgcn_perm(a.z, a.x, 0x07060302u);  // (a1, a5)
             const uint32_t p2 = __builtin_amdgcn_perm(a.w, a.y, 0x05040100u);  // (a2, a6)
             const uint32_t p3 = __builtin_amdgcn_perm(a.w, a.y, 0x07060302u);  // (a3, a7)
             af = __builtin_bit_cast(half8_t, make_uint4(p0, p1, p2, p3));
-          } else {
-            af = half8_t{};
           }
           if (GS == 64) {
             const half8_t w0 = (lg < 2) ? wf[v] : half8_t{};
