@@ -21,8 +21,9 @@ fields it carries
   hbm_stages    the bandwidth-bound kernels: algorithmic bytes, GB/s, fraction of 8 TB/s;
   w4a16         the W4A16 kernel at the batch sizes 1, 4, 16, 64, 512 for 4096x4096 and
                 11008x4096, over rotated weight copies (> 256 MB, so HBM and not the
-                Infinity Cache is measured): GB/s and fraction of 8 TB/s (TFLOP/s and MFMA
-                fraction at M = 512);
+                Infinity Cache is measured), replayed from a HIP graph (GPU time per call;
+                `us_eager`: the same calls issued one by one from Python): GB/s and fraction
+                of 8 TB/s (TFLOP/s and MFMA fraction at M = 512);
   cpu_baseline  the CPU oracle on a bounded sample of the same layer, scaled to ms per layer.
 """
 from __future__ import annotations
@@ -151,10 +152,25 @@ def log(*a):
 
 # ---------------------------------------------------------------------------------------------
 def w4a16_sweep(awq, torch):
-    """Time W4A16 over rotated weight copies with HIP events on the current stream."""
+    """Time W4A16 over rotated weight copies with HIP events. `us` is the GPU time per call:
+    one pass over every copy is captured in a HIP graph and replayed (the result of a replay is
+    checked against the eager calls), so the host's launch rate does not enter; `us_eager` is the
+    same pass issued call by call from Python."""
     import numpy as np
     import workloads
     out = []
+    st = torch.cuda.current_stream()
+
+    def elapsed_us(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
     for (n, k) in ((4096, 4096), (11008, 4096)):
         qw, sc, s = workloads.w4a16_random_artifacts(n, k, config=4)
         wbytes = qw.nbytes + sc.nbytes
@@ -165,29 +181,40 @@ def w4a16_sweep(awq, torch):
         for m in (1, 4, 16, 64, 512):
             A = torch.from_numpy(workloads.w4a16_activations(m, k, config=4)).cuda()
             Y = torch.empty((m, n), dtype=torch.float16, device="cuda")
-            for i in range(copies):                     # warm-up, one pass over every copy
-                awq.w4a16_gemm(A, qws[i], scs[i], s_d, out=Y)
-            reps = max(copies, 200)
-            st = torch.cuda.current_stream()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+            def one_pass():
+                for i in range(copies):
+                    awq.w4a16_gemm(A, qws[i], scs[i], s_d, out=Y)
+            one_pass()                                  # warm-up
             torch.cuda.synchronize()
-            e0.record(st)
-            for r in range(reps):
-                i = r % copies
-                awq.w4a16_gemm(A, qws[i], scs[i], s_d, out=Y)
-            e1.record(st)
-            e1.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
+            y_eager = Y.clone()
+            us_eager = elapsed_us(one_pass, 2) / copies
+            graph = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(st)
+            with torch.cuda.stream(side):
+                one_pass()
+                side.synchronize()
+                with torch.cuda.graph(graph, stream=side):
+                    one_pass()
+            torch.cuda.synchronize()
+            Y.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(Y, y_eager):
+                raise RuntimeError(f"W4A16 graph replay differs from the eager result (M={m})")
+            us = elapsed_us(graph.replay, 3) / copies
             nbytes = n * k // 2 + n * (k // 128) * 2 + k * 2 + m * k * 2 + m * n * 2
             flops = 2.0 * m * n * k
-            rec = {"n": n, "k": k, "m": m, "us": round(us, 3), "bytes": nbytes,
-                   "gbs": round(nbytes / us / 1e3, 1),
+            rec = {"n": n, "k": k, "m": m, "us": round(us, 3), "us_eager": round(us_eager, 3),
+                   "bytes": nbytes, "gbs": round(nbytes / us / 1e3, 1),
                    "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
                    "tflops": round(flops / us / 1e6, 2)}
             if m >= 512:
                 rec["mfma_frac"] = round(flops / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4)
             out.append(rec)
             log("w4a16", rec)
+            del graph
         del qws, scs
         torch.cuda.empty_cache()
     return out
