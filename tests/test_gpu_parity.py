@@ -445,6 +445,80 @@ def test_full_c2_layer(awq):
     assert oracle.accuracy_report(Y_g, ref)["rel_fro"] <= W4A16_RTOL
 
 
+def _full_size_layer_check(awq, name, W, X, bits, row_step):
+    """A full-size layer (65536 tokens) in the launch configuration the benchmark times: both
+    search forms on the GPU, then against the oracle what it can compute at this size in a minute
+    or two: s_X (every channel, bit-exact), H = X^T X in fp64 once, the loss at alpha = 0, at the
+    GPU's alpha* and at alpha = 19 (both forms within 1e-4), the codes, packed words and fp16
+    steps of sampled rows at alpha* (bit-exact), and W4A16 on those rows. alpha* itself is checked
+    against the sampled oracle losses (it must not be beaten by them beyond the tie band), and the
+    two forms must choose the same alpha*."""
+    M, K = X.shape
+    N = W.shape[0]
+    say(name, W.shape, X.shape, "bits", bits)
+    Wt, Xt = dev(W), dev(X)
+    sx, flags = awq.act_stats(Xt)
+    res_g = awq.search_layer(Wt, Xt, sx, awq.AwqConfig(bits=bits, form="gram"), flags=flags)
+    res_d = awq.search_layer(Wt, Xt, sx, awq.AwqConfig(bits=bits), flags=flags)
+    p = awq.pack_int4(Wt, res_g.s_best, awq.AwqConfig(bits=bits), flags=flags, with_codes=True)
+    A = workloads.w4a16_activations(16, K, config=5)
+    Y = awq.w4a16_gemm(dev(A), p.qweight, p.scales16, p.s16)
+    sx_g = host(sx)
+    losses_g, bg = host(res_g.losses), int(host(res_g.best)[0])
+    losses_d, bd = host(res_d.losses), int(host(res_d.best)[0])
+    rows = np.arange(0, N, row_step)
+    codes_g = host(p.codes)[rows]
+    qw_g = host(p.qweight).view(np.uint32)[rows]
+    sc_g = host(p.scales16)[rows]
+    Y_g = host(Y)[:, rows]
+    assert int(host(flags)[0]) == 0
+    say(f"gpu: alpha* gram {bg} direct {bd}")
+    del Xt, Wt, res_g, res_d, p, Y
+    torch.cuda.empty_cache()
+    assert bd == bg or oracle.relative_gap(losses_g) <= 2 * LOSS_RTOL
+    sx_o = oracle.act_stats(X)
+    assert np.array_equal(sx_g, sx_o)
+    say("oracle: H = X^T X in fp64 ...")
+    H = oracle.gram(X)
+    S = oracle.scale_table(sx_o, 20)
+    lo = {}
+    for i in sorted({0, bg, 19}):
+        q, d = oracle.quantize(W, S[i], bits=bits)
+        lo[i] = oracle.loss_gram(H, oracle.error_matrix(W, q, d, S[i]), M)
+        rg = abs(losses_g[i] - lo[i]) / lo[i]
+        rd = abs(losses_d[i] - lo[i]) / lo[i]
+        say(f"oracle alpha {i}: L = {lo[i]:.9e}  gram rel {rg:.2e}  direct rel {rd:.2e}")
+        assert rg <= LOSS_RTOL and rd <= LOSS_RTOL
+    assert lo[bg] <= min(lo.values()) * (1 + 2 * LOSS_RTOL)
+    o = oracle.pack_layer(W[rows], S[bg], bits=bits)
+    assert np.array_equal(codes_g, o["codes"])
+    assert np.array_equal(qw_g, o["qweight"])
+    assert np.array_equal(sc_g.view(np.uint16), o["scales16"].view(np.uint16))
+    ref = oracle.w4a16(A, o["qweight"], o["scales16"], o["s16"])
+    assert oracle.accuracy_report(Y_g, ref)["rel_fro"] <= W4A16_RTOL
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_full_c3_down_layer(awq):
+    """LLaMA-7B MLP down projection at full size: W fp16 [4096, 11008], X fp16 [65536, 11008]
+    = |N(0,1)| with 110 channels x30."""
+    W = workloads.weight(3, 4096, 11008, j=2)
+    X = workloads.activations(3, 65536, workloads.channel_gains_choice(3, 11008, 110, 30.0, j=2),
+                              np.float16, j=2, absolute=True)
+    _full_size_layer_check(awq, "full c3 down", W, X, 4, row_step=67)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_full_c5_mlp_layer_int3(awq):
+    """70B-class MLP projection at full size, INT3: W fp16 [28672, 8192], X fp16 [65536, 8192]
+    with 1% of the channels x50."""
+    W = workloads.c5_weight(28672, j=3)
+    X = workloads.c5_x()
+    _full_size_layer_check(awq, "full c5 mlp int3", W, X, 3, row_step=211)
+
+
 # ------------------------------------------------------------------------------------------------
 # Clipping search and clipped packing
 CLIP_ERR_RTOL = 5e-3     # per (ratio, row, group) error: fp16 E' and correlation operand
