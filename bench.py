@@ -15,7 +15,9 @@ fields it carries
                 every MFMA kernel of the step the same way;
   stages_ms     mean duration of every kernel of the search;
   other_form    the search in the other form (a few repetitions): ms and its loss kernel;
-  clip_search   the clipping search at s* (11 ratios 1 .. 0.5) and the clipped pack: ms;
+  clip_search   the clipping search at s* (11 ratios 1 .. 0.5) and the clipped pack: ms; and
+                the same search on the operand the step's Gram-form search left in its
+                workspace (awq_clip_search_gram);
   shared_qkv    one alpha for three 4096x4096 weights reading the same X, and the fold of s^-1
                 into the producing norm weight: ms;
   hbm_stages    the bandwidth-bound kernels: algorithmic bytes, GB/s, fraction of 8 TB/s;
@@ -392,6 +394,22 @@ def main():
                     "pack_clipped_ms": round(statistics.mean(ptimes), 4),
                     "groups_clipped_frac": round(float((ratios < 1.0).mean()), 4),
                     "mean_ratio": round(float(ratios.mean()), 4)}
+        if args.form == "gram":
+            # the same search on the operand the step's search left in its workspace
+            gcfg = awq.AwqConfig(bits=4, group=128, n_grid=N_GRID, form="gram", n_clip=11,
+                                 clip_min=0.5)
+            gtimes = []
+            for r in range(args.clip_reps + 1):
+                c0, c1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+                c0.record(st)
+                crg = awq.clip_search_gram(W, s_star, ws_search, gcfg, flags=flags)
+                c1.record(st)
+                c1.synchronize()
+                if r:
+                    gtimes.append(c0.elapsed_time(c1))
+            rg = crg.clip.cpu().numpy()
+            clip_rec["after_gram_search_ms"] = round(statistics.mean(gtimes), 4)
+            clip_rec["after_gram_search_same_ratio_frac"] = round(float((rg == ratios).mean()), 5)
         log("clip search", clip_rec)
         del ws_c
 

@@ -78,7 +78,9 @@ enum {
   AWQ_FLAG_STEP_UNDERFLOW = 1u << 7,   /* a group with max|w s| > 0 got step 0 (codes set to 0)*/
   AWQ_FLAG_CLIP_RANGE = 1u << 8,       /* a clip ratio given to awq_pack_int4 is outside (0, 1]; */
                                        /* that group was packed unclipped                       */
-  AWQ_FLAG_FOLD_RANGE = 1u << 9        /* awq_fold_scale turned a finite parameter into Inf      */
+  AWQ_FLAG_FOLD_RANGE = 1u << 9,       /* awq_fold_scale turned a finite parameter into Inf      */
+  AWQ_FLAG_NO_GRAM = 1u << 10          /* awq_clip_search_gram: the workspace holds no operand of */
+                                       /* a Gram-form search with this K; nothing was written    */
 };
 
 /* How awq_search_layer evaluates the loss (same value, different contraction):
@@ -242,6 +244,33 @@ awq_status awq_clip_search(const void* W, awq_dtype wdt, int64_t N, int64_t K, c
                            awq_dtype xdt, int64_t M, const float* s, const awq_cfg* cfg,
                            float* clip, float* clip_err, uint32_t* flags, void* ws,
                            size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * awq_clip_search_gram -- the clipping search of awq_clip_search right after a Gram-form
+ * awq_search_layer / awq_search_layers on the same X: H_gg and d are taken from that search's
+ * workspace (its d = sqrt(diag X^T X) and the diagonal blocks of its correlation operand), so X
+ * is not read again. Same ratios grid, error, choice and outputs as awq_clip_search; the errors
+ * differ from it only by the rounding of the two preparations (their X^T X is summed over
+ * different token chunks).
+ * W, s, clip, clip_err, flags  as in awq_clip_search (W: any weight that read that X, e.g. each
+ *          of q, k, v after awq_search_layers).
+ * cfg      as in awq_clip_search, with form == AWQ_FORM_GRAM and the n_grid of the search (they
+ *          locate the operand in its workspace).
+ * search_ws, search_ws_bytes  the search's workspace (device), at least
+ *          awq_clip_search_gram_ws_bytes(K, cfg) bytes; read only. The last call that wrote it
+ *          must be that search, with the same K and cfg->n_grid. Checked on the device: if the
+ *          workspace holds no Gram-form operand for this K (a direct-form search, another K, or
+ *          a search that did not reach that point), AWQ_FLAG_NO_GRAM is raised and clip and
+ *          clip_err are not written.
+ * Limits: as awq_clip_search, and K <= 32768 (the Gram form's limit).
+ * Errors: AWQ_ERR_NULL, AWQ_ERR_SHAPE, AWQ_ERR_DTYPE, AWQ_ERR_CONFIG (also form != GRAM),
+ *         AWQ_ERR_WORKSPACE.
+ * ---------------------------------------------------------------------------------------- */
+size_t awq_clip_search_gram_ws_bytes(int64_t K, const awq_cfg* cfg);
+awq_status awq_clip_search_gram(const void* W, awq_dtype wdt, int64_t N, int64_t K,
+                                const float* s, const awq_cfg* cfg, const void* search_ws,
+                                size_t search_ws_bytes, float* clip, float* clip_err,
+                                uint32_t* flags, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * awq_pack_int4 -- the stored result of [eng] 三 (QuantLinear(q_weight, scales_per_group,

@@ -30,6 +30,7 @@ FLAG_NONFINITE_LOSS = 1 << 6
 FLAG_STEP_UNDERFLOW = 1 << 7
 FLAG_CLIP_RANGE = 1 << 8
 FLAG_FOLD_RANGE = 1 << 9
+FLAG_NO_GRAM = 1 << 10
 
 
 class AwqCfg(ctypes.Structure):
@@ -62,6 +63,9 @@ SIGNATURES = {
     "awq_clip_workspace_bytes": (_SZ, [_I64, _I64, _I64, _E, ctypes.POINTER(AwqCfg)]),
     "awq_clip_search": (_E, [_P, _E, _I64, _I64, _P, _E, _I64, _P, ctypes.POINTER(AwqCfg), _P,
                              _P, _P, _P, _SZ, _P]),
+    "awq_clip_search_gram_ws_bytes": (_SZ, [_I64, ctypes.POINTER(AwqCfg)]),
+    "awq_clip_search_gram": (_E, [_P, _E, _I64, _I64, _P, ctypes.POINTER(AwqCfg), _P, _SZ, _P,
+                                  _P, _P, _P]),
     "awq_pack_int4": (_E, [_P, _E, _I64, _I64, _P, _P, ctypes.POINTER(AwqCfg), _P, _P, _P, _P,
                            _P, _P, _P]),
     "w4a16_gemm": (_E, [_P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P]),

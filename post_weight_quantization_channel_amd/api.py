@@ -184,6 +184,36 @@ def clip_search(W: torch.Tensor, X: torch.Tensor, s: torch.Tensor, cfg: AwqConfi
     return ClipResult(clip, err, flags)
 
 
+def clip_search_gram(W: torch.Tensor, s: torch.Tensor, search_workspace: torch.Tensor,
+                     cfg: AwqConfig = AwqConfig(form="gram"), with_err: bool = False,
+                     flags: torch.Tensor | None = None) -> ClipResult:
+    """The clipping search of clip_search, with H_gg and d taken from the workspace of the
+    Gram-form search (search_layer / search_layers with this `cfg` and an explicit workspace)
+    that just ran on the same X, instead of being formed from X again."""
+    lib = _lib.load()
+    _dev(W, "W")
+    _dev(s, "s")
+    _dev(search_workspace, "search_workspace")
+    N, K = W.shape
+    if s.shape != (K,) or s.dtype != torch.float32:
+        raise ValueError("shape mismatch: W [N,K], s fp32 [K]")
+    if cfg.form != "gram":
+        raise ValueError("clip_search_gram needs the configuration of a Gram-form search")
+    c = cfg.c()
+    if lib.awq_clip_search_gram_ws_bytes(K, c) == 0:
+        raise ValueError("invalid shape or config for the clipping search")
+    flags = _flags(W.device, flags)
+    G = K // cfg.group
+    clip = torch.empty((N, G), dtype=torch.float32, device=W.device)
+    err = torch.empty((cfg.n_clip, N, G), dtype=torch.float32, device=W.device) \
+        if with_err else None
+    check("awq_clip_search_gram", lib.awq_clip_search_gram(
+        W.data_ptr(), _DT[W.dtype], N, K, s.data_ptr(), c, search_workspace.data_ptr(),
+        search_workspace.numel() * search_workspace.element_size(), clip.data_ptr(),
+        err.data_ptr() if err is not None else None, flags.data_ptr(), _stream(W)))
+    return ClipResult(clip, err, flags)
+
+
 def search_layers(Ws: list, X: torch.Tensor, sx: torch.Tensor, cfg: AwqConfig = AwqConfig(),
                   flags: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None) -> SearchResult:

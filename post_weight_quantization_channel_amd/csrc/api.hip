@@ -106,7 +106,7 @@ const char* awq_status_string(awq_status status) {
   return "unknown awq_status";
 }
 
-int32_t awq_version(void) { return 10400; }
+int32_t awq_version(void) { return 10500; }
 
 size_t awq_act_stats_workspace_bytes(int64_t M, int64_t K) {
   if (M < 1 || K < 1 || M > kMaxDim || K > kMaxDim) return 0;
@@ -207,8 +207,8 @@ awq_status search_impl(const void* const* Ws, const int64_t* Ns, int n_w, awq_dt
                                    reinterpret_cast<float*>(base + L.Hpart),
                                    reinterpret_cast<double*>(base + L.d64),
                                    reinterpret_cast<float*>(base + L.d32),
-                                   reinterpret_cast<uint16_t*>(base + L.B), flags, stream,
-                                   ev ? ev + 2 : nullptr);
+                                   reinterpret_cast<uint16_t*>(base + L.B), &ctrl->gram_k,
+                                   flags, stream, ev ? ev + 2 : nullptr);
   } else {
     if (e == hipSuccess && xdt != AWQ_F16) {
       auto* x16 = reinterpret_cast<uint16_t*>(base + L.X16);
@@ -376,13 +376,48 @@ awq_status awq_clip_search(const void* W, awq_dtype wdt, int64_t N, int64_t K, c
   hipError_t e = awq::launch_gram_prepare(X, (int)xdt, M, K, L.plan,
                                           reinterpret_cast<uint16_t*>(base + L.Xt),
                                           reinterpret_cast<float*>(base + L.Hpart),
-                                          reinterpret_cast<double*>(base + L.d64), d32, Bd, flags,
-                                          stream, nullptr);
+                                          reinterpret_cast<double*>(base + L.d64), d32, Bd,
+                                          nullptr, flags, stream, nullptr);
   if (e == hipSuccess)
-    e = awq::launch_clip_search(W, (int)wdt, N, K, s, d32, Bd, cfg->n_clip, cfg->clip_min,
-                                cfg->bits, cfg->group, cfg->zero_point != 0, clip, clip_err,
-                                flags, stream);
+    e = awq::launch_clip_search(W, (int)wdt, N, K, s, d32, Bd, (int64_t)awq::kLossBM * awq::kLossBN,
+                                awq::kLossBN, nullptr,
+                                cfg->n_clip, cfg->clip_min, cfg->bits, cfg->group,
+                                cfg->zero_point != 0, clip, clip_err, flags, stream);
   return hip_status(e);
+}
+
+size_t awq_clip_search_gram_ws_bytes(int64_t K, const awq_cfg* cfg) {
+  if (check_clip_cfg(cfg) != AWQ_OK || cfg->form != AWQ_FORM_GRAM) return 0;
+  if (K < 128 || K % cfg->group || K > kMaxGramK) return 0;
+  const SearchLayout L = search_layout(awq::kGramMAlign, 1, K, AWQ_F16, cfg->n_grid,
+                                       AWQ_FORM_GRAM);
+  return L.B + (size_t)K * (size_t)K * 2;
+}
+
+awq_status awq_clip_search_gram(const void* W, awq_dtype wdt, int64_t N, int64_t K,
+                                const float* s, const awq_cfg* cfg, const void* search_ws,
+                                size_t search_ws_bytes, float* clip, float* clip_err,
+                                uint32_t* flags, hipStream_t stream) {
+  if (!W || !s || !cfg || !clip || !flags || !search_ws) return AWQ_ERR_NULL;
+  const awq_status cs = check_clip_cfg(cfg);
+  if (cs != AWQ_OK) return cs;
+  if (cfg->form != AWQ_FORM_GRAM) return AWQ_ERR_CONFIG;
+  if (wdt != AWQ_F16 && wdt != AWQ_F32) return AWQ_ERR_DTYPE;
+  if (N < 1 || N > kMaxDim || K < 128 || K % cfg->group || K > kMaxGramK || !aligned16(W) ||
+      !aligned16(s))
+    return AWQ_ERR_SHAPE;
+  const size_t need = awq_clip_search_gram_ws_bytes(K, cfg);
+  if (search_ws_bytes < need || !aligned16(search_ws)) return AWQ_ERR_WORKSPACE;
+  // the search's operand: its offsets depend on K and n_grid only (not on M or N)
+  const SearchLayout L = search_layout(awq::kGramMAlign, 1, K, AWQ_F16, cfg->n_grid,
+                                       AWQ_FORM_GRAM);
+  const char* base = static_cast<const char*>(search_ws);
+  const auto* ctrl = reinterpret_cast<const awq::SearchCtrl*>(base + L.ctrl);
+  return hip_status(awq::launch_clip_search(
+      W, (int)wdt, N, K, s, reinterpret_cast<const float*>(base + L.d32),
+      reinterpret_cast<const uint16_t*>(base + L.B), (int64_t)awq::kLossBN * K + awq::kLossBN, K,
+      &ctrl->gram_k, cfg->n_clip, cfg->clip_min, cfg->bits, cfg->group, cfg->zero_point != 0, clip,
+      clip_err, flags, stream));
 }
 
 awq_status awq_fold_scale(void* prev, awq_dtype dtype, int64_t rows, int64_t cols, int64_t ld,

@@ -45,7 +45,8 @@ __device__ __forceinline__ float clip_ratio(int j, int n_clip, float clip_min) {
 template <int DT, int GS, bool ZP>
 __global__ __launch_bounds__(256) void clip_search_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s,
-    const float* __restrict__ d32, const uint16_t* __restrict__ Bd, int n_clip, float clip_min,
+    const float* __restrict__ d32, const uint16_t* __restrict__ Bd, int64_t bd_block,
+    int64_t bd_pitch, const uint32_t* __restrict__ gram_k, int n_clip, float clip_min,
     float qmin, float qmax, float* __restrict__ clip, float* __restrict__ clip_err,
     uint32_t* __restrict__ flags) {
   constexpr int ES = (DT == kF32) ? 4 : 2;
@@ -62,15 +63,22 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i = lane & 15, q = lane >> 4;
 
-  // B_gg: rows l, columns k of the group, from the diagonal 256 x 256 block holding it
+  // with the operand of a preceding Gram-form search: that search must have been the last to
+  // write it, for this K (uniform over the grid: every workgroup leaves, one raises the flag)
+  if (gram_k && *gram_k != (uint32_t)K) {
+    if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) atomicOr(flags, kFlagNoGram);
+    return;
+  }
+  // B_gg: rows l, columns k of the group, from the diagonal 256 x 256 block holding it (block a
+  // at Bd + a * bd_block, rows bd_pitch elements apart)
   {
     const int64_t c0 = (int64_t)g * GS;
     const int o = (int)(c0 % 256);
-    const uint16_t* src = Bd + (c0 / 256) * (256 * 256) + (int64_t)o * 256 + o;
+    const uint16_t* src = Bd + (c0 / 256) * bd_block + (int64_t)o * bd_pitch + o;
     for (int idx = tid; idx < GS * (GS / 8); idx += 256) {
       const int l = idx / (GS / 8), ch = idx % (GS / 8);
       *reinterpret_cast<uint4*>(&Bg[l * kPitch + ch * 8]) =
-          *reinterpret_cast<const uint4*>(src + l * 256 + ch * 8);
+          *reinterpret_cast<const uint4*>(src + l * bd_pitch + ch * 8);
     }
   }
 
@@ -227,16 +235,17 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
 }
 
 hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, const float* s,
-                              const float* d32, const uint16_t* Bd, int n_clip, float clip_min,
-                              int bits, int group, bool zero_point, float* clip, float* clip_err,
-                              uint32_t* flags, hipStream_t stream) {
+                              const float* d32, const uint16_t* Bd, int64_t bd_block,
+                              int64_t bd_pitch, const uint32_t* gram_k, int n_clip,
+                              float clip_min, int bits, int group, bool zero_point, float* clip,
+                              float* clip_err, uint32_t* flags, hipStream_t stream) {
   const float qmax = zero_point ? (float)((1 << bits) - 1) : (float)((1 << (bits - 1)) - 1);
   const float qmin = zero_point ? 0.0f : -(float)(1 << (bits - 1));
   dim3 grid((unsigned)((N + kClipRows - 1) / kClipRows), (unsigned)(K / group));
 #define AWQ_CLIP(DT_, GS_, ZP_)                                                                  \
-  clip_search_kernel<DT_, GS_, ZP_><<<grid, 256, 0, stream>>>(W, N, K, s, d32, Bd, n_clip,        \
-                                                              clip_min, qmin, qmax, clip,        \
-                                                              clip_err, flags)
+  clip_search_kernel<DT_, GS_, ZP_><<<grid, 256, 0, stream>>>(                                    \
+      W, N, K, s, d32, Bd, bd_block, bd_pitch, gram_k, n_clip, clip_min, qmin, qmax, clip,       \
+      clip_err, flags)
   if (dtype == kF32) {
     if (group == 64) {
       if (zero_point) AWQ_CLIP(kF32, 64, true); else AWQ_CLIP(kF32, 64, false);

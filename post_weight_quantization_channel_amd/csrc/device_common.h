@@ -33,6 +33,7 @@ enum : uint32_t {
   kFlagStepUnderflow = 1u << 7,
   kFlagClipRange = 1u << 8,
   kFlagFoldRange = 1u << 9,
+  kFlagNoGram = 1u << 10,
 };
 
 __device__ __forceinline__ float h2f(uint16_t b) {

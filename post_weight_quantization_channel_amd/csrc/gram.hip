@@ -196,9 +196,11 @@ __global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restric
                                                           int64_t K, int t, int64_t T, int S,
                                                           int diag,
                                                           const double* __restrict__ d64,
-                                                          uint16_t* __restrict__ B) {
+                                                          uint16_t* __restrict__ B,
+                                                          uint32_t* __restrict__ gram_k) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;   // float4 index
   constexpr int64_t kPerTile = kLossBM * kLossBN / 4;
+  if (g == 0 && gram_k) *gram_k = (uint32_t)K;   // read by later launches only
   if (g >= T * kPerTile) return;
   const int64_t tile = g / kPerTile;
   const int rem = (int)(g % kPerTile);
@@ -350,7 +352,8 @@ __global__ __launch_bounds__(kloop::kThreads, 1) void gram_loss_kernel(
 // ------------------------------------------------------------------------------------------
 hipError_t launch_gram_prepare(const void* X, int xdt, int64_t M, int64_t K, const GramPlan& p,
                                uint16_t* Xt, float* Hpart, double* d64, float* d32, uint16_t* B,
-                               uint32_t* flags, hipStream_t stream, hipEvent_t* ev) {
+                               uint32_t* gram_k, uint32_t* flags, hipStream_t stream,
+                               hipEvent_t* ev) {
   hipError_t e = hipSuccess;
   {
     dim3 grid((unsigned)(K / 64), (unsigned)((p.Mp + 255) / 256));
@@ -384,7 +387,7 @@ hipError_t launch_gram_prepare(const void* X, int xdt, int64_t M, int64_t K, con
     const int64_t threads = p.T * (kLossBM * kLossBN / 4);
     gram_finish_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(Hpart, K, p.t, p.T,
                                                                               p.S, (int)p.diag,
-                                                                              d64, B);
+                                                                              d64, B, gram_k);
     e = hipGetLastError();
   }
   return e;

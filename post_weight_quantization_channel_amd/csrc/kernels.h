@@ -22,6 +22,7 @@ constexpr int kLossBK = 32;
 struct SearchCtrl {        // lives at the start of the search workspace
   uint32_t absmax_bits;    // max |W| as fp32 bits (atomicMax on non-negative floats)
   uint32_t done;           // grid points whose loss is final (finalize's completion count)
+  uint32_t gram_k;         // K of the Gram-form operand B in this workspace (0: none)
 };
 
 // Gram form (gram.hip): H = X^T X over token chunks, then the lower-triangular operand B.
@@ -39,9 +40,12 @@ struct GramPlan {
 GramPlan gram_plan(int64_t M, int64_t K, bool diag = false);
 // transpose -> ev[0] -> X^T X partials -> ev[1] -> d and B. B is [K, K] (row l, column k), or
 // with plan.diag the t diagonal blocks [t][256][256] (block a: rows and columns 256 a ..).
+// gram_k: nullptr, or where the finish pass records K (the operand is then complete once the
+// stream has passed this call).
 hipError_t launch_gram_prepare(const void* X, int xdt, int64_t M, int64_t K, const GramPlan& p,
                                uint16_t* Xt, float* Hpart, double* d64, float* d32, uint16_t* B,
-                               uint32_t* flags, hipStream_t stream, hipEvent_t* ev);
+                               uint32_t* gram_k, uint32_t* flags, hipStream_t stream,
+                               hipEvent_t* ev);
 hipError_t launch_gram_loss(const uint16_t* Estack, int64_t N, int64_t K, const uint16_t* B,
                             int n_grid, double* partials, hipStream_t stream);
 
@@ -81,11 +85,16 @@ hipError_t launch_fold(void* prev, int dtype, int64_t rows, int64_t cols, int64_
 // ---- clipping search (clip.hip) ----
 // Per (row, group of 128): the ratio of the grid 1 .. clip_min whose clipped quantization of
 // W * s gives the smallest group error E_g H_gg E_g^T, with H_gg taken from the diagonal blocks
-// of the correlation operand (Bd) and d = sqrt(diag H).
+// of the correlation operand and d = sqrt(diag H). The diagonal block a of the operand starts
+// at Bd + a * bd_block with rows bd_pitch elements apart ([t][256][256] from the diagonal-only
+// preparation: 65536 and 256; the full [K][K] operand of a Gram-form search: 256 K + 256 and K).
+// gram_k: nullptr, or the workspace's record of the K its operand was formed for; when it differs
+// from K nothing is written and AWQ_FLAG_NO_GRAM is raised.
 hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, const float* s,
-                              const float* d32, const uint16_t* Bd, int n_clip, float clip_min,
-                              int bits, int group, bool zero_point, float* clip, float* clip_err,
-                              uint32_t* flags, hipStream_t stream);
+                              const float* d32, const uint16_t* Bd, int64_t bd_block,
+                              int64_t bd_pitch, const uint32_t* gram_k, int n_clip,
+                              float clip_min, int bits, int group, bool zero_point, float* clip,
+                              float* clip_err, uint32_t* flags, hipStream_t stream);
 
 // ---- W4A16 ----
 // group 128 or 64; zeros [N, K/group] (zero-point codes) or nullptr; s16 nullptr: s folded

@@ -28,6 +28,7 @@ __global__ __launch_bounds__(256) void search_prep_kernel(const float* __restric
   if (idx == 0) {
     ctrl->absmax_bits = 0u;
     ctrl->done = 0u;
+    ctrl->gram_k = 0u;   // set again by the Gram form's finish pass
   }
   if (idx >= (int64_t)n_grid * K) return;
   const int i = (int)(idx / K);

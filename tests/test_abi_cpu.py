@@ -34,6 +34,7 @@ def test_header_declares_the_calls():
     for n in ("awq_act_stats", "awq_search_layer", "awq_pack_int4", "w4a16_gemm",
               "awq_search_workspace_bytes", "awq_act_stats_workspace_bytes",
               "awq_clip_search", "awq_clip_workspace_bytes", "awq_search_layers",
+              "awq_clip_search_gram", "awq_clip_search_gram_ws_bytes",
               "awq_fold_scale",
               "awq_status_string", "awq_version"):
         assert n in names
@@ -49,7 +50,7 @@ def test_status_strings(lib):
     for code in range(7):
         s = lib.awq_status_string(code).decode()
         assert s.startswith("AWQ_")
-    assert lib.awq_version() == 10400
+    assert lib.awq_version() == 10500
 
 
 def cfg(bits=4, group=128, n_grid=20, s_floor=1e-5, form=0, n_clip=11, clip_min=0.5,
@@ -231,6 +232,40 @@ def test_clip_search_rejects(lib):
     assert need >= 512 * 12 + 2 * 65536 * 2 + 512 * 384 * 2 + 2 * 65536 * 4
     assert _clip(lib, ws_bytes=need - 1) == E.AWQ_ERR_WORKSPACE
     assert lib.awq_clip_workspace_bytes(300, 256, 512, 1, cfg(clip_min=2.0)) == 0
+
+
+def _clip_gram(lib, **kw):
+    a = dict(W=FAKE, wdt=1, N=256, K=512, s=FAKE, cfg=cfg(form=1), ws=FAKE2, ws_bytes=1 << 40,
+             clip=FAKE, err=None, flags=FAKE)
+    a.update(kw)
+    c = a["cfg"]
+    return lib.awq_clip_search_gram(a["W"], a["wdt"], a["N"], a["K"], a["s"],
+                                    ctypes.byref(c) if c is not None else None, a["ws"],
+                                    a["ws_bytes"], a["clip"], a["err"], a["flags"], None)
+
+
+def test_clip_search_gram_rejects(lib):
+    E = _lib
+    for k in ("W", "s", "clip", "flags", "ws"):
+        assert _clip_gram(lib, **{k: None}) == E.AWQ_ERR_NULL, k
+    assert _clip_gram(lib, cfg=None) == E.AWQ_ERR_NULL
+    assert _clip_gram(lib, cfg=cfg(form=0)) == E.AWQ_ERR_CONFIG      # needs a Gram-form search
+    assert _clip_gram(lib, cfg=cfg(form=1, n_clip=1)) == E.AWQ_ERR_CONFIG
+    assert _clip_gram(lib, wdt=2) == E.AWQ_ERR_DTYPE
+    assert _clip_gram(lib, K=500) == E.AWQ_ERR_SHAPE
+    assert _clip_gram(lib, K=32768 + 128) == E.AWQ_ERR_SHAPE
+    assert _clip_gram(lib, N=0) == E.AWQ_ERR_SHAPE
+    assert _clip_gram(lib, s=FAKE + 4) == E.AWQ_ERR_SHAPE
+    need = lib.awq_clip_search_gram_ws_bytes(512, cfg(form=1))
+    # the operand sits after the control block, the scale table and d: at least K^2 fp16 in all
+    assert need >= 512 * 512 * 2 + 20 * 512 * 4 + 512 * 12
+    # it lies inside a Gram-form search workspace of any M and N for this K and n_grid
+    for (M, N) in ((128, 1), (300, 256), (65536, 4096)):
+        assert lib.awq_search_workspace_bytes(M, N, 512, 1, cfg(form=1)) >= need
+    assert _clip_gram(lib, ws_bytes=need - 1) == E.AWQ_ERR_WORKSPACE
+    assert _clip_gram(lib, ws=FAKE2 + 8) == E.AWQ_ERR_WORKSPACE
+    assert lib.awq_clip_search_gram_ws_bytes(512, cfg(form=0)) == 0
+    assert lib.awq_clip_search_gram_ws_bytes(500, cfg(form=1)) == 0
 
 
 def test_search_layers_rejects(lib):

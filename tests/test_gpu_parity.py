@@ -570,6 +570,85 @@ def test_clip_search_parity(awq, name, make, bits, n_clip, clip_min):
     assert int(host(r.flags)[0]) == 0
 
 
+def _check_clip_against_oracle(r, W, X, s, bits, n_clip, clip_min):
+    orc = oracle.clip_search(W, X, s, bits=bits, n_clip=n_clip, clip_min=clip_min)
+    err_g = host(r.err).astype(np.float64)
+    err_o = orc["err"]
+    scale = err_o.max(axis=0, keepdims=True)
+    rel = np.abs(err_g - err_o) / np.maximum(scale, 1e-300)
+    assert rel.max() <= CLIP_ERR_RTOL
+    ratio_g = host(r.clip)
+    grid = oracle.clip_grid(n_clip, clip_min)
+    assert np.isin(ratio_g, grid).all()
+    j_g = np.searchsorted(-grid, -ratio_g)
+    rows, groups = np.indices(ratio_g.shape)
+    chosen = err_o[j_g, rows, groups]
+    assert (chosen <= err_o.min(axis=0) * (1 + CLIP_BAND) + 1e-12 * scale[0]).all()
+    return float(rel.max()), float((j_g == orc["best"]).mean())
+
+
+@pytest.mark.parametrize("name,make,bits,n_clip,clip_min", CLIP_CASES,
+                         ids=[c[0] for c in CLIP_CASES])
+def test_clip_search_gram_parity(awq, name, make, bits, n_clip, clip_min):
+    """The clipping search on the operand a Gram-form search left in its workspace: against the
+    oracle at the search's own s*, as the standalone clipping search."""
+    W, X = make()
+    say("clip search after the search", name, W.shape, X.shape, "bits", bits)
+    cfg = awq.AwqConfig(bits=bits, n_clip=n_clip, clip_min=clip_min, form="gram")
+    Wt, Xt = dev(W), dev(X)
+    sx, flags = awq.act_stats(Xt)
+    ws = torch.empty(awq.search_workspace_bytes(X.shape[0], W.shape[0], W.shape[1],
+                                                Xt.dtype, cfg), dtype=torch.uint8, device="cuda")
+    res = awq.search_layer(Wt, Xt, sx, cfg, flags=flags, workspace=ws)
+    r = awq.clip_search_gram(Wt, res.s_best, ws, cfg, with_err=True, flags=flags)
+    rel, same = _check_clip_against_oracle(r, W, X, host(res.s_best), bits, n_clip, clip_min)
+    say(f"max err rel {rel:.2e}; same ratio as the oracle in {100 * same:.2f}%")
+    assert int(host(flags)[0]) == 0
+
+
+def test_clip_search_gram_after_shared_search(awq):
+    """q, k, v searched together (one s*), then each clipped from the shared workspace."""
+    X = workloads.c2_like_layer(n=8, k=512, m=640, config=57).X
+    Ws = [workloads.weight(57, n, 512, j=j) for j, n in enumerate((256, 128, 128))]
+    cfg = awq.AwqConfig(form="gram")
+    Xt = dev(X)
+    sx, flags = awq.act_stats(Xt)
+    Wts = [dev(W) for W in Ws]
+    ws = torch.empty(awq.search_workspace_bytes(640, 512, 512, Xt.dtype, cfg), dtype=torch.uint8,
+                     device="cuda")
+    res = awq.search_layers(Wts, Xt, sx, cfg, flags=flags, workspace=ws)
+    s = host(res.s_best)
+    for W, Wt in zip(Ws, Wts):
+        r = awq.clip_search_gram(Wt, res.s_best, ws, cfg, with_err=True, flags=flags)
+        rel, same = _check_clip_against_oracle(r, W, X, s, 4, cfg.n_clip, cfg.clip_min)
+        say(f"{W.shape}: max err rel {rel:.2e}; same ratio {100 * same:.2f}%")
+    assert int(host(flags)[0]) == 0
+
+
+def test_clip_search_gram_refuses_a_direct_form_workspace(awq):
+    """A workspace last written by a direct-form search holds no Gram operand: the call raises
+    AWQ_FLAG_NO_GRAM; after a Gram-form search the same workspace is accepted again."""
+    from post_weight_quantization_channel_amd import _lib
+    W, X = _lognormal_layer(58, 256, 512, 400)
+    Wt, Xt = dev(W), dev(X)
+    sx, _ = awq.act_stats(Xt)
+    cfg_g = awq.AwqConfig(form="gram")
+    nbytes = max(awq.search_workspace_bytes(400, 256, 512, Xt.dtype, cfg_g),
+                 awq.search_workspace_bytes(400, 256, 512, Xt.dtype, awq.AwqConfig()))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    awq.search_layer(Wt, Xt, sx, cfg_g, workspace=ws)
+    res = awq.search_layer(Wt, Xt, sx, awq.AwqConfig(), workspace=ws)   # direct form, same ws
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    r = awq.clip_search_gram(Wt, res.s_best, ws, cfg_g, with_err=False, flags=flags)
+    assert int(host(flags)[0]) == _lib.FLAG_NO_GRAM
+    # the Gram-form search again: accepted
+    res = awq.search_layer(Wt, Xt, sx, cfg_g, workspace=ws)
+    flags.zero_()
+    r = awq.clip_search_gram(Wt, res.s_best, ws, cfg_g, with_err=True, flags=flags)
+    assert int(host(flags)[0]) == 0
+    _check_clip_against_oracle(r, W, X, host(res.s_best), 4, cfg_g.n_clip, cfg_g.clip_min)
+
+
 def test_pack_with_clip_bit_exact(awq):
     """The oracle's clip ratios (and random ratios in (0, 1]) fed to both packers: codes, packed
     words and fp16 steps bit-identical."""
