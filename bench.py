@@ -11,9 +11,10 @@ synthetic (seeded, see workloads/) and resident in HBM before the timed region.
 Prints ONE JSON line. `value` is milliseconds per layer (lower is better). Besides the contract
 fields it carries
   roofline      the step's longest kernel against the dense fp16 MFMA peak, its duration
-                measured with HIP events on the library's stream in every step; `mfma` lists
-                every MFMA kernel of the step the same way;
-  stages_ms     mean duration of every kernel of the search;
+                measured with HIP events on the library's stream (in extra steps after the
+                timed ones, whose search call waits for its events); `mfma` lists every MFMA
+                kernel of the step the same way;
+  stages_ms     mean duration of every kernel of the search (the same extra steps);
   other_form    the search in the other form (a few repetitions): ms and its loss kernel;
   clip_search   the clipping search at s* (11 ratios 1 .. 0.5) and the clipped pack: ms; and
                 the same search on the operand the step's Gram-form search left in its
@@ -300,6 +301,8 @@ def main():
     st = torch.cuda.current_stream()
 
     def step(prof):
+        # prof: a dict for the per-kernel durations of the search (that call then blocks until
+        # the search is done), or None (nothing blocks: the timed steps)
         e0, e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
         e0.record(st)
         sx, _ = awq.act_stats(X, flags=flags, workspace=ws_stats)
@@ -323,14 +326,18 @@ def main():
     torch.cuda.synchronize()
     t_start.record(st)
     for _ in range(args.steps):
-        prof = {}
-        res, evs, _ = step(prof)
-        stage_runs.append(prof)
+        res, evs, _ = step(None)
         ev_runs.append(evs)
     t_end.record(st)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+    # the per-kernel breakdown of the search, from further steps outside the timed region
+    for _ in range(max(3, min(args.steps, 10))):
+        prof = {}
+        step(prof)
+        stage_runs.append(prof)
+    torch.cuda.synchronize()
 
     stats_ms = statistics.mean(a.elapsed_time(b) for a, b, _, _ in ev_runs)
     pack_ms = statistics.mean(c.elapsed_time(d) for _, _, c, d in ev_runs)
