@@ -12,8 +12,10 @@
 //     read as zeros without branches;
 //   * four LDS stages of 32 KiB: the loads of steps k+1..k+4 are in flight while step k
 //     computes (one stage ahead left the waves waiting ~40% of the time on loads whose lines
-//     missed L2; LDS bank conflicts: none). Fragment reads of the next step overlap the second
-//     half of the current step's MFMAs;
+//     missed L2; with four, dropping the wait for them saves nothing: they land in time; LDS
+//     bank conflicts: none). Fragment reads of the next step overlap the second half of the
+//     current step's MFMAs; a stage's refill is split over two half steps, and every load
+//     address is scalar arithmetic plus one per-lane offset (no vector ALU work per load);
 //   * LDS layout: row r holds its 4 chunks of 16 bytes at positions c ^ f(r),
 //     f(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1), so the 128-bit fragment reads of 8 (and of 16)
 //     consecutive rows at one chunk touch distinct banks whether the LDS has 32 or 64 banks.
