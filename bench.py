@@ -21,6 +21,8 @@ fields it carries
                 workspace (awq_clip_search_gram);
   shared_qkv    one alpha for three 4096x4096 weights reading the same X, and the fold of s^-1
                 into the producing norm weight: ms;
+  quant_variants  groups of 64 and zero-point codes (and both): the search (ms, its quantize
+                and loss kernels), the pack, and W4A16 at M = 1 and 512 on 4096x4096;
   hbm_stages    the bandwidth-bound kernels: algorithmic bytes, GB/s, fraction of 8 TB/s;
   w4a16         the W4A16 kernel at the batch sizes 1, 4, 16, 64, 512 for 4096x4096 and
                 11008x4096, over rotated weight copies (> 256 MB, so HBM and not the
@@ -60,6 +62,8 @@ def parse():
                     help="repetitions of the search in the other form (0: skip)")
     ap.add_argument("--clip-reps", type=int, default=5,
                     help="repetitions of the clipping search at s* (0: skip)")
+    ap.add_argument("--variant-reps", type=int, default=2,
+                    help="repetitions of the zero-point / group-64 search, pack and W4A16")
     ap.add_argument("--shared-reps", type=int, default=3,
                     help="repetitions of the shared q/k/v search and the fold (0: skip)")
     ap.add_argument("--mode", choices=("bench", "traffic"), default="bench",
@@ -154,15 +158,15 @@ def log(*a):
 
 
 # ---------------------------------------------------------------------------------------------
-def w4a16_sweep(awq, torch):
-    """Time W4A16 over rotated weight copies with HIP events. `us` is the GPU time per call:
-    one pass over every copy is captured in a HIP graph and replayed (the result of a replay is
-    checked against the eager calls), so the host's launch rate does not enter; `us_eager` is the
-    same pass issued call by call from Python."""
+def w4a16_time(awq, torch, n, k, ms, group=128, zero_point=False):
+    """Time W4A16 at the batch sizes `ms` on an [n, k] weight over rotated copies with HIP events.
+    `us` is the GPU time per call: one pass over every copy is captured in a HIP graph and
+    replayed (the result of a replay is checked against the eager calls), so the host's launch
+    rate does not enter; `us_eager` is the same pass issued call by call from Python."""
     import numpy as np
     import workloads
-    out = []
     st = torch.cuda.current_stream()
+    out = []
 
     def elapsed_us(fn, reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -174,52 +178,66 @@ def w4a16_sweep(awq, torch):
         e1.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps
 
-    for (n, k) in ((4096, 4096), (11008, 4096)):
-        qw, sc, s = workloads.w4a16_random_artifacts(n, k, config=4)
-        wbytes = qw.nbytes + sc.nbytes
-        copies = max(4, int(600e6 // wbytes) + 1)      # > 2 x the 256 MB Infinity Cache
-        qws = [torch.from_numpy(qw.view(np.int32)).cuda() for _ in range(copies)]
-        scs = [torch.from_numpy(sc).cuda() for _ in range(copies)]
-        s_d = torch.from_numpy(s).cuda()
-        for m in (1, 4, 16, 64, 512):
-            A = torch.from_numpy(workloads.w4a16_activations(m, k, config=4)).cuda()
-            Y = torch.empty((m, n), dtype=torch.float16, device="cuda")
+    qw, sc, s = workloads.w4a16_random_artifacts(n, k, group=group, config=4)
+    zs = workloads.w4a16_random_zeros(n, k, group=group, config=4) if zero_point else None
+    wbytes = qw.nbytes + sc.nbytes + (zs.nbytes if zs is not None else 0)
+    copies = max(4, int(600e6 // wbytes) + 1)           # > 2 x the 256 MB Infinity Cache
+    qws = [torch.from_numpy(qw.view(np.int32)).cuda() for _ in range(copies)]
+    scs = [torch.from_numpy(sc).cuda() for _ in range(copies)]
+    zds = [torch.from_numpy(zs).cuda() for _ in range(copies)] if zs is not None else None
+    s_d = torch.from_numpy(s).cuda()
+    for m in ms:
+        A = torch.from_numpy(workloads.w4a16_activations(m, k, config=4)).cuda()
+        Y = torch.empty((m, n), dtype=torch.float16, device="cuda")
 
-            def one_pass():
-                for i in range(copies):
-                    awq.w4a16_gemm(A, qws[i], scs[i], s_d, out=Y)
-            one_pass()                                  # warm-up
-            torch.cuda.synchronize()
-            y_eager = Y.clone()
-            us_eager = elapsed_us(one_pass, 2) / copies
-            graph = torch.cuda.CUDAGraph()
-            side = torch.cuda.Stream()
-            side.wait_stream(st)
-            with torch.cuda.stream(side):
+        def one_pass():
+            for i in range(copies):
+                awq.w4a16_gemm(A, qws[i], scs[i], s_d, group=group, out=Y,
+                               zeros=zds[i] if zds is not None else None)
+        one_pass()                                      # warm-up
+        torch.cuda.synchronize()
+        y_eager = Y.clone()
+        us_eager = elapsed_us(one_pass, 2) / copies
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(st)
+        with torch.cuda.stream(side):
+            one_pass()
+            side.synchronize()
+            with torch.cuda.graph(graph, stream=side):
                 one_pass()
-                side.synchronize()
-                with torch.cuda.graph(graph, stream=side):
-                    one_pass()
-            torch.cuda.synchronize()
-            Y.zero_()
-            graph.replay()
-            torch.cuda.synchronize()
-            if not torch.equal(Y, y_eager):
-                raise RuntimeError(f"W4A16 graph replay differs from the eager result (M={m})")
-            us = elapsed_us(graph.replay, 3) / copies
-            nbytes = n * k // 2 + n * (k // 128) * 2 + k * 2 + m * k * 2 + m * n * 2
-            flops = 2.0 * m * n * k
-            rec = {"n": n, "k": k, "m": m, "us": round(us, 3), "us_eager": round(us_eager, 3),
-                   "bytes": nbytes, "gbs": round(nbytes / us / 1e3, 1),
-                   "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
-                   "tflops": round(flops / us / 1e6, 2)}
-            if m >= 512:
-                rec["mfma_frac"] = round(flops / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4)
-            out.append(rec)
-            log("w4a16", rec)
-            del graph
-        del qws, scs
-        torch.cuda.empty_cache()
+        torch.cuda.synchronize()
+        Y.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(Y, y_eager):
+            raise RuntimeError(f"W4A16 graph replay differs from the eager result (M={m})")
+        us = elapsed_us(graph.replay, 3) / copies
+        nbytes = (n * k // 2 + n * (k // group) * 2 + (n * (k // group) if zero_point else 0) +
+                  k * 2 + m * k * 2 + m * n * 2)
+        flops = 2.0 * m * n * k
+        rec = {"n": n, "k": k, "m": m, "us": round(us, 3), "us_eager": round(us_eager, 3),
+               "bytes": nbytes, "gbs": round(nbytes / us / 1e3, 1),
+               "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+               "tflops": round(flops / us / 1e6, 2)}
+        if group != 128 or zero_point:
+            rec.update({"group": group, "zero_point": zero_point})
+        if m >= 512:
+            rec["mfma_frac"] = round(flops / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4)
+        out.append(rec)
+        log("w4a16", rec)
+        del graph
+    del qws, scs, zds
+    torch.cuda.empty_cache()
+    return out
+
+
+def w4a16_sweep(awq, torch):
+    """The symmetric group-128 kernel at the batch sizes 1, 4, 16, 64, 512 for 4096x4096 and
+    11008x4096."""
+    out = []
+    for (n, k) in ((4096, 4096), (11008, 4096)):
+        out += w4a16_time(awq, torch, n, k, (1, 4, 16, 64, 512))
     return out
 
 
@@ -453,6 +471,38 @@ def main():
         log("shared q/k/v search", shared_rec)
         del Wk, Wv, rs
 
+    # zero-point codes and groups of 64: the search, the pack and W4A16 in those forms
+    variants_rec = None
+    if args.variant_reps > 0:
+        variants_rec = []
+        for (grp, zp) in ((64, False), (128, True), (64, True)):
+            vcfg = awq.AwqConfig(bits=4, group=grp, n_grid=N_GRID, form=args.form,
+                                 zero_point=zp)
+            sx_v, _ = awq.act_stats(X, workspace=ws_stats)
+            runs, tpack = [], []
+            for r in range(args.variant_reps + 1):      # the first run is a warm-up
+                prof = {}
+                rv = awq.search_layer(W, X, sx_v, vcfg, workspace=ws_search, stage_ms=prof)
+                p0, p1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+                p0.record(st)
+                awq.pack_int4(W, rv.s_best, vcfg)
+                p1.record(st)
+                p1.synchronize()
+                if r:
+                    runs.append(prof)
+                    tpack.append(p0.elapsed_time(p1))
+            vst = {k: statistics.mean(rr[k] for rr in runs) for k in runs[0]}
+            rec = {"group": grp, "zero_point": zp, "form": args.form,
+                   "search_ms": round(sum(vst.values()), 3),
+                   "quantize_stack_ms": round(vst["quantize_stack"], 4),
+                   "loss_ms": round(vst["loss"], 4),
+                   "pack_ms": round(statistics.mean(tpack), 4),
+                   "alpha_star": int(rv.best.item())}
+            log("variant", rec)
+            rec["w4a16"] = [] if args.no_w4a16_sweep else \
+                w4a16_time(awq, torch, N_, K_, (1, 512), group=grp, zero_point=zp)
+            variants_rec.append(rec)
+
     other_form = None
     if args.other_form_reps > 0:
         oform = "direct" if args.form == "gram" else "gram"
@@ -509,6 +559,7 @@ def main():
         "other_form": other_form,
         "clip_search": clip_rec,
         "shared_qkv": shared_rec,
+        "quant_variants": variants_rec,
         "hbm_stages": other,
         "w4a16": w4,
         "alpha_star": best,
