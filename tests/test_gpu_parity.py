@@ -893,6 +893,32 @@ def test_clip_search_group_and_zero_point(awq, group, zp):
     say(f"same ratio as the oracle in {100 * (j_g == orc['best']).mean():.2f}% of (row, group)")
 
 
+@pytest.mark.parametrize("group,zp", QUANT_VARIANTS, ids=QV_IDS)
+def test_clip_search_gram_group_and_zero_point(awq, group, zp):
+    """The clipping search after a Gram-form search, with groups of 64 and zero-point codes."""
+    W, X = _lognormal_layer(130 + group, 200, 384, 600)
+    say("clip search after the search", "group", group, "zero point", zp)
+    cfg = awq.AwqConfig(group=group, zero_point=zp, form="gram")
+    Wt, Xt = dev(W), dev(X)
+    sx, flags = awq.act_stats(Xt)
+    ws = torch.empty(awq.search_workspace_bytes(600, 200, 384, Xt.dtype, cfg), dtype=torch.uint8,
+                     device="cuda")
+    res = awq.search_layer(Wt, Xt, sx, cfg, flags=flags, workspace=ws)
+    r = awq.clip_search_gram(Wt, res.s_best, ws, cfg, with_err=True, flags=flags)
+    orc = oracle.clip_search(W, X, host(res.s_best), group=group, zero_point=zp)
+    err_g = host(r.err).astype(np.float64)
+    err_o = orc["err"]
+    scale = err_o.max(axis=0, keepdims=True)
+    rel = np.abs(err_g - err_o) / np.maximum(scale, 1e-300)
+    say(f"max err rel {rel.max():.2e}")
+    assert rel.max() <= CLIP_ERR_RTOL
+    grid = oracle.clip_grid(11, 0.5)
+    j_g = np.searchsorted(-grid, -host(r.clip))
+    rows, groups = np.indices(j_g.shape)
+    assert (err_o[j_g, rows, groups] <= err_o.min(axis=0) * (1 + CLIP_BAND) + 1e-12 * scale[0]).all()
+    assert int(host(flags)[0]) == 0
+
+
 W4A16_ZP_CASES = [(g, zp, n, k, m) for (g, zp) in QUANT_VARIANTS for (n, k, m) in
                   ((384, 512, 1), (384, 512, 16), (256, 4096, 40), (320, 512, 100))] + \
                  [(64, False, 4096, 4096, 1), (128, True, 11008, 4096, 4)]
