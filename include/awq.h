@@ -215,6 +215,28 @@ awq_status awq_search_layer_profiled(const void* W, awq_dtype wdt, int64_t N, in
                                      hipStream_t stream, float* stage_ms);
 
 /* ------------------------------------------------------------------------------------------
+ * awq_stats_search_layer -- awq_act_stats followed by awq_search_layer on the same X, in one
+ *   call ([notes] 方法: s_X is a statistic of the layer input, the grid search uses it).
+ * sx     out, fp32 [K]: what awq_act_stats writes for this X, bit for bit (fp64 sums of 256
+ *        tokens per chunk, reduced by the same final pass; with fp16 X these sums are exact,
+ *        so their order does not matter, unless AWQ_FLAG_STATS_INEXACT is raised); the search
+ *        then uses it.
+ * In the Gram form with fp16 X the column sums are taken by the pass that transposes X, so X
+ *   is read once for both; otherwise the statistics pass runs first.
+ * stage_ms  NULL: asynchronous, like awq_search_layer. Non-NULL: host array of
+ *        AWQ_SEARCH_STAGES floats filled as by awq_search_layer_profiled (this call then BLOCKS
+ *        until the stream has finished it), the statistics counted in the X preparation stage.
+ * ws     device workspace of at least awq_search_workspace_bytes(M, N, K, xdt, cfg) bytes.
+ * flags  in/out: those of awq_act_stats and of awq_search_layer.
+ * Errors: as awq_search_layer (sx is an output here); AWQ_ERR_SHAPE also when M > 256 * 65535.
+ * ---------------------------------------------------------------------------------------- */
+awq_status awq_stats_search_layer(const void* W, awq_dtype wdt, int64_t N, int64_t K,
+                                  const void* X, awq_dtype xdt, int64_t M, const awq_cfg* cfg,
+                                  float* sx, double* losses, int32_t* best, float* s_best,
+                                  uint32_t* flags, void* ws, size_t ws_bytes,
+                                  hipStream_t stream, float* stage_ms);
+
+/* ------------------------------------------------------------------------------------------
  * awq_clip_search -- clipping of the scaled-up weights, one of the further optimisations listed
  * in [notes] 方法 (the page gives no details; the reading below is this library's).
  * For every output row n and group g of input channels, each ratio r_j of the grid in

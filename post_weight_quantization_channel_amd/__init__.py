@@ -5,11 +5,11 @@ The engine is the HIP library libawq.so (C ABI in include/awq.h); this package h
 """
 from .api import (AwqConfig, ClipResult, PackResult, SearchResult, act_stats,
                   act_stats_workspace_bytes, clip_search, clip_search_gram, clip_workspace_bytes,
-                  fold_scale,
-                  pack_int4, search_layer, search_layers, search_workspace_bytes, w4a16_gemm)
+                  fold_scale, pack_int4, search_layer, search_layers, search_workspace_bytes,
+                  stats_search_layer, w4a16_gemm)
 from ._lib import AwqError
 
 __all__ = ["AwqConfig", "AwqError", "ClipResult", "PackResult", "SearchResult", "act_stats",
            "act_stats_workspace_bytes", "clip_search", "clip_search_gram", "clip_workspace_bytes",
-           "fold_scale",
-           "pack_int4", "search_layer", "search_layers", "search_workspace_bytes", "w4a16_gemm"]
+           "fold_scale", "pack_int4", "search_layer", "search_layers", "search_workspace_bytes",
+           "stats_search_layer", "w4a16_gemm"]

@@ -57,6 +57,9 @@ SIGNATURES = {
     "awq_search_layer_profiled": (_E, [_P, _E, _I64, _I64, _P, _E, _I64, _P,
                                        ctypes.POINTER(AwqCfg), _P, _P, _P, _P, _P, _SZ, _P,
                                        ctypes.POINTER(ctypes.c_float)]),
+    "awq_stats_search_layer": (_E, [_P, _E, _I64, _I64, _P, _E, _I64, ctypes.POINTER(AwqCfg),
+                                    _P, _P, _P, _P, _P, _P, _SZ, _P,
+                                    ctypes.POINTER(ctypes.c_float)]),
     "awq_search_layers": (_E, [ctypes.POINTER(_P), ctypes.POINTER(_I64), _I32, _E, _I64, _P, _E,
                                _I64, _P, ctypes.POINTER(AwqCfg), _P, _P, _P, _P, _P, _SZ, _P]),
     "awq_fold_scale": (_E, [_P, _E, _I64, _I64, _I64, _P, _I32, _P, _P]),

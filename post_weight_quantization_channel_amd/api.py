@@ -143,6 +143,41 @@ def search_layer(W: torch.Tensor, X: torch.Tensor, sx: torch.Tensor,
     return SearchResult(losses, best, s_best, flags)
 
 
+def stats_search_layer(W: torch.Tensor, X: torch.Tensor, cfg: AwqConfig = AwqConfig(),
+                       flags: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                       stage_ms: dict | None = None) -> tuple[torch.Tensor, SearchResult]:
+    """act_stats and search_layer in one call: returns (s_X, result), s_X identical to what
+    act_stats gives for this X. In the Gram form with fp16 X the column sums come out of the
+    pass that transposes X (X is read once for both). `stage_ms` as in search_layer, with the
+    statistics counted in the X preparation stage."""
+    lib = _lib.load()
+    for t, nm in ((W, "W"), (X, "X")):
+        _dev(t, nm)
+    N, K = W.shape
+    M = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError("shape mismatch: W [N,K], X [M,K]")
+    c = cfg.c()
+    flags = _flags(W.device, flags)
+    nbytes = lib.awq_search_workspace_bytes(M, N, K, _DT[X.dtype], c)
+    if nbytes == 0:
+        raise ValueError("invalid shape or config for the search")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    sx = torch.empty(K, dtype=torch.float32, device=W.device)
+    losses = torch.empty(cfg.n_grid, dtype=torch.float64, device=W.device)
+    best = torch.empty(1, dtype=torch.int32, device=W.device)
+    s_best = torch.empty(K, dtype=torch.float32, device=W.device)
+    ms = (ctypes.c_float * len(_lib.SEARCH_STAGES))() if stage_ms is not None else None
+    check("awq_stats_search_layer", lib.awq_stats_search_layer(
+        W.data_ptr(), _DT[W.dtype], N, K, X.data_ptr(), _DT[X.dtype], M, c, sx.data_ptr(),
+        losses.data_ptr(), best.data_ptr(), s_best.data_ptr(), flags.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), _stream(W), ms))
+    if stage_ms is not None:
+        stage_ms.update({k: float(v) for k, v in zip(_lib.SEARCH_STAGES, ms)})
+    return sx, SearchResult(losses, best, s_best, flags)
+
+
 @dataclasses.dataclass
 class ClipResult:
     clip: torch.Tensor               # fp32 [N, K/group]: the chosen ratios

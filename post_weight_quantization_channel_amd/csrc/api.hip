@@ -38,6 +38,8 @@ constexpr int64_t kMaxGramMp = (int64_t(1) << 23) - awq::kGramMAlign;
 struct SearchLayout {
   size_t ctrl, S, X16, E, partials, total;
   size_t d64, d32, B, Xt, Hpart;   // Gram form only (Xt and Hpart share memory with E)
+  size_t stats;                    // chunk partials of s_X when the search takes it (in Hpart
+                                   // or in E: both are written only after s_X is final)
   int64_t tiles_per_alpha;
   awq::GramPlan plan;
 };
@@ -55,6 +57,7 @@ SearchLayout search_layout(int64_t M, int64_t N, int64_t K, awq_dtype xdt, int n
   L.S = off;
   off += align_up((size_t)n_grid * (size_t)K * sizeof(float));
   const size_t e_bytes = align_up((size_t)n_grid * (size_t)N * (size_t)K * 2);
+  const size_t stats_bytes = align_up((size_t)awq::stats_chunks(M) * (size_t)K * sizeof(double));
   if (form == AWQ_FORM_GRAM) {
     L.plan = awq::gram_plan(M, K);
     L.tiles_per_alpha = tilesN * L.plan.t;
@@ -67,10 +70,12 @@ SearchLayout search_layout(int64_t M, int64_t N, int64_t K, awq_dtype xdt, int n
     L.partials = off;
     off += align_up((size_t)n_grid * (size_t)L.tiles_per_alpha * sizeof(double));
     const size_t xt_bytes = align_up((size_t)K * (size_t)L.plan.Mp * 2);
-    const size_t h_bytes = align_up((size_t)L.plan.S * (size_t)L.plan.T *
-                                    (size_t)(awq::kLossBM * awq::kLossBN) * sizeof(float));
+    size_t h_bytes = align_up((size_t)L.plan.S * (size_t)L.plan.T *
+                              (size_t)(awq::kLossBM * awq::kLossBN) * sizeof(float));
+    if (h_bytes < stats_bytes) h_bytes = stats_bytes;
     L.Xt = off;
     L.Hpart = off + xt_bytes;
+    L.stats = L.Hpart;
     L.E = off;
     off += (xt_bytes + h_bytes > e_bytes) ? xt_bytes + h_bytes : e_bytes;
   } else {
@@ -79,7 +84,8 @@ SearchLayout search_layout(int64_t M, int64_t N, int64_t K, awq_dtype xdt, int n
     L.X16 = off;
     if (xdt != AWQ_F16) off += align_up((size_t)M * (size_t)K * 2);
     L.E = off;
-    off += e_bytes;
+    L.stats = off;
+    off += (e_bytes > stats_bytes) ? e_bytes : stats_bytes;
     L.partials = off;
     off += align_up((size_t)n_grid * (size_t)L.tiles_per_alpha * sizeof(double));
   }
@@ -106,7 +112,7 @@ const char* awq_status_string(awq_status status) {
   return "unknown awq_status";
 }
 
-int32_t awq_version(void) { return 10500; }
+int32_t awq_version(void) { return 10600; }
 
 size_t awq_act_stats_workspace_bytes(int64_t M, int64_t K) {
   if (M < 1 || K < 1 || M > kMaxDim || K > kMaxDim) return 0;
@@ -153,16 +159,18 @@ size_t awq_search_workspace_bytes(int64_t M, int64_t N, int64_t K, awq_dtype xdt
 namespace {
 
 // Shared body of the search calls: the weights Ws[0..n_w) (N_l rows each, all reading the same
-// X) are searched together, their rows stacked in one error stack. With `ev` non-null, event
-// ev[j] is recorded before stage j and ev[AWQ_SEARCH_STAGES] after the last stage.
+// X) are searched together, their rows stacked in one error stack. With sx_out non-null (and sx
+// null), s_X is computed first into sx_out and used; in the Gram form with fp16 X it comes out
+// of the transpose pass. With `ev` non-null (2 * AWQ_SEARCH_STAGES events), stage j is bracketed
+// by ev[2j] and ev[2j + 1].
 constexpr int kMaxSharedWeights = 64;
 
 awq_status search_impl(const void* const* Ws, const int64_t* Ns, int n_w, awq_dtype wdt,
                        int64_t K, const void* X, awq_dtype xdt, int64_t M, const float* sx,
-                       const awq_cfg* cfg, double* losses, int32_t* best, float* s_best,
-                       uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream,
-                       hipEvent_t* ev) {
-  if (!Ws || !Ns || !X || !sx || !cfg || !losses || !best || !s_best || !flags)
+                       float* sx_out, const awq_cfg* cfg, double* losses, int32_t* best,
+                       float* s_best, uint32_t* flags, void* ws, size_t ws_bytes,
+                       hipStream_t stream, hipEvent_t* ev) {
+  if (!Ws || !Ns || !X || !(sx || sx_out) || !cfg || !losses || !best || !s_best || !flags)
     return AWQ_ERR_NULL;
   if (n_w < 1 || n_w > kMaxSharedWeights) return AWQ_ERR_SHAPE;
   int64_t N = 0;
@@ -177,6 +185,7 @@ awq_status search_impl(const void* const* Ws, const int64_t* Ns, int n_w, awq_dt
   if (!valid_dtype(xdt)) return AWQ_ERR_DTYPE;
   // K <= 2^22 keeps the loss kernel's 32-bit buffer offsets (256 rows x 2K bytes) in range
   if (!search_shape_ok(M, N, K, cfg) || !aligned16(X)) return AWQ_ERR_SHAPE;
+  if (sx_out && awq::stats_chunks(M) > 65535) return AWQ_ERR_SHAPE;
   const SearchLayout L = search_layout(M, N, K, xdt, cfg->n_grid, cfg->form);
   if ((int64_t)L.tiles_per_alpha * cfg->n_grid > (int64_t(1) << 31) - 1) return AWQ_ERR_SHAPE;
   if (!ws || ws_bytes < L.total || !aligned16(ws)) return AWQ_ERR_WORKSPACE;
@@ -186,42 +195,71 @@ awq_status search_impl(const void* const* Ws, const int64_t* Ns, int n_w, awq_dt
   auto* S = reinterpret_cast<float*>(base + L.S);
   auto* E = reinterpret_cast<uint16_t*>(base + L.E);
   auto* partials = reinterpret_cast<double*>(base + L.partials);
+  auto* stats = reinterpret_cast<double*>(base + L.stats);
+  auto* Xt = reinterpret_cast<uint16_t*>(base + L.Xt);
   const bool gram = cfg->form == AWQ_FORM_GRAM;
   const float* dcol = gram ? reinterpret_cast<const float*>(base + L.d32) : nullptr;
   const uint16_t* B = reinterpret_cast<const uint16_t*>(base + L.B);
   const uint16_t* X16 = static_cast<const uint16_t*>(X);
 
   hipError_t e = hipSuccess;
-  auto mark = [&](int j) {
-    if (ev && e == hipSuccess) e = hipEventRecord(ev[j], stream);
+  auto mark = [&](int idx) {
+    if (ev && e == hipSuccess) e = hipEventRecord(ev[idx], stream);
   };
-  mark(0);
+  // X preparation: the transpose (Gram) or the fp16 copy of a non-fp16 X (direct), preceded by
+  // the statistics when the search takes them
+  auto x_prep = [&]() {
+    mark(2 * 1);
+    if (gram) {
+      const bool fused = sx_out && xdt == AWQ_F16;
+      if (sx_out && !fused && e == hipSuccess)
+        e = awq::launch_stats(X, (int)xdt, M, K, K, sx_out, flags, stats, stream);
+      if (e == hipSuccess)
+        e = awq::launch_gram_transpose(X, (int)xdt, M, K, L.plan.Mp, Xt,
+                                       fused ? stats : nullptr, flags, stream);
+      if (fused && e == hipSuccess)
+        e = awq::launch_stats_final(stats, awq::stats_chunks(M), M, K, (int)xdt, sx_out, flags,
+                                    stream);
+    } else {
+      if (sx_out && e == hipSuccess)
+        e = awq::launch_stats(X, (int)xdt, M, K, K, sx_out, flags, stats, stream);
+      if (e == hipSuccess && xdt != AWQ_F16) {
+        auto* x16 = reinterpret_cast<uint16_t*>(base + L.X16);
+        e = awq::launch_x_to_f16(X, (int)xdt, M * K, x16, flags, stream);
+        X16 = x16;
+      }
+    }
+    mark(2 * 1 + 1);
+  };
+  // s_X must be final before the scale table; otherwise X is prepared after it
+  if (sx_out) {
+    x_prep();
+    sx = sx_out;
+  }
+  mark(2 * 0);
   if (e == hipSuccess)
     e = awq::launch_search_prep(sx, (int)K, cfg->n_grid, cfg->s_floor, S, ctrl, stream);
-  mark(1);
+  mark(2 * 0 + 1);
+  if (!sx_out) x_prep();
+  // X^T X (stage 2), then d and the correlation operand (stage 3)
+  mark(2 * 2);
   if (gram) {
-    // records ev[2] after the transpose and ev[3] after the X^T X partials
     if (e == hipSuccess)
-      e = awq::launch_gram_prepare(X, (int)xdt, M, K, L.plan,
-                                   reinterpret_cast<uint16_t*>(base + L.Xt),
-                                   reinterpret_cast<float*>(base + L.Hpart),
-                                   reinterpret_cast<double*>(base + L.d64),
-                                   reinterpret_cast<float*>(base + L.d32),
-                                   reinterpret_cast<uint16_t*>(base + L.B), &ctrl->gram_k,
-                                   flags, stream, ev ? ev + 2 : nullptr);
+      e = awq::launch_gram_hmat(Xt, K, L.plan, reinterpret_cast<float*>(base + L.Hpart),
+                                reinterpret_cast<double*>(base + L.d64),
+                                reinterpret_cast<float*>(base + L.d32),
+                                reinterpret_cast<uint16_t*>(base + L.B), &ctrl->gram_k, stream,
+                                ev ? ev[2 * 2 + 1] : nullptr, ev ? ev[2 * 3] : nullptr);
   } else {
-    if (e == hipSuccess && xdt != AWQ_F16) {
-      auto* x16 = reinterpret_cast<uint16_t*>(base + L.X16);
-      e = awq::launch_x_to_f16(X, (int)xdt, M * K, x16, flags, stream);
-      X16 = x16;
-    }
-    mark(2);
-    mark(3);
+    mark(2 * 2 + 1);
+    mark(2 * 3);
   }
-  mark(4);
+  mark(2 * 3 + 1);
+  mark(2 * 4);
   for (int l = 0; l < n_w && e == hipSuccess; ++l)
     e = awq::launch_absmax(Ws[l], (int)wdt, Ns[l], K, dcol, ctrl, flags, stream);
-  mark(5);
+  mark(2 * 4 + 1);
+  mark(2 * 5);
   int64_t row = 0;
   for (int l = 0; l < n_w && e == hipSuccess; ++l) {
     e = awq::launch_quantize_stack(Ws[l], (int)wdt, Ns[l], K, S, cfg->n_grid, cfg->bits,
@@ -229,19 +267,41 @@ awq_status search_impl(const void* const* Ws, const int64_t* Ns, int n_w, awq_dt
                                    flags, stream);
     row += Ns[l];
   }
-  mark(6);
+  mark(2 * 5 + 1);
+  mark(2 * 6);
   if (e == hipSuccess) {
     if (gram)
       e = awq::launch_gram_loss(E, N, K, B, cfg->n_grid, partials, stream);
     else
       e = awq::launch_lossgemm(X16, M, K, E, N, cfg->n_grid, partials, stream);
   }
-  mark(7);
+  mark(2 * 6 + 1);
+  mark(2 * 7);
   if (e == hipSuccess)
     e = awq::launch_finalize(partials, L.tiles_per_alpha, cfg->n_grid, M, N, K, S, ctrl, losses,
                              best, s_best, flags, stream);
-  mark(8);
+  mark(2 * 7 + 1);
   return hip_status(e);
+}
+
+// Runs search_impl with 2 * AWQ_SEARCH_STAGES events and reads the stage durations back.
+extern "C++" template <class F>
+awq_status run_profiled(float* stage_ms, F&& run) {
+  hipEvent_t ev[2 * AWQ_SEARCH_STAGES] = {};
+  int made = 0;
+  for (; made < 2 * AWQ_SEARCH_STAGES; ++made)
+    if (hipEventCreate(&ev[made]) != hipSuccess) break;
+  awq_status st = AWQ_ERR_HIP;
+  if (made == 2 * AWQ_SEARCH_STAGES) {
+    st = run(ev);
+    if (st == AWQ_OK && hipEventSynchronize(ev[2 * AWQ_SEARCH_STAGES - 1]) != hipSuccess)
+      st = AWQ_ERR_HIP;
+    for (int j = 0; st == AWQ_OK && j < AWQ_SEARCH_STAGES; ++j)
+      if (hipEventElapsedTime(&stage_ms[j], ev[2 * j], ev[2 * j + 1]) != hipSuccess)
+        st = AWQ_ERR_HIP;
+  }
+  for (int j = 0; j < made; ++j) (void)hipEventDestroy(ev[j]);
+  return st;
 }
 
 }  // namespace
@@ -250,9 +310,9 @@ awq_status awq_search_layer(const void* W, awq_dtype wdt, int64_t N, int64_t K,
                             const void* X, awq_dtype xdt, int64_t M, const float* sx,
                             const awq_cfg* cfg, double* losses, int32_t* best, float* s_best,
                             uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!W) return AWQ_ERR_NULL;
-  return search_impl(&W, &N, 1, wdt, K, X, xdt, M, sx, cfg, losses, best, s_best, flags, ws,
-                     ws_bytes, stream, nullptr);
+  if (!W || !sx) return AWQ_ERR_NULL;
+  return search_impl(&W, &N, 1, wdt, K, X, xdt, M, sx, nullptr, cfg, losses, best, s_best,
+                     flags, ws, ws_bytes, stream, nullptr);
 }
 
 awq_status awq_search_layers(const void* const* W, const int64_t* N, int32_t n_w,
@@ -260,8 +320,9 @@ awq_status awq_search_layers(const void* const* W, const int64_t* N, int32_t n_w
                              const float* sx, const awq_cfg* cfg, double* losses,
                              int32_t* best, float* s_best, uint32_t* flags, void* ws,
                              size_t ws_bytes, hipStream_t stream) {
-  return search_impl(W, N, n_w, wdt, K, X, xdt, M, sx, cfg, losses, best, s_best, flags, ws,
-                     ws_bytes, stream, nullptr);
+  if (!sx) return AWQ_ERR_NULL;
+  return search_impl(W, N, n_w, wdt, K, X, xdt, M, sx, nullptr, cfg, losses, best, s_best,
+                     flags, ws, ws_bytes, stream, nullptr);
 }
 
 awq_status awq_search_layer_profiled(const void* W, awq_dtype wdt, int64_t N, int64_t K,
@@ -269,22 +330,26 @@ awq_status awq_search_layer_profiled(const void* W, awq_dtype wdt, int64_t N, in
                                      const awq_cfg* cfg, double* losses, int32_t* best,
                                      float* s_best, uint32_t* flags, void* ws, size_t ws_bytes,
                                      hipStream_t stream, float* stage_ms) {
-  if (!stage_ms) return AWQ_ERR_NULL;
-  hipEvent_t ev[AWQ_SEARCH_STAGES + 1] = {};
-  int made = 0;
-  for (; made <= AWQ_SEARCH_STAGES; ++made)
-    if (hipEventCreate(&ev[made]) != hipSuccess) break;
-  awq_status st = AWQ_ERR_HIP;
-  if (made == AWQ_SEARCH_STAGES + 1) {
-    st = W ? search_impl(&W, &N, 1, wdt, K, X, xdt, M, sx, cfg, losses, best, s_best, flags,
-                         ws, ws_bytes, stream, ev)
-           : AWQ_ERR_NULL;
-    if (st == AWQ_OK && hipEventSynchronize(ev[AWQ_SEARCH_STAGES]) != hipSuccess) st = AWQ_ERR_HIP;
-    for (int j = 0; st == AWQ_OK && j < AWQ_SEARCH_STAGES; ++j)
-      if (hipEventElapsedTime(&stage_ms[j], ev[j], ev[j + 1]) != hipSuccess) st = AWQ_ERR_HIP;
-  }
-  for (int j = 0; j < made; ++j) (void)hipEventDestroy(ev[j]);
-  return st;
+  if (!stage_ms || !W || !sx) return AWQ_ERR_NULL;
+  return run_profiled(stage_ms, [&](hipEvent_t* ev) {
+    return search_impl(&W, &N, 1, wdt, K, X, xdt, M, sx, nullptr, cfg, losses, best, s_best,
+                       flags, ws, ws_bytes, stream, ev);
+  });
+}
+
+awq_status awq_stats_search_layer(const void* W, awq_dtype wdt, int64_t N, int64_t K,
+                                  const void* X, awq_dtype xdt, int64_t M, const awq_cfg* cfg,
+                                  float* sx, double* losses, int32_t* best, float* s_best,
+                                  uint32_t* flags, void* ws, size_t ws_bytes,
+                                  hipStream_t stream, float* stage_ms) {
+  if (!W || !sx) return AWQ_ERR_NULL;
+  if (!stage_ms)
+    return search_impl(&W, &N, 1, wdt, K, X, xdt, M, nullptr, sx, cfg, losses, best, s_best,
+                       flags, ws, ws_bytes, stream, nullptr);
+  return run_profiled(stage_ms, [&](hipEvent_t* ev) {
+    return search_impl(&W, &N, 1, wdt, K, X, xdt, M, nullptr, sx, cfg, losses, best, s_best,
+                       flags, ws, ws_bytes, stream, ev);
+  });
 }
 
 awq_status awq_pack_int4(const void* W, awq_dtype wdt, int64_t N, int64_t K, const float* s,

@@ -60,51 +60,92 @@ GramPlan gram_plan(int64_t M, int64_t K, bool diag) {
 // permutes, 8 rows of 16 bytes out. Lane l of a wave takes channel block l % 8 and token block
 // l / 8, so a load instruction reads 8 runs of 128 contiguous bytes (one per token row) and a
 // store instruction writes 8 runs of 128 contiguous bytes (one per channel row of Xt).
-template <int DT>
+//
+// With STATS (fp16 X only), the same pass also takes the column sums of |x| that s_X needs:
+// each lane adds its 8 rows per channel in fp64, the 8 token blocks of a wave are added by lane
+// shuffles and the 4 waves through LDS, and the workgroup writes the sums of its 256 tokens to
+// stats[blockIdx.y][k] -- the chunk partials of the statistics pass, 256 tokens per chunk. For
+// fp16 every partial sum is exact (all |x| are multiples of 2^-24 and the final pass flags sums
+// of 2^29 or more), so the order of these additions does not change s_X.
+template <int DT, bool STATS>
 __global__ __launch_bounds__(256) void gram_transpose_kernel(const void* __restrict__ X,
                                                              int64_t M, int64_t K, int64_t Mp,
                                                              uint16_t* __restrict__ Xt,
+                                                             double* __restrict__ stats,
                                                              uint32_t* __restrict__ flags) {
+  static_assert(!STATS || DT == kF16, "the fused statistics take fp16 X");
   constexpr int ES = (DT == kF32) ? 4 : 2;
+  __shared__ double wcol[STATS ? 4 : 1][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t k0 = (int64_t)blockIdx.x * 64 + (lane & 7) * 8;
   const int64_t m0 = (int64_t)blockIdx.y * 256 + wave * 64 + (lane >> 3) * 8;
-  if (m0 >= Mp) return;   // Mp is a multiple of 64: whole waves leave together
-  bool over = false;
-  uint32_t v[8][4];       // v[r][w]: channels 2w, 2w+1 of token row m0 + r
+  // Mp is a multiple of 64: whole waves are past it together
+  if (!STATS && m0 >= Mp) return;
+  double cs[8];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int64_t m = m0 + r;
-    if (m < M) {
-      if (DT == kF16) {
-        const uint4 u = *reinterpret_cast<const uint4*>(
-            reinterpret_cast<const char*>(X) + (m * K + k0) * ES);
-        v[r][0] = u.x; v[r][1] = u.y; v[r][2] = u.z; v[r][3] = u.w;
-      } else {
-        float f[8];
-        load8_f32<DT>(reinterpret_cast<const char*>(X) + (m * K + k0) * ES, f);
+  for (int c = 0; c < 8; ++c) cs[c] = 0.0;
+  if (m0 < Mp) {
+    bool over = false;
+    uint32_t v[8][4];       // v[r][w]: channels 2w, 2w+1 of token row m0 + r
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint16_t lo = f2h(f[2 * w]), hi = f2h(f[2 * w + 1]);
-          over |= ((lo & 0x7C00u) == 0x7C00u) || ((hi & 0x7C00u) == 0x7C00u);
-          v[r][w] = (uint32_t)lo | ((uint32_t)hi << 16);
+    for (int r = 0; r < 8; ++r) {
+      const int64_t m = m0 + r;
+      if (m < M) {
+        if (DT == kF16) {
+          const uint4 u = *reinterpret_cast<const uint4*>(
+              reinterpret_cast<const char*>(X) + (m * K + k0) * ES);
+          v[r][0] = u.x; v[r][1] = u.y; v[r][2] = u.z; v[r][3] = u.w;
+        } else {
+          float f[8];
+          load8_f32<DT>(reinterpret_cast<const char*>(X) + (m * K + k0) * ES, f);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint16_t lo = f2h(f[2 * w]), hi = f2h(f[2 * w + 1]);
+            over |= ((lo & 0x7C00u) == 0x7C00u) || ((hi & 0x7C00u) == 0x7C00u);
+            v[r][w] = (uint32_t)lo | ((uint32_t)hi << 16);
+          }
         }
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) v[r][w] = 0u;
+        for (int w = 0; w < 4; ++w) v[r][w] = 0u;
+      }
+    }
+    if (STATS) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          cs[c] += (double)fabsf(h2f((uint16_t)(v[r][c >> 1] >> (16 * (c & 1)))));
+    }
+    // output row c (channel k0 + c) holds tokens m0..m0+7: word w = (token 2w, token 2w+1)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t o[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(v[2 * w + 1][c >> 1], v[2 * w][c >> 1], sel);
+      *reinterpret_cast<uint4*>(Xt + (k0 + c) * Mp + m0) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    if (DT != kF16) wave_flag(flags, over, kFlagXF16Range);
+  }
+  if (STATS) {
+    // the 8 token blocks of the wave (lane bits 3..5), then the 4 waves
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      cs[c] += __shfl_xor(cs[c], 8);
+      cs[c] += __shfl_xor(cs[c], 16);
+      cs[c] += __shfl_xor(cs[c], 32);
+    }
+    if (lane < 8) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) wcol[wave][lane * 8 + c] = cs[c];
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const double t = ((wcol[0][lane] + wcol[1][lane]) + wcol[2][lane]) + wcol[3][lane];
+      stats[(int64_t)blockIdx.y * K + (int64_t)blockIdx.x * 64 + lane] = t;
     }
   }
-  // output row c (channel k0 + c) holds tokens m0..m0+7: word w = (token 2w, token 2w+1)
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t o[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(v[2 * w + 1][c >> 1], v[2 * w][c >> 1], sel);
-    *reinterpret_cast<uint4*>(Xt + (k0 + c) * Mp + m0) = make_uint4(o[0], o[1], o[2], o[3]);
-  }
-  if (DT != kF16) wave_flag(flags, over, kFlagXF16Range);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -350,34 +391,40 @@ __global__ __launch_bounds__(kloop::kThreads, 1) void gram_loss_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
-hipError_t launch_gram_prepare(const void* X, int xdt, int64_t M, int64_t K, const GramPlan& p,
-                               uint16_t* Xt, float* Hpart, double* d64, float* d32, uint16_t* B,
-                               uint32_t* gram_k, uint32_t* flags, hipStream_t stream,
-                               hipEvent_t* ev) {
-  hipError_t e = hipSuccess;
-  {
-    dim3 grid((unsigned)(K / 64), (unsigned)((p.Mp + 255) / 256));
-    switch (xdt) {
-      case kF16:
-        gram_transpose_kernel<kF16><<<grid, 256, 0, stream>>>(X, M, K, p.Mp, Xt, flags);
-        break;
-      case kBF16:
-        gram_transpose_kernel<kBF16><<<grid, 256, 0, stream>>>(X, M, K, p.Mp, Xt, flags);
-        break;
-      default:
-        gram_transpose_kernel<kF32><<<grid, 256, 0, stream>>>(X, M, K, p.Mp, Xt, flags);
-        break;
-    }
-    e = hipGetLastError();
+hipError_t launch_gram_transpose(const void* X, int xdt, int64_t M, int64_t K, int64_t Mp,
+                                 uint16_t* Xt, double* stats, uint32_t* flags,
+                                 hipStream_t stream) {
+  dim3 grid((unsigned)(K / 64), (unsigned)((Mp + 255) / 256));
+  if (stats) {
+    if (xdt != kF16) return hipErrorInvalidValue;
+    gram_transpose_kernel<kF16, true><<<grid, 256, 0, stream>>>(X, M, K, Mp, Xt, stats, flags);
+    return hipGetLastError();
   }
-  if (e == hipSuccess && ev) e = hipEventRecord(ev[0], stream);
-  if (e == hipSuccess) {
-    gram_gemm_kernel<<<(unsigned)(p.T * p.S), kloop::kThreads, 0, stream>>>(Xt, K, p.Mp, p.t, p.T,
-                                                                            p.chunk, (int)p.diag,
-                                                                            Hpart);
-    e = hipGetLastError();
+  switch (xdt) {
+    case kF16:
+      gram_transpose_kernel<kF16, false><<<grid, 256, 0, stream>>>(X, M, K, Mp, Xt, nullptr, flags);
+      break;
+    case kBF16:
+      gram_transpose_kernel<kBF16, false><<<grid, 256, 0, stream>>>(X, M, K, Mp, Xt, nullptr,
+                                                                     flags);
+      break;
+    default:
+      gram_transpose_kernel<kF32, false><<<grid, 256, 0, stream>>>(X, M, K, Mp, Xt, nullptr,
+                                                                    flags);
+      break;
   }
-  if (e == hipSuccess && ev) e = hipEventRecord(ev[1], stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_gram_hmat(const uint16_t* Xt, int64_t K, const GramPlan& p, float* Hpart,
+                            double* d64, float* d32, uint16_t* B, uint32_t* gram_k,
+                            hipStream_t stream, hipEvent_t ev, hipEvent_t ev2) {
+  gram_gemm_kernel<<<(unsigned)(p.T * p.S), kloop::kThreads, 0, stream>>>(Xt, K, p.Mp, p.t, p.T,
+                                                                          p.chunk, (int)p.diag,
+                                                                          Hpart);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ev) e = hipEventRecord(ev, stream);
+  if (e == hipSuccess && ev2) e = hipEventRecord(ev2, stream);
   if (e == hipSuccess) {
     gram_diag_kernel<<<(unsigned)((K + 255) / 256), 256, 0, stream>>>(Hpart, K, p.t, p.T, p.S,
                                                                       (int)p.diag, d64, d32);
@@ -390,6 +437,18 @@ hipError_t launch_gram_prepare(const void* X, int xdt, int64_t M, int64_t K, con
                                                                               d64, B, gram_k);
     e = hipGetLastError();
   }
+  return e;
+}
+
+hipError_t launch_gram_prepare(const void* X, int xdt, int64_t M, int64_t K, const GramPlan& p,
+                               uint16_t* Xt, float* Hpart, double* d64, float* d32, uint16_t* B,
+                               uint32_t* gram_k, uint32_t* flags, hipStream_t stream,
+                               hipEvent_t* ev) {
+  hipError_t e = launch_gram_transpose(X, xdt, M, K, p.Mp, Xt, nullptr, flags, stream);
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[0], stream);
+  if (e == hipSuccess)
+    e = launch_gram_hmat(Xt, K, p, Hpart, d64, d32, B, gram_k, stream, ev ? ev[1] : nullptr,
+                         nullptr);
   return e;
 }
 

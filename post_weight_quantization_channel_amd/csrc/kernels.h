@@ -11,6 +11,9 @@ namespace awq {
 // ---- activation statistics ----
 constexpr int kStatsRowsPerChunk = 256;
 int64_t stats_chunks(int64_t M);
+// the second pass of launch_stats on chunk partials [chunks][K] (256 rows per chunk)
+hipError_t launch_stats_final(const double* partials, int64_t chunks, int64_t M, int64_t K,
+                              int dtype, float* sx, uint32_t* flags, hipStream_t stream);
 hipError_t launch_stats(const void* X, int dtype, int64_t M, int64_t K, int64_t ldx, float* sx,
                         uint32_t* flags, double* partials, hipStream_t stream);
 
@@ -42,6 +45,15 @@ GramPlan gram_plan(int64_t M, int64_t K, bool diag = false);
 // with plan.diag the t diagonal blocks [t][256][256] (block a: rows and columns 256 a ..).
 // gram_k: nullptr, or where the finish pass records K (the operand is then complete once the
 // stream has passed this call).
+// The two halves of launch_gram_prepare. stats: nullptr, or (fp16 X only) [ceil(M/256)][K] fp64
+// column sums of |x| per 256 tokens, the chunk partials that launch_stats_final reduces.
+hipError_t launch_gram_transpose(const void* X, int xdt, int64_t M, int64_t K, int64_t Mp,
+                                 uint16_t* Xt, double* stats, uint32_t* flags,
+                                 hipStream_t stream);
+// X^T X partials -> ev, ev2 (each if not null) -> d and B
+hipError_t launch_gram_hmat(const uint16_t* Xt, int64_t K, const GramPlan& p, float* Hpart,
+                            double* d64, float* d32, uint16_t* B, uint32_t* gram_k,
+                            hipStream_t stream, hipEvent_t ev, hipEvent_t ev2);
 hipError_t launch_gram_prepare(const void* X, int xdt, int64_t M, int64_t K, const GramPlan& p,
                                uint16_t* Xt, float* Hpart, double* d64, float* d32, uint16_t* B,
                                uint32_t* gram_k, uint32_t* flags, hipStream_t stream,

@@ -106,6 +106,11 @@ hipError_t launch_stats(const void* X, int dtype, int64_t M, int64_t K, int64_t 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_stats_final(partials, chunks, M, K, dtype, sx, flags, stream);
+}
+
+hipError_t launch_stats_final(const double* partials, int64_t chunks, int64_t M, int64_t K,
+                              int dtype, float* sx, uint32_t* flags, hipStream_t stream) {
   stats_final_kernel<<<(unsigned)((K + 31) / 32), 256, 0, stream>>>(partials, chunks, M, K,
                                                                      dtype, sx, flags);
   return hipGetLastError();

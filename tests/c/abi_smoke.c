@@ -27,7 +27,7 @@ int main(void) {
   cfg.clip_min = 0.5f;
   cfg.zero_point = 0;
 
-  EXPECT(awq_version() >= 10500);
+  EXPECT(awq_version() >= 10600);
   EXPECT(strncmp(awq_status_string(AWQ_ERR_SHAPE), "AWQ_ERR_SHAPE", 13) == 0);
   EXPECT(awq_act_stats_workspace_bytes(65536, 4096) > 0);
   EXPECT(awq_search_workspace_bytes(65536, 4096, 4096, AWQ_F16, &cfg) > 0);

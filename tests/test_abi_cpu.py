@@ -35,7 +35,7 @@ def test_header_declares_the_calls():
               "awq_search_workspace_bytes", "awq_act_stats_workspace_bytes",
               "awq_clip_search", "awq_clip_workspace_bytes", "awq_search_layers",
               "awq_clip_search_gram", "awq_clip_search_gram_ws_bytes",
-              "awq_fold_scale",
+              "awq_fold_scale", "awq_stats_search_layer", "awq_search_layer_profiled",
               "awq_status_string", "awq_version"):
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
@@ -50,7 +50,7 @@ def test_status_strings(lib):
     for code in range(7):
         s = lib.awq_status_string(code).decode()
         assert s.startswith("AWQ_")
-    assert lib.awq_version() == 10500
+    assert lib.awq_version() == 10600
 
 
 def cfg(bits=4, group=128, n_grid=20, s_floor=1e-5, form=0, n_clip=11, clip_min=0.5,
@@ -164,6 +164,44 @@ def test_search_rejects(lib):
     assert _search(lib, ws=None) == E.AWQ_ERR_WORKSPACE
     need = lib.awq_search_workspace_bytes(300, 256, 512, 1, cfg())
     assert _search(lib, ws_bytes=need - 1) == E.AWQ_ERR_WORKSPACE
+
+
+def _stats_search(lib, **kw):
+    a = dict(W=FAKE, wdt=1, N=256, K=512, X=FAKE2, xdt=1, M=300, cfg=cfg(), sx=FAKE,
+             losses=FAKE, best=FAKE, s_best=FAKE, flags=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    c = a["cfg"]
+    return lib.awq_stats_search_layer(a["W"], a["wdt"], a["N"], a["K"], a["X"], a["xdt"], a["M"],
+                                      ctypes.byref(c) if c is not None else None, a["sx"],
+                                      a["losses"], a["best"], a["s_best"], a["flags"], a["ws"],
+                                      a["ws_bytes"], None, None)
+
+
+def test_stats_search_rejects(lib):
+    E = _lib
+    for k in ("W", "X", "sx", "losses", "best", "s_best", "flags"):
+        assert _stats_search(lib, **{k: None}) == E.AWQ_ERR_NULL, k
+    assert _stats_search(lib, cfg=None) == E.AWQ_ERR_NULL
+    assert _stats_search(lib, cfg=cfg(bits=5)) == E.AWQ_ERR_CONFIG
+    assert _stats_search(lib, xdt=9) == E.AWQ_ERR_DTYPE
+    assert _stats_search(lib, K=500) == E.AWQ_ERR_SHAPE
+    assert _stats_search(lib, M=0) == E.AWQ_ERR_SHAPE
+    # more than 65535 chunks of 256 tokens for the statistics pass
+    assert _stats_search(lib, M=256 * 65535 + 1, N=1, K=128) == E.AWQ_ERR_SHAPE
+    assert _stats_search(lib, ws=None) == E.AWQ_ERR_WORKSPACE
+    for form in (E.AWQ_FORM_DIRECT, E.AWQ_FORM_GRAM):
+        c = cfg(form=form)
+        need = lib.awq_search_workspace_bytes(300, 256, 512, 1, c)
+        assert _stats_search(lib, cfg=c, ws_bytes=need - 1) == E.AWQ_ERR_WORKSPACE
+
+
+def test_search_workspace_holds_the_statistics_partials(lib):
+    # one token and few channels: the statistics' chunk partials (fp64 [1][K]) still fit in the
+    # region they share (the direct form's error stack is only n_grid * N * K fp16)
+    for form in (_lib.AWQ_FORM_DIRECT, _lib.AWQ_FORM_GRAM):
+        for M, N, K in ((1, 1, 128), (65536, 1, 128), (300, 3, 256)):
+            need = lib.awq_search_workspace_bytes(M, N, K, 1, cfg(form=form, n_grid=2))
+            assert need >= ((M + 255) // 256) * K * 8
 
 
 def test_pack_rejects(lib):
