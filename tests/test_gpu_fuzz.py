@@ -3,6 +3,10 @@ a multiple of the group, token counts from 1 up), dtypes of W and X, 3 and 4 bit
 and 128, symmetric and zero-point codes, both search forms. The configurations are drawn once
 from a fixed seed, so the list is the same on every run.
 
+Every other configuration goes through awq_stats_search_layer (s_X and the search in one call;
+in the Gram form with fp16 X the column sums come from the transpose pass), the rest through
+awq_act_stats then awq_search_layer.
+
 Per configuration: s_X bit-exact; every per-alpha loss within the bar of the parity tests (1e-4
 relative with at least 64 weight rows, 2e-3 below); alpha* equal to the oracle's unless the
 oracle's two best losses are within twice that bar; at the GPU's alpha*, codes, packed words,
@@ -31,7 +35,7 @@ def _configs(count=24, seed=2024):
             form=str(g.choice(["direct", "gram"])),
             wdt=[np.float16, np.float32][int(g.integers(0, 2))],
             xdt=["f16", "bf16", "f32"][int(g.integers(0, 3))],
-            outliers=int(g.integers(0, 6)), seed=int(g.integers(0, 2**31))))
+            outliers=int(g.integers(0, 6)), seed=int(g.integers(0, 2**31)), fused=c % 2 == 1))
     return out
 
 
@@ -74,8 +78,12 @@ def test_fuzz_path_against_oracle(awq, cfg):
     Xt = torch.from_numpy(X).cuda().to(tdt)
     acfg = awq.AwqConfig(bits=cfg["bits"], group=cfg["group"], form=cfg["form"],
                          zero_point=cfg["zp"])
-    sx, flags = awq.act_stats(Xt)
-    res = awq.search_layer(Wt, Xt, sx, acfg, flags=flags)
+    if cfg["fused"]:
+        sx, res = awq.stats_search_layer(Wt, Xt, acfg)
+        flags = res.flags
+    else:
+        sx, flags = awq.act_stats(Xt)
+        res = awq.search_layer(Wt, Xt, sx, acfg, flags=flags)
     bg = int(res.best.item())
     p = awq.pack_int4(Wt, res.s_best, acfg, flags=flags, with_codes=True)
     # W4A16 walks K in 128-channel steps: with groups of 64 it needs K % 128 == 0
