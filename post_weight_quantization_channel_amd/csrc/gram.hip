@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void gram_transpose_kernel(const void* __restr
         for (int w = 0; w < 4; ++w) v[r][w] = 0u;
       }
     }
-    if (STATS) {
+    if constexpr (STATS) {
 #pragma unroll
       for (int r = 0; r < 8; ++r)
 #pragma unroll
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void gram_transpose_kernel(const void* __restr
     }
     if (DT != kF16) wave_flag(flags, over, kFlagXF16Range);
   }
-  if (STATS) {
+  if constexpr (STATS) {
     // the 8 token blocks of the wave (lane bits 3..5), then the 4 waves
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
