@@ -10,7 +10,9 @@
 // (eight interleaved slices per column, combined in slice order) and divides by M in fp64 before
 // the single rounding to fp32, so a run is reproducible bit for bit. For fp16 inputs every
 // partial sum is exact (all |x| are multiples of 2^-24 and the sums stay below 2^29, which is
-// checked), so the result does not depend on the reduction order at all.
+// checked), so the result does not depend on the reduction order at all. The Gram-form search
+// can take the same chunk partials in its transpose pass (gram.hip) and reduce them with the
+// final pass here, which then gives the same s_X bit for bit.
 #include "device_common.h"
 #include "kernels.h"
 

@@ -116,3 +116,23 @@ def test_clip_after_stats_search(awq):
     torch.cuda.synchronize()
     assert np.array_equal(c1.clip.cpu().numpy(), c2.clip.cpu().numpy())
     assert int(c1.flags.item()) == 0
+
+
+def test_stats_search_flags(awq):
+    """The fused call raises the statistics pass's flags: fp16 column sums of 2^29 or more
+    (no longer exact) and a non-finite activation."""
+    from post_weight_quantization_channel_amd import _lib as L
+    rng = np.random.default_rng(48)
+    W = (0.02 * rng.standard_normal((64, 128))).astype(np.float16)
+    Xb = rng.standard_normal((9000, 128)).astype(np.float16)
+    Xb[:, 5] = 60000.0                      # 9000 * 60000 > 2^29
+    print("   stats_search_layer flags", W.shape, Xb.shape, flush=True)
+    for form in ("direct", "gram"):
+        cfg = awq.AwqConfig(form=form)
+        _, r = awq.stats_search_layer(torch.from_numpy(W).cuda(), torch.from_numpy(Xb).cuda(), cfg)
+        assert int(r.flags.item()) & L.FLAG_STATS_INEXACT, form
+        Xi = Xb.copy()
+        Xi[:, 5] = 1.0
+        Xi[3, 9] = np.inf
+        _, r = awq.stats_search_layer(torch.from_numpy(W).cuda(), torch.from_numpy(Xi).cuda(), cfg)
+        assert int(r.flags.item()) & L.FLAG_NONFINITE_X, form
