@@ -68,8 +68,15 @@ __device__ __forceinline__ int perm8(int t) { return ((t & 3) << 1) | (t >> 2); 
 // Bytes of the skinny kernel's LDS regions (the launcher sizes the dynamic LDS with the same).
 __host__ __device__ constexpr int64_t w4a16_red_bytes(int MB) { return (int64_t)kWaves * MB * 64 * 16; }
 
-template <int MB, bool ACT_LDS, int GS, bool ZP, bool HAS_S>
-__global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restrict__ A, int64_t M,
+// SMALL: the 1/s (or A / s) table has at most kThreads 16-byte chunks and the steps at most
+// kThreads entries (one of each per thread: K <= 4096 with groups of 128, K <= 2048 with groups of
+// 64, and M * K <= 4096 when A is staged), so the prologue holds one load of each per thread.
+// The decode instance (one batch row staged in LDS, symmetric codes, groups of 128) then fits
+// in 80 VGPRs without spilling: held to that, three 512-thread workgroups fit on a CU and a
+// GEMV with more than 512 workgroups (N > 8192) runs in one round instead of two.
+template <int MB, bool ACT_LDS, int GS, bool ZP, bool HAS_S, bool SMALL>
+__global__ __launch_bounds__(kThreads, (MB == 1 && SMALL && ACT_LDS && GS == 128 && !ZP) ? 6 : 1)
+void w4a16_kernel(const uint16_t* __restrict__ A, int64_t M,
                                                          int64_t N, int64_t K,
                                                          const uint32_t* __restrict__ qweight,
                                                          const uint16_t* __restrict__ scales16,
@@ -107,16 +114,17 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restr
   const int gr = (int)groups;
   // ---- 1. table loads into registers (at most kTableIters per thread) ------------------------
   const int tchunks = ACT_LDS ? (int)mrows * kc : kc;           // 16-byte chunks of the table
-  uint4 ta[kTableIters], ts[kTableIters];
+  constexpr int kTI = SMALL ? 1 : kTableIters;
+  uint4 ta[kTI], ts[kTI];
 #pragma unroll
-  for (int it = 0; it < kTableIters; ++it) {
+  for (int it = 0; it < kTI; ++it) {
     const int e = tid + it * kThreads;
     const int ec = e < tchunks ? e : 0;
     const int k8 = ACT_LDS ? ec % kc : ec;
     ts[it] = *reinterpret_cast<const uint4*>(s16 + (int64_t)k8 * 8);
     if (ACT_LDS) ta[it] = *reinterpret_cast<const uint4*>(A + (m0 + ec / kc) * K + (int64_t)k8 * 8);
   }
-  constexpr int kStepIters = (kMaxK / GS * kRows + kThreads - 1) / kThreads;
+  constexpr int kStepIters = SMALL ? 1 : (kMaxK / GS * kRows + kThreads - 1) / kThreads;
   const int ng = (int)ngr;
   uint16_t sraw[kStepIters];
   uint8_t zraw[kStepIters];
@@ -154,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_kernel(const uint16_t* __restr
   // ---- 3. tables into LDS (straight-line: out-of-range entries go to a trash slot, so no
   // load above is sunk into a conditional block and waited for there) ------------------------
 #pragma unroll
-  for (int it = 0; it < kTableIters; ++it) {
+  for (int it = 0; it < kTI; ++it) {
     const int e = tid + it * kThreads;
     const uint32_t sw[4] = {ts[it].x, ts[it].y, ts[it].z, ts[it].w};
     uint32_t aw[4] = {0u, 0u, 0u, 0u};
@@ -522,19 +530,32 @@ static hipError_t w4a16_dispatch(const uint16_t* A, int64_t M, int64_t N, int64_
   hipError_t e = hipSuccess;
   for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += 64) {
     const int64_t rest = M - m0;
+    // SMALL instances: one table chunk and one step entry per thread at most
+    const bool steps_small = (K / GS) * kRows <= kThreads;
     if (rest <= 16 && (size_t)rest * K * 2 <= kActLdsBytes) {
       const size_t lds = region0((size_t)rest * K * 2, 1) + tables;
-      w4a16_kernel<1, true, GS, ZP, HAS_S><<<blocks, kThreads, lds, stream>>>(A, M, N, K, qweight,
-                                                                       scales16, zeros, s16, Y, m0);
+      if (steps_small && rest * (K / 8) <= kThreads)
+        w4a16_kernel<1, true, GS, ZP, HAS_S, true><<<blocks, kThreads, lds, stream>>>(
+            A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
+      else
+        w4a16_kernel<1, true, GS, ZP, HAS_S, false><<<blocks, kThreads, lds, stream>>>(
+            A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
     } else if (rest <= 16) {
-      w4a16_kernel<1, false, GS, ZP, HAS_S><<<blocks, kThreads, region0((size_t)K * 2, 1) + tables,
-                                       stream>>>(A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
+      const size_t lds = region0((size_t)K * 2, 1) + tables;
+      if (steps_small && K / 8 <= kThreads)
+        w4a16_kernel<1, false, GS, ZP, HAS_S, true><<<blocks, kThreads, lds, stream>>>(
+            A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
+      else
+        w4a16_kernel<1, false, GS, ZP, HAS_S, false><<<blocks, kThreads, lds, stream>>>(
+            A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
     } else if (rest <= 32) {
-      w4a16_kernel<2, false, GS, ZP, HAS_S><<<blocks, kThreads, region0((size_t)K * 2, 2) + tables,
-                                       stream>>>(A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
+      w4a16_kernel<2, false, GS, ZP, HAS_S, false><<<blocks, kThreads,
+                                                      region0((size_t)K * 2, 2) + tables, stream>>>(
+          A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
     } else {
-      w4a16_kernel<4, false, GS, ZP, HAS_S><<<blocks, kThreads, region0((size_t)K * 2, 4) + tables,
-                                       stream>>>(A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
+      w4a16_kernel<4, false, GS, ZP, HAS_S, false><<<blocks, kThreads,
+                                                      region0((size_t)K * 2, 4) + tables, stream>>>(
+          A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
     }
     e = hipGetLastError();
   }
