@@ -68,14 +68,15 @@ __device__ __forceinline__ int perm8(int t) { return ((t & 3) << 1) | (t >> 2); 
 // Bytes of the skinny kernel's LDS regions (the launcher sizes the dynamic LDS with the same).
 __host__ __device__ constexpr int64_t w4a16_red_bytes(int MB) { return (int64_t)kWaves * MB * 64 * 16; }
 
-// SMALL: the 1/s (or A / s) table has at most kThreads 16-byte chunks and the steps at most
-// kThreads entries (one of each per thread: K <= 4096 with groups of 128, K <= 2048 with groups of
-// 64, and M * K <= 4096 when A is staged), so the prologue holds one load of each per thread.
-// The decode instance (one batch row staged in LDS, symmetric codes, groups of 128) then fits
-// in 80 VGPRs without spilling: held to that, three 512-thread workgroups fit on a CU and a
-// GEMV with more than 512 workgroups (N > 8192) runs in one round instead of two.
-template <int MB, bool ACT_LDS, int GS, bool ZP, bool HAS_S, bool SMALL>
-__global__ __launch_bounds__(kThreads, (MB == 1 && SMALL && ACT_LDS && GS == 128 && !ZP) ? 6 : 1)
+// SR > 0: a row has at most kThreads 16-byte chunks of channels and the steps at most kThreads
+// entries (K <= 4096 with groups of 128, K <= 2048 with groups of 64), so thread t loads chunk t
+// of 1/s and, when A is staged, chunk t of each of the (at most SR) staged rows: the prologue
+// holds 1 + SR loads per thread instead of up to 2 kTableIters. The staged instances with
+// symmetric codes and groups of 128 then fit in 80 VGPRs without spilling: held to that,
+// three 512-thread workgroups fit on a CU, and a GEMV with more than 512 workgroups (N > 8192)
+// runs in one round instead of two.
+template <int MB, bool ACT_LDS, int GS, bool ZP, bool HAS_S, int SR>
+__global__ __launch_bounds__(kThreads, (MB == 1 && SR > 0 && ACT_LDS && GS == 128 && !ZP) ? 6 : 1)
 void w4a16_kernel(const uint16_t* __restrict__ A, int64_t M,
                                                          int64_t N, int64_t K,
                                                          const uint32_t* __restrict__ qweight,
@@ -114,17 +115,30 @@ void w4a16_kernel(const uint16_t* __restrict__ A, int64_t M,
   const int gr = (int)groups;
   // ---- 1. table loads into registers (at most kTableIters per thread) ------------------------
   const int tchunks = ACT_LDS ? (int)mrows * kc : kc;           // 16-byte chunks of the table
-  constexpr int kTI = SMALL ? 1 : kTableIters;
-  uint4 ta[kTI], ts[kTI];
+  constexpr int kTI = SR ? 1 : kTableIters;                      // 1/s loads per thread
+  constexpr int kTA = !ACT_LDS ? 1 : (SR ? SR : kTableIters);    // A loads per thread
+  uint4 ta[kTA], ts[kTI];
+  if constexpr (SR > 0) {
+    const int k8 = tid < kc ? tid : 0;
+    ts[0] = *reinterpret_cast<const uint4*>(s16 + (int64_t)k8 * 8);
+    if (ACT_LDS) {
 #pragma unroll
-  for (int it = 0; it < kTI; ++it) {
-    const int e = tid + it * kThreads;
-    const int ec = e < tchunks ? e : 0;
-    const int k8 = ACT_LDS ? ec % kc : ec;
-    ts[it] = *reinterpret_cast<const uint4*>(s16 + (int64_t)k8 * 8);
-    if (ACT_LDS) ta[it] = *reinterpret_cast<const uint4*>(A + (m0 + ec / kc) * K + (int64_t)k8 * 8);
+      for (int r = 0; r < kTA; ++r) {
+        const int64_t rr = r < mrows ? r : mrows - 1;
+        ta[r] = *reinterpret_cast<const uint4*>(A + (m0 + rr) * K + (int64_t)k8 * 8);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < kTI; ++it) {
+      const int e = tid + it * kThreads;
+      const int ec = e < tchunks ? e : 0;
+      const int k8 = ACT_LDS ? ec % kc : ec;
+      ts[it] = *reinterpret_cast<const uint4*>(s16 + (int64_t)k8 * 8);
+      if (ACT_LDS) ta[it] = *reinterpret_cast<const uint4*>(A + (m0 + ec / kc) * K + (int64_t)k8 * 8);
+    }
   }
-  constexpr int kStepIters = SMALL ? 1 : (kMaxK / GS * kRows + kThreads - 1) / kThreads;
+  constexpr int kStepIters = SR ? 1 : (kMaxK / GS * kRows + kThreads - 1) / kThreads;
   const int ng = (int)ngr;
   uint16_t sraw[kStepIters];
   uint8_t zraw[kStepIters];
@@ -161,12 +175,10 @@ void w4a16_kernel(const uint16_t* __restrict__ A, int64_t M,
 
   // ---- 3. tables into LDS (straight-line: out-of-range entries go to a trash slot, so no
   // load above is sunk into a conditional block and waited for there) ------------------------
-#pragma unroll
-  for (int it = 0; it < kTI; ++it) {
-    const int e = tid + it * kThreads;
-    const uint32_t sw[4] = {ts[it].x, ts[it].y, ts[it].z, ts[it].w};
-    uint32_t aw[4] = {0u, 0u, 0u, 0u};
-    if (ACT_LDS) { aw[0] = ta[it].x; aw[1] = ta[it].y; aw[2] = ta[it].z; aw[3] = ta[it].w; }
+  // table entry: fp16(a / s) (a = 1 without staging) of 8 channels, in the permuted order
+  auto table_chunk = [&](const uint4& sv4, const uint4& av4, uint4* dst) {
+    const uint32_t sw[4] = {sv4.x, sv4.y, sv4.z, sv4.w};
+    const uint32_t aw[4] = {av4.x, av4.y, av4.z, av4.w};
     uint16_t h[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -177,8 +189,22 @@ void w4a16_kernel(const uint16_t* __restrict__ A, int64_t M,
     uint32_t w[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) w[p] = (uint32_t)h[2 * p] | ((uint32_t)h[2 * p + 1] << 16);
-    uint4* dst = (e < tchunks) ? reinterpret_cast<uint4*>(table + e * 8) : trash;
     *dst = make_uint4(w[0], w[1], w[2], w[3]);
+  };
+  if constexpr (SR > 0) {
+#pragma unroll
+    for (int r = 0; r < (ACT_LDS ? kTA : 1); ++r) {
+      const bool ok = tid < kc && (!ACT_LDS || r < mrows);
+      table_chunk(ts[0], ACT_LDS ? ta[r] : make_uint4(0, 0, 0, 0),
+                  ok ? reinterpret_cast<uint4*>(table + (int64_t)r * K + tid * 8) : trash);
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < kTI; ++it) {
+      const int e = tid + it * kThreads;
+      table_chunk(ts[it], ACT_LDS ? ta[it] : make_uint4(0, 0, 0, 0),
+                  (e < tchunks) ? reinterpret_cast<uint4*>(table + e * 8) : trash);
+    }
   }
 #pragma unroll
   for (int it = 0; it < kStepIters; ++it) {
@@ -530,31 +556,34 @@ static hipError_t w4a16_dispatch(const uint16_t* A, int64_t M, int64_t N, int64_
   hipError_t e = hipSuccess;
   for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += 64) {
     const int64_t rest = M - m0;
-    // SMALL instances: one table chunk and one step entry per thread at most
-    const bool steps_small = (K / GS) * kRows <= kThreads;
+    // one chunk of channels and one step entry per thread at most: the SR > 0 instances
+    const bool small = (K / GS) * kRows <= kThreads && K / 8 <= kThreads;
     if (rest <= 16 && (size_t)rest * K * 2 <= kActLdsBytes) {
       const size_t lds = region0((size_t)rest * K * 2, 1) + tables;
-      if (steps_small && rest * (K / 8) <= kThreads)
-        w4a16_kernel<1, true, GS, ZP, HAS_S, true><<<blocks, kThreads, lds, stream>>>(
+      if (small && rest == 1)
+        w4a16_kernel<1, true, GS, ZP, HAS_S, 1><<<blocks, kThreads, lds, stream>>>(
+            A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
+      else if (small && rest <= 4)
+        w4a16_kernel<1, true, GS, ZP, HAS_S, 4><<<blocks, kThreads, lds, stream>>>(
             A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
       else
-        w4a16_kernel<1, true, GS, ZP, HAS_S, false><<<blocks, kThreads, lds, stream>>>(
+        w4a16_kernel<1, true, GS, ZP, HAS_S, 0><<<blocks, kThreads, lds, stream>>>(
             A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
     } else if (rest <= 16) {
       const size_t lds = region0((size_t)K * 2, 1) + tables;
-      if (steps_small && K / 8 <= kThreads)
-        w4a16_kernel<1, false, GS, ZP, HAS_S, true><<<blocks, kThreads, lds, stream>>>(
+      if (small)
+        w4a16_kernel<1, false, GS, ZP, HAS_S, 1><<<blocks, kThreads, lds, stream>>>(
             A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
       else
-        w4a16_kernel<1, false, GS, ZP, HAS_S, false><<<blocks, kThreads, lds, stream>>>(
+        w4a16_kernel<1, false, GS, ZP, HAS_S, 0><<<blocks, kThreads, lds, stream>>>(
             A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
     } else if (rest <= 32) {
-      w4a16_kernel<2, false, GS, ZP, HAS_S, false><<<blocks, kThreads,
-                                                      region0((size_t)K * 2, 2) + tables, stream>>>(
+      w4a16_kernel<2, false, GS, ZP, HAS_S, 0><<<blocks, kThreads,
+                                                  region0((size_t)K * 2, 2) + tables, stream>>>(
           A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
     } else {
-      w4a16_kernel<4, false, GS, ZP, HAS_S, false><<<blocks, kThreads,
-                                                      region0((size_t)K * 2, 4) + tables, stream>>>(
+      w4a16_kernel<4, false, GS, ZP, HAS_S, 0><<<blocks, kThreads,
+                                                  region0((size_t)K * 2, 4) + tables, stream>>>(
           A, M, N, K, qweight, scales16, zeros, s16, Y, m0);
     }
     e = hipGetLastError();
