@@ -68,10 +68,10 @@ __device__ __forceinline__ int perm8(int t) { return ((t & 3) << 1) | (t >> 2); 
 // Bytes of the skinny kernel's LDS regions (the launcher sizes the dynamic LDS with the same).
 __host__ __device__ constexpr int64_t w4a16_red_bytes(int MB) { return (int64_t)kWaves * MB * 64 * 16; }
 
-// SR > 0: a row has at most kThreads 16-byte chunks of channels and the steps at most kThreads
-// entries (K <= 4096 with groups of 128, K <= 2048 with groups of 64), so thread t loads chunk t
-// of 1/s and, when A is staged, chunk t of each of the (at most SR) staged rows: the prologue
-// holds 1 + SR loads per thread instead of up to 2 kTableIters. The staged instances with
+// SR > 0: a row has at most kThreads 16-byte chunks of channels (K <= 4096), so thread t loads
+// chunk t of 1/s and, when A is staged, chunk t of each of the (at most SR) staged rows: the
+// prologue holds 1 + SR table loads per thread instead of up to 2 kTableIters, and 1 (groups of
+// 128) or 2 (groups of 64) step loads instead of up to 6. The staged instances with
 // symmetric codes and groups of 128 then fit in 80 VGPRs without spilling: held to that,
 // three 512-thread workgroups fit on a CU, and a GEMV with more than 512 workgroups (N > 8192)
 // runs in one round instead of two.
@@ -138,7 +138,9 @@ void w4a16_kernel(const uint16_t* __restrict__ A, int64_t M,
       if (ACT_LDS) ta[it] = *reinterpret_cast<const uint4*>(A + (m0 + ec / kc) * K + (int64_t)k8 * 8);
     }
   }
-  constexpr int kStepIters = SR ? 1 : (kMaxK / GS * kRows + kThreads - 1) / kThreads;
+  // steps: with SR > 0, K <= 4096 holds at most (4096 / GS) * kRows of them (1 or 2 per thread)
+  constexpr int kStepIters = SR ? (4096 / GS * kRows + kThreads - 1) / kThreads
+                                : (kMaxK / GS * kRows + kThreads - 1) / kThreads;
   const int ng = (int)ngr;
   uint16_t sraw[kStepIters];
   uint8_t zraw[kStepIters];
@@ -557,7 +559,7 @@ static hipError_t w4a16_dispatch(const uint16_t* A, int64_t M, int64_t N, int64_
   for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += 64) {
     const int64_t rest = M - m0;
     // one chunk of channels and one step entry per thread at most: the SR > 0 instances
-    const bool small = (K / GS) * kRows <= kThreads && K / 8 <= kThreads;
+    const bool small = K / 8 <= kThreads;   // then the steps take at most 2 loads per thread
     if (rest <= 16 && (size_t)rest * K * 2 <= kActLdsBytes) {
       const size_t lds = region0((size_t)rest * K * 2, 1) + tables;
       if (small && rest == 1)
