@@ -71,12 +71,14 @@ __host__ __device__ constexpr int64_t w4a16_red_bytes(int MB) { return (int64_t)
 // SR > 0: a row has at most kThreads 16-byte chunks of channels (K <= 4096), so thread t loads
 // chunk t of 1/s and, when A is staged, chunk t of each of the (at most SR) staged rows: the
 // prologue holds 1 + SR table loads per thread instead of up to 2 kTableIters, and 1 (groups of
-// 128) or 2 (groups of 64) step loads instead of up to 6. The staged instances with
-// symmetric codes and groups of 128 then fit in 80 VGPRs without spilling: held to that,
-// three 512-thread workgroups fit on a CU, and a GEMV with more than 512 workgroups (N > 8192)
-// runs in one round instead of two.
+// 128) or 2 (groups of 64) step loads instead of up to 6, and a wave's groups (at most 4) are
+// one chunk of weight loads, so the second chunk buffer goes too. These instances fit in 80
+// VGPRs without spilling. The staged ones are held to that: three 512-thread workgroups fit on
+// a CU, and a GEMV with more than 512 workgroups (N > 8192) runs in one round instead of two.
+// (Held to it too, the unstaged ones (batches of 5 to 16) ran 2% slower at 11008 x 4096:
+// they are bound by reading A once per workgroup, not by residency.)
 template <int MB, bool ACT_LDS, int GS, bool ZP, bool HAS_S, int SR>
-__global__ __launch_bounds__(kThreads, (MB == 1 && SR > 0 && ACT_LDS && GS == 128 && !ZP) ? 6 : 1)
+__global__ __launch_bounds__(kThreads, (MB == 1 && SR > 0 && ACT_LDS) ? 6 : 1)
 void w4a16_kernel(const uint16_t* __restrict__ A, int64_t M,
                                                          int64_t N, int64_t K,
                                                          const uint32_t* __restrict__ qweight,
@@ -306,14 +308,19 @@ void w4a16_kernel(const uint16_t* __restrict__ A, int64_t M,
     }
   };
 
-  // chunks alternate between the two register buffers (static indices: no scratch)
-  const int nchunks = (my_groups + kChunk - 1) / kChunk;
-  for (int c = 0; c < nchunks; c += 2) {
-    if (c + 1 < nchunks) load_chunk(c + 1, wbuf[1]);
-    process(wbuf[0], c);
-    if (c + 1 < nchunks) {
-      if (c + 2 < nchunks) load_chunk(c + 2, wbuf[0]);
-      process(wbuf[1], c + 1);
+  if constexpr (SR > 0) {
+    // K <= 4096: at most 32 groups, so a wave's groups (at most 4) are the one chunk in flight
+    process(wbuf[0], 0);
+  } else {
+    // chunks alternate between the two register buffers (static indices: no scratch)
+    const int nchunks = (my_groups + kChunk - 1) / kChunk;
+    for (int c = 0; c < nchunks; c += 2) {
+      if (c + 1 < nchunks) load_chunk(c + 1, wbuf[1]);
+      process(wbuf[0], c);
+      if (c + 1 < nchunks) {
+        if (c + 2 < nchunks) load_chunk(c + 2, wbuf[0]);
+        process(wbuf[1], c + 1);
+      }
     }
   }
 
