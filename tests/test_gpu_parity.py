@@ -922,7 +922,8 @@ def test_clip_search_gram_group_and_zero_point(awq, group, zp):
 
 W4A16_ZP_CASES = [(g, zp, n, k, m) for (g, zp) in QUANT_VARIANTS for (n, k, m) in
                   ((384, 512, 1), (384, 512, 16), (256, 4096, 40), (320, 512, 100))] + \
-                 [(64, False, 4096, 4096, 1), (128, True, 11008, 4096, 4), (64, True, 4096, 4096, 3)]
+                 [(64, False, 4096, 4096, 1), (128, True, 11008, 4096, 4), (64, True, 4096, 4096, 3),
+                  (64, True, 256, 12288, 80)]   # tiled path whose tables take the register-staged kernel
 
 
 @pytest.mark.parametrize("group,zp,n,k,m", W4A16_ZP_CASES)
