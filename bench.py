@@ -21,8 +21,8 @@ fields it carries
   clip_search   the clipping search at s* (11 ratios 1 .. 0.5) and the clipped pack: ms; and
                 the same search on the operand the step's Gram-form search left in its
                 workspace (awq_clip_search_gram);
-  shared_qkv    one alpha for three 4096x4096 weights reading the same X, and the fold of s^-1
-                into the producing norm weight: ms;
+  shared_qkv    one alpha for three 4096x4096 weights reading the same X (s_X taken in the same
+                call), and the fold of s^-1 into the producing norm weight: ms;
   quant_variants  groups of 64 and zero-point codes (and both): the search (ms, its quantize
                 and loss kernels), the pack, and W4A16 at M = 1 and 512 on 4096x4096;
   hbm_stages    the bandwidth-bound kernels: algorithmic bytes, GB/s, fraction of 8 TB/s;
@@ -469,13 +469,13 @@ def main():
         scfg = awq.AwqConfig(bits=4, group=128, n_grid=N_GRID, form=args.form)
         ws_search = torch.empty(awq.search_workspace_bytes(M_, 3 * N_, K_, torch.float16, scfg),
                                 dtype=torch.uint8, device=dev)
-        sx_s, _ = awq.act_stats(X, workspace=ws_stats)
         gamma = torch.ones((1, K_), dtype=torch.float16, device=dev)
         t_sh, t_fold = [], []
         for r in range(args.shared_reps + 1):          # the first run is a warm-up
             e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
             e0.record(st)
-            rs = awq.search_layers([W, Wk, Wv], X, sx_s, scfg, workspace=ws_search)
+            # s_X in the same call, as in the step (awq_stats_search_layers)
+            _, rs = awq.search_layers([W, Wk, Wv], X, None, scfg, workspace=ws_search)
             e1.record(st)
             awq.fold_scale(gamma, rs.s_best, axis=1)
             e2.record(st)

@@ -182,6 +182,18 @@ awq_status awq_search_layers(const void* const* W, const int64_t* N, int32_t n_w
                              size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * awq_stats_search_layers -- awq_act_stats followed by awq_search_layers on the same X, in one
+ *   call: sx is an output, as in awq_stats_search_layer (identical to awq_act_stats's; in the
+ *   Gram form with fp16 X the column sums come out of the pass that transposes X). Everything
+ *   else as awq_search_layers.
+ * ---------------------------------------------------------------------------------------- */
+awq_status awq_stats_search_layers(const void* const* W, const int64_t* N, int32_t n_w,
+                                   awq_dtype wdt, int64_t K, const void* X, awq_dtype xdt,
+                                   int64_t M, const awq_cfg* cfg, float* sx, double* losses,
+                                   int32_t* best, float* s_best, uint32_t* flags, void* ws,
+                                   size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * awq_fold_scale -- fold s^-1 into the previous operator's parameters, in place ([notes] 方法,
  * further optimisations: fuse the input's down-scaling into the previous operator).
  * prev   device [rows, cols] with row stride ld elements, dtype AWQ_F16, AWQ_BF16 or AWQ_F32.

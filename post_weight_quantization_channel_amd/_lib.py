@@ -62,6 +62,9 @@ SIGNATURES = {
                                     ctypes.POINTER(ctypes.c_float)]),
     "awq_search_layers": (_E, [ctypes.POINTER(_P), ctypes.POINTER(_I64), _I32, _E, _I64, _P, _E,
                                _I64, _P, ctypes.POINTER(AwqCfg), _P, _P, _P, _P, _P, _SZ, _P]),
+    "awq_stats_search_layers": (_E, [ctypes.POINTER(_P), ctypes.POINTER(_I64), _I32, _E, _I64, _P,
+                                     _E, _I64, ctypes.POINTER(AwqCfg), _P, _P, _P, _P, _P, _P, _SZ,
+                                     _P]),
     "awq_fold_scale": (_E, [_P, _E, _I64, _I64, _I64, _P, _I32, _P, _P]),
     "awq_clip_workspace_bytes": (_SZ, [_I64, _I64, _I64, _E, ctypes.POINTER(AwqCfg)]),
     "awq_clip_search": (_E, [_P, _E, _I64, _I64, _P, _E, _I64, _P, ctypes.POINTER(AwqCfg), _P,

@@ -249,15 +249,18 @@ def clip_search_gram(W: torch.Tensor, s: torch.Tensor, search_workspace: torch.T
     return ClipResult(clip, err, flags)
 
 
-def search_layers(Ws: list, X: torch.Tensor, sx: torch.Tensor, cfg: AwqConfig = AwqConfig(),
-                  flags: torch.Tensor | None = None,
-                  workspace: torch.Tensor | None = None) -> SearchResult:
-    """One alpha for several weights that read the same X (rows stacked, no copy)."""
+def search_layers(Ws: list, X: torch.Tensor, sx: torch.Tensor | None,
+                  cfg: AwqConfig = AwqConfig(), flags: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None):
+    """One alpha for several weights that read the same X (rows stacked, no copy). With
+    sx = None, s_X is taken in the same call (awq_stats_search_layers) and (s_X, result) is
+    returned; otherwise the result."""
     lib = _lib.load()
     for i, W in enumerate(Ws):
         _dev(W, f"W[{i}]")
     _dev(X, "X")
-    _dev(sx, "sx")
+    if sx is not None:
+        _dev(sx, "sx")
     K = X.shape[1]
     if any(W.shape[1] != K or W.dtype != Ws[0].dtype for W in Ws):
         raise ValueError("every W must be [N_l, K] with the dtype of W[0]")
@@ -275,6 +278,15 @@ def search_layers(Ws: list, X: torch.Tensor, sx: torch.Tensor, cfg: AwqConfig = 
     s_best = torch.empty(K, dtype=torch.float32, device=X.device)
     ptrs = (ctypes.c_void_p * len(Ws))(*[W.data_ptr() for W in Ws])
     rows = (ctypes.c_int64 * len(Ws))(*Ns)
+    if sx is None:
+        sx_out = torch.empty(K, dtype=torch.float32, device=X.device)
+        check("awq_stats_search_layers", lib.awq_stats_search_layers(
+            ptrs, rows, len(Ws), _DT[Ws[0].dtype], K, X.data_ptr(), _DT[X.dtype], M, c,
+            sx_out.data_ptr(), losses.data_ptr(), best.data_ptr(), s_best.data_ptr(),
+            flags.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(X)))
+        return sx_out, SearchResult(losses, best, s_best, flags)
+    if sx.shape != (K,) or sx.dtype != torch.float32:
+        raise ValueError("sx must be fp32 [K]")
     check("awq_search_layers", lib.awq_search_layers(
         ptrs, rows, len(Ws), _DT[Ws[0].dtype], K, X.data_ptr(), _DT[X.dtype], M, sx.data_ptr(),
         c, losses.data_ptr(), best.data_ptr(), s_best.data_ptr(), flags.data_ptr(),

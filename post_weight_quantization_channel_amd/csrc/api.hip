@@ -325,6 +325,16 @@ awq_status awq_search_layers(const void* const* W, const int64_t* N, int32_t n_w
                      flags, ws, ws_bytes, stream, nullptr);
 }
 
+awq_status awq_stats_search_layers(const void* const* W, const int64_t* N, int32_t n_w,
+                                   awq_dtype wdt, int64_t K, const void* X, awq_dtype xdt,
+                                   int64_t M, const awq_cfg* cfg, float* sx, double* losses,
+                                   int32_t* best, float* s_best, uint32_t* flags, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  if (!sx) return AWQ_ERR_NULL;
+  return search_impl(W, N, n_w, wdt, K, X, xdt, M, nullptr, sx, cfg, losses, best, s_best,
+                     flags, ws, ws_bytes, stream, nullptr);
+}
+
 awq_status awq_search_layer_profiled(const void* W, awq_dtype wdt, int64_t N, int64_t K,
                                      const void* X, awq_dtype xdt, int64_t M, const float* sx,
                                      const awq_cfg* cfg, double* losses, int32_t* best,

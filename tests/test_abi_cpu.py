@@ -36,6 +36,7 @@ def test_header_declares_the_calls():
               "awq_clip_search", "awq_clip_workspace_bytes", "awq_search_layers",
               "awq_clip_search_gram", "awq_clip_search_gram_ws_bytes",
               "awq_fold_scale", "awq_stats_search_layer", "awq_search_layer_profiled",
+              "awq_stats_search_layers",
               "awq_status_string", "awq_version"):
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
@@ -334,6 +335,30 @@ def test_search_layers_rejects(lib):
     assert lib.awq_search_layers(None, None, 1, 1, 512, FAKE2, 1, 300, FAKE,
                                  ctypes.byref(cfg()), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
                                  None) == E.AWQ_ERR_NULL
+
+
+def test_stats_search_layers_rejects(lib):
+    E = _lib
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+
+    def call(ptrs=(FAKE, FAKE + 4096), rows=(100, 60), **kw):
+        a = dict(wdt=1, K=512, X=FAKE2, xdt=1, M=300, cfg=cfg(), sx=FAKE, losses=FAKE,
+                 best=FAKE, s_best=FAKE, flags=FAKE, ws=FAKE, ws_bytes=1 << 40)
+        a.update(kw)
+        pa = (P * len(ptrs))(*ptrs)
+        ra = (I64 * len(rows))(*rows)
+        c = a["cfg"]
+        return lib.awq_stats_search_layers(pa, ra, len(ptrs), a["wdt"], a["K"], a["X"], a["xdt"],
+                                           a["M"], ctypes.byref(c) if c is not None else None,
+                                           a["sx"], a["losses"], a["best"], a["s_best"],
+                                           a["flags"], a["ws"], a["ws_bytes"], None)
+    assert call(sx=None) == E.AWQ_ERR_NULL
+    assert call(ptrs=(FAKE, None)) == E.AWQ_ERR_NULL
+    assert call(cfg=cfg(bits=2)) == E.AWQ_ERR_CONFIG
+    assert call(M=256 * 65535 + 1, K=128, rows=(1, 1)) == E.AWQ_ERR_SHAPE
+    need = lib.awq_search_workspace_bytes(300, 160, 512, 1, cfg())
+    assert call(ws_bytes=need - 1) == E.AWQ_ERR_WORKSPACE
 
 
 def test_fold_scale_rejects(lib):

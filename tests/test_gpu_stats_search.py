@@ -136,3 +136,25 @@ def test_stats_search_flags(awq):
         Xi[3, 9] = np.inf
         _, r = awq.stats_search_layer(torch.from_numpy(W).cuda(), torch.from_numpy(Xi).cuda(), cfg)
         assert int(r.flags.item()) & L.FLAG_NONFINITE_X, form
+
+
+@pytest.mark.parametrize("form", ("direct", "gram"))
+def test_stats_search_layers_equals_stats_then_search(awq, form):
+    """awq_stats_search_layers against act_stats + search_layers on q/k/v-like weights."""
+    g = np.random.default_rng(49)
+    X = workloads.c2_like_layer(n=8, k=384, m=700, config=50).X
+    Ws = [torch.from_numpy((0.02 * g.standard_normal((n, 384))).astype(np.float16)).cuda()
+          for n in (200, 64, 136)]
+    print("   stats_search_layers", form, [tuple(W.shape) for W in Ws], X.shape, flush=True)
+    Xt = torch.from_numpy(X).cuda()
+    cfg = awq.AwqConfig(form=form)
+    sx_f, rf = awq.search_layers(Ws, Xt, None, cfg)
+    sx_s, fl = awq.act_stats(Xt)
+    rs = awq.search_layers(Ws, Xt, sx_s, cfg, flags=fl)
+    torch.cuda.synchronize()
+    assert np.array_equal(sx_f.cpu().numpy(), sx_s.cpu().numpy())
+    assert np.array_equal(sx_f.cpu().numpy(), oracle.act_stats(X))
+    assert np.array_equal(rf.losses.cpu().numpy(), rs.losses.cpu().numpy())
+    assert int(rf.best.item()) == int(rs.best.item())
+    assert np.array_equal(rf.s_best.cpu().numpy(), rs.s_best.cpu().numpy())
+    assert int(rf.flags.item()) == int(rs.flags.item()) == 0
