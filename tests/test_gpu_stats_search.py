@@ -158,3 +158,30 @@ def test_stats_search_layers_equals_stats_then_search(awq, form):
     assert int(rf.best.item()) == int(rs.best.item())
     assert np.array_equal(rf.s_best.cpu().numpy(), rs.s_best.cpu().numpy())
     assert int(rf.flags.item()) == int(rs.flags.item()) == 0
+
+
+def test_whole_path_on_a_side_stream(awq):
+    """Every call launches on the caller's stream: the path run under a side stream (torch's
+    current stream there) gives the default stream's results bit for bit."""
+    W, X = _layer(51, 320, 512, 900)
+    print("   whole path on a side stream", W.shape, X.shape, flush=True)
+    Wt, Xt = torch.from_numpy(W).cuda(), torch.from_numpy(X).cuda()
+    A = torch.from_numpy(workloads.w4a16_activations(3, 512, config=5)).cuda()
+
+    def path(form):
+        cfg = awq.AwqConfig(form=form)
+        sx, r = awq.stats_search_layer(Wt, Xt, cfg)
+        p = awq.pack_int4(Wt, r.s_best, cfg, flags=r.flags)
+        Y = awq.w4a16_gemm(A, p.qweight, p.scales16, p.s16)
+        return [sx, r.losses, r.s_best, p.qweight, p.scales16, Y, r.flags]
+
+    for form in ("direct", "gram"):
+        ref = [t.clone() for t in path(form)]
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            out = path(form)
+        side.synchronize()
+        for a, b in zip(ref, out):
+            assert torch.equal(a, b), form
