@@ -755,7 +755,11 @@ static hipError_t w4a16_dispatch(const uint16_t* A, int64_t M, int64_t N, int64_
                                  hipStream_t stream) {
   const unsigned blocks = (unsigned)((N + kRows - 1) / kRows);
   const size_t tables = (size_t)(K / GS) * kRows * (ZP ? 6 : 4) + 16;   // steps, zeros, trash
-  if (M > 64) {
+  // The tiled kernel above 64 batch rows, and from 49 on for tall weights: each skinny
+  // workgroup reads all of A, which at N = 11008 costs more than the tiles' unpacking (measured
+  // at M = 64: 49.5 against 39.8 us; equal near M = 48; at N = 4096 the skinny kernel wins
+  // throughout, 19.7 against ~36 us at M = 64).
+  if (M > 64 || (M > 48 && N >= 8192)) {
     const int64_t tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
     const int64_t dyn = w4a16_dma_tables(K, GS, ZP);
     // (three stages, loads two steps ahead, measured slower: the loop is bound by LDS traffic,
