@@ -42,6 +42,12 @@ __device__ __forceinline__ float h2f(uint16_t b) {
 __device__ __forceinline__ uint16_t f2h(float f) {  // round to nearest even
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
+// Two values rounded to nearest even fp16, a in the low half: one packed conversion on gfx950.
+__device__ __forceinline__ uint32_t f2h2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+}
 __device__ __forceinline__ float bf2f(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
@@ -108,6 +114,22 @@ __device__ __forceinline__ float group_max(float v) {
   v = fmaxf(v, dpp_f32<AWQ_DPP_ROW_HALF_MIRROR>(v));
   if (GL == 16) v = fmaxf(v, dpp_f32<AWQ_DPP_ROW_MIRROR>(v));
   return v;
+}
+
+// Maximum of non-negative values (a group's max |x|) over its GL lanes. For x >= 0 the fp32
+// order is the order of the bit patterns as unsigned integers, so the steps run on integer max,
+// which takes the DPP operand directly (fp32 max first quiets its inputs, one extra instruction
+// per step).
+template <int GL>
+__device__ __forceinline__ float group_absmax(float v) {
+  uint32_t u = __float_as_uint(v);
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, AWQ_DPP_QUAD_1032, 0xF, 0xF, false));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, AWQ_DPP_QUAD_2301, 0xF, 0xF, false));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, AWQ_DPP_ROW_HALF_MIRROR, 0xF, 0xF,
+                                                   false));
+  if (GL == 16)
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, AWQ_DPP_ROW_MIRROR, 0xF, 0xF, false));
+  return __uint_as_float(u);
 }
 
 // Sum over the 16 lanes of a DPP row, as a butterfly (adjacent pairs, pairs of pairs, the two
@@ -191,9 +213,33 @@ __device__ __forceinline__ void quant_codes(const float (&v)[NV], const QuantSte
   for (int t = 0; t < NV; ++t) q[t] = fminf(fmaxf(q[t], qmin), qmax);
 }
 
-// Codes of ws[] for the group maximum m (every |ws| <= m); returns Delta. Here each element
-// takes its own (rarely used) division branch: for 8 elements per lane that measured faster
-// than quant_codes' single block.
+// The codes of 8 values for one step: q = med3(rint(fp32(ws / Delta)) [+ z], qmin, qmax). The fast
+// quotients are formed first and their largest distance from an integer is kept; only when
+// that distance is within 2^-17 of one half (or the step needs exact division) does the lane
+// enter the block that redoes the near-half elements by IEEE division. med3 equals the clamp for
+// every finite value.
+template <bool ZP>
+__device__ __forceinline__ void codes8(const float (&ws)[8], const QuantStep& st, float z,
+                                       float qmin, float qmax, float (&q)[8]) {
+  float dev = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const float tq = ws[t] * st.rcp;
+    q[t] = rintf(tq);
+    dev = fmaxf(dev, fabsf(tq - q[t]));
+  }
+  if (st.exact_only || dev > 0.5f - 0x1p-17f) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float tq = ws[t] * st.rcp;
+      if (st.exact_only || fabsf(tq - rintf(tq)) > 0.5f - 0x1p-17f) q[t] = rintf(ws[t] / st.delta);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) q[t] = __builtin_amdgcn_fmed3f(ZP ? q[t] + z : q[t], qmin, qmax);
+}
+
+// Codes of ws[] for the group maximum m (every |ws| <= m); returns Delta.
 __device__ __forceinline__ float quant8_core(const float (&ws)[8], float m, float qmin,
                                              float qmax, float (&q)[8], bool& underflow) {
   const QuantStep st = quant_step(m, qmax);
@@ -203,13 +249,7 @@ __device__ __forceinline__ float quant8_core(const float (&ws)[8], float m, floa
     for (int t = 0; t < 8; ++t) q[t] = 0.0f;
     return 0.0f;
   }
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const float tq = ws[t] * st.rcp;
-    float qq = rintf(tq);
-    if (st.exact_only || fabsf(tq - qq) > 0.5f - 0x1p-17f) qq = rintf(ws[t] / st.delta);
-    q[t] = fminf(fmaxf(qq, qmin), qmax);
-  }
+  codes8<false>(ws, st, 0.0f, qmin, qmax, q);
   return st.delta;
 }
 
@@ -239,7 +279,7 @@ __device__ __forceinline__ float quant8_g(float (&ws)[8], float ratio, float qmi
     float m = 0.0f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(ws[t]));
-    m = group_max<GL>(m);
+    m = group_absmax<GL>(m);
     const float c = ratio * m;
 #pragma unroll
     for (int t = 0; t < 8; ++t) ws[t] = fminf(fmaxf(ws[t], -c), c);
@@ -248,7 +288,7 @@ __device__ __forceinline__ float quant8_g(float (&ws)[8], float ratio, float qmi
     float m = 0.0f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(ws[t]));
-    m = group_max<GL>(m);
+    m = group_absmax<GL>(m);
     z = 0.0f;
     return quant8_core(ws, m, qmin, qmax, q, underflow);
   }
@@ -270,13 +310,7 @@ __device__ __forceinline__ float quant8_g(float (&ws)[8], float ratio, float qmi
     return 0.0f;
   }
   z = fminf(fmaxf(rintf(-mn / st.delta), 0.0f), qmax);   // once per group: IEEE division
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const float tq = ws[t] * st.rcp;
-    float qq = rintf(tq);
-    if (st.exact_only || fabsf(tq - qq) > 0.5f - 0x1p-17f) qq = rintf(ws[t] / st.delta);
-    q[t] = fminf(fmaxf(qq + z, 0.0f), qmax);
-  }
+  codes8<true>(ws, st, z, 0.0f, qmax, q);
   return st.delta;
 }
 

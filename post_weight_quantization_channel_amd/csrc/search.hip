@@ -232,7 +232,7 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
         const float e0 = (__builtin_fmaf(q[2 * t] * delta, inv[2 * t], -w[r][2 * t])) * cs[2 * t];
         const float e1 =
             (__builtin_fmaf(q[2 * t + 1] * delta, inv[2 * t + 1], -w[r][2 * t + 1])) * cs[2 * t + 1];
-        packed[t] = (uint32_t)f2h(e0) | ((uint32_t)f2h(e1) << 16);
+        packed[t] = f2h2(e0, e1);
       }
       *reinterpret_cast<uint4*>(Estack + i * stride_alpha + (row0 + r) * K + c8 * 8) =
           make_uint4(packed[0], packed[1], packed[2], packed[3]);
