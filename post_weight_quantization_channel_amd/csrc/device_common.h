@@ -150,10 +150,14 @@ __device__ __forceinline__ float row16_sum(float v) {
 //
 //   Delta = fp32(m / qmax),  q = clamp(rint(fp32(ws / Delta)), qmin, qmax)
 //
-// The quotient is formed as t' = fp32(ws * fp32(1/Delta)) first. For |ws| <= m, |t'| <= ~7 and
-// |t' - fp32(ws/Delta)| <= 1.2e-6, so rint(t') equals the specified rint(fp32(ws/Delta)) unless t'
-// lies within that distance of a half-integer; in that case (probability ~1.5e-5 per element) and
-// whenever Delta is not a normal number, the exact quotient is computed by IEEE division.
+// The quotient is formed as t' = fp32(ws * r) first, r = v_rcp_f32(Delta) (within 1 ulp of
+// 1/Delta, so |r Delta - 1| <= 2^-23). Every code decision that can survive the clamp has
+// |t| <= 16 (|ws| <= m in the symmetric form; in the zero-point form quotients beyond the clamp
+// range give the clamped code on both sides), where |t' - fp32(ws/Delta)| <= 16 (2^-23 + 2^-24) +
+// 2^-20 < 3.9e-6 < 2^-17. So rint(t') equals the specified rint(fp32(ws/Delta)) unless t' lies
+// within 2^-17 of a half-integer; in that case (probability ~1.5e-5 per element), and whenever
+// Delta lies outside [2^-126, 2^125] (r then not a normal number), the exact quotient is computed
+// by IEEE division.
 // Power-of-two exponent e for storing values bounded by m in fp16 as v * 2^e: 2^e m lies in
 // [2^14, 2^15), so the values stay finite and keep normal fp16 precision (e = 0 for m = 0 or a
 // non-finite m; e clamped to [-100, 100]).
@@ -170,7 +174,7 @@ __device__ __forceinline__ int escale_for_max(float m) {
 
 struct QuantStep {
   float delta;      // Delta = fp32(m / qmax); 0 for m = 0 or when the quotient underflows
-  float rcp;        // fp32(1 / Delta); 0 when Delta is 0 (every code is then 0)
+  float rcp;        // 1/Delta within 1 ulp; 0 when Delta is 0 (every code is then 0)
   bool exact_only;  // Delta or 1/Delta is not a normal number: always divide
 };
 
@@ -178,8 +182,8 @@ __device__ __forceinline__ QuantStep quant_step(float m, float qmax) {
   QuantStep st;
   st.delta = m / qmax;
   if (st.delta > 0.0f) {
-    st.rcp = 1.0f / st.delta;
-    st.exact_only = !(st.delta >= 0x1p-126f) || !(st.rcp < 0x1p+127f);
+    st.rcp = __builtin_amdgcn_rcpf(st.delta);
+    st.exact_only = !(st.delta >= 0x1p-126f) || !(st.delta <= 0x1p+125f);
   } else {
     st.delta = 0.0f;
     st.rcp = 0.0f;
