@@ -178,9 +178,23 @@ struct QuantStep {
   bool exact_only;  // Delta or 1/Delta is not a normal number: always divide
 };
 
+// Delta = fp32(m / qmax) by one corrected product (Markstein's correction step): y = fp32(1/qmax),
+// d0 = fp32(m y), r = m - qmax d0 (exact, one fma), Delta = fp32(d0 + r y). It equals the IEEE
+// quotient for every fp32 significand of m with qmax in {3, 7, 15} (checked exhaustively against
+// IEEE division), and all three steps scale exactly by powers of two while m lies in
+// [2^-90, 2^100]; outside that range (and for 0, Inf, NaN) the IEEE division is taken.
 __device__ __forceinline__ QuantStep quant_step(float m, float qmax) {
   QuantStep st;
-  st.delta = m / qmax;
+  const float y = 1.0f / qmax;   // loop-invariant: hoisted by the compiler
+  const float d0 = m * y;
+  st.delta = __builtin_fmaf(__builtin_fmaf(-qmax, d0, m), y, d0);
+  if (!(m >= 0x1p-90f && m <= 0x1p100f)) {
+    // a real branch: without the empty volatile asm the compiler computes the division for
+    // every group and selects
+    float mm = m;
+    asm volatile("" : "+v"(mm));
+    st.delta = mm / qmax;
+  }
   if (st.delta > 0.0f) {
     st.rcp = __builtin_amdgcn_rcpf(st.delta);
     st.exact_only = !(st.delta >= 0x1p-126f) || !(st.delta <= 0x1p+125f);
