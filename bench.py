@@ -298,9 +298,9 @@ def main():
         traffic_pass()
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
-              "(the search shards by layer or by output rows with one small exchange; see the "
-              "design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the "
+              "path runs on one GPU (the search would shard by layer, or by output rows with one "
+              "small exchange of per-grid-point loss sums)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
