@@ -599,8 +599,12 @@ __global__ __launch_bounds__(256) void w4a16_tiled_dma_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t tilesN = (N + TBN - 1) / TBN;
-  const int64_t m0 = (int64_t)(blockIdx.x / tilesN) * TBM;
-  const int64_t n0 = (int64_t)(blockIdx.x % tilesN) * TBN;
+  // Workgroup b runs on XCD b % 8: when the grid divides by 8, XCD x takes the x-th contiguous
+  // eighth of the row-major tile order, so the tiles in one XCD's L2 share activation rows.
+  int64_t bl = blockIdx.x;
+  if ((gridDim.x & 7u) == 0) bl = (int64_t)(blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int64_t m0 = (bl / tilesN) * TBM;
+  const int64_t n0 = (bl % tilesN) * TBN;
   const int64_t groups = K / 128;
 
   // ---- tables (plain loads: the compiler's waits here cost nothing) -------------------------
