@@ -327,7 +327,16 @@ __device__ __forceinline__ float quant8_g(float (&ws)[8], float ratio, float qmi
     z = 0.0f;
     return 0.0f;
   }
-  z = fminf(fmaxf(rintf(-mn / st.delta), 0.0f), qmax);   // once per group: IEEE division
+  // z = clamp(rint(fp32(-min / Delta)), 0, qmax) by the fast quotient and the near-half test of
+  // the codes (only |t| <= 16 can decide the clamped value); the IEEE division in a real branch
+  float nm = -mn;
+  const float tz = nm * st.rcp;
+  float zq = rintf(tz);
+  if (st.exact_only || fabsf(tz - zq) > 0.5f - 0x1p-17f) {
+    asm volatile("" : "+v"(nm));
+    zq = rintf(nm / st.delta);
+  }
+  z = __builtin_amdgcn_fmed3f(zq, 0.0f, qmax);
   codes8<true>(ws, st, z, 0.0f, qmax, q);
   return st.delta;
 }
