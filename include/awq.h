@@ -68,10 +68,14 @@ typedef enum { AWQ_F32 = 0, AWQ_F16 = 1, AWQ_BF16 = 2 } awq_dtype;
 enum {
   AWQ_FLAG_NONFINITE_X = 1u << 0,      /* X holds an Inf or NaN                                */
   AWQ_FLAG_NONFINITE_W = 1u << 1,      /* W holds an Inf or NaN                                */
-  AWQ_FLAG_STATS_INEXACT = 1u << 2,    /* a column sum of |X| reached 2^29 (fp16/bf16 X): the   */
-                                       /* fp64 sum is no longer exact / order-free              */
-  AWQ_FLAG_X_F16_RANGE = 1u << 3,      /* fp32/bf16 X has a value beyond fp16 range; the loss   */
-                                       /* contraction runs on fp16 operands                     */
+  AWQ_FLAG_STATS_INEXACT = 1u << 2,    /* a column sum of |X| may have been rounded in fp64, so */
+                                       /* it is no longer order-free: fp16 X with a sum of 2^29 */
+                                       /* or more; bf16 / fp32 X with S >= 2^(53 + e - p), e the */
+                                       /* exponent of the column's smallest non-zero |x|, p = 7  */
+                                       /* (bf16) or 23 (fp32)                                    */
+  AWQ_FLAG_X_F16_RANGE = 1u << 3,      /* fp32/bf16 X has a value beyond fp16 range where X is  */
+                                       /* converted to fp16: the fp16 contractions and the Gram  */
+                                       /* form's operand (not the fp32 contraction)              */
   AWQ_FLAG_SCALE16_OVERFLOW = 1u << 4, /* a group step or s exceeds the fp16 range at packing   */
   AWQ_FLAG_SCALE16_SUBNORMAL = 1u << 5,/* a non-zero group step or s is fp16-subnormal or 0     */
   AWQ_FLAG_NONFINITE_LOSS = 1u << 6,   /* some L_i is not finite                                */
@@ -80,16 +84,23 @@ enum {
                                        /* that group was packed unclipped                       */
   AWQ_FLAG_FOLD_RANGE = 1u << 9,       /* awq_fold_scale turned a finite parameter into Inf      */
   AWQ_FLAG_NO_GRAM = 1u << 10          /* awq_clip_search_gram: the workspace holds no operand of */
-                                       /* a Gram-form search with this K; nothing was written    */
+                                       /* a Gram-form search with this K and n_grid; nothing was */
+                                       /* written                                                */
 };
 
 /* How awq_search_layer evaluates the loss (same value, different contraction):
  *   AWQ_FORM_DIRECT  ||X E_i^T||_F^2 as one fp16 GEMM of X [M,K] with the n_grid error matrices
  *                    (2 M N K n_grid flops);
  *   AWQ_FORM_GRAM    H = X^T X once (about M K^2 flops), then sum_n E_i,n H E_i,n^T for each
- *                    grid point (about N K^2 flops each): the quadratic form the GPTQ section of
- *                    "一文搞懂大模型量化技术：GGUF、GPTQ、AWQ" builds on. Needs K <= 32768 and
- *                    M <= 2^23 - 128. */
+ *                    grid point (about N K^2 flops each): the quadratic form in H = X^T X that
+ *                    the GPTQ section of "量化方案详解"
+ *                    (luoboask.github.io/fde-learning/04-inference-optimization/
+ *                    quantization-schemes/) writes its layer objective as. Needs K <= 32768 and
+ *                    M <= 2^23 - 128.
+ * Layers with N < 256 weight rows or M < 256 tokens take, in either form, an fp32 contraction
+ * on the vector ALUs instead (X read in its own dtype, fp32 error matrices, fp64 sums): with few
+ * rows or tokens the fp16 rounding of E does not average out below 1e-4 of the loss. The Gram form still forms its operand
+ * there, for awq_clip_search_gram. */
 enum { AWQ_FORM_DIRECT = 0, AWQ_FORM_GRAM = 1 };
 
 typedef struct {
@@ -121,9 +132,13 @@ int32_t awq_version(void);
  *   over calibration samples).
  * X      [M, K] with row stride ldx elements (ldx >= K, ldx % 8 == 0, K % 8 == 0), dtype xdt
  *        (AWQ_F16, AWQ_BF16 or AWQ_F32); 16-byte aligned.
- * sx     out, fp32 [K]: sx[k] = fp32( (sum_m |X[m,k]|) / M ), the sum accumulated in fp64
- *        (exact for fp16/bf16 while below 2^29, see AWQ_FLAG_STATS_INEXACT) and the division
- *        done in fp64 before the single rounding to fp32.
+ * sx     out, fp32 [K]: sx[k] = fp32( (sum_m |X[m,k]|) / M ), the sum accumulated in fp64 and
+ *        the division done in fp64 before the single rounding to fp32. The sum is exact, hence
+ *        independent of the order of the additions, unless AWQ_FLAG_STATS_INEXACT is raised:
+ *        for fp16 X while it stays below 2^29 (every |x| is a multiple of 2^-24); for bf16 and
+ *        fp32 X while it stays below 2^(53 + e - p) (every |x| of the column is a multiple of
+ *        2^(e - p), e the exponent of its smallest non-zero |x|, p = 7 or 23), which wide
+ *        dynamic ranges can break.
  * flags  in/out, uint32 [1]: NONFINITE_X, STATS_INEXACT.
  * ws     device workspace of at least awq_act_stats_workspace_bytes(M, K) bytes.
  * Errors: NULL pointers -> AWQ_ERR_NULL; M < 1, K < 8, shape/stride rules -> AWQ_ERR_SHAPE;
@@ -148,7 +163,9 @@ awq_status awq_act_stats(const void* X, awq_dtype xdt, int64_t M, int64_t K, int
  *   L_i = ||X E_i^T||_F^2 / (M N), E_i = q Delta / s_i - W, contracted on fp16 operands with
  *   fp32 accumulation and fp64 reduction (relative error ~1e-5). In the Gram form the fp16
  *   operands are the correlation matrix D^-1 H D^-1 (D = diag(sqrt(H_kk))) and E_i D; H itself
- *   is accumulated in fp32 over token chunks and summed in fp64.
+ *   is accumulated in fp32 over token chunks and summed in fp64. Layers with N < 256 or
+ *   M < 256 use fp32 operands instead (see AWQ_FORM_GRAM above; relative error ~1e-6).
+ *   The scale table s_i is left in the workspace: fp32 [n_grid][K] at byte offset 256.
  * losses out, fp64 [n_grid]; best out, int32 [1] = i*; s_best out, fp32 [K] = s_{i*}.
  * flags  in/out: NONFINITE_W, X_F16_RANGE, NONFINITE_LOSS.
  * ws     device workspace of at least awq_search_workspace_bytes(M, N, K, xdt, cfg) bytes
@@ -289,13 +306,13 @@ awq_status awq_clip_search(const void* W, awq_dtype wdt, int64_t N, int64_t K, c
  * W, s, clip, clip_err, flags  as in awq_clip_search (W: any weight that read that X, e.g. each
  *          of q, k, v after awq_search_layers).
  * cfg      as in awq_clip_search, with form == AWQ_FORM_GRAM and the n_grid of the search (they
- *          locate the operand in its workspace).
+ *          locate the operand in its workspace; the search records both there).
  * search_ws, search_ws_bytes  the search's workspace (device), at least
  *          awq_clip_search_gram_ws_bytes(K, cfg) bytes; read only. The last call that wrote it
  *          must be that search, with the same K and cfg->n_grid. Checked on the device: if the
- *          workspace holds no Gram-form operand for this K (a direct-form search, another K, or
- *          a search that did not reach that point), AWQ_FLAG_NO_GRAM is raised and clip and
- *          clip_err are not written.
+ *          workspace holds no Gram-form operand for this K and n_grid (a direct-form search,
+ *          another K or grid size, or a search that did not reach that point),
+ *          AWQ_FLAG_NO_GRAM is raised and clip and clip_err are not written.
  * Limits: as awq_clip_search, and K <= 32768 (the Gram form's limit).
  * Errors: AWQ_ERR_NULL, AWQ_ERR_SHAPE, AWQ_ERR_DTYPE, AWQ_ERR_CONFIG (also form != GRAM),
  *         AWQ_ERR_WORKSPACE.

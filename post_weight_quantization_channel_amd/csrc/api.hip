@@ -35,8 +35,16 @@ constexpr int64_t kMaxW4A16K = 12288;   // the W4A16 kernel keeps per-channel ta
 constexpr int64_t kMaxGramK = 32768;
 constexpr int64_t kMaxGramMp = (int64_t(1) << 23) - awq::kGramMAlign;
 
+// Layers with fewer than awq::kPreciseRows weight rows or awq::kPreciseTokens tokens (256 each)
+// take the losses from the fp32 vector-ALU contraction (lossvalu.hip) on an fp32 error stack, in either
+// form; the Gram form still prepares its operand (awq_clip_search_gram reads it).
+bool precise_path(int64_t M, int64_t N) {
+  return N < awq::kPreciseRows || M < awq::kPreciseTokens;
+}
+
 struct SearchLayout {
   size_t ctrl, S, X16, E, partials, total;
+  bool precise;                    // fp32 error stack and the vector-ALU contraction
   size_t d64, d32, B, Xt, Hpart;   // Gram form only (Xt and Hpart share memory with E)
   size_t stats;                    // chunk partials of s_X when the search takes it (in Hpart
                                    // or in E: both are written only after s_X is final)
@@ -50,17 +58,19 @@ struct SearchLayout {
 SearchLayout search_layout(int64_t M, int64_t N, int64_t K, awq_dtype xdt, int n_grid,
                            int form) {
   SearchLayout L{};
+  L.precise = precise_path(M, N);
   const int64_t tilesN = (N + awq::kLossBN - 1) / awq::kLossBN;
   size_t off = 0;
   L.ctrl = off;
   off += align_up(sizeof(awq::SearchCtrl));
   L.S = off;
   off += align_up((size_t)n_grid * (size_t)K * sizeof(float));
-  const size_t e_bytes = align_up((size_t)n_grid * (size_t)N * (size_t)K * 2);
-  const size_t stats_bytes = align_up((size_t)awq::stats_chunks(M) * (size_t)K * sizeof(double));
+  const size_t e_bytes = align_up((size_t)n_grid * (size_t)N * (size_t)K * (L.precise ? 4 : 2));
+  const int64_t valu_tiles = awq::loss_valu_tiles(M, N);
+  const size_t stats_bytes = align_up(awq::stats_workspace_bytes(M, K));
   if (form == AWQ_FORM_GRAM) {
     L.plan = awq::gram_plan(M, K);
-    L.tiles_per_alpha = tilesN * L.plan.t;
+    L.tiles_per_alpha = L.precise ? valu_tiles : tilesN * L.plan.t;
     L.d64 = off;
     off += align_up((size_t)K * sizeof(double));
     L.d32 = off;
@@ -80,9 +90,9 @@ SearchLayout search_layout(int64_t M, int64_t N, int64_t K, awq_dtype xdt, int n
     off += (xt_bytes + h_bytes > e_bytes) ? xt_bytes + h_bytes : e_bytes;
   } else {
     const int64_t tilesM = (M + awq::kLossBM - 1) / awq::kLossBM;
-    L.tiles_per_alpha = tilesM * tilesN;
+    L.tiles_per_alpha = L.precise ? valu_tiles : tilesM * tilesN;
     L.X16 = off;
-    if (xdt != AWQ_F16) off += align_up((size_t)M * (size_t)K * 2);
+    if (xdt != AWQ_F16 && !L.precise) off += align_up((size_t)M * (size_t)K * 2);
     L.E = off;
     L.stats = off;
     off += (e_bytes > stats_bytes) ? e_bytes : stats_bytes;
@@ -116,7 +126,7 @@ int32_t awq_version(void) { return 10600; }
 
 size_t awq_act_stats_workspace_bytes(int64_t M, int64_t K) {
   if (M < 1 || K < 1 || M > kMaxDim || K > kMaxDim) return 0;
-  return align_up((size_t)awq::stats_chunks(M) * (size_t)K * sizeof(double));
+  return align_up(awq::stats_workspace_bytes(M, K));
 }
 
 awq_status awq_act_stats(const void* X, awq_dtype xdt, int64_t M, int64_t K, int64_t ldx,
@@ -128,8 +138,7 @@ awq_status awq_act_stats(const void* X, awq_dtype xdt, int64_t M, int64_t K, int
       ldx > kMaxDim || !aligned16(X) || awq::stats_chunks(M) > 65535)
     return AWQ_ERR_SHAPE;
   if (!ws || ws_bytes < awq_act_stats_workspace_bytes(M, K)) return AWQ_ERR_WORKSPACE;
-  return hip_status(awq::launch_stats(X, (int)xdt, M, K, ldx, sx, flags,
-                                      static_cast<double*>(ws), stream));
+  return hip_status(awq::launch_stats(X, (int)xdt, M, K, ldx, sx, flags, ws, stream));
 }
 
 namespace {
@@ -198,7 +207,9 @@ awq_status search_impl(const void* const* Ws, const int64_t* Ns, int n_w, awq_dt
   auto* stats = reinterpret_cast<double*>(base + L.stats);
   auto* Xt = reinterpret_cast<uint16_t*>(base + L.Xt);
   const bool gram = cfg->form == AWQ_FORM_GRAM;
-  const float* dcol = gram ? reinterpret_cast<const float*>(base + L.d32) : nullptr;
+  // the Gram form's fp16 stack holds E d (column-scaled); the fp32 stack of small layers holds E
+  const float* dcol = (gram && !L.precise) ? reinterpret_cast<const float*>(base + L.d32)
+                                           : nullptr;
   const uint16_t* B = reinterpret_cast<const uint16_t*>(base + L.B);
   const uint16_t* X16 = static_cast<const uint16_t*>(X);
 
@@ -218,12 +229,11 @@ awq_status search_impl(const void* const* Ws, const int64_t* Ns, int n_w, awq_dt
         e = awq::launch_gram_transpose(X, (int)xdt, M, K, L.plan.Mp, Xt,
                                        fused ? stats : nullptr, flags, stream);
       if (fused && e == hipSuccess)
-        e = awq::launch_stats_final(stats, awq::stats_chunks(M), M, K, (int)xdt, sx_out, flags,
-                                    stream);
+        e = awq::launch_stats_final(stats, awq::stats_chunks(M), M, K, sx_out, flags, stream);
     } else {
       if (sx_out && e == hipSuccess)
         e = awq::launch_stats(X, (int)xdt, M, K, K, sx_out, flags, stats, stream);
-      if (e == hipSuccess && xdt != AWQ_F16) {
+      if (e == hipSuccess && xdt != AWQ_F16 && !L.precise) {
         auto* x16 = reinterpret_cast<uint16_t*>(base + L.X16);
         e = awq::launch_x_to_f16(X, (int)xdt, M * K, x16, flags, stream);
         X16 = x16;
@@ -262,15 +272,20 @@ awq_status search_impl(const void* const* Ws, const int64_t* Ns, int n_w, awq_dt
   mark(2 * 5);
   int64_t row = 0;
   for (int l = 0; l < n_w && e == hipSuccess; ++l) {
+    void* dst = L.precise ? static_cast<void*>(reinterpret_cast<float*>(base + L.E) + row * K)
+                          : static_cast<void*>(E + row * K);
     e = awq::launch_quantize_stack(Ws[l], (int)wdt, Ns[l], K, S, cfg->n_grid, cfg->bits,
-                                   cfg->group, cfg->zero_point != 0, dcol, ctrl, E + row * K, N,
-                                   flags, stream);
+                                   cfg->group, cfg->zero_point != 0, dcol, ctrl, dst, L.precise,
+                                   N, flags, stream);
     row += Ns[l];
   }
   mark(2 * 5 + 1);
   mark(2 * 6);
   if (e == hipSuccess) {
-    if (gram)
+    if (L.precise)
+      e = awq::launch_loss_valu(X, (int)xdt, M, K, reinterpret_cast<const float*>(base + L.E), N,
+                                cfg->n_grid, partials, stream);
+    else if (gram)
       e = awq::launch_gram_loss(E, N, K, B, cfg->n_grid, partials, stream);
     else
       e = awq::launch_lossgemm(X16, M, K, E, N, cfg->n_grid, partials, stream);
@@ -455,7 +470,7 @@ awq_status awq_clip_search(const void* W, awq_dtype wdt, int64_t N, int64_t K, c
                                           nullptr, flags, stream, nullptr);
   if (e == hipSuccess)
     e = awq::launch_clip_search(W, (int)wdt, N, K, s, d32, Bd, (int64_t)awq::kLossBM * awq::kLossBN,
-                                awq::kLossBN, nullptr,
+                                awq::kLossBN, nullptr, 0,
                                 cfg->n_clip, cfg->clip_min, cfg->bits, cfg->group,
                                 cfg->zero_point != 0, clip, clip_err, flags, stream);
   return hip_status(e);
@@ -491,8 +506,8 @@ awq_status awq_clip_search_gram(const void* W, awq_dtype wdt, int64_t N, int64_t
   return hip_status(awq::launch_clip_search(
       W, (int)wdt, N, K, s, reinterpret_cast<const float*>(base + L.d32),
       reinterpret_cast<const uint16_t*>(base + L.B), (int64_t)awq::kLossBN * K + awq::kLossBN, K,
-      &ctrl->gram_k, cfg->n_clip, cfg->clip_min, cfg->bits, cfg->group, cfg->zero_point != 0, clip,
-      clip_err, flags, stream));
+      ctrl, cfg->n_grid, cfg->n_clip, cfg->clip_min, cfg->bits, cfg->group,
+      cfg->zero_point != 0, clip, clip_err, flags, stream));
 }
 
 awq_status awq_fold_scale(void* prev, awq_dtype dtype, int64_t rows, int64_t cols, int64_t ld,

@@ -46,7 +46,7 @@ template <int DT, int GS, bool ZP>
 __global__ __launch_bounds__(256) void clip_search_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s,
     const float* __restrict__ d32, const uint16_t* __restrict__ Bd, int64_t bd_block,
-    int64_t bd_pitch, const uint32_t* __restrict__ gram_k, int n_clip, float clip_min,
+    int64_t bd_pitch, const SearchCtrl* __restrict__ ctrl, int n_grid, int n_clip, float clip_min,
     float qmin, float qmax, float* __restrict__ clip, float* __restrict__ clip_err,
     uint32_t* __restrict__ flags) {
   constexpr int ES = (DT == kF32) ? 4 : 2;
@@ -64,8 +64,9 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
   const int i = lane & 15, q = lane >> 4;
 
   // with the operand of a preceding Gram-form search: that search must have been the last to
-  // write it, for this K (uniform over the grid: every workgroup leaves, one raises the flag)
-  if (gram_k && *gram_k != (uint32_t)K) {
+  // write it, for this K and this grid size (the operand's offsets follow from both; uniform
+  // over the grid: every workgroup leaves, one raises the flag)
+  if (ctrl && (ctrl->gram_k != (uint32_t)K || ctrl->n_grid != (uint32_t)n_grid)) {
     if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) atomicOr(flags, kFlagNoGram);
     return;
   }
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
 
 hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, const float* s,
                               const float* d32, const uint16_t* Bd, int64_t bd_block,
-                              int64_t bd_pitch, const uint32_t* gram_k, int n_clip,
+                              int64_t bd_pitch, const SearchCtrl* ctrl, int n_grid, int n_clip,
                               float clip_min, int bits, int group, bool zero_point, float* clip,
                               float* clip_err, uint32_t* flags, hipStream_t stream) {
   const float qmax = zero_point ? (float)((1 << bits) - 1) : (float)((1 << (bits - 1)) - 1);
@@ -244,7 +245,7 @@ hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, co
   dim3 grid((unsigned)((N + kClipRows - 1) / kClipRows), (unsigned)(K / group));
 #define AWQ_CLIP(DT_, GS_, ZP_)                                                                  \
   clip_search_kernel<DT_, GS_, ZP_><<<grid, 256, 0, stream>>>(                                    \
-      W, N, K, s, d32, Bd, bd_block, bd_pitch, gram_k, n_clip, clip_min, qmin, qmax, clip,       \
+      W, N, K, s, d32, Bd, bd_block, bd_pitch, ctrl, n_grid, n_clip, clip_min, qmin, qmax, clip,  \
       clip_err, flags)
   if (dtype == kF32) {
     if (group == 64) {

@@ -1,8 +1,9 @@
 // Gram form of the AWQ loss: the objective of the AWQ notes (bg51717.github.io/14592, section
 // 方法), L(s) = ||Q(W s)(s^-1 X) - W X||_F^2 / (M N), written with E = Q(W s)/s - W as
 //   L = sum_n E_n H E_n^T / (M N),   H = X^T X,
-// the quadratic form that GPTQ ("一文搞懂大模型量化技术：GGUF、GPTQ、AWQ", section on GPTQ) builds
-// its layer objective on. H is computed once per layer; each grid point then costs a K x K
+// the quadratic form in H = X^T X that the GPTQ section of "量化方案详解"
+// (luoboask.github.io/fde-learning/04-inference-optimization/quantization-schemes/) writes its
+// layer objective as. H is computed once per layer; each grid point then costs a K x K
 // contraction instead of an M x K one.
 //
 // Conditioning for fp16 operands. With d_k = sqrt(H_kk) (d_k = 0 for a channel that is zero in

@@ -11,11 +11,14 @@ namespace awq {
 // ---- activation statistics ----
 constexpr int kStatsRowsPerChunk = 256;
 int64_t stats_chunks(int64_t M);
-// the second pass of launch_stats on chunk partials [chunks][K] (256 rows per chunk)
+// workspace of launch_stats: fp64 chunk partials [chunks][K], then (bf16 / fp32 X) the smallest
+// exponent field per chunk and column, uint8 [chunks][K]
+size_t stats_workspace_bytes(int64_t M, int64_t K);
+// the second pass of launch_stats on fp16 chunk partials [chunks][K] (256 rows per chunk)
 hipError_t launch_stats_final(const double* partials, int64_t chunks, int64_t M, int64_t K,
-                              int dtype, float* sx, uint32_t* flags, hipStream_t stream);
+                              float* sx, uint32_t* flags, hipStream_t stream);
 hipError_t launch_stats(const void* X, int dtype, int64_t M, int64_t K, int64_t ldx, float* sx,
-                        uint32_t* flags, double* partials, hipStream_t stream);
+                        uint32_t* flags, void* ws, hipStream_t stream);
 
 // ---- search ----
 constexpr int kLossBM = 256;
@@ -26,6 +29,8 @@ struct SearchCtrl {        // lives at the start of the search workspace
   uint32_t absmax_bits;    // max |W| as fp32 bits (atomicMax on non-negative floats)
   uint32_t done;           // grid points whose loss is final (finalize's completion count)
   uint32_t gram_k;         // K of the Gram-form operand B in this workspace (0: none)
+  uint32_t n_grid;         // grid points of the search that last wrote this workspace (the
+                           // offsets of its Gram operand depend on it)
 };
 
 // Gram form (gram.hip): H = X^T X over token chunks, then the lower-triangular operand B.
@@ -70,11 +75,21 @@ hipError_t launch_x_to_f16(const void* X, int dtype, int64_t count, uint16_t* X1
                            uint32_t* flags, hipStream_t stream);
 // E_i * 2^escale (dcol == nullptr) or E_i[n,k] * dcol[k] * 2^escale, for the N rows of W, written
 // to rows 0..N-1 of Estack whose grid-point slices are ld_rows rows apart (ld_rows >= N: several
-// weights fill one stack)
+// weights fill one stack); fp16, or fp32 with f32_stack (then dcol must be nullptr)
 hipError_t launch_quantize_stack(const void* W, int dtype, int64_t N, int64_t K, const float* S,
                                  int n_grid, int bits, int group, bool zero_point,
-                                 const float* dcol, const SearchCtrl* ctrl, uint16_t* Estack,
-                                 int64_t ld_rows, uint32_t* flags, hipStream_t stream);
+                                 const float* dcol, const SearchCtrl* ctrl, void* Estack,
+                                 bool f32_stack, int64_t ld_rows, uint32_t* flags,
+                                 hipStream_t stream);
+// Layers with fewer rows or tokens than this take the fp32 vector-ALU contraction.
+constexpr int64_t kPreciseRows = 256;
+constexpr int64_t kPreciseTokens = 256;
+// per-grid-point partials of launch_loss_valu: 256-token blocks x 16-row chunks
+int64_t loss_valu_tiles(int64_t M, int64_t N);
+// the loss of every grid point on an fp32 error stack [n_grid][N][K] (times 2^escale), X [M, K]
+// read in its own dtype
+hipError_t launch_loss_valu(const void* X, int xdt, int64_t M, int64_t K, const float* Estack,
+                            int64_t N, int n_grid, double* partials, hipStream_t stream);
 hipError_t launch_lossgemm(const uint16_t* X16, int64_t M, int64_t K, const uint16_t* Estack,
                            int64_t N, int n_grid, double* partials, hipStream_t stream);
 hipError_t launch_finalize(const double* partials, int64_t tiles_per_alpha, int n_grid,
@@ -100,11 +115,12 @@ hipError_t launch_fold(void* prev, int dtype, int64_t rows, int64_t cols, int64_
 // of the correlation operand and d = sqrt(diag H). The diagonal block a of the operand starts
 // at Bd + a * bd_block with rows bd_pitch elements apart ([t][256][256] from the diagonal-only
 // preparation: 65536 and 256; the full [K][K] operand of a Gram-form search: 256 K + 256 and K).
-// gram_k: nullptr, or the workspace's record of the K its operand was formed for; when it differs
-// from K nothing is written and AWQ_FLAG_NO_GRAM is raised.
+// ctrl: nullptr, or the control block of the Gram-form search whose operand is read; when its
+// record of K or of the grid size differs from K and n_grid nothing is written and
+// AWQ_FLAG_NO_GRAM is raised.
 hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, const float* s,
                               const float* d32, const uint16_t* Bd, int64_t bd_block,
-                              int64_t bd_pitch, const uint32_t* gram_k, int n_clip,
+                              int64_t bd_pitch, const SearchCtrl* ctrl, int n_grid, int n_clip,
                               float clip_min, int bits, int group, bool zero_point, float* clip,
                               float* clip_err, uint32_t* flags, hipStream_t stream);
 

@@ -29,6 +29,7 @@ __global__ __launch_bounds__(256) void search_prep_kernel(const float* __restric
     ctrl->absmax_bits = 0u;
     ctrl->done = 0u;
     ctrl->gram_k = 0u;   // set again by the Gram form's finish pass
+    ctrl->n_grid = (uint32_t)n_grid;
   }
   if (idx >= (int64_t)n_grid * K) return;
   const int i = (int)(idx / K);
@@ -169,12 +170,14 @@ constexpr int kQuantRows = 4;  // rows per thread in quantize_stack
 // 128 channels; 8 for 64), so the group maximum (and minimum) is four (three) DPP steps. The
 // scale row s_i for the thread's 8 channels is loaded once per alpha and reused for all its rows.
 // Stores: 16 bytes per lane, 1 KiB per wave, contiguous. ZP: zero-point codes, E = (q - z) Delta
-// / s - w.
-template <int DT, bool COL, int GL, bool ZP>
+// / s - w. F32: the stack is fp32 (the vector-ALU contraction of small layers) and E is formed as
+// fp32(fp32(fp32(q Delta) / s) - w) with an IEEE quotient, times the power of two.
+template <int DT, bool COL, int GL, bool ZP, bool F32>
 __global__ __launch_bounds__(256) void quantize_stack_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ S, int n_grid,
     float qmin, float qmax, const float* __restrict__ dcol, const SearchCtrl* __restrict__ ctrl,
-    uint16_t* __restrict__ Estack, int64_t ld_rows, uint32_t* __restrict__ flags) {
+    void* __restrict__ Estack_, int64_t ld_rows, uint32_t* __restrict__ flags) {
+  static_assert(!(F32 && COL), "the fp32 stack holds E itself");
   constexpr int ES = (DT == kF32) ? 4 : 2;
   const int64_t chunks = K / 8;
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -224,6 +227,16 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
 #pragma unroll
         for (int t = 0; t < 8; ++t) q[t] -= z;   // exact: small integers
       }
+      if constexpr (F32) {
+        float ev[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) ev[t] = ((q[t] * delta) / s[t] - w[r][t]) * cs[t];
+        float* dst = static_cast<float*>(Estack_) + i * stride_alpha + (row0 + r) * K + c8 * 8;
+        *reinterpret_cast<float4*>(dst) = make_float4(ev[0], ev[1], ev[2], ev[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(ev[4], ev[5], ev[6], ev[7]);
+        continue;
+      }
+      uint16_t* __restrict__ Estack = static_cast<uint16_t*>(Estack_);
       uint32_t packed[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -240,13 +253,13 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
   }
 }
 
-template <int DT, bool COL>
+template <int DT, bool COL, bool F32>
 static void qs_dispatch(int group, bool zp, unsigned blocks, hipStream_t stream, const void* W,
                         int64_t N, int64_t K, const float* S, int n_grid, float qmin, float qmax,
-                        const float* dcol, const SearchCtrl* ctrl, uint16_t* Estack,
+                        const float* dcol, const SearchCtrl* ctrl, void* Estack,
                         int64_t ld_rows, uint32_t* flags) {
 #define AWQ_QS(GL_, ZP_)                                                                         \
-  quantize_stack_kernel<DT, COL, GL_, ZP_><<<blocks, 256, 0, stream>>>(                          \
+  quantize_stack_kernel<DT, COL, GL_, ZP_, F32><<<blocks, 256, 0, stream>>>(                     \
       W, N, K, S, n_grid, qmin, qmax, dcol, ctrl, Estack, ld_rows, flags)
   if (group == 64) {
     if (zp) AWQ_QS(8, true); else AWQ_QS(8, false);
@@ -258,27 +271,25 @@ static void qs_dispatch(int group, bool zp, unsigned blocks, hipStream_t stream,
 
 hipError_t launch_quantize_stack(const void* W, int dtype, int64_t N, int64_t K, const float* S,
                                  int n_grid, int bits, int group, bool zero_point,
-                                 const float* dcol, const SearchCtrl* ctrl, uint16_t* Estack,
-                                 int64_t ld_rows, uint32_t* flags, hipStream_t stream) {
+                                 const float* dcol, const SearchCtrl* ctrl, void* Estack,
+                                 bool f32_stack, int64_t ld_rows, uint32_t* flags,
+                                 hipStream_t stream) {
   const float qmax = zero_point ? (float)((1 << bits) - 1) : (float)((1 << (bits - 1)) - 1);
   const float qmin = zero_point ? 0.0f : -(float)(1 << (bits - 1));
   const int64_t threads = ((N + kQuantRows - 1) / kQuantRows) * (K / 8);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
-  if (dtype == kF32) {
-    if (dcol)
-      qs_dispatch<kF32, true>(group, zero_point, blocks, stream, W, N, K, S, n_grid, qmin, qmax,
-                              dcol, ctrl, Estack, ld_rows, flags);
-    else
-      qs_dispatch<kF32, false>(group, zero_point, blocks, stream, W, N, K, S, n_grid, qmin, qmax,
-                               dcol, ctrl, Estack, ld_rows, flags);
+#define AWQ_QSD(DT_, COL_, F32_)                                                                 \
+  qs_dispatch<DT_, COL_, F32_>(group, zero_point, blocks, stream, W, N, K, S, n_grid, qmin, qmax, \
+                               dcol, ctrl, Estack, ld_rows, flags)
+  if (f32_stack) {
+    if (dcol) return hipErrorInvalidValue;   // the fp32 stack holds E itself
+    if (dtype == kF32) AWQ_QSD(kF32, false, true); else AWQ_QSD(kF16, false, true);
+  } else if (dtype == kF32) {
+    if (dcol) AWQ_QSD(kF32, true, false); else AWQ_QSD(kF32, false, false);
   } else {
-    if (dcol)
-      qs_dispatch<kF16, true>(group, zero_point, blocks, stream, W, N, K, S, n_grid, qmin, qmax,
-                              dcol, ctrl, Estack, ld_rows, flags);
-    else
-      qs_dispatch<kF16, false>(group, zero_point, blocks, stream, W, N, K, S, n_grid, qmin, qmax,
-                               dcol, ctrl, Estack, ld_rows, flags);
+    if (dcol) AWQ_QSD(kF16, true, false); else AWQ_QSD(kF16, false, false);
   }
+#undef AWQ_QSD
   return hipGetLastError();
 }
 

@@ -118,12 +118,21 @@ def loss_exact(X, W, codes, deltas, s, group: int) -> Fraction:
     return tot / (M * N)
 
 
+F16_MAX = Fraction(65504)
+F16_OVERFLOW = Fraction(65520)   # 65504 + half an ulp of the top binade (2^15 / 2^10 / 2)
+
+
 def rn16(fr: Fraction) -> np.float16:
-    """Round an exact rational to the nearest fp16 value, ties to the even significand."""
+    """Round an exact rational to the nearest fp16 value, ties to the even significand; IEEE 754
+    overflow: a magnitude of at least 65520 (where rounding with an unbounded exponent would give
+    2^16) becomes an infinity of that sign."""
     if fr == 0:
         return np.float16(0.0)
+    if abs(fr) >= F16_OVERFLOW:
+        return np.float16(np.inf) if fr > 0 else np.float16(-np.inf)
     f = np.float16(float(fr))
-    cands = [f, np.nextafter(f, np.float16(np.inf)), np.nextafter(f, np.float16(-np.inf))]
+    with np.errstate(over="ignore"):
+        cands = [f, np.nextafter(f, np.float16(np.inf)), np.nextafter(f, np.float16(-np.inf))]
     best = None
     for c in cands:
         if not np.isfinite(c):
@@ -154,3 +163,24 @@ def quantize_group_exact_zp(w, s, bits: int, ratio=None):
     z = min(max(round_half_even(Fraction(float(rn32(-mn / d)))), 0), qmax_u)
     codes = [min(max(round_half_even(Fraction(float(rn32(v / d)))) + z, 0), qmax_u) for v in ws]
     return codes, delta, z
+
+
+def stats_sum_may_round(X, mantissa_bits: int) -> bool:
+    """True when some column sum of |X| can round in fp64 for bf16 (7 fraction bits) or fp32 (23)
+    values: every |x| of a column is a multiple of 2^(e - 127 - p), e the smallest exponent field
+    of its non-zero values (1 for subnormals), so partial sums below 2^(53 + e - 127 - p) are
+    exact. The column sum itself is taken with math.fsum (correctly rounded)."""
+    import math
+    X = np.asarray(X, dtype=np.float32)
+    b = np.abs(X).view(np.uint32)
+    f = (b >> 23).astype(np.int64)
+    f = np.where(f == 0, 1, f)
+    f = np.where(b == 0, 255, f)
+    e = f.min(axis=0)
+    for k in range(X.shape[1]):
+        if e[k] == 255:
+            continue
+        S = math.fsum(np.abs(X[:, k]).astype(np.float64).tolist())
+        if S >= math.ldexp(1.0, int(53 + e[k] - 127 - mantissa_bits)):
+            return True
+    return False

@@ -60,8 +60,9 @@ def cfg(bits=4, group=128, n_grid=20, s_floor=1e-5, form=0, n_clip=11, clip_min=
 
 
 def test_workspace_queries(lib):
-    # stats: one fp64 partial per (256-row chunk, column)
-    assert lib.awq_act_stats_workspace_bytes(65536, 4096) == 256 * 4096 * 8
+    # stats: one fp64 partial and one exponent byte per (256-row chunk, column)
+    assert lib.awq_act_stats_workspace_bytes(65536, 4096) == 256 * 4096 * 9
+    assert lib.awq_act_stats_workspace_bytes(300, 72) == 1280 + 256   # each part 256-aligned
     assert lib.awq_act_stats_workspace_bytes(0, 4096) == 0
     ws = lib.awq_search_workspace_bytes(65536, 4096, 4096, _lib.AWQ_F16, cfg())
     estack = 20 * 4096 * 4096 * 2
@@ -71,6 +72,11 @@ def test_workspace_queries(lib):
     assert lib.awq_search_workspace_bytes(256, 512, 512, _lib.AWQ_F16, cfg(bits=5)) == 0
     assert lib.awq_search_workspace_bytes(256, 512, 512, _lib.AWQ_F16, cfg(n_grid=1)) == 0
     assert lib.awq_search_workspace_bytes(256, 512, 512, _lib.AWQ_F16, cfg(form=2)) == 0
+    # fewer than 256 rows or tokens: an fp32 error stack and no fp16 copy of X
+    small = lib.awq_search_workspace_bytes(4096, 255, 1024, _lib.AWQ_F32, cfg())
+    assert 20 * 255 * 1024 * 4 < small < 20 * 255 * 1024 * 4 + 2**20
+    small = lib.awq_search_workspace_bytes(255, 512, 1024, _lib.AWQ_F32, cfg())
+    assert 20 * 512 * 1024 * 4 < small < 20 * 512 * 1024 * 4 + 2**20
 
 
 def _gram_chunks(M, K):

@@ -7,10 +7,10 @@ Every other configuration goes through awq_stats_search_layer (s_X and the searc
 in the Gram form with fp16 X the column sums come from the transpose pass), the rest through
 awq_act_stats then awq_search_layer.
 
-Per configuration: s_X bit-exact; every per-alpha loss within the bar of the parity tests (1e-4
-relative with at least 64 weight rows, 2e-3 below); alpha* equal to the oracle's unless the
-oracle's two best losses are within twice that bar; at the GPU's alpha*, codes, packed words,
-fp16 steps and zero points bit-exact; W4A16 on the packed result within 2e-3 of the oracle's
+Per configuration: s_X bit-exact; every per-alpha loss within 1e-4 relative of the oracle's
+(layers with fewer than 256 rows or tokens take the fp32 contraction); alpha* equal to the
+oracle's unless the oracle's two best losses are within twice that bar; at the GPU's alpha*,
+codes, packed words, fp16 steps and zero points bit-exact; W4A16 on the packed result within 2e-3 of the oracle's
 (when K is a multiple of 128, which W4A16 needs with groups of 64).
 """
 import numpy as np
@@ -18,8 +18,10 @@ import pytest
 import torch
 
 import oracle
+from tests import exact_ref as ex
 
 pytestmark = pytest.mark.gpu
+FLAG_STATS_INEXACT = 1 << 2
 
 def _configs(count=24, seed=2024):
     g = np.random.default_rng(seed)
@@ -93,14 +95,18 @@ def test_fuzz_path_against_oracle(awq, cfg):
         Y = awq.w4a16_gemm(torch.from_numpy(A).cuda(), p.qweight, p.scales16, p.s16,
                            group=cfg["group"], zeros=p.zeros)
     torch.cuda.synchronize()
-    assert int(flags.item()) == 0
+    # bf16 / fp32 column sums that may round in fp64 are flagged (then s_X is the sum in this
+    # library's order; it still matches the oracle's here)
+    bits = {"f16": None, "bf16": 7, "f32": 23}[cfg["xdt"]]
+    may_round = bits is not None and ex.stats_sum_may_round(X, bits)
+    assert int(flags.item()) == (FLAG_STATS_INEXACT if may_round else 0)
 
     sx_o = oracle.act_stats(X)
     assert np.array_equal(sx.cpu().numpy(), sx_o)
     form = "gram" if 2 * cfg["m"] > cfg["k"] else "direct"
     orc = oracle.search_layer(W, X, sx_o, bits=cfg["bits"], group=cfg["group"], form=form,
                               zero_point=cfg["zp"])
-    tol = 1e-4 if cfg["n"] >= 64 else 2e-3
+    tol = 1e-4
     lg = res.losses.cpu().numpy()
     live = orc["losses"] > 0
     rel = np.abs(lg - orc["losses"])[live] / orc["losses"][live]

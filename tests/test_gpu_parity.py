@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import workloads
+from tests import exact_ref as ex
 
 pytestmark = pytest.mark.gpu
 
@@ -42,13 +43,6 @@ def host(t):
 def say(*a):
     print("  ", *a, flush=True)
 
-
-# The contraction runs on fp16 error matrices: each E entry carries a relative rounding error of
-# at most 2^-12, so one output's squared error is off by up to ~2 * 2^-12 ~ 5e-4 relative when a
-# few input channels dominate it. Over many weight rows these errors are independent and the
-# loss error shrinks like 1/sqrt(rows) (3-5e-5 at 384 rows, below 1e-4 for every benchmarked
-# layer). Layers with only a handful of rows get the single-output bound instead.
-TINY_ROWS_RTOL = 2e-3
 
 
 def check_alpha(losses_gpu, losses_orc, best_gpu, best_orc, tol=LOSS_RTOL):
@@ -131,11 +125,98 @@ def test_search_parity(awq, name, make, bits, n_grid, form):
     orc = oracle.search_layer(W, Xref, sx_o, bits=bits, n_grid=n_grid)
     lg = host(res.losses)
     bg = int(host(res.best)[0])
-    tol = LOSS_RTOL if W.shape[0] >= 64 else TINY_ROWS_RTOL
-    err, gap = check_alpha(lg, orc["losses"], bg, orc["best"], tol)
+    err, gap = check_alpha(lg, orc["losses"], bg, orc["best"])
     say(f"max loss rel err {err:.2e}, oracle gap {gap:.2e}, alpha* {bg} / {orc['best']}")
     assert np.array_equal(host(res.s_best), orc["scales"][bg])
     assert int(host(res.flags)[0]) == 0
+
+
+# Layers below 256 rows or 256 tokens take the fp32 contraction; these straddle both limits,
+# with X in each dtype (the fp32 path reads X as given, the fp16 one converts it).
+PRECISE_CASES = [
+    ("rows63_f32x_m1500", 63, 512, 1500, np.float32),
+    ("rows5_bf16x_m900", 5, 768, 900, "bf16"),
+    ("rows255_f16x_m700", 255, 512, 700, np.float16),
+    ("rows256_f16x_m700", 256, 512, 700, np.float16),
+    ("tokens1_f32x_n300", 300, 384, 1, np.float32),
+    ("tokens255_bf16x_n300", 300, 256, 255, "bf16"),
+    ("tokens256_f16x_n320", 320, 640, 256, np.float16),
+]
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("name,n,k,m,xdt", PRECISE_CASES, ids=[c[0] for c in PRECISE_CASES])
+def test_search_parity_small_layers(awq, name, n, k, m, xdt, form):
+    """Every per-alpha loss within 1e-4 at any layer size: the fp32 contraction below 256 rows or
+    tokens, the fp16 ones from there on."""
+    W, X = _lognormal_layer(60, n, k, m, np.float32 if xdt == "bf16" else xdt)
+    say("search", form, name, W.shape, X.shape, xdt)
+    Xt = dev(X).to(torch.bfloat16) if xdt == "bf16" else dev(X)
+    Xref = Xt.float().cpu().numpy() if xdt == "bf16" else X
+    sx, flags = awq.act_stats(Xt)
+    res = awq.search_layer(dev(W), Xt, sx, awq.AwqConfig(form=form), flags=flags)
+    sx_o = oracle.act_stats(Xref)
+    assert np.array_equal(host(sx), sx_o)
+    orc = oracle.search_layer(W, Xref, sx_o)
+    bg = int(host(res.best)[0])
+    err, gap = check_alpha(host(res.losses), orc["losses"], bg, orc["best"])
+    say(f"max loss rel err {err:.2e}, oracle gap {gap:.2e}, alpha* {bg} / {orc['best']}")
+    assert np.array_equal(host(res.s_best), orc["scales"][bg])
+    bits = {"bf16": 7}.get(xdt, 23 if xdt is np.float32 else None)
+    may_round = bits is not None and ex.stats_sum_may_round(Xref, bits)
+    assert int(host(flags)[0]) == (4 if may_round else 0)
+
+
+SCALE_TABLE_CASES = [
+    ("c1", lambda: workloads.c1_layer().X, 20),
+    ("c2_like_k4096", lambda: workloads.c2_like_layer(n=8, k=4096, m=2048, config=61).X, 20),
+    ("c2_like_dead_channels_grid7", lambda: _dead_channel_x(62), 7),
+]
+
+
+def _dead_channel_x(seed):
+    X = workloads.c2_like_layer(n=8, k=1024, m=700, config=seed).X
+    X[:, 5] = 0            # s_X = 0: the floor
+    X[:, 9] = X[:, 9] * np.float16(1e-3)
+    return X
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("name,make,n_grid", SCALE_TABLE_CASES,
+                         ids=[c[0] for c in SCALE_TABLE_CASES])
+def test_scale_table_bit_exact(awq, name, make, n_grid, form):
+    """The whole table s_i = fp32(max(s_X, s_floor)^alpha_i), every grid point and channel (not
+    only the chosen row), read back from the search workspace (fp32 [n_grid][K] at byte offset
+    256) and compared bitwise with the oracle's."""
+    X = make()
+    K = X.shape[1]
+    W = workloads.weight(63, 128, K)
+    say("scale table", name, form, X.shape, "grid", n_grid)
+    Xt = dev(X)
+    sx, _ = awq.act_stats(Xt)
+    cfg = awq.AwqConfig(form=form, n_grid=n_grid)
+    ws = torch.empty(awq.search_workspace_bytes(X.shape[0], 128, K, Xt.dtype, cfg),
+                     dtype=torch.uint8, device="cuda")
+    awq.search_layer(dev(W), Xt, sx, cfg, workspace=ws)
+    S_gpu = host(ws[256:256 + n_grid * K * 4]).view(np.float32).reshape(n_grid, K)
+    S_orc = oracle.scale_table(oracle.act_stats(X), n_grid)
+    diff = np.argwhere(S_gpu.view(np.uint32) != S_orc.view(np.uint32))
+    assert diff.size == 0, f"{len(diff)} entries differ, first {diff[:5].tolist()}"
+
+
+def test_stats_flag_inexact_bf16_and_fp32_sums(awq):
+    """A column whose values span more binades than fp64 holds (2^100 next to 2^-60) cannot be
+    summed exactly: AWQ_FLAG_STATS_INEXACT; columns of ordinary data leave it clear."""
+    from post_weight_quantization_channel_amd import _lib
+    X = workloads.c2_like_layer(n=8, k=256, m=300, config=64).X.astype(np.float32)
+    for tdt in (torch.float32, torch.bfloat16):
+        sx, flags = awq.act_stats(dev(X).to(tdt))
+        assert int(host(flags)[0]) == 0, tdt
+        Xw = X.copy()
+        Xw[0, 17] = np.float32(2.0 ** 100)
+        Xw[1, 17] = np.float32(2.0 ** -60)
+        sx, flags = awq.act_stats(dev(Xw).to(tdt))
+        assert int(host(flags)[0]) == _lib.FLAG_STATS_INEXACT, tdt
 
 
 @pytest.mark.parametrize("form", FORMS)
@@ -337,11 +418,20 @@ def test_flags_are_raised(awq):
     sx, _ = awq.act_stats(dev(X))
     r = awq.search_layer(dev(Wn), dev(X), sx)
     assert int(host(r.flags)[0]) & L.FLAG_NONFINITE_W
+    # fp32 X beyond the fp16 range: flagged where X is converted to fp16 -- the fp16 contractions
+    # (256 rows and 300 tokens) and the Gram form's operand, which every Gram-form search forms --
+    # but not by a direct-form search of a smaller layer (64 rows, 100 tokens: fp32 contraction)
+    Wb = (0.02 * np.random.default_rng(47).standard_normal((256, 256))).astype(np.float16)
+    Xb = np.random.default_rng(48).standard_normal((300, 256)).astype(np.float32)
+    Xb[5, 9] = 1e6
+    sxb, _ = awq.act_stats(dev(Xb))
     Xf = X.astype(np.float32)
     Xf[5, 9] = 1e6
     for form in FORMS:
-        r = awq.search_layer(dev(W), dev(Xf), sx, awq.AwqConfig(form=form))
+        r = awq.search_layer(dev(Wb), dev(Xb), sxb, awq.AwqConfig(form=form))
         assert int(host(r.flags)[0]) & L.FLAG_X_F16_RANGE, form
+        r = awq.search_layer(dev(W), dev(Xf), sx, awq.AwqConfig(form=form))
+        assert bool(int(host(r.flags)[0]) & L.FLAG_X_F16_RANGE) == (form == "gram"), form
     Xb = np.full((9000, 8), 60000.0, np.float16)
     _, f = awq.act_stats(dev(Xb))
     assert int(host(f)[0]) & L.FLAG_STATS_INEXACT
@@ -649,6 +739,28 @@ def test_clip_search_gram_refuses_a_direct_form_workspace(awq):
     r = awq.clip_search_gram(Wt, res.s_best, ws, cfg_g, with_err=True, flags=flags)
     assert int(host(flags)[0]) == 0
     _check_clip_against_oracle(r, W, X, host(res.s_best), 4, cfg_g.n_clip, cfg_g.clip_min)
+
+
+def test_clip_search_gram_refuses_another_grid_size(awq):
+    """The Gram operand's place in the search workspace depends on n_grid: a clipping call whose
+    n_grid differs from the search's raises AWQ_FLAG_NO_GRAM and writes nothing."""
+    from post_weight_quantization_channel_amd import _lib
+    W, X = _lognormal_layer(59, 256, 512, 400)
+    Wt, Xt = dev(W), dev(X)
+    sx, _ = awq.act_stats(Xt)
+    cfg20 = awq.AwqConfig(form="gram")
+    cfg10 = awq.AwqConfig(form="gram", n_grid=10)
+    ws = torch.empty(awq.search_workspace_bytes(400, 256, 512, Xt.dtype, cfg20),
+                     dtype=torch.uint8, device="cuda")
+    res = awq.search_layer(Wt, Xt, sx, cfg20, workspace=ws)
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    awq.clip_search_gram(Wt, res.s_best, ws, cfg10, flags=flags)
+    assert int(host(flags)[0]) == _lib.FLAG_NO_GRAM
+    # the matching grid size is accepted
+    flags.zero_()
+    r = awq.clip_search_gram(Wt, res.s_best, ws, cfg20, with_err=True, flags=flags)
+    assert int(host(flags)[0]) == 0
+    _check_clip_against_oracle(r, W, X, host(res.s_best), 4, cfg20.n_clip, cfg20.clip_min)
 
 
 def test_pack_with_clip_bit_exact(awq):

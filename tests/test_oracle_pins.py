@@ -566,3 +566,95 @@ def test_p16_group64_equals_group128_when_both_halves_hold_the_maximum():
     q128, d128 = oracle.quantize(W, s, 4, 128)
     assert np.array_equal(q64, q128)
     assert np.array_equal(d64, np.repeat(d128, 2, axis=1))
+
+
+# --- fp16 storage of steps and s, and the checks' own metrics -----------------------------------
+def _f16_boundary_values():
+    """Exact rationals at the places where an fp16 rounding goes wrong most easily."""
+    two = Fraction(2)
+    return [
+        Fraction(1) + two ** -11,                 # tie between 1 and 1 + 2^-10: to even (1)
+        Fraction(1) + 3 * two ** -11,             # tie: to even (1 + 2^-9)
+        Fraction(1) + two ** -11 + two ** -20,    # just above the tie: up
+        two ** -14,                               # smallest normal
+        two ** -14 - two ** -25,                  # tie between the largest subnormal and 2^-14
+        two ** -14 - 3 * two ** -25,              # tie between two subnormals: to even
+        two ** -25,                               # half the smallest subnormal: to 0 (even)
+        3 * two ** -26,                           # above that half: the smallest subnormal
+        Fraction(65504),                          # largest finite
+        Fraction(65519),                          # rounds down to 65504
+        Fraction(65520),                          # the overflow threshold: Inf
+        Fraction(3, 10), Fraction(1, 3), Fraction(7, 5) * two ** -20,
+    ]
+
+
+def test_pack_stores_steps_and_s_as_correctly_rounded_fp16():
+    """"AWQ 量化方案..." section 三 stores per-group FP16 scales and the per-channel scale: the
+    oracle's fp16 steps and s must be the correctly rounded fp16 of the fp32 values (ties to
+    even, subnormals, overflow to Inf), checked here against exact rationals at every boundary
+    case rather than against numpy's own cast."""
+    vals = _f16_boundary_values()
+    # s16: pack_layer rounds the given fp32 s; each value is first made an fp32 number
+    s32 = np.array([np.float32(float(v)) for v in vals], dtype=np.float32)
+    # the boundary cases must survive fp32 exactly for the pin to mean what it says
+    for v, f in zip(vals[:11], s32[:11]):
+        assert Fraction(float(f)) == v
+    K = 128 * ((len(vals) + 127) // 128)
+    s = np.ones(K, np.float32)
+    s[:len(vals)] = s32
+    W = np.zeros((len(vals), K), np.float32)
+    # steps: row r has one group whose max |w s| is 7 * target, so Delta = fp32(7 t / 7) = t
+    for r, f in enumerate(s32):
+        W[r, len(vals)] = np.float32(7.0) * f          # channel with s = 1
+    with np.errstate(over="ignore"):
+        o = oracle.pack_layer(W, s, bits=4, group=128)
+    for j, f in enumerate(s32):
+        want = ex.rn16(Fraction(float(f)))
+        got = o["s16"][j]
+        assert (np.isinf(want) and np.isinf(got)) or got == want, (float(f), got, want)
+        d = o["delta"][j, len(vals) // 128]
+        if j < 11:          # 7 t is exact in fp32 there, so Delta = t is the boundary value
+            assert d == f
+        want_d = ex.rn16(Fraction(float(d)))
+        got_d = o["scales16"][j, len(vals) // 128]
+        assert (np.isinf(want_d) and np.isinf(got_d)) or got_d == want_d, (float(f), got_d)
+    # spot values the exact rounding must give
+    assert ex.rn16(vals[0]) == np.float16(1.0)
+    assert ex.rn16(vals[1]) == np.float16(1.0 + 2.0 ** -9)
+    assert ex.rn16(vals[4]) == np.float16(2.0 ** -14)
+    assert ex.rn16(vals[6]) == np.float16(0.0)
+    assert ex.rn16(vals[7]) == np.float16(2.0 ** -24)
+    assert ex.rn16(vals[9]) == np.float16(65504.0) and np.isinf(ex.rn16(vals[10]))
+
+
+def test_relative_gap_hand_computed():
+    """(runner-up - best) / best over the grid: the quantity that decides when the GPU's alpha*
+    must equal the oracle's ([notes] 方法: alpha* = argmin L). Hand-computed values."""
+    assert oracle.relative_gap([3.0, 1.0, 1.5, 2.0]) == 0.5
+    assert oracle.relative_gap([2.5, 2.0]) == 0.25
+    assert oracle.relative_gap([4.0, 1.0, 1.0]) == 0.0          # a tie: no gap
+    assert oracle.relative_gap([1.0, 1.25, 4.0]) == 0.25
+    assert oracle.relative_gap([0.0, 1.0]) == float("inf")      # a zero loss: any other is worse
+    # order-free: the same set in any order
+    g = np.random.default_rng(4)
+    ls = g.uniform(1.0, 2.0, 20)
+    assert oracle.relative_gap(ls) == oracle.relative_gap(ls[::-1])
+    srt = np.sort(ls)
+    assert oracle.relative_gap(ls) == (srt[1] - srt[0]) / srt[0]
+
+
+def test_accuracy_report_hand_computed():
+    """The metrics of "FlashAttention的量化：INT8和FP8怎么用才不影响精度？", section 精度验证 (max
+    abs, max rel, mean abs) and the relative Frobenius error of the W4A16 bar, on a case worked
+    by hand: test [1, 2, 3.5, 0.25], reference [1, 2.5, 3, 0]."""
+    r = oracle.accuracy_report(np.array([1.0, 2.0, 3.5, 0.25]), np.array([1.0, 2.5, 3.0, 0.0]))
+    assert r["max_abs"] == 0.5
+    # relative errors 0, 0.2, 1/6 and 0.25 / 1e-6 (|ref| clamped at 1e-6)
+    assert r["max_rel"] == pytest.approx(0.25 / 1e-6, rel=1e-15)
+    assert r["mean_abs"] == pytest.approx((0.0 + 0.5 + 0.5 + 0.25) / 4, rel=1e-15)
+    assert r["rel_fro"] == pytest.approx(math.sqrt(0.25 + 0.25 + 0.0625) / math.sqrt(1 + 6.25 + 9),
+                                         rel=1e-15)
+    r = oracle.accuracy_report(np.array([[3.0, 4.0]]), np.array([[0.0, 0.0]]))
+    assert r["rel_fro"] == pytest.approx(5.0 / 1e-300, rel=1e-12)   # a zero reference
+    r = oracle.accuracy_report(np.array([1.0, -2.0]), np.array([1.0, -2.0]))
+    assert r["max_abs"] == 0.0 and r["rel_fro"] == 0.0
