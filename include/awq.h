@@ -364,6 +364,27 @@ awq_status w4a16_gemm(const uint16_t* A, int64_t M, int64_t N, int64_t K, int32_
                       const uint32_t* qweight, const uint16_t* scales16, const uint8_t* zeros,
                       const uint16_t* s16, uint16_t* Y, hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------------
+ * awq_act_stats_noalloc -- awq_act_stats for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same inputs,
+ * outputs, flags and results (bit for bit) as awq_act_stats, without the workspace argument: the
+ * scratch lives in a static device array of AWQ_NOALLOC_SCRATCH_BYTES inside the library, one
+ * per GPU, held until the process ends. The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); on the first call made on a device it looks the array's device
+ * address up once (hipGetSymbolAddress).
+ * Runs on the current device; `stream` must belong to it. Calls that overlap on one GPU share the
+ * array and race: order them (one stream, or events). The array keeps the last call's contents;
+ * every byte a call reads it has written first, so nothing needs clearing.
+ * Limit: awq_act_stats_workspace_bytes(M, K) <= AWQ_NOALLOC_SCRATCH_BYTES (32 MiB), i.e.
+ * ceil(M / 256) * K <= about 3.7 million (65536 tokens: K <= 14563); larger shapes return
+ * AWQ_ERR_WORKSPACE before any HIP call.
+ * Errors: as awq_act_stats; AWQ_ERR_WORKSPACE for shapes beyond the limit; AWQ_ERR_HIP when the
+ * device or the array's address cannot be obtained, or a launch fails.
+ * ---------------------------------------------------------------------------------------- */
+#define AWQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+awq_status awq_act_stats_noalloc(const void* X, awq_dtype xdt, int64_t M, int64_t K,
+                                 int64_t ldx, float* sx, uint32_t* flags, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -75,7 +75,11 @@ SIGNATURES = {
     "awq_pack_int4": (_E, [_P, _E, _I64, _I64, _P, _P, ctypes.POINTER(AwqCfg), _P, _P, _P, _P,
                            _P, _P, _P]),
     "w4a16_gemm": (_E, [_P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P]),
+    "awq_act_stats_noalloc": (_E, [_P, _E, _I64, _I64, _I64, _P, _P, _P]),
 }
+
+# bytes of the library's static scratch array (AWQ_NOALLOC_SCRATCH_BYTES in awq.h)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 

@@ -106,6 +106,26 @@ def act_stats(X: torch.Tensor, flags: torch.Tensor | None = None,
     return sx, flags
 
 
+def act_stats_noalloc(X: torch.Tensor, sx: torch.Tensor,
+                      flags: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """act_stats into caller-provided sx (fp32 [K]) and flags (int32 [1]) with the library's
+    static scratch instead of a workspace: the C call allocates nothing, and neither does this
+    binding (usable under graph capture). Overlapping calls on one GPU race."""
+    lib = _lib.load()
+    if not X.is_cuda or X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be a 2-D device tensor with unit column stride")
+    M, K = X.shape
+    _dev(sx, "sx")
+    _dev(flags, "flags")
+    if sx.shape != (K,) or sx.dtype != torch.float32 or flags.numel() != 1 or \
+            flags.dtype != torch.int32:
+        raise ValueError("sx must be fp32 [K] and flags int32 [1]")
+    ldx = X.stride(0) if M > 1 else K
+    check("awq_act_stats_noalloc", lib.awq_act_stats_noalloc(
+        X.data_ptr(), _DT[X.dtype], M, K, ldx, sx.data_ptr(), flags.data_ptr(), _stream(X)))
+    return sx, flags
+
+
 def search_layer(W: torch.Tensor, X: torch.Tensor, sx: torch.Tensor,
                  cfg: AwqConfig = AwqConfig(), flags: torch.Tensor | None = None,
                  workspace: torch.Tensor | None = None,

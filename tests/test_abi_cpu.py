@@ -130,6 +130,24 @@ def test_act_stats_rejects(lib):
     assert f(FAKE, 1, 4, 8, 8, FAKE, FAKE, None, 1 << 20, None) == _lib.AWQ_ERR_WORKSPACE
 
 
+def test_act_stats_noalloc_rejects(lib):
+    """Host checks of the call that allocates nothing, before any HIP call: the same argument
+    rules as awq_act_stats, and shapes whose scratch exceeds the static array's 32 MiB."""
+    f = lib.awq_act_stats_noalloc
+    assert f(None, 1, 4, 8, 8, FAKE, FAKE, None) == _lib.AWQ_ERR_NULL
+    assert f(FAKE, 1, 4, 8, 8, None, FAKE, None) == _lib.AWQ_ERR_NULL
+    assert f(FAKE, 7, 4, 8, 8, FAKE, FAKE, None) == _lib.AWQ_ERR_DTYPE
+    assert f(FAKE, 1, 0, 8, 8, FAKE, FAKE, None) == _lib.AWQ_ERR_SHAPE
+    assert f(FAKE, 1, 4, 12, 12, FAKE, FAKE, None) == _lib.AWQ_ERR_SHAPE
+    assert f(FAKE + 2, 1, 4, 8, 8, FAKE, FAKE, None) == _lib.AWQ_ERR_SHAPE
+    lim = _lib.NOALLOC_SCRATCH_BYTES
+    # 65536 tokens (256 chunks): K = 14560 fits, 14568 does not
+    assert lib.awq_act_stats_workspace_bytes(65536, 14560) <= lim
+    assert lib.awq_act_stats_workspace_bytes(65536, 14568) > lim
+    assert f(FAKE, 1, 65536, 14568, 14568, FAKE, FAKE, None) == _lib.AWQ_ERR_WORKSPACE
+    assert f(FAKE, 1, 1 << 20, 4096, 4096, FAKE, FAKE, None) == _lib.AWQ_ERR_WORKSPACE
+
+
 def _search(lib, **kw):
     a = dict(W=FAKE, wdt=1, N=256, K=512, X=FAKE2, xdt=1, M=300, sx=FAKE, cfg=cfg(),
              losses=FAKE, best=FAKE, s_best=FAKE, flags=FAKE, ws=FAKE, ws_bytes=1 << 40)
