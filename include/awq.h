@@ -354,11 +354,17 @@ awq_status awq_pack_int4(const void* W, awq_dtype wdt, int64_t N, int64_t K, con
  *          zeros uint8 [N, K/group] for zero-point codes, or NULL for symmetric ones;
  *          s16 fp16 bits [K], or NULL when s^-1 has been folded into the producer of A (then
  *          Y = A (c(q) * step)^T); Y out, fp16 bits [M, N]. group 128 or 64; K % 128 == 0,
- *          K <= 12288.
- * Products are formed on fp16 operands (fp16(1/s) and fp16(c(q) * fp16(1/s)), each rounded
- * once) with fp32 accumulation; the per-group step multiplies the fp32 partial of each group;
- * Y is rounded once to fp16 (relative Frobenius error ~5e-4).
- * Errors: AWQ_ERR_NULL, AWQ_ERR_SHAPE (M < 1, N < 1, K % 128, K > 12288), AWQ_ERR_CONFIG.
+ *          K <= 32768.
+ * Arithmetic: no fp16 value holds 1/s or A/s directly, so no s (a dead channel's s_floor
+ * included) can overflow fp16. With one activation row, a' = fp32(A rcp(s)) is stored as
+ * fp16(a' 2^-e) with one power of two per 128-channel block (its largest |value| in
+ * [2^14, 2^15)), multiplied with the exact codes in fp32 (v_dot2_f32_f16). With more rows the
+ * weight operand is fp16(c(q) r_k), r_k = fp16(2^b rcp(s_k)) with 2^b per 128-channel block (its
+ * largest r_k in [2^10, 2^11)), against the fp16 activations. Accumulation is fp32; the group
+ * step (times the block's power of two) multiplies the fp32 partial of each group; Y is rounded
+ * once to fp16 (relative Frobenius error ~3e-4). A channel keeps full fp16 precision while the
+ * s values of its 128-channel block span less than 2^24.
+ * Errors: AWQ_ERR_NULL, AWQ_ERR_SHAPE (M < 1, N < 1, K % 128, K > 32768), AWQ_ERR_CONFIG.
  * ---------------------------------------------------------------------------------------- */
 awq_status w4a16_gemm(const uint16_t* A, int64_t M, int64_t N, int64_t K, int32_t group,
                       const uint32_t* qweight, const uint16_t* scales16, const uint8_t* zeros,

@@ -29,7 +29,7 @@ awq_status check_cfg(const awq_cfg* cfg) {
 // Largest accepted extent of one dimension; keeps every element index and tile index in range.
 constexpr int64_t kMaxDim = int64_t(1) << 24;
 constexpr int64_t kMaxSearchK = int64_t(1) << 22;
-constexpr int64_t kMaxW4A16K = 12288;   // the W4A16 kernel keeps per-channel tables in LDS
+constexpr int64_t kMaxW4A16K = 32768;   // the W4A16 kernels keep per-channel tables in LDS
 // Gram form: the K x K operand is stored (2 GiB at K = 32768); 256 rows of the transposed X
 // must fit a 32-bit buffer range.
 constexpr int64_t kMaxGramK = 32768;

@@ -125,6 +125,21 @@ hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, co
                               float* clip_err, uint32_t* flags, hipStream_t stream);
 
 // ---- W4A16 ----
+// one activation row (M = 1): fp16 dot products against the block-scaled A / s table; K up to
+// kW4a16GemvMaxK; dynamic LDS of w4a16_gemv_lds_bytes(1, K) bytes (the launcher passes it)
+constexpr int64_t kW4a16GemvMaxK = 8192;
+size_t w4a16_gemv_lds_bytes(int MB, int64_t K);
+hipError_t launch_w4a16_gemv(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
+                             const uint32_t* qweight, const uint16_t* scales16,
+                             const uint8_t* zeros, const uint16_t* s16, uint16_t* Y,
+                             hipStream_t stream);
+// any M (passes of 64 rows), K up to kW4a16SkinnyMaxK, dynamic LDS of w4a16_skinny_lds_bytes
+constexpr int64_t kW4a16SkinnyMaxK = 32768;
+size_t w4a16_skinny_lds_bytes(int MB, int64_t K, int GS, bool ZP);
+hipError_t launch_w4a16_skinny(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
+                               const uint32_t* qweight, const uint16_t* scales16,
+                               const uint8_t* zeros, const uint16_t* s16, uint16_t* Y,
+                               hipStream_t stream);
 // group 128 or 64; zeros [N, K/group] (zero-point codes) or nullptr; s16 nullptr: s folded
 hipError_t launch_w4a16(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
                         const uint32_t* qweight, const uint16_t* scales16, const uint8_t* zeros,

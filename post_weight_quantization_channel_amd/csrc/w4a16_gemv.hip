@@ -1,0 +1,257 @@
+// W4A16 for one activation row (decode): QuantLinear.forward of "AWQ 量化方案..."
+// (qwbw.cn/news/39982), section 三 -- scale the input per channel, dequantize, linear:
+//   Y[n] = sum_k (A[k] / s[k]) * c(q[n,k]) * step[n, k/G],
+// c(q) = q for symmetric codes, q - z[n, k/G] for zero-point ones. The activation is divided by
+// s because the weight was multiplied by s (AWQ notes, bg51717.github.io/14592, section 方法).
+//
+// The bytes of the packed weight are all that matters at this size, so the kernel is a streaming
+// read with as little arithmetic per code as possible:
+//   * a' = A / s is formed once per workgroup in fp32 and stored in LDS as fp16 scaled by a power
+//     of two per 128-channel block, a'' = fp16(a' 2^-e), with 2^-e max|a'| in [2^14, 2^15): no
+//     value of A or s can overflow it (a dead channel's s_floor gives a huge 1/s, which fp16 1/s
+//     or fp16 A/s cannot hold);
+//   * the activation and s loads are issued first, the code loads right after them, so the
+//     table is built while the codes stream in;
+//   * a wave owns 4 weight rows and all of K; lane l takes the 32-channel chunks l, l + 64, ... of
+//     each row (16 bytes of codes per row and chunk); a chunk of a'' read from LDS serves four
+//     rows;
+//   * decoding: x = w ^ 0x88888888 turns each two's-complement nibble into u = q + 8 (zero-point
+//     codes are unsigned already, u = q); (x >> 4j) & 0x000F000F | 0x64006400 is the fp16 pair
+//     (1024 + u_j, 1024 + u_{j+4}), and one packed subtract of 1024 + zc (zc = 8, or z) gives
+//     (c(q_j), c(q_{j+4})) exactly; v_dot2_f32_f16 against the a'' pair (j, j + 4) adds both
+//     exact products in fp32. (Summing (1024 + u) a'' and subtracting the offset times the
+//     chunk's sum afterwards would save the subtract but lose everything else in the block to
+//     the rounding of one huge term: a dead channel's a'' next to q = 0.) The chunk's sum times
+//     step 2^e goes into the row's partial;
+//   * the four rows' partials are summed over the wave's 64 lanes by a transposing butterfly
+//     (each exchange halves the values a lane holds), in a fixed order.
+// Rounding: a'' one fp16 rounding (of the fp32 a' = A rcp(s)); products exact, sums fp32; Y
+// rounded once to fp16.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace awq {
+
+namespace {
+constexpr int kGvRows = 4;     // weight rows per wave
+constexpr int kGvWaves = 4;    // waves per workgroup
+constexpr int kGvPos = 2;      // chunk positions per lane whose loads are in flight together
+constexpr int kChunkBytes = 80;   // LDS bytes per 32-channel chunk: 64 of a'', 16 of padding
+}  // namespace
+
+// LDS bytes of the tables: K/32 chunks, then the K/128 block factors 2^-e (fp32).
+size_t w4a16_gemv_lds_bytes(int MB, int64_t K) {
+  return (size_t)MB * ((size_t)(K / 32) * kChunkBytes + (size_t)(K / 128) * sizeof(float));
+}
+
+// ONE: every chunk position of a lane fits one load batch (K <= 64 * 32 * kGvPos = 4096), so
+// there is one set of load registers and no loop. TI: table entries of 8 channels per thread
+// (K <= 2048 TI); all their loads are unconditional, issued before the code loads, and only the
+// LDS stores are conditional -- a load inside a conditional block would be issued there, after
+// the code loads, and waiting for it would wait for all of them.
+template <int GS, bool ZP, bool HAS_S, bool ONE, int TI>
+__global__ __launch_bounds__(256) void w4a16_gemv_kernel(
+    const uint16_t* __restrict__ A, int64_t N, int64_t K, const uint32_t* __restrict__ qweight,
+    const uint16_t* __restrict__ scales16, const uint8_t* __restrict__ zeros,
+    const uint16_t* __restrict__ s16, uint16_t* __restrict__ Y) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t n0 = ((int64_t)blockIdx.x * kGvWaves + wave) * kGvRows;
+  const int nch = (int)(K / 32);                 // 32-channel chunks of a row
+  const int64_t ngr = K / GS;                    // quantization groups of a row
+  const int64_t wpr = K / 8;                     // uint32 words of a row
+  const int npos = (nch + 63) / 64;              // chunk positions of a lane (the last partial)
+  float* bfac = reinterpret_cast<float*>(lds + (size_t)nch * kChunkBytes);   // [K/128] 2^-e
+
+  // ---- 1. activation and s loads of this thread's table entries (8 channels each) ----------
+  uint4 araw[TI], sraw[TI];
+  const int nq8 = (int)(K / 8);
+#pragma unroll
+  for (int it = 0; it < TI; ++it) {
+    const int q8 = tid + 256 * it;
+    const int qc = q8 < nq8 ? q8 : 0;
+    araw[it] = *reinterpret_cast<const uint4*>(A + (int64_t)qc * 8);
+    sraw[it] = HAS_S ? *reinterpret_cast<const uint4*>(s16 + (int64_t)qc * 8)
+                     : make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+  }
+
+  // ---- 2. this wave's code loads (rows past N read row N - 1, never stored) ----------------
+  const uint32_t* wrow[kGvRows];
+  int64_t srow[kGvRows];
+#pragma unroll
+  for (int r = 0; r < kGvRows; ++r) {
+    const int64_t n = (n0 + r < N) ? n0 + r : N - 1;
+    wrow[r] = qweight + n * wpr;
+    srow[r] = n * ngr;
+  }
+  // codes, steps and zero points of positions p0 .. p0 + kGvPos - 1 (a chunk past the row reads
+  // chunk 0: its step is zeroed at use, so it adds nothing)
+  struct Buf {
+    uint4 w[kGvPos][kGvRows];
+    uint32_t st[kGvPos][kGvRows];   // fp16 step bits (32-bit registers: no merged halves)
+    uint32_t z[kGvPos][kGvRows];    // zero points (ZP)
+  };
+  auto load = [&](int p0, Buf& buf) {
+#pragma unroll
+    for (int j = 0; j < kGvPos; ++j) {
+      const int c = lane + 64 * (p0 + j);
+      const int cc = c < nch ? c : 0;
+      const int64_t g = ((int64_t)cc * 32) / GS;
+#pragma unroll
+      for (int r = 0; r < kGvRows; ++r) {
+        buf.w[j][r] = *reinterpret_cast<const uint4*>(wrow[r] + 4 * cc);
+        buf.st[j][r] = scales16[srow[r] + g];
+        if (ZP) buf.z[j][r] = zeros[srow[r] + g];
+      }
+    }
+  };
+  Buf wb[ONE ? 1 : 2];
+  load(0, wb[0]);
+  asm volatile("" : : "v"(wrow[0]) : "memory");   // the code loads stay ahead of the table
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 3. the a'' table: 16 consecutive threads hold one 128-channel block ------------------
+#pragma unroll
+  for (int it = 0; it < TI; ++it) {
+    const int q8 = tid + 256 * it;
+    {
+      const uint32_t aw[4] = {araw[it].x, araw[it].y, araw[it].z, araw[it].w};
+      const uint32_t sw[4] = {sraw[it].x, sraw[it].y, sraw[it].z, sraw[it].w};
+      float v[8];
+      float mx = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float a = h2f((uint16_t)(aw[t >> 1] >> (16 * (t & 1))));
+        const float sv = h2f((uint16_t)(sw[t >> 1] >> (16 * (t & 1))));
+        v[t] = a * __builtin_amdgcn_rcpf(sv);
+        mx = fmaxf(mx, fabsf(v[t]));
+      }
+      mx = group_absmax<16>(mx);                  // the 128-channel block of this thread
+      const int e = escale_for_max(mx);           // 2^e mx in [2^14, 2^15); 0 for 0 or Inf/NaN
+      const float sc = ldexpf(1.0f, e);
+      uint16_t h[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) h[t] = f2h(v[t] * sc);
+      // pairs in the decode order (t, t + 4)
+      const uint32_t p0 = (uint32_t)h[0] | ((uint32_t)h[4] << 16);
+      const uint32_t p1 = (uint32_t)h[1] | ((uint32_t)h[5] << 16);
+      const uint32_t p2 = (uint32_t)h[2] | ((uint32_t)h[6] << 16);
+      const uint32_t p3 = (uint32_t)h[3] | ((uint32_t)h[7] << 16);
+      if (q8 < nq8) {
+        char* d = lds + (size_t)(q8 >> 2) * kChunkBytes + (q8 & 3) * 16;
+        *reinterpret_cast<uint4*>(d) = make_uint4(p0, p1, p2, p3);
+        if ((q8 & 15) == 0) bfac[q8 >> 4] = ldexpf(1.0f, -e);
+      }
+    }
+  }
+  __syncthreads();
+
+  float part[kGvRows];
+#pragma unroll
+  for (int r = 0; r < kGvRows; ++r) part[r] = 0.0f;
+
+  auto process = [&](int p0, const Buf& buf) {
+#pragma unroll
+    for (int j = 0; j < kGvPos; ++j) {
+      const int c = lane + 64 * (p0 + j);
+      const bool ok = c < nch;
+      const int cc = ok ? c : 0;
+      const char* ch = lds + (size_t)cc * kChunkBytes;
+      uint32_t ap[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 t4 = *reinterpret_cast<const uint4*>(ch + 16 * i);
+        ap[4 * i] = t4.x; ap[4 * i + 1] = t4.y; ap[4 * i + 2] = t4.z; ap[4 * i + 3] = t4.w;
+      }
+      const float f = ok ? bfac[cc >> 2] : 0.0f;   // 2^-e of the chunk's block
+#pragma unroll
+      for (int r = 0; r < kGvRows; ++r) {
+        const uint32_t words[4] = {buf.w[j][r].x, buf.w[j][r].y, buf.w[j][r].z, buf.w[j][r].w};
+        // fp16 subtrahend: 1032 (signed codes, biased by the xor) or 1024 + z
+        const _Float16 subh = ZP ? (_Float16)(1024.0f + (float)buf.z[j][r]) : (_Float16)1032.0f;
+        const half2_t sub2 = half2_t{subh, subh};
+        float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {             // word v: channels 8v .. 8v + 7 of the chunk
+          const uint32_t x = ZP ? words[v] : (words[v] ^ 0x88888888u);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const uint32_t bits = ((x >> (4 * jj)) & 0x000F000Fu) | 0x64006400u;
+            const half2_t qp = __builtin_bit_cast(half2_t, bits) - sub2;
+            const half2_t apair = __builtin_bit_cast(half2_t, ap[4 * v + jj]);
+            if (jj & 1)
+              acc1 = __builtin_amdgcn_fdot2(qp, apair, acc1, false);
+            else
+              acc0 = __builtin_amdgcn_fdot2(qp, apair, acc0, false);
+          }
+        }
+        part[r] = __builtin_fmaf(h2f((uint16_t)buf.st[j][r]) * f, acc0 + acc1, part[r]);
+      }
+    }
+  };
+
+  if constexpr (ONE) {
+    process(0, wb[0]);
+  } else {
+    // positions in pairs, the loads of the next pair in flight while one pair is processed
+    for (int p = 0; p < npos; p += 2 * kGvPos) {
+      if (p + kGvPos < npos) load(p + kGvPos, wb[ONE ? 0 : 1]);
+      process(p, wb[0]);
+      if (p + kGvPos < npos) {
+        if (p + 2 * kGvPos < npos) load(p + 2 * kGvPos, wb[0]);
+        process(p + kGvPos, wb[ONE ? 0 : 1]);
+      }
+    }
+  }
+
+  // ---- sums over the 64 lanes: rows 0,1 go to lanes with bit 5 clear, 2,3 to the others;
+  // then bit 4 splits each pair; the remaining 16 lanes add up in four steps ------------------
+  const bool b5 = (lane & 32) != 0, b4 = (lane & 16) != 0;
+  const float give0 = b5 ? part[0] : part[2], give1 = b5 ? part[1] : part[3];
+  float k0 = b5 ? part[2] : part[0], k1 = b5 ? part[3] : part[1];
+  k0 += __shfl_xor(give0, 32);
+  k1 += __shfl_xor(give1, 32);
+  const float give = b4 ? k0 : k1;
+  float kk = b4 ? k1 : k0;
+  kk += __shfl_xor(give, 16);
+  kk += __shfl_xor(kk, 8);
+  kk += __shfl_xor(kk, 4);
+  kk += __shfl_xor(kk, 2);
+  kk += __shfl_xor(kk, 1);
+  const int row = (b5 ? 2 : 0) + (b4 ? 1 : 0);
+  if ((lane & 15) == 0 && n0 + row < N) Y[n0 + row] = f2h(kk);
+}
+
+hipError_t launch_w4a16_gemv(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
+                             const uint32_t* qweight, const uint16_t* scales16,
+                             const uint8_t* zeros, const uint16_t* s16, uint16_t* Y,
+                             hipStream_t stream) {
+  if (M != 1 || K > kW4a16GemvMaxK) return hipErrorInvalidValue;
+  const unsigned blocks = (unsigned)((N + kGvRows * kGvWaves - 1) / (kGvRows * kGvWaves));
+  const size_t lds = w4a16_gemv_lds_bytes(1, K);
+  const bool one = K <= 64 * 32 * kGvPos;   // K <= 4096: table entries of 2 passes at most
+#define AWQ_GV1(GS_, ZP_, HS_, ONE_, TI_)                                                        \
+  w4a16_gemv_kernel<GS_, ZP_, HS_, ONE_, TI_><<<blocks, 256, lds, stream>>>(                     \
+      A, N, K, qweight, scales16, zeros, s16, Y)
+#define AWQ_GV(GS_, ZP_, HS_)                                                                    \
+  do {                                                                                           \
+    if (K <= 2048) AWQ_GV1(GS_, ZP_, HS_, true, 1);                                             \
+    else if (one) AWQ_GV1(GS_, ZP_, HS_, true, 2);                                              \
+    else AWQ_GV1(GS_, ZP_, HS_, false, 4);                                                      \
+  } while (0)
+#define AWQ_GV_S(GS_, ZP_) \
+  do { if (s16) AWQ_GV(GS_, ZP_, true); else AWQ_GV(GS_, ZP_, false); } while (0)
+#define AWQ_GV_Z(GS_) \
+  do { if (zeros) AWQ_GV_S(GS_, true); else AWQ_GV_S(GS_, false); } while (0)
+  if (group == 64)
+    AWQ_GV_Z(64);
+  else
+    AWQ_GV_Z(128);
+#undef AWQ_GV_Z
+#undef AWQ_GV_S
+#undef AWQ_GV
+#undef AWQ_GV1
+  return hipGetLastError();
+}
+
+}  // namespace awq

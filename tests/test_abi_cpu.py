@@ -412,7 +412,7 @@ def test_w4a16_rejects(lib):
     assert call(M=0) == E.AWQ_ERR_SHAPE
     assert call(K=200) == E.AWQ_ERR_SHAPE
     assert call(K=192, group=64) == E.AWQ_ERR_SHAPE              # the kernels step 128 channels
-    assert call(K=12288 + 128) == E.AWQ_ERR_SHAPE
+    assert call(K=32768 + 128) == E.AWQ_ERR_SHAPE
     assert call(N=0) == E.AWQ_ERR_SHAPE
     assert call(A=FAKE + 8) == E.AWQ_ERR_SHAPE
     assert call(s16=FAKE + 8) == E.AWQ_ERR_SHAPE

@@ -1036,7 +1036,11 @@ def test_clip_search_gram_group_and_zero_point(awq, group, zp):
 W4A16_ZP_CASES = [(g, zp, n, k, m) for (g, zp) in QUANT_VARIANTS for (n, k, m) in
                   ((384, 512, 1), (384, 512, 16), (256, 4096, 40), (320, 512, 100))] + \
                  [(64, False, 4096, 4096, 1), (128, True, 11008, 4096, 4), (64, True, 4096, 4096, 3),
-                  (64, True, 256, 12288, 80)]   # tiled path whose tables take the register-staged kernel
+                  (64, True, 256, 12288, 80),
+                  # K beyond the tiled kernel's LDS tables (skinny kernel in passes) and beyond
+                  # the one-row kernel's (skinny kernel at M = 1)
+                  (64, True, 192, 28672, 100), (128, False, 256, 28672, 1),
+                  (64, False, 320, 16384, 1), (128, True, 128, 32768, 17)]
 
 
 @pytest.mark.parametrize("group,zp,n,k,m", W4A16_ZP_CASES)
@@ -1049,6 +1053,40 @@ def test_w4a16_group_and_zero_point(awq, group, zp, n, k, m):
                        zeros=None if z is None else dev(z))
     ref = oracle.w4a16(A, qw, sc, s, group=group, zeros=z)
     rep = oracle.accuracy_report(host(Y).astype(np.float64), ref)
+    say(rep)
+    assert rep["rel_fro"] <= W4A16_RTOL
+
+
+DEAD_CHANNEL_CASES = [(g, zp, m) for (g, zp) in ((128, False), (64, True))
+                      for m in (1, 16, 100, 512)]
+
+
+@pytest.mark.parametrize("group,zp,m", DEAD_CHANNEL_CASES)
+def test_w4a16_dead_channel_at_alpha_one(awq, group, zp, m):
+    """A channel that is zero in every calibration token gets s = s_floor = 1e-5 at alpha = 1,
+    whose fp16 (a subnormal) has a reciprocal far beyond fp16; a channel of huge activations
+    gets a large s in the same 128-channel block. The packed layer is then applied to
+    activations that are not zero on the dead channel: every kernel (one row, the small-batch
+    and the tiled one) must stay finite and within 2e-3 of the oracle."""
+    from post_weight_quantization_channel_amd import _lib as L
+    W, X = _lognormal_layer(81, 512, 1024, 600)
+    X[:, 70] = 0
+    X[:, 75] *= np.float16(60.0)
+    sx = oracle.act_stats(X)
+    s = oracle.scale_table(sx, 20)[19]               # alpha = 1: max(s_X, 1e-5)
+    assert s[70] == np.float32(1e-5)
+    cfg = awq.AwqConfig(group=group, zero_point=zp)
+    p = awq.pack_int4(dev(W), dev(s), cfg)
+    o = oracle.pack_layer(W, s, group=group, zero_point=zp)
+    assert np.array_equal(host(p.qweight).view(np.uint32), o["qweight"])
+    assert int(host(p.flags)[0]) & L.FLAG_SCALE16_SUBNORMAL      # fp16(1e-5) is subnormal
+    A = workloads.w4a16_activations(m, 1024, config=4, j=82)
+    say("w4a16 dead channel", "M", m, "group", group, "zero point", zp)
+    Y = awq.w4a16_gemm(dev(A), p.qweight, p.scales16, p.s16, group=group, zeros=p.zeros)
+    y = host(Y).astype(np.float64)
+    assert np.all(np.isfinite(y))
+    ref = oracle.w4a16(A, o["qweight"], o["scales16"], o["s16"], group=group, zeros=o["zeros"])
+    rep = oracle.accuracy_report(y, ref)
     say(rep)
     assert rep["rel_fro"] <= W4A16_RTOL
 
