@@ -31,7 +31,16 @@ fields it carries
                 Infinity Cache is measured), replayed from a HIP graph (GPU time per call;
                 `us_eager`: the same calls issued one by one from Python): GB/s and fraction
                 of 8 TB/s (TFLOP/s and MFMA fraction at M = 512);
-  cpu_baseline  the CPU oracle on a bounded sample of the same layer, scaled to ms per layer.
+  cpu_baseline  the CPU oracle on a bounded sample of the same layer, scaled to ms per layer;
+  layers        the other layer shapes of the workloads, each searched (s_X in the same call,
+                Gram form, 20 alpha points) and packed like the step: the LLaMA-7B MLP trio
+                (gate and up 11008x4096 sharing one X, down 4096x11008 with its own X) and the
+                70B-class shapes (8192x8192, 1024x8192, 28672x8192 on one X of 8192 channels)
+                in INT4 and INT3: ms per layer, the kernel breakdown, the MFMA fractions of the
+                two contractions (on executed and on strict-triangle flops), and the oracle's
+                time for the layer scaled from the step's CPU sample (not run: minutes each);
+                plus gate and up searched together (one s) and an estimate for one LLaMA-7B
+                decoder block and a 32-block model, as context.
 """
 from __future__ import annotations
 
@@ -68,6 +77,8 @@ def parse():
                     help="repetitions of the zero-point / group-64 search, pack and W4A16")
     ap.add_argument("--shared-reps", type=int, default=3,
                     help="repetitions of the shared q/k/v search and the fold (0: skip)")
+    ap.add_argument("--layer-reps", type=int, default=2,
+                    help="repetitions of each other layer shape's search (0: skip them)")
     ap.add_argument("--mode", choices=("bench", "traffic"), default="bench",
                     help="traffic: one 1 GiB device copy (counter calibration) and one pass of "
                          "the path in each form, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
@@ -237,6 +248,115 @@ def w4a16_time(awq, torch, n, k, ms, group=128, zero_point=False):
     return out
 
 
+def layer_sweep(awq, torch, reps, cpu_parts):
+    """The MLP trio of LLaMA-7B and the 70B-class shapes through the step's search and pack
+    (s_X in the same call, Gram form): ms per layer, kernel breakdown and MFMA fractions; the
+    oracle's time scaled from the C2 sample (`cpu_parts`: its parts in ms, or None)."""
+    import numpy as np
+    import workloads
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream()
+
+    def oracle_estimate(n, k):
+        # the oracle's parts at C2 scale as: statistics M K, H = X^T X  M K^2, the 20 grid
+        # points N K^2 (the loss contraction dominates), packing N K
+        if not cpu_parts:
+            return None
+        f = k / K_
+        est = (cpu_parts["stats"] * f + cpu_parts["gram"] * f * f +
+               cpu_parts["alpha_points"] * (n / N_) * f * f + cpu_parts["pack_w4a16"] * (n / N_) * f)
+        return {"ms_estimate": round(est, 0), "run": False,
+                "why": "scaled from the step's oracle sample (each layer would take minutes of "
+                       "host time; the benchmark keeps to a few minutes)"}
+
+    def one(name, Wt, Xt, bits, n, k):
+        cfg = awq.AwqConfig(bits=bits, group=128, n_grid=N_GRID, form="gram")
+        ws = torch.empty(awq.search_workspace_bytes(M_, n, k, torch.float16, cfg),
+                         dtype=torch.uint8, device=dev)
+        times = []
+        for r in range(reps + 1):                      # the first run is a warm-up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            sx, res = awq.stats_search_layer(Wt, Xt, cfg, workspace=ws)
+            awq.pack_int4(Wt, res.s_best, cfg)
+            e1.record(st)
+            e1.synchronize()
+            if r:
+                times.append(e0.elapsed_time(e1))
+        prof = {}
+        sx, res = awq.stats_search_layer(Wt, Xt, cfg, workspace=ws, stage_ms=prof)
+        losses = np.sort(res.losses.cpu().numpy())
+        fl_loss = gram_loss_flops(n, k, N_GRID)
+        strict = float(N_GRID) * n * k * k
+        fl_gemm = gram_gemm_flops(M_, k)
+        rec = {"layer": name, "N": n, "K": k, "M": M_, "bits": bits,
+               "ms": round(statistics.mean(times), 3),
+               "stages_ms": {kk: round(v, 4) for kk, v in prof.items()},
+               "gram_loss": {"ms": round(prof["loss"], 4),
+                             "frac_executed": round(fl_loss / (prof["loss"] * 1e-3) / 1e12 /
+                                                    MFMA_F16_PEAK_TFLOPS, 4),
+                             "frac_strict_triangle": round(strict / (prof["loss"] * 1e-3) /
+                                                           1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
+               "gram_gemm": {"ms": round(prof["gram_gemm"], 4),
+                             "frac_executed": round(fl_gemm / (prof["gram_gemm"] * 1e-3) / 1e12 /
+                                                    MFMA_F16_PEAK_TFLOPS, 4)},
+               "alpha_star": int(res.best.item()),
+               "loss_gap": float((losses[1] - losses[0]) / losses[0]),
+               "flags": int(res.flags.item()),
+               "oracle": oracle_estimate(n, k)}
+        log("layer", rec)
+        del ws
+        torch.cuda.empty_cache()
+        return rec
+
+    out = []
+    log("generating the LLaMA-7B MLP trio (X 65536x4096 and 65536x11008 fp16) ...")
+    gate, up, down = workloads.c3_layers(m=M_)
+    Xg = torch.from_numpy(gate.X).to(dev)
+    Wg = torch.from_numpy(gate.W).to(dev)
+    Wu = torch.from_numpy(up.W).to(dev)
+    out.append(one("llama7b_mlp_gate_11008x4096", Wg, Xg, 4, 11008, 4096))
+    out.append(one("llama7b_mlp_up_11008x4096", Wu, Xg, 4, 11008, 4096))
+    # gate and up read the same X: one s for both (awq_stats_search_layers)
+    cfg = awq.AwqConfig(bits=4, group=128, n_grid=N_GRID, form="gram")
+    ws = torch.empty(awq.search_workspace_bytes(M_, 2 * 11008, 4096, torch.float16, cfg),
+                     dtype=torch.uint8, device=dev)
+    gu = []
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        _, rgu = awq.search_layers([Wg, Wu], Xg, None, cfg, workspace=ws)
+        awq.pack_int4(Wg, rgu.s_best, cfg)
+        awq.pack_int4(Wu, rgu.s_best, cfg)
+        e1.record(st)
+        e1.synchronize()
+        if r:
+            gu.append(e0.elapsed_time(e1))
+    gateup = {"layer": "llama7b_mlp_gate+up_shared_s", "ms": round(statistics.mean(gu), 3),
+              "alpha_star": int(rgu.best.item())}
+    log("layer", gateup)
+    del ws, Xg, Wg, Wu, gate, up
+    torch.cuda.empty_cache()
+    Xd = torch.from_numpy(down.X).to(dev)
+    Wd = torch.from_numpy(down.W).to(dev)
+    out.append(one("llama7b_mlp_down_4096x11008", Wd, Xd, 4, 4096, 11008))
+    del Xd, Wd, down
+    torch.cuda.empty_cache()
+
+    log("generating the 70B-class activations (X 65536x8192 fp16) ...")
+    X5 = torch.from_numpy(workloads.c5_x(m=M_)).to(dev)
+    for (n, j, nm) in ((8192, 0, "attn_8192x8192"), (1024, 1, "gqa_kv_1024x8192"),
+                       (28672, 3, "mlp_28672x8192")):
+        W5 = torch.from_numpy(workloads.c5_weight(n, j=j)).to(dev)
+        for bits in (4, 3):
+            out.append(one(f"70b_{nm}_int{bits}", W5, X5, bits, n, 8192))
+        del W5
+        torch.cuda.empty_cache()
+    del X5
+    torch.cuda.empty_cache()
+    return out, gateup
+
+
 def w4a16_sweep(awq, torch):
     """The symmetric group-128 kernel at the batch sizes 1, 4, 16, 64, 512 for 4096x4096 and
     11008x4096."""
@@ -256,11 +376,15 @@ def cpu_baseline(L, n_grid):
     decode-sized W4A16 (x1)."""
     import numpy as np
     import oracle
+    # the host cores this process may run on; the BLAS pool is sized to them (capped by the
+    # OMP_NUM_THREADS share the host gives a job, when set), and `cores` is what it used
+    affinity = len(os.sched_getaffinity(0))
+    cores = min(affinity, int(os.environ.get("OMP_NUM_THREADS", affinity) or affinity))
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
     except Exception:  # pragma: no cover
-        cores = 1
+        limiter = None
     Ms = 4096
     Xs = L.X[:Ms]
     t = {}
@@ -284,7 +408,10 @@ def cpu_baseline(L, n_grid):
     oracle.w4a16(A, p["qweight"], p["scales16"], p["s16"])
     t["pack_w4a16"] = time.perf_counter() - t0
     total_ms = 1e3 * sum(t.values())
+    if limiter is not None:
+        limiter.restore_original_limits()
     return {"value": round(total_ms, 1), "unit": "ms/layer", "cores": int(cores),
+            "affinity_cores": affinity,
             "kind": "oracle",
             "sample": "stats and H=X^T X over 4096 of 65536 tokens (x16), quantize+Gram loss "
                       "for 2 of 20 alpha points (x10), argmin+pack+W4A16(M=1) once",
@@ -562,6 +689,23 @@ def main():
         log("cpu baseline (oracle on a bounded sample) ...")
         cpu = cpu_baseline(L, N_GRID)
         log("cpu baseline", cpu)
+    del L
+
+    layers, block = None, None
+    if args.layer_reps > 0:
+        layers, gateup = layer_sweep(awq, torch, args.layer_reps,
+                                     cpu["parts_ms"] if cpu else None)
+        # one LLaMA-7B decoder block: q/k/v with one s, o (the step's layer), gate/up with one
+        # s, down; the pages quote about 3 minutes (and about 2) for a whole 7B model, on
+        # hardware they do not state
+        down_ms = next(r["ms"] for r in layers if r["layer"].startswith("llama7b_mlp_down"))
+        if shared_rec is not None:
+            block_ms = shared_rec["search_ms"] + ms_per_step + gateup["ms"] + down_ms
+            block = {"block_ms": round(block_ms, 2), "model_32_blocks_s": round(32 * block_ms / 1e3, 2),
+                     "parts": {"qkv_shared": shared_rec["search_ms"], "o": round(ms_per_step, 3),
+                               "gate_up_shared": gateup["ms"], "down": down_ms},
+                     "note": "context only: calibration activations of each layer resident on "
+                             "the GPU; excludes running the model to collect them"}
 
     line = {
         "metric": "AWQ search ms per 4096x4096 layer + % MFMA peak; W4A16 GEMV HBM GB/s",
@@ -582,6 +726,8 @@ def main():
         "quant_variants": variants_rec,
         "hbm_stages": other,
         "w4a16": w4,
+        "layers": layers,
+        "llama7b_block_estimate": block,
         "alpha_star": best,
         "loss_gap": float((ls[1] - ls[0]) / ls[0]),
         "flags": flag_bits,
