@@ -52,8 +52,11 @@ size_t w4a16_skinny_lds_bytes(int MB, int64_t K, int GS, bool ZP) {
 // unconditional (indices clamped), issued before the weight loads: a load inside a conditional
 // block is issued there, and since loads complete in order, waiting for it would mean waiting
 // for all the weight loads in flight.
+// TI = 1 (K <= 4096): a wave's blocks (at most 4) are one chunk of loads, so there is one load
+// buffer and no loop; with MB = 1 these instances fit in 80 VGPRs (6 waves per SIMD), so three
+// workgroups fit on a CU and a weight of up to 768 row blocks (12288 rows) runs in one round.
 template <int MB, int GS, bool ZP, bool HAS_S, int TI>
-__global__ __launch_bounds__(kThreads) void w4a16_skinny_kernel(
+__global__ __launch_bounds__(kThreads, (MB == 1 && TI == 1) ? 6 : 1) void w4a16_skinny_kernel(
     const uint16_t* __restrict__ A, int64_t M, int64_t N, int64_t K,
     const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales16,
     const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ s16,
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_skinny_kernel(
   const bool nok = n < N;
   const uint4* wrow = reinterpret_cast<const uint4*>(qweight + (nok ? n : N - 1) * words_per_row) + lg;
   const int my_blocks = (gr - wave + kWaves - 1) / kWaves;     // g = wave + kWaves i
-  uint4 wbuf[2][kChunk];
+  uint4 wbuf[TI == 1 ? 1 : 2][kChunk];
   auto load_chunk = [&](int c, uint4 (&dst)[kChunk]) {
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
@@ -247,14 +250,18 @@ __global__ __launch_bounds__(kThreads) void w4a16_skinny_kernel(
     }
   };
 
-  // chunks alternate between the two register buffers (static indices: no scratch)
-  const int nchunks = (my_blocks + kChunk - 1) / kChunk;
-  for (int c = 0; c < nchunks; c += 2) {
-    if (c + 1 < nchunks) load_chunk(c + 1, wbuf[1]);
-    process(wbuf[0], c);
-    if (c + 1 < nchunks) {
-      if (c + 2 < nchunks) load_chunk(c + 2, wbuf[0]);
-      process(wbuf[1], c + 1);
+  if constexpr (TI == 1) {
+    process(wbuf[0], 0);
+  } else {
+    // chunks alternate between the two register buffers (static indices: no scratch)
+    const int nchunks = (my_blocks + kChunk - 1) / kChunk;
+    for (int c = 0; c < nchunks; c += 2) {
+      if (c + 1 < nchunks) load_chunk(c + 1, wbuf[TI == 1 ? 0 : 1]);
+      process(wbuf[0], c);
+      if (c + 1 < nchunks) {
+        if (c + 2 < nchunks) load_chunk(c + 2, wbuf[0]);
+        process(wbuf[TI == 1 ? 0 : 1], c + 1);
+      }
     }
   }
 
