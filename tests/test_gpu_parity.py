@@ -355,7 +355,7 @@ def _w4a16_case(n, k, m, seed):
 
 W4A16_CASES = [(384, 512, m) for m in (1, 3, 16, 17, 64, 100)] + \
               [(4096, 4096, m) for m in (1, 4, 16, 64, 512)] + \
-              [(11008, 4096, m) for m in (1, 64)] + [(4096, 11008, 16)] + \
+              [(11008, 4096, m) for m in (1, 4, 16, 64, 512)] + [(4096, 11008, 16)] + \
               [(1024, 8192, 1), (256, 12288, 2)] + \
               [(8192, 4096, 49), (8192, 4096, 48)]   # tiled from 49 rows on tall weights
 
@@ -537,17 +537,36 @@ def test_full_c2_layer(awq):
     assert oracle.accuracy_report(Y_g, ref)["rel_fro"] <= W4A16_RTOL
 
 
-def _full_size_layer_check(awq, name, W, X, bits, row_step):
+@pytest.fixture(scope="module")
+def c3_x_gram():
+    """The LLaMA-7B MLP gate/up input at full size, X fp16 [65536, 4096], with the oracle's s_X
+    and H = X^T X in fp64, built once for every test that uses it."""
+    X = workloads.activations(3, 65536, workloads.channel_gains_lognormal(3, 4096, 0.01, 50.0),
+                              np.float16)
+    return X, oracle.act_stats(X), oracle.gram(X)
+
+
+@pytest.fixture(scope="module")
+def c5_x_gram():
+    """The 70B-class input at full size, X fp16 [65536, 8192], with the oracle's s_X and
+    H = X^T X in fp64, built once for every 70B-class layer."""
+    X = workloads.c5_x()
+    return X, oracle.act_stats(X), oracle.gram(X)
+
+
+def _full_size_layer_check(awq, name, W, X, bits, row_step, every_alpha=False, sx_o=None,
+                           H=None):
     """A full-size layer (65536 tokens) in the launch configuration the benchmark times: both
-    search forms on the GPU, then against the oracle what it can compute at this size in a minute
-    or two: s_X (every channel, bit-exact), H = X^T X in fp64 once, the loss at alpha = 0, at the
-    GPU's alpha* and at alpha = 19 (both forms within 1e-4), the codes, packed words and fp16
-    steps of sampled rows at alpha* (bit-exact), and W4A16 on those rows. alpha* itself is checked
-    against the sampled oracle losses (it must not be beaten by them beyond the tie band), and the
-    two forms must choose the same alpha*."""
+    search forms on the GPU, then against the oracle: s_X (every channel, bit-exact), H = X^T X in
+    fp64, the loss of both forms within 1e-4 at every grid point (every_alpha) or, where 20
+    oracle contractions of the layer would take minutes, at alpha = 0, the GPU's alpha* and
+    alpha = 19, the codes, packed words and fp16 steps of sampled rows at alpha* (bit-exact), and
+    W4A16 on those rows. With every grid point alpha* follows the tie-band rule; otherwise it is
+    checked against the sampled oracle losses (it must not be beaten by them beyond the band)
+    and the two forms must choose the same alpha*."""
     M, K = X.shape
     N = W.shape[0]
-    say(name, W.shape, X.shape, "bits", bits)
+    say(name, W.shape, X.shape, "bits", bits, "every alpha" if every_alpha else "3 alphas")
     Wt, Xt = dev(W), dev(X)
     sx, flags = awq.act_stats(Xt)
     res_g = awq.search_layer(Wt, Xt, sx, awq.AwqConfig(bits=bits, form="gram"), flags=flags)
@@ -567,21 +586,31 @@ def _full_size_layer_check(awq, name, W, X, bits, row_step):
     say(f"gpu: alpha* gram {bg} direct {bd}")
     del Xt, Wt, res_g, res_d, p, Y
     torch.cuda.empty_cache()
-    assert bd == bg or oracle.relative_gap(losses_g) <= 2 * LOSS_RTOL
-    sx_o = oracle.act_stats(X)
+    if sx_o is None:
+        sx_o = oracle.act_stats(X)
     assert np.array_equal(sx_g, sx_o)
-    say("oracle: H = X^T X in fp64 ...")
-    H = oracle.gram(X)
+    if H is None:
+        say("oracle: H = X^T X in fp64 ...")
+        H = oracle.gram(X)
     S = oracle.scale_table(sx_o, 20)
+    grid = range(20) if every_alpha else sorted({0, bg, bd, 19})
     lo = {}
-    for i in sorted({0, bg, 19}):
+    for i in grid:
         q, d = oracle.quantize(W, S[i], bits=bits)
         lo[i] = oracle.loss_gram(H, oracle.error_matrix(W, q, d, S[i]), M)
         rg = abs(losses_g[i] - lo[i]) / lo[i]
         rd = abs(losses_d[i] - lo[i]) / lo[i]
         say(f"oracle alpha {i}: L = {lo[i]:.9e}  gram rel {rg:.2e}  direct rel {rd:.2e}")
         assert rg <= LOSS_RTOL and rd <= LOSS_RTOL
-    assert lo[bg] <= min(lo.values()) * (1 + 2 * LOSS_RTOL)
+    if every_alpha:
+        lo_all = np.array([lo[i] for i in range(20)])
+        best_o = oracle.argmin_lowest(lo_all)
+        check_alpha(losses_g, lo_all, bg, best_o)
+        check_alpha(losses_d, lo_all, bd, best_o)
+        say(f"oracle alpha* {best_o}, gap {oracle.relative_gap(lo_all):.2e}")
+    else:
+        assert bd == bg or oracle.relative_gap(losses_g) <= 2 * LOSS_RTOL
+        assert lo[bg] <= min(lo.values()) * (1 + 2 * LOSS_RTOL)
     o = oracle.pack_layer(W[rows], S[bg], bits=bits)
     assert np.array_equal(codes_g, o["codes"])
     assert np.array_equal(qw_g, o["qweight"])
@@ -592,23 +621,51 @@ def _full_size_layer_check(awq, name, W, X, bits, row_step):
 
 @pytest.mark.slow
 @pytest.mark.timeout(900)
-def test_full_c3_down_layer(awq):
-    """LLaMA-7B MLP down projection at full size: W fp16 [4096, 11008], X fp16 [65536, 11008]
-    = |N(0,1)| with 110 channels x30."""
-    W = workloads.weight(3, 4096, 11008, j=2)
-    X = workloads.activations(3, 65536, workloads.channel_gains_choice(3, 11008, 110, 30.0, j=2),
-                              np.float16, j=2, absolute=True)
-    _full_size_layer_check(awq, "full c3 down", W, X, 4, row_step=67)
+def test_full_c3_gate_layer(awq, c3_x_gram):
+    """LLaMA-7B MLP gate projection at full size, every grid point: W fp16 [11008, 4096],
+    X fp16 [65536, 4096] (lognormal gains, top 1% x50)."""
+    X, sx_o, H = c3_x_gram
+    W = workloads.weight(3, 11008, 4096, j=0)
+    _full_size_layer_check(awq, "full c3 gate", W, X, 4, row_step=103, every_alpha=True,
+                           sx_o=sx_o, H=H)
 
 
 @pytest.mark.slow
 @pytest.mark.timeout(900)
-def test_full_c5_mlp_layer_int3(awq):
-    """70B-class MLP projection at full size, INT3: W fp16 [28672, 8192], X fp16 [65536, 8192]
-    with 1% of the channels x50."""
-    W = workloads.c5_weight(28672, j=3)
-    X = workloads.c5_x()
-    _full_size_layer_check(awq, "full c5 mlp int3", W, X, 3, row_step=211)
+def test_full_c3_down_layer(awq):
+    """LLaMA-7B MLP down projection at full size, every grid point: W fp16 [4096, 11008],
+    X fp16 [65536, 11008] = |N(0,1)| with 110 channels x30."""
+    W = workloads.weight(3, 4096, 11008, j=2)
+    X = workloads.activations(3, 65536, workloads.channel_gains_choice(3, 11008, 110, 30.0, j=2),
+                              np.float16, j=2, absolute=True)
+    _full_size_layer_check(awq, "full c3 down", W, X, 4, row_step=67, every_alpha=True)
+
+
+C5_FULL_EVERY_ALPHA = [("c5_8192x8192_int4", 8192, 0, 4), ("c5_8192x8192_int3", 8192, 0, 3),
+                       ("c5_1024x8192_int4", 1024, 1, 4)]
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,n,j,bits", C5_FULL_EVERY_ALPHA, ids=[c[0] for c in C5_FULL_EVERY_ALPHA])
+def test_full_c5_layer_every_alpha(awq, c5_x_gram, name, n, j, bits):
+    """70B-class projections at full size (X fp16 [65536, 8192], 1% of the channels x50), every
+    grid point: the square attention projection in INT4 and INT3, and the 1024-row K/V
+    projection."""
+    X, sx_o, H = c5_x_gram
+    _full_size_layer_check(awq, "full " + name, workloads.c5_weight(n, j=j), X, bits,
+                           row_step=max(1, n // 97), every_alpha=True, sx_o=sx_o, H=H)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("bits", [4, 3])
+def test_full_c5_mlp_layer(awq, c5_x_gram, bits):
+    """70B-class MLP projection at full size, INT4 and INT3: W fp16 [28672, 8192],
+    X fp16 [65536, 8192] with 1% of the channels x50 (oracle losses at alpha = 0, alpha*, 19)."""
+    X, sx_o, H = c5_x_gram
+    _full_size_layer_check(awq, f"full c5 mlp int{bits}", workloads.c5_weight(28672, j=3), X,
+                           bits, row_step=211, sx_o=sx_o, H=H)
 
 
 # ------------------------------------------------------------------------------------------------
