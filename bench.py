@@ -79,7 +79,9 @@ def parse():
                     help="repetitions of the shared q/k/v search and the fold (0: skip)")
     ap.add_argument("--layer-reps", type=int, default=2,
                     help="repetitions of each other layer shape's search (0: skip them)")
-    ap.add_argument("--mode", choices=("bench", "traffic"), default="bench",
+    ap.add_argument("--counters", default=None,
+                    help="record mode: directory holding one rocprofv3 CSV directory per pass")
+    ap.add_argument("--mode", choices=("bench", "traffic", "record"), default="bench",
                     help="traffic: one 1 GiB device copy (counter calibration) and one pass of "
                          "the path in each form, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
     return ap.parse_args()
@@ -167,10 +169,156 @@ def traffic_pass():
                    p.s16)
     torch.cuda.synchronize()
     log("path pass done")
+    # W4A16 on random artefacts of the two LLaMA-7B shapes, one call per batch size, in this
+    # order (the counter record matches dispatches to these calls by order)
+    for n, k, m in W4A16_COUNTER_CALLS:
+        qw = torch.randint(-2**31, 2**31 - 1, (n, k // 8), dtype=torch.int32, device=dev,
+                           generator=g)
+        sc = (0.01 * torch.rand(n, k // 128, device=dev, generator=g) + 1e-3).half()
+        s16 = (1.0 + torch.rand(k, device=dev, generator=g)).half()
+        A = torch.randn(m, k, device=dev, generator=g).half()
+        awq.w4a16_gemm(A, qw, sc, s16)
+        torch.cuda.synchronize()
+    log("w4a16 calls done")
+
+
+# (n, k, m) of the W4A16 calls of the counter pass
+W4A16_COUNTER_CALLS = [(4096, 4096, 1), (4096, 4096, 16), (4096, 4096, 64), (4096, 4096, 512),
+                       (11008, 4096, 1), (11008, 4096, 4), (11008, 4096, 16)]
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "awq_path_c2_counters.txt")
+COUNTER_PASSES = {
+    "trace": "--kernel-trace --stats",
+    "fetch": "--pmc FETCH_SIZE",
+    "write": "--pmc WRITE_SIZE",
+    "mfma": "--pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVES "
+            "SQ_INSTS_VALU_MFMA_MOPS_F16 GRBM_GUI_ACTIVE",
+}
+
+
+def record_counters(ctr_dir):
+    """Write the counter record that `measured_traffic` reads and its text summary from the CSV
+    output of rocprofv3 passes over `bench.py --mode traffic`: one directory per pass under
+    `ctr_dir` (trace, fetch, write, mfma), each made by
+        rocprofv3 <pass counters> --output-format csv -d <ctr_dir>/<pass> -o t \
+            -- python3 bench.py --mode traffic
+    Every pass runs the same launches in the same order, so dispatch ids match across passes
+    (checked by kernel name). Byte counters are scaled by what they read for the 1 GiB copy."""
+    import csv
+    import collections
+
+    def load(sub, fname):
+        with open(os.path.join(ctr_dir, sub, fname)) as f:
+            return list(csv.DictReader(f))
+
+    def counters(sub):
+        vals, names, grid = collections.defaultdict(dict), {}, {}
+        for r in load(sub, "t_counter_collection.csv"):
+            i = int(r["Dispatch_Id"])
+            names[i], grid[i] = r["Kernel_Name"], int(r["Grid_Size"])
+            vals[i][r["Counter_Name"]] = vals[i].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        return vals, names, grid
+
+    dur, tnames = {}, {}
+    for r in load("trace", "t_kernel_trace.csv"):
+        i = int(r["Dispatch_Id"])
+        dur[i] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        tnames[i] = r["Kernel_Name"]
+    fetch, fnames, grid = counters("fetch")
+    write, wnames, _ = counters("write")
+    mfma, mnames, _ = counters("mfma")
+    for i, n in tnames.items():
+        for other in (fnames, wnames, mnames):
+            if i in other and other[i] != n:
+                raise RuntimeError(f"dispatch {i}: {n} vs {other[i]} (passes out of step)")
+    copies = [i for i, n in fnames.items() if "copyBuffer" in n]
+    big = max(copies, key=lambda i: fetch[i]["FETCH_SIZE"])
+    rf = (1 << 30) / (fetch[big]["FETCH_SIZE"] * 1024.0)
+    wf = (1 << 30) / (write[big]["WRITE_SIZE"] * 1024.0)
+
+    def short(name):
+        name = name.replace("void ", "").replace("awq::", "")
+        cut = name.find("(")
+        return name[:cut] if cut > 0 else name
+
+    t_ = -(-K_ // 256)
+    algo = {"lossgemm_kernel": M_ * K_ * 2 + N_GRID * N_ * K_ * 2,
+            "gram_loss_kernel": N_GRID * N_ * K_ * 2 + K_ * K_ * 2}
+    w4_calls = iter(W4A16_COUNTER_CALLS)
+    rows, kernels = [], {}
+    seen_w4 = 0
+    for i in sorted(tnames):
+        n = short(tnames[i])
+        if "awq" not in tnames[i] and i != big:
+            continue
+        if i not in fetch or i not in write or i not in mfma:
+            continue
+        fb = fetch[i]["FETCH_SIZE"] * 1024.0 * rf
+        wb = write[i]["WRITE_SIZE"] * 1024.0 * wf
+        c = mfma[i]
+        cyc = c["GRBM_GUI_ACTIVE"] / 8.0           # the counter sums the 8 XCDs
+        us = dur[i]
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024.0 / cyc if cyc else 0.0   # 1024 SIMDs
+        label = n
+        a_bytes = algo.get(n)
+        if n == "gram_gemm_kernel":
+            # X^T read once plus the fp32 partial tiles written, one 256 x 256 tile per workgroup
+            a_bytes = (-(-M_ // 128) * 128) * K_ * 2 + (grid[i] // 256) * 256 * 256 * 4
+        if n.startswith("w4a16") and seen_w4 >= 1:
+            nn, kk, mm = next(w4_calls)
+            label = f"w4a16 {nn}x{kk} M={mm}: {n}"
+            a_bytes = nn * kk // 2 + nn * (kk // 128) * 2 + kk * 2 + mm * kk * 2 + mm * nn * 2
+        if n.startswith("w4a16"):
+            seen_w4 += 1                           # the first is the path pass's decode call
+        rows.append((i, label, grid[i], us, fb, wb, a_bytes, c["SQ_INSTS_MFMA"], busy,
+                     cyc / us / 1e3 if us > 0 else 0.0))
+        if n in ("lossgemm_kernel", "gram_loss_kernel", "gram_gemm_kernel") and n not in kernels:
+            kernels[n] = {"fetch_kib": fetch[i]["FETCH_SIZE"], "write_kib": write[i]["WRITE_SIZE"],
+                          "hbm_bytes_per_launch": int(fb + wb),
+                          "algorithmic_bytes_per_launch": int(a_bytes),
+                          "mfma_insts": int(c["SQ_INSTS_MFMA"]), "mfma_busy": round(busy, 4),
+                          "clock_ghz": round(cyc / us / 1e3, 3), "trace_us": round(us, 1),
+                          "src_sha256_16": source_digest(n)}
+    cmds = [f"rocprofv3 {v} --output-format csv -d <dir>/{k} -o t -- python3 bench.py --mode traffic"
+            for k, v in COUNTER_PASSES.items()]
+    rec = {"workload": f"{N_}x{K_} fp16 layer, {M_} fp16 tokens, {N_GRID} alpha points; "
+                       "W4A16 calls " + ", ".join(f"{n}x{k} M={m}" for n, k, m in W4A16_COUNTER_CALLS),
+           "read_factor": rf, "write_factor": wf, "commands": cmds, "kernels": kernels}
+    with open(TRAFFIC_RECORD, "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = [
+        "# rocprofv3 counters of one pass of the path (bench.py --mode traffic): a 1 GiB device",
+        f"# copy, the search of a {N_}x{K_} fp16 layer with {M_} fp16 tokens at {N_GRID} grid points",
+        "# in each form (direct, Gram), clipping search, pack, one decode call, then W4A16 calls on",
+        "# random artefacts (shapes in brackets).",
+        "#",
+        "# commands (from /tmp, TMPDIR=/tmp), one run per pass:",
+    ] + [f"#   {c}" for c in cmds] + [
+        "# then: python3 bench.py --mode record --counters <dir>",
+        "#",
+        f"# read factor {rf:.4f}, write factor {wf:.4f} (FETCH_SIZE / WRITE_SIZE of the 1 GiB copy);",
+        "# the byte counters count traffic leaving L2 toward memory (Infinity Cache hits included).",
+        "# us: kernel-trace duration of the same dispatch (trace pass). clock: GRBM_GUI_ACTIVE / 8",
+        "# XCDs / us (meaningless for dispatches of a few us, where the counter window dominates).",
+        "# mfma_busy: SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8); busy x clock is",
+        "# the MFMA rate in units of one SIMD fully busy at 1 GHz (2.4 = the 2.5 PFLOP/s peak).",
+        "",
+        f"{'dispatch':>8} {'kernel':66s} {'grid':>10} {'us':>10} {'read_MB':>10} {'write_MB':>9} "
+        f"{'algo_MB':>9} {'ratio':>6} {'mfma_insts':>11} {'busy':>6} {'clock':>6} {'busyxclk':>8}",
+    ]
+    for (i, label, g, us, fb, wb, ab, mi, busy, clk) in rows:
+        ratio = f"{(fb + wb) / ab:6.2f}" if ab else "     -"
+        amb = f"{ab / 1e6:9.1f}" if ab else "        -"
+        lines.append(f"{i:8d} {label[:66]:66s} {g:10d} {us:10.1f} {fb / 1e6:10.1f} {wb / 1e6:9.1f} "
+                     f"{amb} {ratio} {int(mi):11d} {busy:6.3f} {clk:6.2f} {busy * clk:8.3f}")
+    with open(COUNTER_SUMMARY, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("wrote", TRAFFIC_RECORD, "and", COUNTER_SUMMARY)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -421,6 +569,9 @@ def cpu_baseline(L, n_grid):
 # ---------------------------------------------------------------------------------------------
 def main():
     args = parse()
+    if args.mode == "record":
+        record_counters(args.counters)
+        return
     if args.mode == "traffic":
         traffic_pass()
         return
