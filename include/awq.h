@@ -273,8 +273,11 @@ awq_status awq_stats_search_layer(const void* W, awq_dtype wdt, int64_t N, int64
  * exactly as in awq_search_layer (so that Delta = c / (2^(b-1)-1)), and scored by the output
  * error the group causes on its own,
  *   err_j[n, g] = sum_m ( sum_{k in g} X[m,k] E[n,k] )^2,  E = Q(W s)/s - W,
- * evaluated as E_g H_gg E_g^T with the group's diagonal block of H = X^T X (fp16 correlation
- * operand and error rows, fp32 accumulation, as in the Gram form of awq_search_layer).
+ * evaluated as E_g H_gg E_g^T with the group's diagonal block of H = X^T X, in the conditioned
+ * form of the Gram-form search: the error rows and the correlation block each as the sum of a
+ * high and a low fp16 part (about 2^-22 relative), three MFMA products accumulated in fp32, the
+ * final sum against the fp32 error rows. H is formed from X rounded to fp16 (exact for fp16 X;
+ * for fp32 / bf16 X that rounding, up to 2^-11 per element, is the larger error).
  * clip[n, g] = r of the smallest error (the lowest j on ties).
  * W        [N, K], dtype wdt (AWQ_F16 or AWQ_F32); X [M, K] (row stride K), dtype xdt;
  * s        fp32 [K], the scale to clip at (typically s_best of awq_search_layer).

@@ -45,7 +45,7 @@ bool precise_path(int64_t M, int64_t N) {
 struct SearchLayout {
   size_t ctrl, S, X16, E, partials, total;
   bool precise;                    // fp32 error stack and the vector-ALU contraction
-  size_t d64, d32, B, Xt, Hpart;   // Gram form only (Xt and Hpart share memory with E)
+  size_t d64, d32, B, Blo, Xt, Hpart;   // Gram form only (Xt and Hpart share memory with E)
   size_t stats;                    // chunk partials of s_X when the search takes it (in Hpart
                                    // or in E: both are written only after s_X is final)
   int64_t tiles_per_alpha;
@@ -53,8 +53,9 @@ struct SearchLayout {
 };
 
 // Direct form: ctrl | S | X16 (non-fp16 X) | E stack | partials.
-// Gram form:   ctrl | S | d64 | d32 | B | partials | union(Xt + Hpart, E stack); Xt and the H
-//              partials are dead before the error stack is written.
+// Gram form:   ctrl | S | d64 | d32 | B | Blo | partials | union(Xt + Hpart, E stack); Xt and
+//              the H partials are dead before the error stack is written. Blo (the low-order
+//              parts of B's diagonal 256 x 256 blocks) serves the clipping search only.
 SearchLayout search_layout(int64_t M, int64_t N, int64_t K, awq_dtype xdt, int n_grid,
                            int form) {
   SearchLayout L{};
@@ -77,6 +78,8 @@ SearchLayout search_layout(int64_t M, int64_t N, int64_t K, awq_dtype xdt, int n
     off += align_up((size_t)K * sizeof(float));
     L.B = off;
     off += align_up((size_t)K * (size_t)K * 2);
+    L.Blo = off;
+    off += align_up((size_t)L.plan.t * (size_t)(awq::kLossBM * awq::kLossBN) * 2);
     L.partials = off;
     off += align_up((size_t)n_grid * (size_t)L.tiles_per_alpha * sizeof(double));
     const size_t xt_bytes = align_up((size_t)K * (size_t)L.plan.Mp * 2);
@@ -258,7 +261,8 @@ awq_status search_impl(const void* const* Ws, const int64_t* Ns, int n_w, awq_dt
       e = awq::launch_gram_hmat(Xt, K, L.plan, reinterpret_cast<float*>(base + L.Hpart),
                                 reinterpret_cast<double*>(base + L.d64),
                                 reinterpret_cast<float*>(base + L.d32),
-                                reinterpret_cast<uint16_t*>(base + L.B), &ctrl->gram_k, stream,
+                                reinterpret_cast<uint16_t*>(base + L.B),
+                                reinterpret_cast<uint16_t*>(base + L.Blo), &ctrl->gram_k, stream,
                                 ev ? ev[2 * 2 + 1] : nullptr, ev ? ev[2 * 3] : nullptr);
   } else {
     mark(2 * 2 + 1);
@@ -399,7 +403,7 @@ awq_status awq_pack_int4(const void* W, awq_dtype wdt, int64_t N, int64_t K, con
 namespace {
 
 struct ClipLayout {
-  size_t d64, d32, Bd, Xt, Hpart, total;
+  size_t d64, d32, Bd, Bdl, Xt, Hpart, total;
   awq::GramPlan plan;
 };
 
@@ -412,6 +416,8 @@ ClipLayout clip_layout(int64_t M, int64_t K) {
   L.d32 = off;
   off += align_up((size_t)K * sizeof(float));
   L.Bd = off;
+  off += align_up((size_t)L.plan.t * (size_t)(awq::kLossBM * awq::kLossBN) * 2);
+  L.Bdl = off;
   off += align_up((size_t)L.plan.t * (size_t)(awq::kLossBM * awq::kLossBN) * 2);
   L.Xt = off;
   off += align_up((size_t)K * (size_t)L.plan.Mp * 2);
@@ -463,14 +469,15 @@ awq_status awq_clip_search(const void* W, awq_dtype wdt, int64_t N, int64_t K, c
   char* base = static_cast<char*>(ws);
   auto* d32 = reinterpret_cast<float*>(base + L.d32);
   auto* Bd = reinterpret_cast<uint16_t*>(base + L.Bd);
+  auto* Bdl = reinterpret_cast<uint16_t*>(base + L.Bdl);
   hipError_t e = awq::launch_gram_prepare(X, (int)xdt, M, K, L.plan,
                                           reinterpret_cast<uint16_t*>(base + L.Xt),
                                           reinterpret_cast<float*>(base + L.Hpart),
-                                          reinterpret_cast<double*>(base + L.d64), d32, Bd,
+                                          reinterpret_cast<double*>(base + L.d64), d32, Bd, Bdl,
                                           nullptr, flags, stream, nullptr);
   if (e == hipSuccess)
     e = awq::launch_clip_search(W, (int)wdt, N, K, s, d32, Bd, (int64_t)awq::kLossBM * awq::kLossBN,
-                                awq::kLossBN, nullptr, 0,
+                                awq::kLossBN, Bdl, nullptr, 0,
                                 cfg->n_clip, cfg->clip_min, cfg->bits, cfg->group,
                                 cfg->zero_point != 0, clip, clip_err, flags, stream);
   return hip_status(e);
@@ -481,7 +488,7 @@ size_t awq_clip_search_gram_ws_bytes(int64_t K, const awq_cfg* cfg) {
   if (K < 128 || K % cfg->group || K > kMaxGramK) return 0;
   const SearchLayout L = search_layout(awq::kGramMAlign, 1, K, AWQ_F16, cfg->n_grid,
                                        AWQ_FORM_GRAM);
-  return L.B + (size_t)K * (size_t)K * 2;
+  return L.Blo + (size_t)L.plan.t * (size_t)(awq::kLossBM * awq::kLossBN) * 2;
 }
 
 awq_status awq_clip_search_gram(const void* W, awq_dtype wdt, int64_t N, int64_t K,
@@ -506,7 +513,7 @@ awq_status awq_clip_search_gram(const void* W, awq_dtype wdt, int64_t N, int64_t
   return hip_status(awq::launch_clip_search(
       W, (int)wdt, N, K, s, reinterpret_cast<const float*>(base + L.d32),
       reinterpret_cast<const uint16_t*>(base + L.B), (int64_t)awq::kLossBN * K + awq::kLossBN, K,
-      ctrl, cfg->n_grid, cfg->n_clip, cfg->clip_min, cfg->bits, cfg->group,
+      reinterpret_cast<const uint16_t*>(base + L.Blo), ctrl, cfg->n_grid, cfg->n_clip, cfg->clip_min, cfg->bits, cfg->group,
       cfg->zero_point != 0, clip, clip_err, flags, stream));
 }
 

@@ -12,15 +12,22 @@
 // operand B_gg (strict lower correlations, 1/2 diagonal) is the diagonal block of the
 // block-diagonal correlation operand.
 //
+// Precision: each error is compared across ratios that differ little, so the contraction is
+// carried to ~2^-22 rather than fp16's 2^-11: E' = E'_hi + E'_lo and B = B_hi + B_lo (each part
+// fp16; B_lo from the operand's preparation), and P = E'_lo B_hi + E'_hi B_lo + E'_hi B_hi in
+// fp32 accumulation (E'_lo B_lo, below 2^-22 relative, is left out); the epilogue takes E' in
+// fp32.
+//
 // gfx950 layout: a workgroup of 4 waves takes 64 rows of one group of GS channels (128 or 64).
 // Lane (i = lane % 16, q = lane / 16) of a wave owns row 16 w + i and the channels 32 kb + 8 q + t
 // (kb < GS / 32, t < 8) of the group: exactly the A operand of v_mfma_f32_16x16x32_f16 for the
 // group's 32-channel K blocks, so the quantized E' goes from registers straight into the MFMA.
-// B_gg sits in LDS and its lower-triangular 32 x 16 fragments in registers (20 for 128 channels,
-// 6 for 64); P for 16 rows costs that many MFMAs. The epilogue needs E' in the accumulator layout
-// (lane holds rows 4 q .. 4 q + 3 of column 16 cb + i), which it reads back from a per-wave LDS
-// tile. With zero points (ZP) the clipped range is [max(min, -c), min(max, c)] of the unclipped
-// group extremes, so the ratios need no further cross-lane reductions.
+// B_gg sits in LDS and the lower-triangular 32 x 16 fragments of its two parts in registers (20
+// each for 128 channels, 6 for 64); P for 16 rows costs three times that many MFMAs. The
+// epilogue needs E' in the accumulator layout (lane holds rows 4 q .. 4 q + 3 of column
+// 16 cb + i), which it reads back from a per-wave fp32 LDS tile. With zero points (ZP) the
+// clipped range is [max(min, -c), min(max, c)] of the unclipped group extremes, so the ratios
+// need no further cross-lane reductions.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -46,7 +53,8 @@ template <int DT, int GS, bool ZP>
 __global__ __launch_bounds__(256) void clip_search_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s,
     const float* __restrict__ d32, const uint16_t* __restrict__ Bd, int64_t bd_block,
-    int64_t bd_pitch, const SearchCtrl* __restrict__ ctrl, int n_grid, int n_clip, float clip_min,
+    int64_t bd_pitch, const uint16_t* __restrict__ Bdl, const SearchCtrl* __restrict__ ctrl,
+    int n_grid, int n_clip, float clip_min,
     float qmin, float qmax, float* __restrict__ clip, float* __restrict__ clip_err,
     uint32_t* __restrict__ flags) {
   constexpr int ES = (DT == kF32) ? 4 : 2;
@@ -54,9 +62,10 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
   constexpr int CB = GS / 16;               // 16-channel column blocks per group
   constexpr int NF = frag_base(CB);         // lower-triangular B fragments
   constexpr int kPitch = GS + 8;            // LDS row pitch in halves (no bank conflicts)
+  constexpr int kPitchF = GS + 4;           // fp32 E' tile pitch in floats (no bank conflicts)
   constexpr int NV = 8 * KB;                // channels per lane
   __shared__ __attribute__((aligned(16))) uint16_t Bg[GS * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t Et[kClipWaves][16 * kPitch];
+  __shared__ __attribute__((aligned(16))) float Et[kClipWaves][16 * kPitchF];
   const int64_t G = K / GS;
   const int g = blockIdx.y;
   const int64_t n0 = (int64_t)blockIdx.x * kClipRows;
@@ -100,7 +109,7 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
       for (int t = 0; t < 8; ++t) w[t] = 0.0f;
     }
     load8_f32<kF32>(s + kb0 + 32 * kb, sv);
-    load8_f32<kF32>(d32 + kb0 + 32 * kb, dv);
+    load8_f32<kF32>(d32 + kb0 + 32 * kb, dv);   // d / s below: correctly rounded
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       bad |= !isfinite(w[t]);
@@ -109,7 +118,7 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
       mx = fmaxf(mx, ws[kb][t]);
       nmn = fmaxf(nmn, -ws[kb][t]);
       md = fmaxf(md, fabsf(w[t]) * dv[t]);
-      ca[kb][t] = dv[t] * __builtin_amdgcn_rcpf(sv[t]);
+      ca[kb][t] = dv[t] / sv[t];
       cb_[kb][t] = w[t] * dv[t];
     }
   }
@@ -136,13 +145,22 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
     }
   __syncthreads();
 
-  half8_t bf[NF];
+  half8_t bf[NF], bfl[NF];
+  {
+    // B_lo fragments straight from memory: the diagonal block holding the group, [256][256]
+    const int64_t c0 = (int64_t)g * GS;
+    const int o = (int)(c0 % 256);
+    const uint16_t* srcl = Bdl + (c0 / 256) * (int64_t)(kLossBM * kLossBN) + (int64_t)o * kLossBN + o;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int kb = 0; kb <= cb / 2; ++kb)
-      bf[frag_base(cb) + kb] =
-          *reinterpret_cast<const half8_t*>(&Bg[(16 * cb + i) * kPitch + 32 * kb + 8 * q]);
+      for (int kb = 0; kb <= cb / 2; ++kb) {
+        bf[frag_base(cb) + kb] =
+            *reinterpret_cast<const half8_t*>(&Bg[(16 * cb + i) * kPitch + 32 * kb + 8 * q]);
+        bfl[frag_base(cb) + kb] = *reinterpret_cast<const half8_t*>(
+            srcl + (int64_t)(16 * cb + i) * kLossBN + 32 * kb + 8 * q);
+      }
+  }
 
   // lanes i < 4 of each 16-lane quarter track row R = 4 q + i of the accumulator layout
   const int R = 4 * q + (i & 3);
@@ -151,7 +169,7 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
   float best = 0.0f;
   int best_j = 0;
   bool uf_any = false;
-  uint16_t* et = Et[wave];
+  float* et = Et[wave];
 
   for (int j = 0; j < n_clip; ++j) {
     const float c = clip_ratio(j, n_clip, clip_min) * m;
@@ -175,27 +193,34 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
       uf_any |= (c > 0.0f) && !(st.delta > 0.0f);
       quant_codes(v, st, qmin, qmax, qv);
     }
-    half8_t af[KB];
+    half8_t af[KB], al[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      uint32_t wd[4];
+      float evs[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const float ev = __builtin_fmaf(qv[8 * kb + t] * st.delta, ca[kb][t], -cb_[kb][t]);
         const uint16_t h = f2h(ev);
         af[kb][t] = __builtin_bit_cast(_Float16, h);
-        if (t & 1)
-          wd[t >> 1] |= (uint32_t)h << 16;
-        else
-          wd[t >> 1] = h;
+        al[kb][t] = __builtin_bit_cast(_Float16, f2h(ev - h2f(h)));   // exact difference
+        evs[t] = ev;
       }
-      *reinterpret_cast<uint4*>(&et[i * kPitch + 32 * kb + 8 * q]) =
-          make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      float* dst = &et[i * kPitchF + 32 * kb + 8 * q];
+      *reinterpret_cast<float4*>(dst) = make_float4(evs[0], evs[1], evs[2], evs[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(evs[4], evs[5], evs[6], evs[7]);
     }
     floatx4 acc[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       acc[cb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      // the two small cross terms first, then the leading one
+#pragma unroll
+      for (int kb = 0; kb <= cb / 2; ++kb) {
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[kb], bf[frag_base(cb) + kb], acc[cb],
+                                                        0, 0, 0);
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[kb], bfl[frag_base(cb) + kb], acc[cb],
+                                                        0, 0, 0);
+      }
 #pragma unroll
       for (int kb = 0; kb <= cb / 2; ++kb)
         acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[kb], bf[frag_base(cb) + kb], acc[cb],
@@ -212,8 +237,7 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
       part[rr] = 0.0f;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
-        part[rr] = __builtin_fmaf(h2f(et[(4 * q + rr) * kPitch + 16 * cb + i]), acc[cb][rr],
-                                  part[rr]);
+        part[rr] = __builtin_fmaf(et[(4 * q + rr) * kPitchF + 16 * cb + i], acc[cb][rr], part[rr]);
     }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) part[rr] = row16_sum(part[rr]);   // the 16 columns i
@@ -237,15 +261,17 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
 
 hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, const float* s,
                               const float* d32, const uint16_t* Bd, int64_t bd_block,
-                              int64_t bd_pitch, const SearchCtrl* ctrl, int n_grid, int n_clip,
-                              float clip_min, int bits, int group, bool zero_point, float* clip,
-                              float* clip_err, uint32_t* flags, hipStream_t stream) {
+                              int64_t bd_pitch, const uint16_t* Bdl, const SearchCtrl* ctrl,
+                              int n_grid, int n_clip, float clip_min, int bits, int group,
+                              bool zero_point, float* clip, float* clip_err, uint32_t* flags,
+                              hipStream_t stream) {
   const float qmax = zero_point ? (float)((1 << bits) - 1) : (float)((1 << (bits - 1)) - 1);
   const float qmin = zero_point ? 0.0f : -(float)(1 << (bits - 1));
   dim3 grid((unsigned)((N + kClipRows - 1) / kClipRows), (unsigned)(K / group));
 #define AWQ_CLIP(DT_, GS_, ZP_)                                                                  \
   clip_search_kernel<DT_, GS_, ZP_><<<grid, 256, 0, stream>>>(                                    \
-      W, N, K, s, d32, Bd, bd_block, bd_pitch, ctrl, n_grid, n_clip, clip_min, qmin, qmax, clip,  \
+      W, N, K, s, d32, Bd, bd_block, bd_pitch, Bdl, ctrl, n_grid, n_clip, clip_min, qmin, qmax,   \
+      clip,                                                                                      \
       clip_err, flags)
   if (dtype == kF32) {
     if (group == 64) {

@@ -233,12 +233,15 @@ __global__ __launch_bounds__(256) void gram_diag_kernel(const float* __restrict_
 
 // One thread per float4 of the fragment order: tokens-chunk sums in fp64 (chunk order fixed),
 // then B[l][k..k+3] for the four channels k..k+3 (consecutive A rows) of output row l. With
-// `diag`, B is stored as the diagonal blocks only: block a at B + 65536 a, row l - 256 a.
+// `diag`, B is stored as the diagonal blocks only: block a at B + 65536 a, row l - 256 a. With
+// Blo, the diagonal blocks' low-order parts fp16(b - fp16(b)) go to Blo in that same layout
+// (b the correlation in fp64): the clipping search carries the operand to ~2^-22 with them.
 __global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restrict__ Hpart,
                                                           int64_t K, int t, int64_t T, int S,
                                                           int diag,
                                                           const double* __restrict__ d64,
                                                           uint16_t* __restrict__ B,
+                                                          uint16_t* __restrict__ Blo,
                                                           uint32_t* __restrict__ gram_k) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;   // float4 index
   constexpr int64_t kPerTile = kLossBM * kLossBN / 4;
@@ -268,24 +271,28 @@ __global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restric
     h[3] += (double)p.w;
   }
   const double dl = d64[l];
-  uint16_t o[4];
+  uint16_t o[4], lo[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t kq = k + q;
-    float v = 0.0f;
+    double vd = 0.0;
     if (kq == l) {
-      v = 0.5f;
+      vd = 0.5;
     } else if (kq < l) {
       const double dk = d64[kq];
-      v = (dk > 0.0 && dl > 0.0) ? (float)(h[q] / (dk * dl)) : 0.0f;
+      vd = (dk > 0.0 && dl > 0.0) ? h[q] / (dk * dl) : 0.0;
     }
-    o[q] = f2h(v);
+    o[q] = f2h((float)vd);
+    lo[q] = f2h((float)(vd - (double)h2f(o[q])));
   }
-  const int64_t off = diag ? (int64_t)a * (kLossBM * kLossBN) + (l - (int64_t)a * kLossBN) * kLossBN +
-                                (k - (int64_t)a * kLossBM)
-                          : l * K + k;
+  const int64_t doff = (int64_t)a * (kLossBM * kLossBN) + (l - (int64_t)a * kLossBN) * kLossBN +
+                       (k - (int64_t)a * kLossBM);
+  const int64_t off = diag ? doff : l * K + k;
   *reinterpret_cast<uint2*>(B + off) =
       make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+  if (Blo && a == b)
+    *reinterpret_cast<uint2*>(Blo + doff) = make_uint2((uint32_t)lo[0] | ((uint32_t)lo[1] << 16),
+                                                       (uint32_t)lo[2] | ((uint32_t)lo[3] << 16));
 }
 
 // ------------------------------------------------------------------------------------------
@@ -418,8 +425,8 @@ hipError_t launch_gram_transpose(const void* X, int xdt, int64_t M, int64_t K, i
 }
 
 hipError_t launch_gram_hmat(const uint16_t* Xt, int64_t K, const GramPlan& p, float* Hpart,
-                            double* d64, float* d32, uint16_t* B, uint32_t* gram_k,
-                            hipStream_t stream, hipEvent_t ev, hipEvent_t ev2) {
+                            double* d64, float* d32, uint16_t* B, uint16_t* Blo,
+                            uint32_t* gram_k, hipStream_t stream, hipEvent_t ev, hipEvent_t ev2) {
   gram_gemm_kernel<<<(unsigned)(p.T * p.S), kloop::kThreads, 0, stream>>>(Xt, K, p.Mp, p.t, p.T,
                                                                           p.chunk, (int)p.diag,
                                                                           Hpart);
@@ -435,7 +442,7 @@ hipError_t launch_gram_hmat(const uint16_t* Xt, int64_t K, const GramPlan& p, fl
     const int64_t threads = p.T * (kLossBM * kLossBN / 4);
     gram_finish_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(Hpart, K, p.t, p.T,
                                                                               p.S, (int)p.diag,
-                                                                              d64, B, gram_k);
+                                                                              d64, B, Blo, gram_k);
     e = hipGetLastError();
   }
   return e;
@@ -443,12 +450,12 @@ hipError_t launch_gram_hmat(const uint16_t* Xt, int64_t K, const GramPlan& p, fl
 
 hipError_t launch_gram_prepare(const void* X, int xdt, int64_t M, int64_t K, const GramPlan& p,
                                uint16_t* Xt, float* Hpart, double* d64, float* d32, uint16_t* B,
-                               uint32_t* gram_k, uint32_t* flags, hipStream_t stream,
-                               hipEvent_t* ev) {
+                               uint16_t* Blo, uint32_t* gram_k, uint32_t* flags,
+                               hipStream_t stream, hipEvent_t* ev) {
   hipError_t e = launch_gram_transpose(X, xdt, M, K, p.Mp, Xt, nullptr, flags, stream);
   if (e == hipSuccess && ev) e = hipEventRecord(ev[0], stream);
   if (e == hipSuccess)
-    e = launch_gram_hmat(Xt, K, p, Hpart, d64, d32, B, gram_k, stream, ev ? ev[1] : nullptr,
+    e = launch_gram_hmat(Xt, K, p, Hpart, d64, d32, B, Blo, gram_k, stream, ev ? ev[1] : nullptr,
                          nullptr);
   return e;
 }

@@ -55,14 +55,16 @@ GramPlan gram_plan(int64_t M, int64_t K, bool diag = false);
 hipError_t launch_gram_transpose(const void* X, int xdt, int64_t M, int64_t K, int64_t Mp,
                                  uint16_t* Xt, double* stats, uint32_t* flags,
                                  hipStream_t stream);
-// X^T X partials -> ev, ev2 (each if not null) -> d and B
+// X^T X partials -> ev, ev2 (each if not null) -> d and B. Blo: nullptr, or [t][256][256] fp16,
+// the low-order parts fp16(b - fp16(b)) of the operand's diagonal blocks (block a: rows and
+// columns 256 a ..), for the clipping search.
 hipError_t launch_gram_hmat(const uint16_t* Xt, int64_t K, const GramPlan& p, float* Hpart,
-                            double* d64, float* d32, uint16_t* B, uint32_t* gram_k,
-                            hipStream_t stream, hipEvent_t ev, hipEvent_t ev2);
+                            double* d64, float* d32, uint16_t* B, uint16_t* Blo,
+                            uint32_t* gram_k, hipStream_t stream, hipEvent_t ev, hipEvent_t ev2);
 hipError_t launch_gram_prepare(const void* X, int xdt, int64_t M, int64_t K, const GramPlan& p,
                                uint16_t* Xt, float* Hpart, double* d64, float* d32, uint16_t* B,
-                               uint32_t* gram_k, uint32_t* flags, hipStream_t stream,
-                               hipEvent_t* ev);
+                               uint16_t* Blo, uint32_t* gram_k, uint32_t* flags,
+                               hipStream_t stream, hipEvent_t* ev);
 hipError_t launch_gram_loss(const uint16_t* Estack, int64_t N, int64_t K, const uint16_t* B,
                             int n_grid, double* partials, hipStream_t stream);
 
@@ -115,12 +117,14 @@ hipError_t launch_fold(void* prev, int dtype, int64_t rows, int64_t cols, int64_
 // of the correlation operand and d = sqrt(diag H). The diagonal block a of the operand starts
 // at Bd + a * bd_block with rows bd_pitch elements apart ([t][256][256] from the diagonal-only
 // preparation: 65536 and 256; the full [K][K] operand of a Gram-form search: 256 K + 256 and K).
+// Bdl: the low-order parts of the diagonal blocks, [t][256][256] (launch_gram_hmat's Blo).
 // ctrl: nullptr, or the control block of the Gram-form search whose operand is read; when its
 // record of K or of the grid size differs from K and n_grid nothing is written and
 // AWQ_FLAG_NO_GRAM is raised.
 hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, const float* s,
                               const float* d32, const uint16_t* Bd, int64_t bd_block,
-                              int64_t bd_pitch, const SearchCtrl* ctrl, int n_grid, int n_clip,
+                              int64_t bd_pitch, const uint16_t* Bdl, const SearchCtrl* ctrl,
+                              int n_grid, int n_clip,
                               float clip_min, int bits, int group, bool zero_point, float* clip,
                               float* clip_err, uint32_t* flags, hipStream_t stream);
 

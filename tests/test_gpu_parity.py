@@ -670,8 +670,31 @@ def test_full_c5_mlp_layer(awq, c5_x_gram, bits):
 
 # ------------------------------------------------------------------------------------------------
 # Clipping search and clipped packing
-CLIP_ERR_RTOL = 5e-3     # per (ratio, row, group) error: fp16 E' and correlation operand
-CLIP_BAND = 1e-2         # a chosen ratio may differ from the oracle's only inside this band
+# Clipping-search bars, relative to each (row, group)'s largest error over the ratios. The group
+# errors are carried to about 2^-22 (hi and lo fp16 parts of E' and of the correlation operand,
+# fp32 accumulation; measured <= 3e-6): 1e-5. X in fp32 or bf16 enters the Gram operand rounded
+# to fp16 (2^-11 per element moves H itself; measured 1.3e-4): 5e-4.
+CLIP_ERR_RTOL = 1e-5
+CLIP_ERR_RTOL_ROUNDED_X = 5e-4
+CLIP_BAND = 2e-5         # the chosen ratio's oracle error may exceed the best by this (+ the bar)
+
+
+def clip_err_rtol(X):
+    return CLIP_ERR_RTOL if np.asarray(X).dtype == np.float16 else CLIP_ERR_RTOL_ROUNDED_X
+
+
+def _assert_clip(err_g, err_o, ratio_g, grid, tol):
+    """Every error within `tol` of its group's scale; every chosen ratio on the grid and, by the
+    oracle's errors, within the band of the best. Returns (max rel err, chosen grid indices)."""
+    scale = err_o.max(axis=0, keepdims=True)          # per (row, group): the largest ratio error
+    rel = np.abs(err_g - err_o) / np.maximum(scale, 1e-300)
+    assert rel.max() <= tol, f"clip error rel {rel.max():.3e} > {tol}"
+    assert np.isin(ratio_g, grid).all()
+    j_g = np.searchsorted(-grid, -ratio_g)            # grid is decreasing
+    rows, groups = np.indices(ratio_g.shape)
+    chosen = err_o[j_g, rows, groups]
+    assert (chosen <= err_o.min(axis=0) * (1 + CLIP_BAND) + 2 * tol * scale[0]).all()
+    return float(rel.max()), j_g
 
 
 def _oracle_s_best(W, X, bits=4):
@@ -700,20 +723,9 @@ def test_clip_search_parity(awq, name, make, bits, n_clip, clip_min):
     cfg = awq.AwqConfig(bits=bits, n_clip=n_clip, clip_min=clip_min)
     r = awq.clip_search(dev(W), dev(X), dev(s), cfg, with_err=True)
     orc = oracle.clip_search(W, X, s, bits=bits, n_clip=n_clip, clip_min=clip_min)
-    err_g = host(r.err).astype(np.float64)
-    err_o = orc["err"]
-    scale = err_o.max(axis=0, keepdims=True)          # per (row, group): the largest ratio error
-    rel = np.abs(err_g - err_o) / np.maximum(scale, 1e-300)
-    say(f"max err rel {rel.max():.2e} (relative to each group's largest error)")
-    assert rel.max() <= CLIP_ERR_RTOL
-    ratio_g = host(r.clip)
-    grid = oracle.clip_grid(n_clip, clip_min)
-    assert np.isin(ratio_g, grid).all()
-    j_g = np.searchsorted(-grid, -ratio_g)            # grid is decreasing
-    rows, groups = np.indices(ratio_g.shape)
-    chosen = err_o[j_g, rows, groups]
-    best = err_o.min(axis=0)
-    assert (chosen <= best * (1 + CLIP_BAND) + 1e-12 * scale[0]).all()
+    rel, j_g = _assert_clip(host(r.err).astype(np.float64), orc["err"], host(r.clip),
+                            oracle.clip_grid(n_clip, clip_min), clip_err_rtol(X))
+    say(f"max err rel {rel:.2e} (relative to each group's largest error)")
     same = (j_g == orc["best"]).mean()
     say(f"same ratio as the oracle in {100 * same:.2f}% of (row, group)")
     assert int(host(r.flags)[0]) == 0
@@ -721,19 +733,9 @@ def test_clip_search_parity(awq, name, make, bits, n_clip, clip_min):
 
 def _check_clip_against_oracle(r, W, X, s, bits, n_clip, clip_min):
     orc = oracle.clip_search(W, X, s, bits=bits, n_clip=n_clip, clip_min=clip_min)
-    err_g = host(r.err).astype(np.float64)
-    err_o = orc["err"]
-    scale = err_o.max(axis=0, keepdims=True)
-    rel = np.abs(err_g - err_o) / np.maximum(scale, 1e-300)
-    assert rel.max() <= CLIP_ERR_RTOL
-    ratio_g = host(r.clip)
-    grid = oracle.clip_grid(n_clip, clip_min)
-    assert np.isin(ratio_g, grid).all()
-    j_g = np.searchsorted(-grid, -ratio_g)
-    rows, groups = np.indices(ratio_g.shape)
-    chosen = err_o[j_g, rows, groups]
-    assert (chosen <= err_o.min(axis=0) * (1 + CLIP_BAND) + 1e-12 * scale[0]).all()
-    return float(rel.max()), float((j_g == orc["best"]).mean())
+    rel, j_g = _assert_clip(host(r.err).astype(np.float64), orc["err"], host(r.clip),
+                            oracle.clip_grid(n_clip, clip_min), clip_err_rtol(X))
+    return rel, float((j_g == orc["best"]).mean())
 
 
 @pytest.mark.parametrize("name,make,bits,n_clip,clip_min", CLIP_CASES,
@@ -879,7 +881,7 @@ def test_end_to_end_with_clipping(awq):
     agree = host(cr.clip) == oc["ratio"]
     rows = agree.all(axis=1)          # output columns whose every group took the oracle's ratio
     say(f"ratios agree in {100 * agree.mean():.2f}% of groups, {100 * rows.mean():.1f}% of rows")
-    assert agree.mean() >= 0.95 and rows.mean() >= 0.8
+    assert agree.mean() >= 0.99 and rows.mean() >= 0.9
     qw = host(p.qweight).view(np.uint32).reshape(384, 4, 16)
     assert np.array_equal(qw[agree], o["qweight"].reshape(384, 4, 16)[agree])
     ref = oracle.w4a16(A, o["qweight"], o["scales16"], o["s16"])
@@ -1051,16 +1053,9 @@ def test_clip_search_group_and_zero_point(awq, group, zp):
     cfg = awq.AwqConfig(group=group, zero_point=zp)
     r = awq.clip_search(dev(W), dev(X), dev(s), cfg, with_err=True)
     orc = oracle.clip_search(W, X, s, group=group, zero_point=zp)
-    err_g = host(r.err).astype(np.float64)
-    err_o = orc["err"]
-    scale = err_o.max(axis=0, keepdims=True)
-    rel = np.abs(err_g - err_o) / np.maximum(scale, 1e-300)
-    say(f"max err rel {rel.max():.2e}")
-    assert rel.max() <= CLIP_ERR_RTOL
-    grid = oracle.clip_grid(11, 0.5)
-    j_g = np.searchsorted(-grid, -host(r.clip))
-    rows, groups = np.indices(j_g.shape)
-    assert (err_o[j_g, rows, groups] <= err_o.min(axis=0) * (1 + CLIP_BAND) + 1e-12 * scale[0]).all()
+    rel, j_g = _assert_clip(host(r.err).astype(np.float64), orc["err"], host(r.clip),
+                            oracle.clip_grid(11, 0.5), clip_err_rtol(X))
+    say(f"max err rel {rel:.2e}")
     say(f"same ratio as the oracle in {100 * (j_g == orc['best']).mean():.2f}% of (row, group)")
 
 
@@ -1077,16 +1072,9 @@ def test_clip_search_gram_group_and_zero_point(awq, group, zp):
     res = awq.search_layer(Wt, Xt, sx, cfg, flags=flags, workspace=ws)
     r = awq.clip_search_gram(Wt, res.s_best, ws, cfg, with_err=True, flags=flags)
     orc = oracle.clip_search(W, X, host(res.s_best), group=group, zero_point=zp)
-    err_g = host(r.err).astype(np.float64)
-    err_o = orc["err"]
-    scale = err_o.max(axis=0, keepdims=True)
-    rel = np.abs(err_g - err_o) / np.maximum(scale, 1e-300)
-    say(f"max err rel {rel.max():.2e}")
-    assert rel.max() <= CLIP_ERR_RTOL
-    grid = oracle.clip_grid(11, 0.5)
-    j_g = np.searchsorted(-grid, -host(r.clip))
-    rows, groups = np.indices(j_g.shape)
-    assert (err_o[j_g, rows, groups] <= err_o.min(axis=0) * (1 + CLIP_BAND) + 1e-12 * scale[0]).all()
+    rel, _ = _assert_clip(host(r.err).astype(np.float64), orc["err"], host(r.clip),
+                          oracle.clip_grid(11, 0.5), clip_err_rtol(X))
+    say(f"max err rel {rel:.2e}")
     assert int(host(flags)[0]) == 0
 
 
@@ -1169,7 +1157,7 @@ def test_end_to_end_group64_zero_point(awq):
     agree = host(cr.clip) == oc["ratio"]
     rows = agree.all(axis=1)          # output columns whose every group took the oracle's ratio
     say(f"ratios agree in {100 * agree.mean():.2f}% of groups, {100 * rows.mean():.1f}% of rows")
-    assert agree.mean() >= 0.95 and rows.mean() >= 0.8
+    assert agree.mean() >= 0.99 and rows.mean() >= 0.9
     ref = oracle.w4a16(A, o["qweight"], o["scales16"], o["s16"], group=64, zeros=o["zeros"])
     rep = oracle.accuracy_report(host(Y)[:, rows], ref[:, rows])
     say(rep)
