@@ -81,7 +81,7 @@ def parse():
                     help="repetitions of each other layer shape's search (0: skip them)")
     ap.add_argument("--counters", default=None,
                     help="record mode: directory holding one rocprofv3 CSV directory per pass")
-    ap.add_argument("--mode", choices=("bench", "traffic", "record"), default="bench",
+    ap.add_argument("--mode", choices=("bench", "traffic", "record", "ceilings"), default="bench",
                     help="traffic: one 1 GiB device copy (counter calibration) and one pass of "
                          "the path in each form, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
     return ap.parse_args()
@@ -180,6 +180,45 @@ def traffic_pass():
         awq.w4a16_gemm(A, qw, sc, s16)
         torch.cuda.synchronize()
     log("w4a16 calls done")
+
+
+def ceiling_pass(sizes=(1 << 30, M_ * K_ * 2, N_GRID * N_ * K_ * 2), reps=20, echo=True):
+    """Reference rates of plain streams on this GPU, with torch's own elementwise and reduction
+    kernels over fp16 buffers, HIP events on the current stream: a write-only fill, a copy, and a
+    read-only reduction, by default at 1 GiB and at the sizes of the path's bandwidth-bound
+    kernels (the 65536 x 4096 fp16 activations, 537 MB; the 20 x 4096 x 4096 fp16 error stack,
+    671 MB)."""
+    import torch
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream()
+    out = []
+    for nbytes in sizes:
+        src = torch.ones(nbytes // 2, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        acc = torch.empty((), dtype=torch.float32, device=dev)
+        ops = {"write (fill_)": (lambda: dst.fill_(2.0), nbytes),
+               "copy (copy_)": (lambda: dst.copy_(src), 2 * nbytes),
+               "read (sum to fp32)": (lambda: torch.sum(src, dim=0, dtype=torch.float32, out=acc),
+                                         nbytes)}
+        for name, (fn, moved) in ops.items():
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(reps):
+                fn()
+            e1.record(st)
+            e1.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            rec = {"op": name, "bytes": nbytes, "moved": moved, "us": round(us, 1),
+                   "gbs": round(moved / us / 1e3, 1),
+                   "hbm_frac": round(moved / us / 1e3 / HBM_PEAK_GBS, 4)}
+            if echo:
+                print(json.dumps(rec), flush=True)
+            out.append(rec)
+        del src, dst
+        torch.cuda.empty_cache()
+    return out
 
 
 # (n, k, m) of the W4A16 calls of the counter pass
@@ -572,6 +611,9 @@ def main():
     if args.mode == "record":
         record_counters(args.counters)
         return
+    if args.mode == "ceilings":
+        ceiling_pass()
+        return
     if args.mode == "traffic":
         traffic_pass()
         return
@@ -692,6 +734,25 @@ def main():
     for v in other.values():
         v["gbs"] = round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)
         v["hbm_frac"] = round(v["gbs"] / HBM_PEAK_GBS, 4)
+    # the stream rates this GPU reaches with torch's own fill and copy kernels at these sizes:
+    # read-dominated stages against the copy, the write-dominated error stack against the fill
+    rates = {(r["op"].split()[0], r["bytes"]): r["gbs"]
+             for r in ceiling_pass(sizes=(M_ * K_ * 2, N_GRID * N_ * K_ * 2), reps=10, echo=False)}
+    ceil_of = {"act_stats_standalone": ("copy", M_ * K_ * 2),
+               "act_stats_in_search": ("copy", M_ * K_ * 2),
+               "x_transpose_and_stats": ("copy", M_ * K_ * 2),
+               "quantize_stack": ("write", N_GRID * N_ * K_ * 2)}
+    for k, v in other.items():
+        if k in ceil_of:
+            op, nb = ceil_of[k]
+            v["stream_ceiling"] = {"op": "torch " + ("fill_" if op == "write" else "copy_"),
+                                   "bytes": nb, "gbs": rates[(op, nb)]}
+            v["vs_ceiling"] = round(v["gbs"] / rates[(op, nb)], 4)
+    # quantize_stack is bound by its vector ALU work (the quantizer at 20 grid points per weight:
+    # about 13 VALU instructions per element, the VALU busy for ~92% of the kernel in the counter
+    # record); pack moves 42 MB in a single short launch
+    other["quantize_stack"]["bound"] = "alu"
+    other["pack"]["bound"] = "launch"
 
     # clipping search at s* (a further optimisation of the method, reported beside the step)
     clip_rec = None
