@@ -131,7 +131,7 @@ hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, co
 // ---- W4A16 ----
 // one activation row (M = 1): fp16 dot products against the block-scaled A / s table; K up to
 // kW4a16GemvMaxK; dynamic LDS of w4a16_gemv_lds_bytes(1, K) bytes (the launcher passes it)
-constexpr int64_t kW4a16GemvMaxK = 8192;
+constexpr int64_t kW4a16GemvMaxK = 32768;
 size_t w4a16_gemv_lds_bytes(int MB, int64_t K);
 hipError_t launch_w4a16_gemv(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
                              const uint32_t* qweight, const uint16_t* scales16,

@@ -12,9 +12,10 @@
 //     or fp16 A/s cannot hold);
 //   * the activation and s loads are issued first, the code loads right after them, so the
 //     table is built while the codes stream in;
-//   * a wave owns 4 weight rows and all of K; lane l takes the 32-channel chunks l, l + 64, ... of
-//     each row (16 bytes of codes per row and chunk); a chunk of a'' read from LDS serves four
-//     rows;
+//   * a workgroup of 8 waves owns 16 weight rows, a wave 2 rows and all of K (more waves per CU
+//     to hide the latency of their loads: 4 waves of 4 rows were 12-15% slower, 16 waves of one
+//     row slower still); lane l takes the 32-channel chunks l, l + 64, ... of each row (16 bytes
+//     of codes per row and chunk); a chunk of a'' read from LDS serves both rows;
 //   * decoding: x = w ^ 0x88888888 turns each two's-complement nibble into u = q + 8 (zero-point
 //     codes are unsigned already, u = q); (x >> 4j) & 0x000F000F | 0x64006400 is the fp16 pair
 //     (1024 + u_j, 1024 + u_{j+4}), and one packed subtract of 1024 + zc (zc = 8, or z) gives
@@ -23,8 +24,8 @@
 //     chunk's sum afterwards would save the subtract but lose everything else in the block to
 //     the rounding of one huge term: a dead channel's a'' next to q = 0.) The chunk's sum times
 //     step 2^e goes into the row's partial;
-//   * the four rows' partials are summed over the wave's 64 lanes by a transposing butterfly
-//     (each exchange halves the values a lane holds), in a fixed order.
+//   * the two rows' partials are summed over the wave's 64 lanes by a transposing butterfly
+//     (the first exchange halves the values a lane holds), in a fixed order.
 // Rounding: a'' one fp16 rounding (of the fp32 a' = A rcp(s)); products exact, sums fp32; Y
 // rounded once to fp16.
 #include "device_common.h"
@@ -33,8 +34,9 @@
 namespace awq {
 
 namespace {
-constexpr int kGvRows = 4;     // weight rows per wave
-constexpr int kGvWaves = 4;    // waves per workgroup
+constexpr int kGvRows = 2;     // weight rows per wave
+constexpr int kGvWaves = 8;    // waves per workgroup
+constexpr int kGvThreads = 64 * kGvWaves;
 constexpr int kGvPos = 2;      // chunk positions per lane whose loads are in flight together
 constexpr int kChunkBytes = 80;   // LDS bytes per 32-channel chunk: 64 of a'', 16 of padding
 }  // namespace
@@ -46,11 +48,11 @@ size_t w4a16_gemv_lds_bytes(int MB, int64_t K) {
 
 // ONE: every chunk position of a lane fits one load batch (K <= 64 * 32 * kGvPos = 4096), so
 // there is one set of load registers and no loop. TI: table entries of 8 channels per thread
-// (K <= 2048 TI); all their loads are unconditional, issued before the code loads, and only the
+// (K <= 4096 TI); all their loads are unconditional, issued before the code loads, and only the
 // LDS stores are conditional -- a load inside a conditional block would be issued there, after
 // the code loads, and waiting for it would wait for all of them.
 template <int GS, bool ZP, bool HAS_S, bool ONE, int TI>
-__global__ __launch_bounds__(256) void w4a16_gemv_kernel(
+__global__ __launch_bounds__(kGvThreads) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ A, int64_t N, int64_t K, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales16, const uint8_t* __restrict__ zeros,
     const uint16_t* __restrict__ s16, uint16_t* __restrict__ Y) {
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(
   const int nq8 = (int)(K / 8);
 #pragma unroll
   for (int it = 0; it < TI; ++it) {
-    const int q8 = tid + 256 * it;
+    const int q8 = tid + kGvThreads * it;
     const int qc = q8 < nq8 ? q8 : 0;
     araw[it] = *reinterpret_cast<const uint4*>(A + (int64_t)qc * 8);
     sraw[it] = HAS_S ? *reinterpret_cast<const uint4*>(s16 + (int64_t)qc * 8)
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(
   // ---- 3. the a'' table: 16 consecutive threads hold one 128-channel block ------------------
 #pragma unroll
   for (int it = 0; it < TI; ++it) {
-    const int q8 = tid + 256 * it;
+    const int q8 = tid + kGvThreads * it;
     {
       const uint32_t aw[4] = {araw[it].x, araw[it].y, araw[it].z, araw[it].w};
       const uint32_t sw[4] = {sraw[it].x, sraw[it].y, sraw[it].z, sraw[it].w};
@@ -204,22 +206,25 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(
     }
   }
 
-  // ---- sums over the 64 lanes: rows 0,1 go to lanes with bit 5 clear, 2,3 to the others;
-  // then bit 4 splits each pair; the remaining 16 lanes add up in four steps ------------------
-  const bool b5 = (lane & 32) != 0, b4 = (lane & 16) != 0;
-  const float give0 = b5 ? part[0] : part[2], give1 = b5 ? part[1] : part[3];
-  float k0 = b5 ? part[2] : part[0], k1 = b5 ? part[3] : part[1];
-  k0 += __shfl_xor(give0, 32);
-  k1 += __shfl_xor(give1, 32);
-  const float give = b4 ? k0 : k1;
-  float kk = b4 ? k1 : k0;
-  kk += __shfl_xor(give, 16);
+  // ---- sums over the 64 lanes (two rows: row 0 goes to the lanes with bit 5 clear, row 1 to
+  // the others, then 32 lanes add up in five steps; one row: six steps) --------------------
+  static_assert(kGvRows == 1 || kGvRows == 2, "one or two rows per wave");
+  const bool b5 = (lane & 32) != 0;
+  float kk;
+  if constexpr (kGvRows == 2) {
+    const float give = b5 ? part[0] : part[kGvRows - 1];
+    kk = b5 ? part[kGvRows - 1] : part[0];
+    kk += __shfl_xor(give, 32);
+  } else {
+    kk = part[0] + __shfl_xor(part[0], 32);
+  }
+  kk += __shfl_xor(kk, 16);
   kk += __shfl_xor(kk, 8);
   kk += __shfl_xor(kk, 4);
   kk += __shfl_xor(kk, 2);
   kk += __shfl_xor(kk, 1);
-  const int row = (b5 ? 2 : 0) + (b4 ? 1 : 0);
-  if ((lane & 15) == 0 && n0 + row < N) Y[n0 + row] = f2h(kk);
+  const int row = (kGvRows == 2 && b5) ? 1 : 0;
+  if ((lane & (kGvRows == 2 ? 31 : 63)) == 0 && n0 + row < N) Y[n0 + row] = f2h(kk);
 }
 
 hipError_t launch_w4a16_gemv(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
@@ -229,15 +234,17 @@ hipError_t launch_w4a16_gemv(const uint16_t* A, int64_t M, int64_t N, int64_t K,
   if (M != 1 || K > kW4a16GemvMaxK) return hipErrorInvalidValue;
   const unsigned blocks = (unsigned)((N + kGvRows * kGvWaves - 1) / (kGvRows * kGvWaves));
   const size_t lds = w4a16_gemv_lds_bytes(1, K);
-  const bool one = K <= 64 * 32 * kGvPos;   // K <= 4096: table entries of 2 passes at most
+  const bool one = K <= 64 * 32 * kGvPos;   // K <= 4096: one table entry per thread, one batch
 #define AWQ_GV1(GS_, ZP_, HS_, ONE_, TI_)                                                        \
-  w4a16_gemv_kernel<GS_, ZP_, HS_, ONE_, TI_><<<blocks, 256, lds, stream>>>(                     \
+  w4a16_gemv_kernel<GS_, ZP_, HS_, ONE_, TI_><<<blocks, kGvThreads, lds, stream>>>(              \
       A, N, K, qweight, scales16, zeros, s16, Y)
 #define AWQ_GV(GS_, ZP_, HS_)                                                                    \
   do {                                                                                           \
-    if (K <= 2048) AWQ_GV1(GS_, ZP_, HS_, true, 1);                                             \
-    else if (one) AWQ_GV1(GS_, ZP_, HS_, true, 2);                                              \
-    else AWQ_GV1(GS_, ZP_, HS_, false, 4);                                                      \
+    if (one) AWQ_GV1(GS_, ZP_, HS_, true, 1);                                                   \
+    else if (K <= 8 * kGvThreads) AWQ_GV1(GS_, ZP_, HS_, false, 1);                             \
+    else if (K <= 16 * kGvThreads) AWQ_GV1(GS_, ZP_, HS_, false, 2);                            \
+    else if (K <= 32 * kGvThreads) AWQ_GV1(GS_, ZP_, HS_, false, 4);                            \
+    else AWQ_GV1(GS_, ZP_, HS_, false, 8);                                                      \
   } while (0)
 #define AWQ_GV_S(GS_, ZP_) \
   do { if (s16) AWQ_GV(GS_, ZP_, true); else AWQ_GV(GS_, ZP_, false); } while (0)

@@ -356,6 +356,7 @@ def _w4a16_case(n, k, m, seed):
 W4A16_CASES = [(384, 512, m) for m in (1, 3, 16, 17, 64, 100)] + \
               [(4096, 4096, m) for m in (1, 4, 16, 64, 512)] + \
               [(11008, 4096, m) for m in (1, 4, 16, 64, 512)] + [(4096, 11008, 16)] + \
+              [(4096, 11008, 1), (1024, 28672, 1), (130, 32768, 1)] + \
               [(1024, 8192, 1), (256, 12288, 2)] + \
               [(8192, 4096, 49), (8192, 4096, 48)]   # tiled from 49 rows on tall weights
 
