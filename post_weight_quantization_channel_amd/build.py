@@ -12,6 +12,11 @@ post_weight_quantization_channel_amd/libawq.so. Arithmetic flags:
   -Xclang -target-feature -Xclang -packed-fp32-ops
                                         no packed fp32 (v_pk_*_f32) instructions
 Denormals are left enabled (no -fgpu-flush-denormals-to-zero), no fast-math.
+Per-source additions (FILE_FLAGS):
+  w4a16.hip: -mllvm -amdgpu-mfma-vgpr-form
+                                        MFMA results in VGPRs: the tiled kernel scales every
+                                        group's partial sums with vector instructions, which would
+                                        otherwise first copy them out of AGPRs
 """
 from __future__ import annotations
 
@@ -37,6 +42,10 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 
+FILE_FLAGS = {
+    "w4a16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -47,7 +56,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 target feature and says so; drop that line
     err = "\n".join(ln for ln in r.stderr.splitlines()

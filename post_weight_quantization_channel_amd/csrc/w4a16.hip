@@ -20,33 +20,32 @@ namespace awq {
 
 // ---------------------------------------------------------------------------------------------
 // Larger batches: a tiled MFMA GEMM. Workgroup tile 128 (batch rows m) x 64 (weight rows n), one
-// 128-channel block of K per step, 4 waves of 64 x 32 (2 x 2), each a 4 x 2 grid of
+// 128-channel block of K per step, 4 waves of 64 x 32 (2 x 2), each a grid of 4 (m) x 2 (n)
 // v_mfma_f32_16x16x32_f16 blocks (weights as the A operand, activations as B).
 //
-// Every main-loop load is moved into LDS by the buffer unit (buffer_load ... lds), so that no
-// load's result goes through a register and the compiler places no wait on them: the kernel
-// orders LDS against these loads itself, with vmcnt waits and barriers. Per K step the workgroup
-// moves the activation tile (128 rows x 256 B, 8 loads of 1 KiB per wave, written in the swizzled
-// layout the fragment reads expect: lane i of a load fills physical chunk i % 16 of its row, so it
-// fetches the logical chunk (i % 16) ^ (row & 15)) and the raw codes of its 64 weight rows
-// (64 x 64 B, one load per wave). The steps (and zero points) of the 64 rows for all K, r_k for
-// all K and 2^-b per block are tables in LDS filled once. Step g:
-//   wait for step g's loads; barrier; issue step g + 1's loads into the other stage (its last
-//   reader, step g - 1, is behind the barrier); unpack step g's codes into fp16(c(q) r_k) in the
-//   swizzled layout; barrier; the MFMAs of step g into a fresh fp32 partial per group, added to
-//   the accumulators times step 2^-b of each row.
-// Rows past M or N read as zeros (the buffer ranges end at the last valid row) and their outputs
-// are not stored.
+// The activation tile of a step (128 rows x 256 B, 8 loads of 1 KiB per wave) is moved into LDS
+// by the buffer unit (buffer_load ... lds), so that no load's result goes through a register and
+// the compiler places no wait on it: the kernel orders LDS against these loads itself, with
+// vmcnt waits and barriers. It lands in the swizzled layout the fragment reads expect: lane i of
+// a load fills physical chunk i % 16 of its row, so it fetches the logical chunk
+// (i % 16) ^ (row & 15). Each wave loads the packed codes of its 32 weight rows into registers
+// and turns them into the MFMA operand itself: there is no unpacked weight tile in LDS, and one
+// barrier per step. The two waves of an n-half both unpack its rows. The steps (and zero points)
+// of the 64 rows for all K, r_k for all K and 2^-b per block are tables in LDS filled once.
+// Step g: wait for step g's loads; barrier (everyone's have landed, and the other stage's last
+// reader, step g - 1, is done); issue step g + 1's loads into the other stage; the MFMAs of step
+// g into a fresh fp32 partial per group, added to the accumulators times step 2^-b of each row.
+// (A third stage, two steps ahead, was no faster; with the codes staged in LDS too, one workgroup
+// per CU fit instead of two, and 11008 rows at M = 512 took 106 instead of 89 us.)
+// Rows past M read as zeros (the buffer range ends at the last valid row), rows past N read row
+// N - 1, and neither's outputs are stored.
 namespace {
 constexpr int TBM = 128, TBN = 64, TBK = 128;
 __device__ __forceinline__ int tswz(int row, int chunk) {   // byte offset inside a 256-byte row
   return row * (TBK * 2) + ((chunk ^ (row & 15)) << 4);
 }
-constexpr int kRawStage = TBN * 64;                   // 4 KiB of packed codes per step
 constexpr int kAStage = TBM * TBK * 2;                // 32 KiB of activations per step
-constexpr int kWStage = TBN * TBK * 2;                // 16 KiB of unpacked weights per step
-// two stages each of activations, codes and unpacked weights: 104 KiB
-constexpr int kDmaSmem = 2 * (kAStage + kRawStage + kWStage);
+constexpr int kRwSmem = 2 * kAStage;                  // two stages: 64 KiB
 // s_waitcnt immediate: at most n vector-memory loads outstanding (gfx9 encoding: vmcnt in bits
 // [3:0] and [15:14]; expcnt and lgkmcnt left at their maxima)
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
@@ -54,19 +53,26 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 
 // bytes of the dynamic tables: fp16 r [K], fp32 2^-b [K/128], fp16 steps [K/GS][64], (ZP) uint8
 // zeros [K/GS][64]
-__host__ __device__ constexpr int64_t w4a16_dma_tables(int64_t K, int GS, bool ZP) {
+__host__ __device__ constexpr int64_t w4a16_tiled_tables(int64_t K, int GS, bool ZP) {
   return K * 2 + (K / 128) * 4 + (int64_t)TBN * (K / GS) * 2 + (ZP ? (int64_t)TBN * (K / GS) : 0);
 }
 
+// Which channels a lane holds: with G = 128 lane group lg takes words 4 lg .. 4 lg + 3 of a row's
+// 16 words per step and MFMA kk its word 4 lg + kk, i.e. channels 32 lg + 8 kk ..; with G = 64
+// MFMA kk takes word 4 kk + lg (channels 32 kk + 8 lg ..), so MFMAs 0, 1 cover the step's first
+// group and 2, 3 the second. The activation fragment of a lane holds the same 8 channels, in
+// natural order: a code word is decoded in pairs (2j, 2j + 1), byte j of the word spread to bytes
+// 0 and 2 (v_perm), then (t & 0x00F0000F) | 0x64006400 is the fp16 pair (1024 + u_2j,
+// 1024 + 16 u_2j+1) and one packed fma with (1, 1/16) and -(1032, 72) (or -(1024 + z, 64 + z))
+// gives (c(q_2j), c(q_2j+1)) exactly; times the r pair, rounded once.
+
 template <int GS, bool ZP, bool HAS_S>
-__global__ __launch_bounds__(256) void w4a16_tiled_dma_kernel(
+__global__ __launch_bounds__(256) void w4a16_tiled_kernel(
     const uint16_t* __restrict__ A, int64_t M, int64_t N, int64_t K,
     const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales16,
     const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ s16,
     uint16_t* __restrict__ Y) {
-  __shared__ __attribute__((aligned(1024))) char smem[kDmaSmem];
-  // LDS: activation stages [2][32 KiB], unpacked weight stages [2][16 KiB], code stages [2][4 KiB]
-  constexpr int kWBase = 2 * kAStage, kRawBase = 2 * kAStage + 2 * kWStage;
+  __shared__ __attribute__((aligned(1024))) char smem[kRwSmem];
   extern __shared__ __attribute__((aligned(16))) char dyn[];
   const int64_t ngr = K / GS;
   uint16_t* rtab = reinterpret_cast<uint16_t*>(dyn);                      // [K]
@@ -78,18 +84,15 @@ __global__ __launch_bounds__(256) void w4a16_tiled_dma_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 15, lg = lane >> 4;
   const int64_t tilesN = (N + TBN - 1) / TBN;
-  // Workgroup b runs on XCD b % 8: when the grid divides by 8, XCD x takes the x-th contiguous
-  // eighth of the row-major tile order, so the tiles in one XCD's L2 share activation rows.
   int64_t bl = blockIdx.x;
   if ((gridDim.x & 7u) == 0) bl = (int64_t)(blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   const int64_t m0 = (bl / tilesN) * TBM;
   const int64_t n0 = (bl % tilesN) * TBN;
   const int64_t groups = K / 128;
 
-  // ---- tables (plain loads: the compiler's waits here cost nothing). r_k = fp16(2^b / s_k):
-  // the 16 chunks of a 128-channel block are 16 consecutive threads (one DPP row; K / 8 is a
-  // multiple of 16, so a row is all inside or all past the loop) ---------------------------
+  // ---- tables: r_k = fp16(2^b / s_k) in natural order, 2^-b per block, steps, zero points ----
   for (int64_t k8 = tid; k8 < K / 8; k8 += 256) {
     float inv[8];
     float mx = 0.0f;
@@ -121,23 +124,16 @@ __global__ __launch_bounds__(256) void w4a16_tiled_dma_kernel(
     if (ZP) z_lds[e] = zeros[row * ngr + gq];
   }
 
-  // ---- buffer loads into LDS ----------------------------------------------------------------
+  // ---- activation stages ---------------------------------------------------------------------
   const int64_t arows = (M - m0 < TBM) ? M - m0 : TBM;
-  const int64_t wrows = (N - n0 < TBN) ? N - n0 : TBN;
   const rsrc_t ra = make_rsrc(A + m0 * K, (uint32_t)(arows * K * 2));
-  const rsrc_t rw = make_rsrc(qweight + n0 * (K / 8), (uint32_t)(wrows * (K / 2)));
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
-  // activation load j of this wave: tile rows 32 wave + 4 j + lane / 16; the lane's logical
-  // chunk depends on the row mod 16, i.e. on j mod 4 -- four per-lane offsets
   uint32_t avoff[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const int rl = 4 * jj + (lane >> 4);
     avoff[jj] = (uint32_t)((lane >> 4) * K * 2) + (uint32_t)((((lane & 15) ^ (rl & 15))) << 4);
   }
-  // raw codes: this wave's load covers weight rows 16 wave + lane / 4, bytes 16 (lane % 4) of the
-  // step's 64
-  const uint32_t wvoff = (uint32_t)((lane >> 2) * (K / 2)) + (uint32_t)((lane & 3) * 16);
   auto issue = [&](int64_t g, int st) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -145,44 +141,27 @@ __global__ __launch_bounds__(256) void w4a16_tiled_dma_kernel(
       const uint32_t so = (uint32_t)((32 * wave + 4 * j) * K * 2) + (uint32_t)(g * 256);
       buffer_load16_lds_so(ra, lds, avoff[j & 3], so);
     }
-    const uint32_t lds = lds0 + (uint32_t)(kRawBase + st * kRawStage) + (uint32_t)(wave * 1024);
-    const uint32_t so = (uint32_t)(16 * wave * (K / 2)) + (uint32_t)(g * 64);
-    buffer_load16_lds_so(rw, lds, wvoff, so);
   };
-
-  // ---- unpack: thread t owns weight row t / 4, channels 32 (t % 4) .. + 31 of the step -------
-  const int wrow_l = tid >> 2, wq = tid & 3;
-  auto unpack = [&](int64_t g, int st) {
-    const char* raw = smem + kRawBase + st * kRawStage;
-    char* sw = smem + kWBase + (int)(g & 1) * kWStage;
-    const uint4 wv = *reinterpret_cast<const uint4*>(raw + wrow_l * 64 + wq * 16);
-    const int64_t gq = (GS == 64) ? 2 * g + (wq >> 1) : g;
-    const _Float16 subh = ZP ? (_Float16)(1024.0f + (float)z_lds[gq * TBN + wrow_l])
-                             : (_Float16)1032.0f;
-    const half2_t sub2 = half2_t{subh, subh};
-    const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
+  // this wave's code rows
+  const uint32_t* wr[2];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const uint4 iv = *reinterpret_cast<const uint4*>(rtab + g * 128 + wq * 32 + v * 8);
-      // r pairs (j, j + 4) to match the unpack order
-      const uint32_t i04 = __builtin_amdgcn_perm(iv.z, iv.x, 0x05040100u);
-      const uint32_t i15 = __builtin_amdgcn_perm(iv.z, iv.x, 0x07060302u);
-      const uint32_t i26 = __builtin_amdgcn_perm(iv.w, iv.y, 0x05040100u);
-      const uint32_t i37 = __builtin_amdgcn_perm(iv.w, iv.y, 0x07060302u);
-      const uint32_t rp[4] = {i04, i15, i26, i37};
-      const uint32_t x = ZP ? words[v] : (words[v] ^ 0x88888888u);
-      uint32_t pr[4];
+  for (int nb = 0; nb < 2; ++nb) {
+    const int64_t n = n0 + 32 * wn + 16 * nb + li;
+    wr[nb] = qweight + (n < N ? n : N - 1) * (K / 8);
+  }
+  struct Codes {
+    uint32_t w[2][4];   // [nb][kk]: the word MFMA kk of the step takes
+  };
+  auto load_codes = [&](int64_t g, Codes& c) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t bits = ((x >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-        const half2_t q = __builtin_bit_cast(half2_t, bits) - sub2;
-        pr[j] = __builtin_bit_cast(uint32_t, q * __builtin_bit_cast(half2_t, rp[j]));
+    for (int nb = 0; nb < 2; ++nb) {
+      if (GS == 128) {
+        const uint4 v = *reinterpret_cast<const uint4*>(wr[nb] + g * 16 + 4 * lg);
+        c.w[nb][0] = v.x; c.w[nb][1] = v.y; c.w[nb][2] = v.z; c.w[nb][3] = v.w;
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) c.w[nb][kk] = wr[nb][g * 16 + 4 * kk + lg];
       }
-      const uint32_t n01 = __builtin_amdgcn_perm(pr[1], pr[0], 0x05040100u);
-      const uint32_t n23 = __builtin_amdgcn_perm(pr[3], pr[2], 0x05040100u);
-      const uint32_t n45 = __builtin_amdgcn_perm(pr[1], pr[0], 0x07060302u);
-      const uint32_t n67 = __builtin_amdgcn_perm(pr[3], pr[2], 0x07060302u);
-      *reinterpret_cast<uint4*>(sw + tswz(wrow_l, wq * 4 + v)) = make_uint4(n01, n23, n45, n67);
     }
   };
 
@@ -191,16 +170,25 @@ __global__ __launch_bounds__(256) void w4a16_tiled_dma_kernel(
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const int li = lane & 15, lg = lane >> 4;
-  // per group: MFMAs into a fresh partial, then acc += partial * step 2^-b of each weight row
-  // (rows wn 32 + 16 i + 4 lg + r of this lane: four consecutive entries of the step table)
   constexpr int kKKPerGroup = (GS == 64) ? 2 : 4;
-  auto compute = [&](int64_t g, int st) {
+  // the fp16 exponent bits of the decode, held in a register so that the mask-and-insert is one
+  // v_and_or_b32 (a VALU instruction reads one scalar or literal operand)
+  uint32_t magic = 0x64006400u;
+  asm volatile("" : "+v"(magic));
+  auto compute = [&](int64_t g, int st, const Codes& c) {
     const char* sa = smem + st * kAStage;
-    const char* sw = smem + kWBase + (int)(g & 1) * kWStage;
     const float bs = bfac[g];
 #pragma unroll
     for (int h = 0; h < 4 / kKKPerGroup; ++h) {
+      const int64_t gq = (GS == 64) ? 2 * g + h : g;
+      half2_t sub2[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        // subtrahends of the decoded pair (1024 + u, 64 + u'): 1032 and 72 for signed codes
+        // (biased by the xor), 1024 + z and 64 + z with zero points
+        const float z = ZP ? (float)z_lds[gq * TBN + 32 * wn + 16 * nb + li] : 8.0f;
+        sub2[nb] = half2_t{(_Float16)(1024.0f + z), (_Float16)(64.0f + z)};
+      }
       floatx4 part[2][4];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -208,49 +196,71 @@ __global__ __launch_bounds__(256) void w4a16_tiled_dma_kernel(
         for (int j = 0; j < 4; ++j) part[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = h * kKKPerGroup; kk < (h + 1) * kKKPerGroup; ++kk) {
-        const int chunk = kk * 4 + lg;         // this lane's 8 channels of the 32-wide slice
+        const int ch = (GS == 128) ? 4 * lg + kk : 4 * kk + lg;   // the lane's 8-channel chunk
+        const uint4 rv = *reinterpret_cast<const uint4*>(rtab + g * 128 + ch * 8);
+        const uint32_t rp[4] = {rv.x, rv.y, rv.z, rv.w};
         half8_t wf[2], af[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          wf[i] = *reinterpret_cast<const half8_t*>(sw + tswz(wn * 32 + i * 16 + li, chunk));
+        for (int nb = 0; nb < 2; ++nb) {
+          const uint32_t x = ZP ? c.w[nb][kk] : (c.w[nb][kk] ^ 0x88888888u);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          af[j] = *reinterpret_cast<const half8_t*>(sa + tswz(wm * 64 + j * 16 + li, chunk));
+          for (int j = 0; j < 4; ++j) {
+            // byte j (channels 2j, 2j + 1) to bytes 0 and 2
+            const uint32_t t =
+                __builtin_amdgcn_perm(x, x, 0x0C000C00u | (uint32_t)j | ((uint32_t)j << 16));
+            const uint32_t bits = (t & 0x00F0000Fu) | magic;
+            const half2_t q = __builtin_elementwise_fma(
+                __builtin_bit_cast(half2_t, bits), half2_t{(_Float16)1.0f, (_Float16)0.0625f},
+                -sub2[nb]);
+            const half2_t wv = q * __builtin_bit_cast(half2_t, rp[j]);
+            wf[nb][2 * j] = wv[0];
+            wf[nb][2 * j + 1] = wv[1];
+          }
+        }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int mb = 0; mb < 4; ++mb)
+          af[mb] = *reinterpret_cast<const half8_t*>(sa + tswz(wm * 64 + mb * 16 + li, ch));
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[i], af[j], part[i][j], 0, 0, 0);
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+            part[nb][mb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[nb], af[mb], part[nb][mb], 0, 0, 0);
       }
-      const int64_t gq = (GS == 64) ? 2 * g + h : g;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint2 sr = *reinterpret_cast<const uint2*>(st_lds + gq * TBN + wn * 32 + i * 16 +
+      for (int nb = 0; nb < 2; ++nb) {
+        const uint2 sr = *reinterpret_cast<const uint2*>(st_lds + gq * TBN + wn * 32 + nb * 16 +
                                                          4 * lg);
         const float sc[4] = {h2f((uint16_t)(sr.x & 0xFFFFu)) * bs, h2f((uint16_t)(sr.x >> 16)) * bs,
                              h2f((uint16_t)(sr.y & 0xFFFFu)) * bs, h2f((uint16_t)(sr.y >> 16)) * bs};
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(part[i][j][r], sc[r], acc[i][j][r]);
+          for (int r = 0; r < 4; ++r)
+            acc[nb][mb][r] = __builtin_fmaf(part[nb][mb][r], sc[r], acc[nb][mb][r]);
       }
     }
   };
 
-  // ---- main loop: 9 loads per wave per step, issued one step ahead -------------------------
+  // ---- main loop: step g + 1 in flight while step g computes; two sets of code registers take
+  // turns (the loop unrolled by two, so that their indices are static) ------------------------
+  Codes cb[2];
   issue(0, 0);
-  for (int64_t g = 0; g < groups; ++g) {
-    const int st = (int)(g & 1);
+  load_codes(0, cb[0]);
+  auto step = [&](int64_t g, int st, const Codes& cur, Codes& nxt) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));    // this wave's loads of step g have landed
-    __syncthreads();                              // everyone's; and step g - 1 is read
-    if (g + 1 < groups) issue(g + 1, st ^ 1);
-    unpack(g, st);
-    __syncthreads();
-    compute(g, st);
+    __syncthreads();                              // everyone's; and stage st ^ 1 is read
+    if (g + 1 < groups) {
+      issue(g + 1, st ^ 1);
+      load_codes(g + 1, nxt);
+    }
+    compute(g, st, cur);
+  };
+  for (int64_t g = 0; g < groups; g += 2) {
+    step(g, 0, cb[0], cb[1]);
+    if (g + 1 < groups) step(g + 1, 1, cb[1], cb[0]);
   }
 
-  // D layout of the 16x16 MFMA: lane holds D[4 (lane / 16) + r][lane % 16] -> weight rows
-  // 4 lg + r of block i, batch row li of block j.
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -277,12 +287,12 @@ static hipError_t w4a16_tiled(const uint16_t* A, int64_t M, int64_t N, int64_t K
                               const uint8_t* zeros, const uint16_t* s16, uint16_t* Y,
                               hipStream_t stream) {
   const int64_t tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
-  const size_t dyn = (size_t)w4a16_dma_tables(K, GS, ZP);
+  const size_t dyn = (size_t)w4a16_tiled_tables(K, GS, ZP);
   if (s16)
-    w4a16_tiled_dma_kernel<GS, ZP, true><<<(unsigned)tiles, 256, dyn, stream>>>(
+    w4a16_tiled_kernel<GS, ZP, true><<<(unsigned)tiles, 256, dyn, stream>>>(
         A, M, N, K, qweight, scales16, zeros, s16, Y);
   else
-    w4a16_tiled_dma_kernel<GS, ZP, false><<<(unsigned)tiles, 256, dyn, stream>>>(
+    w4a16_tiled_kernel<GS, ZP, false><<<(unsigned)tiles, 256, dyn, stream>>>(
         A, M, N, K, qweight, scales16, zeros, s16, Y);
   return hipGetLastError();
 }
@@ -294,11 +304,11 @@ hipError_t launch_w4a16(const uint16_t* A, int64_t M, int64_t N, int64_t K, int 
     return launch_w4a16_gemv(A, M, N, K, group, qweight, scales16, zeros, s16, Y, stream);
   // the tiled kernel above 64 batch rows, and from 49 on for tall weights (each skinny
   // workgroup reads all of A, which at 8192+ weight rows costs more than the tiles' unpacking),
-  // while its tables fit next to the 104 KiB of stages; otherwise the skinny kernel in passes
+  // while its tables fit next to the 64 KiB of stages; otherwise the skinny kernel in passes
   // of 64 rows
   const bool zp = zeros != nullptr;
   const bool tiled = (M > 64 || (M > 48 && N >= 8192)) &&
-                     kDmaSmem + w4a16_dma_tables(K, group, zp) <= 160 * 1024;
+                     kRwSmem + w4a16_tiled_tables(K, group, zp) <= 160 * 1024;
   if (!tiled)
     return launch_w4a16_skinny(A, M, N, K, group, qweight, scales16, zeros, s16, Y, stream);
   if (group == 64)
