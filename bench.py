@@ -361,11 +361,13 @@ def record_counters(ctr_dir):
 
 
 # ---------------------------------------------------------------------------------------------
-def w4a16_time(awq, torch, n, k, ms, group=128, zero_point=False):
+def w4a16_time(awq, torch, n, k, ms, group=128, zero_point=False, ws=True):
     """Time W4A16 at the batch sizes `ms` on an [n, k] weight over rotated copies with HIP events.
     `us` is the GPU time per call: one pass over every copy is captured in a HIP graph and
     replayed (the result of a replay is checked against the eager calls), so the host's launch
-    rate does not enter; `us_eager` is the same pass issued call by call from Python."""
+    rate does not enter; `us_eager` is the same pass issued call by call from Python.
+    ws: w4a16_gemm_ws with one workspace (K split over workgroups for M <= 64), else
+    w4a16_gemm."""
     import numpy as np
     import workloads
     st = torch.cuda.current_stream()
@@ -392,11 +394,17 @@ def w4a16_time(awq, torch, n, k, ms, group=128, zero_point=False):
     for m in ms:
         A = torch.from_numpy(workloads.w4a16_activations(m, k, config=4)).cuda()
         Y = torch.empty((m, n), dtype=torch.float16, device="cuda")
+        wsp = torch.zeros(max(1, awq.w4a16_gemm_workspace_bytes(m, n, k, group)),
+                          dtype=torch.uint8, device="cuda")
 
         def one_pass():
             for i in range(copies):
-                awq.w4a16_gemm(A, qws[i], scs[i], s_d, group=group, out=Y,
-                               zeros=zds[i] if zds is not None else None)
+                if ws:
+                    awq.w4a16_gemm_ws(A, qws[i], scs[i], s_d, group=group, out=Y,
+                                      zeros=zds[i] if zds is not None else None, workspace=wsp)
+                else:
+                    awq.w4a16_gemm(A, qws[i], scs[i], s_d, group=group, out=Y,
+                                   zeros=zds[i] if zds is not None else None)
         one_pass()                                      # warm-up
         torch.cuda.synchronize()
         y_eager = Y.clone()
@@ -419,7 +427,8 @@ def w4a16_time(awq, torch, n, k, ms, group=128, zero_point=False):
         nbytes = (n * k // 2 + n * (k // group) * 2 + (n * (k // group) if zero_point else 0) +
                   k * 2 + m * k * 2 + m * n * 2)
         flops = 2.0 * m * n * k
-        rec = {"n": n, "k": k, "m": m, "us": round(us, 3), "us_eager": round(us_eager, 3),
+        rec = {"n": n, "k": k, "m": m, "entry": "w4a16_gemm_ws" if ws else "w4a16_gemm",
+               "us": round(us, 3), "us_eager": round(us_eager, 3),
                "bytes": nbytes, "gbs": round(nbytes / us / 1e3, 1),
                "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
                "tflops": round(flops / us / 1e6, 2)}

@@ -374,6 +374,25 @@ awq_status w4a16_gemm(const uint16_t* A, int64_t M, int64_t N, int64_t K, int32_
                       const uint16_t* s16, uint16_t* Y, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * w4a16_gemm_ws -- w4a16_gemm with a workspace: the same operation, arguments, arithmetic and
+ * errors. Where it pays -- 33 <= M <= 64; 17 <= M <= 32 with N >= 8192; 16 <= M <= 32 with
+ * K >= 8192 -- a kernel splits K over workgroups (64 weight rows each) and a second one adds
+ * the slices' fp32 partial sums in a fixed slice order (results do not depend on scheduling;
+ * they may differ from w4a16_gemm's in the last bits of Y, which adds in another order).
+ * Elsewhere it is w4a16_gemm and needs no workspace.
+ * ws       device workspace of at least w4a16_gemm_workspace_bytes(M, N, K, group) bytes (0:
+ *          ws may be NULL): scratch for the slices' partial sums, any contents. The call
+ *          launches two kernels on `stream` (the slices, then their sum).
+ * Calls that share a workspace must not overlap (one stream, or events between them).
+ * Errors: as w4a16_gemm; AWQ_ERR_WORKSPACE when ws is NULL or smaller than required.
+ * ---------------------------------------------------------------------------------------- */
+size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group);
+awq_status w4a16_gemm_ws(const uint16_t* A, int64_t M, int64_t N, int64_t K, int32_t group,
+                         const uint32_t* qweight, const uint16_t* scales16, const uint8_t* zeros,
+                         const uint16_t* s16, uint16_t* Y, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * awq_act_stats_noalloc -- awq_act_stats for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same inputs,
  * outputs, flags and results (bit for bit) as awq_act_stats, without the workspace argument: the

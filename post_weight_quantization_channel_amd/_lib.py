@@ -75,6 +75,8 @@ SIGNATURES = {
     "awq_pack_int4": (_E, [_P, _E, _I64, _I64, _P, _P, ctypes.POINTER(AwqCfg), _P, _P, _P, _P,
                            _P, _P, _P]),
     "w4a16_gemm": (_E, [_P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P]),
+    "w4a16_gemm_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
+    "w4a16_gemm_ws": (_E, [_P, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "awq_act_stats_noalloc": (_E, [_P, _E, _I64, _I64, _I64, _P, _P, _P]),
 }
 

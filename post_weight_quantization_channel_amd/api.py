@@ -364,12 +364,7 @@ def pack_int4(W: torch.Tensor, s: torch.Tensor, cfg: AwqConfig = AwqConfig(),
     return PackResult(qweight, scales16, s16, codes, flags, zeros)
 
 
-def w4a16_gemm(A: torch.Tensor, qweight: torch.Tensor, scales16: torch.Tensor,
-               s16: torch.Tensor | None, group: int = 128, out: torch.Tensor | None = None,
-               zeros: torch.Tensor | None = None) -> torch.Tensor:
-    """Y = (A / s) (c(q) * step)^T, fp16 [M, N], c(q) = q (symmetric) or q - z (zeros given);
-    s16 = None when s^-1 is folded into A's producer."""
-    lib = _lib.load()
+def _w4a16_check(A, qweight, scales16, s16, group, zeros):
     for t, nm in ((A, "A"), (qweight, "qweight"), (scales16, "scales16")):
         _dev(t, nm)
     if s16 is not None:
@@ -386,6 +381,16 @@ def w4a16_gemm(A: torch.Tensor, qweight: torch.Tensor, scales16: torch.Tensor,
         _dev(zeros, "zeros")
         if zeros.shape != (N, K // group) or zeros.dtype != torch.uint8:
             raise ValueError("zeros must be uint8 [N, K/group]")
+    return M, N, K
+
+
+def w4a16_gemm(A: torch.Tensor, qweight: torch.Tensor, scales16: torch.Tensor,
+               s16: torch.Tensor | None, group: int = 128, out: torch.Tensor | None = None,
+               zeros: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = (A / s) (c(q) * step)^T, fp16 [M, N], c(q) = q (symmetric) or q - z (zeros given);
+    s16 = None when s^-1 is folded into A's producer."""
+    lib = _lib.load()
+    M, N, K = _w4a16_check(A, qweight, scales16, s16, group, zeros)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=A.device)
     check("w4a16_gemm", lib.w4a16_gemm(A.data_ptr(), M, N, K, group, qweight.data_ptr(),
@@ -393,4 +398,48 @@ def w4a16_gemm(A: torch.Tensor, qweight: torch.Tensor, scales16: torch.Tensor,
                                        zeros.data_ptr() if zeros is not None else None,
                                        s16.data_ptr() if s16 is not None else None, out.data_ptr(),
                                        _stream(A)))
+    return out
+
+
+def w4a16_gemm_workspace_bytes(M: int, N: int, K: int, group: int = 128) -> int:
+    """Bytes of the w4a16_gemm_ws workspace for these sizes (0: none needed)."""
+    return int(_lib.load().w4a16_gemm_workspace_bytes(M, N, K, group))
+
+
+# w4a16_gemm_ws workspaces kept per (device, stream), so that calls on one stream share one
+_W4A16_WS: dict = {}
+
+
+def w4a16_gemm_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """The cached w4a16_gemm_ws workspace of the current stream on `device`, at least `nbytes`
+    bytes (a larger one replaces a smaller one)."""
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _W4A16_WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _W4A16_WS[key] = ws
+    return ws
+
+
+def w4a16_gemm_ws(A: torch.Tensor, qweight: torch.Tensor, scales16: torch.Tensor,
+                  s16: torch.Tensor | None, group: int = 128, out: torch.Tensor | None = None,
+                  zeros: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """w4a16_gemm with a workspace (K split over workgroups for M <= 64). workspace: a uint8
+    device tensor of at least w4a16_gemm_workspace_bytes bytes, or None for the cached one of
+    the current stream."""
+    lib = _lib.load()
+    M, N, K = _w4a16_check(A, qweight, scales16, s16, group, zeros)
+    need = w4a16_gemm_workspace_bytes(M, N, K, group)
+    if workspace is None:
+        workspace = w4a16_gemm_workspace(A.device, need)
+    else:
+        _dev(workspace, "workspace")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    check("w4a16_gemm_ws", lib.w4a16_gemm_ws(
+        A.data_ptr(), M, N, K, group, qweight.data_ptr(), scales16.data_ptr(),
+        zeros.data_ptr() if zeros is not None else None,
+        s16.data_ptr() if s16 is not None else None, out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(A)))
     return out

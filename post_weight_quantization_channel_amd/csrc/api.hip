@@ -125,7 +125,7 @@ const char* awq_status_string(awq_status status) {
   return "unknown awq_status";
 }
 
-int32_t awq_version(void) { return 10600; }
+int32_t awq_version(void) { return 10700; }
 
 size_t awq_act_stats_workspace_bytes(int64_t M, int64_t K) {
   if (M < 1 || K < 1 || M > kMaxDim || K > kMaxDim) return 0;
@@ -539,6 +539,32 @@ awq_status w4a16_gemm(const uint16_t* A, int64_t M, int64_t N, int64_t K, int32_
     return AWQ_ERR_SHAPE;
   return hip_status(awq::launch_w4a16(A, M, N, K, group, qweight, scales16, zeros, s16, Y,
                                       stream));
+}
+
+size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group) {
+  if ((group != 128 && group != 64) || M < 1 || N < 1 || K < 128 || K % 128 || M > kMaxDim ||
+      N > kMaxDim || K > kMaxW4A16K)
+    return 0;
+  if (!awq::w4a16_prefer_split(M, N, K)) return 0;
+  return awq::w4a16_splitk_plan(M, N, K).ws_bytes;
+}
+
+awq_status w4a16_gemm_ws(const uint16_t* A, int64_t M, int64_t N, int64_t K, int32_t group,
+                         const uint32_t* qweight, const uint16_t* scales16, const uint8_t* zeros,
+                         const uint16_t* s16, uint16_t* Y, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  if (!A || !qweight || !scales16 || !Y) return AWQ_ERR_NULL;
+  if (group != 128 && group != 64) return AWQ_ERR_CONFIG;
+  if (M < 1 || N < 1 || K < 128 || K % 128 || M > kMaxDim || N > kMaxDim || K > kMaxW4A16K ||
+      !aligned16(A) || !aligned16(qweight) || (s16 && !aligned16(s16)))
+    return AWQ_ERR_SHAPE;
+  if (!awq::w4a16_prefer_split(M, N, K))
+    return hip_status(awq::launch_w4a16(A, M, N, K, group, qweight, scales16, zeros, s16, Y,
+                                        stream));
+  const awq::W4a16SplitPlan p = awq::w4a16_splitk_plan(M, N, K);
+  if (p.ws_bytes > 0 && (!ws || ws_bytes < p.ws_bytes)) return AWQ_ERR_WORKSPACE;
+  return hip_status(awq::launch_w4a16_splitk(A, M, N, K, group, qweight, scales16, zeros, s16, Y,
+                                             ws, ws_bytes, stream));
 }
 
 }  // extern "C"

@@ -420,6 +420,10 @@ __device__ __forceinline__ void buffer_load16_lds_so(rsrc_t r, uint32_t lds, uin
       : "memory");
 }
 
+// s_waitcnt immediate: at most n vector-memory loads outstanding (gfx9 encoding: vmcnt in bits
+// [3:0] and [15:14]; expcnt and lgkmcnt left at their maxima)
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
+
 __device__ __forceinline__ void flag_or(uint32_t* flags, uint32_t bits) {
   if (bits) atomicOr(flags, bits);
 }

@@ -144,6 +144,23 @@ hipError_t launch_w4a16_skinny(const uint16_t* A, int64_t M, int64_t N, int64_t 
                                const uint32_t* qweight, const uint16_t* scales16,
                                const uint8_t* zeros, const uint16_t* s16, uint16_t* Y,
                                hipStream_t stream);
+// 1 <= M <= 64 with K split over workgroups (w4a16_splitk.hip): 64 weight rows per workgroup,
+// S slices of KB 128-channel blocks; with S > 1 the fp32 partials go through a workspace of
+// ws_bytes and a second kernel adds them
+constexpr int64_t kW4a16SplitTarget = 512;   // workgroups the slices aim at
+struct W4a16SplitPlan {
+  int MB;            // 16-row blocks of activations
+  int64_t tiles;     // 64-row weight tiles
+  int64_t S;         // K slices
+  int64_t KB;        // blocks per slice
+  size_t ws_bytes;   // 0 when S == 1
+};
+W4a16SplitPlan w4a16_splitk_plan(int64_t M, int64_t N, int64_t K);
+bool w4a16_prefer_split(int64_t M, int64_t N, int64_t K);
+hipError_t launch_w4a16_splitk(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
+                               const uint32_t* qweight, const uint16_t* scales16,
+                               const uint8_t* zeros, const uint16_t* s16, uint16_t* Y,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
 // group 128 or 64; zeros [N, K/group] (zero-point codes) or nullptr; s16 nullptr: s folded
 hipError_t launch_w4a16(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
                         const uint32_t* qweight, const uint16_t* scales16, const uint8_t* zeros,

@@ -46,9 +46,6 @@ __device__ __forceinline__ int tswz(int row, int chunk) {   // byte offset insid
 }
 constexpr int kAStage = TBM * TBK * 2;                // 32 KiB of activations per step
 constexpr int kRwSmem = 2 * kAStage;                  // two stages: 64 KiB
-// s_waitcnt immediate: at most n vector-memory loads outstanding (gfx9 encoding: vmcnt in bits
-// [3:0] and [15:14]; expcnt and lgkmcnt left at their maxima)
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 }  // namespace
 
 // bytes of the dynamic tables: fp16 r [K], fp32 2^-b [K/128], fp16 steps [K/GS][64], (ZP) uint8

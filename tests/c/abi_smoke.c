@@ -43,6 +43,9 @@ int main(void) {
   uint32_t flags = 0;
   EXPECT(awq_act_stats(NULL, AWQ_F16, 16, 16, 16, sx, &flags, NULL, 0, NULL) == AWQ_ERR_NULL);
   EXPECT(w4a16_gemm(NULL, 1, 16, 128, 128, NULL, NULL, NULL, NULL, NULL, NULL) == AWQ_ERR_NULL);
+  EXPECT(w4a16_gemm_workspace_bytes(64, 4096, 4096, 128) > 0);
+  EXPECT(w4a16_gemm_ws(NULL, 16, 4096, 4096, 128, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) ==
+         AWQ_ERR_NULL);
 
   if (failures) return 1;
   printf("C ABI ok (version %d)\n", (int)awq_version());

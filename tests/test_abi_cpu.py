@@ -32,6 +32,7 @@ def lib():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("awq_act_stats", "awq_search_layer", "awq_pack_int4", "w4a16_gemm",
+              "w4a16_gemm_ws", "w4a16_gemm_workspace_bytes",
               "awq_search_workspace_bytes", "awq_act_stats_workspace_bytes",
               "awq_clip_search", "awq_clip_workspace_bytes", "awq_search_layers",
               "awq_clip_search_gram", "awq_clip_search_gram_ws_bytes",
@@ -51,7 +52,7 @@ def test_status_strings(lib):
     for code in range(7):
         s = lib.awq_status_string(code).decode()
         assert s.startswith("AWQ_")
-    assert lib.awq_version() == 10600
+    assert lib.awq_version() == 10700
 
 
 def cfg(bits=4, group=128, n_grid=20, s_floor=1e-5, form=0, n_clip=11, clip_min=0.5,
@@ -416,6 +417,49 @@ def test_w4a16_rejects(lib):
     assert call(N=0) == E.AWQ_ERR_SHAPE
     assert call(A=FAKE + 8) == E.AWQ_ERR_SHAPE
     assert call(s16=FAKE + 8) == E.AWQ_ERR_SHAPE
+
+
+def test_w4a16_ws_rejects(lib):
+    E = _lib
+    f = lib.w4a16_gemm_ws
+    need = lib.w4a16_gemm_workspace_bytes(64, 4096, 4096, 128)
+
+    def call(A=FAKE, M=64, N=4096, K=4096, group=128, qw=FAKE, sc=FAKE, zeros=None, s16=FAKE,
+             ws=FAKE, ws_bytes=need):
+        return f(A, M, N, K, group, qw, sc, zeros, s16, FAKE, ws, ws_bytes, None)
+    assert call(A=None) == E.AWQ_ERR_NULL
+    assert call(group=32) == E.AWQ_ERR_CONFIG
+    assert call(M=0) == E.AWQ_ERR_SHAPE
+    assert call(K=200) == E.AWQ_ERR_SHAPE
+    assert call(K=32768 + 128) == E.AWQ_ERR_SHAPE
+    assert call(A=FAKE + 8) == E.AWQ_ERR_SHAPE
+    assert call(ws=None) == E.AWQ_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == E.AWQ_ERR_WORKSPACE
+
+
+def test_w4a16_workspace_bytes(lib):
+    """The split plan: 64-row tiles, slices of >= 4 blocks, at most 512 workgroups; partials of
+    S x tiles x 4 waves x MB x 1 KiB. It is taken above 32 rows, from 17 rows with N >= 8192,
+    from 16 rows with K >= 8192; elsewhere no workspace."""
+    wsb = lib.w4a16_gemm_workspace_bytes
+    # 4096 x 4096: 64 tiles, 8 slices of 4 blocks
+    assert wsb(33, 4096, 4096, 128) == 8 * 64 * 4 * 4 * 1024
+    assert wsb(64, 4096, 4096, 64) == 8 * 64 * 4 * 4 * 1024
+    assert wsb(16, 4096, 4096, 128) == 0 and wsb(32, 4096, 4096, 128) == 0
+    # 11008 x 4096: 172 tiles, 2 slices of 16 blocks (3 would be 516 workgroups)
+    assert wsb(17, 11008, 4096, 128) == 2 * 172 * 4 * 2 * 1024
+    assert wsb(16, 11008, 4096, 128) == 0
+    # 1024 x 8192: 16 tiles, 16 slices of 4 blocks
+    assert wsb(16, 1024, 8192, 128) == 16 * 16 * 4 * 1024
+    assert wsb(15, 1024, 8192, 128) == 0
+    # one slice (no workspace): more than 256 tiles, or K of fewer than 8 blocks
+    assert wsb(48, 32768, 4096, 128) == 0
+    assert wsb(48, 4096, 896, 128) == 0
+    # at most 64 blocks per slice: K = 16384 on 1024 tiles still takes two slices
+    assert wsb(16, 65536, 16384, 128) == 2 * 1024 * 4 * 1 * 1024
+    # one row, and batches above 64 rows, take the kernels of w4a16_gemm
+    assert wsb(65, 4096, 4096, 128) == 0 and wsb(1, 1024, 8192, 128) == 0
+    assert wsb(16, 4096, 200, 128) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
