@@ -375,16 +375,21 @@ awq_status w4a16_gemm(const uint16_t* A, int64_t M, int64_t N, int64_t K, int32_
 
 /* ------------------------------------------------------------------------------------------
  * w4a16_gemm_ws -- w4a16_gemm with a workspace: the same operation, arguments, arithmetic and
- * errors. Where it pays -- 33 <= M <= 64; 17 <= M <= 32 with N >= 8192; 16 <= M <= 32 with
- * K >= 8192 -- a kernel splits K over workgroups (64 weight rows each) and a second one adds
- * the slices' fp32 partial sums in a fixed slice order (results do not depend on scheduling;
- * they may differ from w4a16_gemm's in the last bits of Y, which adds in another order).
+ * errors. Where it pays, K is split over workgroups and a second kernel adds the slices' fp32
+ * partial sums in a fixed slice order (results do not depend on scheduling; they may differ
+ * from w4a16_gemm's in the last bits of Y, which adds in another order):
+ *   33 <= M <= 64; 17 <= M <= 32 with N >= 8192; 16 <= M <= 32 with K >= 8192: workgroups of
+ *     64 weight rows and all M rows;
+ *   M > 64 while the 128 x 64 output tiles number fewer than 256 (CUs would idle): the tiled
+ *     kernel on slices of at least 8 steps of 128 channels.
  * Elsewhere it is w4a16_gemm and needs no workspace.
- * ws       device workspace of at least w4a16_gemm_workspace_bytes(M, N, K, group) bytes (0:
- *          ws may be NULL): scratch for the slices' partial sums, any contents. The call
- *          launches two kernels on `stream` (the slices, then their sum).
+ * ws       device workspace, 16-byte aligned, of at least w4a16_gemm_workspace_bytes(M, N, K,
+ *          group) bytes (0: ws may be NULL): scratch for the slices' partial sums, any
+ *          contents. With slices the call launches two kernels on `stream` (the slices, then
+ *          their sum).
  * Calls that share a workspace must not overlap (one stream, or events between them).
- * Errors: as w4a16_gemm; AWQ_ERR_WORKSPACE when ws is NULL or smaller than required.
+ * Errors: as w4a16_gemm; AWQ_ERR_WORKSPACE when ws is needed and NULL or smaller than required,
+ *         or is not 16-byte aligned.
  * ---------------------------------------------------------------------------------------- */
 size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group);
 awq_status w4a16_gemm_ws(const uint16_t* A, int64_t M, int64_t N, int64_t K, int32_t group,

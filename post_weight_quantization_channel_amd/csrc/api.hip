@@ -545,6 +545,7 @@ size_t w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group
   if ((group != 128 && group != 64) || M < 1 || N < 1 || K < 128 || K % 128 || M > kMaxDim ||
       N > kMaxDim || K > kMaxW4A16K)
     return 0;
+  if (M > 64) return awq::w4a16_tiled_plan(M, N, K, true).ws_bytes;
   if (!awq::w4a16_prefer_split(M, N, K)) return 0;
   return awq::w4a16_splitk_plan(M, N, K).ws_bytes;
 }
@@ -558,6 +559,16 @@ awq_status w4a16_gemm_ws(const uint16_t* A, int64_t M, int64_t N, int64_t K, int
   if (M < 1 || N < 1 || K < 128 || K % 128 || M > kMaxDim || N > kMaxDim || K > kMaxW4A16K ||
       !aligned16(A) || !aligned16(qweight) || (s16 && !aligned16(s16)))
     return AWQ_ERR_SHAPE;
+  if (ws && !aligned16(ws)) return AWQ_ERR_WORKSPACE;
+  if (M > 64) {
+    const awq::W4a16TiledPlan tp = awq::w4a16_tiled_plan(M, N, K, true);
+    if (tp.S == 1)
+      return hip_status(awq::launch_w4a16(A, M, N, K, group, qweight, scales16, zeros, s16, Y,
+                                          stream));
+    if (!ws || ws_bytes < tp.ws_bytes) return AWQ_ERR_WORKSPACE;
+    return hip_status(awq::launch_w4a16_tiled_split(A, M, N, K, group, qweight, scales16, zeros,
+                                                    s16, Y, ws, ws_bytes, stream));
+  }
   if (!awq::w4a16_prefer_split(M, N, K))
     return hip_status(awq::launch_w4a16(A, M, N, K, group, qweight, scales16, zeros, s16, Y,
                                         stream));

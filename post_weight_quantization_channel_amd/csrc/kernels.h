@@ -161,6 +161,21 @@ hipError_t launch_w4a16_splitk(const uint16_t* A, int64_t M, int64_t N, int64_t 
                                const uint32_t* qweight, const uint16_t* scales16,
                                const uint8_t* zeros, const uint16_t* s16, uint16_t* Y,
                                void* ws, size_t ws_bytes, hipStream_t stream);
+// M > 64 (the tiled kernel, w4a16.hip) with K split over workgroups while the tiles leave CUs
+// idle: S slices of KB steps, fp32 partials [S][M][N] (slice stride `stride` floats) in a
+// workspace of ws_bytes, added by a second kernel
+struct W4a16TiledPlan {
+  int64_t tiles;     // 128 x 64 output tiles
+  int64_t S;         // K slices
+  int64_t KB;        // 128-channel steps per slice
+  int64_t stride;    // M N rounded up to a multiple of 4
+  size_t ws_bytes;   // 0 when S == 1
+};
+W4a16TiledPlan w4a16_tiled_plan(int64_t M, int64_t N, int64_t K, bool split);
+hipError_t launch_w4a16_tiled_split(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
+                                    const uint32_t* qweight, const uint16_t* scales16,
+                                    const uint8_t* zeros, const uint16_t* s16, uint16_t* Y,
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
 // group 128 or 64; zeros [N, K/group] (zero-point codes) or nullptr; s16 nullptr: s folded
 hipError_t launch_w4a16(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
                         const uint32_t* qweight, const uint16_t* scales16, const uint8_t* zeros,

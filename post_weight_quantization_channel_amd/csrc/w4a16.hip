@@ -5,10 +5,14 @@
 // c(q) = q for symmetric codes, q - z[n, k/G] for zero-point codes. The activation is divided by
 // s because the weight was multiplied by s (AWQ notes, bg51717.github.io/14592, section 方法).
 //
-// Three kernels by batch size M:
+// Kernels by batch size M:
 //   M = 1        w4a16_gemv.hip: fp16 dot products against a block-scaled A / s table;
-//   2 <= M <= 64 w4a16_skinny.hip: MFMA with the activations read straight from memory;
-//   M > 64       the tiled kernel below (and from 49 rows on for weights of 8192 rows or more).
+//   2 <= M <= 64 w4a16_skinny.hip: MFMA with the activations read straight from memory; with a
+//                workspace, where it pays, w4a16_splitk.hip: K split over workgroups of 64
+//                weight rows;
+//   M > 64       the tiled kernel below (and from 49 rows on for weights of 8192 rows or more);
+//                with a workspace, while the tiles leave CUs idle, on K slices whose fp32
+//                partials w4a16_sum_slices_kernel adds in slice order.
 // All of them apply 1/s without an fp16 value that a tiny s could overflow: either A / s is kept
 // in fp32 and stored scaled by a power of two per 128-channel block, or the weight operand is
 // fp16(q r_k) with r_k = fp16(2^b / s_k), 2^b chosen per block so that the block's largest r_k lies
@@ -68,14 +72,18 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
     const uint16_t* __restrict__ A, int64_t M, int64_t N, int64_t K,
     const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales16,
     const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ s16,
-    uint16_t* __restrict__ Y) {
+    uint16_t* __restrict__ Y, int64_t tiles, int KB, float* __restrict__ partials,
+    int64_t slice_stride) {
   __shared__ __attribute__((aligned(1024))) char smem[kRwSmem];
   extern __shared__ __attribute__((aligned(16))) char dyn[];
+  // tables of this workgroup's K slice (KB blocks from kb0)
   const int64_t ngr = K / GS;
-  uint16_t* rtab = reinterpret_cast<uint16_t*>(dyn);                      // [K]
-  float* bfac = reinterpret_cast<float*>(dyn + K * 2);                    // [K/128]
-  uint16_t* st_lds = reinterpret_cast<uint16_t*>(dyn + K * 2 + (K / 128) * 4);   // [ngr][64]
-  uint8_t* z_lds = reinterpret_cast<uint8_t*>(st_lds + TBN * ngr);        // [ngr][64] (ZP)
+  const int64_t kc = (int64_t)KB * 128;                                    // slice channels
+  constexpr int kGpb = 128 / GS;
+  uint16_t* rtab = reinterpret_cast<uint16_t*>(dyn);                       // [kc]
+  float* bfac = reinterpret_cast<float*>(dyn + kc * 2);                    // [KB]
+  uint16_t* st_lds = reinterpret_cast<uint16_t*>(dyn + kc * 2 + (int64_t)KB * 4);  // [KB kGpb][64]
+  uint8_t* z_lds = reinterpret_cast<uint8_t*>(st_lds + TBN * KB * kGpb);   // [KB kGpb][64] (ZP)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -85,17 +93,20 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
   const int64_t tilesN = (N + TBN - 1) / TBN;
   int64_t bl = blockIdx.x;
   if ((gridDim.x & 7u) == 0) bl = (int64_t)(blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-  const int64_t m0 = (bl / tilesN) * TBM;
-  const int64_t n0 = (bl % tilesN) * TBN;
-  const int64_t groups = K / 128;
+  const int split = (int)(bl / tiles);     // K slice (slice-major: one XCD shares slices)
+  const int64_t tile = bl % tiles;
+  const int64_t m0 = (tile / tilesN) * TBM;
+  const int64_t n0 = (tile % tilesN) * TBN;
+  const int64_t kb0 = (int64_t)split * KB;
+  const int64_t groups = (K / 128 - kb0 < KB) ? K / 128 - kb0 : KB;   // this slice's steps
 
   // ---- tables: r_k = fp16(2^b / s_k) in natural order, 2^-b per block, steps, zero points ----
-  for (int64_t k8 = tid; k8 < K / 8; k8 += 256) {
+  for (int64_t k8 = tid; k8 < groups * 16; k8 += 256) {
     float inv[8];
     float mx = 0.0f;
     if (HAS_S) {
       float sv[8];
-      load8_f32<kF16>(s16 + k8 * 8, sv);
+      load8_f32<kF16>(s16 + kb0 * 128 + k8 * 8, sv);
 #pragma unroll
       for (int t = 0; t < 8; ++t) inv[t] = __builtin_amdgcn_rcpf(sv[t]);
     } else {
@@ -114,8 +125,8 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
     *reinterpret_cast<uint4*>(rtab + k8 * 8) = make_uint4(w[0], w[1], w[2], w[3]);
     if ((k8 & 15) == 0) bfac[k8 >> 4] = ldexpf(1.0f, -b);
   }
-  for (int64_t e = tid; e < TBN * ngr; e += 256) {
-    const int64_t r = e % TBN, gq = e / TBN;
+  for (int64_t e = tid; e < TBN * groups * kGpb; e += 256) {
+    const int64_t r = e % TBN, gq = kb0 * kGpb + e / TBN;
     const int64_t row = (n0 + r < N) ? n0 + r : N - 1;
     st_lds[e] = (n0 + r < N) ? scales16[row * ngr + gq] : (uint16_t)0;
     if (ZP) z_lds[e] = zeros[row * ngr + gq];
@@ -135,7 +146,7 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t lds = lds0 + (uint32_t)(st * kAStage) + (uint32_t)((32 * wave + 4 * j) * 256);
-      const uint32_t so = (uint32_t)((32 * wave + 4 * j) * K * 2) + (uint32_t)(g * 256);
+      const uint32_t so = (uint32_t)((32 * wave + 4 * j) * K * 2) + (uint32_t)((kb0 + g) * 256);
       buffer_load16_lds_so(ra, lds, avoff[j & 3], so);
     }
   };
@@ -144,7 +155,7 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int64_t n = n0 + 32 * wn + 16 * nb + li;
-    wr[nb] = qweight + (n < N ? n : N - 1) * (K / 8);
+    wr[nb] = qweight + (n < N ? n : N - 1) * (K / 8) + kb0 * 16;
   }
   struct Codes {
     uint32_t w[2][4];   // [nb][kk]: the word MFMA kk of the step takes
@@ -258,6 +269,26 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
     if (g + 1 < groups) step(g + 1, 1, cb[1], cb[0]);
   }
 
+  if (partials) {   // one of several K slices: fp32 partial [m][n] of slice `split`
+    float* P = partials + split * slice_stride;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t m = m0 + wm * 64 + j * 16 + li;
+        const int64_t nb = n0 + wn * 32 + i * 16 + 4 * lg;
+        if (m < M) {
+          if (nb + 3 < N && ((N & 3) == 0)) {
+            *reinterpret_cast<floatx4*>(P + m * N + nb) = acc[i][j];
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (nb + r < N) P[m * N + nb + r] = acc[i][j][r];
+          }
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -278,20 +309,94 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
     }
 }
 
+// Y = fp16(sum of the S slices' fp32 partials [S][M][N], slice stride `stride` floats, a multiple
+// of 4), added in slice order 0 .. S-1; four elements per thread, eight slices' loads in flight.
+__global__ __launch_bounds__(256) void w4a16_sum_slices_kernel(const float* __restrict__ P, int S,
+                                                               int64_t stride, int64_t MN,
+                                                               uint16_t* __restrict__ Y) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= MN) return;
+  constexpr int kC = 8;
+  floatx4 t = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < S; j0 += kC) {
+    floatx4 v[kC];
+#pragma unroll
+    for (int u = 0; u < kC; ++u) {
+      const int j = (j0 + u < S) ? j0 + u : 0;
+      v[u] = *reinterpret_cast<const floatx4*>(P + j * stride + e);   // within the padded slice
+    }
+#pragma unroll
+    for (int u = 0; u < kC; ++u)
+      if (j0 + u < S) t = (j0 + u == 0) ? v[u] : t + v[u];
+  }
+  if (e + 3 < MN && (((uintptr_t)(Y + e)) & 7u) == 0) {
+    const uint32_t lo = (uint32_t)f2h(t[0]) | ((uint32_t)f2h(t[1]) << 16);
+    const uint32_t hi = (uint32_t)f2h(t[2]) | ((uint32_t)f2h(t[3]) << 16);
+    *reinterpret_cast<uint2*>(Y + e) = make_uint2(lo, hi);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (e + r < MN) Y[e + r] = f2h(t[r]);
+  }
+}
+
+W4a16TiledPlan w4a16_tiled_plan(int64_t M, int64_t N, int64_t K, bool split) {
+  W4a16TiledPlan p{};
+  p.tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
+  const int64_t nblk = K / 128;
+  int64_t S = 1;
+  if (split && p.tiles < 256) {
+    // slices while fewer tiles than CUs, the grid within two workgroups per CU, at least 8 steps
+    // each (measured, graph replay: 4096 x 4096 at 128 rows 19.7 us vs 36.5 in one slice,
+    // 4096 x 11008 33.6 vs 92.0, 8192 x 8192 40.8 vs 70.0; at 256 tiles two slices are no faster
+    // at 4096 x 4096 x 512 rows and slower at 4096 x 11008: 113 vs 95 us)
+    S = kW4a16SplitTarget / p.tiles;
+    const int64_t smax = nblk / 8;
+    S = S > smax ? smax : S;
+    S = S < 1 ? 1 : S;
+  }
+  p.KB = (nblk + S - 1) / S;
+  p.S = (nblk + p.KB - 1) / p.KB;
+  p.stride = (M * N + 3) / 4 * 4;
+  p.ws_bytes = p.S > 1 ? (size_t)(p.S * p.stride * 4) : 0;
+  return p;
+}
+
 template <int GS, bool ZP>
 static hipError_t w4a16_tiled(const uint16_t* A, int64_t M, int64_t N, int64_t K,
                               const uint32_t* qweight, const uint16_t* scales16,
                               const uint8_t* zeros, const uint16_t* s16, uint16_t* Y,
-                              hipStream_t stream) {
-  const int64_t tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
-  const size_t dyn = (size_t)w4a16_tiled_tables(K, GS, ZP);
+                              const W4a16TiledPlan& p, float* partials, hipStream_t stream) {
+  const size_t dyn = (size_t)w4a16_tiled_tables(p.KB * 128, GS, ZP);
+  const unsigned grid = (unsigned)(p.tiles * p.S);
+  float* P = p.S > 1 ? partials : nullptr;
   if (s16)
-    w4a16_tiled_kernel<GS, ZP, true><<<(unsigned)tiles, 256, dyn, stream>>>(
-        A, M, N, K, qweight, scales16, zeros, s16, Y);
+    w4a16_tiled_kernel<GS, ZP, true><<<grid, 256, dyn, stream>>>(
+        A, M, N, K, qweight, scales16, zeros, s16, Y, p.tiles, (int)p.KB, P, p.stride);
   else
-    w4a16_tiled_kernel<GS, ZP, false><<<(unsigned)tiles, 256, dyn, stream>>>(
-        A, M, N, K, qweight, scales16, zeros, s16, Y);
+    w4a16_tiled_kernel<GS, ZP, false><<<grid, 256, dyn, stream>>>(
+        A, M, N, K, qweight, scales16, zeros, s16, Y, p.tiles, (int)p.KB, P, p.stride);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.S == 1) return e;
+  const int64_t MN = M * N;
+  w4a16_sum_slices_kernel<<<(unsigned)((MN / 4 + 255) / 256 + 1), 256, 0, stream>>>(
+      partials, (int)p.S, p.stride, MN, Y);
   return hipGetLastError();
+}
+
+hipError_t launch_w4a16_tiled_split(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
+                                    const uint32_t* qweight, const uint16_t* scales16,
+                                    const uint8_t* zeros, const uint16_t* s16, uint16_t* Y,
+                                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  const W4a16TiledPlan p = w4a16_tiled_plan(M, N, K, true);
+  if (p.S > 1 && (ws == nullptr || ws_bytes < p.ws_bytes)) return hipErrorInvalidValue;
+  const bool zp = zeros != nullptr;
+  float* P = static_cast<float*>(ws);
+  if (group == 64)
+    return zp ? w4a16_tiled<64, true>(A, M, N, K, qweight, scales16, zeros, s16, Y, p, P, stream)
+              : w4a16_tiled<64, false>(A, M, N, K, qweight, scales16, zeros, s16, Y, p, P, stream);
+  return zp ? w4a16_tiled<128, true>(A, M, N, K, qweight, scales16, zeros, s16, Y, p, P, stream)
+            : w4a16_tiled<128, false>(A, M, N, K, qweight, scales16, zeros, s16, Y, p, P, stream);
 }
 
 hipError_t launch_w4a16(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
@@ -308,11 +413,16 @@ hipError_t launch_w4a16(const uint16_t* A, int64_t M, int64_t N, int64_t K, int 
                      kRwSmem + w4a16_tiled_tables(K, group, zp) <= 160 * 1024;
   if (!tiled)
     return launch_w4a16_skinny(A, M, N, K, group, qweight, scales16, zeros, s16, Y, stream);
+  const W4a16TiledPlan p = w4a16_tiled_plan(M, N, K, false);
   if (group == 64)
-    return zp ? w4a16_tiled<64, true>(A, M, N, K, qweight, scales16, zeros, s16, Y, stream)
-              : w4a16_tiled<64, false>(A, M, N, K, qweight, scales16, zeros, s16, Y, stream);
-  return zp ? w4a16_tiled<128, true>(A, M, N, K, qweight, scales16, zeros, s16, Y, stream)
-            : w4a16_tiled<128, false>(A, M, N, K, qweight, scales16, zeros, s16, Y, stream);
+    return zp ? w4a16_tiled<64, true>(A, M, N, K, qweight, scales16, zeros, s16, Y, p, nullptr,
+                                      stream)
+              : w4a16_tiled<64, false>(A, M, N, K, qweight, scales16, zeros, s16, Y, p, nullptr,
+                                       stream);
+  return zp ? w4a16_tiled<128, true>(A, M, N, K, qweight, scales16, zeros, s16, Y, p, nullptr,
+                                     stream)
+            : w4a16_tiled<128, false>(A, M, N, K, qweight, scales16, zeros, s16, Y, p, nullptr,
+                                      stream);
 }
 
 }  // namespace awq

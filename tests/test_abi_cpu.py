@@ -435,6 +435,8 @@ def test_w4a16_ws_rejects(lib):
     assert call(A=FAKE + 8) == E.AWQ_ERR_SHAPE
     assert call(ws=None) == E.AWQ_ERR_WORKSPACE
     assert call(ws_bytes=need - 1) == E.AWQ_ERR_WORKSPACE
+    assert call(ws=FAKE + 8) == E.AWQ_ERR_WORKSPACE                  # not 16-byte aligned
+    assert call(M=128, ws=None) == E.AWQ_ERR_WORKSPACE               # tiled kernel on slices
 
 
 def test_w4a16_workspace_bytes(lib):
@@ -457,8 +459,18 @@ def test_w4a16_workspace_bytes(lib):
     assert wsb(48, 4096, 896, 128) == 0
     # at most 64 blocks per slice: K = 16384 on 1024 tiles still takes two slices
     assert wsb(16, 65536, 16384, 128) == 2 * 1024 * 4 * 1 * 1024
-    # one row, and batches above 64 rows, take the kernels of w4a16_gemm
-    assert wsb(65, 4096, 4096, 128) == 0 and wsb(1, 1024, 8192, 128) == 0
+    # one row takes w4a16_gemm's kernel
+    assert wsb(1, 1024, 8192, 128) == 0
+    # above 64 rows with fewer than 256 tiles: the tiled kernel on S slices of >= 8 steps while
+    # tiles * S <= 512; partials [S][M][N] fp32, M N rounded up to a multiple of 4
+    assert wsb(128, 4096, 4096, 128) == 4 * 128 * 4096 * 4          # 64 tiles, 4 slices of 8
+    assert wsb(65, 4096, 4096, 128) == 4 * 65 * 4096 * 4
+    assert wsb(128, 11008, 4096, 128) == 2 * 128 * 11008 * 4        # 172 tiles
+    assert wsb(100, 4096, 11008, 64) == 8 * 100 * 4096 * 4          # 86 steps: slices of 11
+    assert wsb(67, 130, 1024, 128) == 0                              # 8 steps: one slice
+    assert wsb(67, 130, 2048, 128) == 2 * 8712 * 4                   # 67 x 130 = 8710 -> 8712
+    assert wsb(512, 11008, 4096, 128) == 0                           # 688 tiles
+    assert wsb(512, 4096, 4096, 128) == 0                            # 256 tiles
     assert wsb(16, 4096, 200, 128) == 0
 
 

@@ -58,7 +58,9 @@ WS_CASES = [(384, 512, m) for m in (1, 2, 16, 17, 64)] + \
            [(11008, 4096, m) for m in (16, 17, 32, 64)] + \
            [(4096, 11008, 16), (4096, 8192, 20), (2048, 8192, 16), (1024, 28672, 2),
             (130, 1024, 40), (1002, 2048, 64), (130, 32768, 48), (32768, 4096, 48),
-            (8192, 4096, 24)]
+            (8192, 4096, 24)] + \
+           [(4096, 4096, 128), (4096, 4096, 65), (11008, 4096, 128), (4096, 11008, 100),
+            (130, 2048, 67), (1002, 4096, 300), (130, 32768, 200), (4096, 4096, 512)]
 
 
 @pytest.mark.parametrize("n,k,m", WS_CASES)
@@ -74,7 +76,8 @@ WS_VARIANTS = [(g, zp, hs) for g in (128, 64) for zp in (False, True) for hs in 
 
 
 @pytest.mark.parametrize("group,zp,with_s", WS_VARIANTS)
-@pytest.mark.parametrize("n,k,m", [(320, 8192, 16), (4096, 4096, 40), (1000, 11008, 20)])
+@pytest.mark.parametrize("n,k,m", [(320, 8192, 16), (4096, 4096, 40), (1000, 11008, 20),
+                                   (1000, 4096, 100)])
 def test_w4a16_ws_group_zero_point_and_folded_s(awq, group, zp, with_s, n, k, m):
     qw, sc, s = workloads.w4a16_random_artifacts(n, k, group=group, config=4, j=n + m)
     z = workloads.w4a16_random_zeros(n, k, group=group, config=4, j=n + m) if zp else None
@@ -108,7 +111,7 @@ def test_w4a16_ws_reuse_and_determinism(awq):
     every result equals, bit for bit, that of the same call on a fresh workspace filled with
     other bytes."""
     from post_weight_quantization_channel_amd import _lib
-    shapes = [(4096, 4096, 64), (1024, 8192, 16), (4096, 4096, 64)]
+    shapes = [(4096, 4096, 128), (4096, 4096, 64), (1024, 8192, 16), (4096, 4096, 128)]
     need = max(awq.w4a16_gemm_workspace_bytes(m, n, k) for n, k, m in shapes)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     ws.fill_(0x5A)
