@@ -26,7 +26,7 @@ fields it carries
   quant_variants  groups of 64 and zero-point codes (and both): the search (ms, its quantize
                 and loss kernels), the pack, and W4A16 at M = 1 and 512 on 4096x4096;
   hbm_stages    the bandwidth-bound kernels: algorithmic bytes, GB/s, fraction of 8 TB/s;
-  w4a16         the W4A16 kernel at the batch sizes 1, 4, 16, 64, 512 for 4096x4096 and
+  w4a16         w4a16_gemm_ws at the batch sizes 1, 4, 16, 64, 128, 512 for 4096x4096 and
                 11008x4096, over rotated weight copies (> 256 MB, so HBM and not the
                 Infinity Cache is measured), replayed from a HIP graph (GPU time per call;
                 `us_eager`: the same calls issued one by one from Python): GB/s and fraction
@@ -171,13 +171,18 @@ def traffic_pass():
     log("path pass done")
     # W4A16 on random artefacts of the two LLaMA-7B shapes, one call per batch size, in this
     # order (the counter record matches dispatches to these calls by order)
-    for n, k, m in W4A16_COUNTER_CALLS:
+    for n, k, m, ws in W4A16_COUNTER_CALLS:
         qw = torch.randint(-2**31, 2**31 - 1, (n, k // 8), dtype=torch.int32, device=dev,
                            generator=g)
         sc = (0.01 * torch.rand(n, k // 128, device=dev, generator=g) + 1e-3).half()
         s16 = (1.0 + torch.rand(k, device=dev, generator=g)).half()
         A = torch.randn(m, k, device=dev, generator=g).half()
-        awq.w4a16_gemm(A, qw, sc, s16)
+        if ws:
+            wsp = torch.empty(max(1, awq.w4a16_gemm_workspace_bytes(m, n, k)), dtype=torch.uint8,
+                              device=dev)
+            awq.w4a16_gemm_ws(A, qw, sc, s16, workspace=wsp)
+        else:
+            awq.w4a16_gemm(A, qw, sc, s16)
         torch.cuda.synchronize()
     log("w4a16 calls done")
 
@@ -221,9 +226,13 @@ def ceiling_pass(sizes=(1 << 30, M_ * K_ * 2, N_GRID * N_ * K_ * 2), reps=20, ec
     return out
 
 
-# (n, k, m) of the W4A16 calls of the counter pass
-W4A16_COUNTER_CALLS = [(4096, 4096, 1), (4096, 4096, 16), (4096, 4096, 64), (4096, 4096, 512),
-                       (11008, 4096, 1), (11008, 4096, 4), (11008, 4096, 16)]
+# (n, k, m, through w4a16_gemm_ws) of the W4A16 calls of the counter pass; a call on K slices
+# is two dispatches (the slices, then their sum)
+W4A16_COUNTER_CALLS = [(4096, 4096, 1, False), (4096, 4096, 16, False), (4096, 4096, 64, False),
+                       (4096, 4096, 64, True), (4096, 4096, 128, True), (4096, 4096, 512, False),
+                       (11008, 4096, 1, False), (11008, 4096, 4, False), (11008, 4096, 16, False),
+                       (11008, 4096, 64, True)]
+W4A16_SUM_KERNELS = ("w4a16_splitk_reduce_kernel", "w4a16_sum_slices_kernel")
 
 
 def log(*a):
@@ -291,6 +300,7 @@ def record_counters(ctr_dir):
     w4_calls = iter(W4A16_COUNTER_CALLS)
     rows, kernels = [], {}
     seen_w4 = 0
+    call_label = ""
     for i in sorted(tnames):
         n = short(tnames[i])
         if "awq" not in tnames[i] and i != big:
@@ -308,9 +318,12 @@ def record_counters(ctr_dir):
         if n == "gram_gemm_kernel":
             # X^T read once plus the fp32 partial tiles written, one 256 x 256 tile per workgroup
             a_bytes = (-(-M_ // 128) * 128) * K_ * 2 + (grid[i] // 256) * 256 * 256 * 4
-        if n.startswith("w4a16") and seen_w4 >= 1:
-            nn, kk, mm = next(w4_calls)
-            label = f"w4a16 {nn}x{kk} M={mm}: {n}"
+        if n.startswith(W4A16_SUM_KERNELS):
+            label = f"{call_label}: {n}"           # the second dispatch of a call on K slices
+        elif n.startswith("w4a16") and seen_w4 >= 1:
+            nn, kk, mm, ws = next(w4_calls)
+            call_label = f"w4a16{'_ws' if ws else ''} {nn}x{kk} M={mm}"
+            label = f"{call_label}: {n}"
             a_bytes = nn * kk // 2 + nn * (kk // 128) * 2 + kk * 2 + mm * kk * 2 + mm * nn * 2
         if n.startswith("w4a16"):
             seen_w4 += 1                           # the first is the path pass's decode call
@@ -326,7 +339,8 @@ def record_counters(ctr_dir):
     cmds = [f"rocprofv3 {v} --output-format csv -d <dir>/{k} -o t -- python3 bench.py --mode traffic"
             for k, v in COUNTER_PASSES.items()]
     rec = {"workload": f"{N_}x{K_} fp16 layer, {M_} fp16 tokens, {N_GRID} alpha points; "
-                       "W4A16 calls " + ", ".join(f"{n}x{k} M={m}" for n, k, m in W4A16_COUNTER_CALLS),
+                       "W4A16 calls " + ", ".join(f"{'w4a16_gemm_ws' if w else 'w4a16_gemm'} {n}x{k} M={m}"
+                                      for n, k, m, w in W4A16_COUNTER_CALLS),
            "read_factor": rf, "write_factor": wf, "commands": cmds, "kernels": kernels}
     with open(TRAFFIC_RECORD, "w") as f:
         json.dump(rec, f, indent=1)
@@ -361,13 +375,13 @@ def record_counters(ctr_dir):
 
 
 # ---------------------------------------------------------------------------------------------
-def w4a16_time(awq, torch, n, k, ms, group=128, zero_point=False, ws=True):
+def w4a16_time(awq, torch, n, k, ms, group=128, zero_point=False, ws=True, with_s=True):
     """Time W4A16 at the batch sizes `ms` on an [n, k] weight over rotated copies with HIP events.
     `us` is the GPU time per call: one pass over every copy is captured in a HIP graph and
     replayed (the result of a replay is checked against the eager calls), so the host's launch
     rate does not enter; `us_eager` is the same pass issued call by call from Python.
-    ws: w4a16_gemm_ws with one workspace (K split over workgroups for M <= 64), else
-    w4a16_gemm."""
+    ws: w4a16_gemm_ws with one workspace (K split over workgroups where it pays), else
+    w4a16_gemm. with_s False: s16 = NULL (s folded into the producer of A)."""
     import numpy as np
     import workloads
     st = torch.cuda.current_stream()
@@ -390,7 +404,7 @@ def w4a16_time(awq, torch, n, k, ms, group=128, zero_point=False, ws=True):
     qws = [torch.from_numpy(qw.view(np.int32)).cuda() for _ in range(copies)]
     scs = [torch.from_numpy(sc).cuda() for _ in range(copies)]
     zds = [torch.from_numpy(zs).cuda() for _ in range(copies)] if zs is not None else None
-    s_d = torch.from_numpy(s).cuda()
+    s_d = torch.from_numpy(s).cuda() if with_s else None
     for m in ms:
         A = torch.from_numpy(workloads.w4a16_activations(m, k, config=4)).cuda()
         Y = torch.empty((m, n), dtype=torch.float16, device="cuda")
@@ -425,7 +439,7 @@ def w4a16_time(awq, torch, n, k, ms, group=128, zero_point=False, ws=True):
             raise RuntimeError(f"W4A16 graph replay differs from the eager result (M={m})")
         us = elapsed_us(graph.replay, 3) / copies
         nbytes = (n * k // 2 + n * (k // group) * 2 + (n * (k // group) if zero_point else 0) +
-                  k * 2 + m * k * 2 + m * n * 2)
+                  (k * 2 if with_s else 0) + m * k * 2 + m * n * 2)
         flops = 2.0 * m * n * k
         rec = {"n": n, "k": k, "m": m, "entry": "w4a16_gemm_ws" if ws else "w4a16_gemm",
                "us": round(us, 3), "us_eager": round(us_eager, 3),
@@ -434,6 +448,8 @@ def w4a16_time(awq, torch, n, k, ms, group=128, zero_point=False, ws=True):
                "tflops": round(flops / us / 1e6, 2)}
         if group != 128 or zero_point:
             rec.update({"group": group, "zero_point": zero_point})
+        if not with_s:
+            rec["s16"] = None
         if m >= 512:
             rec["mfma_frac"] = round(flops / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4)
         out.append(rec)
@@ -554,11 +570,11 @@ def layer_sweep(awq, torch, reps, cpu_parts):
 
 
 def w4a16_sweep(awq, torch):
-    """The symmetric group-128 kernel at the batch sizes 1, 4, 16, 64, 512 for 4096x4096 and
-    11008x4096."""
+    """w4a16_gemm_ws, symmetric codes in groups of 128, at the batch sizes 1, 4, 16, 64, 128,
+    512 for 4096x4096 and 11008x4096."""
     out = []
     for (n, k) in ((4096, 4096), (11008, 4096)):
-        out += w4a16_time(awq, torch, n, k, (1, 4, 16, 64, 512))
+        out += w4a16_time(awq, torch, n, k, (1, 4, 16, 64, 128, 512))
     return out
 
 

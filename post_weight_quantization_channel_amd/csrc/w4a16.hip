@@ -65,9 +65,10 @@ __host__ __device__ constexpr int64_t w4a16_tiled_tables(int64_t K, int GS, bool
 // natural order: a code word is decoded in pairs (2j, 2j + 1), byte j of the word spread to bytes
 // 0 and 2 (v_perm), then (t & 0x00F0000F) | 0x64006400 is the fp16 pair (1024 + u_2j,
 // 1024 + 16 u_2j+1) and one packed fma with (1, 1/16) and -(1032, 72) (or -(1024 + z, 64 + z))
-// gives (c(q_2j), c(q_2j+1)) exactly; times the r pair, rounded once.
+// gives (c(q_2j), c(q_2j+1)) exactly; times the r pair, rounded once (without s the exact pair is
+// the operand).
 
-template <int GS, bool ZP, bool HAS_S>
+template <int GS, bool ZP, bool HAS_S, int NBW>
 __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
     const uint16_t* __restrict__ A, int64_t M, int64_t N, int64_t K,
     const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales16,
@@ -88,7 +89,9 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  constexpr int MBW = 8 / NBW;               // 16-row blocks of m per wave
+  constexpr int WAVES_N = 4 / NBW;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int li = lane & 15, lg = lane >> 4;
   const int64_t tilesN = (N + TBN - 1) / TBN;
   int64_t bl = blockIdx.x;
@@ -100,8 +103,9 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
   const int64_t kb0 = (int64_t)split * KB;
   const int64_t groups = (K / 128 - kb0 < KB) ? K / 128 - kb0 : KB;   // this slice's steps
 
-  // ---- tables: r_k = fp16(2^b / s_k) in natural order, 2^-b per block, steps, zero points ----
-  for (int64_t k8 = tid; k8 < groups * 16; k8 += 256) {
+  // ---- tables: r_k = fp16(2^b / s_k) in natural order, 2^-b per block (with s), steps, zero
+  // points ------------------------------------------------------------------------------------
+  for (int64_t k8 = tid; HAS_S && k8 < groups * 16; k8 += 256) {
     float inv[8];
     float mx = 0.0f;
     if (HAS_S) {
@@ -153,16 +157,16 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
   // this wave's code rows
   const uint32_t* wr[2];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int64_t n = n0 + 32 * wn + 16 * nb + li;
+  for (int nb = 0; nb < NBW; ++nb) {
+    const int64_t n = n0 + 16 * NBW * wn + 16 * nb + li;
     wr[nb] = qweight + (n < N ? n : N - 1) * (K / 8) + kb0 * 16;
   }
   struct Codes {
-    uint32_t w[2][4];   // [nb][kk]: the word MFMA kk of the step takes
+    uint32_t w[NBW][4];   // [nb][kk]: the word MFMA kk of the step takes
   };
   auto load_codes = [&](int64_t g, Codes& c) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NBW; ++nb) {
       if (GS == 128) {
         const uint4 v = *reinterpret_cast<const uint4*>(wr[nb] + g * 16 + 4 * lg);
         c.w[nb][0] = v.x; c.w[nb][1] = v.y; c.w[nb][2] = v.z; c.w[nb][3] = v.w;
@@ -173,11 +177,11 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
     }
   };
 
-  floatx4 acc[2][4];
+  floatx4 acc[NBW][MBW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NBW; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < MBW; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   constexpr int kKKPerGroup = (GS == 64) ? 2 : 4;
   // the fp16 exponent bits of the decode, held in a register so that the mask-and-insert is one
   // v_and_or_b32 (a VALU instruction reads one scalar or literal operand)
@@ -185,31 +189,33 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
   asm volatile("" : "+v"(magic));
   auto compute = [&](int64_t g, int st, const Codes& c) {
     const char* sa = smem + st * kAStage;
-    const float bs = bfac[g];
+    // without s the weight operand is c(q) itself (exact) and no block scale applies
+    const float bs = HAS_S ? bfac[g] : 1.0f;
 #pragma unroll
     for (int h = 0; h < 4 / kKKPerGroup; ++h) {
       const int64_t gq = (GS == 64) ? 2 * g + h : g;
-      half2_t sub2[2];
+      half2_t sub2[NBW];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NBW; ++nb) {
         // subtrahends of the decoded pair (1024 + u, 64 + u'): 1032 and 72 for signed codes
         // (biased by the xor), 1024 + z and 64 + z with zero points
-        const float z = ZP ? (float)z_lds[gq * TBN + 32 * wn + 16 * nb + li] : 8.0f;
+        const float z = ZP ? (float)z_lds[gq * TBN + 16 * NBW * wn + 16 * nb + li] : 8.0f;
         sub2[nb] = half2_t{(_Float16)(1024.0f + z), (_Float16)(64.0f + z)};
       }
-      floatx4 part[2][4];
+      floatx4 part[NBW][MBW];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NBW; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) part[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < MBW; ++j) part[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = h * kKKPerGroup; kk < (h + 1) * kKKPerGroup; ++kk) {
         const int ch = (GS == 128) ? 4 * lg + kk : 4 * kk + lg;   // the lane's 8-channel chunk
-        const uint4 rv = *reinterpret_cast<const uint4*>(rtab + g * 128 + ch * 8);
+        const uint4 rv = HAS_S ? *reinterpret_cast<const uint4*>(rtab + g * 128 + ch * 8)
+                               : make_uint4(0u, 0u, 0u, 0u);
         const uint32_t rp[4] = {rv.x, rv.y, rv.z, rv.w};
-        half8_t wf[2], af[4];
+        half8_t wf[NBW], af[MBW];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < NBW; ++nb) {
           const uint32_t x = ZP ? c.w[nb][kk] : (c.w[nb][kk] ^ 0x88888888u);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -220,29 +226,29 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
             const half2_t q = __builtin_elementwise_fma(
                 __builtin_bit_cast(half2_t, bits), half2_t{(_Float16)1.0f, (_Float16)0.0625f},
                 -sub2[nb]);
-            const half2_t wv = q * __builtin_bit_cast(half2_t, rp[j]);
+            const half2_t wv = HAS_S ? q * __builtin_bit_cast(half2_t, rp[j]) : q;
             wf[nb][2 * j] = wv[0];
             wf[nb][2 * j + 1] = wv[1];
           }
         }
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          af[mb] = *reinterpret_cast<const half8_t*>(sa + tswz(wm * 64 + mb * 16 + li, ch));
+        for (int mb = 0; mb < MBW; ++mb)
+          af[mb] = *reinterpret_cast<const half8_t*>(sa + tswz(wm * 16 * MBW + mb * 16 + li, ch));
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
+          for (int mb = 0; mb < MBW; ++mb)
             part[nb][mb] =
                 __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[nb], af[mb], part[nb][mb], 0, 0, 0);
       }
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const uint2 sr = *reinterpret_cast<const uint2*>(st_lds + gq * TBN + wn * 32 + nb * 16 +
+      for (int nb = 0; nb < NBW; ++nb) {
+        const uint2 sr = *reinterpret_cast<const uint2*>(st_lds + gq * TBN + wn * 16 * NBW + nb * 16 +
                                                          4 * lg);
         const float sc[4] = {h2f((uint16_t)(sr.x & 0xFFFFu)) * bs, h2f((uint16_t)(sr.x >> 16)) * bs,
                              h2f((uint16_t)(sr.y & 0xFFFFu)) * bs, h2f((uint16_t)(sr.y >> 16)) * bs};
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             acc[nb][mb][r] = __builtin_fmaf(part[nb][mb][r], sc[r], acc[nb][mb][r]);
@@ -272,11 +278,11 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
   if (partials) {   // one of several K slices: fp32 partial [m][n] of slice `split`
     float* P = partials + split * slice_stride;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NBW; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t m = m0 + wm * 64 + j * 16 + li;
-        const int64_t nb = n0 + wn * 32 + i * 16 + 4 * lg;
+      for (int j = 0; j < MBW; ++j) {
+        const int64_t m = m0 + wm * 16 * MBW + j * 16 + li;
+        const int64_t nb = n0 + wn * 16 * NBW + i * 16 + 4 * lg;
         if (m < M) {
           if (nb + 3 < N && ((N & 3) == 0)) {
             *reinterpret_cast<floatx4*>(P + m * N + nb) = acc[i][j];
@@ -290,11 +296,11 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NBW; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t m = m0 + wm * 64 + j * 16 + li;
-      const int64_t nb = n0 + wn * 32 + i * 16 + 4 * lg;
+    for (int j = 0; j < MBW; ++j) {
+      const int64_t m = m0 + wm * 16 * MBW + j * 16 + li;
+      const int64_t nb = n0 + wn * 16 * NBW + i * 16 + 4 * lg;
       if (m < M) {
         if (nb + 3 < N && ((N & 3) == 0)) {
           const uint32_t lo = (uint32_t)f2h(acc[i][j][0]) | ((uint32_t)f2h(acc[i][j][1]) << 16);
@@ -370,11 +376,16 @@ static hipError_t w4a16_tiled(const uint16_t* A, int64_t M, int64_t N, int64_t K
   const size_t dyn = (size_t)w4a16_tiled_tables(p.KB * 128, GS, ZP);
   const unsigned grid = (unsigned)(p.tiles * p.S);
   float* P = p.S > 1 ? partials : nullptr;
+  // waves of 64 x 32 (two 16-row weight blocks each) for symmetric groups of 128; with groups of
+  // 64 or zero points, whose per-group work doubles the unpacking cost, waves of 128 x 16 (each
+  // wave unpacks only its own 16 rows; 4096 x 4096 at M = 512: 45.7 vs 57.3 us, while symmetric
+  // groups of 128 run 38.8 vs 37.6 us that way)
+  constexpr int NBW = (GS == 64 || ZP) ? 1 : 2;
   if (s16)
-    w4a16_tiled_kernel<GS, ZP, true><<<grid, 256, dyn, stream>>>(
+    w4a16_tiled_kernel<GS, ZP, true, NBW><<<grid, 256, dyn, stream>>>(
         A, M, N, K, qweight, scales16, zeros, s16, Y, p.tiles, (int)p.KB, P, p.stride);
   else
-    w4a16_tiled_kernel<GS, ZP, false><<<grid, 256, dyn, stream>>>(
+    w4a16_tiled_kernel<GS, ZP, false, NBW><<<grid, 256, dyn, stream>>>(
         A, M, N, K, qweight, scales16, zeros, s16, Y, p.tiles, (int)p.KB, P, p.stride);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;

@@ -191,13 +191,15 @@ __global__ __launch_bounds__(kThreads, (MB == 1 && TI == 1) ? 6 : 1) void w4a16_
 #pragma unroll
       for (int v = 0; v < 4; ++v) {                          // word v: channels kbase + 8v ..
         const uint32_t x = ZP ? words[v] : (words[v] ^ 0x88888888u);
-        const uint4 rv = *reinterpret_cast<const uint4*>(rtab + kbase + 8 * v);
+        const uint4 rv = HAS_S ? *reinterpret_cast<const uint4*>(rtab + kbase + 8 * v)
+                               : make_uint4(0u, 0u, 0u, 0u);
         const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+          // without s the operand is c(q) itself (exact) and no block scale applies
           const uint32_t bits = ((x >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-          const half2_t q = (__builtin_bit_cast(half2_t, bits) - sub2) *
-                            __builtin_bit_cast(half2_t, rw[j]);
+          const half2_t d = __builtin_bit_cast(half2_t, bits) - sub2;
+          const half2_t q = HAS_S ? d * __builtin_bit_cast(half2_t, rw[j]) : d;
           wf[v][2 * j] = q[0];
           wf[v][2 * j + 1] = q[1];
         }
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(kThreads, (MB == 1 && TI == 1) ? 6 : 1) void w4a16_
       // 2^-b; with GS = 64 the two halves of the block have their own steps, so each MFMA is
       // done twice with the A operand of the other half's lanes (lg < 2 hold channels 0..63,
       // lg >= 2 channels 64..127) zeroed
-      const float bs = bfac[g];
+      const float bs = HAS_S ? bfac[g] : 1.0f;
       const int64_t gs0 = (GS == 64) ? 2 * g : g;
       floatx4 st0 = *reinterpret_cast<const floatx4*>(step_lds + gs0 * kRows + 4 * lg);
       floatx4 st1 = st0;

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void w4a16_splitk_kernel(
   for (int b = 0; b < kSkStages && b < nkb; ++b) issue(b);
 
   // ---- tables: r_k = fp16(2^b / s_k) in natural order, 2^-b per block, steps, zero points ----
-  for (int k8 = tid; k8 < nkb * 16; k8 += 256) {
+  for (int k8 = tid; HAS_S && k8 < nkb * 16; k8 += 256) {
     float inv[8];
     float mx = 0.0f;
     if (HAS_S) {
@@ -202,7 +202,8 @@ __global__ __launch_bounds__(256) void w4a16_splitk_kernel(
   auto compute = [&](int b) {
     const char* sa = smem + (b % kSkStages) * kStageB;
     const char* rowp = sa + kAStageB + (16 * wave + li) * 64;   // this lane's code row
-    const float bs = bfac[b];
+    // without s the weight operand is c(q) itself (exact) and no block scale applies
+    const float bs = HAS_S ? bfac[b] : 1.0f;
     // Which channels a lane holds: G = 128: MFMA kk takes word 4 lg + kk (channels
     // 32 lg + 8 kk ..); G = 64: word 4 kk + lg, so MFMAs 0, 1 cover the block's first group
     uint32_t cw[4];
@@ -224,7 +225,8 @@ __global__ __launch_bounds__(256) void w4a16_splitk_kernel(
 #pragma unroll
       for (int kk = h * kKKPerGroup; kk < (h + 1) * kKKPerGroup; ++kk) {
         const int ch = (GS == 128) ? 4 * lg + kk : 4 * kk + lg;   // the lane's 8-channel chunk
-        const uint4 rv = *reinterpret_cast<const uint4*>(rtab + b * 128 + ch * 8);
+        const uint4 rv = HAS_S ? *reinterpret_cast<const uint4*>(rtab + b * 128 + ch * 8)
+                               : make_uint4(0u, 0u, 0u, 0u);
         const uint32_t rp[4] = {rv.x, rv.y, rv.z, rv.w};
         const uint32_t x = ZP ? cw[kk] : (cw[kk] ^ 0x88888888u);
         half8_t wf;
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(256) void w4a16_splitk_kernel(
           const half2_t q = __builtin_elementwise_fma(
               __builtin_bit_cast(half2_t, bits), half2_t{(_Float16)1.0f, (_Float16)0.0625f},
               -sub2);
-          const half2_t wv = q * __builtin_bit_cast(half2_t, rp[j]);
+          const half2_t wv = HAS_S ? q * __builtin_bit_cast(half2_t, rp[j]) : q;
           wf[2 * j] = wv[0];
           wf[2 * j + 1] = wv[1];
         }
