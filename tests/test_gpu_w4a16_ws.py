@@ -132,3 +132,32 @@ def test_w4a16_ws_reuse_and_determinism(awq):
     A = workloads.w4a16_activations(m, k, config=4, j=1)
     with pytest.raises(_lib.AwqError):
         awq.w4a16_gemm_ws(dev(A), dev(qw.view(np.int32)), dev(sc), dev(s), workspace=ws[:1024])
+
+
+def _fuzz_cases(n_cases=16, seed=2026):
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n_cases):
+        n = int(g.choice([int(g.integers(1, 300)), int(g.integers(300, 20000))]))
+        k = 128 * int(g.integers(1, 97))
+        m = int(g.choice([int(g.integers(1, 65)), int(g.integers(65, 300))]))
+        out.append((i, n, k, m, int(g.choice([64, 128])), bool(g.integers(0, 2)),
+                    bool(g.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("i,n,k,m,group,zp,with_s", _fuzz_cases())
+def test_w4a16_ws_fuzz(awq, i, n, k, m, group, zp, with_s):
+    """Seeded random shapes (ragged N and M, K up to 12288), groups, codes and s: both entry
+    points against the oracle on the first 512 rows."""
+    qw, sc, s = workloads.w4a16_random_artifacts(n, k, group=group, config=4, j=100 + i)
+    z = workloads.w4a16_random_zeros(n, k, group=group, config=4, j=100 + i) if zp else None
+    A = workloads.w4a16_activations(m, k, config=4, j=100 + i)
+    s_eff = s if with_s else np.ones_like(s)
+    say("w4a16 fuzz", i, (m, k), "x", (n, k), "group", group, "zero point", zp, "s", with_s,
+        "workspace", awq.w4a16_gemm_workspace_bytes(m, n, k, group))
+    args = (dev(A), dev(qw.view(np.int32)), dev(sc), dev(s) if with_s else None)
+    kw = dict(group=group, zeros=None if z is None else dev(z))
+    rows = slice(0, min(n, 512))
+    _check(awq.w4a16_gemm_ws(*args, **kw), A, qw, sc, s_eff, group=group, z=z, rows=rows)
+    _check(awq.w4a16_gemm(*args, **kw), A, qw, sc, s_eff, group=group, z=z, rows=rows)
