@@ -84,7 +84,8 @@ __global__ __launch_bounds__(256) void absmax_kernel(const void* __restrict__ W,
     load8_f32<DT>(reinterpret_cast<const char*>(W) + c * 8 * ES, v);
     fold(c, v);
   }
-  // wave maximum, then workgroup maximum, then one atomic per workgroup (max is order-free)
+  // wave maximum, then workgroup maximum, then at most one atomic per workgroup (max is
+  // order-free)
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   __shared__ float wmax[4];
   if (__lane_id() == 0) wmax[threadIdx.x >> 6] = m;
@@ -92,7 +93,12 @@ __global__ __launch_bounds__(256) void absmax_kernel(const void* __restrict__ W,
   __syncthreads();
   if (threadIdx.x == 0) {
     const float bm = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    atomicMax(&ctrl->absmax_bits, __float_as_uint(bm));
+    // Atomics on one address serialise; the maximum only grows, so a workgroup whose value
+    // does not exceed one the maximum already held (a device-scope read, parallel across
+    // workgroups) has nothing to add.
+    const uint32_t seen =
+        __hip_atomic_load(&ctrl->absmax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__float_as_uint(bm) > seen) atomicMax(&ctrl->absmax_bits, __float_as_uint(bm));
   }
 }
 
@@ -331,15 +337,20 @@ __global__ __launch_bounds__(256) void finalize_kernel(
   }
   __syncthreads();
   if (!is_last) return;
+  if (tid == 0) __threadfence();
+  __syncthreads();
+  // every grid point's loss at once (device-scope loads, one per thread: a serial scan of
+  // n_grid dependent reads from memory took most of this kernel's ~20 us), then the scan
+  for (int j = tid; j < n_grid; j += 256)
+    red[j] = __hip_atomic_load(losses + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
   if (tid == 0) {
-    __threadfence();
-    volatile double* L = losses;
     int b = 0;
     bool bad = false;
     for (int j = 0; j < n_grid; ++j) {
-      const double v = L[j];
+      const double v = red[j];
       bad |= !isfinite(v);
-      if (v < L[b]) b = j;
+      if (v < red[b]) b = j;
     }
     *best = b;
     sbest = b;
