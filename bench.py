@@ -27,7 +27,8 @@ fields it carries
                 and loss kernels), the pack, and W4A16 at M = 1 and 512 on 4096x4096;
   hbm_stages    the bandwidth-bound kernels: algorithmic bytes, GB/s, fraction of 8 TB/s;
   w4a16         w4a16_gemm_ws at the batch sizes 1, 4, 16, 64, 128, 512 for 4096x4096 and
-                11008x4096, over rotated weight copies (> 256 MB, so HBM and not the
+                11008x4096 (and 1, 16 for 8192x8192, 28672x8192, 8192x28672), over rotated
+                weight copies (> 256 MB, so HBM and not the
                 Infinity Cache is measured), replayed from a HIP graph (GPU time per call;
                 `us_eager`: the same calls issued one by one from Python): GB/s and fraction
                 of 8 TB/s (TFLOP/s and MFMA fraction at M = 512);
@@ -571,10 +572,13 @@ def layer_sweep(awq, torch, reps, cpu_parts):
 
 def w4a16_sweep(awq, torch):
     """w4a16_gemm_ws, symmetric codes in groups of 128, at the batch sizes 1, 4, 16, 64, 128,
-    512 for 4096x4096 and 11008x4096."""
+    512 for 4096x4096 and 11008x4096, and at 1 and 16 for the 70B-class shapes 8192x8192,
+    28672x8192 and 8192x28672 (decode GB/s where the weight is large enough to stream)."""
     out = []
     for (n, k) in ((4096, 4096), (11008, 4096)):
         out += w4a16_time(awq, torch, n, k, (1, 4, 16, 64, 128, 512))
+    for (n, k) in ((8192, 8192), (28672, 8192), (8192, 28672)):
+        out += w4a16_time(awq, torch, n, k, (1, 16))
     return out
 
 
