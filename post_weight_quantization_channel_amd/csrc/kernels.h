@@ -165,7 +165,8 @@ hipError_t launch_w4a16_splitk(const uint16_t* A, int64_t M, int64_t N, int64_t 
 // idle: S slices of KB steps, fp32 partials [S][M][N] (slice stride `stride` floats) in a
 // workspace of ws_bytes, added by a second kernel
 struct W4a16TiledPlan {
-  int64_t tiles;     // 128 x 64 output tiles
+  int tbm;           // batch rows per tile (128 or 64)
+  int64_t tiles;     // tbm x 64 output tiles
   int64_t S;         // K slices
   int64_t KB;        // 128-channel steps per slice
   int64_t stride;    // M N rounded up to a multiple of 4

@@ -25,7 +25,9 @@ namespace awq {
 // ---------------------------------------------------------------------------------------------
 // Larger batches: a tiled MFMA GEMM. Workgroup tile 128 (batch rows m) x 64 (weight rows n), one
 // 128-channel block of K per step, 4 waves of 64 x 32 (2 x 2), each a grid of 4 (m) x 2 (n)
-// v_mfma_f32_16x16x32_f16 blocks (weights as the A operand, activations as B).
+// v_mfma_f32_16x16x32_f16 blocks (weights as the A operand, activations as B); for groups of 64
+// or zero points 4 waves of 128 x 16; on small grids tiles of 64 batch rows (waves of 32 x 32 or
+// 64 x 16).
 //
 // The activation tile of a step (128 rows x 256 B, 8 loads of 1 KiB per wave) is moved into LDS
 // by the buffer unit (buffer_load ... lds), so that no load's result goes through a register and
@@ -44,12 +46,11 @@ namespace awq {
 // Rows past M read as zeros (the buffer range ends at the last valid row), rows past N read row
 // N - 1, and neither's outputs are stored.
 namespace {
-constexpr int TBM = 128, TBN = 64, TBK = 128;
+constexpr int TBN = 64, TBK = 128;
 __device__ __forceinline__ int tswz(int row, int chunk) {   // byte offset inside a 256-byte row
   return row * (TBK * 2) + ((chunk ^ (row & 15)) << 4);
 }
-constexpr int kAStage = TBM * TBK * 2;                // 32 KiB of activations per step
-constexpr int kRwSmem = 2 * kAStage;                  // two stages: 64 KiB
+constexpr int kRwSmem = 2 * 128 * TBK * 2;            // two stages of 128 rows: 64 KiB
 }  // namespace
 
 // bytes of the dynamic tables: fp16 r [K], fp32 2^-b [K/128], fp16 steps [K/GS][64], (ZP) uint8
@@ -68,14 +69,16 @@ __host__ __device__ constexpr int64_t w4a16_tiled_tables(int64_t K, int GS, bool
 // gives (c(q_2j), c(q_2j+1)) exactly; times the r pair, rounded once (without s the exact pair is
 // the operand).
 
-template <int GS, bool ZP, bool HAS_S, int NBW>
+template <int GS, bool ZP, bool HAS_S, int NBW, int BMT>
 __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
     const uint16_t* __restrict__ A, int64_t M, int64_t N, int64_t K,
     const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales16,
     const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ s16,
     uint16_t* __restrict__ Y, int64_t tiles, int KB, float* __restrict__ partials,
     int64_t slice_stride) {
-  __shared__ __attribute__((aligned(1024))) char smem[kRwSmem];
+  // BMT batch rows per tile (128, or 64 where two workgroups per CU beat one)
+  constexpr int kStage = BMT * TBK * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
   extern __shared__ __attribute__((aligned(16))) char dyn[];
   // tables of this workgroup's K slice (KB blocks from kb0)
   const int64_t ngr = K / GS;
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int MBW = 8 / NBW;               // 16-row blocks of m per wave
+  constexpr int MBW = BMT / (16 * NBW);      // 16-row blocks of m per wave
   constexpr int WAVES_N = 4 / NBW;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int li = lane & 15, lg = lane >> 4;
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
   if ((gridDim.x & 7u) == 0) bl = (int64_t)(blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   const int split = (int)(bl / tiles);     // K slice (slice-major: one XCD shares slices)
   const int64_t tile = bl % tiles;
-  const int64_t m0 = (tile / tilesN) * TBM;
+  const int64_t m0 = (tile / tilesN) * BMT;
   const int64_t n0 = (tile % tilesN) * TBN;
   const int64_t kb0 = (int64_t)split * KB;
   const int64_t groups = (K / 128 - kb0 < KB) ? K / 128 - kb0 : KB;   // this slice's steps
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
   }
 
   // ---- activation stages ---------------------------------------------------------------------
-  const int64_t arows = (M - m0 < TBM) ? M - m0 : TBM;
+  const int64_t arows = (M - m0 < BMT) ? M - m0 : BMT;
   const rsrc_t ra = make_rsrc(A + m0 * K, (uint32_t)(arows * K * 2));
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   uint32_t avoff[4];
@@ -148,9 +151,10 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
   }
   auto issue = [&](int64_t g, int st) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t lds = lds0 + (uint32_t)(st * kAStage) + (uint32_t)((32 * wave + 4 * j) * 256);
-      const uint32_t so = (uint32_t)((32 * wave + 4 * j) * K * 2) + (uint32_t)((kb0 + g) * 256);
+    for (int j = 0; j < BMT / 16; ++j) {   // BMT / 4 rows per wave, 4 per load
+      const int r0 = (BMT / 4) * wave + 4 * j;
+      const uint32_t lds = lds0 + (uint32_t)(st * kStage) + (uint32_t)(r0 * 256);
+      const uint32_t so = (uint32_t)(r0 * K * 2) + (uint32_t)((kb0 + g) * 256);
       buffer_load16_lds_so(ra, lds, avoff[j & 3], so);
     }
   };
@@ -188,7 +192,7 @@ __global__ __launch_bounds__(256) void w4a16_tiled_kernel(
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(magic));
   auto compute = [&](int64_t g, int st, const Codes& c) {
-    const char* sa = smem + st * kAStage;
+    const char* sa = smem + st * kStage;
     // without s the weight operand is c(q) itself (exact) and no block scale applies
     const float bs = HAS_S ? bfac[g] : 1.0f;
 #pragma unroll
@@ -348,7 +352,13 @@ __global__ __launch_bounds__(256) void w4a16_sum_slices_kernel(const float* __re
 
 W4a16TiledPlan w4a16_tiled_plan(int64_t M, int64_t N, int64_t K, bool split) {
   W4a16TiledPlan p{};
-  p.tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
+  // Tiles of 128 batch rows; without slices and with at most 128 such tiles (half the CUs or
+  // fewer busy), tiles of 64 rows, two or more workgroups per CU (graph replay: 4096 x 4096 at
+  // M = 128 30.4 vs 36.6 us, M = 256 31.2 vs 36.0, 4096 x 11008 at M = 128 74.4 vs 91.8; at 172
+  // tiles, 11008 x 4096 at M = 128, 41.2 vs 38.5, and with slices 64 rows lose everywhere)
+  const int64_t tiles128 = ((M + 127) / 128) * ((N + TBN - 1) / TBN);
+  p.tbm = (!split && tiles128 <= 128) ? 64 : 128;
+  p.tiles = ((M + p.tbm - 1) / p.tbm) * ((N + TBN - 1) / TBN);
   const int64_t nblk = K / 128;
   int64_t S = 1;
   if (split && p.tiles < 256) {
@@ -381,12 +391,15 @@ static hipError_t w4a16_tiled(const uint16_t* A, int64_t M, int64_t N, int64_t K
   // wave unpacks only its own 16 rows; 4096 x 4096 at M = 512: 45.7 vs 57.3 us, while symmetric
   // groups of 128 run 38.8 vs 37.6 us that way)
   constexpr int NBW = (GS == 64 || ZP) ? 1 : 2;
-  if (s16)
-    w4a16_tiled_kernel<GS, ZP, true, NBW><<<grid, 256, dyn, stream>>>(
-        A, M, N, K, qweight, scales16, zeros, s16, Y, p.tiles, (int)p.KB, P, p.stride);
-  else
-    w4a16_tiled_kernel<GS, ZP, false, NBW><<<grid, 256, dyn, stream>>>(
-        A, M, N, K, qweight, scales16, zeros, s16, Y, p.tiles, (int)p.KB, P, p.stride);
+#define AWQ_TT(HS_, BM_)                                                                         \
+  w4a16_tiled_kernel<GS, ZP, HS_, NBW, BM_><<<grid, 256, dyn, stream>>>(                         \
+      A, M, N, K, qweight, scales16, zeros, s16, Y, p.tiles, (int)p.KB, P, p.stride)
+  if (s16) {
+    if (p.tbm == 64) AWQ_TT(true, 64); else AWQ_TT(true, 128);
+  } else {
+    if (p.tbm == 64) AWQ_TT(false, 64); else AWQ_TT(false, 128);
+  }
+#undef AWQ_TT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
   const int64_t MN = M * N;
