@@ -5,8 +5,9 @@ One step = one pass of the whole path over the LLaMA-7B-shaped attention project
 4096x4096, 65536 calibration tokens = 128 samples x 512 tokens, INT4, group 128, 20 alpha points):
     awq_stats_search_layer (s_X, then the alpha search) -> awq_pack_int4(s*) -> w4a16_gemm
     (decode, M = 1).
-The search runs in the Gram form (H = X^T X once, then one K x K contraction per grid point),
-and s_X comes out of the pass that transposes X for it (awq_act_stats alone is timed as context);
+The search runs in the Gram form (H = X^T X once, read straight from fp16 X, then one K x K
+contraction per grid point), and s_X comes from the statistics pass inside the same call
+(awq_act_stats alone is timed as context);
 --form direct times the direct form (X contracted with every error matrix) instead. Inputs are
 synthetic (seeded, see workloads/) and resident in HBM before the timed region.
 
@@ -94,7 +95,7 @@ CSRC = os.path.join(ROOT, "post_weight_quantization_channel_amd", "csrc")
 KERNEL_SOURCES = {
     "lossgemm_kernel": ("lossgemm.hip", "mfma_kloop.h", "device_common.h"),
     "gram_loss_kernel": ("gram.hip", "mfma_kloop.h", "device_common.h"),
-    "gram_gemm_kernel": ("gram.hip", "mfma_kloop.h", "device_common.h"),
+    "gram_gemm_x_kernel": ("gram.hip", "mfma_kloop.h", "device_common.h"),
 }
 
 
@@ -158,7 +159,7 @@ def traffic_pass():
     sx, flags = awq.act_stats(X)          # the statistics pass on its own
     for form in ("direct", "gram"):
         cfg = awq.AwqConfig(n_grid=N_GRID, form=form)
-        if form == "gram":                  # as in the step: s_X from the transpose pass
+        if form == "gram":                  # as in the step: s_X inside the search call
             _, res = awq.stats_search_layer(W, X, cfg, flags=flags)
         else:
             res = awq.search_layer(W, X, sx, cfg, flags=flags)
@@ -316,9 +317,9 @@ def record_counters(ctr_dir):
         busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024.0 / cyc if cyc else 0.0   # 1024 SIMDs
         label = n
         a_bytes = algo.get(n)
-        if n == "gram_gemm_kernel":
-            # X^T read once plus the fp32 partial tiles written, one 256 x 256 tile per workgroup
-            a_bytes = (-(-M_ // 128) * 128) * K_ * 2 + (grid[i] // 256) * 256 * 256 * 4
+        if n == "gram_gemm_x_kernel":
+            # X read once plus the fp32 partial tiles written, one 256 x 256 tile per workgroup
+            a_bytes = M_ * K_ * 2 + (grid[i] // 256) * 256 * 256 * 4
         if n.startswith(W4A16_SUM_KERNELS):
             label = f"{call_label}: {n}"           # the second dispatch of a call on K slices
         elif n.startswith("w4a16") and seen_w4 >= 1:
@@ -330,7 +331,7 @@ def record_counters(ctr_dir):
             seen_w4 += 1                           # the first is the path pass's decode call
         rows.append((i, label, grid[i], us, fb, wb, a_bytes, c["SQ_INSTS_MFMA"], busy,
                      cyc / us / 1e3 if us > 0 else 0.0))
-        if n in ("lossgemm_kernel", "gram_loss_kernel", "gram_gemm_kernel") and n not in kernels:
+        if n in ("lossgemm_kernel", "gram_loss_kernel", "gram_gemm_x_kernel") and n not in kernels:
             kernels[n] = {"fetch_kib": fetch[i]["FETCH_SIZE"], "write_kib": write[i]["WRITE_SIZE"],
                           "hbm_bytes_per_launch": int(fb + wb),
                           "algorithmic_bytes_per_launch": int(a_bytes),
@@ -675,7 +676,7 @@ def main():
     def step(prof):
         # prof: a dict for the per-kernel durations of the search (that call then blocks until
         # the search is done), or None (nothing blocks: the timed steps). s_X and the search are
-        # one call: in the Gram form the column sums come out of the pass that transposes X.
+        # one call.
         e0, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         e0.record(st)
         sx, res = awq.stats_search_layer(W, X, cfg, flags=flags, workspace=ws_search,
@@ -741,7 +742,7 @@ def main():
 
     if args.form == "gram":
         mfma = [mfma_rec("gram_loss_kernel", stages["loss"], gram_loss_flops(N_, K_, N_GRID)),
-                mfma_rec("gram_gemm_kernel", stages["gram_gemm"], gram_gemm_flops(M_, K_))]
+                mfma_rec("gram_gemm_x_kernel", stages["gram_gemm"], gram_gemm_flops(M_, K_))]
     else:
         mfma = [mfma_rec("lossgemm_kernel", stages["loss"], 2.0 * M_ * N_ * K_ * N_GRID)]
     roofline = max(mfma, key=lambda r: r["launch_ms"])
@@ -753,13 +754,8 @@ def main():
                            "bytes": N_ * K_ * 2 + N_GRID * N_ * K_ * 2},
         "pack": {"ms": round(pack_ms, 4), "bytes": N_ * K_ * 2 + N_ * K_ // 2 + N_ * K_ // 64},
     }
-    if args.form == "gram":
-        # X read once, X^T written, plus the statistics' chunk partials
-        other["x_transpose_and_stats"] = {
-            "ms": round(stages["x_prep"], 4),
-            "bytes": 2 * M_ * K_ * 2 + (-(-M_ // 256)) * K_ * 8}
-    else:
-        other["act_stats_in_search"] = {"ms": round(stages["x_prep"], 4), "bytes": M_ * K_ * 2}
+    # fp16 X: both forms read X as it is, so the search's first stage is the statistics pass
+    other["act_stats_in_search"] = {"ms": round(stages["x_prep"], 4), "bytes": M_ * K_ * 2}
     for v in other.values():
         v["gbs"] = round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)
         v["hbm_frac"] = round(v["gbs"] / HBM_PEAK_GBS, 4)
@@ -769,7 +765,6 @@ def main():
              for r in ceiling_pass(sizes=(M_ * K_ * 2, N_GRID * N_ * K_ * 2), reps=10, echo=False)}
     ceil_of = {"act_stats_standalone": ("copy", M_ * K_ * 2),
                "act_stats_in_search": ("copy", M_ * K_ * 2),
-               "x_transpose_and_stats": ("copy", M_ * K_ * 2),
                "quantize_stack": ("write", N_GRID * N_ * K_ * 2)}
     for k, v in other.items():
         if k in ceil_of:

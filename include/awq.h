@@ -200,8 +200,7 @@ awq_status awq_search_layers(const void* const* W, const int64_t* N, int32_t n_w
 
 /* ------------------------------------------------------------------------------------------
  * awq_stats_search_layers -- awq_act_stats followed by awq_search_layers on the same X, in one
- *   call: sx is an output, as in awq_stats_search_layer (identical to awq_act_stats's; in the
- *   Gram form with fp16 X the column sums come out of the pass that transposes X). Everything
+ *   call: sx is an output, as in awq_stats_search_layer (identical to awq_act_stats's). Everything
  *   else as awq_search_layers.
  * ---------------------------------------------------------------------------------------- */
 awq_status awq_stats_search_layers(const void* const* W, const int64_t* N, int32_t n_w,
@@ -230,7 +229,7 @@ awq_status awq_fold_scale(void* prev, awq_dtype dtype, int64_t rows, int64_t col
  * it BLOCKS the host until the stream has finished the search (it reads the events back).
  * stage_ms  host array of AWQ_SEARCH_STAGES floats (milliseconds), in the order
  *           scale table; X preparation (direct: X to fp16, 0 when X is fp16; Gram: transpose
- *           to fp16 X^T); X^T X (0 in the direct form); d and the correlation operand (0 in
+ *           to fp16 X^T, 0 when X is fp16: X^T X then reads X itself); X^T X (0 in the direct form); d and the correlation operand (0 in
  *           the direct form); max|W| (Gram: max|W d|); quantize + error stack; loss
  *           contraction; finalize.
  * Errors: as awq_search_layer; AWQ_ERR_NULL when stage_ms is NULL; AWQ_ERR_HIP when an event
@@ -250,8 +249,7 @@ awq_status awq_search_layer_profiled(const void* W, awq_dtype wdt, int64_t N, in
  *        tokens per chunk, reduced by the same final pass; with fp16 X these sums are exact,
  *        so their order does not matter, unless AWQ_FLAG_STATS_INEXACT is raised); the search
  *        then uses it.
- * In the Gram form with fp16 X the column sums are taken by the pass that transposes X, so X
- *   is read once for both; otherwise the statistics pass runs first.
+ * The statistics pass runs first, then the search.
  * stage_ms  NULL: asynchronous, like awq_search_layer. Non-NULL: host array of
  *        AWQ_SEARCH_STAGES floats filled as by awq_search_layer_profiled (this call then BLOCKS
  *        until the stream has finished it), the statistics counted in the X preparation stage.

@@ -167,9 +167,8 @@ def stats_search_layer(W: torch.Tensor, X: torch.Tensor, cfg: AwqConfig = AwqCon
                        flags: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                        stage_ms: dict | None = None) -> tuple[torch.Tensor, SearchResult]:
     """act_stats and search_layer in one call: returns (s_X, result), s_X identical to what
-    act_stats gives for this X. In the Gram form with fp16 X the column sums come out of the
-    pass that transposes X (X is read once for both). `stage_ms` as in search_layer, with the
-    statistics counted in the X preparation stage."""
+    act_stats gives for this X. `stage_ms` as in search_layer, with the statistics counted in the
+    X preparation stage."""
     lib = _lib.load()
     for t, nm in ((W, "W"), (X, "X")):
         _dev(t, nm)

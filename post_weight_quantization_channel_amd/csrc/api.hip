@@ -172,8 +172,7 @@ namespace {
 
 // Shared body of the search calls: the weights Ws[0..n_w) (N_l rows each, all reading the same
 // X) are searched together, their rows stacked in one error stack. With sx_out non-null (and sx
-// null), s_X is computed first into sx_out and used; in the Gram form with fp16 X it comes out
-// of the transpose pass. With `ev` non-null (2 * AWQ_SEARCH_STAGES events), stage j is bracketed
+// null), s_X is computed first into sx_out and used. With `ev` non-null (2 * AWQ_SEARCH_STAGES events), stage j is bracketed
 // by ev[2j] and ev[2j + 1].
 constexpr int kMaxSharedWeights = 64;
 
@@ -210,6 +209,7 @@ awq_status search_impl(const void* const* Ws, const int64_t* Ns, int n_w, awq_dt
   auto* stats = reinterpret_cast<double*>(base + L.stats);
   auto* Xt = reinterpret_cast<uint16_t*>(base + L.Xt);
   const bool gram = cfg->form == AWQ_FORM_GRAM;
+  const bool direct = gram && xdt == AWQ_F16 && awq::gram_direct_x(L.plan, K);
   // the Gram form's fp16 stack holds E d (column-scaled); the fp32 stack of small layers holds E
   const float* dcol = (gram && !L.precise) ? reinterpret_cast<const float*>(base + L.d32)
                                            : nullptr;
@@ -220,19 +220,15 @@ awq_status search_impl(const void* const* Ws, const int64_t* Ns, int n_w, awq_dt
   auto mark = [&](int idx) {
     if (ev && e == hipSuccess) e = hipEventRecord(ev[idx], stream);
   };
-  // X preparation: the transpose (Gram) or the fp16 copy of a non-fp16 X (direct), preceded by
-  // the statistics when the search takes them
+  // X preparation: the statistics when the search takes them, then the transpose (Gram form,
+  // unless X^T X reads fp16 X directly) or the fp16 copy of a non-fp16 X (direct form)
   auto x_prep = [&]() {
     mark(2 * 1);
     if (gram) {
-      const bool fused = sx_out && xdt == AWQ_F16;
-      if (sx_out && !fused && e == hipSuccess)
+      if (sx_out && e == hipSuccess)
         e = awq::launch_stats(X, (int)xdt, M, K, K, sx_out, flags, stats, stream);
-      if (e == hipSuccess)
-        e = awq::launch_gram_transpose(X, (int)xdt, M, K, L.plan.Mp, Xt,
-                                       fused ? stats : nullptr, flags, stream);
-      if (fused && e == hipSuccess)
-        e = awq::launch_stats_final(stats, awq::stats_chunks(M), M, K, sx_out, flags, stream);
+      if (!direct && e == hipSuccess)
+        e = awq::launch_gram_transpose(X, (int)xdt, M, K, L.plan.Mp, Xt, flags, stream);
     } else {
       if (sx_out && e == hipSuccess)
         e = awq::launch_stats(X, (int)xdt, M, K, K, sx_out, flags, stats, stream);
@@ -263,7 +259,8 @@ awq_status search_impl(const void* const* Ws, const int64_t* Ns, int n_w, awq_dt
                                 reinterpret_cast<float*>(base + L.d32),
                                 reinterpret_cast<uint16_t*>(base + L.B),
                                 reinterpret_cast<uint16_t*>(base + L.Blo), &ctrl->gram_k, stream,
-                                ev ? ev[2 * 2 + 1] : nullptr, ev ? ev[2 * 3] : nullptr);
+                                ev ? ev[2 * 2 + 1] : nullptr, ev ? ev[2 * 3] : nullptr,
+                                direct ? X16 : nullptr, M);
   } else {
     mark(2 * 2 + 1);
     mark(2 * 3);

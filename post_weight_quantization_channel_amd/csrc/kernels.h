@@ -46,21 +46,23 @@ struct GramPlan {
   int64_t chunk;  // tokens per chunk (multiple of kGramMAlign; the last chunk may be shorter)
 };
 GramPlan gram_plan(int64_t M, int64_t K, bool diag = false);
-// transpose -> ev[0] -> X^T X partials -> ev[1] -> d and B. B is [K, K] (row l, column k), or
+// transpose (unless X^T X reads fp16 X directly) -> ev[0] -> X^T X partials -> ev[1] -> d and B. B is [K, K] (row l, column k), or
 // with plan.diag the t diagonal blocks [t][256][256] (block a: rows and columns 256 a ..).
 // gram_k: nullptr, or where the finish pass records K (the operand is then complete once the
 // stream has passed this call).
-// The two halves of launch_gram_prepare. stats: nullptr, or (fp16 X only) [ceil(M/256)][K] fp64
-// column sums of |x| per 256 tokens, the chunk partials that launch_stats_final reduces.
+// The two halves of launch_gram_prepare.
 hipError_t launch_gram_transpose(const void* X, int xdt, int64_t M, int64_t K, int64_t Mp,
-                                 uint16_t* Xt, double* stats, uint32_t* flags,
-                                 hipStream_t stream);
+                                 uint16_t* Xt, uint32_t* flags, hipStream_t stream);
 // X^T X partials -> ev, ev2 (each if not null) -> d and B. Blo: nullptr, or [t][256][256] fp16,
 // the low-order parts fp16(b - fp16(b)) of the operand's diagonal blocks (block a: rows and
 // columns 256 a ..), for the clipping search.
+// X: nullptr (read the transposed copy Xt [K, Mp]), or fp16 X [M, K] read directly (Xt unused).
 hipError_t launch_gram_hmat(const uint16_t* Xt, int64_t K, const GramPlan& p, float* Hpart,
                             double* d64, float* d32, uint16_t* B, uint16_t* Blo,
-                            uint32_t* gram_k, hipStream_t stream, hipEvent_t ev, hipEvent_t ev2);
+                            uint32_t* gram_k, hipStream_t stream, hipEvent_t ev, hipEvent_t ev2,
+                            const uint16_t* X = nullptr, int64_t M = 0);
+// whether fp16 X is read directly by X^T X (no transposed copy) under plan p
+bool gram_direct_x(const GramPlan& p, int64_t K);
 hipError_t launch_gram_prepare(const void* X, int xdt, int64_t M, int64_t K, const GramPlan& p,
                                uint16_t* Xt, float* Hpart, double* d64, float* d32, uint16_t* B,
                                uint16_t* Blo, uint32_t* gram_k, uint32_t* flags,

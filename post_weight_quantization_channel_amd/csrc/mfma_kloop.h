@@ -195,6 +195,143 @@ __device__ __forceinline__ void kl_run(const char* smem, const Tile& T, int nk,
   kl_run_t<false>(smem, T, nk, acc);
 }
 
+// ------------------------------------------------------------------------------------------
+// The same K loop on operands stored with the reduction index across rows: X itself, [tokens]
+// [channels] row-major, for X^T X without a transposed copy. A stage holds, per operand, BK = 32
+// token rows of the panel's 256 channels (512 bytes each, 16 KiB); the fragment a lane needs (8
+// consecutive tokens of one channel) is gathered by two ds_read_b64_tr_b16.
+//
+// ds_read_b64_tr_b16 (measured on gfx950): within each group of 16 lanes, lane 4 q + r receives,
+// as its element j = 0..3, element r of the 64-bit word that lane 4 j + q addressed. So if lane
+// 4 j + q addresses tokens t0 + j, channels c0 + 4 q .. c0 + 4 q + 3, lane L receives tokens
+// t0 .. t0 + 3 of channel c0 + L: the MFMA operand layout (row = lane, four k values).
+//
+// LDS layout of a token row R: its 32 chunks of 8 channels, chunk c at position
+// 4 ((c / 4) ^ (R % 4)) + c % 4. The 16 lanes of a half-wave read 4 token rows (R % 4 all
+// different) x 4 chunks c0/8 .. c0/8 + 3 (c0 a multiple of 32): 16 distinct positions modulo
+// 16, i.e. all 64 banks, once each.
+struct TileX {
+  rsrc_t ra, rb;        // operand panels: row t = token t of the chunk, 256 channels
+  uint32_t voff[2];     // load lane offsets for slices of even / odd j (the swizzle key alternates)
+  uint32_t soff;        // byte offset of this wave's first token row (wave-uniform)
+  uint32_t row_stride;  // bytes between token rows
+  uint32_t lds0;
+  uint32_t rd[2][4];    // fragment read offsets in a stage: [operand][row block], k half 0
+  int wave;
+};
+
+constexpr int kXRowBytes = BM * 2;   // 512 bytes: one token row of a 256-channel panel
+
+__device__ __forceinline__ void tile_setup_x(TileX& T, const char* smem, uint32_t row_stride) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  T.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  T.lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  T.row_stride = row_stride;
+  // load slice j of a wave fills token rows 8 wave + 2 j + lane / 32 (two per 1 KiB load);
+  // lane l writes physical chunk l % 32, i.e. the logical chunk 4 ((p / 4) ^ (R % 4)) + p % 4
+  const int p = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int jp = 0; jp < 2; ++jp) {
+    const int rk = (2 * jp + hi) & 3;
+    const int c = 4 * ((p >> 2) ^ rk) + (p & 3);
+    T.voff[jp] = (uint32_t)hi * row_stride + (uint32_t)(c * 16);
+  }
+  T.soff = (uint32_t)(T.wave * 8) * row_stride;
+  // fragment reads: lane l = 16 G' + L (G' = l / 16), L = 4 j' + q'. Its word: token row
+  // 16 h + 8 (l / 32) + j' (+ 4 for the second read), channels wbase + 32 i + 16 (G' % 2) + 4 q'.
+  const int L = lane & 15, jq = L >> 2, q = L & 3, g = (lane >> 4) & 1, kh = lane >> 5;
+  const int wm = T.wave >> 1, wn = T.wave & 1;
+#pragma unroll
+  for (int o = 0; o < 2; ++o) {
+    const int wb32 = (o == 0 ? wm : wn) * 4;   // (wave's channel base) / 32
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pos = 4 * (wb32 + (i ^ jq)) + 2 * g + (q >> 1);
+      T.rd[o][i] = (uint32_t)(o * BM * kRowBytes) + (uint32_t)((8 * kh + jq) * kXRowBytes) +
+                   (uint32_t)(pos * 16 + 8 * (q & 1));
+    }
+  }
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// Fragment i (i < 4: A row block i, else B row block i - 4) of k half h from stage `st`.
+__device__ __forceinline__ void kl_read_x(const char* smem, const TileX& T, int st, int h, int i,
+                                          Frags& F) {
+  const int o = i < 4 ? 0 : 1, blk = i & 3;
+  const __attribute__((address_space(3))) char* base =
+      (const __attribute__((address_space(3))) char*)smem + st * kStageBytes + T.rd[o][blk] +
+      16 * h * kXRowBytes;
+  const v4i16_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)base);
+  const v4i16_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + 4 * kXRowBytes));
+  // whole-vector casts and one shuffle (the halves stay in their registers)
+  const half8_t f = __builtin_shufflevector(__builtin_bit_cast(half4_t, v0),
+                                            __builtin_bit_cast(half4_t, v1), 0, 1, 2, 3, 4, 5,
+                                            6, 7);
+  if (o == 0)
+    F.a[h][blk] = f;
+  else
+    F.b[h][blk] = f;
+}
+
+// Load slice idx in [0, 8) of step kt into stage `st` (even idx: A, odd: B; token rows
+// 8 wave + 2 (idx / 2) .. + 1).
+__device__ __forceinline__ void kl_issue_x(const TileX& T, int st, int kt, int idx) {
+  const int j = idx >> 1;
+  const uint32_t lds = T.lds0 + (uint32_t)(st * kStageBytes) + ((idx & 1) ? BM * kRowBytes : 0) +
+                       (uint32_t)((T.wave * 8 + 2 * j) * kXRowBytes);
+  const uint32_t so = T.soff + (uint32_t)(2 * j) * T.row_stride +
+                      (uint32_t)(kt * BK) * T.row_stride;
+  buffer_load16_lds_so((idx & 1) ? T.rb : T.ra, lds, T.voff[j & 1], so);
+}
+
+// kl_step with the X-operand reads and loads (no copies).
+template <bool LO, bool HI, bool MORE, int VM>
+__device__ __forceinline__ void kl_step_x(const char* smem, const TileX& T, int kt, Frags& F,
+                                          floatx16 (&acc)[4][4]) {
+  const int st = kt & 3;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[0][m >> 2], F.b[0][m & 3],
+                                                                acc[m >> 2][m & 3], 0, 0, 0);
+    if ((m & 1) == 0) kl_read_x(smem, T, st, 1, m >> 1, F);
+    if (HI && (m & 3) == 1) kl_issue_x(T, (st + 3) & 3, kt + 3, 4 + (m >> 2));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt(VM) & ~0x0F00);   // + lgkmcnt(0)
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[1][m >> 2], F.b[1][m & 3],
+                                                                acc[m >> 2][m & 3], 0, 0, 0);
+    if (LO && (m & 3) == 0) kl_issue_x(T, st, kt + 4, m >> 2);
+    if (MORE && (m & 1)) kl_read_x(smem, T, (st + 1) & 3, 0, m >> 1, F);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// kl_run on X operands (nk >= 4).
+__device__ __forceinline__ void kl_run_x(const char* smem, const TileX& T, int nk,
+                                         floatx16 (&acc)[4][4]) {
+  Frags F;
+#pragma unroll
+  for (int p = 0; p < kStages; ++p)
+#pragma unroll
+    for (int idx = 0; idx < ((p < kStages - 1) ? 2 * kInstPerOp : kInstPerOp); ++idx)
+      kl_issue_x(T, p, p, idx);
+  __builtin_amdgcn_s_waitcnt(vmcnt(20));           // step 0 has landed
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kl_read_x(smem, T, 0, 0, i, F);
+  for (int kt = 0; kt < nk - 4; ++kt) kl_step_x<true, true, true, 16>(smem, T, kt, F, acc);
+  kl_step_x<false, true, true, 16>(smem, T, nk - 4, F, acc);
+  kl_step_x<false, false, true, 8>(smem, T, nk - 3, F, acc);
+  kl_step_x<false, false, true, 0>(smem, T, nk - 2, F, acc);
+  kl_step_x<false, false, false, 0>(smem, T, nk - 1, F, acc);
+}
+
 __device__ __forceinline__ void acc_zero(floatx16 (&acc)[4][4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
