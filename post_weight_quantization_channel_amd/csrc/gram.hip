@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kloop::kThreads, 1) void gram_loss_kernel(
     // loop; its columns past K pick up neighbouring finite values (or zeros past the panel),
     // which meet P = 0 there and are masked below anyway.
     if (nk == 8 * (lt + 1)) {
-      kl_run_t<true>(smem, T_, nk, acc);
+      kl_run_t<true, true>(smem, T_, nk, acc);
     } else {
       kl_run(smem, T_, nk, acc);
 #pragma unroll

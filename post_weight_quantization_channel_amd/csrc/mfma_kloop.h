@@ -137,14 +137,24 @@ __device__ __forceinline__ void kl_issue_a_to_b(const Tile& T, int st, int ksrc,
 // VM: loads allowed in flight at the wait (those issued after the last load of step kt+1);
 // COPY: in the slots of LO, load operand A of step kt-4 into the B half of stage kt (free after
 // this step's barrier), for an epilogue that reads A of the last eight steps.
-template <bool LO, bool HI, bool MORE, int VM, bool COPY = false>
+// KD >= 0: step KD of the last eight, which cover the diagonal 256 x 256 block of a B that is
+// lower triangular (B[l][k] = 0 for k > l, l and k counted from the tile's first column): the
+// products of block j of wave column half wn have k >= 32 KD and l < 128 wn + 32 (j + 1), so
+// they are all zero when KD > 4 wn + j, and those MFMAs are skipped (the loads and fragment reads
+// stay as they are).
+__device__ __forceinline__ bool kl_block_live(int KD, int j, const Tile& T) {
+  return KD < 0 || KD <= j || (KD - 4 <= j && (T.wave & 1));
+}
+
+template <bool LO, bool HI, bool MORE, int VM, bool COPY = false, int KD = -1>
 __device__ __forceinline__ void kl_step(const char* smem, const Tile& T, int kt, Frags& F,
                                         floatx16 (&acc)[4][4]) {
   const int st = kt & 3;
 #pragma unroll
   for (int m = 0; m < 16; ++m) {
-    acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[0][m >> 2], F.b[0][m & 3],
-                                                                acc[m >> 2][m & 3], 0, 0, 0);
+    if (kl_block_live(KD, m & 3, T))
+      acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[0][m >> 2], F.b[0][m & 3],
+                                                                  acc[m >> 2][m & 3], 0, 0, 0);
     if ((m & 1) == 0) kl_read(smem, T, st, 1, m >> 1, F);
     if (HI && (m & 3) == 1) kl_issue(T, (st + 3) & 3, kt + 3, 4 + (m >> 2));
     __builtin_amdgcn_sched_barrier(0);
@@ -153,8 +163,9 @@ __device__ __forceinline__ void kl_step(const char* smem, const Tile& T, int kt,
   __syncthreads();
 #pragma unroll
   for (int m = 0; m < 16; ++m) {
-    acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[1][m >> 2], F.b[1][m & 3],
-                                                                acc[m >> 2][m & 3], 0, 0, 0);
+    if (kl_block_live(KD, m & 3, T))
+      acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[1][m >> 2], F.b[1][m & 3],
+                                                                  acc[m >> 2][m & 3], 0, 0, 0);
     if (LO && (m & 3) == 0) kl_issue(T, st, kt + 4, m >> 2);
     if (COPY && (m & 3) == 0) kl_issue_a_to_b(T, st, kt - 4, m >> 2);
     if (MORE && (m & 1)) kl_read(smem, T, (st + 1) & 3, 0, m >> 1, F);
@@ -167,7 +178,9 @@ __device__ __forceinline__ void kl_step(const char* smem, const Tile& T, int kt,
 // barrier and the stages are no longer read. With COPY, on return (once vmcnt(0) and a barrier
 // have followed) stage s holds operand A of step nk-8+s in its B half and of step nk-4+s in its
 // A half, s = 0..3 -- when nk is a multiple of 4 -- i.e. A of the last eight steps.
-template <bool COPY>
+// TRI (nk >= 8): the last eight steps are the diagonal block of a lower-triangular B (kl_step's
+// KD); their all-zero MFMA blocks are skipped.
+template <bool COPY, bool TRI = false>
 __device__ __forceinline__ void kl_run_t(const char* smem, const Tile& T, int nk,
                                          floatx16 (&acc)[4][4]) {
   Frags F;
@@ -182,12 +195,18 @@ __device__ __forceinline__ void kl_run_t(const char* smem, const Tile& T, int nk
 #pragma unroll
   for (int i = 0; i < 8; ++i) kl_read(smem, T, 0, 0, i, F);
   // at the wait of step kt, the loads of steps kt+2 and kt+3 (16) may be in flight
-  for (int kt = 0; kt < nk - 4; ++kt) kl_step<true, true, true, 16>(smem, T, kt, F, acc);
+  for (int kt = 0; kt < nk - (TRI ? 8 : 4); ++kt) kl_step<true, true, true, 16>(smem, T, kt, F, acc);
+  if constexpr (TRI) {
+    kl_step<true, true, true, 16, false, 0>(smem, T, nk - 8, F, acc);
+    kl_step<true, true, true, 16, false, 1>(smem, T, nk - 7, F, acc);
+    kl_step<true, true, true, 16, false, 2>(smem, T, nk - 6, F, acc);
+    kl_step<true, true, true, 16, false, 3>(smem, T, nk - 5, F, acc);
+  }
   // the copies (4 per step, from step nk-4 on) come after the last loads of steps nk-1
-  kl_step<false, true, true, 16, COPY>(smem, T, nk - 4, F, acc);
-  kl_step<false, false, true, COPY ? 12 : 8, COPY>(smem, T, nk - 3, F, acc);
-  kl_step<false, false, true, COPY ? 8 : 0, COPY>(smem, T, nk - 2, F, acc);
-  kl_step<false, false, false, COPY ? 12 : 0, COPY>(smem, T, nk - 1, F, acc);
+  kl_step<false, true, true, 16, COPY, TRI ? 4 : -1>(smem, T, nk - 4, F, acc);
+  kl_step<false, false, true, COPY ? 12 : 8, COPY, TRI ? 5 : -1>(smem, T, nk - 3, F, acc);
+  kl_step<false, false, true, COPY ? 8 : 0, COPY, TRI ? 6 : -1>(smem, T, nk - 2, F, acc);
+  kl_step<false, false, false, COPY ? 12 : 0, COPY, TRI ? 7 : -1>(smem, T, nk - 1, F, acc);
 }
 
 __device__ __forceinline__ void kl_run(const char* smem, const Tile& T, int nk,
