@@ -273,8 +273,10 @@ awq_status search_impl(const void* const* Ws, const int64_t* Ns, int n_w, awq_dt
   mark(2 * 5);
   int64_t row = 0;
   for (int l = 0; l < n_w && e == hipSuccess; ++l) {
+    // the Gram form's fp16 stack is K-blocked ([K / 32][N][32] per grid point): this weight's
+    // first row is row `row` of K block 0
     void* dst = L.precise ? static_cast<void*>(reinterpret_cast<float*>(base + L.E) + row * K)
-                          : static_cast<void*>(E + row * K);
+                          : static_cast<void*>(E + row * (dcol ? 32 : K));
     e = awq::launch_quantize_stack(Ws[l], (int)wdt, Ns[l], K, S, cfg->n_grid, cfg->bits,
                                    cfg->group, cfg->zero_point != 0, dcol, ctrl, dst, L.precise,
                                    N, flags, stream);
@@ -474,7 +476,7 @@ awq_status awq_clip_search(const void* W, awq_dtype wdt, int64_t N, int64_t K, c
                                           nullptr, flags, stream, nullptr);
   if (e == hipSuccess)
     e = awq::launch_clip_search(W, (int)wdt, N, K, s, d32, Bd, (int64_t)awq::kLossBM * awq::kLossBN,
-                                awq::kLossBN, Bdl, nullptr, 0,
+                                (int64_t)awq::kLossBN * 32, Bdl, nullptr, 0,
                                 cfg->n_clip, cfg->clip_min, cfg->bits, cfg->group,
                                 cfg->zero_point != 0, clip, clip_err, flags, stream);
   return hip_status(e);
@@ -509,7 +511,8 @@ awq_status awq_clip_search_gram(const void* W, awq_dtype wdt, int64_t N, int64_t
   const auto* ctrl = reinterpret_cast<const awq::SearchCtrl*>(base + L.ctrl);
   return hip_status(awq::launch_clip_search(
       W, (int)wdt, N, K, s, reinterpret_cast<const float*>(base + L.d32),
-      reinterpret_cast<const uint16_t*>(base + L.B), (int64_t)awq::kLossBN * K + awq::kLossBN, K,
+      reinterpret_cast<const uint16_t*>(base + L.B), (int64_t)awq::kLossBN * K + awq::kLossBN * 32,
+      32 * K,
       reinterpret_cast<const uint16_t*>(base + L.Blo), ctrl, cfg->n_grid, cfg->n_clip, cfg->clip_min, cfg->bits, cfg->group,
       cfg->zero_point != 0, clip, clip_err, flags, stream));
 }

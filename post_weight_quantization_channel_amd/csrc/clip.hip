@@ -53,7 +53,7 @@ template <int DT, int GS, bool ZP>
 __global__ __launch_bounds__(256) void clip_search_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s,
     const float* __restrict__ d32, const uint16_t* __restrict__ Bd, int64_t bd_block,
-    int64_t bd_pitch, const uint16_t* __restrict__ Bdl, const SearchCtrl* __restrict__ ctrl,
+    int64_t bd_kstride, const uint16_t* __restrict__ Bdl, const SearchCtrl* __restrict__ ctrl,
     int n_grid, int n_clip, float clip_min,
     float qmin, float qmax, float* __restrict__ clip, float* __restrict__ clip_err,
     uint32_t* __restrict__ flags) {
@@ -79,16 +79,18 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
     if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) atomicOr(flags, kFlagNoGram);
     return;
   }
-  // B_gg: rows l, columns k of the group, from the diagonal 256 x 256 block holding it (block a
-  // at Bd + a * bd_block, rows bd_pitch elements apart)
+  // B_gg: rows l, columns k of the group, from the diagonal 256 x 256 block holding it. The
+  // operand is K-blocked: element (l, k) of block a (l, k < 256 within it) at Bd + a * bd_block +
+  // (k / 32) * bd_kstride + 32 l + k % 32
   {
     const int64_t c0 = (int64_t)g * GS;
     const int o = (int)(c0 % 256);
-    const uint16_t* src = Bd + (c0 / 256) * bd_block + (int64_t)o * bd_pitch + o;
+    const uint16_t* blk = Bd + (c0 / 256) * bd_block;
     for (int idx = tid; idx < GS * (GS / 8); idx += 256) {
       const int l = idx / (GS / 8), ch = idx % (GS / 8);
-      *reinterpret_cast<uint4*>(&Bg[l * kPitch + ch * 8]) =
-          *reinterpret_cast<const uint4*>(src + l * bd_pitch + ch * 8);
+      const int kk = o + 8 * ch, ll = o + l;
+      *reinterpret_cast<uint4*>(&Bg[l * kPitch + ch * 8]) = *reinterpret_cast<const uint4*>(
+          blk + (int64_t)(kk >> 5) * bd_kstride + ll * 32 + (kk & 31));
     }
   }
 
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(256) void clip_search_kernel(
 
 hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, const float* s,
                               const float* d32, const uint16_t* Bd, int64_t bd_block,
-                              int64_t bd_pitch, const uint16_t* Bdl, const SearchCtrl* ctrl,
+                              int64_t bd_kstride, const uint16_t* Bdl, const SearchCtrl* ctrl,
                               int n_grid, int n_clip, float clip_min, int bits, int group,
                               bool zero_point, float* clip, float* clip_err, uint32_t* flags,
                               hipStream_t stream) {
@@ -270,7 +272,7 @@ hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, co
   dim3 grid((unsigned)((N + kClipRows - 1) / kClipRows), (unsigned)(K / group));
 #define AWQ_CLIP(DT_, GS_, ZP_)                                                                  \
   clip_search_kernel<DT_, GS_, ZP_><<<grid, 256, 0, stream>>>(                                    \
-      W, N, K, s, d32, Bd, bd_block, bd_pitch, Bdl, ctrl, n_grid, n_clip, clip_min, qmin, qmax,   \
+      W, N, K, s, d32, Bd, bd_block, bd_kstride, Bdl, ctrl, n_grid, n_clip, clip_min, qmin, qmax,   \
       clip,                                                                                      \
       clip_err, flags)
   if (dtype == kF32) {

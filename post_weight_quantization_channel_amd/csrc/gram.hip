@@ -291,7 +291,12 @@ __global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restric
   }
   const int64_t doff = (int64_t)a * (kLossBM * kLossBN) + (l - (int64_t)a * kLossBN) * kLossBN +
                        (k - (int64_t)a * kLossBM);
-  const int64_t off = diag ? doff : l * K + k;
+  // B is K-blocked, [K / 32][K][32] (with diag: per block, [8][256][32]): the 256 x 32 piece of
+  // one K step of the loss contraction is contiguous
+  const int64_t kl = k - (int64_t)a * kLossBM, ll = l - (int64_t)a * kLossBN;
+  const int64_t off = diag ? (int64_t)a * (kLossBM * kLossBN) + (kl >> 5) * (kLossBN * 32) +
+                                 ll * 32 + (kl & 31)
+                           : (k >> 5) * (K * 32) + l * 32 + (k & 31);
   *reinterpret_cast<uint2*>(B + off) =
       make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
   if (Blo && a == b)
@@ -328,14 +333,19 @@ __global__ __launch_bounds__(kloop::kThreads, 1) void gram_loss_kernel(
   const int alpha = panel / tilesN, nt = panel % tilesN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t rows = (N - (int64_t)nt * BM < BM) ? N - (int64_t)nt * BM : BM;
-  const uint16_t* Ep = Est + ((int64_t)alpha * N + (int64_t)nt * BM) * K;
   const int nk_all = (int)(K / BK);
 
-  Tile T_;
-  T_.ra = make_rsrc(Ep, (uint32_t)(rows * K * 2));
+  // both operands K-blocked: E' [n_grid][K / 32][N][32], B [K / 32][K][32]
+  TileK T_;
+  T_.pa = reinterpret_cast<const char*>(Est + (int64_t)alpha * N * K + (int64_t)nt * BM * BK);
+  T_.ka = (uint64_t)N * kRowBytes;
+  T_.na = (uint32_t)(rows * kRowBytes);
   const int64_t brows = (K - (int64_t)lt * BN < BN) ? K - (int64_t)lt * BN : BN;
-  T_.rb = make_rsrc(B + (int64_t)lt * BN * K, (uint32_t)(brows * K * 2));
-  tile_setup(T_, smem, (uint32_t)(K * 2));
+  T_.pb = reinterpret_cast<const char*>(B + (int64_t)lt * BN * BK);
+  T_.kb = (uint64_t)K * kRowBytes;
+  T_.nb = (uint32_t)(brows * kRowBytes);
+  T_.nkb = nk_all;
+  tile_setup(T_, smem, (uint32_t)kRowBytes);
   const int wn = T_.wave & 1;   // the wave's column half of the tile
   {
     const int nk = (8 * (lt + 1) < nk_all) ? 8 * (lt + 1) : nk_all;
@@ -345,10 +355,10 @@ __global__ __launch_bounds__(kloop::kThreads, 1) void gram_loss_kernel(
     // tile (the last eight steps are exactly these) keeps them in LDS: steps 8 lt + 4 + s stay in
     // the A half of stage s, and steps 8 lt + s are loaded again into the free B half of stage s
     // during the last four steps. The ragged last tile (K % 256 != 0) loads all eight after the
-    // loop; its columns past K pick up neighbouring finite values (or zeros past the panel),
-    // which meet P = 0 there and are masked below anyway.
+    // loop; its columns past K read as zeros (K blocks past the last) and are masked below
+    // anyway.
     if (nk == 8 * (lt + 1)) {
-      kl_run_t<true, true>(smem, T_, nk, acc);
+      kl_run_t<true, true, TileK>(smem, T_, nk, acc);
     } else {
       kl_run(smem, T_, nk, acc);
 #pragma unroll

@@ -46,8 +46,10 @@ struct GramPlan {
   int64_t chunk;  // tokens per chunk (multiple of kGramMAlign; the last chunk may be shorter)
 };
 GramPlan gram_plan(int64_t M, int64_t K, bool diag = false);
-// transpose (unless X^T X reads fp16 X directly) -> ev[0] -> X^T X partials -> ev[1] -> d and B. B is [K, K] (row l, column k), or
-// with plan.diag the t diagonal blocks [t][256][256] (block a: rows and columns 256 a ..).
+// transpose (unless X^T X reads fp16 X directly) -> ev[0] -> X^T X partials -> ev[1] -> d and
+// B. B (row l, column k) is K-blocked: [K / 32][K][32], element (l, k) at (k / 32) 32 K + 32 l +
+// k % 32; with plan.diag only the t diagonal blocks, [t][8][256][32] (block a: rows and columns
+// 256 a ..).
 // gram_k: nullptr, or where the finish pass records K (the operand is then complete once the
 // stream has passed this call).
 // The two halves of launch_gram_prepare.
@@ -79,7 +81,10 @@ hipError_t launch_x_to_f16(const void* X, int dtype, int64_t count, uint16_t* X1
                            uint32_t* flags, hipStream_t stream);
 // E_i * 2^escale (dcol == nullptr) or E_i[n,k] * dcol[k] * 2^escale, for the N rows of W, written
 // to rows 0..N-1 of Estack whose grid-point slices are ld_rows rows apart (ld_rows >= N: several
-// weights fill one stack); fp16, or fp32 with f32_stack (then dcol must be nullptr)
+// weights fill one stack); fp16, or fp32 with f32_stack (then dcol must be nullptr). Row-major
+// ([n_grid][ld_rows][K]), except with dcol (the Gram form's operand): K-blocked,
+// [n_grid][K / 32][ld_rows][32], element (n, k) of slice i at i ld_rows K + (k / 32) 32 ld_rows +
+// 32 n + k % 32 (Estack then points at row 0 of the weight in K block 0).
 hipError_t launch_quantize_stack(const void* W, int dtype, int64_t N, int64_t K, const float* S,
                                  int n_grid, int bits, int group, bool zero_point,
                                  const float* dcol, const SearchCtrl* ctrl, void* Estack,
@@ -117,15 +122,16 @@ hipError_t launch_fold(void* prev, int dtype, int64_t rows, int64_t cols, int64_
 // Per (row, group of 128): the ratio of the grid 1 .. clip_min whose clipped quantization of
 // W * s gives the smallest group error E_g H_gg E_g^T, with H_gg taken from the diagonal blocks
 // of the correlation operand and d = sqrt(diag H). The diagonal block a of the operand starts
-// at Bd + a * bd_block with rows bd_pitch elements apart ([t][256][256] from the diagonal-only
-// preparation: 65536 and 256; the full [K][K] operand of a Gram-form search: 256 K + 256 and K).
+// at Bd + a * bd_block, K-blocked: element (l, k) of it (l, k < 256) at (k / 32) bd_kstride +
+// 32 l + k % 32 (the diagonal-only preparation: 65536 and 8192; the full operand of a Gram-form
+// search: 256 K + 8192 and 32 K).
 // Bdl: the low-order parts of the diagonal blocks, [t][256][256] (launch_gram_hmat's Blo).
 // ctrl: nullptr, or the control block of the Gram-form search whose operand is read; when its
 // record of K or of the grid size differs from K and n_grid nothing is written and
 // AWQ_FLAG_NO_GRAM is raised.
 hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, const float* s,
                               const float* d32, const uint16_t* Bd, int64_t bd_block,
-                              int64_t bd_pitch, const uint16_t* Bdl, const SearchCtrl* ctrl,
+                              int64_t bd_kstride, const uint16_t* Bdl, const SearchCtrl* ctrl,
                               int n_grid, int n_clip,
                               float clip_min, int bits, int group, bool zero_point, float* clip,
                               float* clip_err, uint32_t* flags, hipStream_t stream);

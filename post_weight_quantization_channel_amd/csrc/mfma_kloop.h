@@ -132,6 +132,39 @@ __device__ __forceinline__ void kl_issue_a_to_b(const Tile& T, int st, int ksrc,
   buffer_load16_lds_so(T.ra, lds, T.voff, so);
 }
 
+// ------------------------------------------------------------------------------------------
+// K-blocked operands: a panel stored as [K / 32][rows][32], so that the 256 x 32 tile of one K
+// step is a contiguous 16 KiB block (rows 64 bytes apart). Each load takes a buffer descriptor
+// built for its step: base + kt * (bytes between K blocks), range = the panel's valid rows x 64
+// bytes, so rows past the panel read as zeros and no offset is limited to 32 bits. The LDS
+// layout, and so every fragment read, is that of Tile (row_stride = 64 in tile_setup).
+struct TileK : Tile {
+  const char* pa;    // operand A: panel's first row in K block 0
+  const char* pb;    // operand B
+  uint64_t ka, kb;   // bytes between consecutive K blocks
+  uint32_t na, nb;   // valid rows x 64 bytes
+  int nkb;           // K blocks that exist: steps from nkb on read zeros (an empty range)
+};
+
+__device__ __forceinline__ void kl_issue(const TileK& T, int st, int kt, int idx) {
+  const int j = idx >> 1;
+  const bool b = idx & 1;
+  const uint32_t live = kt < T.nkb ? 1u : 0u;
+  const rsrc_t r = b ? make_rsrc(T.pb + (uint64_t)kt * T.kb, T.nb * live)
+                     : make_rsrc(T.pa + (uint64_t)kt * T.ka, T.na * live);
+  const uint32_t lds = T.lds0 + (uint32_t)(st * kStageBytes) + (b ? BM * kRowBytes : 0) +
+                       (uint32_t)((T.wave * kRowsPerWave + kRowsPerInst * j) * kRowBytes);
+  buffer_load16_lds_so(r, lds, T.voff, T.soff + (uint32_t)(kRowsPerInst * j) * T.row_stride);
+}
+
+__device__ __forceinline__ void kl_issue_a_to_b(const TileK& T, int st, int ksrc, int j) {
+  const uint32_t lds = T.lds0 + (uint32_t)(st * kStageBytes) + BM * kRowBytes +
+                       (uint32_t)((T.wave * kRowsPerWave + kRowsPerInst * j) * kRowBytes);
+  buffer_load16_lds_so(make_rsrc(T.pa + (uint64_t)ksrc * T.ka, ksrc < T.nkb ? T.na : 0u), lds,
+                       T.voff,
+                       T.soff + (uint32_t)(kRowsPerInst * j) * T.row_stride);
+}
+
 // LO: issue loads 0..3 of step kt+4 (into stage kt); HI: issue loads 4..7 of step kt+3 (into
 // stage kt-1, free since the barrier of step kt-1); MORE: read step kt+1's first-half fragments;
 // VM: loads allowed in flight at the wait (those issued after the last load of step kt+1);
@@ -146,8 +179,8 @@ __device__ __forceinline__ bool kl_block_live(int KD, int j, const Tile& T) {
   return KD < 0 || KD <= j || (KD - 4 <= j && (T.wave & 1));
 }
 
-template <bool LO, bool HI, bool MORE, int VM, bool COPY = false, int KD = -1>
-__device__ __forceinline__ void kl_step(const char* smem, const Tile& T, int kt, Frags& F,
+template <bool LO, bool HI, bool MORE, int VM, bool COPY = false, int KD = -1, class TT = Tile>
+__device__ __forceinline__ void kl_step(const char* smem, const TT& T, int kt, Frags& F,
                                         floatx16 (&acc)[4][4]) {
   const int st = kt & 3;
 #pragma unroll
@@ -180,8 +213,8 @@ __device__ __forceinline__ void kl_step(const char* smem, const Tile& T, int kt,
 // A half, s = 0..3 -- when nk is a multiple of 4 -- i.e. A of the last eight steps.
 // TRI (nk >= 8): the last eight steps are the diagonal block of a lower-triangular B (kl_step's
 // KD); their all-zero MFMA blocks are skipped.
-template <bool COPY, bool TRI = false>
-__device__ __forceinline__ void kl_run_t(const char* smem, const Tile& T, int nk,
+template <bool COPY, bool TRI = false, class TT = Tile>
+__device__ __forceinline__ void kl_run_t(const char* smem, const TT& T, int nk,
                                          floatx16 (&acc)[4][4]) {
   Frags F;
   // steps 0..2 in full, loads 0..3 of step 3 (its loads 4..7 follow in step 0)
@@ -195,23 +228,25 @@ __device__ __forceinline__ void kl_run_t(const char* smem, const Tile& T, int nk
 #pragma unroll
   for (int i = 0; i < 8; ++i) kl_read(smem, T, 0, 0, i, F);
   // at the wait of step kt, the loads of steps kt+2 and kt+3 (16) may be in flight
-  for (int kt = 0; kt < nk - (TRI ? 8 : 4); ++kt) kl_step<true, true, true, 16>(smem, T, kt, F, acc);
+  for (int kt = 0; kt < nk - (TRI ? 8 : 4); ++kt)
+    kl_step<true, true, true, 16, false, -1, TT>(smem, T, kt, F, acc);
   if constexpr (TRI) {
-    kl_step<true, true, true, 16, false, 0>(smem, T, nk - 8, F, acc);
-    kl_step<true, true, true, 16, false, 1>(smem, T, nk - 7, F, acc);
-    kl_step<true, true, true, 16, false, 2>(smem, T, nk - 6, F, acc);
-    kl_step<true, true, true, 16, false, 3>(smem, T, nk - 5, F, acc);
+    kl_step<true, true, true, 16, false, 0, TT>(smem, T, nk - 8, F, acc);
+    kl_step<true, true, true, 16, false, 1, TT>(smem, T, nk - 7, F, acc);
+    kl_step<true, true, true, 16, false, 2, TT>(smem, T, nk - 6, F, acc);
+    kl_step<true, true, true, 16, false, 3, TT>(smem, T, nk - 5, F, acc);
   }
   // the copies (4 per step, from step nk-4 on) come after the last loads of steps nk-1
-  kl_step<false, true, true, 16, COPY, TRI ? 4 : -1>(smem, T, nk - 4, F, acc);
-  kl_step<false, false, true, COPY ? 12 : 8, COPY, TRI ? 5 : -1>(smem, T, nk - 3, F, acc);
-  kl_step<false, false, true, COPY ? 8 : 0, COPY, TRI ? 6 : -1>(smem, T, nk - 2, F, acc);
-  kl_step<false, false, false, COPY ? 12 : 0, COPY, TRI ? 7 : -1>(smem, T, nk - 1, F, acc);
+  kl_step<false, true, true, 16, COPY, TRI ? 4 : -1, TT>(smem, T, nk - 4, F, acc);
+  kl_step<false, false, true, COPY ? 12 : 8, COPY, TRI ? 5 : -1, TT>(smem, T, nk - 3, F, acc);
+  kl_step<false, false, true, COPY ? 8 : 0, COPY, TRI ? 6 : -1, TT>(smem, T, nk - 2, F, acc);
+  kl_step<false, false, false, COPY ? 12 : 0, COPY, TRI ? 7 : -1, TT>(smem, T, nk - 1, F, acc);
 }
 
-__device__ __forceinline__ void kl_run(const char* smem, const Tile& T, int nk,
+template <class TT>
+__device__ __forceinline__ void kl_run(const char* smem, const TT& T, int nk,
                                        floatx16 (&acc)[4][4]) {
-  kl_run_t<false>(smem, T, nk, acc);
+  kl_run_t<false, false, TT>(smem, T, nk, acc);
 }
 
 // ------------------------------------------------------------------------------------------

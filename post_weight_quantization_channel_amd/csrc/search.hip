@@ -175,7 +175,8 @@ constexpr int kQuantRows = 4;  // rows per thread in quantize_stack
 // kQuantRows rows; GL = group / 8 consecutive lanes cover one group (16 lanes, a DPP row, for
 // 128 channels; 8 for 64), so the group maximum (and minimum) is four (three) DPP steps. The
 // scale row s_i for the thread's 8 channels is loaded once per alpha and reused for all its rows.
-// Stores: 16 bytes per lane, 1 KiB per wave, contiguous. ZP: zero-point codes, E = (q - z) Delta
+// Stores: 16 bytes per lane, 1 KiB per wave, contiguous (in the K-blocked stack of the Gram form:
+// 64 bytes per 4 lanes, the thread's 4 rows filling 256 contiguous bytes). ZP: zero-point codes, E = (q - z) Delta
 // / s - w. F32: the stack is fp32 (the vector-ALU contraction of small layers) and E is formed as
 // fp32(fp32(fp32(q Delta) / s) - w) with an IEEE quotient, times the power of two.
 template <int DT, bool COL, int GL, bool ZP, bool F32>
@@ -253,7 +254,11 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
             (__builtin_fmaf(q[2 * t + 1] * delta, inv[2 * t + 1], -w[r][2 * t + 1])) * cs[2 * t + 1];
         packed[t] = f2h2(e0, e1);
       }
-      *reinterpret_cast<uint4*>(Estack + i * stride_alpha + (row0 + r) * K + c8 * 8) =
+      // the Gram form's operand is K-blocked ([K / 32][ld_rows][32] per grid point): the 8
+      // channels stay inside one 32-channel block
+      const int64_t off = COL ? (c8 >> 2) * (ld_rows * 32) + (row0 + r) * 32 + (c8 & 3) * 8
+                              : (row0 + r) * K + c8 * 8;
+      *reinterpret_cast<uint4*>(Estack + i * stride_alpha + off) =
           make_uint4(packed[0], packed[1], packed[2], packed[3]);
     }
   }
