@@ -175,8 +175,8 @@ constexpr int kQuantRows = 4;  // rows per thread in quantize_stack
 // kQuantRows rows; GL = group / 8 consecutive lanes cover one group (16 lanes, a DPP row, for
 // 128 channels; 8 for 64), so the group maximum (and minimum) is four (three) DPP steps. The
 // scale row s_i for the thread's 8 channels is loaded once per alpha and reused for all its rows.
-// Stores: 16 bytes per lane, 1 KiB per wave, contiguous (in the K-blocked stack of the Gram form:
-// 64 bytes per 4 lanes, the thread's 4 rows filling 256 contiguous bytes). ZP: zero-point codes, E = (q - z) Delta
+// Stores: 16 bytes per lane, 1 KiB per wave, contiguous (the K-blocked stack of the Gram form
+// takes its own thread layout, below). ZP: zero-point codes, E = (q - z) Delta
 // / s - w. F32: the stack is fp32 (the vector-ALU contraction of small layers) and E is formed as
 // fp32(fp32(fp32(q Delta) / s) - w) with an IEEE quotient, times the power of two.
 template <int DT, bool COL, int GL, bool ZP, bool F32>
@@ -188,10 +188,24 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
   constexpr int ES = (DT == kF32) ? 4 : 2;
   const int64_t chunks = K / 8;
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t rb = id / chunks;
-  const int64_t c8 = id % chunks;
-  const int64_t row0 = rb * kQuantRows;
-  if (row0 >= N) return;  // whole GL-lane groups share rb: no partial group exits here
+  // rows of this thread: rbase + r * rstep, r < kQuantRows
+  int64_t c8, rbase, rstep;
+  if constexpr (COL) {
+    // K-blocked stack: a wave takes 16 rows x 128 channels; DPP row q (16 lanes, one or two
+    // groups) holds rows 4 r + q, so one store instruction writes four runs of 4 rows x 64 bytes
+    // and the thread's four rows complete 1 KiB runs of each 32-channel block
+    const int64_t wid = id >> 6, cblocks = (chunks + 15) / 16;
+    const int lane = threadIdx.x & 63;
+    c8 = (wid % cblocks) * 16 + (lane & 15);
+    rbase = (wid / cblocks) * 16 + (lane >> 4);
+    rstep = 4;
+    if (c8 >= chunks) return;   // K is a multiple of the group: whole groups exit
+  } else {
+    c8 = id % chunks;
+    rbase = (id / chunks) * kQuantRows;
+    rstep = 1;
+  }
+  if (rbase >= N) return;  // whole GL-lane groups share their rows: no partial group exits here
   const int e = escale_from_absmax(ctrl->absmax_bits);
   const float esc = ldexpf(1.0f, e);
   float cs[8];   // per-column factor: 2^escale, times dcol[k] in the Gram form
@@ -208,9 +222,10 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
   bool live[kQuantRows];
 #pragma unroll
   for (int r = 0; r < kQuantRows; ++r) {
-    live[r] = (row0 + r) < N;
+    live[r] = (rbase + r * rstep) < N;
     if (live[r]) {
-      load8_f32<DT>(reinterpret_cast<const char*>(W) + ((row0 + r) * K + c8 * 8) * ES, w[r]);
+      load8_f32<DT>(reinterpret_cast<const char*>(W) + ((rbase + r * rstep) * K + c8 * 8) * ES,
+                    w[r]);
     } else {
 #pragma unroll
       for (int t = 0; t < 8; ++t) w[r][t] = 0.0f;
@@ -238,7 +253,7 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
         float ev[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) ev[t] = ((q[t] * delta) / s[t] - w[r][t]) * cs[t];
-        float* dst = static_cast<float*>(Estack_) + i * stride_alpha + (row0 + r) * K + c8 * 8;
+        float* dst = static_cast<float*>(Estack_) + i * stride_alpha + (rbase + r) * K + c8 * 8;
         *reinterpret_cast<float4*>(dst) = make_float4(ev[0], ev[1], ev[2], ev[3]);
         *reinterpret_cast<float4*>(dst + 4) = make_float4(ev[4], ev[5], ev[6], ev[7]);
         continue;
@@ -256,8 +271,8 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
       }
       // the Gram form's operand is K-blocked ([K / 32][ld_rows][32] per grid point): the 8
       // channels stay inside one 32-channel block
-      const int64_t off = COL ? (c8 >> 2) * (ld_rows * 32) + (row0 + r) * 32 + (c8 & 3) * 8
-                              : (row0 + r) * K + c8 * 8;
+      const int64_t off = COL ? (c8 >> 2) * (ld_rows * 32) + (rbase + r * rstep) * 32 + (c8 & 3) * 8
+                              : (rbase + r) * K + c8 * 8;
       *reinterpret_cast<uint4*>(Estack + i * stride_alpha + off) =
           make_uint4(packed[0], packed[1], packed[2], packed[3]);
     }
@@ -287,7 +302,10 @@ hipError_t launch_quantize_stack(const void* W, int dtype, int64_t N, int64_t K,
                                  hipStream_t stream) {
   const float qmax = zero_point ? (float)((1 << bits) - 1) : (float)((1 << (bits - 1)) - 1);
   const float qmin = zero_point ? 0.0f : -(float)(1 << (bits - 1));
-  const int64_t threads = ((N + kQuantRows - 1) / kQuantRows) * (K / 8);
+  // the K-blocked stack (dcol, fp16): waves of 16 rows x 128 channels
+  const int64_t threads = (dcol && !f32_stack)
+                              ? ((N + 15) / 16) * ((K / 8 + 15) / 16) * 64
+                              : ((N + kQuantRows - 1) / kQuantRows) * (K / 8);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
 #define AWQ_QSD(DT_, COL_, F32_)                                                                 \
   qs_dispatch<DT_, COL_, F32_>(group, zero_point, blocks, stream, W, N, K, S, n_grid, qmin, qmax, \
