@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kloop::kThreads, 1) void gram_loss_kernel(
   T_.kb = (uint64_t)K * kRowBytes;
   T_.nb = (uint32_t)(brows * kRowBytes);
   T_.nkb = nk_all;
-  tile_setup(T_, smem, (uint32_t)kRowBytes);
+  tile_setup_k(T_, smem);   // columns interleaved: block j of column half wn is c = 2 j + wn
   const int wn = T_.wave & 1;   // the wave's column half of the tile
   {
     const int nk = (8 * (lt + 1) < nk_all) ? 8 * (lt + 1) : nk_all;
@@ -372,9 +372,9 @@ __global__ __launch_bounds__(kloop::kThreads, 1) void gram_loss_kernel(
     __builtin_amdgcn_s_waitcnt(vmcnt(0));
     __syncthreads();
 
-    // epilogue: sum over the tile of E'_nl P_nl (P = acc). Columns l of block (wn, j) are those
-    // of step 8 lt + 4 wn + j. Two MFMAs against the identity put the E' block into the layout
-    // of the accumulators exactly (one product by 1 per element, fp16 -> fp32 is exact):
+    // epilogue: sum over the tile of E'_nl P_nl (P = acc). Columns l of block (wn, j) are
+    // c = 2 j + wn, those of step 8 lt + c. Two MFMAs against the identity put the E' block into
+    // the layout of the accumulators exactly (one product by 1 per element, fp16 -> fp32 is exact):
     // D = A_0 I_0 + A_1 I_1 with I_h[k][c] = (c == 16 h + k) over the block's 32 columns.
     const int l32 = lane & 31, lh = lane >> 5;
     half8_t id0, id1;
@@ -388,13 +388,14 @@ __global__ __launch_bounds__(kloop::kThreads, 1) void gram_loss_kernel(
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const char* src = smem + j * kStageBytes + (wn ? 0 : BM * kRowBytes);
+        const int c = 2 * j + wn;
+        const char* src = smem + (c & 3) * kStageBytes + (c >= 4 ? 0 : BM * kRowBytes);
         const half8_t f0 = *reinterpret_cast<const half8_t*>(src + T_.rd[0][0] + i * 32 * kRowBytes);
         const half8_t f1 = *reinterpret_cast<const half8_t*>(src + T_.rd[0][1] + i * 32 * kRowBytes);
         floatx16 ev = {};
         ev = __builtin_amdgcn_mfma_f32_32x32x16_f16(f0, id0, ev, 0, 0, 0);
         ev = __builtin_amdgcn_mfma_f32_32x32x16_f16(f1, id1, ev, 0, 0, 0);
-        const int lcol = wn * 128 + 32 * j + l32;
+        const int lcol = 32 * c + l32;
         const bool lok = (int64_t)lt * BN + lcol < K;
         float s = 0.0f;
 #pragma unroll

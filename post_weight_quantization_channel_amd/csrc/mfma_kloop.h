@@ -146,6 +146,27 @@ struct TileK : Tile {
   int nkb;           // K blocks that exist: steps from nkb on read zeros (an empty range)
 };
 
+// TileK's operand B (the output columns) is interleaved between the two column waves: column
+// half wn takes the 32-column blocks c = 2 j + wn (Tile: c = 4 wn + j), so that the two halves
+// hold equal shares of the diagonal block of a lower-triangular B (kl_block_live below).
+__device__ __forceinline__ void tile_setup_k(TileK& T, const char* smem) {
+  tile_setup(T, smem, (uint32_t)kRowBytes);
+  // B rows 32 wn + l % 32 instead of 128 wn + l % 32: the swizzle depends on bits 1..3 of the row
+  // only, so the offsets just move
+  const uint32_t d = (uint32_t)((T.wave & 1) * 96 * kRowBytes);
+  T.rd[1][0] -= d;
+  T.rd[1][1] -= d;
+}
+
+__device__ __forceinline__ void kl_read(const char* smem, const TileK& T, int st, int h, int i,
+                                        Frags& F) {
+  const char* base = smem + st * kStageBytes;
+  if (i < 4)
+    F.a[h][i] = *reinterpret_cast<const half8_t*>(base + T.rd[0][h] + i * 32 * kRowBytes);
+  else
+    F.b[h][i - 4] = *reinterpret_cast<const half8_t*>(base + T.rd[1][h] + (i - 4) * 64 * kRowBytes);
+}
+
 __device__ __forceinline__ void kl_issue(const TileK& T, int st, int kt, int idx) {
   const int j = idx >> 1;
   const bool b = idx & 1;
@@ -177,6 +198,11 @@ __device__ __forceinline__ void kl_issue_a_to_b(const TileK& T, int st, int ksrc
 // stay as they are).
 __device__ __forceinline__ bool kl_block_live(int KD, int j, const Tile& T) {
   return KD < 0 || KD <= j || (KD - 4 <= j && (T.wave & 1));
+}
+// the same with TileK's interleaved columns (block j of column half wn is c = 2 j + wn): zero
+// when KD > 2 j + wn
+__device__ __forceinline__ bool kl_block_live(int KD, int j, const TileK& T) {
+  return KD < 0 || KD <= 2 * j || (KD == 2 * j + 1 && (T.wave & 1));
 }
 
 template <bool LO, bool HI, bool MORE, int VM, bool COPY = false, int KD = -1, class TT = Tile>
