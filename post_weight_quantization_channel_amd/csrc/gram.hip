@@ -228,8 +228,19 @@ __global__ __launch_bounds__(256) void gram_diag_kernel(const float* __restrict_
   const int lane = r + 32 * ((r >> 2) & 1);
   const int e = 4 * (r >> 3) + (r & 3);
   const int64_t off = frag_off(3 * wm, i, i, e, lane);
+  // the chunks' values are loaded eight at a time (past the last chunk: the last one again, not
+  // added), then added in chunk order
   double h = 0.0;
-  for (int c = 0; c < S; ++c) h += (double)Hpart[((int64_t)c * T + tile) * (kLossBM * kLossBN) + off];
+  const float* src = Hpart + tile * (kLossBM * kLossBN) + off;
+  const int64_t cs = T * (kLossBM * kLossBN);
+  for (int c0 = 0; c0 < S; c0 += 8) {
+    float p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) p[u] = src[(int64_t)(c0 + u < S ? c0 + u : S - 1) * cs];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c0 + u < S) h += (double)p[u];
+  }
   const double d = sqrt(h);
   d64[k] = d;
   d32[k] = (float)d;
@@ -265,14 +276,25 @@ __global__ __launch_bounds__(256) void gram_finish_kernel(const float* __restric
   const int64_t l = (int64_t)b * kLossBN + wn * 128 + 32 * j + (lane & 31);
   const int64_t k = (int64_t)a * kLossBM + wm * 128 + 32 * i + 8 * e4 + 4 * (lane >> 5);
   if (l >= K || k >= K) return;   // k is a multiple of 4 and K of 128: k..k+3 all valid
+  // the chunks' partials are loaded eight at a time (independent loads in flight), then added in
+  // chunk order
   double h[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int c = 0; c < S; ++c) {
-    const float4 p = *reinterpret_cast<const float4*>(Hpart + ((int64_t)c * T + tile) * (4 * kPerTile) +
-                                                      (int64_t)rem * 4);
-    h[0] += (double)p.x;
-    h[1] += (double)p.y;
-    h[2] += (double)p.z;
-    h[3] += (double)p.w;
+  const float* src = Hpart + tile * (4 * kPerTile) + (int64_t)rem * 4;
+  const int64_t cs = T * (4 * kPerTile);
+  for (int c0 = 0; c0 < S; c0 += 8) {
+    float4 p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)   // past the last chunk: the last chunk again, not added
+      p[u] = *reinterpret_cast<const float4*>(src + (int64_t)(c0 + u < S ? c0 + u : S - 1) * cs);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (c0 + u < S) {
+        h[0] += (double)p[u].x;
+        h[1] += (double)p[u].y;
+        h[2] += (double)p[u].z;
+        h[3] += (double)p[u].w;
+      }
+    }
   }
   const double dl = d64[l];
   uint16_t o[4], lo[4];
