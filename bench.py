@@ -122,18 +122,36 @@ def measured_traffic(kernel):
 
 
 def gram_loss_flops(N, K, n_grid):
-    """MFMA flops of one Gram-form loss launch: per grid point and 256-row tile of E, column
-    tile lt runs min(8 (lt + 1), K / 32) K steps of a 256 x 256 x 32 product (the lower
-    triangle plus the diagonal blocks in full): ~ n_grid N K (K + 256)."""
+    """The method's flops in one Gram-form loss launch: the quadratic form E H E^T of every grid
+    point with H symmetric, one multiply-add per pair of channels and weight row, i.e.
+    n_grid N K^2 (the strict triangle; the diagonal adds n_grid N K more)."""
+    return float(n_grid) * N * K * K
+
+
+def gram_loss_executed_flops(N, K, n_grid):
+    """MFMA flops the Gram-form loss kernel issues: per grid point and 256-row tile of E, column
+    tile lt runs nk = min(8 (lt + 1), K / 32) K steps of a 256 x 256 x 32 product. In a full tile
+    the last eight steps cover the diagonal block of the lower-triangular operand, and step d
+    of them (d = 0..7) issues only the products of its 8 - d live 32-column blocks (36 of 64 in
+    all, i.e. 4.5 steps' worth); the ragged last tile runs all its steps in full."""
     t = -(-K // 256)
     tiles_n = -(-N // 256)
-    steps = sum(min(8 * (lt + 1), K // 32) for lt in range(t))
+    steps = 0.0
+    for lt in range(t):
+        nk = min(8 * (lt + 1), K // 32)
+        steps += (nk - 8 + 4.5) if nk == 8 * (lt + 1) else nk
     return 2.0 * 256 * 256 * 32 * steps * tiles_n * n_grid
 
 
 def gram_gemm_flops(M, K):
-    """MFMA flops of X^T X: the t (t + 1) / 2 upper-triangle 256 x 256 tiles over the padded
-    token count: ~ M K (K + 256)."""
+    """The method's flops of H = X^T X: one multiply-add per token and pair of channels of the
+    symmetric product, M K^2."""
+    return float(M) * K * K
+
+
+def gram_gemm_executed_flops(M, K):
+    """MFMA flops of X^T X as the kernel runs it: the t (t + 1) / 2 upper-triangle 256 x 256
+    tiles over the padded token count: ~ M K (K + 256)."""
     t = -(-K // 256)
     Mp = -(-M // 128) * 128
     return 2.0 * 256 * 256 * Mp * (t * (t + 1) // 2)
@@ -501,19 +519,21 @@ def layer_sweep(awq, torch, reps, cpu_parts):
         sx, res = awq.stats_search_layer(Wt, Xt, cfg, workspace=ws, stage_ms=prof)
         losses = np.sort(res.losses.cpu().numpy())
         fl_loss = gram_loss_flops(n, k, N_GRID)
-        strict = float(N_GRID) * n * k * k
+        ex_loss = gram_loss_executed_flops(n, k, N_GRID)
         fl_gemm = gram_gemm_flops(M_, k)
+        ex_gemm = gram_gemm_executed_flops(M_, k)
+
+        def frac(fl, ms):
+            return round(fl / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
         rec = {"layer": name, "N": n, "K": k, "M": M_, "bits": bits,
                "ms": round(statistics.mean(times), 3),
                "stages_ms": {kk: round(v, 4) for kk, v in prof.items()},
                "gram_loss": {"ms": round(prof["loss"], 4),
-                             "frac_executed": round(fl_loss / (prof["loss"] * 1e-3) / 1e12 /
-                                                    MFMA_F16_PEAK_TFLOPS, 4),
-                             "frac_strict_triangle": round(strict / (prof["loss"] * 1e-3) /
-                                                           1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
+                             "frac": frac(fl_loss, prof["loss"]),
+                             "frac_executed": frac(ex_loss, prof["loss"])},
                "gram_gemm": {"ms": round(prof["gram_gemm"], 4),
-                             "frac_executed": round(fl_gemm / (prof["gram_gemm"] * 1e-3) / 1e12 /
-                                                    MFMA_F16_PEAK_TFLOPS, 4)},
+                             "frac": frac(fl_gemm, prof["gram_gemm"]),
+                             "frac_executed": frac(ex_gemm, prof["gram_gemm"])},
                "alpha_star": int(res.best.item()),
                "loss_gap": float((losses[1] - losses[0]) / losses[0]),
                "flags": int(res.flags.item()),
@@ -732,17 +752,25 @@ def main():
     log(f"ms/step {ms_per_step:.3f}; stages {stages}; stats {stats_ms:.4f} ms; pack "
         f"{pack_ms:.4f} ms; alpha* {best}; flags {flag_bits}")
 
-    def mfma_rec(kernel, ms, flops):
+    def mfma_rec(kernel, ms, flops, executed=None):
+        # achieved: the method's flops (n N K^2 for the loss, M K^2 for X^T X; N M K per grid
+        # point for the direct form); the flops the kernel issues are reported beside them
         achieved = flops / (ms * 1e-3) / 1e12
-        return {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 1),
-                "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(kernel), "flops_per_launch": flops,
-                "launch_ms": round(ms, 4)}
+        rec = {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 1),
+               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+               "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+               "traffic": measured_traffic(kernel), "flops_per_launch": flops,
+               "launch_ms": round(ms, 4)}
+        if executed is not None:
+            rec["executed_flops_per_launch"] = executed
+            rec["frac_executed"] = round(executed / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
+        return rec
 
     if args.form == "gram":
-        mfma = [mfma_rec("gram_loss_kernel", stages["loss"], gram_loss_flops(N_, K_, N_GRID)),
-                mfma_rec("gram_gemm_x_kernel", stages["gram_gemm"], gram_gemm_flops(M_, K_))]
+        mfma = [mfma_rec("gram_loss_kernel", stages["loss"], gram_loss_flops(N_, K_, N_GRID),
+                         gram_loss_executed_flops(N_, K_, N_GRID)),
+                mfma_rec("gram_gemm_x_kernel", stages["gram_gemm"], gram_gemm_flops(M_, K_),
+                         gram_gemm_executed_flops(M_, K_))]
     else:
         mfma = [mfma_rec("lossgemm_kernel", stages["loss"], 2.0 * M_ * N_ * K_ * N_GRID)]
     roofline = max(mfma, key=lambda r: r["launch_ms"])
@@ -906,7 +934,8 @@ def main():
         if oform == "direct":
             orec = mfma_rec("lossgemm_kernel", ost["loss"], 2.0 * M_ * N_ * K_ * N_GRID)
         else:
-            orec = mfma_rec("gram_loss_kernel", ost["loss"], gram_loss_flops(N_, K_, N_GRID))
+            orec = mfma_rec("gram_loss_kernel", ost["loss"], gram_loss_flops(N_, K_, N_GRID),
+                            gram_loss_executed_flops(N_, K_, N_GRID))
         other_form = {"form": oform, "search_ms": round(sum(ost.values()), 3),
                       "alpha_star": int(ro.best.item()),
                       "max_loss_rel_diff": float(np.max(np.abs(lo - losses) / losses)),

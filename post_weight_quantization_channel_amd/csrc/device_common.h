@@ -356,6 +356,33 @@ __device__ __forceinline__ float quant8_clip(float (&ws)[8], float ratio, float 
   return quant8_core(ws, c, qmin, qmax, q, underflow);
 }
 
+// The eight codes of one packed word as four exact fp16 pairs p[j] = (c_j, c_{j+4}), where
+// c = q for two's-complement nibbles and c = q - z for unsigned zero-point nibbles (z the
+// group's zero point). Each pair costs one mask-and-xor (a single v_bitop3_b32) and one packed
+// fp16 operation, plus one shift per word:
+//   * the xor constant both flips bit 3 of each nibble (u = q + 8 for signed codes; zero-point
+//     codes are unsigned already, u = q) and places the exponent 0x6400 around it;
+//   * nibbles j, j + 4 of pairs 0 and 2 sit at mantissa bits 0..3: the fp16 value is 1024 + u,
+//     and subtracting 1024 + zc (zc = 8 or z) gives c;
+//   * nibbles of pairs 1 and 3 stay at bits 4..7 (no shift): the value is 1024 + 16 u, and
+//     fma(v, 1/16, -(64 + zc)) gives c;
+// every intermediate is an integer below 2^11, so all of it is exact.
+// sub_lo = 1024 + zc, sub_hi = -(64 + zc), both as fp16 pairs.
+template <bool ZP>
+__device__ __forceinline__ void unpack_word8(uint32_t w, half2_t sub_lo, half2_t sub_hi,
+                                             half2_t (&p)[4]) {
+  constexpr uint32_t kLo = ZP ? 0x64006400u : 0x64086408u;   // exponent + flip of bit 3
+  constexpr uint32_t kHi = ZP ? 0x64006400u : 0x64806480u;   // the same for bits 4..7
+  const half2_t sixteenth = half2_t{(_Float16)0.0625f, (_Float16)0.0625f};
+  const uint32_t y = w >> 8;
+  p[0] = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) ^ kLo) - sub_lo;
+  p[1] = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, (w & 0x00F000F0u) ^ kHi),
+                                   sixteenth, sub_hi);
+  p[2] = __builtin_bit_cast(half2_t, (y & 0x000F000Fu) ^ kLo) - sub_lo;
+  p[3] = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, (y & 0x00F000F0u) ^ kHi),
+                                   sixteenth, sub_hi);
+}
+
 // Buffer resource over [base, base + num_bytes): loads at offsets >= num_bytes return zero,
 // which handles ragged tiles without branches. Word 1 holds the top 16 address bits with
 // stride 0 (raw buffer); word 3 = 0x00020000 is the raw 32-bit data format used for untyped

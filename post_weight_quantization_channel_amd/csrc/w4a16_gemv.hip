@@ -16,14 +16,12 @@
 //     to hide the latency of their loads: 4 waves of 4 rows were 12-15% slower, 16 waves of one
 //     row slower still); lane l takes the 32-channel chunks l, l + 64, ... of each row (16 bytes
 //     of codes per row and chunk); a chunk of a'' read from LDS serves both rows;
-//   * decoding: x = w ^ 0x88888888 turns each two's-complement nibble into u = q + 8 (zero-point
-//     codes are unsigned already, u = q); (x >> 4j) & 0x000F000F | 0x64006400 is the fp16 pair
-//     (1024 + u_j, 1024 + u_{j+4}), and one packed subtract of 1024 + zc (zc = 8, or z) gives
-//     (c(q_j), c(q_{j+4})) exactly; v_dot2_f32_f16 against the a'' pair (j, j + 4) adds both
-//     exact products in fp32. (Summing (1024 + u) a'' and subtracting the offset times the
-//     chunk's sum afterwards would save the subtract but lose everything else in the block to
-//     the rounding of one huge term: a dead channel's a'' next to q = 0.) The chunk's sum times
-//     step 2^e goes into the row's partial;
+//   * decoding: each word of 8 codes gives the exact fp16 pairs (c(q_j), c(q_{j+4})) in one
+//     shift, four mask-and-xor and four packed fp16 operations (unpack_word8); v_dot2_f32_f16
+//     against the a'' pair (j, j + 4) adds both exact products in fp32. (Summing (1024 + u) a''
+//     and subtracting the offset times the chunk's sum afterwards would save the packed
+//     operation but lose everything else in the block to the rounding of one huge term: a dead
+//     channel's a'' next to q = 0.) The chunk's sum times step 2^e goes into the row's partial;
 //   * the two rows' partials are summed over the wave's 64 lanes by a transposing butterfly
 //     (the first exchange halves the values a lane holds), in a fixed order.
 // Rounding: a'' one fp16 rounding (of the fp32 a' = A rcp(s)); products exact, sums fp32; Y
@@ -169,22 +167,22 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_kernel(
 #pragma unroll
       for (int r = 0; r < kGvRows; ++r) {
         const uint32_t words[4] = {buf.w[j][r].x, buf.w[j][r].y, buf.w[j][r].z, buf.w[j][r].w};
-        // fp16 subtrahend: 1032 (signed codes, biased by the xor) or 1024 + z
-        const _Float16 subh = ZP ? (_Float16)(1024.0f + (float)buf.z[j][r]) : (_Float16)1032.0f;
-        const half2_t sub2 = half2_t{subh, subh};
+        // fp16 subtrahends of the unpack: zc = 8 (signed codes, biased by the flip) or z
+        const float zc = ZP ? (float)buf.z[j][r] : 8.0f;
+        const _Float16 slo = (_Float16)(1024.0f + zc), shi = (_Float16)(-64.0f - zc);
+        const half2_t sub_lo = half2_t{slo, slo}, sub_hi = half2_t{shi, shi};
         float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {             // word v: channels 8v .. 8v + 7 of the chunk
-          const uint32_t x = ZP ? words[v] : (words[v] ^ 0x88888888u);
+          half2_t qp[4];
+          unpack_word8<ZP>(words[v], sub_lo, sub_hi, qp);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            const uint32_t bits = ((x >> (4 * jj)) & 0x000F000Fu) | 0x64006400u;
-            const half2_t qp = __builtin_bit_cast(half2_t, bits) - sub2;
             const half2_t apair = __builtin_bit_cast(half2_t, ap[4 * v + jj]);
             if (jj & 1)
-              acc1 = __builtin_amdgcn_fdot2(qp, apair, acc1, false);
+              acc1 = __builtin_amdgcn_fdot2(qp[jj], apair, acc1, false);
             else
-              acc0 = __builtin_amdgcn_fdot2(qp, apair, acc0, false);
+              acc0 = __builtin_amdgcn_fdot2(qp[jj], apair, acc0, false);
           }
         }
         part[r] = __builtin_fmaf(h2f((uint16_t)buf.st[j][r]) * f, acc0 + acc1, part[r]);

@@ -11,11 +11,11 @@
 //   * a workgroup owns 16 weight rows and all of K; its 8 waves take the 128-channel blocks
 //     round-robin, every lane issuing the 16-byte loads of its blocks (up to 4 at a time,
 //     double-buffered) before unpacking any of them;
-//   * unpacking: one 32-bit word holds the codes of 8 consecutive channels; x = w ^ 0x88888888
-//     turns each nibble into q + 8, (x >> 4j) & 0x000F000F | 0x64006400 is the fp16 pair
-//     (1024 + q_j + 8, 1024 + q_{j+4} + 8) and one packed subtract gives (q_j, q_{j+4}) exactly
-//     (zero-point codes: subtract 1024 + z). The MFMA k slots therefore hold channels in the
-//     order 0,4,1,5,2,6,3,7 of each 8, and the activations are permuted the same way;
+//   * unpacking: one 32-bit word holds the codes of 8 consecutive channels; one shift, four
+//     mask-and-xor and four packed fp16 operations turn it into the exact fp16 pairs (q_j,
+//     q_{j+4}), j = 0..3 (zero-point codes: q - z), as unpack_word8 describes. The MFMA k slots
+//     therefore hold channels in the order 0,4,1,5,2,6,3,7 of each 8, and the activations are
+//     permuted the same way;
 //   * 1/s enters the weight operand as fp16(q * r_k), r_k = fp16(2^b / s_k) with one power of
 //     two 2^b per 128-channel block chosen so that the block's largest r_k lies in [2^10, 2^11):
 //     |q r_k| < 2^15, so no s -- not even a dead channel's s_floor -- can overflow fp16 (an
@@ -179,27 +179,27 @@ __global__ __launch_bounds__(kThreads, (MB == 1 && TI == 1) ? 6 : 1) void w4a16_
       const int64_t g = wave + kWaves * i;                  // 128-channel block
       const int64_t kbase = g * 128 + lg * 32;              // this lane's 32 channels
       const uint32_t words[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
-      // fp16 subtrahend of the unpack: 1032 (signed codes, biased by the xor) or 1024 + z of
-      // this lane's row and group (the lane's 32 channels lie in one group for GS = 64 too)
-      half2_t sub2 = half2_t{(_Float16)1032.0f, (_Float16)1032.0f};
+      // fp16 subtrahends of the unpack: zc = 8 (signed codes, biased by the flip) or z of this
+      // lane's row and group (the lane's 32 channels lie in one group for GS = 64 too)
+      _Float16 slo = (_Float16)1032.0f, shi = (_Float16)-72.0f;
       if (ZP) {
         const int64_t gz = (GS == 64) ? 2 * g + (lg >> 1) : g;
-        const _Float16 zh = __builtin_bit_cast(_Float16, zero_lds[gz * kRows + li]);
-        sub2 = half2_t{zh, zh};
+        slo = __builtin_bit_cast(_Float16, zero_lds[gz * kRows + li]);
+        shi = (_Float16)960.0f - slo;   // -(64 + z), exact
       }
+      const half2_t sub_lo = half2_t{slo, slo}, sub_hi = half2_t{shi, shi};
       half8_t wf[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {                          // word v: channels kbase + 8v ..
-        const uint32_t x = ZP ? words[v] : (words[v] ^ 0x88888888u);
         const uint4 rv = HAS_S ? *reinterpret_cast<const uint4*>(rtab + kbase + 8 * v)
                                : make_uint4(0u, 0u, 0u, 0u);
         const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+        half2_t d[4];
+        unpack_word8<ZP>(words[v], sub_lo, sub_hi, d);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           // without s the operand is c(q) itself (exact) and no block scale applies
-          const uint32_t bits = ((x >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-          const half2_t d = __builtin_bit_cast(half2_t, bits) - sub2;
-          const half2_t q = HAS_S ? d * __builtin_bit_cast(half2_t, rw[j]) : d;
+          const half2_t q = HAS_S ? d[j] * __builtin_bit_cast(half2_t, rw[j]) : d[j];
           wf[v][2 * j] = q[0];
           wf[v][2 * j + 1] = q[1];
         }
