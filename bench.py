@@ -251,7 +251,7 @@ def ceiling_pass(sizes=(1 << 30, M_ * K_ * 2, N_GRID * N_ * K_ * 2), reps=20, ec
 W4A16_COUNTER_CALLS = [(4096, 4096, 1, False), (4096, 4096, 16, False), (4096, 4096, 64, False),
                        (4096, 4096, 64, True), (4096, 4096, 128, True), (4096, 4096, 512, False),
                        (11008, 4096, 1, False), (11008, 4096, 4, False), (11008, 4096, 16, False),
-                       (11008, 4096, 64, True)]
+                       (11008, 4096, 64, True), (28672, 8192, 1, False)]
 W4A16_SUM_KERNELS = ("w4a16_splitk_reduce_kernel", "w4a16_sum_slices_kernel")
 
 
