@@ -32,9 +32,6 @@
 namespace awq {
 
 namespace {
-constexpr int kGvRows = 2;     // weight rows per wave
-constexpr int kGvWaves = 8;    // waves per workgroup
-constexpr int kGvThreads = 64 * kGvWaves;
 constexpr int kGvPos = 2;      // chunk positions per lane whose loads are in flight together
 constexpr int kChunkBytes = 80;   // LDS bytes per 32-channel chunk: 64 of a'', 16 of padding
 }  // namespace
@@ -49,11 +46,13 @@ size_t w4a16_gemv_lds_bytes(int MB, int64_t K) {
 // (K <= 4096 TI); all their loads are unconditional, issued before the code loads, and only the
 // LDS stores are conditional -- a load inside a conditional block would be issued there, after
 // the code loads, and waiting for it would wait for all of them.
-template <int GS, bool ZP, bool HAS_S, bool ONE, int TI>
-__global__ __launch_bounds__(kGvThreads) void w4a16_gemv_kernel(
+// RW weight rows per wave, NW waves per workgroup.
+template <int GS, bool ZP, bool HAS_S, bool ONE, int TI, int RW, int NW>
+__global__ __launch_bounds__(64 * NW) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ A, int64_t N, int64_t K, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales16, const uint8_t* __restrict__ zeros,
     const uint16_t* __restrict__ s16, uint16_t* __restrict__ Y) {
+  constexpr int kGvRows = RW, kGvWaves = NW, kGvThreads = 64 * NW;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n0 = ((int64_t)blockIdx.x * kGvWaves + wave) * kGvRows;
@@ -204,25 +203,30 @@ __global__ __launch_bounds__(kGvThreads) void w4a16_gemv_kernel(
     }
   }
 
-  // ---- sums over the 64 lanes (two rows: row 0 goes to the lanes with bit 5 clear, row 1 to
-  // the others, then 32 lanes add up in five steps; one row: six steps) --------------------
-  static_assert(kGvRows == 1 || kGvRows == 2, "one or two rows per wave");
-  const bool b5 = (lane & 32) != 0;
-  float kk;
-  if constexpr (kGvRows == 2) {
-    const float give = b5 ? part[0] : part[kGvRows - 1];
-    kk = b5 ? part[kGvRows - 1] : part[0];
-    kk += __shfl_xor(give, 32);
-  } else {
-    kk = part[0] + __shfl_xor(part[0], 32);
+  // ---- sums over the 64 lanes: log2(RW) transposing exchanges (lanes with the exchange's lane
+  // bit set keep the upper half of their rows and send the lower half, the others the reverse),
+  // then the plain butterfly over the lanes below the last exchanged bit; a fixed order ---------
+  static_assert(kGvRows == 1 || kGvRows == 2 || kGvRows == 4, "one, two or four rows per wave");
+  float v[kGvRows];
+#pragma unroll
+  for (int r = 0; r < kGvRows; ++r) v[r] = part[r];
+  int row = 0;
+  constexpr int kLastMask = (kGvRows == 4) ? 16 : (kGvRows == 2) ? 32 : 64;
+#pragma unroll
+  for (int n = kGvRows, mask = 32; n > 1; n >>= 1, mask >>= 1) {
+    const bool hi = (lane & mask) != 0;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+      const float keep = hi ? v[n / 2 + i] : v[i];
+      const float give = hi ? v[i] : v[n / 2 + i];
+      v[i] = keep + __shfl_xor(give, mask);
+    }
+    if (hi) row += n / 2;
   }
-  kk += __shfl_xor(kk, 16);
-  kk += __shfl_xor(kk, 8);
-  kk += __shfl_xor(kk, 4);
-  kk += __shfl_xor(kk, 2);
-  kk += __shfl_xor(kk, 1);
-  const int row = (kGvRows == 2 && b5) ? 1 : 0;
-  if ((lane & (kGvRows == 2 ? 31 : 63)) == 0 && n0 + row < N) Y[n0 + row] = f2h(kk);
+  float kk = v[0];
+#pragma unroll
+  for (int m = kLastMask / 2; m >= 1; m >>= 1) kk += __shfl_xor(kk, m);
+  if ((lane & (kLastMask - 1)) == 0 && n0 + row < N) Y[n0 + row] = f2h(kk);
 }
 
 hipError_t launch_w4a16_gemv(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
@@ -230,15 +234,18 @@ hipError_t launch_w4a16_gemv(const uint16_t* A, int64_t M, int64_t N, int64_t K,
                              const uint8_t* zeros, const uint16_t* s16, uint16_t* Y,
                              hipStream_t stream) {
   if (M != 1 || K > kW4a16GemvMaxK) return hipErrorInvalidValue;
-  const unsigned blocks = (unsigned)((N + kGvRows * kGvWaves - 1) / (kGvRows * kGvWaves));
+  constexpr int RW = 2, NW = 8;
+  constexpr int kGvThreads = 64 * NW;
+  static_assert(kW4a16GemvMaxK <= 64 * kGvThreads, "table entries per thread: at most 8");
+  const unsigned blocks = (unsigned)((N + RW * NW - 1) / (RW * NW));
   const size_t lds = w4a16_gemv_lds_bytes(1, K);
   const bool one = K <= 64 * 32 * kGvPos;   // K <= 4096: one table entry per thread, one batch
 #define AWQ_GV1(GS_, ZP_, HS_, ONE_, TI_)                                                        \
-  w4a16_gemv_kernel<GS_, ZP_, HS_, ONE_, TI_><<<blocks, kGvThreads, lds, stream>>>(              \
+  w4a16_gemv_kernel<GS_, ZP_, HS_, ONE_, TI_, RW, NW><<<blocks, kGvThreads, lds, stream>>>(      \
       A, N, K, qweight, scales16, zeros, s16, Y)
 #define AWQ_GV(GS_, ZP_, HS_)                                                                    \
   do {                                                                                           \
-    if (one) AWQ_GV1(GS_, ZP_, HS_, true, 1);                                                   \
+    if (one) AWQ_GV1(GS_, ZP_, HS_, true, (4096 / 8 + kGvThreads - 1) / kGvThreads);            \
     else if (K <= 8 * kGvThreads) AWQ_GV1(GS_, ZP_, HS_, false, 1);                             \
     else if (K <= 16 * kGvThreads) AWQ_GV1(GS_, ZP_, HS_, false, 2);                            \
     else if (K <= 32 * kGvThreads) AWQ_GV1(GS_, ZP_, HS_, false, 4);                            \
