@@ -236,6 +236,11 @@ __device__ __forceinline__ void quant_codes(const float (&v)[NV], const QuantSte
 // that distance is within 2^-17 of one half (or the step needs exact division) does the lane
 // enter the block that redoes the near-half elements by IEEE division. med3 equals the clamp for
 // every finite value.
+// The symmetric codes of the fast path need no clamp: there Delta = fp32(m / qmax) is a normal
+// number (exact_only false), so Delta >= (m / qmax)(1 - 2^-24), v_rcp_f32 is within one ulp of
+// 1 / Delta, and every |ws| <= m gives |fp32(ws rcp)| <= qmax (1 + 2^-21) < qmax + 1/2, i.e.
+// |q| <= qmax. A step of 0 has rcp = 0 and gives codes 0 on the fast path. Zero-point codes add z
+// and are clamped on both paths (q + z can pass either end by one).
 template <bool ZP>
 __device__ __forceinline__ void codes8(const float (&ws)[8], const QuantStep& st, float z,
                                        float qmin, float qmax, float (&q)[8]) {
@@ -252,21 +257,21 @@ __device__ __forceinline__ void codes8(const float (&ws)[8], const QuantStep& st
       const float tq = ws[t] * st.rcp;
       if (st.exact_only || fabsf(tq - rintf(tq)) > 0.5f - 0x1p-17f) q[t] = rintf(ws[t] / st.delta);
     }
-  }
 #pragma unroll
-  for (int t = 0; t < 8; ++t) q[t] = __builtin_amdgcn_fmed3f(ZP ? q[t] + z : q[t], qmin, qmax);
+    for (int t = 0; t < 8; ++t) q[t] = __builtin_amdgcn_fmed3f(ZP ? q[t] + z : q[t], qmin, qmax);
+  } else if (ZP) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) q[t] = __builtin_amdgcn_fmed3f(q[t] + z, qmin, qmax);
+  }
 }
 
-// Codes of ws[] for the group maximum m (every |ws| <= m); returns Delta.
+// Codes of ws[] for the group maximum m (every |ws| <= m); returns Delta. A zero step (m = 0, or
+// m / qmax below the smallest subnormal) gives codes 0 without a branch: quant_step returns
+// rcp = 0 and exact_only false for it.
 __device__ __forceinline__ float quant8_core(const float (&ws)[8], float m, float qmin,
                                              float qmax, float (&q)[8], bool& underflow) {
   const QuantStep st = quant_step(m, qmax);
   underflow = (m > 0.0f) && !(st.delta > 0.0f);
-  if (!(st.delta > 0.0f)) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) q[t] = 0.0f;
-    return 0.0f;
-  }
   codes8<false>(ws, st, 0.0f, qmin, qmax, q);
   return st.delta;
 }

@@ -233,10 +233,10 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
   }
   const size_t stride_alpha = (size_t)ld_rows * (size_t)K;
   for (int i = 0; i < n_grid; ++i) {
-    float s[8], inv[8];
+    float s[8], ics[8];   // ics: cs / s (v_rcp_f32, one rounding more)
     load8_f32<kF32>(S + (size_t)i * K + c8 * 8, s);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) inv[t] = __builtin_amdgcn_rcpf(s[t]);
+    for (int t = 0; t < 8; ++t) ics[t] = __builtin_amdgcn_rcpf(s[t]) * cs[t];
 #pragma unroll
     for (int r = 0; r < kQuantRows; ++r) {
       if (!live[r]) continue;  // uniform over the GL-lane group
@@ -262,11 +262,14 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
       uint32_t packed[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        // E = (q Delta)/s - w (q already centred by z), then scaled (by the exact power of two,
-        // or by d_k 2^escale) and rounded once to fp16
-        const float e0 = (__builtin_fmaf(q[2 * t] * delta, inv[2 * t], -w[r][2 * t])) * cs[2 * t];
-        const float e1 =
-            (__builtin_fmaf(q[2 * t + 1] * delta, inv[2 * t + 1], -w[r][2 * t + 1])) * cs[2 * t + 1];
+        // E = (q Delta)/s - w (q already centred by z), scaled (by the exact power of two, or by
+        // d_k 2^escale) and rounded to fp16, as (q Delta - ws) (cs / s): q Delta - ws is exact in
+        // one fma for every unclamped code (|q Delta - ws| <= Delta / 2 is a multiple of half an
+        // ulp of Delta or of ws); what remains are the roundings of ws = w s (at most
+        // 2^-24 |ws| <= 2^-24 qmax Delta) and of cs / s (2^-23 relative), small against error
+        // terms of size ~Delta / 2 and against their fp16 rounding
+        const float e0 = __builtin_fmaf(q[2 * t], delta, -ws[2 * t]) * ics[2 * t];
+        const float e1 = __builtin_fmaf(q[2 * t + 1], delta, -ws[2 * t + 1]) * ics[2 * t + 1];
         packed[t] = f2h2(e0, e1);
       }
       // the Gram form's operand is K-blocked ([K / 32][ld_rows][32] per grid point): the 8
