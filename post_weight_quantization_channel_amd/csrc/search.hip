@@ -193,11 +193,14 @@ __global__ __launch_bounds__(256) void quantize_stack_kernel(
   if constexpr (COL) {
     // K-blocked stack: a wave takes 16 rows x 128 channels; DPP row q (16 lanes, one or two
     // groups) holds rows 4 r + q, so one store instruction writes four runs of 4 rows x 64 bytes
-    // and the thread's four rows complete 1 KiB runs of each 32-channel block
-    const int64_t wid = id >> 6, cblocks = (chunks + 15) / 16;
+    // and the thread's four rows complete 1 KiB runs of each 32-channel block. Consecutive waves
+    // take consecutive row blocks of one 128-channel column, so a workgroup's stores fill four
+    // 4 KiB runs and consecutive workgroups continue them (column-block-first order spread each
+    // workgroup's stores over sixteen blocks 256 KiB apart)
+    const int64_t wid = id >> 6, rblocks = (N + 15) / 16;
     const int lane = threadIdx.x & 63;
-    c8 = (wid % cblocks) * 16 + (lane & 15);
-    rbase = (wid / cblocks) * 16 + (lane >> 4);
+    c8 = (wid / rblocks) * 16 + (lane & 15);
+    rbase = (wid % rblocks) * 16 + (lane >> 4);
     rstep = 4;
     if (c8 >= chunks) return;   // K is a multiple of the group: whole groups exit
   } else {
