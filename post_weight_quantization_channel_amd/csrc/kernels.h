@@ -137,10 +137,13 @@ hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, co
                               float* clip_err, uint32_t* flags, hipStream_t stream);
 
 // ---- W4A16 ----
-// one activation row (M = 1): fp16 dot products against the block-scaled A / s table; K up to
-// kW4a16GemvMaxK; dynamic LDS of w4a16_gemv_lds_bytes(1, K) bytes (the launcher passes it)
+// one or two activation rows: fp16 dot products against the block-scaled A / s tables (one per
+// row), the codes decoded once for both rows; M = 1 with K up to kW4a16GemvMaxK, M = 2 with
+// K <= 8192 (w4a16_gemv_fits); dynamic LDS of w4a16_gemv_lds_bytes(M, K) bytes (the launcher
+// passes it)
 constexpr int64_t kW4a16GemvMaxK = 32768;
 size_t w4a16_gemv_lds_bytes(int MB, int64_t K);
+bool w4a16_gemv_fits(int64_t M, int64_t K);
 hipError_t launch_w4a16_gemv(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
                              const uint32_t* qweight, const uint16_t* scales16,
                              const uint8_t* zeros, const uint16_t* s16, uint16_t* Y,

@@ -426,7 +426,7 @@ hipError_t launch_w4a16_tiled_split(const uint16_t* A, int64_t M, int64_t N, int
 hipError_t launch_w4a16(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
                         const uint32_t* qweight, const uint16_t* scales16, const uint8_t* zeros,
                         const uint16_t* s16, uint16_t* Y, hipStream_t stream) {
-  if (M == 1 && K <= kW4a16GemvMaxK)
+  if (w4a16_gemv_fits(M, K))
     return launch_w4a16_gemv(A, M, N, K, group, qweight, scales16, zeros, s16, Y, stream);
   // the tiled kernel above 64 batch rows, and from 49 on for tall weights (each skinny
   // workgroup reads all of A, which at 8192+ weight rows costs more than the tiles' unpacking),

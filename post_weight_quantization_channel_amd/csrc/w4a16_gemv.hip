@@ -1,6 +1,6 @@
-// W4A16 for one activation row (decode): QuantLinear.forward of "AWQ 量化方案..."
+// W4A16 for one or two activation rows (decode): QuantLinear.forward of "AWQ 量化方案..."
 // (qwbw.cn/news/39982), section 三 -- scale the input per channel, dequantize, linear:
-//   Y[n] = sum_k (A[k] / s[k]) * c(q[n,k]) * step[n, k/G],
+//   Y[m, n] = sum_k (A[m, k] / s[k]) * c(q[n,k]) * step[n, k/G],
 // c(q) = q for symmetric codes, q - z[n, k/G] for zero-point ones. The activation is divided by
 // s because the weight was multiplied by s (AWQ notes, bg51717.github.io/14592, section 方法).
 //
@@ -22,6 +22,7 @@
 //     and subtracting the offset times the chunk's sum afterwards would save the packed
 //     operation but lose everything else in the block to the rounding of one huge term: a dead
 //     channel's a'' next to q = 0.) The chunk's sum times step 2^e goes into the row's partial;
+//   * with two activation rows each has its own a'' table and the decoded code pairs serve both;
 //   * the two rows' partials are summed over the wave's 64 lanes by a transposing butterfly
 //     (the first exchange halves the values a lane holds), in a fixed order.
 // Rounding: a'' one fp16 rounding (of the fp32 a' = A rcp(s)); products exact, sums fp32; Y
@@ -36,40 +37,53 @@ constexpr int kGvPos = 2;      // chunk positions per lane whose loads are in fl
 constexpr int kChunkBytes = 80;   // LDS bytes per 32-channel chunk: 64 of a'', 16 of padding
 }  // namespace
 
-// LDS bytes of the tables: K/32 chunks, then the K/128 block factors 2^-e (fp32).
-size_t w4a16_gemv_lds_bytes(int MB, int64_t K) {
-  return (size_t)MB * ((size_t)(K / 32) * kChunkBytes + (size_t)(K / 128) * sizeof(float));
+// LDS bytes of one activation row's table: K/32 chunks, then the K/128 block factors 2^-e
+// (fp32), rounded up to 16 bytes; MB rows' tables follow one another.
+__host__ __device__ static inline size_t gemv_table_bytes(int64_t K) {
+  return ((size_t)(K / 32) * kChunkBytes + (size_t)(K / 128) * sizeof(float) + 15) & ~(size_t)15;
 }
+size_t w4a16_gemv_lds_bytes(int MB, int64_t K) { return (size_t)MB * gemv_table_bytes(K); }
 
 // ONE: every chunk position of a lane fits one load batch (K <= 64 * 32 * kGvPos = 4096), so
 // there is one set of load registers and no loop. TI: table entries of 8 channels per thread
 // (K <= 4096 TI); all their loads are unconditional, issued before the code loads, and only the
 // LDS stores are conditional -- a load inside a conditional block would be issued there, after
 // the code loads, and waiting for it would wait for all of them.
-// RW weight rows per wave, NW waves per workgroup.
-template <int GS, bool ZP, bool HAS_S, bool ONE, int TI, int RW, int NW>
+// RW weight rows per wave, NW waves per workgroup, MB activation rows (M <= MB; rows past M
+// read row M - 1 and are not stored): one a'' table per activation row, the codes decoded once
+// for all of them.
+template <int GS, bool ZP, bool HAS_S, bool ONE, int TI, int RW, int NW, int MB>
 __global__ __launch_bounds__(64 * NW) void w4a16_gemv_kernel(
-    const uint16_t* __restrict__ A, int64_t N, int64_t K, const uint32_t* __restrict__ qweight,
-    const uint16_t* __restrict__ scales16, const uint8_t* __restrict__ zeros,
-    const uint16_t* __restrict__ s16, uint16_t* __restrict__ Y) {
+    const uint16_t* __restrict__ A, int64_t M, int64_t N, int64_t K,
+    const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales16,
+    const uint8_t* __restrict__ zeros, const uint16_t* __restrict__ s16,
+    uint16_t* __restrict__ Y) {
   constexpr int kGvRows = RW, kGvWaves = NW, kGvThreads = 64 * NW;
   extern __shared__ __attribute__((aligned(16))) char lds[];
+  const size_t tbytes = gemv_table_bytes(K);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n0 = ((int64_t)blockIdx.x * kGvWaves + wave) * kGvRows;
   const int nch = (int)(K / 32);                 // 32-channel chunks of a row
   const int64_t ngr = K / GS;                    // quantization groups of a row
   const int64_t wpr = K / 8;                     // uint32 words of a row
   const int npos = (nch + 63) / 64;              // chunk positions of a lane (the last partial)
-  float* bfac = reinterpret_cast<float*>(lds + (size_t)nch * kChunkBytes);   // [K/128] 2^-e
+  // table of activation row m: lds + m tbytes; its block factors [K/128] 2^-e after the chunks
+  auto bfac = [&](int m) {
+    return reinterpret_cast<float*>(lds + m * tbytes + (size_t)nch * kChunkBytes);
+  };
 
   // ---- 1. activation and s loads of this thread's table entries (8 channels each) ----------
-  uint4 araw[TI], sraw[TI];
+  uint4 araw[MB][TI], sraw[TI];
   const int nq8 = (int)(K / 8);
 #pragma unroll
   for (int it = 0; it < TI; ++it) {
     const int q8 = tid + kGvThreads * it;
     const int qc = q8 < nq8 ? q8 : 0;
-    araw[it] = *reinterpret_cast<const uint4*>(A + (int64_t)qc * 8);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const int64_t mr = (m < M) ? m : M - 1;
+      araw[m][it] = *reinterpret_cast<const uint4*>(A + mr * K + (int64_t)qc * 8);
+    }
     sraw[it] = HAS_S ? *reinterpret_cast<const uint4*>(s16 + (int64_t)qc * 8)
                      : make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
   }
@@ -109,12 +123,13 @@ __global__ __launch_bounds__(64 * NW) void w4a16_gemv_kernel(
   asm volatile("" : : "v"(wrow[0]) : "memory");   // the code loads stay ahead of the table
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- 3. the a'' table: 16 consecutive threads hold one 128-channel block ------------------
+  // ---- 3. the a'' tables: 16 consecutive threads hold one 128-channel block ----------------
 #pragma unroll
   for (int it = 0; it < TI; ++it) {
     const int q8 = tid + kGvThreads * it;
-    {
-      const uint32_t aw[4] = {araw[it].x, araw[it].y, araw[it].z, araw[it].w};
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const uint32_t aw[4] = {araw[m][it].x, araw[m][it].y, araw[m][it].z, araw[m][it].w};
       const uint32_t sw[4] = {sraw[it].x, sraw[it].y, sraw[it].z, sraw[it].w};
       float v[8];
       float mx = 0.0f;
@@ -137,17 +152,19 @@ __global__ __launch_bounds__(64 * NW) void w4a16_gemv_kernel(
       const uint32_t p2 = (uint32_t)h[2] | ((uint32_t)h[6] << 16);
       const uint32_t p3 = (uint32_t)h[3] | ((uint32_t)h[7] << 16);
       if (q8 < nq8) {
-        char* d = lds + (size_t)(q8 >> 2) * kChunkBytes + (q8 & 3) * 16;
+        char* d = lds + m * tbytes + (size_t)(q8 >> 2) * kChunkBytes + (q8 & 3) * 16;
         *reinterpret_cast<uint4*>(d) = make_uint4(p0, p1, p2, p3);
-        if ((q8 & 15) == 0) bfac[q8 >> 4] = ldexpf(1.0f, -e);
+        if ((q8 & 15) == 0) bfac(m)[q8 >> 4] = ldexpf(1.0f, -e);
       }
     }
   }
   __syncthreads();
 
-  float part[kGvRows];
+  float part[kGvRows][MB];
 #pragma unroll
-  for (int r = 0; r < kGvRows; ++r) part[r] = 0.0f;
+  for (int r = 0; r < kGvRows; ++r)
+#pragma unroll
+    for (int m = 0; m < MB; ++m) part[r][m] = 0.0f;
 
   auto process = [&](int p0, const Buf& buf) {
 #pragma unroll
@@ -155,36 +172,56 @@ __global__ __launch_bounds__(64 * NW) void w4a16_gemv_kernel(
       const int c = lane + 64 * (p0 + j);
       const bool ok = c < nch;
       const int cc = ok ? c : 0;
-      const char* ch = lds + (size_t)cc * kChunkBytes;
-      uint32_t ap[16];
+      float f[MB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 t4 = *reinterpret_cast<const uint4*>(ch + 16 * i);
-        ap[4 * i] = t4.x; ap[4 * i + 1] = t4.y; ap[4 * i + 2] = t4.z; ap[4 * i + 3] = t4.w;
-      }
-      const float f = ok ? bfac[cc >> 2] : 0.0f;   // 2^-e of the chunk's block
+      for (int m = 0; m < MB; ++m) f[m] = ok ? bfac(m)[cc >> 2] : 0.0f;   // 2^-e of the block
+      half2_t sub_lo[kGvRows], sub_hi[kGvRows];
 #pragma unroll
       for (int r = 0; r < kGvRows; ++r) {
-        const uint32_t words[4] = {buf.w[j][r].x, buf.w[j][r].y, buf.w[j][r].z, buf.w[j][r].w};
         // fp16 subtrahends of the unpack: zc = 8 (signed codes, biased by the flip) or z
         const float zc = ZP ? (float)buf.z[j][r] : 8.0f;
         const _Float16 slo = (_Float16)(1024.0f + zc), shi = (_Float16)(-64.0f - zc);
-        const half2_t sub_lo = half2_t{slo, slo}, sub_hi = half2_t{shi, shi};
-        float acc0 = 0.0f, acc1 = 0.0f;
+        sub_lo[r] = half2_t{slo, slo};
+        sub_hi[r] = half2_t{shi, shi};
+      }
+      float acc0[kGvRows][MB], acc1[kGvRows][MB];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {             // word v: channels 8v .. 8v + 7 of the chunk
+      for (int r = 0; r < kGvRows; ++r)
+#pragma unroll
+        for (int m = 0; m < MB; ++m) acc0[r][m] = acc1[r][m] = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {               // word v: channels 8v .. 8v + 7 of the chunk
+        uint4 a4[MB];                             // the a'' pairs (t, t + 4) of those channels
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+          a4[m] = *reinterpret_cast<const uint4*>(lds + m * tbytes + (size_t)cc * kChunkBytes +
+                                                  16 * v);
+#pragma unroll
+        for (int r = 0; r < kGvRows; ++r) {
+          const uint32_t wv = v == 0 ? buf.w[j][r].x : v == 1 ? buf.w[j][r].y
+                            : v == 2 ? buf.w[j][r].z : buf.w[j][r].w;
           half2_t qp[4];
-          unpack_word8<ZP>(words[v], sub_lo, sub_hi, qp);
+          unpack_word8<ZP>(wv, sub_lo[r], sub_hi[r], qp);
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const half2_t apair = __builtin_bit_cast(half2_t, ap[4 * v + jj]);
-            if (jj & 1)
-              acc1 = __builtin_amdgcn_fdot2(qp[jj], apair, acc1, false);
-            else
-              acc0 = __builtin_amdgcn_fdot2(qp[jj], apair, acc0, false);
+          for (int m = 0; m < MB; ++m) {
+            const uint32_t ap[4] = {a4[m].x, a4[m].y, a4[m].z, a4[m].w};
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const half2_t apair = __builtin_bit_cast(half2_t, ap[jj]);
+              if (jj & 1)
+                acc1[r][m] = __builtin_amdgcn_fdot2(qp[jj], apair, acc1[r][m], false);
+              else
+                acc0[r][m] = __builtin_amdgcn_fdot2(qp[jj], apair, acc0[r][m], false);
+            }
           }
         }
-        part[r] = __builtin_fmaf(h2f((uint16_t)buf.st[j][r]) * f, acc0 + acc1, part[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < kGvRows; ++r) {
+        const float st = h2f((uint16_t)buf.st[j][r]);
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+          part[r][m] = __builtin_fmaf(st * f[m], acc0[r][m] + acc1[r][m], part[r][m]);
       }
     }
   };
@@ -207,49 +244,63 @@ __global__ __launch_bounds__(64 * NW) void w4a16_gemv_kernel(
   // bit set keep the upper half of their rows and send the lower half, the others the reverse),
   // then the plain butterfly over the lanes below the last exchanged bit; a fixed order ---------
   static_assert(kGvRows == 1 || kGvRows == 2 || kGvRows == 4, "one, two or four rows per wave");
-  float v[kGvRows];
-#pragma unroll
-  for (int r = 0; r < kGvRows; ++r) v[r] = part[r];
-  int row = 0;
   constexpr int kLastMask = (kGvRows == 4) ? 16 : (kGvRows == 2) ? 32 : 64;
 #pragma unroll
-  for (int n = kGvRows, mask = 32; n > 1; n >>= 1, mask >>= 1) {
-    const bool hi = (lane & mask) != 0;
+  for (int m = 0; m < MB; ++m) {
+    float v[kGvRows];
 #pragma unroll
-    for (int i = 0; i < n / 2; ++i) {
-      const float keep = hi ? v[n / 2 + i] : v[i];
-      const float give = hi ? v[i] : v[n / 2 + i];
-      v[i] = keep + __shfl_xor(give, mask);
+    for (int r = 0; r < kGvRows; ++r) v[r] = part[r][m];
+    int row = 0;
+#pragma unroll
+    for (int n = kGvRows, mask = 32; n > 1; n >>= 1, mask >>= 1) {
+      const bool hi = (lane & mask) != 0;
+#pragma unroll
+      for (int i = 0; i < n / 2; ++i) {
+        const float keep = hi ? v[n / 2 + i] : v[i];
+        const float give = hi ? v[i] : v[n / 2 + i];
+        v[i] = keep + __shfl_xor(give, mask);
+      }
+      if (hi) row += n / 2;
     }
-    if (hi) row += n / 2;
-  }
-  float kk = v[0];
+    float kk = v[0];
 #pragma unroll
-  for (int m = kLastMask / 2; m >= 1; m >>= 1) kk += __shfl_xor(kk, m);
-  if ((lane & (kLastMask - 1)) == 0 && n0 + row < N) Y[n0 + row] = f2h(kk);
+    for (int mk = kLastMask / 2; mk >= 1; mk >>= 1) kk += __shfl_xor(kk, mk);
+    if ((lane & (kLastMask - 1)) == 0 && n0 + row < N && m < M) Y[m * N + n0 + row] = f2h(kk);
+  }
+}
+
+// Two activation rows share the decoded codes with K <= 8192 (4096 x 4096: 5.7 against 5.9 us
+// in the small-batch MFMA kernel, 11008 x 4096: 10.2 against 11.3, 8192 x 8192: 13.1 against
+// 15.8); four rows took 185 VGPRs and were slower than that kernel (4096 x 4096: 7.0 against
+// 5.9 us).
+bool w4a16_gemv_fits(int64_t M, int64_t K) {
+  return (M == 1 && K <= kW4a16GemvMaxK) || (M == 2 && K <= 8192);
 }
 
 hipError_t launch_w4a16_gemv(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
                              const uint32_t* qweight, const uint16_t* scales16,
                              const uint8_t* zeros, const uint16_t* s16, uint16_t* Y,
                              hipStream_t stream) {
-  if (M != 1 || K > kW4a16GemvMaxK) return hipErrorInvalidValue;
+  if (!w4a16_gemv_fits(M, K)) return hipErrorInvalidValue;
   constexpr int RW = 2, NW = 8;
   constexpr int kGvThreads = 64 * NW;
   static_assert(kW4a16GemvMaxK <= 64 * kGvThreads, "table entries per thread: at most 8");
+  const int mb = (int)M;
   const unsigned blocks = (unsigned)((N + RW * NW - 1) / (RW * NW));
-  const size_t lds = w4a16_gemv_lds_bytes(1, K);
+  const size_t lds = w4a16_gemv_lds_bytes(mb, K);
   const bool one = K <= 64 * 32 * kGvPos;   // K <= 4096: one table entry per thread, one batch
-#define AWQ_GV1(GS_, ZP_, HS_, ONE_, TI_)                                                        \
-  w4a16_gemv_kernel<GS_, ZP_, HS_, ONE_, TI_, RW, NW><<<blocks, kGvThreads, lds, stream>>>(      \
-      A, N, K, qweight, scales16, zeros, s16, Y)
+#define AWQ_GV1(GS_, ZP_, HS_, ONE_, TI_, MB_)                                                   \
+  w4a16_gemv_kernel<GS_, ZP_, HS_, ONE_, TI_, RW, NW, MB_><<<blocks, kGvThreads, lds, stream>>>( \
+      A, M, N, K, qweight, scales16, zeros, s16, Y)
 #define AWQ_GV(GS_, ZP_, HS_)                                                                    \
   do {                                                                                           \
-    if (one) AWQ_GV1(GS_, ZP_, HS_, true, (4096 / 8 + kGvThreads - 1) / kGvThreads);            \
-    else if (K <= 8 * kGvThreads) AWQ_GV1(GS_, ZP_, HS_, false, 1);                             \
-    else if (K <= 16 * kGvThreads) AWQ_GV1(GS_, ZP_, HS_, false, 2);                            \
-    else if (K <= 32 * kGvThreads) AWQ_GV1(GS_, ZP_, HS_, false, 4);                            \
-    else AWQ_GV1(GS_, ZP_, HS_, false, 8);                                                      \
+    if (mb == 2 && one) AWQ_GV1(GS_, ZP_, HS_, true, 1, 2);                                      \
+    else if (mb == 2) AWQ_GV1(GS_, ZP_, HS_, false, 2, 2);                                       \
+    else if (one) AWQ_GV1(GS_, ZP_, HS_, true, (4096 / 8 + kGvThreads - 1) / kGvThreads, 1);    \
+    else if (K <= 8 * kGvThreads) AWQ_GV1(GS_, ZP_, HS_, false, 1, 1);                          \
+    else if (K <= 16 * kGvThreads) AWQ_GV1(GS_, ZP_, HS_, false, 2, 1);                         \
+    else if (K <= 32 * kGvThreads) AWQ_GV1(GS_, ZP_, HS_, false, 4, 1);                         \
+    else AWQ_GV1(GS_, ZP_, HS_, false, 8, 1);                                                   \
   } while (0)
 #define AWQ_GV_S(GS_, ZP_) \
   do { if (s16) AWQ_GV(GS_, ZP_, true); else AWQ_GV(GS_, ZP_, false); } while (0)
