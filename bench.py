@@ -592,12 +592,12 @@ def layer_sweep(awq, torch, reps, cpu_parts):
 
 
 def w4a16_sweep(awq, torch):
-    """w4a16_gemm_ws, symmetric codes in groups of 128, at the batch sizes 1, 4, 16, 64, 128,
+    """w4a16_gemm_ws, symmetric codes in groups of 128, at the batch sizes 1, 2, 4, 16, 64, 128,
     512 for 4096x4096 and 11008x4096, and at 1 and 16 for the 70B-class shapes 8192x8192,
     28672x8192 and 8192x28672 (decode GB/s where the weight is large enough to stream)."""
     out = []
     for (n, k) in ((4096, 4096), (11008, 4096)):
-        out += w4a16_time(awq, torch, n, k, (1, 4, 16, 64, 128, 512))
+        out += w4a16_time(awq, torch, n, k, (1, 2, 4, 16, 64, 128, 512))
     for (n, k) in ((8192, 8192), (28672, 8192), (8192, 28672)):
         out += w4a16_time(awq, torch, n, k, (1, 16))
     return out
