@@ -948,7 +948,7 @@ def test_fold_overflow_is_flagged(awq):
 
 
 @pytest.mark.parametrize("n,k,m", [(384, 512, 1), (384, 512, 16), (256, 4096, 3),
-                                   (4096, 4096, 1), (320, 512, 100)])
+                                   (4096, 4096, 1), (320, 512, 100), (300, 8192, 2)])
 def test_w4a16_without_s(awq, n, k, m):
     A, qw, sc, _ = _w4a16_case(n, k, m, seed=n + m + 7)
     say("w4a16 without s", (m, k), "x", (n, k))
@@ -1086,7 +1086,11 @@ W4A16_ZP_CASES = [(g, zp, n, k, m) for (g, zp) in QUANT_VARIANTS for (n, k, m) i
                   # K beyond the tiled kernel's LDS tables (skinny kernel in passes) and beyond
                   # the one-row kernel's (skinny kernel at M = 1)
                   (64, True, 192, 28672, 100), (128, False, 256, 28672, 1),
-                  (64, False, 320, 16384, 1), (128, True, 128, 32768, 17)]
+                  (64, False, 320, 16384, 1), (128, True, 128, 32768, 17),
+                  # two activation rows through the decode kernel (K <= 8192), ragged N, and
+                  # just past its K limit (small-batch kernel)
+                  (64, True, 333, 8192, 2), (128, True, 4096, 4096, 2), (64, False, 70, 1024, 2),
+                  (128, False, 256, 8320, 2)]
 
 
 @pytest.mark.parametrize("group,zp,n,k,m", W4A16_ZP_CASES)
