@@ -139,7 +139,7 @@ hipError_t launch_clip_search(const void* W, int dtype, int64_t N, int64_t K, co
 // ---- W4A16 ----
 // one or two activation rows: fp16 dot products against the block-scaled A / s tables (one per
 // row), the codes decoded once for both rows; M = 1 with K up to kW4a16GemvMaxK, M = 2 with
-// K <= 16384 (w4a16_gemv_fits); dynamic LDS of w4a16_gemv_lds_bytes(M, K) bytes (the launcher
+// K <= 28672 (w4a16_gemv_fits); dynamic LDS of w4a16_gemv_lds_bytes(M, K) bytes (the launcher
 // passes it)
 constexpr int64_t kW4a16GemvMaxK = 32768;
 size_t w4a16_gemv_lds_bytes(int MB, int64_t K);

@@ -269,12 +269,13 @@ __global__ __launch_bounds__(64 * NW) void w4a16_gemv_kernel(
   }
 }
 
-// Two activation rows share the decoded codes with K <= 16384 (4096 x 4096: 5.7 against 5.9 us
-// in the small-batch MFMA kernel, 11008 x 4096: 10.2 against 11.3, 8192 x 8192: 13.1 against
-// 15.8, 4096 x 11008: 11.0 against 14.1, 1024 x 16384: 11.0 against 16.0); four rows took 185
-// VGPRs and were slower than that kernel (4096 x 4096: 7.0 against 5.9 us).
+// Two activation rows share the decoded codes with K <= 28672, where their two tables (145 KiB)
+// still fit the LDS (4096 x 4096: 5.7 against 5.9 us in the small-batch MFMA kernel, 11008 x
+// 4096: 10.2 against 11.3, 8192 x 8192: 13.1 against 15.8, 4096 x 11008: 11.0 against 14.1,
+// 1024 x 16384: 11.0 against 16.0, 8192 x 28672: 43 against 50); four rows took 185 VGPRs and
+// were slower than that kernel (4096 x 4096: 7.0 against 5.9 us).
 bool w4a16_gemv_fits(int64_t M, int64_t K) {
-  return (M == 1 && K <= kW4a16GemvMaxK) || (M == 2 && K <= 16384);
+  return (M == 1 && K <= kW4a16GemvMaxK) || (M == 2 && K <= 28672);
 }
 
 hipError_t launch_w4a16_gemv(const uint16_t* A, int64_t M, int64_t N, int64_t K, int group,
@@ -296,7 +297,8 @@ hipError_t launch_w4a16_gemv(const uint16_t* A, int64_t M, int64_t N, int64_t K,
   do {                                                                                           \
     if (mb == 2 && one) AWQ_GV1(GS_, ZP_, HS_, true, 1, 2);                                      \
     else if (mb == 2 && K <= 8192) AWQ_GV1(GS_, ZP_, HS_, false, 2, 2);                          \
-    else if (mb == 2) AWQ_GV1(GS_, ZP_, HS_, false, 4, 2);                                       \
+    else if (mb == 2 && K <= 16384) AWQ_GV1(GS_, ZP_, HS_, false, 4, 2);                         \
+    else if (mb == 2) AWQ_GV1(GS_, ZP_, HS_, false, 8, 2);                                       \
     else if (one) AWQ_GV1(GS_, ZP_, HS_, true, (4096 / 8 + kGvThreads - 1) / kGvThreads, 1);    \
     else if (K <= 8 * kGvThreads) AWQ_GV1(GS_, ZP_, HS_, false, 1, 1);                          \
     else if (K <= 16 * kGvThreads) AWQ_GV1(GS_, ZP_, HS_, false, 2, 1);                         \

@@ -1087,10 +1087,11 @@ W4A16_ZP_CASES = [(g, zp, n, k, m) for (g, zp) in QUANT_VARIANTS for (n, k, m) i
                   # the one-row kernel's (skinny kernel at M = 1)
                   (64, True, 192, 28672, 100), (128, False, 256, 28672, 1),
                   (64, False, 320, 16384, 1), (128, True, 128, 32768, 17),
-                  # two activation rows through the decode kernel (K <= 16384), ragged N, and
+                  # two activation rows through the decode kernel (K <= 28672), ragged N, and
                   # just past its K limit (small-batch kernel)
                   (64, True, 333, 8192, 2), (128, True, 4096, 4096, 2), (64, False, 70, 1024, 2),
-                  (128, False, 256, 8320, 2), (64, True, 200, 16384, 2), (128, False, 96, 16512, 2)]
+                  (128, False, 256, 8320, 2), (64, True, 200, 16384, 2), (128, False, 96, 16512, 2),
+                  (128, True, 100, 28672, 2), (64, False, 80, 28800, 2)]
 
 
 @pytest.mark.parametrize("group,zp,n,k,m", W4A16_ZP_CASES)
